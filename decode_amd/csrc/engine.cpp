@@ -1,0 +1,753 @@
+// engine.cpp -- host side of libdecode: the C ABI of include/decode.h.
+//
+// Model load, context creation (all memory reserved for the worst case up
+// front), batch validation, ubatch splitting with up-front cell reservation,
+// the per-layer launch sequence, HIP-graph capture and replay of decode
+// steps, and on-demand logits / greedy-token readback.  Every arithmetic
+// step of the decoder runs in the kernels of this directory; this file only
+// moves bytes and launches work.
+#include "../../include/decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <vector>
+
+#include "kernels.h"
+
+int attention_chunk();
+
+// --------------------------------------------------------------- logging
+static void (*g_log_cb)(int, const char *, void *) = nullptr;
+static void *g_log_ud = nullptr;
+
+static void logf(int level, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (g_log_cb)
+        g_log_cb(level, buf, g_log_ud);
+    else if (level >= 3)
+        fprintf(stderr, "libdecode: %s\n", buf);
+}
+#define LOGE(...) logf(3, __VA_ARGS__)
+#define LOGW(...) logf(2, __VA_ARGS__)
+#define LOGI(...) logf(1, __VA_ARGS__)
+
+#define HIP_OK(expr, onfail)                                                          \
+    do {                                                                              \
+        hipError_t e_ = (expr);                                                       \
+        if (e_ != hipSuccess) {                                                       \
+            LOGE("%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), __FILE__, __LINE__); \
+            onfail;                                                                   \
+        }                                                                             \
+    } while (0)
+
+// --------------------------------------------------------------- memory
+struct Mem {
+    dec_allocator a{};
+    bool custom = false;
+    std::vector<void *> owned;
+
+    void *get(size_t bytes) {
+        bytes = (bytes + 255) & ~(size_t)255;
+        if (bytes == 0) bytes = 256;
+        void *p = nullptr;
+        if (custom) {
+            p = a.alloc(bytes, a.ud);
+        } else if (hipMalloc(&p, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            p = nullptr;
+        }
+        if (p) owned.push_back(p);
+        else LOGE("device allocation of %zu bytes failed", bytes);
+        return p;
+    }
+    void release() {
+        for (void *p : owned) {
+            if (custom) a.free(p, a.ud);
+            else (void)hipFree(p);
+        }
+        owned.clear();
+    }
+};
+
+static bool is_device_ptr(const void *p) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return at.type == hipMemoryTypeDevice;
+}
+
+// --------------------------------------------------------------- model
+struct Layer {
+    QMat wqkv, wo, wgu, wdown;
+    float *attn_norm = nullptr, *ffn_norm = nullptr;
+};
+
+struct dec_model {
+    dec_hparams hp{};
+    int qd = 0, kd = 0, F = 0, Fp = 0;
+    QMat tok, out;
+    float *out_norm = nullptr;
+    std::vector<Layer> layers;
+    Mem mem;
+    hipStream_t stream = nullptr;
+    int n_ctx_refs = 0;
+};
+
+static bool alloc_qmat(Mem &mem, QMat &m, int wtype, int N, int K) {
+    m.wtype = wtype;
+    m.N = N;
+    m.K = K;
+    size_t qbytes;
+    if (wtype == DEC_F32) qbytes = (size_t)N * K * 4;
+    else if (wtype == DEC_Q8_0) qbytes = (size_t)N * K;
+    else qbytes = (size_t)N * K / 2;
+    m.qs = mem.get(qbytes);
+    if (!m.qs) return false;
+    if (wtype != DEC_F32) {
+        m.d = (uint16_t *)mem.get((size_t)N * (K / 32) * 2);
+        if (!m.d) return false;
+    } else if (hipMemset(m.qs, 0, qbytes) != hipSuccess) {   // padding must read as zero
+        return false;
+    }
+    return true;
+}
+
+// Stages one fp32 source tensor on the device (if it is host memory) and
+// stores it into rows of m.
+struct Loader {
+    Mem &mem;
+    hipStream_t s;
+    float *stage = nullptr;
+    size_t stage_elems = 0;
+
+    bool put(const float *src, int rows, int K_src, QMat &m, int mode, int row_off) {
+        if (!src) {
+            LOGE("missing weight tensor");
+            return false;
+        }
+        const size_t n = (size_t)rows * K_src;
+        const float *dsrc = src;
+        if (!is_device_ptr(src)) {
+            if (n > stage_elems) {
+                LOGE("staging buffer too small");
+                return false;
+            }
+            HIP_OK(hipMemcpyAsync(stage, src, n * 4, hipMemcpyHostToDevice, s), return false);
+            dsrc = stage;
+        }
+        if (m.wtype == DEC_F32)
+            launch_copy_f32(dsrc, rows, K_src, m, mode, row_off, s);
+        else
+            launch_quantize(dsrc, rows, K_src, m, mode, row_off, s);
+        HIP_OK(hipGetLastError(), return false);
+        if (dsrc == stage) HIP_OK(hipStreamSynchronize(s), return false);   // stage reused next
+        return true;
+    }
+    bool vec(const float *src, int n, float **dst) {
+        if (!src) {
+            LOGE("missing norm vector");
+            return false;
+        }
+        *dst = (float *)mem.get((size_t)n * 4);
+        if (!*dst) return false;
+        HIP_OK(hipMemcpyAsync(*dst, src, (size_t)n * 4, hipMemcpyDefault, s), return false);
+        return true;
+    }
+};
+
+static bool valid_hparams(const dec_hparams &h) {
+    if (h.n_layer <= 0 || h.n_embd <= 0 || h.n_head <= 0 || h.n_head_kv <= 0 || h.head_dim <= 0 ||
+        h.n_ff <= 0 || h.n_vocab <= 0)
+        return false;
+    if (h.head_dim != 64 && h.head_dim != 128 && h.head_dim != 256) return false;
+    if (h.n_head % h.n_head_kv || h.n_head / h.n_head_kv > 8) return false;
+    if (h.wtype != DEC_F32 && h.wtype != DEC_Q8_0 && h.wtype != DEC_Q4_0) return false;
+    if (h.kvtype != DEC_F32 && h.kvtype != DEC_F16) return false;
+    if (h.n_embd % 32 || (h.n_head * h.head_dim) % 32) return false;
+    if (h.wtype != DEC_F32 && h.n_ff % 32) return false;
+    if (!(h.rms_eps >= 0.f) || !(h.rope_base > 0.f)) return false;
+    return true;
+}
+
+extern "C" dec_model *dec_model_load(const dec_hparams *hp, const dec_weights *w,
+                                     const dec_allocator *alloc, void *hip_stream) {
+    if (!hp || !w || !valid_hparams(*hp)) {
+        LOGE("dec_model_load: invalid hyper-parameters");
+        return nullptr;
+    }
+    if (alloc && (!alloc->alloc || !alloc->free)) {
+        LOGE("dec_model_load: allocator needs both callbacks");
+        return nullptr;
+    }
+    dec_model *m = new dec_model();
+    m->hp = *hp;
+    if (alloc) {
+        m->mem.a = *alloc;
+        m->mem.custom = true;
+    }
+    m->stream = (hipStream_t)hip_stream;
+    const dec_hparams &h = m->hp;
+    m->qd = h.n_head * h.head_dim;
+    m->kd = h.n_head_kv * h.head_dim;
+    m->F = h.n_ff;
+    m->Fp = (h.n_ff + 31) / 32 * 32;
+    const int d = h.n_embd, V = h.n_vocab, qd = m->qd, kd = m->kd, F = m->F, Fp = m->Fp;
+
+    bool ok = alloc_qmat(m->mem, m->tok, h.wtype, V, d) && alloc_qmat(m->mem, m->out, h.wtype, V, d);
+    m->layers.resize(h.n_layer);
+    for (int l = 0; ok && l < h.n_layer; l++) {
+        Layer &L = m->layers[l];
+        ok = alloc_qmat(m->mem, L.wqkv, h.wtype, qd + 2 * kd, d) && alloc_qmat(m->mem, L.wo, h.wtype, d, qd) &&
+             alloc_qmat(m->mem, L.wgu, h.wtype, 2 * Fp, d) && alloc_qmat(m->mem, L.wdown, h.wtype, d, Fp);
+    }
+    size_t stage = 0;
+    auto need = [&](const float *p, size_t n) {
+        if (p && !is_device_ptr(p) && n > stage) stage = n;
+    };
+    need(w->tok_embd, (size_t)V * d);
+    need(w->output, (size_t)V * d);
+    for (int l = 0; l < h.n_layer; l++) {
+        if (!w->wq || !w->wk || !w->wv || !w->wo || !w->ffn_gate || !w->ffn_up || !w->ffn_down ||
+            !w->attn_norm || !w->ffn_norm) {
+            ok = false;
+            break;
+        }
+        need(w->wq[l], (size_t)qd * d);
+        need(w->wk[l], (size_t)kd * d);
+        need(w->wv[l], (size_t)kd * d);
+        need(w->wo[l], (size_t)d * qd);
+        need(w->ffn_gate[l], (size_t)F * d);
+        need(w->ffn_up[l], (size_t)F * d);
+        need(w->ffn_down[l], (size_t)d * F);
+    }
+    Loader ld{m->mem, m->stream};
+    if (ok && stage) {
+        ld.stage = (float *)m->mem.get(stage * 4);
+        ld.stage_elems = stage;
+        ok = ld.stage != nullptr;
+    }
+    ok = ok && ld.put(w->tok_embd, V, d, m->tok, 0, 0) && ld.put(w->output, V, d, m->out, 0, 0) &&
+         ld.vec(w->output_norm, d, &m->out_norm);
+    for (int l = 0; ok && l < h.n_layer; l++) {
+        Layer &L = m->layers[l];
+        ok = ld.put(w->wq[l], qd, d, L.wqkv, 0, 0) && ld.put(w->wk[l], kd, d, L.wqkv, 0, qd) &&
+             ld.put(w->wv[l], kd, d, L.wqkv, 0, qd + kd) && ld.put(w->wo[l], d, qd, L.wo, 0, 0) &&
+             ld.put(w->ffn_gate[l], F, d, L.wgu, 1, 0) && ld.put(w->ffn_up[l], F, d, L.wgu, 2, 0) &&
+             ld.put(w->ffn_down[l], d, F, L.wdown, 0, 0) && ld.vec(w->attn_norm[l], d, &L.attn_norm) &&
+             ld.vec(w->ffn_norm[l], d, &L.ffn_norm);
+    }
+    if (ok) HIP_OK(hipStreamSynchronize(m->stream), ok = false);
+    if (!ok) {
+        LOGE("dec_model_load failed");
+        m->mem.release();
+        delete m;
+        return nullptr;
+    }
+    LOGI("model loaded: %d layers, d=%d, wtype=%d", h.n_layer, d, h.wtype);
+    return m;
+}
+
+extern "C" void dec_model_free(dec_model *m) {
+    if (!m) return;
+    if (m->n_ctx_refs) LOGW("dec_model_free: %d contexts still alive", m->n_ctx_refs);
+    (void)hipStreamSynchronize(m->stream);
+    m->mem.release();
+    delete m;
+}
+
+// Export of one stored matrix in its file form (GGUF-style blocks).
+extern "C" int64_t dec_model_tensor_blocks(const dec_model *m, int32_t id, int32_t layer, void *dst,
+                                           size_t cap) {
+    if (!m || id < 0 || id > 8) return 0;
+    const dec_hparams &h = m->hp;
+    if (id >= 2 && (layer < 0 || layer >= h.n_layer)) return 0;
+    const QMat *src = nullptr;
+    int rows = 0, cols = 0, mode = 0, row_off = 0;
+    const int d = h.n_embd;
+    switch (id) {
+    case DEC_T_TOK_EMBD: src = &m->tok; rows = h.n_vocab; cols = d; break;
+    case DEC_T_OUTPUT: src = &m->out; rows = h.n_vocab; cols = d; break;
+    case DEC_T_WQ: src = &m->layers[layer].wqkv; rows = m->qd; cols = d; break;
+    case DEC_T_WK: src = &m->layers[layer].wqkv; rows = m->kd; cols = d; row_off = m->qd; break;
+    case DEC_T_WV: src = &m->layers[layer].wqkv; rows = m->kd; cols = d; row_off = m->qd + m->kd; break;
+    case DEC_T_WO: src = &m->layers[layer].wo; rows = d; cols = m->qd; break;
+    case DEC_T_FFN_GATE: src = &m->layers[layer].wgu; rows = m->F; cols = d; mode = 1; break;
+    case DEC_T_FFN_UP: src = &m->layers[layer].wgu; rows = m->F; cols = d; mode = 2; break;
+    case DEC_T_FFN_DOWN: src = &m->layers[layer].wdown; rows = d; cols = m->F; break;
+    }
+    const int wt = src->wtype;
+    const int nb = cols / 32;
+    const size_t row_bytes = wt == DEC_F32 ? (size_t)cols * 4 : (size_t)nb * (wt == DEC_Q8_0 ? 34 : 18);
+    const size_t total = row_bytes * rows;
+    if (!dst || cap < total) return -(int64_t)total;
+    if (hipStreamSynchronize(m->stream) != hipSuccess) return 0;
+
+    // copy the whole stored matrix once, then pick rows / interleave blocks
+    const size_t srow_q = wt == DEC_F32 ? (size_t)src->K * 4 : (wt == DEC_Q8_0 ? (size_t)src->K : (size_t)src->K / 2);
+    std::vector<uint8_t> q((size_t)src->N * srow_q);
+    std::vector<uint16_t> sc(wt == DEC_F32 ? 0 : (size_t)src->N * (src->K / 32));
+    if (hipMemcpy(q.data(), src->qs, q.size(), hipMemcpyDeviceToHost) != hipSuccess) return 0;
+    if (!sc.empty() && hipMemcpy(sc.data(), src->d, sc.size() * 2, hipMemcpyDeviceToHost) != hipSuccess)
+        return 0;
+    uint8_t *o = (uint8_t *)dst;
+    for (int r = 0; r < rows; r++) {
+        int sr = r + row_off;
+        if (mode == 1) sr = ((r >> 5) << 6) + (r & 31);
+        if (mode == 2) sr = ((r >> 5) << 6) + 32 + (r & 31);
+        const uint8_t *qr = q.data() + (size_t)sr * srow_q;
+        if (wt == DEC_F32) {
+            memcpy(o, qr, (size_t)cols * 4);
+            o += (size_t)cols * 4;
+            continue;
+        }
+        const int qb = wt == DEC_Q8_0 ? 32 : 16;
+        const uint16_t *sr_d = sc.data() + (size_t)sr * (src->K / 32);
+        for (int b = 0; b < nb; b++) {
+            o[0] = (uint8_t)(sr_d[b] & 0xff);
+            o[1] = (uint8_t)(sr_d[b] >> 8);
+            memcpy(o + 2, qr + (size_t)b * qb, qb);
+            o += 2 + qb;
+        }
+    }
+    return (int64_t)total;
+}
+
+// --------------------------------------------------------------- context
+struct dec_ctx {
+    dec_model *m = nullptr;
+    dec_ctx_params p{};
+    hipStream_t s = nullptr;
+    bool own_stream = false;
+    int n_ctx = 0, n_batch = 0, n_ubatch = 0, n_seq = 0, Tmax = 0, step_cap = 0, n_out_cap = 0;
+    Mem mem;
+    std::vector<KVLayer> kv;
+    float *rope_cs = nullptr;
+    float *x = nullptr, *q = nullptr, *part = nullptr, *ml = nullptr, *logits = nullptr;
+    uint16_t *xn = nullptr, *o = nullptr, *h = nullptr;
+    int32_t *amax = nullptr, *dev_step = nullptr, *host_step = nullptr;
+    int chunk = 0, max_chunks = 0;
+    hipEvent_t staged = nullptr;
+    bool staged_pending = false;
+    std::vector<int> pos_max;
+    int n_out = 0;
+    std::vector<float> host_logits;
+    bool logits_fetched = false;
+    std::vector<int32_t> host_amax;
+    bool amax_fetched = false;
+    std::map<int, hipGraphExec_t> graphs;
+    dec_stats st{};
+};
+
+extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
+    if (!m || !pp) return nullptr;
+    dec_ctx_params p = *pp;
+    if (p.kv_unified) {
+        LOGE("dec_ctx_new: only one cache stream per sequence is supported (kv_unified = 0)");
+        return nullptr;
+    }
+    dec_ctx *c = new dec_ctx();
+    c->m = m;
+    c->p = p;
+    c->mem.a = m->mem.a;
+    c->mem.custom = m->mem.custom;
+    const dec_hparams &h = m->hp;
+    uint32_t n_ctx = p.n_ctx ? p.n_ctx : 4096;
+    n_ctx = (n_ctx + 255) / 256 * 256;
+    uint32_t n_batch = p.n_batch ? p.n_batch : n_ctx;
+    if (n_batch > n_ctx) n_batch = n_ctx;
+    uint32_t n_ubatch = p.n_ubatch ? p.n_ubatch : 512;
+    if (n_ubatch > n_batch) n_ubatch = n_batch;
+    const uint32_t n_seq = p.n_seq_max ? p.n_seq_max : 1;
+    if (n_seq > 256) {
+        delete c;
+        return nullptr;
+    }
+    c->n_ctx = (int)n_ctx;
+    c->n_batch = (int)n_batch;
+    c->n_ubatch = (int)n_ubatch;
+    c->n_seq = (int)n_seq;
+    c->Tmax = (int)(n_ubatch > n_seq ? n_ubatch : n_seq);
+    c->step_cap = (int)(n_batch > n_seq ? n_batch : n_seq);
+    c->n_out_cap = c->step_cap;
+    c->pos_max.assign(n_seq, -1);
+    if (p.hip_stream) {
+        c->s = (hipStream_t)p.hip_stream;
+    } else {
+        HIP_OK(hipStreamCreateWithFlags(&c->s, hipStreamNonBlocking), delete c; return nullptr);
+        c->own_stream = true;
+    }
+    const int d = h.n_embd, qd = m->qd, Fp = m->Fp, V = h.n_vocab, hd = h.head_dim;
+    const size_t esz = h.kvtype == DEC_F16 ? 2 : 4;
+    const size_t kv_elems = (size_t)n_seq * h.n_head_kv * n_ctx * hd;
+    bool ok = true;
+    c->kv.resize(h.n_layer);
+    for (int l = 0; ok && l < h.n_layer; l++) {
+        KVLayer &L = c->kv[l];
+        L.kvtype = h.kvtype;
+        L.n_ctx = (int)n_ctx;
+        L.n_kv = h.n_head_kv;
+        L.hd = hd;
+        L.k = c->mem.get(kv_elems * esz);
+        L.v = c->mem.get(kv_elems * esz);
+        ok = L.k && L.v;
+    }
+    c->chunk = attention_chunk();
+    c->max_chunks = (int)((n_ctx + c->chunk - 1) / c->chunk);
+    const size_t T = (size_t)c->Tmax;
+    if (ok) {
+        c->rope_cs = (float *)c->mem.get((size_t)n_ctx * hd * 4);
+        c->x = (float *)c->mem.get(T * d * 4);
+        c->xn = (uint16_t *)c->mem.get(T * d * 2);
+        c->q = (float *)c->mem.get(T * qd * 4);
+        c->o = (uint16_t *)c->mem.get(T * qd * 2);
+        c->h = (uint16_t *)c->mem.get(T * Fp * 2);
+        c->part = (float *)c->mem.get(T * h.n_head * c->max_chunks * hd * 4);
+        c->ml = (float *)c->mem.get(T * h.n_head * c->max_chunks * 2 * 4);
+        c->logits = (float *)c->mem.get((size_t)c->n_out_cap * V * 4);
+        c->amax = (int32_t *)c->mem.get((size_t)c->n_out_cap * 4);
+        c->dev_step = (int32_t *)c->mem.get((size_t)c->step_cap * 3 * 4);
+        ok = c->rope_cs && c->x && c->xn && c->q && c->o && c->h && c->part && c->ml && c->logits &&
+             c->amax && c->dev_step;
+    }
+    if (ok) HIP_OK(hipHostMalloc((void **)&c->host_step, (size_t)c->step_cap * 3 * 4, 0), ok = false);
+    if (ok) HIP_OK(hipEventCreateWithFlags(&c->staged, hipEventDisableTiming), ok = false);
+    if (ok) {
+        launch_rope_table(c->rope_cs, (int)n_ctx, hd, h.rope_base, c->s);
+        HIP_OK(hipGetLastError(), ok = false);
+    }
+    if (ok) HIP_OK(hipStreamSynchronize(c->s), ok = false);
+    if (!ok) {
+        LOGE("dec_ctx_new failed");
+        dec_ctx_free(c);
+        return nullptr;
+    }
+    m->n_ctx_refs++;
+    LOGI("context: n_ctx=%u n_batch=%u n_ubatch=%u n_seq=%u", n_ctx, n_batch, n_ubatch, n_seq);
+    return c;
+}
+
+extern "C" void dec_ctx_free(dec_ctx *c) {
+    if (!c) return;
+    if (c->s) (void)hipStreamSynchronize(c->s);
+    for (auto &g : c->graphs) (void)hipGraphExecDestroy(g.second);
+    if (c->staged) (void)hipEventDestroy(c->staged);
+    if (c->host_step) (void)hipHostFree(c->host_step);
+    c->mem.release();
+    if (c->own_stream) (void)hipStreamDestroy(c->s);
+    if (c->m && c->kv.size()) c->m->n_ctx_refs--;
+    delete c;
+}
+
+// Waits until the pinned staging buffer may be rewritten.
+static bool wait_staging(dec_ctx *c) {
+    if (c->staged_pending) {
+        HIP_OK(hipEventSynchronize(c->staged), return false);
+        c->staged_pending = false;
+    }
+    return true;
+}
+
+static bool stage_step(dec_ctx *c, int n) {
+    const size_t cap = (size_t)c->step_cap;
+    for (int k = 0; k < 3; k++)
+        HIP_OK(hipMemcpyAsync(c->dev_step + k * cap, c->host_step + k * cap, (size_t)n * 4,
+                              hipMemcpyHostToDevice, c->s),
+               return false);
+    HIP_OK(hipEventRecord(c->staged, c->s), return false);
+    c->staged_pending = true;
+    return true;
+}
+
+// Whether a call with T tokens uses the mat-vec kernels (decode-sized).
+static bool use_matvec(const dec_ctx *c, int T) {
+    return c->m->hp.wtype != DEC_F32 && T <= 2;
+}
+
+// Enqueues the layers for T tokens whose ids / positions / sequences live at
+// dev_step + off (+cap, +2cap).  Output rows: `n_rows` rows starting at
+// token row `row0` produce logits at logits row `out_row0`.
+static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out_row0) {
+    dec_model *m = c->m;
+    const dec_hparams &h = m->hp;
+    const int d = h.n_embd, qd = m->qd, Fp = m->Fp, V = h.n_vocab;
+    const size_t cap = (size_t)c->step_cap;
+    const int32_t *tok = c->dev_step + off;
+    TokInfo ti;
+    ti.pos = c->dev_step + cap + off;
+    ti.seq = c->dev_step + 2 * cap + off;
+    hipStream_t s = c->s;
+    const bool mv = use_matvec(c, T);
+    bool ok = true;
+
+    launch_embed(m->tok, tok, T, c->x, d, s);
+    for (int l = 0; ok && l < h.n_layer; l++) {
+        const Layer &L = m->layers[l];
+        EpiArgs eq;
+        eq.epi = EPI_QKV;
+        eq.qout = c->q;
+        eq.qd = qd;
+        eq.kd = m->kd;
+        eq.kv = c->kv[l];
+        eq.tok = ti;
+        eq.rope_cs = c->rope_cs;
+        if (mv) {
+            InArgs in;
+            in.x32 = c->x;
+            in.norm_g = L.attn_norm;
+            in.eps = h.rms_eps;
+            in.ldx = d;
+            ok = ok && launch_matvec(L.wqkv, in, eq, T, s);
+        } else {
+            launch_rmsnorm(c->x, d, L.attn_norm, d, h.rms_eps, nullptr, T, c->xn, d, s);
+            ok = ok && launch_gemm(L.wqkv, c->xn, d, eq, T, s);
+        }
+        AttnArgs at;
+        at.q = c->q;
+        at.kv = c->kv[l];
+        at.tok = ti;
+        at.H = h.n_head;
+        at.part = c->part;
+        at.ml = c->ml;
+        at.max_chunks = c->max_chunks;
+        at.chunk = c->chunk;
+        at.o = c->o;
+        ok = ok && launch_attention(at, T, s);
+
+        EpiArgs er;
+        er.epi = EPI_RESID;
+        er.y = c->x;
+        er.ldy = d;
+        if (mv) {
+            InArgs in;
+            in.x16 = c->o;
+            in.ldx = qd;
+            ok = ok && launch_matvec(L.wo, in, er, T, s);
+        } else {
+            ok = ok && launch_gemm(L.wo, c->o, qd, er, T, s);
+        }
+        EpiArgs eg;
+        eg.epi = EPI_SWIGLU;
+        eg.h = c->h;
+        eg.ldh = Fp;
+        if (mv) {
+            InArgs in;
+            in.x32 = c->x;
+            in.norm_g = L.ffn_norm;
+            in.eps = h.rms_eps;
+            in.ldx = d;
+            ok = ok && launch_matvec(L.wgu, in, eg, T, s);
+        } else {
+            launch_rmsnorm(c->x, d, L.ffn_norm, d, h.rms_eps, nullptr, T, c->xn, d, s);
+            ok = ok && launch_gemm(L.wgu, c->xn, d, eg, T, s);
+        }
+        if (mv) {
+            InArgs in;
+            in.x16 = c->h;
+            in.ldx = Fp;
+            ok = ok && launch_matvec(L.wdown, in, er, T, s);
+        } else {
+            ok = ok && launch_gemm(L.wdown, c->h, Fp, er, T, s);
+        }
+    }
+    if (ok && n_rows > 0) {
+        EpiArgs eo;
+        eo.epi = EPI_STORE;
+        eo.y = c->logits + (size_t)out_row0 * V;
+        eo.ldy = V;
+        if (use_matvec(c, n_rows)) {
+            InArgs in;
+            in.x32 = c->x + (size_t)row0 * d;
+            in.norm_g = m->out_norm;
+            in.eps = h.rms_eps;
+            in.ldx = d;
+            ok = launch_matvec(m->out, in, eo, n_rows, s);
+        } else {
+            launch_rmsnorm(c->x + (size_t)row0 * d, d, m->out_norm, d, h.rms_eps, nullptr, n_rows, c->xn, d, s);
+            ok = launch_gemm(m->out, c->xn, d, eo, n_rows, s);
+        }
+        launch_argmax(c->logits + (size_t)out_row0 * V, V, n_rows, c->amax + out_row0, s);
+    }
+    if (!ok) LOGE("kernel launch rejected a shape");
+    return ok && hipGetLastError() == hipSuccess;
+}
+
+static void reset_outputs(dec_ctx *c, int n_out) {
+    c->n_out = n_out;
+    c->logits_fetched = false;
+    c->amax_fetched = false;
+}
+
+extern "C" int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int32_t seq,
+                               int32_t output_all) {
+    if (!c || !tokens || n <= 0 || n > c->n_batch || seq < 0 || seq >= c->n_seq) return -1;
+    const int V = c->m->hp.n_vocab;
+    for (int i = 0; i < n; i++)
+        if (tokens[i] < 0 || tokens[i] >= V) {
+            LOGE("dec_prefill: token %d at %d out of range", tokens[i], i);
+            return -1;
+        }
+    const int p0 = c->pos_max[seq] + 1;
+    if (p0 + n > c->n_ctx) {
+        LOGW("dec_prefill: %d tokens do not fit (sequence at %d, n_ctx %d)", n, p0, c->n_ctx);
+        return 1;   // cells are reserved for the whole batch up front: nothing changes
+    }
+    if (!wait_staging(c)) return -3;
+    const size_t cap = (size_t)c->step_cap;
+    for (int i = 0; i < n; i++) {
+        c->host_step[i] = tokens[i];
+        c->host_step[cap + i] = p0 + i;
+        c->host_step[2 * cap + i] = seq;
+    }
+    if (!stage_step(c, n)) return -3;
+    c->st.n_prefill_calls++;
+    reset_outputs(c, 0);
+    for (int u = 0; u < n; u += c->n_ubatch) {
+        if (u > 0 && c->p.abort_cb && c->p.abort_cb(c->p.abort_ud)) {
+            LOGW("dec_prefill: aborted after %d of %d tokens", u, n);
+            return 2;
+        }
+        const int T = n - u < c->n_ubatch ? n - u : c->n_ubatch;
+        const bool last = u + T == n;
+        int row0 = 0, n_rows = 0;
+        if (output_all) {
+            n_rows = T;
+        } else if (last) {
+            row0 = T - 1;
+            n_rows = 1;
+        }
+        if (!run_tokens(c, u, T, row0, n_rows, output_all ? u : 0)) return -3;
+        c->pos_max[seq] = p0 + u + T - 1;
+        c->st.n_ubatches++;
+        reset_outputs(c, output_all ? u + T : (last ? 1 : 0));
+    }
+    return 0;
+}
+
+extern "C" int32_t dec_decode(dec_ctx *c, const int32_t *tokens, const int32_t *seq_ids, int32_t n) {
+    if (!c || !tokens || !seq_ids || n <= 0 || n > c->n_seq || n > c->Tmax) return -1;
+    const int V = c->m->hp.n_vocab;
+    std::vector<char> seen(c->n_seq, 0);
+    for (int i = 0; i < n; i++) {
+        const int sq = seq_ids[i];
+        if (tokens[i] < 0 || tokens[i] >= V || sq < 0 || sq >= c->n_seq || seen[sq]) return -1;
+        seen[sq] = 1;
+        if (c->pos_max[sq] + 1 >= c->n_ctx) return 1;
+    }
+    if (!wait_staging(c)) return -3;
+    const size_t cap = (size_t)c->step_cap;
+    for (int i = 0; i < n; i++) {
+        c->host_step[i] = tokens[i];
+        c->host_step[cap + i] = c->pos_max[seq_ids[i]] + 1;
+        c->host_step[2 * cap + i] = seq_ids[i];
+    }
+    if (!stage_step(c, n)) return -3;
+    auto it = c->graphs.find(n);
+    if (it == c->graphs.end()) {
+        hipGraph_t g = nullptr;
+        HIP_OK(hipStreamBeginCapture(c->s, hipStreamCaptureModeThreadLocal), return -3);
+        const bool ok = run_tokens(c, 0, n, 0, n, 0);
+        const hipError_t e = hipStreamEndCapture(c->s, &g);
+        if (!ok || e != hipSuccess || !g) {
+            LOGE("dec_decode: graph capture failed (%s)", hipGetErrorString(e));
+            if (g) (void)hipGraphDestroy(g);
+            return -3;
+        }
+        hipGraphExec_t ex = nullptr;
+        const hipError_t ei = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(g);
+        if (ei != hipSuccess) {
+            LOGE("dec_decode: graph instantiate failed (%s)", hipGetErrorString(ei));
+            return -3;
+        }
+        it = c->graphs.emplace(n, ex).first;
+        c->st.n_graph_captures++;
+    } else {
+        c->st.n_graph_replays++;
+    }
+    HIP_OK(hipGraphLaunch(it->second, c->s), return -3);
+    for (int i = 0; i < n; i++) c->pos_max[seq_ids[i]]++;
+    c->st.n_decode_calls++;
+    reset_outputs(c, n);
+    return 0;
+}
+
+static int resolve_row(const dec_ctx *c, int i) {
+    if (c->n_out <= 0) return -1;
+    if (i < 0) i += c->n_out;
+    if (i < 0 || i >= c->n_out) return -1;
+    return i;
+}
+
+extern "C" const float *dec_get_logits(dec_ctx *c, int32_t i) {
+    if (!c) return nullptr;
+    const int r = resolve_row(c, i);
+    if (r < 0) return nullptr;
+    const size_t V = (size_t)c->m->hp.n_vocab;
+    if (!c->logits_fetched) {
+        if (c->host_logits.size() < (size_t)c->n_out * V) c->host_logits.resize((size_t)c->n_out * V);
+        HIP_OK(hipStreamSynchronize(c->s), return nullptr);
+        HIP_OK(hipMemcpy(c->host_logits.data(), c->logits, (size_t)c->n_out * V * 4, hipMemcpyDeviceToHost),
+               return nullptr);
+        c->logits_fetched = true;
+    }
+    return c->host_logits.data() + (size_t)r * V;
+}
+
+static bool fetch_amax(dec_ctx *c) {
+    if (c->amax_fetched) return true;
+    c->host_amax.resize(c->n_out);
+    HIP_OK(hipMemcpyAsync(c->host_amax.data(), c->amax, (size_t)c->n_out * 4, hipMemcpyDeviceToHost, c->s),
+           return false);
+    HIP_OK(hipStreamSynchronize(c->s), return false);
+    c->amax_fetched = true;
+    return true;
+}
+
+extern "C" int32_t dec_argmax(dec_ctx *c, int32_t i) {
+    if (!c) return -1;
+    const int r = resolve_row(c, i);
+    if (r < 0 || !fetch_amax(c)) return -1;
+    return c->host_amax[r];
+}
+
+extern "C" int32_t dec_argmax_all(dec_ctx *c, int32_t *out, int32_t cap) {
+    if (!c || c->n_out <= 0) return 0;
+    if (!out || cap < c->n_out) return -1;
+    if (!fetch_amax(c)) return -1;
+    memcpy(out, c->host_amax.data(), (size_t)c->n_out * 4);
+    return c->n_out;
+}
+
+extern "C" int32_t dec_seq_pos_max(const dec_ctx *c, int32_t seq) {
+    if (!c || seq < 0 || seq >= c->n_seq) return -1;
+    return c->pos_max[seq];
+}
+
+extern "C" int32_t dec_seq_clear(dec_ctx *c, int32_t seq) {
+    if (!c || seq < 0 || seq >= c->n_seq) return -1;
+    c->pos_max[seq] = -1;
+    return 0;
+}
+
+extern "C" void dec_get_stats(const dec_ctx *c, dec_stats *out) {
+    if (!c || !out) return;
+    *out = c->st;
+}
+
+extern "C" void dec_set_log_callback(void (*cb)(int, const char *, void *), void *ud) {
+    g_log_cb = cb;
+    g_log_ud = ud;
+}
+
+extern "C" const char *dec_version(void) { return "libdecode 0.1 (gfx950, HIP)"; }

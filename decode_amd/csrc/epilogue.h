@@ -1,0 +1,83 @@
+// epilogue.h -- output handling shared by the mat-vec and the GEMM kernels.
+//
+// Output rows are handled in pairs so that the two values a RoPE rotation
+// or a SwiGLU product needs always meet in one lane:
+//   PAIR_ADJ: pair p = rows (2p, 2p+1)    (RoPE rotates adjacent elements)
+//   PAIR_GU : gate/up matrices are stored interleaved in groups of 32 rows
+//             (32 gate rows, then the 32 matching up rows); pair p = feature p
+//             = rows (64*(p/32) + p%32, same + 32).
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+DEV void pair_rows(int mode, int p, int &r0, int &r1) {
+    if (mode == PAIR_GU) {
+        r0 = ((p >> 5) << 6) + (p & 31);
+        r1 = r0 + 32;
+    } else {
+        r0 = 2 * p;
+        r1 = r0 + 1;
+    }
+}
+
+DEV void store_kv_pair(void *base, int kvtype, size_t idx, float a, float b) {
+    if (kvtype == T_F16) {
+        h2 v;
+        v.x = (f16)a;
+        v.y = (f16)b;
+        *(h2 *)((uint16_t *)base + idx) = v;
+    } else {
+        *(float2 *)((float *)base + idx) = make_float2(a, b);
+    }
+}
+
+// Applies the epilogue to the pair (r0, r1) = values (a, b) of token t.
+// p is the pair index (the feature index for SWIGLU).
+DEV void epi_pair(const EpiArgs &e, int t, int p, int r0, int r1, float a, float b) {
+    switch (e.epi) {
+    case EPI_STORE: {
+        float *y = e.y + (size_t)t * e.ldy;
+        y[r0] = a;
+        y[r1] = b;
+        break;
+    }
+    case EPI_RESID: {
+        float *y = e.y + (size_t)t * e.ldy;
+        y[r0] += a;
+        y[r1] += b;
+        break;
+    }
+    case EPI_SWIGLU: {
+        const float hv = silu(a) * b;
+        ((f16 *)e.h)[(size_t)t * e.ldh + p] = (f16)hv;
+        break;
+    }
+    case EPI_QKV: {
+        const int hd = e.kv.hd;
+        const int pos = e.tok.pos[t];
+        if (r0 < e.qd + e.kd) {
+            // RoPE: rotate the adjacent pair by pos * base^(-2i/hd)
+            const int rr = r0 < e.qd ? r0 : r0 - e.qd;
+            const int i = (rr % hd) >> 1;
+            const float2 cs = *(const float2 *)(e.rope_cs + ((size_t)pos * (hd >> 1) + i) * 2);
+            const float ra = a * cs.x - b * cs.y;
+            const float rb = a * cs.y + b * cs.x;
+            if (r0 < e.qd) {
+                float *q = e.qout + (size_t)t * e.qd;
+                *(float2 *)(q + r0) = make_float2(ra, rb);
+            } else {
+                const int g = rr / hd, el = rr % hd;
+                const size_t idx = (((size_t)e.tok.seq[t] * e.kv.n_kv + g) * e.kv.n_ctx + pos) * hd + el;
+                store_kv_pair(e.kv.k, e.kv.kvtype, idx, ra, rb);
+            }
+        } else {
+            const int rr = r0 - e.qd - e.kd;
+            const int g = rr / hd, el = rr % hd;
+            const size_t idx = (((size_t)e.tok.seq[t] * e.kv.n_kv + g) * e.kv.n_ctx + pos) * hd + el;
+            store_kv_pair(e.kv.v, e.kv.kvtype, idx, a, b);
+        }
+        break;
+    }
+    }
+}

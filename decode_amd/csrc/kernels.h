@@ -1,0 +1,109 @@
+// kernels.h -- argument structs and host launchers of the libdecode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// One stored (possibly fused) weight matrix [N][K], row-major.
+//   F32 : qs = float[N][K]
+//   Q8_0: qs = int8 codes [N][K],           d = f16 scales [N][K/32]
+//   Q4_0: qs = packed nibbles [N][K/2]      d = f16 scales [N][K/32]
+//         (16 bytes per 32-weight block, byte k = code k | code k+16 << 4)
+struct QMat {
+    int wtype = 0;
+    int N = 0, K = 0;
+    void *qs = nullptr;
+    uint16_t *d = nullptr;
+};
+
+// How output rows of a matrix pair up in an epilogue.
+enum PairMode { PAIR_ADJ = 0, PAIR_GU = 1 };
+
+// Epilogues shared by the mat-vec and the GEMMs.
+enum Epi {
+    EPI_STORE = 0,   // y[t][n] = acc                         (f32)
+    EPI_RESID = 1,   // y[t][n] += acc                        (f32 residual stream)
+    EPI_QKV = 2,     // RoPE on q,k; q -> qout f32; k,v -> cache (kvtype)
+    EPI_SWIGLU = 3,  // rows interleaved 32 gate / 32 up; h[t][j] = f16(silu(g) * u)
+};
+
+// Per-token step data, device arrays indexed by the token's row in the call.
+struct TokInfo {
+    const int32_t *pos = nullptr;   // position of the token in its sequence
+    const int32_t *seq = nullptr;   // sequence id
+};
+
+// KV cache of one layer: [n_seq][n_head_kv][n_ctx][head_dim], kvtype elements.
+struct KVLayer {
+    void *k = nullptr, *v = nullptr;
+    int kvtype = 0;
+    int n_ctx = 0, n_kv = 0, hd = 0;
+};
+
+struct EpiArgs {
+    int epi = EPI_STORE;
+    float *y = nullptr;        // STORE / RESID: [T][ldy]
+    int ldy = 0;
+    uint16_t *h = nullptr;     // SWIGLU: f16 [T][ldh]
+    int ldh = 0;
+    float *qout = nullptr;     // QKV: f32 [T][qd]
+    int qd = 0, kd = 0;
+    KVLayer kv;
+    TokInfo tok;
+    const float *rope_cs = nullptr;  // [n_ctx][hd/2][2] (cos, sin)
+};
+
+// Input of a mat-vec / GEMM: either an f32 residual row normalized on the
+// fly (RMSNorm prologue) or an f16 activation row.
+struct InArgs {
+    const float *x32 = nullptr;      // [T][ldx] f32; used when norm_g != nullptr
+    const float *norm_g = nullptr;
+    float eps = 0.f;
+    const uint16_t *x16 = nullptr;   // [T][ldx] f16 when no prologue
+    int ldx = 0;
+    const int32_t *row_idx = nullptr;  // optional gather: input row of output row t
+};
+
+// ---- launchers (all asynchronous on `s`) ---------------------------------
+// Block quantization of fp32 rows on the device (bit-exact with the block
+// definitions).  Source rows [rows][K] f32 (device); row r goes to stored row
+// dst_row(r) of `m` where mode 0: r + row_off, 1: gate slot, 2: up slot.
+void launch_quantize(const float *src, int rows, int K, QMat &m, int mode, int row_off,
+                     hipStream_t s);
+// fp32 copy into a (possibly padded) F32 matrix: src [rows][K_src] -> m rows
+// dst_row(r), columns [0, K_src); the caller zero-fills padding beforehand.
+void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, int row_off,
+                     hipStream_t s);
+
+// y = W x for T tokens (decode).  Q8_0 / Q4_0 only.
+bool launch_matvec(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, hipStream_t s);
+// Y = X W^T for T tokens (prefill / batched decode): MFMA for Q8_0 / Q4_0
+// with N % 128 == 0, a plain fp32 kernel otherwise.
+bool launch_gemm(const QMat &W, const uint16_t *X, int ldx, const EpiArgs &ep, int T,
+                 hipStream_t s);
+
+// x[t] = dequantized row tok[t] of the embedding table (f32).
+void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, hipStream_t s);
+// xn[t] = f16(rmsnorm(x[row_idx ? row_idx[t] : t]) * g)
+void launch_rmsnorm(const float *x, int ldx, const float *g, int d, float eps,
+                    const int32_t *row_idx, int T, uint16_t *xn, int ldn, hipStream_t s);
+// out[t] = argmax of logits row t (lowest index on ties)
+void launch_argmax(const float *logits, int V, int T, int32_t *out, hipStream_t s);
+// cos/sin table [n_ctx][hd/2][2] with theta = p * base^(-2i/hd) in double
+void launch_rope_table(float *cs, int n_ctx, int hd, float base, hipStream_t s);
+
+// Causal attention of T tokens against their sequences' cached rows
+// (positions 0..pos[t]), split over key chunks of `chunk` rows, then merged.
+struct AttnArgs {
+    const float *q = nullptr;     // [T][H*hd] f32 (after RoPE)
+    KVLayer kv;
+    TokInfo tok;
+    int H = 0;
+    float *part = nullptr;        // [T][H][max_chunks][hd] partial outputs
+    float *ml = nullptr;          // [T][H][max_chunks][2] running max / sum
+    int max_chunks = 0, chunk = 0;
+    uint16_t *o = nullptr;        // [T][H*hd] f16 output
+};
+bool launch_attention(const AttnArgs &a, int T, hipStream_t s);
+
+// f16 -> (rows of) GGUF-style export helpers are host code in engine.cpp.

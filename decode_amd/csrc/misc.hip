@@ -1,0 +1,217 @@
+// misc.hip -- small kernels of the decoder step and of weight loading (gfx950).
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+DEV int dst_row(int mode, int r, int row_off) {
+    if (mode == 1) return ((r >> 5) << 6) + (r & 31);        // gate slot of a 64-row group
+    if (mode == 2) return ((r >> 5) << 6) + 32 + (r & 31);   // up slot
+    return r + row_off;
+}
+
+// ---- block quantization ----------------------------------------------------
+// Q8_0: d = max|x| / 127; codes = round-half-away(x * (1/d)).
+// Q4_0: m = element of largest magnitude (first on ties), d = m / -8;
+//       codes = min(15, floor(x * (1/d) + 8.5)).
+// fp32 arithmetic with no contraction, so codes match any IEEE fp32
+// implementation of the same steps bit for bit; the scale is stored as f16
+// (round to nearest even).
+__global__ __launch_bounds__(256) void k_quantize(const float *src, int rows, int K, QMat m,
+                                                  int mode, int row_off) {
+#pragma clang fp contract(off)
+    const int nb = K >> 5;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)rows * nb) return;
+    const int r = (int)(idx / nb), b = (int)(idx % nb);
+    const float *x = src + (size_t)r * K + b * 32;
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 32; j += 4) {
+        const float4 t = *(const float4 *)(x + j);
+        v[j] = t.x; v[j + 1] = t.y; v[j + 2] = t.z; v[j + 3] = t.w;
+    }
+    const int dr = dst_row(mode, r, row_off);
+    if (m.wtype == T_Q8_0) {
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
+        float d = amax / 127.0f;
+        // keep the f16 rounding a separate step: a fused multiply-add form of
+        // the conversion would turn a -0 scale into +0
+        asm volatile("" : "+v"(d));
+        const float id = d != 0.f ? 1.0f / d : 0.f;
+        m.d[(size_t)dr * nb + b] = f32_to_f16_bits(d);
+        uint32_t packed[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int q = (int)roundf(v[4 * i + e] * id);
+                w |= ((uint32_t)(q & 0xff)) << (8 * e);
+            }
+            packed[i] = w;
+        }
+        uint4 *dst = (uint4 *)((int8_t *)m.qs + (size_t)dr * K + b * 32);
+        dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    } else {
+        float amax = 0.f, mx = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            const float a = fabsf(v[j]);
+            if (a > amax) { amax = a; mx = v[j]; }
+        }
+        float d = mx / -8.0f;
+        asm volatile("" : "+v"(d));   // see above: an all-zero block has scale -0
+        const float id = d != 0.f ? 1.0f / d : 0.f;
+        m.d[(size_t)dr * nb + b] = f32_to_f16_bits(d);
+        int code[32];
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            const float t = v[j] * id;
+            const float s = t + 8.5f;
+            int c = (int)floorf(s);
+            c = c > 15 ? 15 : (c < 0 ? 0 : c);
+            code[j] = c;
+        }
+        uint32_t packed[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int k = 4 * i + e;
+                w |= (uint32_t)(code[k] | (code[k + 16] << 4)) << (8 * e);
+            }
+            packed[i] = w;
+        }
+        *(uint4 *)((uint8_t *)m.qs + (size_t)dr * (K >> 1) + b * 16) =
+            make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_copy_f32(const float *src, int rows, int K_src, QMat m,
+                                                  int mode, int row_off) {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)rows * K_src) return;
+    const int r = (int)(idx / K_src), k = (int)(idx % K_src);
+    ((float *)m.qs)[(size_t)dst_row(mode, r, row_off) * m.K + k] = src[idx];
+}
+
+// ---- embedding: x[t] = dequantized row tok[t] (the article's get_rows) -----
+__global__ __launch_bounds__(256) void k_embed(QMat E, const int32_t *tok, float *x, int ldx) {
+    const int t = blockIdx.x;
+    const int row = tok[t];
+    const int K = E.K, nb = K >> 5;
+    float *xr = x + (size_t)t * ldx;
+    for (int j = threadIdx.x; j < K; j += 256) {
+        float v;
+        if (E.wtype == T_F32) {
+            v = ((const float *)E.qs)[(size_t)row * K + j];
+        } else {
+            const int b = j >> 5, e = j & 31;
+            const float d = f16_bits_to_f32(E.d[(size_t)row * nb + b]);
+            if (E.wtype == T_Q8_0) {
+                v = (float)((const int8_t *)E.qs)[(size_t)row * K + j] * d;
+            } else {
+                const uint8_t byte = ((const uint8_t *)E.qs)[(size_t)row * (K >> 1) + b * 16 + (e & 15)];
+                const int c = e < 16 ? (byte & 15) : (byte >> 4);
+                v = (float)(c - 8) * d;
+            }
+        }
+        xr[j] = v;
+    }
+}
+
+// ---- RMSNorm to f16: xn = f16(x * (1/sqrt(mean(x^2) + eps)) * g) ----------
+__global__ __launch_bounds__(256) void k_rmsnorm(const float *x, int ldx, const float *g, int d,
+                                                 float eps, const int32_t *row_idx, uint16_t *xn,
+                                                 int ldn) {
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    const int row = row_idx ? row_idx[t] : t;
+    const float *xr = x + (size_t)row * ldx;
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < d; j += 256) ss += xr[j] * xr[j];
+    ss = block_sum256(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    f16 *o = (f16 *)xn + (size_t)t * ldn;
+    for (int j = threadIdx.x; j < d; j += 256) o[j] = (f16)(xr[j] * r * g[j]);
+}
+
+// ---- greedy: index of the largest logit, lowest index on ties --------------
+__global__ __launch_bounds__(256) void k_argmax(const float *logits, int V, int32_t *out) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int t = blockIdx.x;
+    const float *l = logits + (size_t)t * V;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int j = threadIdx.x; j < V; j += 256) {
+        const float v = l[j];
+        if (v > bv) { bv = v; bi = j; }      // j increases: first max kept per thread
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { sv[w] = bv; si[w] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < 4; k++)
+            if (sv[k] > bv || (sv[k] == bv && si[k] < bi)) { bv = sv[k]; bi = si[k]; }
+        if (bi == 0x7fffffff) bi = 0;
+        out[t] = bi;
+    }
+}
+
+// ---- RoPE angles: theta = p * base^(-2i/hd), evaluated in double ----------
+__global__ __launch_bounds__(256) void k_rope_table(float *cs, int n_ctx, int hd, float base) {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    const int half = hd >> 1;
+    if (idx >= (long long)n_ctx * half) return;
+    const int p = (int)(idx / half), i = (int)(idx % half);
+    const double th = (double)p * pow((double)base, -2.0 * (double)i / (double)hd);
+    cs[2 * idx + 0] = (float)cos(th);
+    cs[2 * idx + 1] = (float)sin(th);
+}
+
+}  // namespace
+
+void launch_quantize(const float *src, int rows, int K, QMat &m, int mode, int row_off,
+                     hipStream_t s) {
+    const long long n = (long long)rows * (K / 32);
+    hipLaunchKernelGGL(k_quantize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows, K, m,
+                       mode, row_off);
+}
+
+void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, int row_off,
+                     hipStream_t s) {
+    const long long n = (long long)rows * K_src;
+    hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows, K_src,
+                       m, mode, row_off);
+}
+
+void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, hipStream_t s) {
+    hipLaunchKernelGGL(k_embed, dim3(T), dim3(256), 0, s, E, tok, x, ldx);
+}
+
+void launch_rmsnorm(const float *x, int ldx, const float *g, int d, float eps,
+                    const int32_t *row_idx, int T, uint16_t *xn, int ldn, hipStream_t s) {
+    hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), 0, s, x, ldx, g, d, eps, row_idx, xn, ldn);
+}
+
+void launch_argmax(const float *logits, int V, int T, int32_t *out, hipStream_t s) {
+    hipLaunchKernelGGL(k_argmax, dim3(T), dim3(256), 0, s, logits, V, out);
+}
+
+void launch_rope_table(float *cs, int n_ctx, int hd, float base, hipStream_t s) {
+    const long long n = (long long)n_ctx * (hd / 2);
+    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, cs, n_ctx, hd,
+                       base);
+}

@@ -1,0 +1,195 @@
+/*
+ * decode.h -- C ABI of libdecode.so: one LLaMA-style decoder step on an
+ * MI355X (gfx950), with block-quantized weights and an f16 KV cache.
+ *
+ * The calls follow the inference loop of the article "llama.cpp AI LLM
+ * Engine - how it works" (romankryvolapov.com): load the weights (steps 2-6),
+ * create a context that owns the KV cache and every work buffer (step 7),
+ * run a prompt as a batch split into ubatches (steps 10-13), run one new
+ * token per step (the generation loop of step 8 and the KV-cache appendix),
+ * read the logits (step 14) and take the greedy token (step 15).
+ * Tokenization, text and sampler chains are not part of this library.
+ *
+ * Conventions for every call:
+ *  - Handles are opaque and owned by the library.
+ *  - Host arrays passed in are read during the call only; the caller keeps
+ *    ownership.  Pointers returned stay valid until the next prefill /
+ *    decode / free on the same context.
+ *  - All device work runs on one HIP stream: the one given at creation
+ *    (hip_stream, a hipStream_t), or the null stream when that is NULL.
+ *  - Calls on one context must not overlap (no internal locking).
+ *  - Errors are reported through return values (documented per call) and
+ *    a message to the log callback; nothing aborts the process.
+ */
+#ifndef DECODE_H
+#define DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  Q8_0: blocks of 32 weights = f16 scale + 32 int8 codes
+ * (34 bytes).  Q4_0: blocks of 32 weights = f16 scale + 16 bytes of 4-bit
+ * codes offset by 8; byte k holds code k (low nibble) and code k+16 (high
+ * nibble) (18 bytes).  The article names these as GGUF tensor types of
+ * fixed-size blocks sharing one scale (step 2c). */
+typedef enum { DEC_F32 = 0, DEC_F16 = 1, DEC_Q8_0 = 2, DEC_Q4_0 = 3 } dec_type;
+
+/* Hyper-parameters (the article's step 4: embedding length, block count,
+ * feed-forward length, head count, KV head count, RoPE frequency base).
+ * wtype applies to every 2-D matrix (F32, Q8_0 or Q4_0); kvtype is the
+ * cache element type (F32 or F16).  Quantized types need n_embd, n_ff and
+ * n_head*head_dim to be multiples of 32; head_dim must be even and at most
+ * 256, and n_head a multiple of n_head_kv. */
+typedef struct {
+    int32_t n_layer, n_embd, n_head, n_head_kv, head_dim, n_ff, n_vocab;
+    float   rms_eps;     /* 1e-5 */
+    float   rope_base;   /* 10000 */
+    int32_t wtype, kvtype;
+} dec_hparams;
+
+/* fp32 source weights, row-major [out][in] (the article's step 6 tensor set
+ * for the LLaMA family: tok_embd, output_norm, output, and per layer
+ * attn_norm, q/k/v, wo, ffn_norm, ffn_gate, ffn_up, ffn_down).
+ * Per-layer members are arrays of n_layer pointers.  Each pointer may be
+ * host memory or device memory of the current HIP device; the library
+ * copies / quantizes them on the device during dec_model_load and does not
+ * keep them.  Shapes: tok_embd, output [n_vocab][n_embd]; wq
+ * [n_head*head_dim][n_embd]; wk, wv [n_head_kv*head_dim][n_embd]; wo
+ * [n_embd][n_head*head_dim]; ffn_gate, ffn_up [n_ff][n_embd]; ffn_down
+ * [n_embd][n_ff]; norms [n_embd]. */
+typedef struct {
+    const float *tok_embd, *output_norm, *output;
+    const float *const *attn_norm, *const *wq, *const *wk, *const *wv, *const *wo;
+    const float *const *ffn_norm, *const *ffn_gate, *const *ffn_up, *const *ffn_down;
+} dec_weights;
+
+/* Optional device-memory provider.  alloc returns a device pointer of at
+ * least `bytes` (aligned to 256) or NULL; free releases it.  NULL allocator
+ * -> hipMalloc / hipFree.  The Python binding routes this to PyTorch. */
+typedef struct {
+    void *(*alloc)(size_t bytes, void *ud);
+    void  (*free)(void *ptr, void *ud);
+    void  *ud;
+} dec_allocator;
+
+typedef struct dec_model dec_model;
+typedef struct dec_ctx   dec_ctx;
+
+/* Loads (copies, and for Q8_0/Q4_0 quantizes on the device) every weight.
+ * Returns a model handle, or NULL on invalid hyper-parameters, a NULL
+ * weight pointer, allocation failure or a device error (article step 2a:
+ * the load entry returns the model or nullptr).  The allocator struct is
+ * copied; hip_stream is used for the load only. */
+dec_model *dec_model_load(const dec_hparams *hp, const dec_weights *w,
+                          const dec_allocator *alloc, void *hip_stream);
+
+/* Tensor ids for dec_model_tensor_blocks. */
+enum { DEC_T_TOK_EMBD = 0, DEC_T_OUTPUT = 1, DEC_T_WQ = 2, DEC_T_WK = 3, DEC_T_WV = 4,
+       DEC_T_WO = 5, DEC_T_FFN_GATE = 6, DEC_T_FFN_UP = 7, DEC_T_FFN_DOWN = 8 };
+
+/* Copies one stored matrix to host memory dst in its file form: GGUF-style
+ * blocks (34 or 18 bytes each, row-major, scale first) for Q8_0 / Q4_0, or
+ * fp32 rows for F32.  `layer` is ignored for tok_embd and output.  Returns
+ * the byte count; when dst is NULL or cap is too small returns minus the
+ * needed size (the article's size-probe convention, step 9); 0 on a bad id
+ * or layer.  Synchronizes the load stream. */
+int64_t dec_model_tensor_blocks(const dec_model *m, int32_t tensor_id, int32_t layer,
+                                void *dst, size_t cap);
+
+/* Frees the model.  Contexts created from it must be freed first. */
+void dec_model_free(dec_model *m);
+
+/* Context parameters (article step 7).  n_ctx: positions per sequence,
+ * rounded up to a multiple of 256 (0 -> 4096).  n_batch: most tokens one
+ * prefill call may take (0 -> n_ctx, clamped to n_ctx).  n_ubatch: most
+ * tokens run through the layers at once (0 -> 512, clamped to n_batch).
+ * n_seq_max: independent sequences, each with its own n_ctx cells
+ * (0 -> 1).  kv_unified must be 0 (one cache stream per sequence).
+ * abort_cb (optional) is polled between ubatches; a nonzero return stops
+ * the call with status 2. */
+typedef struct {
+    uint32_t n_ctx, n_batch, n_ubatch, n_seq_max;
+    int32_t  kv_unified;
+    void    *hip_stream;
+    int    (*abort_cb)(void *ud);
+    void    *abort_ud;
+} dec_ctx_params;
+
+/* Creates a context and allocates, for the worst case, the KV cache
+ * (n_layer x n_seq_max x n_ctx positions), the activation buffers for
+ * n_ubatch tokens, and the logits buffer (n_batch rows).  Nothing is
+ * allocated afterwards (the article's worst-case reservation, step 7 / 13b).
+ * Returns NULL on invalid parameters or allocation failure. */
+dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *p);
+
+/* Runs n prompt tokens of one sequence, continuing at seq_pos_max(seq)+1
+ * (article step 10: missing positions are filled from the cache).  The
+ * batch is split into ubatches of at most n_ubatch tokens, and cache cells
+ * for all of them are reserved before any runs (steps 11-12).  Logits are
+ * produced for the last token only, or for every token when output_all is
+ * nonzero; rows are appended in batch order (step 14).
+ * Returns 0 ok | 1 not enough free cells (nothing changed) | 2 aborted by
+ * abort_cb (finished ubatches stay in the cache, later ones are rolled
+ * back) | -1 invalid input (n <= 0, n > n_batch, token out of range, bad
+ * seq_id) | -2 allocation failure | -3 device error (the article's
+ * llama_decode codes, step 11). */
+int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int32_t seq_id,
+                    int32_t output_all);
+
+/* One generation step: token i belongs to sequence seq_ids[i] and is placed
+ * at that sequence's next position; K and V are appended before attending
+ * (KV-cache appendix).  All n sequences must differ; n <= n_seq_max.
+ * Logits are produced for every token, row i for token i.  The step's
+ * kernel sequence is captured once per n as a HIP graph and replayed (the
+ * article's graph reuse, step 13b).  Return codes as dec_prefill. */
+int32_t dec_decode(dec_ctx *c, const int32_t *tokens, const int32_t *seq_ids, int32_t n);
+
+/* Logits row i of the last call: i >= 0 is the i-th output row, -1 the
+ * last one (article step 14, llama_get_logits_ith).  Synchronizes the
+ * stream and copies the rows to host memory on first use.  Returns n_vocab
+ * floats, or NULL for an invalid index or when no call has produced
+ * logits. */
+const float *dec_get_logits(dec_ctx *c, int32_t i);
+
+/* Greedy token of output row i (same indexing as dec_get_logits): the
+ * index of the largest logit, lowest index on ties, computed on the device
+ * (article step 15, greedy sampler; on-device sampling avoids copying the
+ * logits).  Returns -1 for an invalid index. */
+int32_t dec_argmax(dec_ctx *c, int32_t i);
+
+/* Copies the greedy tokens of all n output rows of the last call into out
+ * (n = the value returned); returns -1 if cap is too small. */
+int32_t dec_argmax_all(dec_ctx *c, int32_t *out, int32_t cap);
+
+/* Largest cached position of a sequence, -1 when empty (the memory module's
+ * seq_pos_max, KV-cache appendix). */
+int32_t dec_seq_pos_max(const dec_ctx *c, int32_t seq);
+
+/* Forgets every cached position of a sequence.  Returns 0, or -1 for a bad
+ * seq. */
+int32_t dec_seq_clear(dec_ctx *c, int32_t seq);
+
+/* Counters since creation (the article's "graphs reused" count, step 13b). */
+typedef struct {
+    int64_t n_prefill_calls, n_ubatches, n_decode_calls;
+    int64_t n_graph_captures, n_graph_replays;
+} dec_stats;
+void dec_get_stats(const dec_ctx *c, dec_stats *out);
+
+void dec_ctx_free(dec_ctx *c);
+
+/* Log sink: level 0 debug, 1 info, 2 warning, 3 error.  NULL restores the
+ * default (errors to stderr). */
+void dec_set_log_callback(void (*cb)(int level, const char *msg, void *ud), void *ud);
+
+/* Library build string (target, version). */
+const char *dec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,168 @@
+"""GPU-vs-oracle parity of the whole decoder step through the C ABI.
+
+Every case runs the same seeded fp32 weights through libdecode (HIP, gfx950)
+and through the oracle, then compares: quantized block bytes bit for bit,
+greedy tokens exactly, logits within max-abs 2e-2 and 1e-2 relative to the
+row's largest |logit|.  Teacher-forced runs feed both sides the oracle's
+tokens so that logits are compared on identical histories.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import (ABS_TOL, assert_logits_close, compare_runs, gpu_greedy, logit_err,
+                      small_hp, top2_margin)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dec():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_amd
+    decode_amd.lib()
+    return decode_amd
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.load("f64")
+    return oracle
+
+
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_0, synth.F32])
+def test_stored_blocks_bit_exact(dec, orc, wtype):
+    hp = small_hp(wtype, synth.F16, n_ff=544 if wtype == synth.F32 else 512)
+    w = synth.weights_numpy(hp, 31, threads=4)
+    # blocks with ties, zeros and extreme values exercise the rounding rules
+    w["wq"][0][:4] = 0.0
+    w["wq"][0][4, :32] = np.arange(32, dtype=np.float32) - 16
+    w["wk"][1][3, :32] = 1e-8
+    gm = dec.Model(hp, w)
+    om = orc.Model(hp, w)
+    for name in ("tok_embd", "output"):
+        assert np.array_equal(gm.tensor_blocks(name), om.tensor_bytes(name)), name
+    for l in range(hp["n_layer"]):
+        for name in ("wq", "wk", "wv", "wo", "ffn_gate", "ffn_up", "ffn_down"):
+            assert np.array_equal(gm.tensor_blocks(name, l), om.tensor_bytes(name, l)), (name, l)
+
+
+def test_tiny_workload_matches_oracle(dec, orc):
+    """2 layers, d 256, fp32 weights and KV: 16-token prompt, 16 greedy steps."""
+    W = synth.WORKLOADS["tiny"]
+    hp = synth.hparams(W)
+    w = synth.weights_numpy(hp, W["seed"], threads=4)
+    prompt = synth.prompt(hp["n_vocab"], W["n_prompt"], 2001)
+    om = orc.Model(hp, w)
+    o_toks, o_rows = orc.run_greedy(om, prompt, W["n_decode"], 256)
+    gm = dec.Model(hp, w)
+    ctx = dec.Context(gm, n_ctx=256, n_ubatch=W["n_ubatch"])
+    g_toks, g_rows = gpu_greedy(ctx, prompt, W["n_decode"], teacher=o_toks)
+    compare_runs(g_toks, g_rows, o_toks, o_rows, "tiny teacher-forced")
+    ctx.clear(0)
+    f_toks, f_rows = gpu_greedy(ctx, prompt, W["n_decode"])
+    assert f_toks == o_toks
+    st = ctx.stats()
+    assert st["n_graph_captures"] == 1 and st["n_graph_replays"] == 2 * W["n_decode"] - 1
+
+
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_0])
+def test_quantized_multi_ubatch_matches_oracle(dec, orc, wtype):
+    hp = small_hp(wtype, synth.F16, n_embd=512, n_head=8, n_head_kv=2, n_ff=1024, n_vocab=2048)
+    w = synth.weights_numpy(hp, 40 + wtype, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 150, 41)
+    n_dec = 12
+    om = orc.Model(hp, w)
+    o_toks, o_rows = orc.run_greedy(om, prompt, n_dec, 512)
+    gm = dec.Model(hp, w)
+    ctx = dec.Context(gm, n_ctx=512, n_ubatch=64)      # 3 ubatches, ragged tail of 22
+    g_toks, g_rows = gpu_greedy(ctx, prompt, n_dec, teacher=o_toks)
+    compare_runs(g_toks, g_rows, o_toks, o_rows, f"wtype {wtype}")
+    ctx.clear(0)
+    f_toks, _ = gpu_greedy(ctx, prompt, n_dec)
+    assert f_toks == o_toks
+
+
+def test_output_all_rows_and_indices(dec, orc):
+    hp = small_hp(synth.Q8_0, synth.F16)
+    w = synth.weights_numpy(hp, 50, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 70, 51)
+    om = orc.Model(hp, w)
+    oc = orc.Context(om, 1, 256)
+    o_rows = [oc.eval(0, int(t)) for t in prompt]
+    gm = dec.Model(hp, w)
+    ctx = dec.Context(gm, n_ctx=256, n_ubatch=32)
+    assert ctx.prefill(prompt, 0, output_all=True) == 0
+    for i in (0, 1, 31, 32, 33, 63, 64, 69):
+        assert_logits_close(ctx.logits(i), o_rows[i], f"row {i}")
+        assert ctx.argmax(i) == int(np.argmax(ctx.logits(i)))
+    assert np.array_equal(ctx.logits(-1), ctx.logits(69))
+    assert ctx.logits(70) is None and ctx.argmax(70) == -1
+    am = ctx.argmax_all()
+    assert am.size == 70 and am[5] == ctx.argmax(5)
+
+
+def test_decode_equals_recompute_on_gpu(dec):
+    hp = small_hp(synth.Q4_0, synth.F16)
+    w = synth.weights_numpy(hp, 60, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 40, 61)
+    gm = dec.Model(hp, w)
+    ctx = dec.Context(gm, n_ctx=256, n_ubatch=64)
+    toks, rows = gpu_greedy(ctx, prompt, 10)
+    full = np.concatenate([prompt, np.array(toks[:-1], np.int32)])
+    ctx2 = dec.Context(gm, n_ctx=256, n_ubatch=64)
+    assert ctx2.prefill(full, 0) == 0
+    ma, _ = logit_err(ctx2.logits(-1), rows[-1])
+    assert ma <= ABS_TOL
+    assert ctx2.argmax(-1) == toks[-1]
+
+
+def test_batched_decode_equals_single_sequences(dec, orc):
+    hp = small_hp(synth.Q8_0, synth.F16)
+    w = synth.weights_numpy(hp, 70, threads=4)
+    gm = dec.Model(hp, w)
+    om = orc.Model(hp, w)
+    S = 5
+    prompts = [synth.prompt(hp["n_vocab"], 20 + 3 * s, 300 + s) for s in range(S)]
+    ctx = dec.Context(gm, n_ctx=256, n_ubatch=32, n_seq_max=S)
+    for s in range(S):
+        assert ctx.prefill(prompts[s], s) == 0
+    oc = orc.Context(om, S, 256)
+    for s in range(S):
+        for t in prompts[s]:
+            oc.eval(s, int(t), want_logits=False)
+    # feed every sequence the same fixed tokens for 4 steps, all sequences in one call
+    feeds = synth.prompt(hp["n_vocab"], 4 * S, 77).reshape(4, S)
+    for k in range(4):
+        assert ctx.decode(feeds[k], np.arange(S)) == 0
+        for s in range(S):
+            ol = oc.eval(s, int(feeds[k][s]))
+            assert_logits_close(ctx.logits(s), ol, f"step {k} seq {s}")
+    assert [ctx.pos_max(s) for s in range(S)] == [len(prompts[s]) + 3 for s in range(S)]
+
+
+def test_return_codes_and_rollback(dec):
+    hp = small_hp(synth.Q8_0, synth.F16)
+    w = synth.weights_numpy(hp, 80, threads=4)
+    gm = dec.Model(hp, w)
+    ctx = dec.Context(gm, n_ctx=256, n_batch=256, n_ubatch=32)
+    p = synth.prompt(hp["n_vocab"], 200, 81)
+    assert ctx.prefill(p, 0) == 0 and ctx.pos_max(0) == 199
+    assert ctx.prefill(p[:100], 0) == 1 and ctx.pos_max(0) == 199     # no room: nothing changes
+    assert ctx.prefill([hp["n_vocab"]], 0) == -1                        # token out of range
+    assert ctx.prefill(p[:5], 1) == -1                                  # seq out of range
+    assert ctx.decode([1, 2], [0, 0]) == -1                             # duplicate sequence
+    calls = []
+
+    def abort(ud):
+        calls.append(1)
+        return 1 if len(calls) >= 2 else 0
+
+    ctx2 = dec.Context(gm, n_ctx=256, n_ubatch=32, abort=abort)
+    assert ctx2.prefill(p[:100], 0) == 2
+    assert ctx2.pos_max(0) == 63            # two ubatches of 32 finished and kept
+    ctx2.clear(0)
+    assert ctx2.pos_max(0) == -1
