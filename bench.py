@@ -1,0 +1,233 @@
+"""Benchmark of the decoder hot path on one MI355X.
+
+Workload (default): 8B-shape LLaMA-style decoder with Q4_0 weights drawn
+from N(0, 0.02) and an f16 KV cache; a 4096-token random prompt prefilled
+in 8 ubatches of 512, then greedy decode at batch 1 (one token per step,
+each step = decode call + on-device argmax + 4-byte readback, the
+generation loop of the article's step 8).  A "step" is one decode token.
+
+Prints ONE JSON line: decode tokens/s (value), prefill tokens/s, the
+roofline of the dominant decode kernel (the fused gate/up mat-vec, timed
+live with HIP events captured into the decode graph on the library's
+stream) and of the dominant prefill kernel (gate/up MFMA GEMM), and the
+CPU oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA, TFLOP/s
+METRIC = "decode tokens/s + % HBM roofline (8B-shape Q4_0, bs=1); prefill tokens/s"
+
+
+def block_bytes(wtype: int) -> float:
+    return {2: 34.0, 3: 18.0}.get(wtype, 128.0) / 32.0
+
+
+def algorithmic(hp, n_prompt, steps):
+    """Bytes per decode token (weights once + KV rows read at the mean context)
+    and FLOPs of the prefill, counted as in the design doc."""
+    d, L, F, V = hp["n_embd"], hp["n_layer"], hp["n_ff"], hp["n_vocab"]
+    qd, kd = hp["n_head"] * hp["head_dim"], hp["n_head_kv"] * hp["head_dim"]
+    per_layer = d * (qd + 2 * kd) + qd * d + 3 * F * d
+    params = L * per_layer + V * d                       # output matrix; embedding: one row
+    wbytes = params * block_bytes(hp["wtype"]) + d * block_bytes(hp["wtype"])
+    kv_row = L * 2 * kd * (2 if hp["kvtype"] == 1 else 4)   # bytes per cached position
+    mean_ctx = n_prompt + (steps + 1) / 2.0
+    tok_bytes = wbytes + kv_row * mean_ctx
+    lin_flops = 2.0 * L * per_layer * n_prompt
+    attn_flops = 4.0 * hp["head_dim"] * hp["n_head"] * L * n_prompt * (n_prompt + 1) / 2.0
+    out_flops = 2.0 * V * d
+    return dict(weight_bytes=wbytes, kv_row_bytes=kv_row, mean_ctx=mean_ctx, token_bytes=tok_bytes,
+                prefill_flops=lin_flops + attn_flops + out_flops)
+
+
+def cpu_baseline(hp, weights_dev, prompt, n_prompt_tokens, n_decode_tokens):
+    """The oracle (f64 build, as it stands) on a bounded sample of the same
+    workload: n_prompt_tokens prompt tokens, then n_decode_tokens decode
+    steps; decode tokens/s over the decode steps."""
+    import numpy as np
+
+    import oracle
+    host = {}
+    for k, v in weights_dev.items():
+        host[k] = [t.cpu().numpy() for t in v] if isinstance(v, list) else v.cpu().numpy()
+    om = oracle.Model(hp, host, "f64")
+    del host
+    ctx = oracle.Context(om, 1, n_prompt_tokens + n_decode_tokens + 1)
+    for t in prompt[:n_prompt_tokens - 1]:
+        ctx.eval(0, int(t), want_logits=False)
+    lg = ctx.eval(0, int(prompt[n_prompt_tokens - 1]))
+    tok = oracle.argmax(lg)
+    t0 = time.perf_counter()
+    for _ in range(n_decode_tokens):
+        lg = ctx.eval(0, tok)
+        tok = oracle.argmax(lg)
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": n_decode_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"f64 oracle, same weights: {n_prompt_tokens}-token prompt then "
+                      f"{n_decode_tokens} greedy decode steps at context <= "
+                      f"{n_prompt_tokens + n_decode_tokens} ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=8, help="untimed decode steps (graph capture)")
+    ap.add_argument("--workload", default="8b_q4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-prompt", type=int, default=3)
+    ap.add_argument("--cpu-decode", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on exactly one GPU (the decode step of one sequence "
+              "batch on one MI355X); --gpus N>1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_amd as dec
+    import synth
+
+    W = synth.WORKLOADS[args.workload]
+    hp = synth.hparams(W)
+    n_prompt = W["n_prompt"]
+    steps, warm = args.steps, args.warmup
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    sp = stream.cuda_stream
+    dec.lib()
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        weights = synth.weights_torch(hp, W["seed"], "cuda")
+    torch.cuda.synchronize()
+    log(f"weights generated in {time.perf_counter() - t0:.1f} s")
+    t0 = time.perf_counter()
+    model = dec.Model(hp, weights, stream=sp)
+    torch.cuda.synchronize()
+    log(f"model loaded (quantized on device) in {time.perf_counter() - t0:.1f} s")
+    if args.no_cpu_baseline:
+        del weights
+        torch.cuda.empty_cache()
+
+    prompt = synth.prompt(hp["n_vocab"], n_prompt, 2000 + W["seed"] % 1000)
+    n_ctx = n_prompt + steps + warm + 8
+    ctx = dec.Context(model, n_ctx=n_ctx, n_batch=n_prompt, n_ubatch=W["n_ubatch"], stream=sp)
+    probe_layer = hp["n_layer"] // 2
+    ctx.set_probe(dec.K_FFN_GU, probe_layer)
+
+    # warm-up: prefill + decode steps (captures the decode graph)
+    assert ctx.prefill(prompt, 0) == 0
+    tok = ctx.argmax(-1)
+    for _ in range(warm):
+        assert ctx.decode([tok], [0]) == 0
+        tok = ctx.argmax(0)
+    ctx.clear(0)
+    ctx.set_probe(dec.K_FFN_GU, probe_layer)
+    torch.cuda.synchronize()
+    log("warm-up done")
+
+    # timed prefill
+    t0 = time.perf_counter()
+    assert ctx.prefill(prompt, 0) == 0
+    tok = ctx.argmax(-1)
+    prefill_s = time.perf_counter() - t0
+    pf_probe = ctx.probe()
+    ctx.set_probe(dec.K_FFN_GU, probe_layer)
+
+    # timed decode: the generation loop, one token per step
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        rc = ctx.decode([tok], [0])
+        if rc != 0:
+            raise RuntimeError(f"dec_decode returned {rc}")
+        tok = ctx.argmax(0)
+    torch.cuda.synchronize()
+    decode_s = time.perf_counter() - t0
+    dc_probe = ctx.probe()
+    st = ctx.stats()
+    log(f"prefill {n_prompt / prefill_s:.0f} tok/s, decode {steps / decode_s:.1f} tok/s")
+
+    alg = algorithmic(hp, n_prompt, steps)
+    F, d = hp["n_ff"], hp["n_embd"]
+    gu_bytes = 2 * F * d * block_bytes(hp["wtype"])
+    gu_avg_s = dc_probe[0] / 1e3 / max(dc_probe[1], 1) if dc_probe and dc_probe[1] else None
+    roofline = None
+    if gu_avg_s:
+        ach = gu_bytes / gu_avg_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "k_matvec (gate/up, Q4_0 mat-vec + RMSNorm prologue + SwiGLU epilogue)",
+                    "bytes_per_launch": gu_bytes, "avg_us": round(gu_avg_s * 1e6, 2),
+                    "launches_timed": dc_probe[1]}
+    pf_roof = None
+    if pf_probe and pf_probe[1]:
+        T = W["n_ubatch"]
+        flops = 2.0 * T * 2 * F * d
+        avg = pf_probe[0] / 1e3 / pf_probe[1]
+        ach = flops / avg / 1e12
+        pf_roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                   "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
+                   "kernel": "k_gemm_mfma (gate/up, ubatch 512)", "avg_us": round(avg * 1e6, 1)}
+    step_gbs = alg["token_bytes"] / (decode_s / steps) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host cores")
+        cpu = cpu_baseline(hp, weights, prompt, args.cpu_prompt, args.cpu_decode)
+        del weights
+
+    out = {
+        "metric": METRIC,
+        "value": round(steps / decode_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(decode_s / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "8B-shape decoder, Q4_0 weights N(0,0.02), f16 KV cache, batch 1: "
+                               f"{n_prompt}-token random prompt in ubatches of {W['n_ubatch']}, "
+                               f"then {steps} greedy decode steps",
+                   "n_layer": hp["n_layer"], "d_model": d, "heads": hp["n_head"],
+                   "kv_heads": hp["n_head_kv"], "head_dim": hp["head_dim"], "ffn": F,
+                   "vocab": hp["n_vocab"], "prefill_tokens": n_prompt, "n_ubatch": W["n_ubatch"],
+                   "mean_decode_context": alg["mean_ctx"]},
+        "precision": {"weights": "q4_0", "activations": "f16", "accumulate": "f32", "kv": "f16"},
+        "prefill_tokens_per_s": round(n_prompt / prefill_s, 1),
+        "prefill_ms": round(prefill_s * 1e3, 2),
+        "decode_step_hbm": {"bytes_per_token": int(alg["token_bytes"]), "achieved_GBs": round(step_gbs, 1),
+                            "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "prefill_mfma": {"flops": alg["prefill_flops"],
+                         "achieved_TFLOPs": round(alg["prefill_flops"] / prefill_s / 1e12, 1),
+                         "frac": round(alg["prefill_flops"] / prefill_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+        "roofline": roofline,
+        "prefill_roofline": pf_roof,
+        "graph_replays": st["n_graph_replays"],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libdecode.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "decode.h")
 
 F32, F16, Q8_0, Q4_0 = 0, 1, 2, 3
+K_QKV, K_ATTN, K_WO, K_FFN_GU, K_FFN_DOWN, K_OUTPUT = 0, 1, 2, 3, 4, 5
 TENSOR_IDS = {"tok_embd": 0, "output": 1, "wq": 2, "wk": 3, "wv": 4, "wo": 5,
               "ffn_gate": 6, "ffn_up": 7, "ffn_down": 8}
 
@@ -101,6 +102,9 @@ def lib() -> C.CDLL:
         "dec_get_stats": (None, [vp, vp]),
         "dec_ctx_free": (None, [vp]),
         "dec_set_log_callback": (None, [LOG_FN, vp]),
+        "dec_set_probe": (i32, [vp, i32, i32]),
+        "dec_get_probe": (i32, [vp, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
+        "dec_set_use_graphs": (i32, [vp, i32]),
         "dec_version": (C.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -239,6 +243,18 @@ class Context:
         s = Stats()
         self.L.dec_get_stats(self.ptr, C.byref(s))
         return {k: int(getattr(s, k)) for k, _ in Stats._fields_}
+
+    def set_probe(self, role: int, layer: int = 0) -> int:
+        return int(self.L.dec_set_probe(self.ptr, role, layer))
+
+    def probe(self):
+        ms, n = C.c_double(), C.c_int64()
+        if self.L.dec_get_probe(self.ptr, C.byref(ms), C.byref(n)) != 0:
+            return None
+        return float(ms.value), int(n.value)
+
+    def use_graphs(self, on: bool) -> bool:
+        return bool(self.L.dec_set_use_graphs(self.ptr, int(on)))
 
     def close(self):
         if getattr(self, "ptr", None):

@@ -101,8 +101,15 @@ struct dec_model {
     std::vector<Layer> layers;
     Mem mem;
     hipStream_t stream = nullptr;
-    int n_ctx_refs = 0;
+    int n_ctx_refs = 0;        // live contexts; the model's memory outlives them
+    bool free_requested = false;
 };
+
+static void model_release(dec_model *m) {
+    (void)hipStreamSynchronize(m->stream);
+    m->mem.release();
+    delete m;
+}
 
 static bool alloc_qmat(Mem &mem, QMat &m, int wtype, int N, int K) {
     m.wtype = wtype;
@@ -260,10 +267,13 @@ extern "C" dec_model *dec_model_load(const dec_hparams *hp, const dec_weights *w
 
 extern "C" void dec_model_free(dec_model *m) {
     if (!m) return;
-    if (m->n_ctx_refs) LOGW("dec_model_free: %d contexts still alive", m->n_ctx_refs);
-    (void)hipStreamSynchronize(m->stream);
-    m->mem.release();
-    delete m;
+    if (m->n_ctx_refs) {
+        // contexts still read the weights: release with the last of them
+        LOGW("dec_model_free: %d contexts still alive, freeing with the last one", m->n_ctx_refs);
+        m->free_requested = true;
+        return;
+    }
+    model_release(m);
 }
 
 // Export of one stored matrix in its file form (GGUF-style blocks).
@@ -346,8 +356,75 @@ struct dec_ctx {
     std::vector<int32_t> host_amax;
     bool amax_fetched = false;
     std::map<int, hipGraphExec_t> graphs;
+    bool use_graphs = true;
+    bool registered = false;   // counted in m->n_ctx_refs
     dec_stats st{};
+    // timing probe: a pool of event pairs for launches made directly on the
+    // stream, and one pair that lives inside the captured decode graph
+    static constexpr int NPROBE = 64;
+    int pr_role = -1, pr_layer = -1;
+    hipEvent_t pr_e0[NPROBE] = {}, pr_e1[NPROBE] = {};
+    int pr_used = 0;
+    double pr_ms = 0.0;
+    int64_t pr_n = 0;
+    // A probed decode step runs as graph(before the probed kernel), the probed
+    // kernel launched directly between two events, graph(after): HIP cannot
+    // time events that were captured into a graph.  seg_req selects which
+    // launches run_tokens emits; seg_cur tracks where the sequence is.
+    int seg_req = 0, seg_cur = 1;
+    std::map<int, hipGraphExec_t> graphs_post;
 };
+
+enum { SEG_ALL = 0, SEG_PRE = 1, SEG_MID = 2, SEG_POST = 3 };
+static bool emit(const dec_ctx *c) { return c->seg_req == SEG_ALL || c->seg_req == c->seg_cur; }
+
+static void drop_graphs(dec_ctx *c) {
+    for (auto &g : c->graphs) (void)hipGraphExecDestroy(g.second);
+    for (auto &g : c->graphs_post) (void)hipGraphExecDestroy(g.second);
+    c->graphs.clear();
+    c->graphs_post.clear();
+}
+
+static void probe_add(dec_ctx *c, hipEvent_t a, hipEvent_t b) {
+    if (hipEventSynchronize(b) != hipSuccess) {
+        (void)hipGetLastError();
+        return;
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, a, b) == hipSuccess) {
+        c->pr_ms += ms;
+        c->pr_n++;
+    } else {
+        (void)hipGetLastError();
+    }
+}
+
+// Adds every recorded interval to the totals (waits for their end events).
+static void probe_collect(dec_ctx *c) {
+    for (int i = 0; i < c->pr_used; i++) probe_add(c, c->pr_e0[i], c->pr_e1[i]);
+    c->pr_used = 0;
+}
+
+static bool probe_hit(const dec_ctx *c, int role, int layer) {
+    return c->pr_role == role && (role == DEC_K_OUTPUT || c->pr_layer == layer);
+}
+
+static void probe_begin(dec_ctx *c, int role, int layer) {
+    if (!probe_hit(c, role, layer)) return;
+    c->seg_cur = SEG_MID;
+    if (!emit(c)) return;
+    if (c->pr_used == dec_ctx::NPROBE) probe_collect(c);
+    (void)hipEventRecord(c->pr_e0[c->pr_used], c->s);
+}
+
+static void probe_end(dec_ctx *c, int role, int layer) {
+    if (!probe_hit(c, role, layer)) return;
+    if (emit(c)) {
+        (void)hipEventRecord(c->pr_e1[c->pr_used], c->s);
+        c->pr_used++;
+    }
+    c->seg_cur = SEG_POST;
+}
 
 extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
     if (!m || !pp) return nullptr;
@@ -422,6 +499,11 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
     }
     if (ok) HIP_OK(hipHostMalloc((void **)&c->host_step, (size_t)c->step_cap * 3 * 4, 0), ok = false);
     if (ok) HIP_OK(hipEventCreateWithFlags(&c->staged, hipEventDisableTiming), ok = false);
+    for (int i = 0; ok && i < dec_ctx::NPROBE; i++) {
+        HIP_OK(hipEventCreate(&c->pr_e0[i]), ok = false);
+        if (ok) HIP_OK(hipEventCreate(&c->pr_e1[i]), ok = false);
+    }
+
     if (ok) {
         launch_rope_table(c->rope_cs, (int)n_ctx, hd, h.rope_base, c->s);
         HIP_OK(hipGetLastError(), ok = false);
@@ -433,6 +515,7 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
         return nullptr;
     }
     m->n_ctx_refs++;
+    c->registered = true;
     LOGI("context: n_ctx=%u n_batch=%u n_ubatch=%u n_seq=%u", n_ctx, n_batch, n_ubatch, n_seq);
     return c;
 }
@@ -440,13 +523,19 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
 extern "C" void dec_ctx_free(dec_ctx *c) {
     if (!c) return;
     if (c->s) (void)hipStreamSynchronize(c->s);
-    for (auto &g : c->graphs) (void)hipGraphExecDestroy(g.second);
+    drop_graphs(c);
     if (c->staged) (void)hipEventDestroy(c->staged);
+    for (int i = 0; i < dec_ctx::NPROBE; i++) {
+        if (c->pr_e0[i]) (void)hipEventDestroy(c->pr_e0[i]);
+        if (c->pr_e1[i]) (void)hipEventDestroy(c->pr_e1[i]);
+    }
+
     if (c->host_step) (void)hipHostFree(c->host_step);
     c->mem.release();
     if (c->own_stream) (void)hipStreamDestroy(c->s);
-    if (c->m && c->kv.size()) c->m->n_ctx_refs--;
+    dec_model *m = c->registered ? c->m : nullptr;
     delete c;
+    if (m && --m->n_ctx_refs == 0 && m->free_requested) model_release(m);
 }
 
 // Waits until the pinned staging buffer may be rewritten.
@@ -474,6 +563,17 @@ static bool use_matvec(const dec_ctx *c, int T) {
     return c->m->hp.wtype != DEC_F32 && T <= 2;
 }
 
+// One unit of work (kernel role `role` of layer `layer`, or role -1 for
+// units the probe never selects): emitted only when its segment is requested.
+template <typename F>
+static bool stage(dec_ctx *c, int role, int layer, F &&f) {
+    probe_begin(c, role, layer);
+    bool ok = true;
+    if (emit(c)) ok = f();
+    probe_end(c, role, layer);
+    return ok;
+}
+
 // Enqueues the layers for T tokens whose ids / positions / sequences live at
 // dev_step + off (+cap, +2cap).  Output rows: `n_rows` rows starting at
 // token row `row0` produce logits at logits row `out_row0`.
@@ -489,8 +589,12 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
     hipStream_t s = c->s;
     const bool mv = use_matvec(c, T);
     bool ok = true;
+    c->seg_cur = SEG_PRE;
 
-    launch_embed(m->tok, tok, T, c->x, d, s);
+    ok = stage(c, -1, -1, [&] {
+        launch_embed(m->tok, tok, T, c->x, d, s);
+        return true;
+    });
     for (int l = 0; ok && l < h.n_layer; l++) {
         const Layer &L = m->layers[l];
         EpiArgs eq;
@@ -501,17 +605,18 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         eq.kv = c->kv[l];
         eq.tok = ti;
         eq.rope_cs = c->rope_cs;
-        if (mv) {
-            InArgs in;
-            in.x32 = c->x;
-            in.norm_g = L.attn_norm;
-            in.eps = h.rms_eps;
-            in.ldx = d;
-            ok = ok && launch_matvec(L.wqkv, in, eq, T, s);
-        } else {
+        ok = ok && stage(c, DEC_K_QKV, l, [&] {
+            if (mv) {
+                InArgs in;
+                in.x32 = c->x;
+                in.norm_g = L.attn_norm;
+                in.eps = h.rms_eps;
+                in.ldx = d;
+                return launch_matvec(L.wqkv, in, eq, T, s);
+            }
             launch_rmsnorm(c->x, d, L.attn_norm, d, h.rms_eps, nullptr, T, c->xn, d, s);
-            ok = ok && launch_gemm(L.wqkv, c->xn, d, eq, T, s);
-        }
+            return launch_gemm(L.wqkv, c->xn, d, eq, T, s);
+        });
         AttnArgs at;
         at.q = c->q;
         at.kv = c->kv[l];
@@ -522,61 +627,69 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         at.max_chunks = c->max_chunks;
         at.chunk = c->chunk;
         at.o = c->o;
-        ok = ok && launch_attention(at, T, s);
+        ok = ok && stage(c, DEC_K_ATTN, l, [&] { return launch_attention(at, T, s); });
 
         EpiArgs er;
         er.epi = EPI_RESID;
         er.y = c->x;
         er.ldy = d;
-        if (mv) {
-            InArgs in;
-            in.x16 = c->o;
-            in.ldx = qd;
-            ok = ok && launch_matvec(L.wo, in, er, T, s);
-        } else {
-            ok = ok && launch_gemm(L.wo, c->o, qd, er, T, s);
-        }
+        ok = ok && stage(c, DEC_K_WO, l, [&] {
+            if (mv) {
+                InArgs in;
+                in.x16 = c->o;
+                in.ldx = qd;
+                return launch_matvec(L.wo, in, er, T, s);
+            }
+            return launch_gemm(L.wo, c->o, qd, er, T, s);
+        });
         EpiArgs eg;
         eg.epi = EPI_SWIGLU;
         eg.h = c->h;
         eg.ldh = Fp;
-        if (mv) {
-            InArgs in;
-            in.x32 = c->x;
-            in.norm_g = L.ffn_norm;
-            in.eps = h.rms_eps;
-            in.ldx = d;
-            ok = ok && launch_matvec(L.wgu, in, eg, T, s);
-        } else {
+        ok = ok && stage(c, DEC_K_FFN_GU, l, [&] {
+            if (mv) {
+                InArgs in;
+                in.x32 = c->x;
+                in.norm_g = L.ffn_norm;
+                in.eps = h.rms_eps;
+                in.ldx = d;
+                return launch_matvec(L.wgu, in, eg, T, s);
+            }
             launch_rmsnorm(c->x, d, L.ffn_norm, d, h.rms_eps, nullptr, T, c->xn, d, s);
-            ok = ok && launch_gemm(L.wgu, c->xn, d, eg, T, s);
-        }
-        if (mv) {
-            InArgs in;
-            in.x16 = c->h;
-            in.ldx = Fp;
-            ok = ok && launch_matvec(L.wdown, in, er, T, s);
-        } else {
-            ok = ok && launch_gemm(L.wdown, c->h, Fp, er, T, s);
-        }
+            return launch_gemm(L.wgu, c->xn, d, eg, T, s);
+        });
+        ok = ok && stage(c, DEC_K_FFN_DOWN, l, [&] {
+            if (mv) {
+                InArgs in;
+                in.x16 = c->h;
+                in.ldx = Fp;
+                return launch_matvec(L.wdown, in, er, T, s);
+            }
+            return launch_gemm(L.wdown, c->h, Fp, er, T, s);
+        });
     }
     if (ok && n_rows > 0) {
         EpiArgs eo;
         eo.epi = EPI_STORE;
         eo.y = c->logits + (size_t)out_row0 * V;
         eo.ldy = V;
-        if (use_matvec(c, n_rows)) {
-            InArgs in;
-            in.x32 = c->x + (size_t)row0 * d;
-            in.norm_g = m->out_norm;
-            in.eps = h.rms_eps;
-            in.ldx = d;
-            ok = launch_matvec(m->out, in, eo, n_rows, s);
-        } else {
-            launch_rmsnorm(c->x + (size_t)row0 * d, d, m->out_norm, d, h.rms_eps, nullptr, n_rows, c->xn, d, s);
-            ok = launch_gemm(m->out, c->xn, d, eo, n_rows, s);
-        }
-        launch_argmax(c->logits + (size_t)out_row0 * V, V, n_rows, c->amax + out_row0, s);
+        ok = stage(c, DEC_K_OUTPUT, -1, [&] {
+            if (use_matvec(c, n_rows)) {
+                InArgs in;
+                in.x32 = c->x + (size_t)row0 * d;
+                in.norm_g = m->out_norm;
+                in.eps = h.rms_eps;
+                in.ldx = d;
+                return launch_matvec(m->out, in, eo, n_rows, s);
+            }
+            launch_rmsnorm(c->x + (size_t)row0 * d, d, m->out_norm, d, h.rms_eps, nullptr, n_rows, c->xn,
+                           d, s);
+            return launch_gemm(m->out, c->xn, d, eo, n_rows, s);
+        });
+        ok = ok && stage(c, -1, -1, [&] {
+            launch_argmax(c->logits + (size_t)out_row0 * V, V, n_rows, c->amax + out_row0, s);
+            return true;
+        });
     }
     if (!ok) LOGE("kernel launch rejected a shape");
     return ok && hipGetLastError() == hipSuccess;
@@ -634,6 +747,29 @@ extern "C" int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int
     return 0;
 }
 
+// Captures the decode step for n tokens (segment `seg` of it) as a graph.
+static hipGraphExec_t capture_step(dec_ctx *c, int n, int seg) {
+    hipGraph_t g = nullptr;
+    HIP_OK(hipStreamBeginCapture(c->s, hipStreamCaptureModeThreadLocal), return nullptr);
+    c->seg_req = seg;
+    const bool ok = run_tokens(c, 0, n, 0, n, 0);
+    c->seg_req = SEG_ALL;
+    const hipError_t e = hipStreamEndCapture(c->s, &g);
+    if (!ok || e != hipSuccess || !g) {
+        LOGE("dec_decode: graph capture failed (%s)", hipGetErrorString(e));
+        if (g) (void)hipGraphDestroy(g);
+        return nullptr;
+    }
+    hipGraphExec_t ex = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (ei != hipSuccess) {
+        LOGE("dec_decode: graph instantiate failed (%s)", hipGetErrorString(ei));
+        return nullptr;
+    }
+    return ex;
+}
+
 extern "C" int32_t dec_decode(dec_ctx *c, const int32_t *tokens, const int32_t *seq_ids, int32_t n) {
     if (!c || !tokens || !seq_ids || n <= 0 || n > c->n_seq || n > c->Tmax) return -1;
     const int V = c->m->hp.n_vocab;
@@ -652,30 +788,37 @@ extern "C" int32_t dec_decode(dec_ctx *c, const int32_t *tokens, const int32_t *
         c->host_step[2 * cap + i] = seq_ids[i];
     }
     if (!stage_step(c, n)) return -3;
-    auto it = c->graphs.find(n);
-    if (it == c->graphs.end()) {
-        hipGraph_t g = nullptr;
-        HIP_OK(hipStreamBeginCapture(c->s, hipStreamCaptureModeThreadLocal), return -3);
-        const bool ok = run_tokens(c, 0, n, 0, n, 0);
-        const hipError_t e = hipStreamEndCapture(c->s, &g);
-        if (!ok || e != hipSuccess || !g) {
-            LOGE("dec_decode: graph capture failed (%s)", hipGetErrorString(e));
-            if (g) (void)hipGraphDestroy(g);
-            return -3;
-        }
-        hipGraphExec_t ex = nullptr;
-        const hipError_t ei = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
-        (void)hipGraphDestroy(g);
-        if (ei != hipSuccess) {
-            LOGE("dec_decode: graph instantiate failed (%s)", hipGetErrorString(ei));
-            return -3;
-        }
-        it = c->graphs.emplace(n, ex).first;
-        c->st.n_graph_captures++;
+    if (!c->use_graphs) {
+        c->seg_req = SEG_ALL;
+        if (!run_tokens(c, 0, n, 0, n, 0)) return -3;
     } else {
-        c->st.n_graph_replays++;
+        const bool split = c->pr_role >= 0;
+        auto it = c->graphs.find(n);
+        if (it == c->graphs.end()) {
+            hipGraphExec_t pre = capture_step(c, n, split ? SEG_PRE : SEG_ALL);
+            if (!pre) return -3;
+            it = c->graphs.emplace(n, pre).first;
+            if (split) {
+                hipGraphExec_t post = capture_step(c, n, SEG_POST);
+                if (!post) {
+                    drop_graphs(c);
+                    return -3;
+                }
+                c->graphs_post[n] = post;
+            }
+            c->st.n_graph_captures++;
+        } else {
+            c->st.n_graph_replays++;
+        }
+        HIP_OK(hipGraphLaunch(it->second, c->s), return -3);
+        if (split) {
+            c->seg_req = SEG_MID;                      // the probed kernel, between its events
+            const bool ok = run_tokens(c, 0, n, 0, n, 0);
+            c->seg_req = SEG_ALL;
+            if (!ok) return -3;
+            HIP_OK(hipGraphLaunch(c->graphs_post[n], c->s), return -3);
+        }
     }
-    HIP_OK(hipGraphLaunch(it->second, c->s), return -3);
     for (int i = 0; i < n; i++) c->pos_max[seq_ids[i]]++;
     c->st.n_decode_calls++;
     reset_outputs(c, n);
@@ -743,6 +886,37 @@ extern "C" int32_t dec_seq_clear(dec_ctx *c, int32_t seq) {
 extern "C" void dec_get_stats(const dec_ctx *c, dec_stats *out) {
     if (!c || !out) return;
     *out = c->st;
+}
+
+extern "C" int32_t dec_set_probe(dec_ctx *c, int32_t role, int32_t layer) {
+    if (!c || role > DEC_K_OUTPUT) return -1;
+    if (role >= 0 && role != DEC_K_OUTPUT && (layer < 0 || layer >= c->m->hp.n_layer)) return -1;
+    (void)hipStreamSynchronize(c->s);
+    c->pr_used = 0;
+    c->pr_ms = 0.0;
+    c->pr_n = 0;
+    const int r = role < 0 ? -1 : role;
+    if (r != c->pr_role || (r >= 0 && r != DEC_K_OUTPUT && layer != c->pr_layer)) {
+        c->pr_role = r;
+        c->pr_layer = layer;
+        drop_graphs(c);   // captured graphs hold (or lack) the probe's event nodes
+    }
+    return 0;
+}
+
+extern "C" int32_t dec_get_probe(dec_ctx *c, double *total_ms, int64_t *count) {
+    if (!c || c->pr_role < 0) return -1;
+    probe_collect(c);
+    if (total_ms) *total_ms = c->pr_ms;
+    if (count) *count = c->pr_n;
+    return 0;
+}
+
+extern "C" int32_t dec_set_use_graphs(dec_ctx *c, int32_t on) {
+    if (!c) return -1;
+    const int32_t prev = c->use_graphs ? 1 : 0;
+    c->use_graphs = on != 0;
+    return prev;
 }
 
 extern "C" void dec_set_log_callback(void (*cb)(int, const char *, void *), void *ud) {

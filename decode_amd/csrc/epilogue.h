@@ -32,10 +32,11 @@ DEV void store_kv_pair(void *base, int kvtype, size_t idx, float a, float b) {
     }
 }
 
-// Applies the epilogue to the pair (r0, r1) = values (a, b) of token t.
+// Applies epilogue EPI to the pair (r0, r1) = values (a, b) of token t.
 // p is the pair index (the feature index for SWIGLU).
+template <int EPI>
 DEV void epi_pair(const EpiArgs &e, int t, int p, int r0, int r1, float a, float b) {
-    switch (e.epi) {
+    switch (EPI) {
     case EPI_STORE: {
         float *y = e.y + (size_t)t * e.ldy;
         y[r0] = a;

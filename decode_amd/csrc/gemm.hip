@@ -56,7 +56,7 @@ DEV void deq16(const QMat &W, int row, int blk, int hb, uint4 raw, uint16_t dbit
     }
 }
 
-template <int WT, int BM>
+template <int WT, int BM, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_mfma(QMat W, const uint16_t *X, int ldx,
                                                    EpiArgs ep, int M, int pair_mode) {
     constexpr int MT = BM / 64;   // 32x32 m-tiles per wavefront
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(QMat W, const uint16_t *X, in
             for (int r = 0; r < 16; r++) {
                 const int i = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 const int r0 = ((g << 6) + i);
-                epi_pair(ep, m, (g << 5) + i, r0, r0 + 32, acc[0][b][r], acc[1][b][r]);
+                epi_pair<EPI>(ep, m, (g << 5) + i, r0, r0 + 32, acc[0][b][r], acc[1][b][r]);
             }
         } else {
 #pragma unroll
@@ -163,13 +163,14 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(QMat W, const uint16_t *X, in
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     const int n = n0 + wn + 32 * a + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                    epi_pair(ep, m, n >> 1, n, n + 1, acc[a][b][r], acc[a][b][r + 1]);
+                    epi_pair<EPI>(ep, m, n >> 1, n, n + 1, acc[a][b][r], acc[a][b][r + 1]);
                 }
         }
     }
 }
 
 // fp32 weights (any K), f16 activations; one thread per (row pair, token).
+template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_f32(QMat W, const uint16_t *X, int ldx, EpiArgs ep,
                                                   int M, int pair_mode) {
     const int p = blockIdx.x * 256 + threadIdx.x;
@@ -186,19 +187,37 @@ __global__ __launch_bounds__(256) void k_gemm_f32(QMat W, const uint16_t *X, int
         a += w0[k] * xv;
         b += w1[k] * xv;
     }
-    epi_pair(ep, m, p, r0, r1, a, b);
+    epi_pair<EPI>(ep, m, p, r0, r1, a, b);
+}
+
+template <int WT, int EPI>
+void launch_mfma_epi(const QMat &W, const uint16_t *X, int ldx, const EpiArgs &ep, int M,
+                     int pair_mode, hipStream_t s) {
+    if (M > 64) {
+        hipLaunchKernelGGL((k_gemm_mfma<WT, 128, EPI>), dim3(W.N / BN, (M + 127) / 128), dim3(256), 0,
+                           s, W, X, ldx, ep, M, pair_mode);
+    } else {
+        hipLaunchKernelGGL((k_gemm_mfma<WT, 64, EPI>), dim3(W.N / BN, (M + 63) / 64), dim3(256), 0, s,
+                           W, X, ldx, ep, M, pair_mode);
+    }
 }
 
 template <int WT>
 void launch_mfma(const QMat &W, const uint16_t *X, int ldx, const EpiArgs &ep, int M,
                  int pair_mode, hipStream_t s) {
-    if (M > 64) {
-        hipLaunchKernelGGL((k_gemm_mfma<WT, 128>), dim3(W.N / BN, (M + 127) / 128), dim3(256), 0, s,
-                           W, X, ldx, ep, M, pair_mode);
-    } else {
-        hipLaunchKernelGGL((k_gemm_mfma<WT, 64>), dim3(W.N / BN, (M + 63) / 64), dim3(256), 0, s,
-                           W, X, ldx, ep, M, pair_mode);
+    switch (ep.epi) {
+    case EPI_STORE: launch_mfma_epi<WT, EPI_STORE>(W, X, ldx, ep, M, pair_mode, s); break;
+    case EPI_RESID: launch_mfma_epi<WT, EPI_RESID>(W, X, ldx, ep, M, pair_mode, s); break;
+    case EPI_QKV: launch_mfma_epi<WT, EPI_QKV>(W, X, ldx, ep, M, pair_mode, s); break;
+    case EPI_SWIGLU: launch_mfma_epi<WT, EPI_SWIGLU>(W, X, ldx, ep, M, pair_mode, s); break;
     }
+}
+
+template <int EPI>
+void launch_f32_epi(const QMat &W, const uint16_t *X, int ldx, const EpiArgs &ep, int M,
+                    int pair_mode, hipStream_t s) {
+    hipLaunchKernelGGL(k_gemm_f32<EPI>, dim3((W.N / 2 + 255) / 256, M), dim3(256), 0, s, W, X, ldx,
+                       ep, M, pair_mode);
 }
 
 }  // namespace
@@ -216,7 +235,12 @@ bool launch_gemm(const QMat &W, const uint16_t *X, int ldx, const EpiArgs &ep, i
         return true;
     }
     if (W.wtype != T_F32) return false;
-    hipLaunchKernelGGL(k_gemm_f32, dim3((W.N / 2 + 255) / 256, M), dim3(256), 0, s, W, X, ldx, ep, M,
-                       pair_mode);
+    switch (ep.epi) {
+    case EPI_STORE: launch_f32_epi<EPI_STORE>(W, X, ldx, ep, M, pair_mode, s); break;
+    case EPI_RESID: launch_f32_epi<EPI_RESID>(W, X, ldx, ep, M, pair_mode, s); break;
+    case EPI_QKV: launch_f32_epi<EPI_QKV>(W, X, ldx, ep, M, pair_mode, s); break;
+    case EPI_SWIGLU: launch_f32_epi<EPI_SWIGLU>(W, X, ldx, ep, M, pair_mode, s); break;
+    default: return false;
+    }
     return true;
 }

@@ -78,7 +78,7 @@ DEV float blockdot_q8(const uint4 q0, const uint4 q1, const h2 *xp) {
     return acc;
 }
 
-template <int WT, int KB, int PU>
+template <int WT, int KB, int PU, int EPI>
 __global__ __launch_bounds__(256) void k_matvec(QMat W, InArgs in, EpiArgs ep, int pair_mode,
                                                 int pairs_per_wave) {
     __shared__ float red[4];
@@ -214,14 +214,14 @@ __global__ __launch_bounds__(256) void k_matvec(QMat W, InArgs in, EpiArgs ep, i
 #pragma unroll
         for (int u = 0; u < PU; u++) {
             if (lane == u && p0 + u < pend)
-                epi_pair(ep, t, p0 + u, rows[2 * u], rows[2 * u + 1], acc[2 * u], acc[2 * u + 1]);
+                epi_pair<EPI>(ep, t, p0 + u, rows[2 * u], rows[2 * u + 1], acc[2 * u], acc[2 * u + 1]);
         }
     }
 }
 
-template <int WT, int KB>
-bool launch_kb(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
-               hipStream_t s) {
+template <int WT, int KB, int EPI>
+bool launch_epi(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
+                hipStream_t s) {
     constexpr int PU = KB >= 5 ? 1 : 2;
     const int npairs = W.N / 2;
     // aim for about 8 wavefronts per CU on 256 CUs
@@ -230,9 +230,21 @@ bool launch_kb(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pa
     ppw = ((ppw + PU - 1) / PU) * PU;
     const int waves = (npairs + ppw - 1) / ppw;
     const int blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((k_matvec<WT, KB, PU>), dim3(blocks, T), dim3(256), 0, s, W, in, ep,
+    hipLaunchKernelGGL((k_matvec<WT, KB, PU, EPI>), dim3(blocks, T), dim3(256), 0, s, W, in, ep,
                        pair_mode, ppw);
     return true;
+}
+
+template <int WT, int KB>
+bool launch_kb(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
+               hipStream_t s) {
+    switch (ep.epi) {
+    case EPI_STORE: return launch_epi<WT, KB, EPI_STORE>(W, in, ep, T, pair_mode, s);
+    case EPI_RESID: return launch_epi<WT, KB, EPI_RESID>(W, in, ep, T, pair_mode, s);
+    case EPI_QKV: return launch_epi<WT, KB, EPI_QKV>(W, in, ep, T, pair_mode, s);
+    case EPI_SWIGLU: return launch_epi<WT, KB, EPI_SWIGLU>(W, in, ep, T, pair_mode, s);
+    default: return false;
+    }
 }
 
 template <int WT>

@@ -16,7 +16,8 @@
  *    ownership.  Pointers returned stay valid until the next prefill /
  *    decode / free on the same context.
  *  - All device work runs on one HIP stream: the one given at creation
- *    (hip_stream, a hipStream_t), or the null stream when that is NULL.
+ *    (hip_stream, a hipStream_t); a context created with NULL makes and owns
+ *    a non-blocking stream of its own (decode graphs are captured on it).
  *  - Calls on one context must not overlap (no internal locking).
  *  - Errors are reported through return values (documented per call) and
  *    a message to the log callback; nothing aborts the process.
@@ -100,7 +101,8 @@ enum { DEC_T_TOK_EMBD = 0, DEC_T_OUTPUT = 1, DEC_T_WQ = 2, DEC_T_WK = 3, DEC_T_W
 int64_t dec_model_tensor_blocks(const dec_model *m, int32_t tensor_id, int32_t layer,
                                 void *dst, size_t cap);
 
-/* Frees the model.  Contexts created from it must be freed first. */
+/* Frees the model.  When contexts created from it are still alive, the
+ * weights are released together with the last of them. */
 void dec_model_free(dec_model *m);
 
 /* Context parameters (article step 7).  n_ctx: positions per sequence,
@@ -179,6 +181,29 @@ typedef struct {
     int64_t n_graph_captures, n_graph_replays;
 } dec_stats;
 void dec_get_stats(const dec_ctx *c, dec_stats *out);
+
+/* Kernel roles of one layer (and the final output projection) for the
+ * timing probe. */
+enum { DEC_K_QKV = 0, DEC_K_ATTN = 1, DEC_K_WO = 2, DEC_K_FFN_GU = 3, DEC_K_FFN_DOWN = 4,
+       DEC_K_OUTPUT = 5 };
+
+/* Timing probe (the article's per-node evaluation callback, step 13b, in
+ * measuring form): HIP timing events are recorded on the context's stream
+ * right before and after the launch(es) of kernel `role` in layer `layer`
+ * (layer ignored for DEC_K_OUTPUT), in prefill ubatches and inside captured
+ * decode steps.  role < 0 disables.  Setting the probe resets the totals;
+ * choosing a different role or layer also drops captured decode graphs.
+ * Returns 0, or -1 on bad arguments. */
+int32_t dec_set_probe(dec_ctx *c, int32_t role, int32_t layer);
+
+/* Probe totals since dec_set_probe: summed milliseconds between the two
+ * events and the number of probed launches.  Synchronizes the stream.
+ * Returns 0, or -1 when no probe is set. */
+int32_t dec_get_probe(dec_ctx *c, double *total_ms, int64_t *count);
+
+/* Decode steps are captured as HIP graphs and replayed (on, the default) or
+ * launched kernel by kernel (off).  Returns the previous setting. */
+int32_t dec_set_use_graphs(dec_ctx *c, int32_t on);
 
 void dec_ctx_free(dec_ctx *c);
 

@@ -166,3 +166,24 @@ def test_return_codes_and_rollback(dec):
     assert ctx2.pos_max(0) == 63            # two ubatches of 32 finished and kept
     ctx2.clear(0)
     assert ctx2.pos_max(0) == -1
+
+
+def test_eager_decode_equals_graph_decode_and_probe_counts(dec):
+    hp = small_hp(synth.Q4_0, synth.F16)
+    w = synth.weights_numpy(hp, 90, threads=4)
+    gm = dec.Model(hp, w)
+    prompt = synth.prompt(hp["n_vocab"], 33, 91)
+    a = dec.Context(gm, n_ctx=256, n_ubatch=16)
+    b = dec.Context(gm, n_ctx=256, n_ubatch=16)
+    assert b.use_graphs(False) is True
+    assert a.set_probe(dec.K_FFN_GU, 1) == 0 and b.set_probe(dec.K_ATTN, 0) == 0
+    ta, ra = gpu_greedy(a, prompt, 6)
+    tb, rb = gpu_greedy(b, prompt, 6)
+    assert ta == tb
+    for x, y in zip(ra, rb):
+        assert np.array_equal(x, y)        # same kernels, same order: bitwise equal
+    ms, n = a.probe()
+    assert n == 3 + 6 and ms > 0           # 3 prefill ubatches + 6 decode steps
+    ms, n = b.probe()
+    assert n == 3 + 6 and ms > 0
+    assert a.stats()["n_graph_captures"] == 1 and b.stats()["n_graph_captures"] == 0
