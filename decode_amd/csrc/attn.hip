@@ -7,18 +7,20 @@
 // Split-K ("flash-decoding" within one GPU): the cached positions are cut
 // into chunks of CH rows.  One 256-thread block handles (chunk, KV head,
 // token) for all query heads of the group that share the KV head, so each
-// K/V row is read from HBM once per token and group.  Per block:
+// K/V row is read from HBM once per token and group.  Every load a block
+// needs (its slice of q, its K rows, its V elements) is issued at entry;
+// then
 //   1. scores s[h][j] = q_h . K_j / sqrt(hd): HD/8 threads per key row, each
-//      reading 16 contiguous bytes, reduced with lane shuffles;
-//   2. per head: m = max_j s, e_j = exp(s_j - m), l = sum_j e_j (one
-//      wavefront per head, wavefront max/sum);
+//      holding 16 contiguous bytes of K, summed with DPP lane exchanges;
+//   2. per head: m = max_j s, e_j = exp(s_j - m), l = sum_j e_j;
 //   3. acc[h][d] = sum_j e_j V_j[d]: HD/2 threads per row, 2 elements each.
-// The block writes (m, l, acc) for its chunk; a second kernel merges the
-// chunks of a (token, head) in chunk order:
+// The block writes (m, l, acc) for its chunk.  A second kernel merges the
+// chunks of each (token, head) in chunk order,
 //   M = max_c m_c, L = sum_c l_c e^(m_c - M), o = sum_c acc_c e^(m_c - M) / L,
-// and writes o in f16 for the output projection.  The grid covers the
-// context's largest chunk count; blocks past a token's last chunk exit, so
-// one captured launch serves every decode step.
+// with the chunk weights computed once per block and the HD-wide sums split
+// over chunk groups, and writes o in f16 for the output projection.  The
+// grid covers the context's largest chunk count; blocks past a token's last
+// chunk exit at once, so one captured launch serves every decode step.
 #include "common.h"
 #include "kernels.h"
 
@@ -55,18 +57,36 @@ struct KVRow<T_F32> {
     DEV float2 load2(const float *p) { return *(const float2 *)p; }
 };
 
-template <int HD, int KVT>
-__global__ __launch_bounds__(256) void k_attn_part(AttnArgs a, int G) {
+// Sum over groups of N consecutive lanes (N = 8, 16 or 32); every lane of a
+// group gets the group's total.
+template <int N>
+DEV float group_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    if (N == 8) {
+        v += dpp_f<0x141>(v);   // row_half_mirror
+    } else {
+        v += dpp_f<0x124>(v);
+        v += dpp_f<0x128>(v);
+        if (N == 32) v += __shfl_xor(v, 16, 64);
+    }
+    return v;
+}
+
+template <int HD, int KVT, int G>
+__global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
+    static_assert(CH == 64, "softmax statistics assume one cached row per lane");
     typedef typename KVRow<KVT>::E E;
     constexpr int TPK = HD / 8;          // threads per key row (scores)
     constexpr int KPP = 256 / TPK;       // key rows per pass
+    constexpr int NP = CH / KPP;         // passes
     constexpr int TPR = HD / 2;          // threads per value row
     constexpr int KG = 256 / TPR;        // value-row groups
+    constexpr int VPT = CH / KG;         // value rows per thread
 
-    __shared__ float qs[GMAX][HD];
-    __shared__ float sc[GMAX][CH];
-    __shared__ float red[KG][GMAX][2][TPR];
-    __shared__ float mls[GMAX][2];
+    __shared__ float sc[G][CH];
+    __shared__ float red[KG][G][2][TPR];
+    __shared__ float mls[G][2];
 
     const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -77,51 +97,61 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a, int G) {
     const int n_kv = a.kv.n_kv;
     const float scale = 1.0f / sqrtf((float)HD);
 
-    for (int i = tid; i < G * HD; i += 256) {
-        const int h = i / HD, e = i % HD;
-        qs[h][e] = a.q[((size_t)t * a.H + g * G + h) * HD + e];
-    }
-    __syncthreads();
-
     const size_t rowbase = (((size_t)seq * n_kv + g) * a.kv.n_ctx + c0) * HD;
     const E *Kb = (const E *)a.kv.k + rowbase;
     const E *Vb = (const E *)a.kv.v + rowbase;
+    const int part = tid % TPK, krow = tid / TPK;
+    const int dp = tid % TPR, kg = tid / TPR;
 
-    // 1. scores
-    {
-        const int part = tid % TPK;
-        for (int j0 = 0; j0 < nk; j0 += KPP) {
-            const int j = j0 + tid / TPK;
-            float kv8[8];
-            if (j < nk)
-                KVRow<KVT>::load8(Kb + (size_t)j * HD + part * 8, kv8);
-            else
+    // ---- issue every load up front ----
+    float kv8[NP][8];
 #pragma unroll
-                for (int e = 0; e < 8; e++) kv8[e] = 0.f;
-            for (int h = 0; h < G; h++) {
-                float s = 0.f;
+    for (int ps = 0; ps < NP; ps++) {
+        const int j = ps * KPP + krow;
+        if (j < nk)
+            KVRow<KVT>::load8(Kb + (size_t)j * HD + part * 8, kv8[ps]);
+        else
 #pragma unroll
-                for (int e = 0; e < 8; e++) s += qs[h][part * 8 + e] * kv8[e];
+            for (int e = 0; e < 8; e++) kv8[ps][e] = 0.f;
+    }
+    float2 vv[VPT];
 #pragma unroll
-                for (int o = TPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-                if (part == 0 && j < nk) sc[h][j] = s * scale;
-            }
+    for (int i = 0; i < VPT; i++) {
+        const int j = kg + KG * i;
+        vv[i] = j < nk ? KVRow<KVT>::load2(Vb + (size_t)j * HD + 2 * dp) : make_float2(0.f, 0.f);
+    }
+    float qv[G][8];
+    const float *qb = a.q + ((size_t)t * a.H + g * G) * HD + part * 8;
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        const float4 lo = *(const float4 *)(qb + h * HD), hi = *(const float4 *)(qb + h * HD + 4);
+        qv[h][0] = lo.x; qv[h][1] = lo.y; qv[h][2] = lo.z; qv[h][3] = lo.w;
+        qv[h][4] = hi.x; qv[h][5] = hi.y; qv[h][6] = hi.z; qv[h][7] = hi.w;
+    }
+
+    // ---- 1. scores ----
+#pragma unroll
+    for (int ps = 0; ps < NP; ps++) {
+        const int j = ps * KPP + krow;
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) s += qv[h][e] * kv8[ps][e];
+            s = group_sum<TPK>(s);
+            if (part == 0 && j < nk) sc[h][j] = s * scale;
         }
     }
     __syncthreads();
 
-    // 2. softmax statistics of the chunk
+    // ---- 2. softmax statistics of the chunk (CH = 64: one row per lane) ----
     for (int h = w; h < G; h += 4) {
-        float m = -INFINITY;
-        for (int j = lane; j < nk; j += 64) m = fmaxf(m, sc[h][j]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (int j = lane; j < nk; j += 64) {
-            const float e = __expf(sc[h][j] - m);
-            sc[h][j] = e;
-            l += e;
-        }
-        l = wave_sum(l);
+        const float sj = lane < nk ? sc[h][lane] : -INFINITY;
+        float m = row16_max(sj);
+        m = fmaxf(fmaxf(readlane_f(m, 0), readlane_f(m, 16)), fmaxf(readlane_f(m, 32), readlane_f(m, 48)));
+        const float e = lane < nk ? __expf(sj - m) : 0.f;
+        sc[h][lane] = e;
+        const float l = wave_sum_dpp(e);
         if (lane == 0) {
             mls[h][0] = m;
             mls[h][1] = l;
@@ -129,21 +159,19 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a, int G) {
     }
     __syncthreads();
 
-    // 3. weighted sum of the value rows
+    // ---- 3. weighted sum of the value rows ----
     {
-        const int dp = tid % TPR, kg = tid / TPR;
-        float2 acc[GMAX];
+        float2 acc[G];
 #pragma unroll
-        for (int h = 0; h < GMAX; h++) acc[h] = make_float2(0.f, 0.f);
-        for (int j = kg; j < nk; j += KG) {
-            const float2 v = KVRow<KVT>::load2(Vb + (size_t)j * HD + 2 * dp);
+        for (int h = 0; h < G; h++) acc[h] = make_float2(0.f, 0.f);
 #pragma unroll
-            for (int h = 0; h < GMAX; h++) {
-                if (h < G) {
-                    const float p = sc[h][j];
-                    acc[h].x += p * v.x;
-                    acc[h].y += p * v.y;
-                }
+        for (int i = 0; i < VPT; i++) {
+            const int j = kg + KG * i;
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                const float p = sc[h][j];          // 0 past nk
+                acc[h].x += p * vv[i].x;
+                acc[h].y += p * vv[i].y;
             }
         }
         for (int h = 0; h < G; h++) {
@@ -167,42 +195,88 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a, int G) {
     }
 }
 
+// Merge of the chunk partials of one (head, token): 256 threads = HD/2
+// element pairs x (512/HD) chunk groups.
 template <int HD>
-__global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a) {
-    const int h = blockIdx.x, t = blockIdx.y, e = threadIdx.x;
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+    constexpr int TPR = HD / 2, CG = 256 / TPR;
+    __shared__ float wgt[1024];
+    __shared__ float red[4];
+    __shared__ float2 part2[CG][TPR];
+    const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nch = a.tok.pos[t] / a.chunk + 1;
     const size_t hh = (size_t)t * a.H + h;
     const float *ml = a.ml + hh * a.max_chunks * 2;
     const float *pa = a.part + hh * a.max_chunks * HD;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; c++) M = fmaxf(M, ml[2 * c]);
-    float L = 0.f, acc = 0.f;
-    for (int c = 0; c < nch; c++) {
-        const float f = __expf(ml[2 * c] - M);
-        L += ml[2 * c + 1] * f;
-        acc += pa[(size_t)c * HD + e] * f;
+    // chunk weights e^(m_c - M) and L
+    float mloc = -INFINITY;
+    for (int cc = tid; cc < nch; cc += 256) mloc = fmaxf(mloc, ml[2 * cc]);
+    mloc = row16_max(mloc);
+    mloc = fmaxf(fmaxf(readlane_f(mloc, 0), readlane_f(mloc, 16)), fmaxf(readlane_f(mloc, 32), readlane_f(mloc, 48)));
+    if (lane == 0) red[w] = mloc;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float lsum = 0.f;
+    for (int cc = tid; cc < nch; cc += 256) {
+        const float f = __expf(ml[2 * cc] - M);
+        wgt[cc] = f;
+        lsum += ml[2 * cc + 1] * f;
     }
-    ((f16 *)a.o)[(size_t)t * a.H * HD + (size_t)h * HD + e] = (f16)(acc / L);
+    lsum = wave_sum_dpp(lsum);
+    if (lane == 0) red[w] = lsum;
+    __syncthreads();
+    const float L = (red[0] + red[1]) + (red[2] + red[3]);
+    // element pair dp, chunk group cg: chunks cg, cg + CG, ...
+    const int dp = tid % TPR, cg = tid / TPR;
+    float2 acc = make_float2(0.f, 0.f);
+#pragma unroll 4
+    for (int cc = cg; cc < nch; cc += CG) {
+        const float2 v = *(const float2 *)(pa + (size_t)cc * HD + 2 * dp);
+        const float f = wgt[cc];
+        acc.x += v.x * f;
+        acc.y += v.y * f;
+    }
+    part2[cg][dp] = acc;
+    __syncthreads();
+    if (cg == 0) {
+        float2 s = part2[0][dp];
+#pragma unroll
+        for (int k = 1; k < CG; k++) {
+            s.x += part2[k][dp].x;
+            s.y += part2[k][dp].y;
+        }
+        h2 o;
+        o.x = (f16)(s.x / L);
+        o.y = (f16)(s.y / L);
+        *(h2 *)((f16 *)a.o + (size_t)t * a.H * HD + (size_t)h * HD + 2 * dp) = o;
+    }
+}
+
+template <int HD, int KVT>
+bool launch_part(const AttnArgs &a, int T, hipStream_t s) {
+    const dim3 grid(a.max_chunks, a.kv.n_kv, T);
+    switch (a.H / a.kv.n_kv) {
+    case 1: hipLaunchKernelGGL((k_attn_part<HD, KVT, 1>), grid, dim3(256), 0, s, a); return true;
+    case 2: hipLaunchKernelGGL((k_attn_part<HD, KVT, 2>), grid, dim3(256), 0, s, a); return true;
+    case 4: hipLaunchKernelGGL((k_attn_part<HD, KVT, 4>), grid, dim3(256), 0, s, a); return true;
+    case 8: hipLaunchKernelGGL((k_attn_part<HD, KVT, 8>), grid, dim3(256), 0, s, a); return true;
+    default: return false;
+    }
 }
 
 template <int HD>
 bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
-    const int G = a.H / a.kv.n_kv;
-    if (G > GMAX) return false;
-    if (a.kv.kvtype == T_F16)
-        hipLaunchKernelGGL((k_attn_part<HD, T_F16>), dim3(a.max_chunks, a.kv.n_kv, T), dim3(256), 0, s,
-                           a, G);
-    else
-        hipLaunchKernelGGL((k_attn_part<HD, T_F32>), dim3(a.max_chunks, a.kv.n_kv, T), dim3(256), 0, s,
-                           a, G);
-    hipLaunchKernelGGL((k_attn_merge<HD>), dim3(a.H, T), dim3(HD), 0, s, a);
+    const bool ok = a.kv.kvtype == T_F16 ? launch_part<HD, T_F16>(a, T, s) : launch_part<HD, T_F32>(a, T, s);
+    if (!ok) return false;
+    hipLaunchKernelGGL((k_attn_merge<HD>), dim3(a.H, T), dim3(256), 0, s, a);
     return true;
 }
 
 }  // namespace
 
 bool launch_attention(const AttnArgs &a, int T, hipStream_t s) {
-    if (a.chunk != CH || T <= 0) return false;
+    if (a.chunk != CH || T <= 0 || a.max_chunks > 1024) return false;
     switch (a.kv.hd) {
     case 64: return launch_hd<64>(a, T, s);
     case 128: return launch_hd<128>(a, T, s);

@@ -55,3 +55,33 @@ DEV uint4 load_stream16(const uint4 *p) {
     const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+
+// DPP lane exchange (v_mov_dpp) of a float.
+template <int CTRL>
+DEV float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Sum over each 16-lane row; every lane of the row gets the row's total.
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:4, row_ror:8.
+DEV float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x124>(v);
+    v += dpp_f<0x128>(v);
+    return v;
+}
+DEV float row16_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x124>(v));
+    v = fmaxf(v, dpp_f<0x128>(v));
+    return v;
+}
+DEV float readlane_f(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+// Sum over the 64 lanes without LDS traffic; the (wave-uniform) total is returned.
+DEV float wave_sum_dpp(float v) {
+    v = row16_sum(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}

@@ -458,6 +458,12 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
     c->step_cap = (int)(n_batch > n_seq ? n_batch : n_seq);
     c->n_out_cap = c->step_cap;
     c->pos_max.assign(n_seq, -1);
+    {
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            matvec_set_num_cu(ncu);
+    }
     if (p.hip_stream) {
         c->s = (hipStream_t)p.hip_stream;
     } else {

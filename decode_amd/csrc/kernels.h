@@ -75,6 +75,8 @@ void launch_quantize(const float *src, int rows, int K, QMat &m, int mode, int r
 void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, int row_off,
                      hipStream_t s);
 
+// Number of compute units the mat-vec grid is sized for (default 256).
+void matvec_set_num_cu(int n);
 // y = W x for T tokens (decode).  Q8_0 / Q4_0 only.
 bool launch_matvec(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, hipStream_t s);
 // Y = X W^T for T tokens (prefill / batched decode): MFMA for Q8_0 / Q4_0

@@ -78,171 +78,207 @@ DEV float blockdot_q8(const uint4 q0, const uint4 q1, const h2 *xp) {
     return acc;
 }
 
-template <int WT, int KB, int PU, int EPI>
-__global__ __launch_bounds__(256) void k_matvec(QMat W, InArgs in, EpiArgs ep, int pair_mode,
-                                                int pairs_per_wave) {
-    __shared__ float red[4];
-    const int lane = threadIdx.x & 63;
+// Code bytes + scales of one pair of rows for this lane's blocks.
+template <int WT, int KB>
+struct PairLoad {
+    uint4 q[2][KB][WT == T_Q4_0 ? 1 : 2];
+    uint16_t d[2][KB];
+};
+
+// Blocks b0 + lane + 64*i (i < KB) below b1 of rows r0, r1.
+template <int WT, int KB>
+DEV void load_pair(const QMat &W, int r0, int r1, int b0, int b1, int lane, PairLoad<WT, KB> &L) {
+    const int K = W.K, nb = K >> 5;
+    const int rows[2] = {r0, r1};
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+        const uint16_t *dr = W.d + (size_t)rows[r] * nb;
+        const uint4 *qr = WT == T_Q4_0
+                              ? (const uint4 *)((const uint8_t *)W.qs + (size_t)rows[r] * (K >> 1))
+                              : (const uint4 *)((const int8_t *)W.qs + (size_t)rows[r] * K);
+#pragma unroll
+        for (int i = 0; i < KB; i++) {
+            const int b = b0 + lane + 64 * i;
+            if (b < b1) {
+                if (WT == T_Q4_0) {
+                    L.q[r][i][0] = load_stream16(qr + b);
+                } else {
+                    L.q[r][i][0] = load_stream16(qr + 2 * b);
+                    L.q[r][i][WT == T_Q4_0 ? 0 : 1] = load_stream16(qr + 2 * b + 1);
+                }
+                L.d[r][i] = dr[b];
+            } else {
+#pragma unroll
+                for (int j = 0; j < (WT == T_Q4_0 ? 1 : 2); j++) L.q[r][i][j] = make_uint4(0, 0, 0, 0);
+                L.d[r][i] = 0;
+            }
+        }
+    }
+}
+
+template <int WT, int KB>
+DEV float dot_row(const PairLoad<WT, KB> &L, int r, const h2 (*xp)[16], const float *xsum) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < KB; i++) {
+        float bd;
+        if (WT == T_Q4_0)
+            bd = blockdot_q4(L.q[r][i][0], xp[i]);
+        else
+            bd = blockdot_q8(L.q[r][i][0], L.q[r][i][WT == T_Q4_0 ? 0 : 1], xp[i]);
+        a += f16_bits_to_f32(L.d[r][i]) * (bd - xsum[i]);
+    }
+    return a;
+}
+
+// NW wavefronts per block (one block per CU): the activation row is staged
+// once per block in LDS (normalized on the way when a norm is given).  The
+// K dimension is cut into S slices of at most 128 blocks; S wavefronts share
+// one row pair, each covering one slice with at most 2 blocks per lane whose
+// activations it keeps in registers.  Row pairs p = g, g + G, ... are
+// streamed with the next pair's loads in flight while the current pair is
+// reduced (DPP within the wavefront; for S > 1 the S partial sums meet in
+// double-buffered LDS and are added in slice order).
+template <int WT, int KB, int S, int EPI>
+__global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, int pair_mode) {
+    constexpr int NW = 16, NT = NW * 64, G = NW / S;
+    __shared__ __attribute__((aligned(16))) f16 xs[S * KB * 64 * 32];
+    __shared__ float red[NW];
+    __shared__ float part[2][NW][2];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int t = blockIdx.y;
     const int K = W.K, nb = K >> 5;
     const int xrow = in.row_idx ? in.row_idx[t] : t;
 
-    // ---- activations of this lane's blocks -> f16 pairs in registers ----
-    float rstd = 1.f;
+    // ---- stage the activation row in LDS as f16 ----
     if (in.norm_g) {
         const float *xr = in.x32 + (size_t)xrow * in.ldx;
         float ss = 0.f;
-        for (int k = threadIdx.x * 4; k < K; k += 1024) {
+        for (int k = tid * 4; k < K; k += NT * 4) {
             const float4 v = *(const float4 *)(xr + k);
             ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
         }
-        ss = block_sum256(ss, red);
-        rstd = 1.0f / sqrtf(ss / (float)K + in.eps);
+        ss = wave_sum_dpp(ss);
+        if (lane == 0) red[w] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; i++) tot += red[i];
+        const float rstd = 1.0f / sqrtf(tot / (float)K + in.eps);
+        for (int k = tid * 4; k < K; k += NT * 4) {
+            const float4 v = *(const float4 *)(xr + k);
+            const float4 g = *(const float4 *)(in.norm_g + k);
+            h2 lo, hi;
+            lo.x = (f16)(v.x * rstd * g.x);
+            lo.y = (f16)(v.y * rstd * g.y);
+            hi.x = (f16)(v.z * rstd * g.z);
+            hi.y = (f16)(v.w * rstd * g.w);
+            *(uint2 *)&xs[k] = make_uint2(h2_bits(lo), h2_bits(hi));
+        }
+    } else {
+        const uint16_t *xr = in.x16 + (size_t)xrow * in.ldx;
+        for (int k = tid * 8; k < K; k += NT * 8) *(uint4 *)&xs[k] = *(const uint4 *)(xr + k);
     }
+    __syncthreads();
+
+    // ---- this wavefront's K slice -> f16 pairs in registers ----
+    const int slice = w % S, grp = w / S;
+    const int nbs = (nb + S - 1) / S;
+    const int b0 = slice * nbs, b1 = min(nb, b0 + nbs);
     h2 xp[KB][16];
     float xsum[KB];
 #pragma unroll
     for (int i = 0; i < KB; i++) {
-        const int b = lane + 64 * i;
+        const int b = b0 + lane + 64 * i;
         f16 xv[32];
-        if (b < nb) {
-            if (in.norm_g) {
-                const float *xr = in.x32 + (size_t)xrow * in.ldx + b * 32;
-                const float *g = in.norm_g + b * 32;
+        if (b < b1) {
 #pragma unroll
-                for (int j = 0; j < 32; j += 4) {
-                    const float4 v = *(const float4 *)(xr + j);
-                    const float4 gg = *(const float4 *)(g + j);
-                    xv[j + 0] = (f16)(v.x * rstd * gg.x);
-                    xv[j + 1] = (f16)(v.y * rstd * gg.y);
-                    xv[j + 2] = (f16)(v.z * rstd * gg.z);
-                    xv[j + 3] = (f16)(v.w * rstd * gg.w);
-                }
-            } else {
-                const uint4 *xr = (const uint4 *)(in.x16 + (size_t)xrow * in.ldx + b * 32);
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const uint4 v = xr[j];
-                    *(uint4 *)&xv[8 * j] = v;
-                }
-            }
+            for (int j = 0; j < 4; j++) *(uint4 *)&xv[8 * j] = *(const uint4 *)&xs[b * 32 + 8 * j];
         } else {
 #pragma unroll
             for (int j = 0; j < 32; j++) xv[j] = (f16)0.f;
         }
-        float s = 0.f;
+        float sum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 32; j++) s += (float)xv[j];
-        xsum[i] = s * (WT == T_Q4_0 ? 1032.f : 1152.f);
+        for (int j = 0; j < 32; j++) sum += (float)xv[j];
+        xsum[i] = sum * (WT == T_Q4_0 ? 1032.f : 1152.f);
         if (WT == T_Q4_0)
             pairs_q4(xv, xp[i]);
         else
             pairs_q8(xv, xp[i]);
     }
 
-    // ---- rows ----
-    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // ---- stream row pairs ----
     const int npairs = W.N >> 1;
-    const int pbeg = wave * pairs_per_wave;
-    const int pend = min(npairs, pbeg + pairs_per_wave);
-    for (int p0 = pbeg; p0 < pend; p0 += PU) {
-        int rows[2 * PU];
-#pragma unroll
-        for (int u = 0; u < PU; u++) {
-            const int p = min(p0 + u, pend - 1);
-            pair_rows(pair_mode, p, rows[2 * u], rows[2 * u + 1]);
+    const int stride = gridDim.x * G;
+    const int first = blockIdx.x * G + grp;
+    const int iters = (npairs + stride - 1) / stride;    // same for every wavefront of the grid
+    int p = first, r0 = 0, r1 = 1;
+    PairLoad<WT, KB> cur;
+    if (p < npairs) {
+        pair_rows(pair_mode, p, r0, r1);
+        load_pair<WT, KB>(W, r0, r1, b0, b1, lane, cur);
+    }
+    for (int it = 0; it < iters; it++) {
+        const int pn = p + stride;
+        int n0 = r0, n1 = r1;
+        PairLoad<WT, KB> nxt;
+        if (pn < npairs) {
+            pair_rows(pair_mode, pn, n0, n1);
+            load_pair<WT, KB>(W, n0, n1, b0, b1, lane, nxt);
         }
-        float acc[2 * PU];
-        if (WT == T_Q4_0) {
-            uint4 q[2 * PU][KB];
-            uint16_t dsc[2 * PU][KB];
-#pragma unroll
-            for (int r = 0; r < 2 * PU; r++) {
-                const uint4 *qr = (const uint4 *)((const uint8_t *)W.qs + (size_t)rows[r] * (K >> 1));
-                const uint16_t *dr = W.d + (size_t)rows[r] * nb;
-#pragma unroll
-                for (int i = 0; i < KB; i++) {
-                    const int b = lane + 64 * i;
-                    if (b < nb) {
-                        q[r][i] = load_stream16(qr + b);
-                        dsc[r][i] = dr[b];
-                    } else {
-                        q[r][i] = make_uint4(0, 0, 0, 0);
-                        dsc[r][i] = 0;
-                    }
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 2 * PU; r++) {
-                float a = 0.f;
-#pragma unroll
-                for (int i = 0; i < KB; i++)
-                    a += f16_bits_to_f32(dsc[r][i]) * (blockdot_q4(q[r][i], xp[i]) - xsum[i]);
-                acc[r] = a;
-            }
+        float a0 = 0.f, a1 = 0.f;
+        if (p < npairs) {
+            a0 = wave_sum_dpp(dot_row<WT, KB>(cur, 0, xp, xsum));
+            a1 = wave_sum_dpp(dot_row<WT, KB>(cur, 1, xp, xsum));
+        }
+        if (S == 1) {
+            if (lane == 0 && p < npairs) epi_pair<EPI>(ep, t, p, r0, r1, a0, a1);
         } else {
-            uint4 q[2 * PU][KB][2];
-            uint16_t dsc[2 * PU][KB];
+            if (lane == 0) {
+                part[it & 1][w][0] = a0;
+                part[it & 1][w][1] = a1;
+            }
+            __syncthreads();
+            if (slice == 0 && lane == 0 && p < npairs) {
+                float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-            for (int r = 0; r < 2 * PU; r++) {
-                const uint4 *qr = (const uint4 *)((const int8_t *)W.qs + (size_t)rows[r] * K);
-                const uint16_t *dr = W.d + (size_t)rows[r] * nb;
-#pragma unroll
-                for (int i = 0; i < KB; i++) {
-                    const int b = lane + 64 * i;
-                    if (b < nb) {
-                        q[r][i][0] = load_stream16(qr + 2 * b);
-                        q[r][i][1] = load_stream16(qr + 2 * b + 1);
-                        dsc[r][i] = dr[b];
-                    } else {
-                        q[r][i][0] = q[r][i][1] = make_uint4(0, 0, 0, 0);
-                        dsc[r][i] = 0;
-                    }
+                for (int j = 0; j < S; j++) {
+                    s0 += part[it & 1][w + j][0];
+                    s1 += part[it & 1][w + j][1];
                 }
-            }
-#pragma unroll
-            for (int r = 0; r < 2 * PU; r++) {
-                float a = 0.f;
-#pragma unroll
-                for (int i = 0; i < KB; i++)
-                    a += f16_bits_to_f32(dsc[r][i]) * (blockdot_q8(q[r][i][0], q[r][i][1], xp[i]) - xsum[i]);
-                acc[r] = a;
+                epi_pair<EPI>(ep, t, p, r0, r1, s0, s1);
             }
         }
-#pragma unroll
-        for (int r = 0; r < 2 * PU; r++) acc[r] = wave_sum(acc[r]);
-#pragma unroll
-        for (int u = 0; u < PU; u++) {
-            if (lane == u && p0 + u < pend)
-                epi_pair<EPI>(ep, t, p0 + u, rows[2 * u], rows[2 * u + 1], acc[2 * u], acc[2 * u + 1]);
-        }
+        p = pn;
+        r0 = n0;
+        r1 = n1;
+        cur = nxt;
     }
 }
 
-template <int WT, int KB, int EPI>
+int g_num_cu = 256;
+
+template <int WT, int KB, int S, int EPI>
 bool launch_epi(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
                 hipStream_t s) {
-    constexpr int PU = KB >= 5 ? 1 : 2;
+    constexpr int G = 16 / S;
     const int npairs = W.N / 2;
-    // aim for about 8 wavefronts per CU on 256 CUs
-    const int target_waves = 2048;
-    int ppw = (npairs + target_waves - 1) / target_waves;
-    ppw = ((ppw + PU - 1) / PU) * PU;
-    const int waves = (npairs + ppw - 1) / ppw;
-    const int blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((k_matvec<WT, KB, PU, EPI>), dim3(blocks, T), dim3(256), 0, s, W, in, ep,
-                       pair_mode, ppw);
+    int blocks = (npairs + G - 1) / G;
+    if (blocks > g_num_cu) blocks = g_num_cu;
+    hipLaunchKernelGGL((k_matvec<WT, KB, S, EPI>), dim3(blocks, T), dim3(1024), 0, s, W, in, ep,
+                       pair_mode);
     return true;
 }
 
-template <int WT, int KB>
-bool launch_kb(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
+template <int WT, int KB, int S>
+bool launch_ks(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
                hipStream_t s) {
     switch (ep.epi) {
-    case EPI_STORE: return launch_epi<WT, KB, EPI_STORE>(W, in, ep, T, pair_mode, s);
-    case EPI_RESID: return launch_epi<WT, KB, EPI_RESID>(W, in, ep, T, pair_mode, s);
-    case EPI_QKV: return launch_epi<WT, KB, EPI_QKV>(W, in, ep, T, pair_mode, s);
-    case EPI_SWIGLU: return launch_epi<WT, KB, EPI_SWIGLU>(W, in, ep, T, pair_mode, s);
+    case EPI_STORE: return launch_epi<WT, KB, S, EPI_STORE>(W, in, ep, T, pair_mode, s);
+    case EPI_RESID: return launch_epi<WT, KB, S, EPI_RESID>(W, in, ep, T, pair_mode, s);
+    case EPI_QKV: return launch_epi<WT, KB, S, EPI_QKV>(W, in, ep, T, pair_mode, s);
+    case EPI_SWIGLU: return launch_epi<WT, KB, S, EPI_SWIGLU>(W, in, ep, T, pair_mode, s);
     default: return false;
     }
 }
@@ -251,21 +287,18 @@ template <int WT>
 bool launch_wt(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
                hipStream_t s) {
     const int nb = W.K / 32;
-    const int kb = (nb + 63) / 64;
-    switch (kb) {
-    case 1: return launch_kb<WT, 1>(W, in, ep, T, pair_mode, s);
-    case 2: return launch_kb<WT, 2>(W, in, ep, T, pair_mode, s);
-    case 3: return launch_kb<WT, 3>(W, in, ep, T, pair_mode, s);
-    case 4: return launch_kb<WT, 4>(W, in, ep, T, pair_mode, s);
-    case 5: return launch_kb<WT, 5>(W, in, ep, T, pair_mode, s);
-    case 6: return launch_kb<WT, 6>(W, in, ep, T, pair_mode, s);
-    case 7: return launch_kb<WT, 7>(W, in, ep, T, pair_mode, s);
-    case 8: return launch_kb<WT, 8>(W, in, ep, T, pair_mode, s);
-    default: return false;
-    }
+    if (nb <= 64) return launch_ks<WT, 1, 1>(W, in, ep, T, pair_mode, s);
+    if (nb <= 128) return launch_ks<WT, 2, 1>(W, in, ep, T, pair_mode, s);
+    if (nb <= 256) return launch_ks<WT, 2, 2>(W, in, ep, T, pair_mode, s);
+    if (nb <= 512) return launch_ks<WT, 2, 4>(W, in, ep, T, pair_mode, s);
+    return false;
 }
 
 }  // namespace
+
+void matvec_set_num_cu(int n) {
+    if (n > 0) g_num_cu = n;
+}
 
 bool launch_matvec(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, hipStream_t s) {
     if (W.K % 32 || W.N % 2 || T <= 0) return false;

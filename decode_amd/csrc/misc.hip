@@ -142,29 +142,37 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *x, int ldx, const 
 }
 
 // ---- greedy: index of the largest logit, lowest index on ties --------------
-__global__ __launch_bounds__(256) void k_argmax(const float *logits, int V, int32_t *out) {
-    __shared__ float sv[4];
-    __shared__ int si[4];
-    const int t = blockIdx.x;
+DEV void amax_take(float &bv, int &bi, float v, int i) {
+    if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
+__global__ __launch_bounds__(1024) void k_argmax(const float *logits, int V, int32_t *out) {
+    __shared__ float sv[16];
+    __shared__ int si[16];
+    const int t = blockIdx.x, tid = threadIdx.x;
     const float *l = logits + (size_t)t * V;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int j = threadIdx.x; j < V; j += 256) {
-        const float v = l[j];
-        if (v > bv) { bv = v; bi = j; }      // j increases: first max kept per thread
+    int j = tid;
+    for (; j + 3 * 1024 < V; j += 4 * 1024) {       // four independent loads in flight
+        const float v0 = l[j], v1 = l[j + 1024], v2 = l[j + 2048], v3 = l[j + 3072];
+        amax_take(bv, bi, v0, j);
+        amax_take(bv, bi, v1, j + 1024);
+        amax_take(bv, bi, v2, j + 2048);
+        amax_take(bv, bi, v3, j + 3072);
     }
+    for (; j < V; j += 1024) amax_take(bv, bi, l[j], j);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const float ov = __shfl_xor(bv, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+        amax_take(bv, bi, ov, oi);
     }
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { sv[w] = bv; si[w] = bi; }
+    const int w = tid >> 6;
+    if ((tid & 63) == 0) { sv[w] = bv; si[w] = bi; }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int k = 1; k < 4; k++)
-            if (sv[k] > bv || (sv[k] == bv && si[k] < bi)) { bv = sv[k]; bi = si[k]; }
+    if (tid == 0) {
+        for (int k = 1; k < 16; k++) amax_take(bv, bi, sv[k], si[k]);
         if (bi == 0x7fffffff) bi = 0;
         out[t] = bi;
     }
@@ -207,7 +215,7 @@ void launch_rmsnorm(const float *x, int ldx, const float *g, int d, float eps,
 }
 
 void launch_argmax(const float *logits, int V, int T, int32_t *out, hipStream_t s) {
-    hipLaunchKernelGGL(k_argmax, dim3(T), dim3(256), 0, s, logits, V, out);
+    hipLaunchKernelGGL(k_argmax, dim3(T), dim3(1024), 0, s, logits, V, out);
 }
 
 void launch_rope_table(float *cs, int n_ctx, int hd, float base, hipStream_t s) {
