@@ -77,7 +77,9 @@ void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, i
 
 // Number of compute units the mat-vec grid is sized for (default 256).
 void matvec_set_num_cu(int n);
-// y = W x for T tokens (decode).  Q8_0 / Q4_0 only.
+// y = W x for T tokens (decode).  Q8_0 / Q4_0 only.  The input row is
+// RMS-normalized (in.norm_g) for every epilogue but EPI_RESID, which takes
+// the f16 row as is.
 bool launch_matvec(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, hipStream_t s);
 // Y = X W^T for T tokens (prefill / batched decode): MFMA for Q8_0 / Q4_0
 // with N % 128 == 0, a plain fp32 kernel otherwise.

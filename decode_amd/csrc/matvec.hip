@@ -31,9 +31,13 @@
 namespace {
 
 // Activation pairs in the order the code extraction produces them.
-// Q4_0 block dword i (bytes 4i..4i+3): low nibbles = codes 4i..4i+3, high
-// nibbles = codes 16+4i..16+4i+3.  Masks 0x000F000F at shifts 0, 4, 8, 12
-// select code pairs (4i,4i+2), (16+4i,18+4i), (4i+1,4i+3), (17+4i,19+4i).
+// Q4_0 block dword i (bytes 4i..4i+3): byte k holds code 4i+k in its low
+// nibble and code 16+4i+k in its high nibble.  Masking a dword with
+// 0x000F000F / 0x00F000F0 and or-ing the f16 exponent of 1024 gives the f16
+// pairs (1024 + q[4i], 1024 + q[4i+2]) and (1024 + 16 q[4i+16], 1024 + 16
+// q[4i+18]) directly; the same masks on the dword shifted right by 8 give
+// codes 4i+1, 4i+3 and 16 q[4i+17], 16 q[4i+19].  All these values are exact
+// in f16.  xp[4i+0..3] hold the matching activation pairs.
 DEV void pairs_q4(const f16 *x, h2 *xp) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -43,8 +47,8 @@ DEV void pairs_q4(const f16 *x, h2 *xp) {
         xp[4 * i + 3] = h2{x[16 + 4 * i + 1], x[16 + 4 * i + 3]};
     }
 }
-// Q8_0 block dword i holds codes 4i..4i+3; masks 0x00FF00FF at shifts 0 and 8
-// select code pairs (4i, 4i+2) and (4i+1, 4i+3).
+// Q8_0 block dword i holds codes 4i..4i+3; after flipping the sign bits,
+// masks 0x00FF00FF at shifts 0 and 8 select (4i, 4i+2) and (4i+1, 4i+3).
 DEV void pairs_q8(const f16 *x, h2 *xp) {
 #pragma unroll
     for (int i = 0; i < 8; i++) {
@@ -53,27 +57,46 @@ DEV void pairs_q8(const f16 *x, h2 *xp) {
     }
 }
 
-DEV float blockdot_q4(const uint4 q, const h2 *xp) {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        acc = dot2(as_h2((w[i] & 0x000F000Fu) | 0x64006400u), xp[4 * i + 0], acc);
-        acc = dot2(as_h2(((w[i] >> 4) & 0x000F000Fu) | 0x64006400u), xp[4 * i + 1], acc);
-        acc = dot2(as_h2(((w[i] >> 8) & 0x000F000Fu) | 0x64006400u), xp[4 * i + 2], acc);
-        acc = dot2(as_h2(((w[i] >> 12) & 0x000F000Fu) | 0x64006400u), xp[4 * i + 3], acc);
-    }
-    return acc;
+// Constants held in registers so that (w & mask) | magic issues as one
+// v_and_or_b32 (these VOP3 forms cannot encode literal constants).
+struct Masks {
+    uint32_t lo4, hi4, lo8, flip, magic;
+};
+DEV Masks make_masks() {
+    Masks m;
+    asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(m.lo4));
+    asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(m.hi4));
+    asm volatile("s_mov_b32 %0, 0x00ff00ff" : "=s"(m.lo8));
+    asm volatile("s_mov_b32 %0, 0x80808080" : "=s"(m.flip));
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m.magic));
+    return m;
 }
 
-DEV float blockdot_q8(const uint4 q0, const uint4 q1, const h2 *xp) {
+// Returns sum_A (1024 + q) x + sum_B (1024 + 16 q) x / 16 over the block, where
+// A are the low-nibble codes 0..15 and B the high-nibble codes 16..31.
+DEV float blockdot_q4(const uint4 q, const h2 *xp, const Masks &m) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t w8 = w[i] >> 8;
+        a = dot2(as_h2((w[i] & m.lo4) | m.magic), xp[4 * i + 0], a);
+        b = dot2(as_h2((w[i] & m.hi4) | m.magic), xp[4 * i + 1], b);
+        a = dot2(as_h2((w8 & m.lo4) | m.magic), xp[4 * i + 2], a);
+        b = dot2(as_h2((w8 & m.hi4) | m.magic), xp[4 * i + 3], b);
+    }
+    return a + b * 0.0625f;
+}
+
+// Returns sum (1024 + 128 + q) x over the block.
+DEV float blockdot_q8(const uint4 q0, const uint4 q1, const h2 *xp, const Masks &m) {
     const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        const uint32_t u = w[i] ^ 0x80808080u;
-        acc = dot2(as_h2((u & 0x00FF00FFu) | 0x64006400u), xp[2 * i + 0], acc);
-        acc = dot2(as_h2(((u >> 8) & 0x00FF00FFu) | 0x64006400u), xp[2 * i + 1], acc);
+        const uint32_t u = w[i] ^ m.flip;
+        acc = dot2(as_h2((u & m.lo8) | m.magic), xp[2 * i + 0], acc);
+        acc = dot2(as_h2(((u >> 8) & m.lo8) | m.magic), xp[2 * i + 1], acc);
     }
     return acc;
 }
@@ -117,32 +140,34 @@ DEV void load_pair(const QMat &W, int r0, int r1, int b0, int b1, int lane, Pair
 }
 
 template <int WT, int KB>
-DEV float dot_row(const PairLoad<WT, KB> &L, int r, const h2 (*xp)[16], const float *xsum) {
+DEV float dot_row(const PairLoad<WT, KB> &L, int r, const h2 (*xp)[16], const float *xsum,
+                  const Masks &m) {
     float a = 0.f;
 #pragma unroll
     for (int i = 0; i < KB; i++) {
         float bd;
         if (WT == T_Q4_0)
-            bd = blockdot_q4(L.q[r][i][0], xp[i]);
+            bd = blockdot_q4(L.q[r][i][0], xp[i], m);
         else
-            bd = blockdot_q8(L.q[r][i][0], L.q[r][i][WT == T_Q4_0 ? 0 : 1], xp[i]);
+            bd = blockdot_q8(L.q[r][i][0], L.q[r][i][WT == T_Q4_0 ? 0 : 1], xp[i], m);
         a += f16_bits_to_f32(L.d[r][i]) * (bd - xsum[i]);
     }
     return a;
 }
 
-// NW wavefronts per block (one block per CU): the activation row is staged
-// once per block in LDS (normalized on the way when a norm is given).  The
-// K dimension is cut into S slices of at most 128 blocks; S wavefronts share
-// one row pair, each covering one slice with at most 2 blocks per lane whose
-// activations it keeps in registers.  Row pairs p = g, g + G, ... are
+// NW wavefronts per block (one block per CU).  The K dimension is cut into S
+// slices of at most 128 blocks; S wavefronts share one row pair, each
+// covering one slice with at most 2 blocks per lane whose activations it
+// keeps in registers.  An f16 input row is read straight into registers; an
+// f32 residual row to be RMS-normalized is normalized once per block into LDS.  Row pairs p = g, g + G, ... are
 // streamed with the next pair's loads in flight while the current pair is
 // reduced (DPP within the wavefront; for S > 1 the S partial sums meet in
 // double-buffered LDS and are added in slice order).
 template <int WT, int KB, int S, int EPI>
 __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, int pair_mode) {
-    constexpr int NW = 16, NT = NW * 64, G = NW / S;
-    __shared__ __attribute__((aligned(16))) f16 xs[S * KB * 64 * 32];
+    constexpr int NW = 16, G = NW / S;
+    // normalized input: staged through LDS (registers would not hold the row)
+    __shared__ __attribute__((aligned(16))) f16 xs[EPI == EPI_RESID ? 8 : S * KB * 64 * 32];
     __shared__ float red[NW];
     __shared__ float part[2][NW][2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -150,11 +175,26 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
     const int K = W.K, nb = K >> 5;
     const int xrow = in.row_idx ? in.row_idx[t] : t;
 
-    // ---- stage the activation row in LDS as f16 ----
-    if (in.norm_g) {
+    const int slice = w % S, grp = w / S;
+    const int nbs = (nb + S - 1) / S;
+    const int b0 = slice * nbs, b1 = min(nb, b0 + nbs);
+    const int npairs = W.N >> 1;
+    const int stride = gridDim.x * G;
+    const int first = blockIdx.x * G + grp;
+    const int iters = (npairs + stride - 1) / stride;    // same for every wavefront of the grid
+    int p = first, r0 = 0, r1 = 1;
+
+    // ---- this wavefront's K slice of the activations -> f16 pairs in registers.
+    //      With a norm, the wavefront also reads the rest of the row for the sum
+    //      of squares: no LDS and no block barrier on the way in. ----
+    // every epilogue except the residual add reads a normalized row
+    constexpr bool NORM = EPI != EPI_RESID;
+    f16 xv[KB][32];
+    if (NORM) {
         const float *xr = in.x32 + (size_t)xrow * in.ldx;
+        const int tid = threadIdx.x;
         float ss = 0.f;
-        for (int k = tid * 4; k < K; k += NT * 4) {
+        for (int k = tid * 4; k < K; k += NW * 256) {
             const float4 v = *(const float4 *)(xr + k);
             ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
         }
@@ -164,56 +204,64 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         float tot = 0.f;
 #pragma unroll
         for (int i = 0; i < NW; i++) tot += red[i];
-        const float rstd = 1.0f / sqrtf(tot / (float)K + in.eps);
-        for (int k = tid * 4; k < K; k += NT * 4) {
+        const float rs = 1.0f / sqrtf(tot / (float)K + in.eps);
+        for (int k = tid * 4; k < K; k += NW * 256) {
             const float4 v = *(const float4 *)(xr + k);
             const float4 g = *(const float4 *)(in.norm_g + k);
             h2 lo, hi;
-            lo.x = (f16)(v.x * rstd * g.x);
-            lo.y = (f16)(v.y * rstd * g.y);
-            hi.x = (f16)(v.z * rstd * g.z);
-            hi.y = (f16)(v.w * rstd * g.w);
+            lo.x = (f16)(v.x * rs * g.x);
+            lo.y = (f16)(v.y * rs * g.y);
+            hi.x = (f16)(v.z * rs * g.z);
+            hi.y = (f16)(v.w * rs * g.w);
             *(uint2 *)&xs[k] = make_uint2(h2_bits(lo), h2_bits(hi));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KB; i++) {
+            const int b = b0 + lane + 64 * i;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (b < b1) v = *(const uint4 *)&xs[b * 32 + 8 * j];
+                *(uint4 *)&xv[i][8 * j] = v;
+            }
         }
     } else {
         const uint16_t *xr = in.x16 + (size_t)xrow * in.ldx;
-        for (int k = tid * 8; k < K; k += NT * 8) *(uint4 *)&xs[k] = *(const uint4 *)(xr + k);
+#pragma unroll
+        for (int i = 0; i < KB; i++) {
+            const int b = b0 + lane + 64 * i;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (b < b1) v = *(const uint4 *)(xr + b * 32 + 8 * j);
+                *(uint4 *)&xv[i][8 * j] = v;
+            }
+        }
     }
-    __syncthreads();
-
-    // ---- this wavefront's K slice -> f16 pairs in registers ----
-    const int slice = w % S, grp = w / S;
-    const int nbs = (nb + S - 1) / S;
-    const int b0 = slice * nbs, b1 = min(nb, b0 + nbs);
     h2 xp[KB][16];
     float xsum[KB];
 #pragma unroll
     for (int i = 0; i < KB; i++) {
-        const int b = b0 + lane + 64 * i;
-        f16 xv[32];
-        if (b < b1) {
+        // offsets removed once per block: Q4_0 keeps 1024 + q on codes 0..15 and
+        // (1024 + 16 q) / 16 on codes 16..31, so sum (q - 8) x needs
+        // 1032 * sum(x[0..15]) + 72 * sum(x[16..31]) subtracted; Q8_0 keeps
+        // 1024 + 128 + q everywhere.
+        float s_lo = 0.f, s_hi = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; j++) *(uint4 *)&xv[8 * j] = *(const uint4 *)&xs[b * 32 + 8 * j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < 32; j++) xv[j] = (f16)0.f;
+        for (int j = 0; j < 16; j++) {
+            s_lo += (float)xv[i][j];
+            s_hi += (float)xv[i][16 + j];
         }
-        float sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 32; j++) sum += (float)xv[j];
-        xsum[i] = sum * (WT == T_Q4_0 ? 1032.f : 1152.f);
+        xsum[i] = WT == T_Q4_0 ? 1032.f * s_lo + 72.f * s_hi : 1152.f * (s_lo + s_hi);
         if (WT == T_Q4_0)
-            pairs_q4(xv, xp[i]);
+            pairs_q4(xv[i], xp[i]);
         else
-            pairs_q8(xv, xp[i]);
+            pairs_q8(xv[i], xp[i]);
     }
 
     // ---- stream row pairs ----
-    const int npairs = W.N >> 1;
-    const int stride = gridDim.x * G;
-    const int first = blockIdx.x * G + grp;
-    const int iters = (npairs + stride - 1) / stride;    // same for every wavefront of the grid
-    int p = first, r0 = 0, r1 = 1;
+    const Masks mk = make_masks();
     PairLoad<WT, KB> cur;
     if (p < npairs) {
         pair_rows(pair_mode, p, r0, r1);
@@ -229,8 +277,8 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         }
         float a0 = 0.f, a1 = 0.f;
         if (p < npairs) {
-            a0 = wave_sum_dpp(dot_row<WT, KB>(cur, 0, xp, xsum));
-            a1 = wave_sum_dpp(dot_row<WT, KB>(cur, 1, xp, xsum));
+            a0 = wave_sum_dpp(dot_row<WT, KB>(cur, 0, xp, xsum, mk));
+            a1 = wave_sum_dpp(dot_row<WT, KB>(cur, 1, xp, xsum, mk));
         }
         if (S == 1) {
             if (lane == 0 && p < npairs) epi_pair<EPI>(ep, t, p, r0, r1, a0, a1);
@@ -262,11 +310,11 @@ int g_num_cu = 256;
 template <int WT, int KB, int S, int EPI>
 bool launch_epi(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
                 hipStream_t s) {
-    constexpr int G = 16 / S;
+    constexpr int NW = 16, G = NW / S;
     const int npairs = W.N / 2;
     int blocks = (npairs + G - 1) / G;
     if (blocks > g_num_cu) blocks = g_num_cu;
-    hipLaunchKernelGGL((k_matvec<WT, KB, S, EPI>), dim3(blocks, T), dim3(1024), 0, s, W, in, ep,
+    hipLaunchKernelGGL((k_matvec<WT, KB, S, EPI>), dim3(blocks, T), dim3(NW * 64), 0, s, W, in, ep,
                        pair_mode);
     return true;
 }
@@ -283,15 +331,32 @@ bool launch_ks(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pa
     }
 }
 
+template <int WT, int KB>
+bool launch_kb(int S, const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
+               hipStream_t s) {
+    switch (S) {
+    case 1: return launch_ks<WT, KB, 1>(W, in, ep, T, pair_mode, s);
+    case 2: return launch_ks<WT, KB, 2>(W, in, ep, T, pair_mode, s);
+    case 4: return launch_ks<WT, KB, 4>(W, in, ep, T, pair_mode, s);
+    case 8: return launch_ks<WT, KB, 8>(W, in, ep, T, pair_mode, s);
+    case 16: return launch_ks<WT, KB, 16>(W, in, ep, T, pair_mode, s);
+    default: return false;
+    }
+}
+
+// K slices per row pair: enough that a lane holds at most 2 blocks, and more
+// while the grid would otherwise leave compute units idle.
 template <int WT>
 bool launch_wt(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
                hipStream_t s) {
-    const int nb = W.K / 32;
-    if (nb <= 64) return launch_ks<WT, 1, 1>(W, in, ep, T, pair_mode, s);
-    if (nb <= 128) return launch_ks<WT, 2, 1>(W, in, ep, T, pair_mode, s);
-    if (nb <= 256) return launch_ks<WT, 2, 2>(W, in, ep, T, pair_mode, s);
-    if (nb <= 512) return launch_ks<WT, 2, 4>(W, in, ep, T, pair_mode, s);
-    return false;
+    const int nb = W.K / 32, npairs = W.N / 2;
+    if (nb > 16 * 128) return false;
+    int S = 1;
+    while (S * 128 < nb) S *= 2;
+    while (S < 16 && (long long)npairs * S < 16LL * g_num_cu) S *= 2;
+    const int nbs = (nb + S - 1) / S;
+    return nbs <= 64 ? launch_kb<WT, 1>(S, W, in, ep, T, pair_mode, s)
+                     : launch_kb<WT, 2>(S, W, in, ep, T, pair_mode, s);
 }
 
 }  // namespace
@@ -302,6 +367,7 @@ void matvec_set_num_cu(int n) {
 
 bool launch_matvec(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, hipStream_t s) {
     if (W.K % 32 || W.N % 2 || T <= 0) return false;
+    if ((in.norm_g != nullptr) != (ep.epi != EPI_RESID)) return false;
     const int pair_mode = ep.epi == EPI_SWIGLU ? PAIR_GU : PAIR_ADJ;
     if (pair_mode == PAIR_GU && W.N % 64) return false;
     if (W.wtype == T_Q4_0) return launch_wt<T_Q4_0>(W, in, ep, T, pair_mode, s);
