@@ -357,6 +357,7 @@ struct dec_ctx {
     bool amax_fetched = false;
     std::map<int, hipGraphExec_t> graphs;
     bool use_graphs = true;
+    bool prefill_mode = false; // run_tokens is running one sequence's consecutive positions
     bool registered = false;   // counted in m->n_ctx_refs
     dec_stats st{};
     // timing probe: a pool of event pairs for launches made directly on the
@@ -633,7 +634,19 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         at.max_chunks = c->max_chunks;
         at.chunk = c->chunk;
         at.o = c->o;
-        ok = ok && stage(c, DEC_K_ATTN, l, [&] { return launch_attention(at, T, s); });
+        ok = ok && stage(c, DEC_K_ATTN, l, [&] {
+            if (c->prefill_mode && T > 1) {
+                FlashArgs fa;
+                fa.q = c->q;
+                fa.kv = c->kv[l];
+                fa.tok = ti;
+                fa.H = h.n_head;
+                fa.T = T;
+                fa.o = c->o;
+                if (launch_flash_prefill(fa, s)) return true;
+            }
+            return launch_attention(at, T, s);
+        });
 
         EpiArgs er;
         er.epi = EPI_RESID;
@@ -745,7 +758,10 @@ extern "C" int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int
             row0 = T - 1;
             n_rows = 1;
         }
-        if (!run_tokens(c, u, T, row0, n_rows, output_all ? u : 0)) return -3;
+        c->prefill_mode = true;
+        const bool ok = run_tokens(c, u, T, row0, n_rows, output_all ? u : 0);
+        c->prefill_mode = false;
+        if (!ok) return -3;
         c->pos_max[seq] = p0 + u + T - 1;
         c->st.n_ubatches++;
         reset_outputs(c, output_all ? u + T : (last ? 1 : 0));

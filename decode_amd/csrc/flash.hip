@@ -1,0 +1,197 @@
+// flash.hip -- causal attention of a prefill ubatch with MFMA (gfx950).
+//
+// The T tokens of a ubatch belong to one sequence and sit at consecutive
+// positions p0 .. p0+T-1; their K,V rows are already in the f16 cache (the
+// QKV epilogue appends them before this kernel runs).  Query row t attends to
+// cached rows 0 .. p0+t.
+//
+// Block = 4 wavefronts sharing one KV head g.  Wavefront w takes query head
+// g*G + hz*Gb + w%Gb and a tile of 32 tokens (w/Gb picks the tile when a
+// group has fewer than 4 heads).  Per 64-key tile, K (row-major) and V
+// (transposed, keys permuted as below) are staged in LDS once for all four
+// wavefronts, then each wavefront runs
+//   S^T[key][q] = K Q^T     v_mfma_f32_32x32x16_f16, 2 key tiles x hd/16 steps
+//   online softmax per query column (a lane holds 16 keys of one query; the
+//   other 16 are in lane l^32), base-2 with log2(e)/sqrt(hd) folded into Q
+//   O^T[d][q] += V^T P^T    4 key steps x hd/32 dim tiles
+// The P operand comes straight from the S^T accumulators: for key step s the
+// lane's eight values r = 8s'..8s'+7 are keys 16s + 8(e>>2) + 4h + (e&3)
+// (h = lane/32, e = 0..7), so V^T is stored with key k at column
+// 16s + 8h + e of its 16-key group, and each lane reads 16 contiguous bytes.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int BKEY = 64;        // keys per tile
+constexpr int KPAD = 8;         // f16 padding of an LDS row
+
+DEV int vt_col(int k) {         // permuted column of key k (0..63) in V^T
+    const int s = k >> 4, rem = k & 15;
+    const int h = (rem >> 2) & 1, e = ((rem >> 3) << 2) | (rem & 3);
+    return (s << 4) | (h << 3) | e;
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
+    constexpr int KS = HD / 16;     // k-steps of Q K^T
+    constexpr int DT = HD / 32;     // 32-row dim tiles of O^T
+    __shared__ __attribute__((aligned(16))) f16 Ks[BKEY][HD + KPAD];
+    __shared__ __attribute__((aligned(16))) f16 Vt[HD][BKEY + KPAD];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int G = a.H / a.kv.n_kv, Gb = G < 4 ? G : 4, Tb = 4 / Gb;
+    const int g = blockIdx.y;
+    const int head = g * G + blockIdx.z * Gb + (w % Gb);
+    const int tok0 = blockIdx.x * 32 * Tb;                  // first token of the block
+    const int tw = tok0 + (w / Gb) * 32;                    // first token of this wavefront
+    const int q_t = tw + (lane & 31);                       // this lane's query column
+    const int p0 = a.tok.pos[0], seq = a.tok.seq[0];
+    const int T = a.T;
+    const bool q_ok = q_t < T;
+    const int qpos = p0 + q_t;
+    const int last_tok = min(T - 1, tok0 + 32 * Tb - 1);
+    const int n_keys = p0 + last_tok + 1;                   // keys any query of the block reads
+    const float qscale = 1.4426950408889634f / sqrtf((float)HD);
+
+    // Q^T operand: lane supplies Q[q][16 ks + 8 (lane/32) + e]
+    h8 qf[KS];
+    {
+        const float *qr = a.q + ((size_t)(q_ok ? q_t : 0) * a.H + head) * HD + 8 * (lane >> 5);
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
+            if (q_ok) {
+                lo = *(const float4 *)(qr + 16 * ks);
+                hi = *(const float4 *)(qr + 16 * ks + 4);
+            }
+            qf[ks][0] = (f16)(lo.x * qscale); qf[ks][1] = (f16)(lo.y * qscale);
+            qf[ks][2] = (f16)(lo.z * qscale); qf[ks][3] = (f16)(lo.w * qscale);
+            qf[ks][4] = (f16)(hi.x * qscale); qf[ks][5] = (f16)(hi.y * qscale);
+            qf[ks][6] = (f16)(hi.z * qscale); qf[ks][7] = (f16)(hi.w * qscale);
+        }
+    }
+
+    f16x acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[dt][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const size_t base = (((size_t)seq * a.kv.n_kv + g) * a.kv.n_ctx) * HD;
+    const uint16_t *Kg = (const uint16_t *)a.kv.k + base;
+    const uint16_t *Vg = (const uint16_t *)a.kv.v + base;
+    constexpr int CHUNKS = BKEY * HD / 8;                   // 16-byte chunks per tile
+    constexpr int CPT = CHUNKS / 256;
+
+    const int ntiles = (n_keys + BKEY - 1) / BKEY;
+    for (int kt = 0; kt < ntiles; kt++) {
+        const int k0 = kt * BKEY;
+        // ---- stage K and V^T of keys k0 .. k0+63 (rows past n_keys read as 0) ----
+        uint4 kr[CPT], vr[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; c++) {
+            const int ch = tid + c * 256, key = ch / (HD / 8), d8 = ch % (HD / 8);
+            const bool ok = k0 + key < n_keys;
+            kr[c] = ok ? *(const uint4 *)(Kg + (size_t)(k0 + key) * HD + d8 * 8) : make_uint4(0, 0, 0, 0);
+            vr[c] = ok ? *(const uint4 *)(Vg + (size_t)(k0 + key) * HD + d8 * 8) : make_uint4(0, 0, 0, 0);
+        }
+        __syncthreads();                                    // previous tile fully consumed
+#pragma unroll
+        for (int c = 0; c < CPT; c++) {
+            const int ch = tid + c * 256, key = ch / (HD / 8), d8 = ch % (HD / 8);
+            *(uint4 *)&Ks[key][d8 * 8] = kr[c];
+            const f16 *v = (const f16 *)&vr[c];
+            const int col = vt_col(key);
+#pragma unroll
+            for (int e = 0; e < 8; e++) Vt[d8 * 8 + e][col] = v[e];
+        }
+        __syncthreads();
+
+        // ---- S^T = K Q^T for two 32-key halves ----
+        f16x s[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) s[mt][r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) {
+                const h8 kf = *(const h8 *)&Ks[mt * 32 + (lane & 31)][16 * ks + 8 * (lane >> 5)];
+                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[mt], 0, 0, 0);
+            }
+        }
+        // ---- causal mask + online softmax over this query column ----
+        float mt_max = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int key = k0 + mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (key > qpos || !q_ok) s[mt][r] = -INFINITY;
+                mt_max = fmaxf(mt_max, s[mt][r]);
+            }
+        mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, 64));
+        const float m_new = fmaxf(m_run, mt_max);
+        const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+        float psum = 0.f;
+        h8 pf[4];
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const float p = m_new == -INFINITY ? 0.f : exp2f(s[mt][r] - m_new);
+                psum += p;
+                pf[mt * 2 + (r >> 3)][r & 7] = (f16)p;
+            }
+        psum += __shfl_xor(psum, 32, 64);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[dt][r] *= alpha;
+        // ---- O^T += V^T P^T ----
+#pragma unroll
+        for (int ss = 0; ss < 4; ss++) {
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const h8 vf = *(const h8 *)&Vt[dt * 32 + (lane & 31)][16 * ss + 8 * (lane >> 5)];
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ss], acc[dt], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- O = O^T / l, f16 ----
+    if (q_ok) {
+        const float inv = 1.0f / l_run;
+        f16 *o = (f16 *)a.o + ((size_t)q_t * a.H + head) * HD;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; r4++) {
+                const int d = dt * 32 + r4 * 8 + (lane >> 5) * 4;
+                h2 lo, hi;
+                lo.x = (f16)(acc[dt][r4 * 4 + 0] * inv);
+                lo.y = (f16)(acc[dt][r4 * 4 + 1] * inv);
+                hi.x = (f16)(acc[dt][r4 * 4 + 2] * inv);
+                hi.y = (f16)(acc[dt][r4 * 4 + 3] * inv);
+                *(uint2 *)(o + d) = make_uint2(h2_bits(lo), h2_bits(hi));
+            }
+    }
+}
+
+}  // namespace
+
+bool launch_flash_prefill(const FlashArgs &a, hipStream_t s) {
+    if (a.kv.kvtype != T_F16 || a.T <= 0) return false;
+    const int G = a.H / a.kv.n_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+    const int Gb = G < 4 ? G : 4, Tb = 4 / Gb;
+    const dim3 grid((a.T + 32 * Tb - 1) / (32 * Tb), a.kv.n_kv, G / Gb);
+    switch (a.kv.hd) {
+    case 64: hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, s, a); return true;
+    case 128: hipLaunchKernelGGL(k_flash_prefill<128>, grid, dim3(256), 0, s, a); return true;
+    default: return false;
+    }
+}

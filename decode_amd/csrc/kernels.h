@@ -110,4 +110,16 @@ struct AttnArgs {
 };
 bool launch_attention(const AttnArgs &a, int T, hipStream_t s);
 
+// Causal attention of a prefill ubatch: T tokens of sequence tok.seq[0] at
+// positions tok.pos[0] + t, f16 cache, MFMA flash attention.  Returns false
+// (nothing launched) when the shape is not covered.
+struct FlashArgs {
+    const float *q = nullptr;     // [T][H*hd] f32 (after RoPE)
+    KVLayer kv;
+    TokInfo tok;
+    int H = 0, T = 0;
+    uint16_t *o = nullptr;        // [T][H*hd] f16 output
+};
+bool launch_flash_prefill(const FlashArgs &a, hipStream_t s);
+
 // f16 -> (rows of) GGUF-style export helpers are host code in engine.cpp.

@@ -69,9 +69,13 @@ def test_tiny_workload_matches_oracle(dec, orc):
     assert st["n_graph_captures"] == 1 and st["n_graph_replays"] == 2 * W["n_decode"] - 1
 
 
-@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_0])
-def test_quantized_multi_ubatch_matches_oracle(dec, orc, wtype):
-    hp = small_hp(wtype, synth.F16, n_embd=512, n_head=8, n_head_kv=2, n_ff=1024, n_vocab=2048)
+@pytest.mark.parametrize("wtype,hd,H,Hkv", [(synth.Q8_0, 64, 8, 2), (synth.Q4_0, 64, 8, 2),
+                                           (synth.Q4_0, 128, 4, 4), (synth.Q8_0, 128, 8, 1)])
+def test_quantized_multi_ubatch_matches_oracle(dec, orc, wtype, hd, H, Hkv):
+    """Prefill in 3 ubatches (the last one ragged) then decode steps; covers MHA
+    and GQA groups of 4 and 8, head_dim 64 and 128."""
+    hp = small_hp(wtype, synth.F16, n_embd=512, n_head=H, n_head_kv=Hkv, head_dim=hd, n_ff=1024,
+                  n_vocab=2048)
     w = synth.weights_numpy(hp, 40 + wtype, threads=4)
     prompt = synth.prompt(hp["n_vocab"], 150, 41)
     n_dec = 12
