@@ -246,10 +246,15 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
             s.x += part2[k][dp].x;
             s.y += part2[k][dp].y;
         }
-        h2 o;
-        o.x = (f16)(s.x / L);
-        o.y = (f16)(s.y / L);
-        *(h2 *)((f16 *)a.o + (size_t)t * a.H * HD + (size_t)h * HD + 2 * dp) = o;
+        const float ox = s.x / L, oy = s.y / L;
+        h2 o, ol;
+        o.x = (f16)ox;
+        o.y = (f16)oy;
+        ol.x = (f16)(ox - (float)o.x);
+        ol.y = (f16)(oy - (float)o.y);
+        const size_t off = (size_t)t * a.H * HD + (size_t)h * HD + 2 * dp;
+        *(h2 *)((f16 *)a.o + off) = o;
+        if (a.o_lo) *(h2 *)((f16 *)a.o_lo + off) = ol;
     }
 }
 

@@ -344,7 +344,8 @@ struct dec_ctx {
     std::vector<KVLayer> kv;
     float *rope_cs = nullptr;
     float *x = nullptr, *q = nullptr, *part = nullptr, *ml = nullptr, *logits = nullptr;
-    uint16_t *xn = nullptr, *o = nullptr, *h = nullptr;
+    uint16_t *xn = nullptr, *xn_lo = nullptr, *o = nullptr, *h = nullptr, *o_lo = nullptr,
+             *h_lo = nullptr;
     int32_t *amax = nullptr, *dev_step = nullptr, *host_step = nullptr;
     int chunk = 0, max_chunks = 0;
     hipEvent_t staged = nullptr;
@@ -356,8 +357,10 @@ struct dec_ctx {
     std::vector<int32_t> host_amax;
     bool amax_fetched = false;
     std::map<int, hipGraphExec_t> graphs;
+    std::map<int, int> seen;   // decode steps run per token count (capture from the second on)
     bool use_graphs = true;
     bool prefill_mode = false; // run_tokens is running one sequence's consecutive positions
+    bool flash_prefill = true; // DECODE_PREFILL_ATTN=splitk selects the split-K kernel instead
     bool registered = false;   // counted in m->n_ctx_refs
     dec_stats st{};
     // timing probe: a pool of event pairs for launches made directly on the
@@ -459,6 +462,7 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
     c->step_cap = (int)(n_batch > n_seq ? n_batch : n_seq);
     c->n_out_cap = c->step_cap;
     c->pos_max.assign(n_seq, -1);
+    if (const char *e = getenv("DECODE_PREFILL_ATTN")) c->flash_prefill = strcmp(e, "splitk") != 0;
     {
         int dev = 0, ncu = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
@@ -493,15 +497,18 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
         c->rope_cs = (float *)c->mem.get((size_t)n_ctx * hd * 4);
         c->x = (float *)c->mem.get(T * d * 4);
         c->xn = (uint16_t *)c->mem.get(T * d * 2);
+        c->xn_lo = (uint16_t *)c->mem.get(T * d * 2);
         c->q = (float *)c->mem.get(T * qd * 4);
         c->o = (uint16_t *)c->mem.get(T * qd * 2);
         c->h = (uint16_t *)c->mem.get(T * Fp * 2);
+        c->o_lo = (uint16_t *)c->mem.get(T * qd * 2);
+        c->h_lo = (uint16_t *)c->mem.get(T * Fp * 2);
         c->part = (float *)c->mem.get(T * h.n_head * c->max_chunks * hd * 4);
         c->ml = (float *)c->mem.get(T * h.n_head * c->max_chunks * 2 * 4);
         c->logits = (float *)c->mem.get((size_t)c->n_out_cap * V * 4);
         c->amax = (int32_t *)c->mem.get((size_t)c->n_out_cap * 4);
         c->dev_step = (int32_t *)c->mem.get((size_t)c->step_cap * 3 * 4);
-        ok = c->rope_cs && c->x && c->xn && c->q && c->o && c->h && c->part && c->ml && c->logits &&
+        ok = c->rope_cs && c->x && c->xn && c->xn_lo && c->q && c->o && c->h && c->o_lo && c->h_lo && c->part && c->ml && c->logits &&
              c->amax && c->dev_step;
     }
     if (ok) HIP_OK(hipHostMalloc((void **)&c->host_step, (size_t)c->step_cap * 3 * 4, 0), ok = false);
@@ -576,7 +583,15 @@ template <typename F>
 static bool stage(dec_ctx *c, int role, int layer, F &&f) {
     probe_begin(c, role, layer);
     bool ok = true;
-    if (emit(c)) ok = f();
+    if (emit(c)) {
+        ok = f();
+        const hipError_t e = hipGetLastError();
+        if (!ok || e != hipSuccess) {
+            LOGE("launch of kernel role %d, layer %d failed: %s", role, layer,
+                 ok ? hipGetErrorString(e) : "shape not supported");
+            ok = false;
+        }
+    }
     probe_end(c, role, layer);
     return ok;
 }
@@ -621,8 +636,8 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 in.ldx = d;
                 return launch_matvec(L.wqkv, in, eq, T, s);
             }
-            launch_rmsnorm(c->x, d, L.attn_norm, d, h.rms_eps, nullptr, T, c->xn, d, s);
-            return launch_gemm(L.wqkv, c->xn, d, eq, T, s);
+            launch_rmsnorm(c->x, d, L.attn_norm, d, h.rms_eps, nullptr, T, c->xn, c->xn_lo, d, s);
+            return launch_gemm(L.wqkv, c->xn, c->xn_lo, d, eq, T, s);
         });
         AttnArgs at;
         at.q = c->q;
@@ -634,8 +649,9 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         at.max_chunks = c->max_chunks;
         at.chunk = c->chunk;
         at.o = c->o;
+        at.o_lo = c->o_lo;
         ok = ok && stage(c, DEC_K_ATTN, l, [&] {
-            if (c->prefill_mode && T > 1) {
+            if (c->prefill_mode && c->flash_prefill && T > 1) {
                 FlashArgs fa;
                 fa.q = c->q;
                 fa.kv = c->kv[l];
@@ -643,6 +659,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 fa.H = h.n_head;
                 fa.T = T;
                 fa.o = c->o;
+                fa.o_lo = c->o_lo;
                 if (launch_flash_prefill(fa, s)) return true;
             }
             return launch_attention(at, T, s);
@@ -656,14 +673,16 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
             if (mv) {
                 InArgs in;
                 in.x16 = c->o;
+                in.x16lo = c->o_lo;
                 in.ldx = qd;
                 return launch_matvec(L.wo, in, er, T, s);
             }
-            return launch_gemm(L.wo, c->o, qd, er, T, s);
+            return launch_gemm(L.wo, c->o, c->o_lo, qd, er, T, s);
         });
         EpiArgs eg;
         eg.epi = EPI_SWIGLU;
         eg.h = c->h;
+        eg.h_lo = c->h_lo;
         eg.ldh = Fp;
         ok = ok && stage(c, DEC_K_FFN_GU, l, [&] {
             if (mv) {
@@ -674,17 +693,18 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 in.ldx = d;
                 return launch_matvec(L.wgu, in, eg, T, s);
             }
-            launch_rmsnorm(c->x, d, L.ffn_norm, d, h.rms_eps, nullptr, T, c->xn, d, s);
-            return launch_gemm(L.wgu, c->xn, d, eg, T, s);
+            launch_rmsnorm(c->x, d, L.ffn_norm, d, h.rms_eps, nullptr, T, c->xn, c->xn_lo, d, s);
+            return launch_gemm(L.wgu, c->xn, c->xn_lo, d, eg, T, s);
         });
         ok = ok && stage(c, DEC_K_FFN_DOWN, l, [&] {
             if (mv) {
                 InArgs in;
                 in.x16 = c->h;
+                in.x16lo = c->h_lo;
                 in.ldx = Fp;
                 return launch_matvec(L.wdown, in, er, T, s);
             }
-            return launch_gemm(L.wdown, c->h, Fp, er, T, s);
+            return launch_gemm(L.wdown, c->h, c->h_lo, Fp, er, T, s);
         });
     }
     if (ok && n_rows > 0) {
@@ -702,8 +722,8 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 return launch_matvec(m->out, in, eo, n_rows, s);
             }
             launch_rmsnorm(c->x + (size_t)row0 * d, d, m->out_norm, d, h.rms_eps, nullptr, n_rows, c->xn,
-                           d, s);
-            return launch_gemm(m->out, c->xn, d, eo, n_rows, s);
+                           c->xn_lo, d, s);
+            return launch_gemm(m->out, c->xn, c->xn_lo, d, eo, n_rows, s);
         });
         ok = ok && stage(c, -1, -1, [&] {
             launch_argmax(c->logits + (size_t)out_row0 * V, V, n_rows, c->amax + out_row0, s);
@@ -810,7 +830,10 @@ extern "C" int32_t dec_decode(dec_ctx *c, const int32_t *tokens, const int32_t *
         c->host_step[2 * cap + i] = seq_ids[i];
     }
     if (!stage_step(c, n)) return -3;
-    if (!c->use_graphs) {
+    // The first step of a shape runs kernel by kernel: every kernel it uses is
+    // then loaded, so the capture of the second step only records launches
+    // (graph reuse applies to repeated shapes, as in the article's step 13b).
+    if (!c->use_graphs || c->seen[n]++ == 0) {
         c->seg_req = SEG_ALL;
         if (!run_tokens(c, 0, n, 0, n, 0)) return -3;
     } else {

@@ -51,7 +51,9 @@ DEV void epi_pair(const EpiArgs &e, int t, int p, int r0, int r1, float a, float
     }
     case EPI_SWIGLU: {
         const float hv = silu(a) * b;
-        ((f16 *)e.h)[(size_t)t * e.ldh + p] = (f16)hv;
+        const f16 hh = (f16)hv;
+        ((f16 *)e.h)[(size_t)t * e.ldh + p] = hh;
+        if (e.h_lo) ((f16 *)e.h_lo)[(size_t)t * e.ldh + p] = (f16)(hv - (float)hh);
         break;
     }
     case EPI_QKV: {

@@ -165,18 +165,21 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
     // ---- O = O^T / l, f16 ----
     if (q_ok) {
         const float inv = 1.0f / l_run;
-        f16 *o = (f16 *)a.o + ((size_t)q_t * a.H + head) * HD;
+        const size_t ob = ((size_t)q_t * a.H + head) * HD;
 #pragma unroll
         for (int dt = 0; dt < DT; dt++)
 #pragma unroll
             for (int r4 = 0; r4 < 4; r4++) {
                 const int d = dt * 32 + r4 * 8 + (lane >> 5) * 4;
-                h2 lo, hi;
-                lo.x = (f16)(acc[dt][r4 * 4 + 0] * inv);
-                lo.y = (f16)(acc[dt][r4 * 4 + 1] * inv);
-                hi.x = (f16)(acc[dt][r4 * 4 + 2] * inv);
-                hi.y = (f16)(acc[dt][r4 * 4 + 3] * inv);
-                *(uint2 *)(o + d) = make_uint2(h2_bits(lo), h2_bits(hi));
+                f16 hv[4], lv[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float y = acc[dt][r4 * 4 + e] * inv;
+                    hv[e] = (f16)y;
+                    lv[e] = (f16)(y - (float)hv[e]);
+                }
+                *(uint2 *)((f16 *)a.o + ob + d) = *(const uint2 *)hv;
+                if (a.o_lo) *(uint2 *)((f16 *)a.o_lo + ob + d) = *(const uint2 *)lv;
             }
     }
 }

@@ -45,6 +45,7 @@ struct EpiArgs {
     float *y = nullptr;        // STORE / RESID: [T][ldy]
     int ldy = 0;
     uint16_t *h = nullptr;     // SWIGLU: f16 [T][ldh]
+    uint16_t *h_lo = nullptr;  // SWIGLU: optional f16 rounding remainder of h
     int ldh = 0;
     float *qout = nullptr;     // QKV: f32 [T][qd]
     int qd = 0, kd = 0;
@@ -60,6 +61,7 @@ struct InArgs {
     const float *norm_g = nullptr;
     float eps = 0.f;
     const uint16_t *x16 = nullptr;   // [T][ldx] f16 when no prologue
+    const uint16_t *x16lo = nullptr; // [T][ldx] f16 remainder: the row is x16 + x16lo
     int ldx = 0;
     const int32_t *row_idx = nullptr;  // optional gather: input row of output row t
 };
@@ -81,16 +83,18 @@ void matvec_set_num_cu(int n);
 // RMS-normalized (in.norm_g) for every epilogue but EPI_RESID, which takes
 // the f16 row as is.
 bool launch_matvec(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, hipStream_t s);
-// Y = X W^T for T tokens (prefill / batched decode): MFMA for Q8_0 / Q4_0
+// Y = X W^T for T tokens (prefill / batched decode), X = Xh + Xl given as two
+// f16 arrays [T][ldx] (value and rounding remainder): MFMA for Q8_0 / Q4_0
 // with N % 128 == 0, a plain fp32 kernel otherwise.
-bool launch_gemm(const QMat &W, const uint16_t *X, int ldx, const EpiArgs &ep, int T,
-                 hipStream_t s);
+bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
+                 int T, hipStream_t s);
 
 // x[t] = dequantized row tok[t] of the embedding table (f32).
 void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, hipStream_t s);
-// xn[t] = f16(rmsnorm(x[row_idx ? row_idx[t] : t]) * g)
+// y = rmsnorm(x[row_idx ? row_idx[t] : t]) * g as f16 value xn[t] and f16
+// rounding remainder xl[t] (y = xn + xl to about 22 bits)
 void launch_rmsnorm(const float *x, int ldx, const float *g, int d, float eps,
-                    const int32_t *row_idx, int T, uint16_t *xn, int ldn, hipStream_t s);
+                    const int32_t *row_idx, int T, uint16_t *xn, uint16_t *xl, int ldn, hipStream_t s);
 // out[t] = argmax of logits row t (lowest index on ties)
 void launch_argmax(const float *logits, int V, int T, int32_t *out, hipStream_t s);
 // cos/sin table [n_ctx][hd/2][2] with theta = p * base^(-2i/hd) in double
@@ -107,6 +111,7 @@ struct AttnArgs {
     float *ml = nullptr;          // [T][H][max_chunks][2] running max / sum
     int max_chunks = 0, chunk = 0;
     uint16_t *o = nullptr;        // [T][H*hd] f16 output
+    uint16_t *o_lo = nullptr;     // [T][H*hd] f16 rounding remainder of the output
 };
 bool launch_attention(const AttnArgs &a, int T, hipStream_t s);
 
@@ -119,6 +124,7 @@ struct FlashArgs {
     TokInfo tok;
     int H = 0, T = 0;
     uint16_t *o = nullptr;        // [T][H*hd] f16 output
+    uint16_t *o_lo = nullptr;     // [T][H*hd] f16 rounding remainder of the output
 };
 bool launch_flash_prefill(const FlashArgs &a, hipStream_t s);
 

@@ -72,6 +72,10 @@ DEV Masks make_masks() {
     return m;
 }
 
+// The activations enter as two f16 parts, x = hi + lo (lo = the f16 rounding
+// of x - hi), so a product uses x to about 22 significant bits: xp[0..15] are
+// the hi pairs, xp[16..31] the lo pairs.
+//
 // Returns sum_A (1024 + q) x + sum_B (1024 + 16 q) x / 16 over the block, where
 // A are the low-nibble codes 0..15 and B the high-nibble codes 16..31.
 DEV float blockdot_q4(const uint4 q, const h2 *xp, const Masks &m) {
@@ -80,10 +84,16 @@ DEV float blockdot_q4(const uint4 q, const h2 *xp, const Masks &m) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const uint32_t w8 = w[i] >> 8;
-        a = dot2(as_h2((w[i] & m.lo4) | m.magic), xp[4 * i + 0], a);
-        b = dot2(as_h2((w[i] & m.hi4) | m.magic), xp[4 * i + 1], b);
-        a = dot2(as_h2((w8 & m.lo4) | m.magic), xp[4 * i + 2], a);
-        b = dot2(as_h2((w8 & m.hi4) | m.magic), xp[4 * i + 3], b);
+        const h2 c0 = as_h2((w[i] & m.lo4) | m.magic), c1 = as_h2((w[i] & m.hi4) | m.magic);
+        const h2 c2 = as_h2((w8 & m.lo4) | m.magic), c3 = as_h2((w8 & m.hi4) | m.magic);
+        a = dot2(c0, xp[4 * i + 0], a);
+        b = dot2(c1, xp[4 * i + 1], b);
+        a = dot2(c2, xp[4 * i + 2], a);
+        b = dot2(c3, xp[4 * i + 3], b);
+        a = dot2(c0, xp[16 + 4 * i + 0], a);
+        b = dot2(c1, xp[16 + 4 * i + 1], b);
+        a = dot2(c2, xp[16 + 4 * i + 2], a);
+        b = dot2(c3, xp[16 + 4 * i + 3], b);
     }
     return a + b * 0.0625f;
 }
@@ -95,11 +105,16 @@ DEV float blockdot_q8(const uint4 q0, const uint4 q1, const h2 *xp, const Masks 
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         const uint32_t u = w[i] ^ m.flip;
-        acc = dot2(as_h2((u & m.lo8) | m.magic), xp[2 * i + 0], acc);
-        acc = dot2(as_h2(((u >> 8) & m.lo8) | m.magic), xp[2 * i + 1], acc);
+        const h2 c0 = as_h2((u & m.lo8) | m.magic), c1 = as_h2(((u >> 8) & m.lo8) | m.magic);
+        acc = dot2(c0, xp[2 * i + 0], acc);
+        acc = dot2(c1, xp[2 * i + 1], acc);
+        acc = dot2(c0, xp[16 + 2 * i + 0], acc);
+        acc = dot2(c1, xp[16 + 2 * i + 1], acc);
     }
     return acc;
 }
+
+constexpr int MV_KMAX = 16384;   // longest input row (elements) staged in LDS
 
 // Code bytes + scales of one pair of rows for this lane's blocks.
 template <int WT, int KB>
@@ -140,7 +155,7 @@ DEV void load_pair(const QMat &W, int r0, int r1, int b0, int b1, int lane, Pair
 }
 
 template <int WT, int KB>
-DEV float dot_row(const PairLoad<WT, KB> &L, int r, const h2 (*xp)[16], const float *xsum,
+DEV float dot_row(const PairLoad<WT, KB> &L, int r, const h2 (*xp)[32], const float *xsum,
                   const Masks &m) {
     float a = 0.f;
 #pragma unroll
@@ -167,7 +182,9 @@ template <int WT, int KB, int S, int EPI>
 __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, int pair_mode) {
     constexpr int NW = 16, G = NW / S;
     // normalized input: staged through LDS (registers would not hold the row)
-    __shared__ __attribute__((aligned(16))) f16 xs[EPI == EPI_RESID ? 8 : S * KB * 64 * 32];
+    constexpr int XS = EPI == EPI_RESID ? 8 : (S * KB * 64 * 32 < MV_KMAX ? S * KB * 64 * 32 : MV_KMAX);
+    __shared__ __attribute__((aligned(16))) f16 xs[XS];
+    __shared__ __attribute__((aligned(16))) f16 xsl[XS];
     __shared__ float red[NW];
     __shared__ float part[2][NW][2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -189,7 +206,7 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
     //      of squares: no LDS and no block barrier on the way in. ----
     // every epilogue except the residual add reads a normalized row
     constexpr bool NORM = EPI != EPI_RESID;
-    f16 xv[KB][32];
+    f16 xv[KB][32], xl[KB][32];
     if (NORM) {
         const float *xr = in.x32 + (size_t)xrow * in.ldx;
         const int tid = threadIdx.x;
@@ -208,12 +225,15 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         for (int k = tid * 4; k < K; k += NW * 256) {
             const float4 v = *(const float4 *)(xr + k);
             const float4 g = *(const float4 *)(in.norm_g + k);
-            h2 lo, hi;
-            lo.x = (f16)(v.x * rs * g.x);
-            lo.y = (f16)(v.y * rs * g.y);
-            hi.x = (f16)(v.z * rs * g.z);
-            hi.y = (f16)(v.w * rs * g.w);
-            *(uint2 *)&xs[k] = make_uint2(h2_bits(lo), h2_bits(hi));
+            const float y[4] = {v.x * rs * g.x, v.y * rs * g.y, v.z * rs * g.z, v.w * rs * g.w};
+            f16 hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                hi[e] = (f16)y[e];
+                lo[e] = (f16)(y[e] - (float)hi[e]);
+            }
+            *(uint2 *)&xs[k] = *(const uint2 *)hi;
+            *(uint2 *)&xsl[k] = *(const uint2 *)lo;
         }
         __syncthreads();
 #pragma unroll
@@ -221,25 +241,34 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
             const int b = b0 + lane + 64 * i;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (b < b1) v = *(const uint4 *)&xs[b * 32 + 8 * j];
+                uint4 v = make_uint4(0, 0, 0, 0), vl = v;
+                if (b < b1) {
+                    v = *(const uint4 *)&xs[b * 32 + 8 * j];
+                    vl = *(const uint4 *)&xsl[b * 32 + 8 * j];
+                }
                 *(uint4 *)&xv[i][8 * j] = v;
+                *(uint4 *)&xl[i][8 * j] = vl;
             }
         }
     } else {
         const uint16_t *xr = in.x16 + (size_t)xrow * in.ldx;
+        const uint16_t *xrl = in.x16lo + (size_t)xrow * in.ldx;
 #pragma unroll
         for (int i = 0; i < KB; i++) {
             const int b = b0 + lane + 64 * i;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (b < b1) v = *(const uint4 *)(xr + b * 32 + 8 * j);
+                uint4 v = make_uint4(0, 0, 0, 0), vl = v;
+                if (b < b1) {
+                    v = *(const uint4 *)(xr + b * 32 + 8 * j);
+                    vl = *(const uint4 *)(xrl + b * 32 + 8 * j);
+                }
                 *(uint4 *)&xv[i][8 * j] = v;
+                *(uint4 *)&xl[i][8 * j] = vl;
             }
         }
     }
-    h2 xp[KB][16];
+    h2 xp[KB][32];
     float xsum[KB];
 #pragma unroll
     for (int i = 0; i < KB; i++) {
@@ -250,14 +279,17 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         float s_lo = 0.f, s_hi = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; j++) {
-            s_lo += (float)xv[i][j];
-            s_hi += (float)xv[i][16 + j];
+            s_lo += (float)xv[i][j] + (float)xl[i][j];
+            s_hi += (float)xv[i][16 + j] + (float)xl[i][16 + j];
         }
         xsum[i] = WT == T_Q4_0 ? 1032.f * s_lo + 72.f * s_hi : 1152.f * (s_lo + s_hi);
-        if (WT == T_Q4_0)
+        if (WT == T_Q4_0) {
             pairs_q4(xv[i], xp[i]);
-        else
+            pairs_q4(xl[i], xp[i] + 16);
+        } else {
             pairs_q8(xv[i], xp[i]);
+            pairs_q8(xl[i], xp[i] + 16);
+        }
     }
 
     // ---- stream row pairs ----
@@ -350,13 +382,15 @@ template <int WT>
 bool launch_wt(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
                hipStream_t s) {
     const int nb = W.K / 32, npairs = W.N / 2;
-    if (nb > 16 * 128) return false;
+    const int slice_max = WT == T_Q8_0 ? 64 : 128;   // blocks per K slice (registers)
+    if (nb > 16 * slice_max) return false;
     int S = 1;
-    while (S * 128 < nb) S *= 2;
+    while (S * slice_max < nb) S *= 2;
     while (S < 16 && (long long)npairs * S < 16LL * g_num_cu) S *= 2;
+    if (ep.epi != EPI_RESID && W.K > MV_KMAX) return false;
     const int nbs = (nb + S - 1) / S;
-    return nbs <= 64 ? launch_kb<WT, 1>(S, W, in, ep, T, pair_mode, s)
-                     : launch_kb<WT, 2>(S, W, in, ep, T, pair_mode, s);
+    if (WT == T_Q8_0 || nbs <= 64) return launch_kb<WT, 1>(S, W, in, ep, T, pair_mode, s);
+    return launch_kb<T_Q4_0, 2>(S, W, in, ep, T, pair_mode, s);
 }
 
 }  // namespace

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void k_embed(QMat E, const int32_t *tok, float
 // ---- RMSNorm to f16: xn = f16(x * (1/sqrt(mean(x^2) + eps)) * g) ----------
 __global__ __launch_bounds__(256) void k_rmsnorm(const float *x, int ldx, const float *g, int d,
                                                  float eps, const int32_t *row_idx, uint16_t *xn,
-                                                 int ldn) {
+                                                 uint16_t *xl, int ldn) {
     __shared__ float red[4];
     const int t = blockIdx.x;
     const int row = row_idx ? row_idx[t] : t;
@@ -138,7 +138,13 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *x, int ldx, const 
     ss = block_sum256(ss, red);
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
     f16 *o = (f16 *)xn + (size_t)t * ldn;
-    for (int j = threadIdx.x; j < d; j += 256) o[j] = (f16)(xr[j] * r * g[j]);
+    f16 *ol = (f16 *)xl + (size_t)t * ldn;
+    for (int j = threadIdx.x; j < d; j += 256) {
+        const float y = xr[j] * r * g[j];
+        const f16 hi = (f16)y;
+        o[j] = hi;
+        ol[j] = (f16)(y - (float)hi);
+    }
 }
 
 // ---- greedy: index of the largest logit, lowest index on ties --------------
@@ -210,8 +216,8 @@ void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, h
 }
 
 void launch_rmsnorm(const float *x, int ldx, const float *g, int d, float eps,
-                    const int32_t *row_idx, int T, uint16_t *xn, int ldn, hipStream_t s) {
-    hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), 0, s, x, ldx, g, d, eps, row_idx, xn, ldn);
+                    const int32_t *row_idx, int T, uint16_t *xn, uint16_t *xl, int ldn, hipStream_t s) {
+    hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), 0, s, x, ldx, g, d, eps, row_idx, xn, xl, ldn);
 }
 
 void launch_argmax(const float *logits, int V, int T, int32_t *out, hipStream_t s) {

@@ -145,9 +145,10 @@ int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int32_t seq_id
 /* One generation step: token i belongs to sequence seq_ids[i] and is placed
  * at that sequence's next position; K and V are appended before attending
  * (KV-cache appendix).  All n sequences must differ; n <= n_seq_max.
- * Logits are produced for every token, row i for token i.  The step's
- * kernel sequence is captured once per n as a HIP graph and replayed (the
- * article's graph reuse, step 13b).  Return codes as dec_prefill. */
+ * Logits are produced for every token, row i for token i.  The first step
+ * with a given n runs kernel by kernel; the second is captured as a HIP
+ * graph and every later one replays it (the article's graph reuse, step
+ * 13b).  Return codes as dec_prefill. */
 int32_t dec_decode(dec_ctx *c, const int32_t *tokens, const int32_t *seq_ids, int32_t n);
 
 /* Logits row i of the last call: i >= 0 is the i-th output row, -1 the

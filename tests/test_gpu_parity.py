@@ -66,7 +66,8 @@ def test_tiny_workload_matches_oracle(dec, orc):
     f_toks, f_rows = gpu_greedy(ctx, prompt, W["n_decode"])
     assert f_toks == o_toks
     st = ctx.stats()
-    assert st["n_graph_captures"] == 1 and st["n_graph_replays"] == 2 * W["n_decode"] - 1
+    # first step of the shape eager, second captured, the rest replayed
+    assert st["n_graph_captures"] == 1 and st["n_graph_replays"] == 2 * W["n_decode"] - 2
 
 
 @pytest.mark.parametrize("wtype,hd,H,Hkv", [(synth.Q8_0, 64, 8, 2), (synth.Q4_0, 64, 8, 2),
