@@ -262,10 +262,10 @@ template <int HD, int KVT>
 bool launch_part(const AttnArgs &a, int T, hipStream_t s) {
     const dim3 grid(a.max_chunks, a.kv.n_kv, T);
     switch (a.H / a.kv.n_kv) {
-    case 1: hipLaunchKernelGGL((k_attn_part<HD, KVT, 1>), grid, dim3(256), 0, s, a); return true;
-    case 2: hipLaunchKernelGGL((k_attn_part<HD, KVT, 2>), grid, dim3(256), 0, s, a); return true;
-    case 4: hipLaunchKernelGGL((k_attn_part<HD, KVT, 4>), grid, dim3(256), 0, s, a); return true;
-    case 8: hipLaunchKernelGGL((k_attn_part<HD, KVT, 8>), grid, dim3(256), 0, s, a); return true;
+    case 1: launch((k_attn_part<HD, KVT, 1>), grid, dim3(256), 0, s, a); return true;
+    case 2: launch((k_attn_part<HD, KVT, 2>), grid, dim3(256), 0, s, a); return true;
+    case 4: launch((k_attn_part<HD, KVT, 4>), grid, dim3(256), 0, s, a); return true;
+    case 8: launch((k_attn_part<HD, KVT, 8>), grid, dim3(256), 0, s, a); return true;
     default: return false;
     }
 }
@@ -274,7 +274,7 @@ template <int HD>
 bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
     const bool ok = a.kv.kvtype == T_F16 ? launch_part<HD, T_F16>(a, T, s) : launch_part<HD, T_F32>(a, T, s);
     if (!ok) return false;
-    hipLaunchKernelGGL((k_attn_merge<HD>), dim3(a.H, T), dim3(256), 0, s, a);
+    launch((k_attn_merge<HD>), dim3(a.H, T), dim3(256), 0, s, a);
     return true;
 }
 

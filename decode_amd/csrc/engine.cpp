@@ -10,6 +10,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -340,10 +341,13 @@ struct dec_ctx {
     hipStream_t s = nullptr;
     bool own_stream = false;
     int n_ctx = 0, n_batch = 0, n_ubatch = 0, n_seq = 0, Tmax = 0, step_cap = 0, n_out_cap = 0;
+    int step_stride = 0;       // n of the staged call: ids at [0,n), positions [n,2n), sequences [2n,3n)
     Mem mem;
     std::vector<KVLayer> kv;
     float *rope_cs = nullptr;
     float *x = nullptr, *q = nullptr, *part = nullptr, *ml = nullptr, *logits = nullptr;
+    float *gws = nullptr;      // K-split partial tiles of the ubatch GEMMs
+    size_t gws_bytes = 0;
     uint16_t *xn = nullptr, *xn_lo = nullptr, *o = nullptr, *h = nullptr, *o_lo = nullptr,
              *h_lo = nullptr;
     int32_t *amax = nullptr, *dev_step = nullptr, *host_step = nullptr;
@@ -363,8 +367,8 @@ struct dec_ctx {
     bool flash_prefill = true; // DECODE_PREFILL_ATTN=splitk selects the split-K kernel instead
     bool registered = false;   // counted in m->n_ctx_refs
     dec_stats st{};
-    // timing probe: a pool of event pairs for launches made directly on the
-    // stream, and one pair that lives inside the captured decode graph
+    // timing probe: a pool of event pairs, each stamped by the kernels of one
+    // probed unit launched directly on the stream (hipExtLaunchKernel)
     static constexpr int NPROBE = 64;
     int pr_role = -1, pr_layer = -1;
     hipEvent_t pr_e0[NPROBE] = {}, pr_e1[NPROBE] = {};
@@ -372,12 +376,14 @@ struct dec_ctx {
     double pr_ms = 0.0;
     int64_t pr_n = 0;
     // A probed decode step runs as graph(before the probed kernel), the probed
-    // kernel launched directly between two events, graph(after): HIP cannot
-    // time events that were captured into a graph.  seg_req selects which
+    // kernel launched directly with its timing events, graph(after): HIP
+    // cannot time events that were captured into a graph.  seg_req selects which
     // launches run_tokens emits; seg_cur tracks where the sequence is.
     int seg_req = 0, seg_cur = 1;
     std::map<int, hipGraphExec_t> graphs_post;
 };
+
+thread_local LaunchProbe g_launch_probe;
 
 enum { SEG_ALL = 0, SEG_PRE = 1, SEG_MID = 2, SEG_POST = 3 };
 static bool emit(const dec_ctx *c) { return c->seg_req == SEG_ALL || c->seg_req == c->seg_cur; }
@@ -418,13 +424,15 @@ static void probe_begin(dec_ctx *c, int role, int layer) {
     c->seg_cur = SEG_MID;
     if (!emit(c)) return;
     if (c->pr_used == dec_ctx::NPROBE) probe_collect(c);
-    (void)hipEventRecord(c->pr_e0[c->pr_used], c->s);
+    g_launch_probe.e0 = c->pr_e0[c->pr_used];
+    g_launch_probe.e1 = c->pr_e1[c->pr_used];
+    g_launch_probe.armed = true;
 }
 
 static void probe_end(dec_ctx *c, int role, int layer) {
     if (!probe_hit(c, role, layer)) return;
     if (emit(c)) {
-        (void)hipEventRecord(c->pr_e1[c->pr_used], c->s);
+        g_launch_probe = LaunchProbe{};
         c->pr_used++;
     }
     c->seg_cur = SEG_POST;
@@ -466,8 +474,10 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
     {
         int dev = 0, ncu = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
             matvec_set_num_cu(ncu);
+            gemm_set_num_cu(ncu);
+        }
     }
     if (p.hip_stream) {
         c->s = (hipStream_t)p.hip_stream;
@@ -505,10 +515,18 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
         c->h_lo = (uint16_t *)c->mem.get(T * Fp * 2);
         c->part = (float *)c->mem.get(T * h.n_head * c->max_chunks * hd * 4);
         c->ml = (float *)c->mem.get(T * h.n_head * c->max_chunks * 2 * 4);
+        // K-split partial tiles of the ubatch GEMMs (the largest any matrix uses)
+        size_t ws = 0;
+        for (const Layer &L : m->layers)
+            for (const QMat *w : {&L.wqkv, &L.wo, &L.wgu, &L.wdown}) ws = std::max(ws, gemm_workspace_bytes(*w, (int)T));
+        ws = std::max(ws, gemm_workspace_bytes(m->out, (int)T));
+        c->gws_bytes = ws;
+        c->gws = ws ? (float *)c->mem.get(ws) : nullptr;
         c->logits = (float *)c->mem.get((size_t)c->n_out_cap * V * 4);
         c->amax = (int32_t *)c->mem.get((size_t)c->n_out_cap * 4);
         c->dev_step = (int32_t *)c->mem.get((size_t)c->step_cap * 3 * 4);
         ok = c->rope_cs && c->x && c->xn && c->xn_lo && c->q && c->o && c->h && c->o_lo && c->h_lo && c->part && c->ml && c->logits &&
+             (c->gws || !c->gws_bytes) &&
              c->amax && c->dev_step;
     }
     if (ok) HIP_OK(hipHostMalloc((void **)&c->host_step, (size_t)c->step_cap * 3 * 4, 0), ok = false);
@@ -561,12 +579,12 @@ static bool wait_staging(dec_ctx *c) {
     return true;
 }
 
+// Copies the call's token ids, positions and sequence ids ([3][n] int32,
+// packed at the start of the pinned staging buffer) to the device in one copy.
 static bool stage_step(dec_ctx *c, int n) {
-    const size_t cap = (size_t)c->step_cap;
-    for (int k = 0; k < 3; k++)
-        HIP_OK(hipMemcpyAsync(c->dev_step + k * cap, c->host_step + k * cap, (size_t)n * 4,
-                              hipMemcpyHostToDevice, c->s),
-               return false);
+    c->step_stride = n;
+    HIP_OK(hipMemcpyAsync(c->dev_step, c->host_step, (size_t)n * 3 * 4, hipMemcpyHostToDevice, c->s),
+           return false);
     HIP_OK(hipEventRecord(c->staged, c->s), return false);
     c->staged_pending = true;
     return true;
@@ -597,17 +615,17 @@ static bool stage(dec_ctx *c, int role, int layer, F &&f) {
 }
 
 // Enqueues the layers for T tokens whose ids / positions / sequences live at
-// dev_step + off (+cap, +2cap).  Output rows: `n_rows` rows starting at
+// dev_step + off (+n, +2n for the n tokens of the staged call).  Output rows: `n_rows` rows starting at
 // token row `row0` produce logits at logits row `out_row0`.
 static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out_row0) {
     dec_model *m = c->m;
     const dec_hparams &h = m->hp;
     const int d = h.n_embd, qd = m->qd, Fp = m->Fp, V = h.n_vocab;
-    const size_t cap = (size_t)c->step_cap;
+    const size_t stride = (size_t)c->step_stride;
     const int32_t *tok = c->dev_step + off;
     TokInfo ti;
-    ti.pos = c->dev_step + cap + off;
-    ti.seq = c->dev_step + 2 * cap + off;
+    ti.pos = c->dev_step + stride + off;
+    ti.seq = c->dev_step + 2 * stride + off;
     hipStream_t s = c->s;
     const bool mv = use_matvec(c, T);
     bool ok = true;
@@ -637,7 +655,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 return launch_matvec(L.wqkv, in, eq, T, s);
             }
             launch_rmsnorm(c->x, d, L.attn_norm, d, h.rms_eps, nullptr, T, c->xn, c->xn_lo, d, s);
-            return launch_gemm(L.wqkv, c->xn, c->xn_lo, d, eq, T, s);
+            return launch_gemm(L.wqkv, c->xn, c->xn_lo, d, eq, T, c->gws, c->gws_bytes, s);
         });
         AttnArgs at;
         at.q = c->q;
@@ -677,7 +695,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 in.ldx = qd;
                 return launch_matvec(L.wo, in, er, T, s);
             }
-            return launch_gemm(L.wo, c->o, c->o_lo, qd, er, T, s);
+            return launch_gemm(L.wo, c->o, c->o_lo, qd, er, T, c->gws, c->gws_bytes, s);
         });
         EpiArgs eg;
         eg.epi = EPI_SWIGLU;
@@ -694,7 +712,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 return launch_matvec(L.wgu, in, eg, T, s);
             }
             launch_rmsnorm(c->x, d, L.ffn_norm, d, h.rms_eps, nullptr, T, c->xn, c->xn_lo, d, s);
-            return launch_gemm(L.wgu, c->xn, c->xn_lo, d, eg, T, s);
+            return launch_gemm(L.wgu, c->xn, c->xn_lo, d, eg, T, c->gws, c->gws_bytes, s);
         });
         ok = ok && stage(c, DEC_K_FFN_DOWN, l, [&] {
             if (mv) {
@@ -704,7 +722,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 in.ldx = Fp;
                 return launch_matvec(L.wdown, in, er, T, s);
             }
-            return launch_gemm(L.wdown, c->h, c->h_lo, Fp, er, T, s);
+            return launch_gemm(L.wdown, c->h, c->h_lo, Fp, er, T, c->gws, c->gws_bytes, s);
         });
     }
     if (ok && n_rows > 0) {
@@ -723,7 +741,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
             }
             launch_rmsnorm(c->x + (size_t)row0 * d, d, m->out_norm, d, h.rms_eps, nullptr, n_rows, c->xn,
                            c->xn_lo, d, s);
-            return launch_gemm(m->out, c->xn, c->xn_lo, d, eo, n_rows, s);
+            return launch_gemm(m->out, c->xn, c->xn_lo, d, eo, n_rows, c->gws, c->gws_bytes, s);
         });
         ok = ok && stage(c, -1, -1, [&] {
             launch_argmax(c->logits + (size_t)out_row0 * V, V, n_rows, c->amax + out_row0, s);
@@ -755,11 +773,10 @@ extern "C" int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int
         return 1;   // cells are reserved for the whole batch up front: nothing changes
     }
     if (!wait_staging(c)) return -3;
-    const size_t cap = (size_t)c->step_cap;
     for (int i = 0; i < n; i++) {
         c->host_step[i] = tokens[i];
-        c->host_step[cap + i] = p0 + i;
-        c->host_step[2 * cap + i] = seq;
+        c->host_step[n + i] = p0 + i;
+        c->host_step[2 * n + i] = seq;
     }
     if (!stage_step(c, n)) return -3;
     c->st.n_prefill_calls++;
@@ -823,11 +840,10 @@ extern "C" int32_t dec_decode(dec_ctx *c, const int32_t *tokens, const int32_t *
         if (c->pos_max[sq] + 1 >= c->n_ctx) return 1;
     }
     if (!wait_staging(c)) return -3;
-    const size_t cap = (size_t)c->step_cap;
     for (int i = 0; i < n; i++) {
         c->host_step[i] = tokens[i];
-        c->host_step[cap + i] = c->pos_max[seq_ids[i]] + 1;
-        c->host_step[2 * cap + i] = seq_ids[i];
+        c->host_step[n + i] = c->pos_max[seq_ids[i]] + 1;
+        c->host_step[2 * n + i] = seq_ids[i];
     }
     if (!stage_step(c, n)) return -3;
     // The first step of a shape runs kernel by kernel: every kernel it uses is

@@ -193,8 +193,8 @@ bool launch_flash_prefill(const FlashArgs &a, hipStream_t s) {
     const int Gb = G < 4 ? G : 4, Tb = 4 / Gb;
     const dim3 grid((a.T + 32 * Tb - 1) / (32 * Tb), a.kv.n_kv, G / Gb);
     switch (a.kv.hd) {
-    case 64: hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, s, a); return true;
-    case 128: hipLaunchKernelGGL(k_flash_prefill<128>, grid, dim3(256), 0, s, a); return true;
+    case 64: launch(k_flash_prefill<64>, grid, dim3(256), 0, s, a); return true;
+    case 128: launch(k_flash_prefill<128>, grid, dim3(256), 0, s, a); return true;
     default: return false;
     }
 }

@@ -8,19 +8,28 @@
 // (2 k-halves x hi/lo) accumulate into a temporary tile that is then scaled
 // by the row's block scale and added to the fp32 result: C += d[n][kb] * T.
 //
-// A 256-thread block computes 128 output features x BM tokens; each
-// wavefront owns a 64 x BM/2 sub-tile.  Codes, activations and scales of a
-// K block are staged in LDS with two stages, so one barrier per K block
-// suffices: the next block's global loads are in flight during the MFMAs and
-// land in the other stage afterwards.  Blocks that share a weight tile are
-// placed on the same XCD (block ids go round-robin over the 8 XCDs), so the
-// tile is fetched from HBM once into that XCD's L2.
+// A 256-thread block computes BN = 128 output features x BM tokens; each
+// wavefront owns a 64 x BM/2 sub-tile.  Pipeline per K block (32 k):
+//   * global loads of codes, scale and both activation parts go to
+//     registers two K blocks ahead (two register sets, the loop unrolled by
+//     two so that each set has fixed registers);
+//   * a K block is converted (codes -> f16) and written to one of two LDS
+//     stages while the other stage feeds the MFMAs; one barrier per K block.
+// Rows of an LDS tile are 40 f16 (80 bytes) apart, so the 16-byte fragment
+// reads of 8 consecutive rows hit disjoint banks.
+// Blocks that share a weight tile are placed on the same XCD (block ids go
+// round-robin over the 8 XCDs), so the tile is fetched from HBM once into
+// that XCD's L2.  When the tile grid is too small to fill the chip (the
+// d x d and d x F matrices at 512 tokens), K is split over 2 or 4 blocks
+// that write fp32 partial tiles; a second kernel adds them in a fixed order
+// and applies the epilogue, so results do not depend on timing.
 // Operand layouts (checked on the device): lane l supplies A[l%32][8(l/32)+e]
 // and B[8(l/32)+e][l%32]; accumulator r of lane l is C[(r/4)*8+(l/32)*4+r%4][l%32].
-// A is the code tile (rows = features), B the activations transposed
-// (columns = tokens), so a lane's accumulators are four runs of 4
-// consecutive features of one token -- RoPE pairs and gate/up pairs meet in
-// one lane and the shared epilogue applies directly.
+// A is the activation tile (rows = tokens) and B the code tile transposed
+// (columns = features): a lane's 16 accumulators of a tile are 16 tokens of
+// ONE feature, so the block scale it applies is a single value per tile.
+// In the epilogue gate/up pairs (feature tiles 32 apart) meet in one lane;
+// RoPE pairs (adjacent features) sit in lanes l and l^1 and are exchanged.
 //
 // Fallback path (fp32 weights, or shapes the MFMA tiling does not cover):
 // one thread per (row pair, token), plain fp32 FMA.
@@ -33,99 +42,129 @@ namespace {
 constexpr int BN = 128;
 constexpr int LDS_STRIDE = 40;   // f16 elements per LDS row (32 + 8 pad)
 
-// 16 codes (half `hb` of a 32-weight block) as exact f16 values.
-template <int WT>
-DEV void codes16(uint4 raw, int hb, h2 *out) {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    if (WT == T_Q4_0) {
-        // codes 16*hb .. 16*hb+15: low (hb=0) or high (hb=1) nibbles of bytes 0..15
-        const h2 off = h2{(f16)1032.f, (f16)1032.f};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t m = (w[i] >> (4 * hb)) & 0x0F0F0F0Fu;
-            const uint32_t p0 = (m & 0x000000FFu) | ((m << 8) & 0x00FF0000u);
-            const uint32_t p1 = ((m >> 16) & 0x000000FFu) | ((m >> 8) & 0x00FF0000u);
-            out[2 * i + 0] = as_h2(p0 | 0x64006400u) - off;
-            out[2 * i + 1] = as_h2(p1 | 0x64006400u) - off;
-        }
-    } else {
-        // codes 16*hb .. 16*hb+15 are the bytes of raw (signed)
-        const h2 off = h2{(f16)1152.f, (f16)1152.f};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t u = w[i] ^ 0x80808080u;
-            const uint32_t p0 = (u & 0x000000FFu) | ((u << 8) & 0x00FF0000u);
-            const uint32_t p1 = ((u >> 16) & 0x000000FFu) | ((u >> 8) & 0x00FF0000u);
-            out[2 * i + 0] = as_h2(p0 | 0x64006400u) - off;
-            out[2 * i + 1] = as_h2(p1 | 0x64006400u) - off;
-        }
-    }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// f16 pairs {1024 + byte0, 1024 + byte1} and {1024 + byte2, 1024 + byte3}
+// of a word whose bytes are all below 0x400 - 1024 (v_perm_b32).
+DEV h2 magic_lo(uint32_t v) { return as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04010400u)); }
+DEV h2 magic_hi(uint32_t v) { return as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04030402u)); }
+
+// Q4_0: the 8 bytes at offset 8h of a block hold codes 8h..8h+7 (low
+// nibbles) and 16+8h..16+8h+7 (high nibbles); out0/out1 get them as exact
+// f16 values q - 8.
+DEV void q4_codes(u32x2 raw, h8 &out0, h8 &out1) {
+    const h2 off = h2{(f16)1032.f, (f16)1032.f};
+    const uint32_t l0 = raw.x & 0x0F0F0F0Fu, l1 = raw.y & 0x0F0F0F0Fu;
+    const uint32_t u0 = (raw.x >> 4) & 0x0F0F0F0Fu, u1 = (raw.y >> 4) & 0x0F0F0F0Fu;
+    const h2 a0 = magic_lo(l0) - off, a1 = magic_hi(l0) - off, a2 = magic_lo(l1) - off, a3 = magic_hi(l1) - off;
+    const h2 b0 = magic_lo(u0) - off, b1 = magic_hi(u0) - off, b2 = magic_lo(u1) - off, b3 = magic_hi(u1) - off;
+    out0 = h8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+    out1 = h8{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
 }
 
-template <int WT, int BM, int EPI>
+// Q8_0: 16 signed byte codes as exact f16 values.
+DEV void q8_codes(u32x4 raw, h8 &out0, h8 &out1) {
+    const h2 off = h2{(f16)1152.f, (f16)1152.f};
+    const uint32_t w0 = raw.x ^ 0x80808080u, w1 = raw.y ^ 0x80808080u;
+    const uint32_t w2 = raw.z ^ 0x80808080u, w3 = raw.w ^ 0x80808080u;
+    const h2 a0 = magic_lo(w0) - off, a1 = magic_hi(w0) - off, a2 = magic_lo(w1) - off, a3 = magic_hi(w1) - off;
+    const h2 b0 = magic_lo(w2) - off, b1 = magic_hi(w2) - off, b2 = magic_lo(w3) - off, b3 = magic_hi(w3) - off;
+    out0 = h8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+    out1 = h8{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+}
+
+// One K block of a block's operands, held in registers between its global
+// load and its LDS store.  Thread t covers weight row t/2, half t%2 of the
+// block, and XC 16-byte chunks of each activation part.
+// (clang vector types: HIP's uint4 is a struct whose copies are memcpys
+// that keep the stage out of registers)
+template <int WT, int XC>
+struct Stage {
+    u32x4 a;          // Q4_0: .x,.y = 8 bytes; Q8_0: 16 bytes
+    uint32_t d;       // f16 scale bits of row t/2 (even threads)
+    u32x4 xh[XC], xl[XC];
+};
+
+template <int WT, int BM, int EPI, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh, const uint16_t *Xl,
-                                                      int ldx, EpiArgs ep, int M, int pair_mode, int NT) {
-    constexpr int MT = BM / 64;   // 32x32 m-tiles per wavefront
+                                                      int ldx, EpiArgs ep, int M, int pair_mode, int NT,
+                                                      int nsplit, float *part) {
+    constexpr int MT = BM / 64;                         // 32x32 token tiles per wavefront
+    constexpr int XC = BM * 4 / 256 > 0 ? BM * 4 / 256 : 1;   // activation chunks per thread and part
+    constexpr bool XALL = BM * 4 >= 256;                // every thread loads activations
     __shared__ __attribute__((aligned(16))) f16 As[2][BN * LDS_STRIDE];
     __shared__ __attribute__((aligned(16))) f16 Bh[2][BM * LDS_STRIDE];
     __shared__ __attribute__((aligned(16))) f16 Bl[2][BM * LDS_STRIDE];
     __shared__ __attribute__((aligned(16))) float Sc[2][BN];
 
-    // block -> (feature tile, token tile); tiles of one feature tile share an XCD
+    // block -> (feature tile, token tile, K split); the tiles of one feature
+    // tile (all token tiles and splits) share an XCD
     const int mtiles = (M + BM - 1) / BM;
+    const int per_nt = mtiles * nsplit;
     const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
-    const int nt = (j / mtiles) * 8 + xcd, mtile = j % mtiles;
+    const int nt = (j / per_nt) * 8 + xcd, rem = j % per_nt;
+    const int mtile = rem % mtiles, split = rem / mtiles;
     if (nt >= NT) return;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n0 = nt * BN, m0 = mtile * BM;
-    const int K = W.K, nb = K >> 5;
+    const int nb_all = W.K >> 5, nb = nb_all / nsplit, kb0 = split * nb;
     const int wn = (w & 1) * 64, wm = (w >> 1) * (BM / 2);
 
     // loader roles
-    const int a_row = tid >> 1, a_half = tid & 1;      // one half-block of one weight row
-    constexpr int XCH = BM * 4;                         // 16-byte chunks of one activation tile
-    constexpr int XPT = (XCH + 255) / 256;              // chunks per thread (per part)
-    const size_t qrow_bytes = WT == T_Q4_0 ? (size_t)(K >> 1) : (size_t)K;
-    const uint8_t *qbase = (const uint8_t *)W.qs + (size_t)(n0 + a_row) * qrow_bytes;
-    const uint16_t *dbase = W.d + (size_t)(n0 + a_row) * nb;
-
-    uint4 araw;
-    uint16_t adb;
-    uint4 xh[XPT], xl[XPT];
-    auto gload = [&](int kb) {
-        if (WT == T_Q4_0)
-            araw = *(const uint4 *)(qbase + (size_t)kb * 16);
-        else
-            araw = *(const uint4 *)(qbase + (size_t)kb * 32 + a_half * 16);
-        adb = dbase[kb];
+    const int a_row = tid >> 1, a_half = tid & 1;
+    const size_t qrow_bytes = WT == T_Q4_0 ? (size_t)(W.K >> 1) : (size_t)W.K;
+    const uint8_t *qbase = (const uint8_t *)W.qs + (size_t)(n0 + a_row) * qrow_bytes +
+                           (WT == T_Q4_0 ? a_half * 8 : a_half * 16);
+    const uint16_t *dbase = W.d + (size_t)(n0 + a_row) * nb_all;
+    const bool x_loader = XALL || tid < BM * 4;
+    const uint16_t *xh_src[XC], *xl_src[XC];
+    int x_lds[XC];
 #pragma unroll
-        for (int c = 0; c < XPT; c++) {
-            const int ch = tid + c * 256;
-            const int mr = ch >> 2, kc = ch & 3;
-            if (ch < XCH && m0 + mr < M) {
-                const size_t off = (size_t)(m0 + mr) * ldx + kb * 32 + kc * 8;
-                xh[c] = *(const uint4 *)(Xh + off);
-                xl[c] = *(const uint4 *)(Xl + off);
-            } else {
-                xh[c] = xl[c] = make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < XC; c++) {
+        const int ch = (XALL ? tid + c * 256 : tid);
+        const int mr = ch >> 2, kc = ch & 3;
+        const int row = min(m0 + mr, M - 1);            // rows past M load row M-1; their outputs are dropped
+        xh_src[c] = Xh + (size_t)row * ldx + kc * 8;
+        xl_src[c] = Xl + (size_t)row * ldx + kc * 8;
+        x_lds[c] = mr * LDS_STRIDE + kc * 8;
+    }
+
+    auto gload = [&](Stage<WT, XC> &r, int kb) __attribute__((always_inline)) {
+        const int k = kb0 + kb;
+        if (WT == T_Q4_0) {
+            const u32x2 v = *(const u32x2 *)(qbase + (size_t)k * 16);
+            r.a = u32x4{v.x, v.y, 0u, 0u};
+        } else {
+            r.a = *(const u32x4 *)(qbase + (size_t)k * 32);
+        }
+        r.d = dbase[k];
+        if (x_loader) {
+#pragma unroll
+            for (int c = 0; c < XC; c++) {
+                r.xh[c] = *(const u32x4 *)(xh_src[c] + k * 32);
+                r.xl[c] = *(const u32x4 *)(xl_src[c] + k * 32);
             }
         }
     };
-    auto lstore = [&](int st) {
-        h2 v[8];
-        codes16<WT>(araw, a_half, v);
-        uint4 *dst = (uint4 *)(&As[st][a_row * LDS_STRIDE + a_half * 16]);
-        dst[0] = __builtin_bit_cast(uint4, *(h8 *)&v[0]);
-        dst[1] = __builtin_bit_cast(uint4, *(h8 *)&v[4]);
-        if (a_half == 0) Sc[st][a_row] = f16_bits_to_f32(adb);
+    auto lstore = [&](const Stage<WT, XC> &r, int st) __attribute__((always_inline)) {
+        h8 c0, c1;
+        f16 *arow = &As[st][a_row * LDS_STRIDE];
+        if (WT == T_Q4_0) {
+            q4_codes(u32x2{r.a.x, r.a.y}, c0, c1);
+            *(h8 *)(arow + 8 * a_half) = c0;           // codes 8h .. 8h+7
+            *(h8 *)(arow + 16 + 8 * a_half) = c1;      // codes 16+8h .. 16+8h+7
+        } else {
+            q8_codes(r.a, c0, c1);
+            *(h8 *)(arow + 16 * a_half) = c0;          // codes 16h .. 16h+7
+            *(h8 *)(arow + 16 * a_half + 8) = c1;      // codes 16h+8 .. 16h+15
+        }
+        if (a_half == 0) Sc[st][a_row] = f16_bits_to_f32((uint16_t)r.d);
+        if (x_loader) {
 #pragma unroll
-        for (int c = 0; c < XPT; c++) {
-            const int ch = tid + c * 256;
-            if (ch < XCH) {
-                const int mr = ch >> 2, kc = ch & 3;
-                *(uint4 *)(&Bh[st][mr * LDS_STRIDE + kc * 8]) = xh[c];
-                *(uint4 *)(&Bl[st][mr * LDS_STRIDE + kc * 8]) = xl[c];
+            for (int c = 0; c < XC; c++) {
+                *(u32x4 *)(&Bh[st][x_lds[c]]) = r.xh[c];
+                *(u32x4 *)(&Bl[st][x_lds[c]]) = r.xl[c];
             }
         }
     };
@@ -138,81 +177,148 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[a][b][r] = 0.f;
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kb = 0; kb < nb; kb++) {
-        const int st = kb & 1;
-        if (kb + 1 < nb) gload(kb + 1);
+    auto compute = [&](int st) __attribute__((always_inline)) {
         f16x tmp[2][MT];
 #pragma unroll
-        for (int a = 0; a < 2; a++)
-#pragma unroll
-            for (int b = 0; b < MT; b++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) tmp[a][b][r] = 0.f;
-#pragma unroll
         for (int kk = 0; kk < 32; kk += 16) {
-            h8 af[2], bh[MT], bl[MT];
+            h8 cf[2], xh[MT], xl[MT];
 #pragma unroll
             for (int a = 0; a < 2; a++)
-                af[a] = *(const h8 *)(&As[st][(wn + 32 * a + (lane & 31)) * LDS_STRIDE + kk + 8 * (lane >> 5)]);
+                cf[a] = *(const h8 *)(&As[st][(wn + 32 * a + (lane & 31)) * LDS_STRIDE + kk + 8 * (lane >> 5)]);
 #pragma unroll
             for (int b = 0; b < MT; b++) {
                 const int off = (wm + 32 * b + (lane & 31)) * LDS_STRIDE + kk + 8 * (lane >> 5);
-                bh[b] = *(const h8 *)(&Bh[st][off]);
-                bl[b] = *(const h8 *)(&Bl[st][off]);
+                xh[b] = *(const h8 *)(&Bh[st][off]);
+                xl[b] = *(const h8 *)(&Bl[st][off]);
             }
+            // consecutive MFMAs write different tiles
 #pragma unroll
             for (int a = 0; a < 2; a++)
 #pragma unroll
-                for (int b = 0; b < MT; b++) {
-                    tmp[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bh[b], tmp[a][b], 0, 0, 0);
-                    tmp[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bl[b], tmp[a][b], 0, 0, 0);
-                }
+                for (int b = 0; b < MT; b++)
+                    tmp[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[b], cf[a], kk ? tmp[a][b] : f16x{}, 0, 0, 0);
+#pragma unroll
+            for (int a = 0; a < 2; a++)
+#pragma unroll
+                for (int b = 0; b < MT; b++)
+                    tmp[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[b], cf[a], tmp[a][b], 0, 0, 0);
         }
-        // C += d[n][kb] * T: the lane's 16 rows of n-tile a are four runs of 4
+        // C += d[n][kb] * T: one scale per lane and feature tile
 #pragma unroll
         for (int a = 0; a < 2; a++) {
-            float sc[16];
-#pragma unroll
-            for (int r4 = 0; r4 < 4; r4++) {
-                const float4 v = *(const float4 *)(&Sc[st][wn + 32 * a + r4 * 8 + (lane >> 5) * 4]);
-                sc[4 * r4 + 0] = v.x; sc[4 * r4 + 1] = v.y; sc[4 * r4 + 2] = v.z; sc[4 * r4 + 3] = v.w;
-            }
+            const float sc = Sc[st][wn + 32 * a + (lane & 31)];
 #pragma unroll
             for (int b = 0; b < MT; b++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) acc[a][b][r] += sc[r] * tmp[a][b][r];
+                for (int r = 0; r < 16; r++) acc[a][b][r] += sc * tmp[a][b][r];
         }
-        if (kb + 1 < nb) lstore(st ^ 1);
+    };
+
+    // Loads past the last K block re-read the last one (their data is never
+    // used), so no load sits behind a branch: the compiler can then wait for
+    // exactly the register set a store needs and leave the other in flight.
+    Stage<WT, XC> r0, r1;
+    gload(r0, 0);
+    gload(r1, min(1, nb - 1));
+    lstore(r0, 0);
+    __syncthreads();
+    gload(r0, min(2, nb - 1));
+    for (int kb = 0; kb < nb; kb += 2) {
+        compute(0);                                     // K block kb from stage 0
+        if (kb + 1 >= nb) break;
+        lstore(r1, 1);                                  // K block kb+1 -> stage 1
         __syncthreads();
+        gload(r1, min(kb + 3, nb - 1));
+        compute(1);                                     // K block kb+1
+        lstore(r0, 0);                                  // K block kb+2 -> stage 0 (unused past the end)
+        __syncthreads();
+        gload(r0, min(kb + 4, nb - 1));
     }
 
     // ---- epilogue ----
+    // lane: feature f = n0 + wn + 32a + (lane & 31); token of accumulator r:
+    // m = m0 + wm + 32b + (r/4)*8 + (lane/32)*4 + r%4
+    const int fl = lane & 31;
+    if (SPLIT) {
+        // fp32 partial tile of this split: part[split][m][n]
+        const int N = W.N;
+#pragma unroll
+        for (int b = 0; b < MT; b++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm + 32 * b + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (m >= M) continue;
+                float *dst = part + ((size_t)split * M + m) * N + n0 + wn + fl;
+                dst[0] = acc[0][b][r];
+                dst[32] = acc[1][b][r];
+            }
+        return;
+    }
 #pragma unroll
     for (int b = 0; b < MT; b++) {
-        const int m = m0 + wm + 32 * b + (lane & 31);
-        if (m >= M) continue;
-        if (pair_mode == PAIR_GU) {
-            // wavefront covers 64 stored rows = 32 gate rows then their 32 up rows
+        const int mb = m0 + wm + 32 * b + (lane >> 5) * 4;
+        if (EPI == EPI_STORE || EPI == EPI_RESID) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = mb + (r >> 2) * 8 + (r & 3);
+                if (m >= M) continue;
+                float *y = ep.y + (size_t)m * ep.ldy + n0 + wn + fl;
+                if (EPI == EPI_STORE) {
+                    y[0] = acc[0][b][r];
+                    y[32] = acc[1][b][r];
+                } else {
+                    y[0] += acc[0][b][r];
+                    y[32] += acc[1][b][r];
+                }
+            }
+        } else if (pair_mode == PAIR_GU) {
+            // gate rows n0+wn .. +31 and their up rows n0+wn+32 .. +63: feature (g*32 + fl)
             const int g = (n0 + wn) >> 6;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int i = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int r0 = ((g << 6) + i);
-                epi_pair<EPI>(ep, m, (g << 5) + i, r0, r0 + 32, acc[0][b][r], acc[1][b][r]);
+                const int m = mb + (r >> 2) * 8 + (r & 3);
+                if (m >= M) continue;
+                const int rr = (g << 6) + fl;
+                epi_pair<EPI>(ep, m, (g << 5) + fl, rr, rr + 32, acc[0][b][r], acc[1][b][r]);
             }
         } else {
+            // adjacent features f (even lane) and f+1 (odd lane): the even lane
+            // takes tokens r < 8 of the pair, the odd lane tokens r >= 8
+            const bool odd = lane & 1;
 #pragma unroll
             for (int a = 0; a < 2; a++)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const int n = n0 + wn + 32 * a + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                    epi_pair<EPI>(ep, m, n >> 1, n, n + 1, acc[a][b][r], acc[a][b][r + 1]);
+                for (int r = 0; r < 8; r++) {
+                    const float send = odd ? acc[a][b][r] : acc[a][b][r + 8];
+                    const float recv = __shfl_xor(send, 1, 64);
+                    const int rr = odd ? r + 8 : r;
+                    const int m = mb + (rr >> 2) * 8 + (rr & 3);
+                    const int f = n0 + wn + 32 * a + (fl & ~1);
+                    const float va = odd ? recv : acc[a][b][r];
+                    const float vb = odd ? acc[a][b][r + 8] : recv;
+                    if (m < M) epi_pair<EPI>(ep, m, f >> 1, f, f + 1, va, vb);
                 }
         }
     }
+}
+
+// Sums the K-split partial tiles in split order and applies the epilogue;
+// one thread per (row pair, token).
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_splitk_sum(const float *part, int nsplit, int N, int M,
+                                                         EpiArgs ep, int pair_mode) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    const int m = blockIdx.y;
+    if (p >= N / 2 || m >= M) return;
+    int r0, r1;
+    pair_rows(pair_mode, p, r0, r1);
+    float a = 0.f, b = 0.f;
+    for (int s = 0; s < nsplit; s++) {
+        const float *row = part + ((size_t)s * M + m) * N;
+        a += row[r0];
+        b += row[r1];
+    }
+    epi_pair<EPI>(ep, m, p, r0, r1, a, b);
 }
 
 // fp32 weights (any K), f16 activations; one thread per (row pair, token).
@@ -237,51 +343,91 @@ __global__ __launch_bounds__(256) void k_gemm_f32(QMat W, const uint16_t *X, con
     epi_pair<EPI>(ep, m, p, r0, r1, a, b);
 }
 
+int g_gemm_cu = 256;
+
+bool mfma_shape(const QMat &W, int ldx) {
+    return (W.wtype == T_Q4_0 || W.wtype == T_Q8_0) && W.N % BN == 0 && W.K % 32 == 0 && ldx % 8 == 0;
+}
+
+// K splits for M tokens: only when the tile grid leaves resident block slots
+// (2 per CU) empty, the largest of 2 and 4 that still fits one round of
+// slots, each split keeping >= 16 K blocks.  (Splitting a grid that already
+// fills the chip only adds partial-tile traffic.)
+int split_for(const QMat &W, int M) {
+    const int bm = M > 64 ? 128 : 64;
+    const long tiles = (long)(W.N / BN) * ((M + bm - 1) / bm);
+    const long slots = 2L * g_gemm_cu;
+    const int nb = W.K / 32;
+    int best = 1;
+    for (int S = 2; S <= 4; S *= 2)
+        if (tiles * S <= slots && nb % S == 0 && nb / S >= 16) best = S;
+    return best;
+}
+
 template <int WT, int EPI>
 void launch_mfma_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
-                     int M, int pair_mode, hipStream_t s) {
+                     int M, int pair_mode, int S, float *ws, hipStream_t s) {
     const int NT = W.N / BN, NT8 = (NT + 7) / 8 * 8;
-    if (M > 64) {
-        const int mt = (M + 127) / 128;
-        hipLaunchKernelGGL((k_gemm_mfma<WT, 128, EPI>), dim3(NT8 * mt), dim3(256), 0, s, W, Xh, Xl, ldx,
-                           ep, M, pair_mode, NT);
+    const int bm = M > 64 ? 128 : 64;
+    const dim3 grid(NT8 * ((M + bm - 1) / bm) * S);
+    if (S > 1) {
+        if (bm == 128)
+            launch((k_gemm_mfma<WT, 128, EPI, true>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode,
+                   NT, S, ws);
+        else
+            launch((k_gemm_mfma<WT, 64, EPI, true>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode,
+                   NT, S, ws);
+        launch(k_gemm_splitk_sum<EPI>, dim3((W.N / 2 + 255) / 256, M), dim3(256), 0, s, (const float *)ws, S,
+               W.N, M, ep, pair_mode);
+    } else if (bm == 128) {
+        launch((k_gemm_mfma<WT, 128, EPI, false>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT,
+               1, (float *)nullptr);
     } else {
-        const int mt = (M + 63) / 64;
-        hipLaunchKernelGGL((k_gemm_mfma<WT, 64, EPI>), dim3(NT8 * mt), dim3(256), 0, s, W, Xh, Xl, ldx,
-                           ep, M, pair_mode, NT);
+        launch((k_gemm_mfma<WT, 64, EPI, false>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT,
+               1, (float *)nullptr);
     }
 }
 
 template <int WT>
 void launch_mfma(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
-                 int M, int pair_mode, hipStream_t s) {
+                 int M, int pair_mode, int S, float *ws, hipStream_t s) {
     switch (ep.epi) {
-    case EPI_STORE: launch_mfma_epi<WT, EPI_STORE>(W, Xh, Xl, ldx, ep, M, pair_mode, s); break;
-    case EPI_RESID: launch_mfma_epi<WT, EPI_RESID>(W, Xh, Xl, ldx, ep, M, pair_mode, s); break;
-    case EPI_QKV: launch_mfma_epi<WT, EPI_QKV>(W, Xh, Xl, ldx, ep, M, pair_mode, s); break;
-    case EPI_SWIGLU: launch_mfma_epi<WT, EPI_SWIGLU>(W, Xh, Xl, ldx, ep, M, pair_mode, s); break;
+    case EPI_STORE: launch_mfma_epi<WT, EPI_STORE>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_RESID: launch_mfma_epi<WT, EPI_RESID>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_QKV: launch_mfma_epi<WT, EPI_QKV>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_SWIGLU: launch_mfma_epi<WT, EPI_SWIGLU>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
     }
 }
 
 template <int EPI>
 void launch_f32_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
                     int M, int pair_mode, hipStream_t s) {
-    hipLaunchKernelGGL(k_gemm_f32<EPI>, dim3((W.N / 2 + 255) / 256, M), dim3(256), 0, s, W, Xh, Xl, ldx,
+    launch(k_gemm_f32<EPI>, dim3((W.N / 2 + 255) / 256, M), dim3(256), 0, s, W, Xh, Xl, ldx,
                        ep, M, pair_mode);
 }
 
 }  // namespace
 
+void gemm_set_num_cu(int n) { g_gemm_cu = n > 0 ? n : 256; }
+
+size_t gemm_workspace_bytes(const QMat &W, int M) {
+    if (M <= 0 || !mfma_shape(W, 8)) return 0;
+    const int S = split_for(W, M);
+    return S > 1 ? (size_t)S * M * W.N * 4 : 0;
+}
+
 bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
-                 int M, hipStream_t s) {
+                 int M, float *ws, size_t ws_bytes, hipStream_t s) {
     if (M <= 0 || W.N % 2 || !Xh || !Xl) return false;
     const int pair_mode = ep.epi == EPI_SWIGLU ? PAIR_GU : PAIR_ADJ;
     if (pair_mode == PAIR_GU && W.N % 64) return false;
-    if ((W.wtype == T_Q4_0 || W.wtype == T_Q8_0) && W.N % BN == 0 && W.K % 32 == 0 && ldx % 8 == 0) {
+    if (mfma_shape(W, ldx)) {
+        int S = split_for(W, M);
+        while (S > 1 && (!ws || (size_t)S * M * W.N * 4 > ws_bytes)) S >>= 1;
         if (W.wtype == T_Q4_0)
-            launch_mfma<T_Q4_0>(W, Xh, Xl, ldx, ep, M, pair_mode, s);
+            launch_mfma<T_Q4_0>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
         else
-            launch_mfma<T_Q8_0>(W, Xh, Xl, ldx, ep, M, pair_mode, s);
+            launch_mfma<T_Q8_0>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
         return true;
     }
     if (W.wtype != T_F32) return false;

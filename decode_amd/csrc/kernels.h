@@ -1,8 +1,31 @@
 // kernels.h -- argument structs and host launchers of the libdecode kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+// Timing of one selected launch.  While `armed`, launch() hands the events to
+// hipExtLaunchKernel, which stamps them with the kernel's own start and end:
+// the first launch takes e0 as its start event, every launch records e1 at
+// its end, so e0..e1 spans the kernels of one probed unit (no event packets
+// of their own in the interval).
+struct LaunchProbe {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    bool armed = false;
+};
+extern thread_local LaunchProbe g_launch_probe;
+
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s, Args... args) {
+    LaunchProbe &p = g_launch_probe;
+    if (p.armed) {
+        hipExtLaunchKernelGGL(kernel, grid, block, shm, s, p.e0, p.e1, 0, args...);
+        p.e0 = nullptr;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
+    }
+}
 
 // One stored (possibly fused) weight matrix [N][K], row-major.
 //   F32 : qs = float[N][K]
@@ -85,9 +108,15 @@ void matvec_set_num_cu(int n);
 bool launch_matvec(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, hipStream_t s);
 // Y = X W^T for T tokens (prefill / batched decode), X = Xh + Xl given as two
 // f16 arrays [T][ldx] (value and rounding remainder): MFMA for Q8_0 / Q4_0
-// with N % 128 == 0, a plain fp32 kernel otherwise.
+// with N % 128 == 0, a plain fp32 kernel otherwise.  `ws` (ws_bytes) holds
+// the fp32 partial tiles of a K split; with too little workspace (or none)
+// the GEMM splits K less (or not at all).
 bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
-                 int T, hipStream_t s);
+                 int T, float *ws, size_t ws_bytes, hipStream_t s);
+// Workspace launch_gemm uses for W at T tokens (0 when it does not split K).
+size_t gemm_workspace_bytes(const QMat &W, int T);
+// Number of compute units the GEMM grid is sized for (default 256).
+void gemm_set_num_cu(int n);
 
 // x[t] = dequantized row tok[t] of the embedding table (f32).
 void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, hipStream_t s);

@@ -346,7 +346,7 @@ bool launch_epi(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int p
     const int npairs = W.N / 2;
     int blocks = (npairs + G - 1) / G;
     if (blocks > g_num_cu) blocks = g_num_cu;
-    hipLaunchKernelGGL((k_matvec<WT, KB, S, EPI>), dim3(blocks, T), dim3(NW * 64), 0, s, W, in, ep,
+    launch((k_matvec<WT, KB, S, EPI>), dim3(blocks, T), dim3(NW * 64), 0, s, W, in, ep,
                        pair_mode);
     return true;
 }

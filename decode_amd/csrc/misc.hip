@@ -200,32 +200,32 @@ __global__ __launch_bounds__(256) void k_rope_table(float *cs, int n_ctx, int hd
 void launch_quantize(const float *src, int rows, int K, QMat &m, int mode, int row_off,
                      hipStream_t s) {
     const long long n = (long long)rows * (K / 32);
-    hipLaunchKernelGGL(k_quantize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows, K, m,
+    launch(k_quantize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows, K, m,
                        mode, row_off);
 }
 
 void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, int row_off,
                      hipStream_t s) {
     const long long n = (long long)rows * K_src;
-    hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows, K_src,
+    launch(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows, K_src,
                        m, mode, row_off);
 }
 
 void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, hipStream_t s) {
-    hipLaunchKernelGGL(k_embed, dim3(T), dim3(256), 0, s, E, tok, x, ldx);
+    launch(k_embed, dim3(T), dim3(256), 0, s, E, tok, x, ldx);
 }
 
 void launch_rmsnorm(const float *x, int ldx, const float *g, int d, float eps,
                     const int32_t *row_idx, int T, uint16_t *xn, uint16_t *xl, int ldn, hipStream_t s) {
-    hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), 0, s, x, ldx, g, d, eps, row_idx, xn, xl, ldn);
+    launch(k_rmsnorm, dim3(T), dim3(256), 0, s, x, ldx, g, d, eps, row_idx, xn, xl, ldn);
 }
 
 void launch_argmax(const float *logits, int V, int T, int32_t *out, hipStream_t s) {
-    hipLaunchKernelGGL(k_argmax, dim3(T), dim3(1024), 0, s, logits, V, out);
+    launch(k_argmax, dim3(T), dim3(1024), 0, s, logits, V, out);
 }
 
 void launch_rope_table(float *cs, int n_ctx, int hd, float base, hipStream_t s) {
     const long long n = (long long)n_ctx * (hd / 2);
-    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, cs, n_ctx, hd,
+    launch(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, cs, n_ctx, hd,
                        base);
 }

@@ -189,16 +189,18 @@ enum { DEC_K_QKV = 0, DEC_K_ATTN = 1, DEC_K_WO = 2, DEC_K_FFN_GU = 3, DEC_K_FFN_
        DEC_K_OUTPUT = 5 };
 
 /* Timing probe (the article's per-node evaluation callback, step 13b, in
- * measuring form): HIP timing events are recorded on the context's stream
- * right before and after the launch(es) of kernel `role` in layer `layer`
- * (layer ignored for DEC_K_OUTPUT), in prefill ubatches and inside captured
- * decode steps.  role < 0 disables.  Setting the probe resets the totals;
+ * measuring form): the launch(es) of kernel `role` in layer `layer` (layer
+ * ignored for DEC_K_OUTPUT) go through hipExtLaunchKernel with a pair of HIP
+ * events, which take the start time of the first kernel and the end time of
+ * the last one.  Applies to prefill ubatches and to decode steps; a probed
+ * decode step replays its graph in two parts around the directly launched
+ * probed kernel.  role < 0 disables.  Setting the probe resets the totals;
  * choosing a different role or layer also drops captured decode graphs.
  * Returns 0, or -1 on bad arguments. */
 int32_t dec_set_probe(dec_ctx *c, int32_t role, int32_t layer);
 
-/* Probe totals since dec_set_probe: summed milliseconds between the two
- * events and the number of probed launches.  Synchronizes the stream.
+/* Probe totals since dec_set_probe: summed kernel milliseconds (first start
+ * to last end per probed unit) and the number of probed units.  Synchronizes the stream.
  * Returns 0, or -1 when no probe is set. */
 int32_t dec_get_probe(dec_ctx *c, double *total_ms, int64_t *count);
 
