@@ -37,25 +37,11 @@ namespace {
 // pairs (1024 + q[4i], 1024 + q[4i+2]) and (1024 + 16 q[4i+16], 1024 + 16
 // q[4i+18]) directly; the same masks on the dword shifted right by 8 give
 // codes 4i+1, 4i+3 and 16 q[4i+17], 16 q[4i+19].  All these values are exact
-// in f16.  xp[4i+0..3] hold the matching activation pairs.
-DEV void pairs_q4(const f16 *x, h2 *xp) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        xp[4 * i + 0] = h2{x[4 * i + 0], x[4 * i + 2]};
-        xp[4 * i + 1] = h2{x[16 + 4 * i + 0], x[16 + 4 * i + 2]};
-        xp[4 * i + 2] = h2{x[4 * i + 1], x[4 * i + 3]};
-        xp[4 * i + 3] = h2{x[16 + 4 * i + 1], x[16 + 4 * i + 3]};
-    }
-}
+// in f16.  So activation pairs 4i+0..3 are (x[4i], x[4i+2]), (x[16+4i],
+// x[16+4i+2]), (x[4i+1], x[4i+3]), (x[16+4i+1], x[16+4i+3]).
 // Q8_0 block dword i holds codes 4i..4i+3; after flipping the sign bits,
-// masks 0x00FF00FF at shifts 0 and 8 select (4i, 4i+2) and (4i+1, 4i+3).
-DEV void pairs_q8(const f16 *x, h2 *xp) {
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        xp[2 * i + 0] = h2{x[4 * i + 0], x[4 * i + 2]};
-        xp[2 * i + 1] = h2{x[4 * i + 1], x[4 * i + 3]};
-    }
-}
+// masks 0x00FF00FF at shifts 0 and 8 select (4i, 4i+2) and (4i+1, 4i+3):
+// activation pair 2i is (x[4i], x[4i+2]), pair 2i+1 is (x[4i+1], x[4i+3]).
 
 // Constants held in registers so that (w & mask) | magic issues as one
 // v_and_or_b32 (these VOP3 forms cannot encode literal constants).
@@ -78,7 +64,7 @@ DEV Masks make_masks() {
 //
 // Returns sum_A (1024 + q) x + sum_B (1024 + 16 q) x / 16 over the block, where
 // A are the low-nibble codes 0..15 and B the high-nibble codes 16..31.
-DEV float blockdot_q4(const uint4 q, const h2 *xp, const Masks &m) {
+DEV float blockdot_q4(const u32x4 q, const h2 *xp, const Masks &m) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     float a = 0.f, b = 0.f;
 #pragma unroll
@@ -99,7 +85,7 @@ DEV float blockdot_q4(const uint4 q, const h2 *xp, const Masks &m) {
 }
 
 // Returns sum (1024 + 128 + q) x over the block.
-DEV float blockdot_q8(const uint4 q0, const uint4 q1, const h2 *xp, const Masks &m) {
+DEV float blockdot_q8(const u32x4 q0, const u32x4 q1, const h2 *xp, const Masks &m) {
     const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     float acc = 0.f;
 #pragma unroll
@@ -114,16 +100,17 @@ DEV float blockdot_q8(const uint4 q0, const uint4 q1, const h2 *xp, const Masks 
     return acc;
 }
 
-constexpr int MV_KMAX = 16384;   // longest input row (elements) staged in LDS
+constexpr int MV_KMAX = 16384;   // longest input row (elements); its LDS image holds 512 blocks
 
 // Code bytes + scales of one pair of rows for this lane's blocks.
 template <int WT, int KB>
 struct PairLoad {
-    uint4 q[2][KB][WT == T_Q4_0 ? 1 : 2];
-    uint16_t d[2][KB];
+    u32x4 q[2][KB][WT == T_Q4_0 ? 1 : 2];
+    uint32_t d[2][KB];
 };
 
-// Blocks b0 + lane + 64*i (i < KB) below b1 of rows r0, r1.
+// Blocks b0 + lane + 64*i (i < KB) of rows r0, r1; lanes past the slice end
+// b1 re-read its last block and get scale 0, so every load is unconditional.
 template <int WT, int KB>
 DEV void load_pair(const QMat &W, int r0, int r1, int b0, int b1, int lane, PairLoad<WT, KB> &L) {
     const int K = W.K, nb = K >> 5;
@@ -131,266 +118,288 @@ DEV void load_pair(const QMat &W, int r0, int r1, int b0, int b1, int lane, Pair
 #pragma unroll
     for (int r = 0; r < 2; r++) {
         const uint16_t *dr = W.d + (size_t)rows[r] * nb;
-        const uint4 *qr = WT == T_Q4_0
-                              ? (const uint4 *)((const uint8_t *)W.qs + (size_t)rows[r] * (K >> 1))
-                              : (const uint4 *)((const int8_t *)W.qs + (size_t)rows[r] * K);
+        const u32x4 *qr = WT == T_Q4_0
+                              ? (const u32x4 *)((const uint8_t *)W.qs + (size_t)rows[r] * (K >> 1))
+                              : (const u32x4 *)((const int8_t *)W.qs + (size_t)rows[r] * K);
 #pragma unroll
         for (int i = 0; i < KB; i++) {
-            const int b = b0 + lane + 64 * i;
-            if (b < b1) {
-                if (WT == T_Q4_0) {
-                    L.q[r][i][0] = load_stream16(qr + b);
-                } else {
-                    L.q[r][i][0] = load_stream16(qr + 2 * b);
-                    L.q[r][i][WT == T_Q4_0 ? 0 : 1] = load_stream16(qr + 2 * b + 1);
-                }
-                L.d[r][i] = dr[b];
+            const int bw = b0 + lane + 64 * i;
+            const int b = bw < b1 ? bw : b1 - 1;
+            // streaming loads: the weights are read once per step
+            if (WT == T_Q4_0) {
+                L.q[r][i][0] = __builtin_nontemporal_load(qr + b);
             } else {
+                L.q[r][i][0] = __builtin_nontemporal_load(qr + 2 * b);
+                L.q[r][i][WT == T_Q4_0 ? 0 : 1] = __builtin_nontemporal_load(qr + 2 * b + 1);
+            }
+            const uint32_t dv = dr[b];
+            L.d[r][i] = bw < b1 ? dv : 0u;
+        }
+    }
+}
+
+constexpr int XROW = 36;   // dwords per LDS image row: 32 pairs + 4 pad (conflict-free 16-byte reads)
+
+// LDS image of the input row, built once per block: per 32-element quant
+// block, 16 value pairs then 16 remainder pairs (f16x2) in the order the code
+// extraction consumes them (the pair order above), padded to XROW dwords,
+// plus the block's offset sum.  Built 8 elements at a time.
+DEV uint32_t pk(f16 a, f16 b) { return h2_bits(h2{a, b}); }
+
+// Value/remainder split of elements k..k+3 and k2..k2+3: with NORM, fp32 x
+// times the RMSNorm factor and gain; otherwise the stored f16 value and
+// remainder.
+template <bool NORM>
+DEV void get8(const InArgs &in, const float *xr, const uint16_t *xh, const uint16_t *xl, float rs, int k,
+              int k2, f16 *hv, f16 *lv) {
+    const int ks[2] = {k, k2};
 #pragma unroll
-                for (int j = 0; j < (WT == T_Q4_0 ? 1 : 2); j++) L.q[r][i][j] = make_uint4(0, 0, 0, 0);
-                L.d[r][i] = 0;
+    for (int h = 0; h < 2; h++) {
+        if (NORM) {
+            const f4 v = *(const f4 *)(xr + ks[h]);
+            const f4 g = *(const f4 *)(in.norm_g + ks[h]);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float y = v[e] * rs * g[e];
+                hv[4 * h + e] = (f16)y;
+                lv[4 * h + e] = (f16)(y - (float)hv[4 * h + e]);
+            }
+        } else {
+            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+            const h4 a = *(const h4 *)(xh + ks[h]);
+            const h4 c = *(const h4 *)(xl + ks[h]);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                hv[4 * h + e] = a[e];
+                lv[4 * h + e] = c[e];
             }
         }
     }
 }
 
-template <int WT, int KB>
-DEV float dot_row(const PairLoad<WT, KB> &L, int r, const h2 (*xp)[32], const float *xsum,
-                  const Masks &m) {
-    float a = 0.f;
+// Quarter i of block b: elements 4i..4i+3 and 16+4i..16+4i+3 (Q4_0) or
+// 8i..8i+7 (Q8_0) -> image dwords 4i..4i+3 (values) and 16+4i.. (remainders).
+// The block's offset sum is the sum over its four quarters, which sit in
+// four consecutive lanes.
+template <int WT, bool NORM>
+DEV void put_quarter(uint32_t *img, float *bsum, int b, int i, const InArgs &in, const float *xr,
+                     const uint16_t *xh, const uint16_t *xl, float rs) {
+    uint32_t *row = img + (size_t)b * XROW;
+    f16 hv[8], lv[8];
+    float s_lo = 0.f, s_hi = 0.f;
+    if (WT == T_Q4_0) {
+        // pairs 4i..4i+3 = (a0,a2) (c0,c2) (a1,a3) (c1,c3): a = x[4i..], c = x[16+4i..]
+        get8<NORM>(in, xr, xh, xl, rs, 32 * b + 4 * i, 32 * b + 16 + 4 * i, hv, lv);
+        *(u32x4 *)(row + 4 * i) = u32x4{pk(hv[0], hv[2]), pk(hv[4], hv[6]), pk(hv[1], hv[3]), pk(hv[5], hv[7])};
+        *(u32x4 *)(row + 16 + 4 * i) = u32x4{pk(lv[0], lv[2]), pk(lv[4], lv[6]), pk(lv[1], lv[3]), pk(lv[5], lv[7])};
 #pragma unroll
-    for (int i = 0; i < KB; i++) {
-        float bd;
-        if (WT == T_Q4_0)
-            bd = blockdot_q4(L.q[r][i][0], xp[i], m);
-        else
-            bd = blockdot_q8(L.q[r][i][0], L.q[r][i][WT == T_Q4_0 ? 0 : 1], xp[i], m);
-        a += f16_bits_to_f32(L.d[r][i]) * (bd - xsum[i]);
+        for (int e = 0; e < 4; e++) {
+            s_lo += (float)hv[e] + (float)lv[e];
+            s_hi += (float)hv[4 + e] + (float)lv[4 + e];
+        }
+    } else {
+        // pairs 4i..4i+3 = (0,2) (1,3) (4,6) (5,7) of x[8i..8i+7]
+        get8<NORM>(in, xr, xh, xl, rs, 32 * b + 8 * i, 32 * b + 8 * i + 4, hv, lv);
+        *(u32x4 *)(row + 4 * i) = u32x4{pk(hv[0], hv[2]), pk(hv[1], hv[3]), pk(hv[4], hv[6]), pk(hv[5], hv[7])};
+        *(u32x4 *)(row + 16 + 4 * i) = u32x4{pk(lv[0], lv[2]), pk(lv[1], lv[3]), pk(lv[4], lv[6]), pk(lv[5], lv[7])};
+#pragma unroll
+        for (int e = 0; e < 8; e++) s_lo += (float)hv[e] + (float)lv[e];
     }
-    return a;
+    // offsets removed once per block: Q4_0 keeps 1024 + q on codes 0..15 and
+    // (1024 + 16 q) / 16 on codes 16..31, so sum (q - 8) x needs
+    // 1032 * sum(x[0..15]) + 72 * sum(x[16..31]) subtracted; Q8_0 keeps
+    // 1024 + 128 + q everywhere.
+    float v = WT == T_Q4_0 ? 1032.f * s_lo + 72.f * s_hi : 1152.f * s_lo;
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    if (i == 0) bsum[b] = v;
 }
 
-// NW wavefronts per block (one block per CU).  The K dimension is cut into S
-// slices of at most 128 blocks; S wavefronts share one row pair, each
-// covering one slice with at most 2 blocks per lane whose activations it
-// keeps in registers.  An f16 input row is read straight into registers; an
-// f32 residual row to be RMS-normalized is normalized once per block into LDS.  Row pairs p = g, g + G, ... are
-// streamed with the next pair's loads in flight while the current pair is
-// reduced (DPP within the wavefront; for S > 1 the S partial sums meet in
-// double-buffered LDS and are added in slice order).
-template <int WT, int KB, int S, int EPI>
+// NW = 16 wavefronts per block, one block per CU.  The K dimension is cut
+// into S slices of at most 64 blocks: lane l of a wavefront covers block
+// b0 + l of its slice, and keeps that block's activations (value and
+// remainder pairs, from the block's LDS image of the input row) in
+// registers.  S wavefronts share one row pair, one slice each.  A wavefront
+// keeps D row pairs of codes in flight: the first D are requested before the
+// input row is read, and each computed pair's registers are refilled with
+// the pair D ahead.  Row sums end with a DPP reduction; for S > 1 the
+// partial sums of all pairs meet in LDS once, after the last pair, and are
+// added in slice order.
+constexpr int MV_MAXIT = 16;   // row pairs per wavefront when K is split
+
+template <int WT, int S, int EPI, int D>
 __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, int pair_mode) {
     constexpr int NW = 16, G = NW / S;
-    // normalized input: staged through LDS (registers would not hold the row)
-    constexpr int XS = EPI == EPI_RESID ? 8 : (S * KB * 64 * 32 < MV_KMAX ? S * KB * 64 * 32 : MV_KMAX);
-    __shared__ __attribute__((aligned(16))) f16 xs[XS];
-    __shared__ __attribute__((aligned(16))) f16 xsl[XS];
+    constexpr bool NORM = EPI != EPI_RESID;   // every epilogue except the residual add reads a normalized row
+    __shared__ __attribute__((aligned(16))) uint32_t img[(MV_KMAX / 32) * XROW];
+    __shared__ float bsum[MV_KMAX / 32];
     __shared__ float red[NW];
-    __shared__ float part[2][NW][2];
+    __shared__ float part[S > 1 ? G * MV_MAXIT * S * 2 : 1];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int t = blockIdx.y;
     const int K = W.K, nb = K >> 5;
     const int xrow = in.row_idx ? in.row_idx[t] : t;
 
     const int slice = w % S, grp = w / S;
-    const int nbs = (nb + S - 1) / S;
+    const int nbs = (nb + S - 1) / S;               // <= 64
     const int b0 = slice * nbs, b1 = min(nb, b0 + nbs);
     const int npairs = W.N >> 1;
     const int stride = gridDim.x * G;
     const int first = blockIdx.x * G + grp;
     const int iters = (npairs + stride - 1) / stride;    // same for every wavefront of the grid
-    int p = first, r0 = 0, r1 = 1;
 
-    // ---- this wavefront's K slice of the activations -> f16 pairs in registers.
-    //      With a norm, the wavefront also reads the rest of the row for the sum
-    //      of squares: no LDS and no block barrier on the way in. ----
-    // every epilogue except the residual add reads a normalized row
-    constexpr bool NORM = EPI != EPI_RESID;
-    f16 xv[KB][32], xl[KB][32];
-    if (NORM) {
+    // ---- code loads of the first D pairs (independent of the input row) ----
+    PairLoad<WT, 1> L[D];
+    auto issue = [&](PairLoad<WT, 1> &dst, int it) __attribute__((always_inline)) {
+        const int p = min(first + it * stride, npairs - 1);   // past the end: re-read the last pair
+        int r0, r1;
+        pair_rows(pair_mode, p, r0, r1);
+        load_pair<WT, 1>(W, r0, r1, b0, b1, lane, dst);
+    };
+#pragma unroll
+    for (int k = 0; k < D; k++) issue(L[k], k);
+
+    // ---- LDS image of the input row, once per block ----
+    {
         const float *xr = in.x32 + (size_t)xrow * in.ldx;
-        const int tid = threadIdx.x;
-        float ss = 0.f;
-        for (int k = tid * 4; k < K; k += NW * 256) {
-            const float4 v = *(const float4 *)(xr + k);
-            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        }
-        ss = wave_sum_dpp(ss);
-        if (lane == 0) red[w] = ss;
-        __syncthreads();
-        float tot = 0.f;
-#pragma unroll
-        for (int i = 0; i < NW; i++) tot += red[i];
-        const float rs = 1.0f / sqrtf(tot / (float)K + in.eps);
-        for (int k = tid * 4; k < K; k += NW * 256) {
-            const float4 v = *(const float4 *)(xr + k);
-            const float4 g = *(const float4 *)(in.norm_g + k);
-            const float y[4] = {v.x * rs * g.x, v.y * rs * g.y, v.z * rs * g.z, v.w * rs * g.w};
-            f16 hi[4], lo[4];
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                hi[e] = (f16)y[e];
-                lo[e] = (f16)(y[e] - (float)hi[e]);
+        const uint16_t *xh = in.x16 + (size_t)xrow * in.ldx;
+        const uint16_t *xl = in.x16lo + (size_t)xrow * in.ldx;
+        float rs = 0.f;
+        if (NORM) {
+            float ss = 0.f;
+            for (int k = tid * 4; k < K; k += NW * 256) {
+                const f4 v = *(const f4 *)(xr + k);
+                ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
             }
-            *(uint2 *)&xs[k] = *(const uint2 *)hi;
-            *(uint2 *)&xsl[k] = *(const uint2 *)lo;
+            ss = wave_sum_dpp(ss);
+            if (lane == 0) red[w] = ss;
+            __syncthreads();
+            float tot = 0.f;
+#pragma unroll
+            for (int i = 0; i < NW; i++) tot += red[i];
+            rs = 1.0f / sqrtf(tot / (float)K + in.eps);
         }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < KB; i++) {
-            const int b = b0 + lane + 64 * i;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                uint4 v = make_uint4(0, 0, 0, 0), vl = v;
-                if (b < b1) {
-                    v = *(const uint4 *)&xs[b * 32 + 8 * j];
-                    vl = *(const uint4 *)&xsl[b * 32 + 8 * j];
-                }
-                *(uint4 *)&xv[i][8 * j] = v;
-                *(uint4 *)&xl[i][8 * j] = vl;
-            }
-        }
-    } else {
-        const uint16_t *xr = in.x16 + (size_t)xrow * in.ldx;
-        const uint16_t *xrl = in.x16lo + (size_t)xrow * in.ldx;
-#pragma unroll
-        for (int i = 0; i < KB; i++) {
-            const int b = b0 + lane + 64 * i;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                uint4 v = make_uint4(0, 0, 0, 0), vl = v;
-                if (b < b1) {
-                    v = *(const uint4 *)(xr + b * 32 + 8 * j);
-                    vl = *(const uint4 *)(xrl + b * 32 + 8 * j);
-                }
-                *(uint4 *)&xv[i][8 * j] = v;
-                *(uint4 *)&xl[i][8 * j] = vl;
-            }
+        // every 4 consecutive threads build one block (whole wavefronts stay in the loop)
+        for (int q = tid; q < ((4 * nb + 63) & ~63); q += NW * 64) {
+            const int b = min(q >> 2, nb - 1);
+            if (q < 4 * nb) put_quarter<WT, NORM>(img, bsum, b, q & 3, in, xr, xh, xl, rs);
         }
     }
-    h2 xp[KB][32];
-    float xsum[KB];
+    __syncthreads();
+
+    // ---- this lane's block of the slice -> registers ----
+    const int bl = b0 + lane;
+    const bool lane_ok = bl < b1;
+    h2 xp[32];
+    {
+        const uint32_t *row = img + (size_t)(lane_ok ? bl : b0) * XROW;
 #pragma unroll
-    for (int i = 0; i < KB; i++) {
-        // offsets removed once per block: Q4_0 keeps 1024 + q on codes 0..15 and
-        // (1024 + 16 q) / 16 on codes 16..31, so sum (q - 8) x needs
-        // 1032 * sum(x[0..15]) + 72 * sum(x[16..31]) subtracted; Q8_0 keeps
-        // 1024 + 128 + q everywhere.
-        float s_lo = 0.f, s_hi = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-            s_lo += (float)xv[i][j] + (float)xl[i][j];
-            s_hi += (float)xv[i][16 + j] + (float)xl[i][16 + j];
-        }
-        xsum[i] = WT == T_Q4_0 ? 1032.f * s_lo + 72.f * s_hi : 1152.f * (s_lo + s_hi);
-        if (WT == T_Q4_0) {
-            pairs_q4(xv[i], xp[i]);
-            pairs_q4(xl[i], xp[i] + 16);
-        } else {
-            pairs_q8(xv[i], xp[i]);
-            pairs_q8(xl[i], xp[i] + 16);
+        for (int j = 0; j < 8; j++) {
+            u32x4 v = *(const u32x4 *)(row + 4 * j);
+            if (!lane_ok) v = u32x4{0u, 0u, 0u, 0u};
+            xp[4 * j] = as_h2(v.x); xp[4 * j + 1] = as_h2(v.y);
+            xp[4 * j + 2] = as_h2(v.z); xp[4 * j + 3] = as_h2(v.w);
         }
     }
+    const float xs = lane_ok ? bsum[bl] : 0.f;
 
     // ---- stream row pairs ----
     const Masks mk = make_masks();
-    PairLoad<WT, KB> cur;
-    if (p < npairs) {
-        pair_rows(pair_mode, p, r0, r1);
-        load_pair<WT, KB>(W, r0, r1, b0, b1, lane, cur);
-    }
-    for (int it = 0; it < iters; it++) {
-        const int pn = p + stride;
-        int n0 = r0, n1 = r1;
-        PairLoad<WT, KB> nxt;
-        if (pn < npairs) {
-            pair_rows(pair_mode, pn, n0, n1);
-            load_pair<WT, KB>(W, n0, n1, b0, b1, lane, nxt);
-        }
-        float a0 = 0.f, a1 = 0.f;
-        if (p < npairs) {
-            a0 = wave_sum_dpp(dot_row<WT, KB>(cur, 0, xp, xsum, mk));
-            a1 = wave_sum_dpp(dot_row<WT, KB>(cur, 1, xp, xsum, mk));
-        }
-        if (S == 1) {
-            if (lane == 0 && p < npairs) epi_pair<EPI>(ep, t, p, r0, r1, a0, a1);
+    auto step = [&](PairLoad<WT, 1> &cur, int it) __attribute__((always_inline)) {
+        if (it >= iters) return;
+        const int p = first + it * stride;
+        float bd0, bd1;
+        if (WT == T_Q4_0) {
+            bd0 = blockdot_q4(cur.q[0][0][0], xp, mk);
+            bd1 = blockdot_q4(cur.q[1][0][0], xp, mk);
         } else {
-            if (lane == 0) {
-                part[it & 1][w][0] = a0;
-                part[it & 1][w][1] = a1;
-            }
-            __syncthreads();
-            if (slice == 0 && lane == 0 && p < npairs) {
-                float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-                for (int j = 0; j < S; j++) {
-                    s0 += part[it & 1][w + j][0];
-                    s1 += part[it & 1][w + j][1];
-                }
-                epi_pair<EPI>(ep, t, p, r0, r1, s0, s1);
+            bd0 = blockdot_q8(cur.q[0][0][0], cur.q[0][0][WT == T_Q4_0 ? 0 : 1], xp, mk);
+            bd1 = blockdot_q8(cur.q[1][0][0], cur.q[1][0][WT == T_Q4_0 ? 0 : 1], xp, mk);
+        }
+        float a0 = f16_bits_to_f32(cur.d[0][0]) * (bd0 - xs);
+        float a1 = f16_bits_to_f32(cur.d[1][0]) * (bd1 - xs);
+        issue(cur, it + D);                              // refill with the pair D ahead
+        a0 = wave_sum_dpp(a0);
+        a1 = wave_sum_dpp(a1);
+        if (p < npairs && lane == 0) {
+            if (S == 1) {
+                int r0, r1;
+                pair_rows(pair_mode, p, r0, r1);
+                epi_pair<EPI>(ep, t, p, r0, r1, a0, a1);
+            } else {
+                float *pp = part + ((grp * MV_MAXIT + it) * S + slice) * 2;
+                pp[0] = a0;
+                pp[1] = a1;
             }
         }
-        p = pn;
-        r0 = n0;
-        r1 = n1;
-        cur = nxt;
+    };
+    for (int it = 0; it < iters; it += D) {
+#pragma unroll
+        for (int k = 0; k < D; k++) step(L[k], it + k);
+    }
+    if (S > 1) {
+        // partial sums of the S slices, added in slice order
+        __syncthreads();
+        for (int i = tid; i < G * iters; i += NW * 64) {
+            const int g = i / iters, it = i % iters;
+            const int p = blockIdx.x * G + g + it * stride;
+            if (p >= npairs) continue;
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int j = 0; j < S; j++) {
+                s0 += part[((g * MV_MAXIT + it) * S + j) * 2];
+                s1 += part[((g * MV_MAXIT + it) * S + j) * 2 + 1];
+            }
+            int r0, r1;
+            pair_rows(pair_mode, p, r0, r1);
+            epi_pair<EPI>(ep, t, p, r0, r1, s0, s1);
+        }
     }
 }
 
 int g_num_cu = 256;
 
-template <int WT, int KB, int S, int EPI>
-bool launch_epi(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
-                hipStream_t s) {
+template <int WT, int S, int EPI>
+bool launch_epi(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode, hipStream_t s) {
     constexpr int NW = 16, G = NW / S;
+    constexpr int D = WT == T_Q4_0 ? 2 : 3;   // row pairs in flight per wavefront (deeper measured slower)
     const int npairs = W.N / 2;
     int blocks = (npairs + G - 1) / G;
     if (blocks > g_num_cu) blocks = g_num_cu;
-    launch((k_matvec<WT, KB, S, EPI>), dim3(blocks, T), dim3(NW * 64), 0, s, W, in, ep,
-                       pair_mode);
+    if (S > 1 && (npairs + blocks * G - 1) / (blocks * G) > MV_MAXIT) return false;
+    launch((k_matvec<WT, S, EPI, D>), dim3(blocks, T), dim3(NW * 64), 0, s, W, in, ep, pair_mode);
     return true;
 }
 
-template <int WT, int KB, int S>
-bool launch_ks(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
-               hipStream_t s) {
+template <int WT, int S>
+bool launch_s(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode, hipStream_t s) {
     switch (ep.epi) {
-    case EPI_STORE: return launch_epi<WT, KB, S, EPI_STORE>(W, in, ep, T, pair_mode, s);
-    case EPI_RESID: return launch_epi<WT, KB, S, EPI_RESID>(W, in, ep, T, pair_mode, s);
-    case EPI_QKV: return launch_epi<WT, KB, S, EPI_QKV>(W, in, ep, T, pair_mode, s);
-    case EPI_SWIGLU: return launch_epi<WT, KB, S, EPI_SWIGLU>(W, in, ep, T, pair_mode, s);
+    case EPI_STORE: return launch_epi<WT, S, EPI_STORE>(W, in, ep, T, pair_mode, s);
+    case EPI_RESID: return launch_epi<WT, S, EPI_RESID>(W, in, ep, T, pair_mode, s);
+    case EPI_QKV: return launch_epi<WT, S, EPI_QKV>(W, in, ep, T, pair_mode, s);
+    case EPI_SWIGLU: return launch_epi<WT, S, EPI_SWIGLU>(W, in, ep, T, pair_mode, s);
     default: return false;
     }
 }
 
-template <int WT, int KB>
-bool launch_kb(int S, const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
-               hipStream_t s) {
-    switch (S) {
-    case 1: return launch_ks<WT, KB, 1>(W, in, ep, T, pair_mode, s);
-    case 2: return launch_ks<WT, KB, 2>(W, in, ep, T, pair_mode, s);
-    case 4: return launch_ks<WT, KB, 4>(W, in, ep, T, pair_mode, s);
-    case 8: return launch_ks<WT, KB, 8>(W, in, ep, T, pair_mode, s);
-    case 16: return launch_ks<WT, KB, 16>(W, in, ep, T, pair_mode, s);
-    default: return false;
-    }
-}
-
-// K slices per row pair: enough that a lane holds at most 2 blocks, and more
-// while the grid would otherwise leave compute units idle.
+// K slices per row pair: the fewest that keep a slice within 64 blocks (one
+// per lane), doubled while the grid would leave compute units idle and the
+// per-wavefront pair count allows.
 template <int WT>
-bool launch_wt(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode,
-               hipStream_t s) {
+bool launch_wt(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode, hipStream_t s) {
     const int nb = W.K / 32, npairs = W.N / 2;
-    const int slice_max = WT == T_Q8_0 ? 64 : 128;   // blocks per K slice (registers)
-    if (nb > 16 * slice_max) return false;
+    if (W.K > MV_KMAX) return false;
     int S = 1;
-    while (S * slice_max < nb) S *= 2;
+    while (S * 64 < nb) S *= 2;
     while (S < 16 && (long long)npairs * S < 16LL * g_num_cu) S *= 2;
-    if (ep.epi != EPI_RESID && W.K > MV_KMAX) return false;
-    const int nbs = (nb + S - 1) / S;
-    if (WT == T_Q8_0 || nbs <= 64) return launch_kb<WT, 1>(S, W, in, ep, T, pair_mode, s);
-    return launch_kb<T_Q4_0, 2>(S, W, in, ep, T, pair_mode, s);
+    switch (S) {
+    case 1: return launch_s<WT, 1>(W, in, ep, T, pair_mode, s);
+    case 2: return launch_s<WT, 2>(W, in, ep, T, pair_mode, s);
+    case 4: return launch_s<WT, 4>(W, in, ep, T, pair_mode, s);
+    case 8: return launch_s<WT, 8>(W, in, ep, T, pair_mode, s);
+    case 16: return launch_s<WT, 16>(W, in, ep, T, pair_mode, s);
+    default: return false;
+    }
 }
 
 }  // namespace
