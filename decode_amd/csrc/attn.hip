@@ -21,6 +21,19 @@
 // over chunk groups, and writes o in f16 for the output projection.  The
 // grid covers the context's largest chunk count; blocks past a token's last
 // chunk exit at once, so one captured launch serves every decode step.
+//
+// f16 cache, head_dim 64 / 128: the chunk partials come from matrix cores
+// instead (k_attn_mfma, 128-key chunks, same partial format).  Each
+// wavefront takes 32 keys:
+//   S^T[key][head] = K Q^T   v_mfma_f32_32x32x16_f16, K rows loaded straight
+//                            into the A operand, Q (scaled by 1/sqrt(hd)) as
+//                            f16 value + remainder fragments built once per
+//                            block in LDS, so every product is exact;
+//   softmax per head column over the wavefront's keys;
+//   O^T[dim][head] += V^T P^T  with P (value + remainder) taken from the S^T
+//                            accumulators and V^T staged in LDS, its keys
+//                            permuted to match the accumulator order.
+// The block's four wavefronts are then combined into one chunk partial.
 #include "common.h"
 #include "kernels.h"
 
@@ -258,6 +271,180 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     }
 }
 
+constexpr int CHM = 128;    // cached rows per chunk of the MFMA kernel (4 wavefronts x 32)
+
+// Column of key k (0..31) in a wavefront's V^T tile: within each 16-key
+// group bits 2 and 3 swap, so that 8 consecutive columns hold the keys a
+// lane's accumulators r = 8s..8s+7 belong to (keys 16s + 8(r/4 % 2) + 4(lane/32) + r%4).
+DEV int vt_key_col(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
+    constexpr int KS = HD / 16;          // k-steps of K Q^T
+    constexpr int DT = HD / 32;          // 32-row dim tiles of O^T
+    constexpr int VC = HD / 16;          // 16-byte V chunks per lane (32 keys x HD/8 chunks / 64 lanes)
+    static_assert(VC % 2 == 0, "two keys per lane");
+    constexpr int VST = 32 + 8;          // f16 stride of a V^T row
+    __shared__ __attribute__((aligned(16))) f16 Vt[4][HD][VST];
+    __shared__ float cm[4][32], cl[4][32];
+    __shared__ __attribute__((aligned(16))) float co[4][GMAX][HD];
+    __shared__ __attribute__((aligned(16))) h8 qf[2][KS][64];   // Q^T operand fragments: value, remainder
+
+    const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int pos = a.tok.pos[t], seq = a.tok.seq[t];
+    const int G = a.H / a.kv.n_kv;
+    const int c0 = c * CHM;
+    if (c0 > pos) return;                              // uniform per block
+    const int k0 = c0 + 32 * w;                        // this wavefront's first key
+    const size_t base = (((size_t)seq * a.kv.n_kv + g) * a.kv.n_ctx) * HD;
+    const f16 *Kb = (const f16 *)a.kv.k + base;
+    const f16 *Vb = (const f16 *)a.kv.v + base;
+
+    // ---- loads: K rows in A-operand layout, V rows for the transpose, Q ----
+    // rows past pos are replaced by row pos (finite data; their weights are 0)
+    const int kr = min(k0 + (lane & 31), pos);
+    h8 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) kf[ks] = *(const h8 *)(Kb + (size_t)kr * HD + 16 * ks + 8 * (lane >> 5));
+    // V: lane l holds keys 2(l%16), 2(l%16)+1 at dims 8 d8 .. 8 d8 + 7 with
+    // d8 = l/16 + 4i, so that its LDS writes pack two keys per dword
+    const int vj = lane & 15, vg = lane >> 4;
+    h8 va[VC / 2], vb[VC / 2];
+#pragma unroll
+    for (int i = 0; i < VC / 2; i++) {
+        const int d8 = vg + 4 * i;
+        va[i] = *(const h8 *)(Vb + (size_t)min(k0 + 2 * vj, pos) * HD + 8 * d8);
+        vb[i] = *(const h8 *)(Vb + (size_t)min(k0 + 2 * vj + 1, pos) * HD + 8 * d8);
+    }
+    const int hc = lane & 31;                          // this lane's head column
+    const bool hv = hc < G;
+    // Q^T operand of lane l, k-step ks: head l%32 (zero past G), dims
+    // 16 ks + 8 (l/32) .. +7, scaled by 1/sqrt(hd), as f16 value + remainder;
+    // built once per block in LDS
+    for (int f = tid; f < KS * 64; f += 256) {
+        const int ks = f / 64, fl = f % 64, fh = fl & 31;
+        h8 vh, vl;
+        if (fh < G) {
+            const float qs = 1.0f / sqrtf((float)HD);
+            const float *qr = a.q + ((size_t)t * a.H + g * G + fh) * HD + 16 * ks + 8 * (fl >> 5);
+            const f4 lo = *(const f4 *)qr, hi = *(const f4 *)(qr + 4);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float y = (e < 4 ? lo[e] : hi[e - 4]) * qs;
+                vh[e] = (f16)y;
+                vl[e] = (f16)(y - (float)vh[e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++) vh[e] = vl[e] = (f16)0.f;
+        }
+        qf[0][ks][fl] = vh;
+        qf[1][ks][fl] = vl;
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T (exact products, fp32 accumulation) ----
+    f16x sacc;
+#pragma unroll
+    for (int r = 0; r < 16; r++) sacc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[0][ks][lane], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[1][ks][lane], sacc, 0, 0, 0);
+    }
+
+    // ---- causal mask and this wavefront's softmax statistics per head ----
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        const int key = k0 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (key > pos) sacc[r] = -INFINITY;
+        m = fmaxf(m, sacc[r]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    float l = 0.f;
+    h8 ph[2], pl[2];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        const float p = m == -INFINITY ? 0.f : __expf(sacc[r] - m);
+        l += p;
+        const f16 p16 = (f16)p;
+        ph[r >> 3][r & 7] = p16;
+        pl[r >> 3][r & 7] = (f16)(p - (float)p16);
+    }
+    l += __shfl_xor(l, 32, 64);
+
+    // ---- V^T of this wavefront's keys into LDS ----
+    // (keys 2j and 2j+1 land in adjacent columns; the element order is
+    // rotated per lane group so the four groups of a store use different banks)
+    {
+        const int col = vt_key_col(2 * vj);
+#pragma unroll
+        for (int i = 0; i < VC / 2; i++) {
+            const int d8 = vg + 4 * i;
+#pragma unroll
+            for (int e0 = 0; e0 < 8; e0++) {
+                const int e = (e0 + 2 * vg) & 7;
+                *(h2 *)&Vt[w][8 * d8 + e][col] = h2{va[i][e], vb[i][e]};
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- O^T = V^T P^T ----
+    f16x o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) o[dt][r] = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++) {
+            const h8 vf = *(const h8 *)(&Vt[w][32 * dt + (lane & 31)][16 * s2 + 8 * (lane >> 5)]);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, ph[s2], o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pl[s2], o[dt], 0, 0, 0);
+        }
+    }
+
+    // ---- combine the four wavefronts into the chunk partial ----
+    if (hv) {
+        if (lane < 32) {
+            cm[w][hc] = m;
+            cl[w][hc] = l;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++)
+                *(f4 *)&co[w][hc][32 * dt + q4 * 8 + (lane >> 5) * 4] =
+                    f4{o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]};
+    }
+    __syncthreads();
+    const size_t mc = (size_t)a.max_chunks;
+    for (int i = tid; i < G * HD; i += 256) {
+        const int h = i / HD, d = i % HD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 4; k++) M = fmaxf(M, cm[k][h]);
+        float acc = 0.f, L = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const float f = cm[k][h] == -INFINITY ? 0.f : __expf(cm[k][h] - M);
+            acc += co[k][h][d] * f;
+            L += cl[k][h] * f;
+        }
+        const size_t hh = (size_t)t * a.H + g * G + h;
+        a.part[(hh * mc + c) * HD + d] = acc;
+        if (d == 0) {
+            a.ml[(hh * mc + c) * 2 + 0] = M;
+            a.ml[(hh * mc + c) * 2 + 1] = L;
+        }
+    }
+}
+
+// Chunk size of the path launch_attention takes for this cache.
+int chunk_for(int kvtype, int hd) { return kvtype == T_F16 && (hd == 64 || hd == 128) ? CHM : CH; }
+
 template <int HD, int KVT>
 bool launch_part(const AttnArgs &a, int T, hipStream_t s) {
     const dim3 grid(a.max_chunks, a.kv.n_kv, T);
@@ -272,7 +459,18 @@ bool launch_part(const AttnArgs &a, int T, hipStream_t s) {
 
 template <int HD>
 bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
-    const bool ok = a.kv.kvtype == T_F16 ? launch_part<HD, T_F16>(a, T, s) : launch_part<HD, T_F32>(a, T, s);
+    bool ok;
+    if (a.chunk == CHM) {
+        if constexpr (HD <= 128) {
+            if (a.H / a.kv.n_kv > GMAX) return false;
+            launch(k_attn_mfma<HD>, dim3(a.max_chunks, a.kv.n_kv, T), dim3(256), 0, s, a);
+            ok = true;
+        } else {
+            return false;
+        }
+    } else {
+        ok = a.kv.kvtype == T_F16 ? launch_part<HD, T_F16>(a, T, s) : launch_part<HD, T_F32>(a, T, s);
+    }
     if (!ok) return false;
     launch((k_attn_merge<HD>), dim3(a.H, T), dim3(256), 0, s, a);
     return true;
@@ -281,7 +479,7 @@ bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
 }  // namespace
 
 bool launch_attention(const AttnArgs &a, int T, hipStream_t s) {
-    if (a.chunk != CH || T <= 0 || a.max_chunks > 1024) return false;
+    if (T <= 0 || a.max_chunks > 1024 || a.chunk != chunk_for(a.kv.kvtype, a.kv.hd)) return false;
     switch (a.kv.hd) {
     case 64: return launch_hd<64>(a, T, s);
     case 128: return launch_hd<128>(a, T, s);
@@ -290,4 +488,4 @@ bool launch_attention(const AttnArgs &a, int T, hipStream_t s) {
     }
 }
 
-int attention_chunk() { return CH; }
+int attention_chunk(int kvtype, int hd) { return chunk_for(kvtype, hd); }

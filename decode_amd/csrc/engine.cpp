@@ -20,7 +20,7 @@
 
 #include "kernels.h"
 
-int attention_chunk();
+int attention_chunk(int kvtype, int hd);
 
 // --------------------------------------------------------------- logging
 static void (*g_log_cb)(int, const char *, void *) = nullptr;
@@ -500,7 +500,7 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
         L.v = c->mem.get(kv_elems * esz);
         ok = L.k && L.v;
     }
-    c->chunk = attention_chunk();
+    c->chunk = attention_chunk(h.kvtype, hd);
     c->max_chunks = (int)((n_ctx + c->chunk - 1) / c->chunk);
     const size_t T = (size_t)c->Tmax;
     if (ok) {
