@@ -33,7 +33,7 @@
 //   O^T[dim][head] += V^T P^T  with P (value + remainder) taken from the S^T
 //                            accumulators and V^T staged in LDS, its keys
 //                            permuted to match the accumulator order.
-// The block's four wavefronts are then combined into one chunk partial.
+// The block's wavefronts are then combined into one chunk partial.
 #include "common.h"
 #include "kernels.h"
 
@@ -271,7 +271,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     }
 }
 
-constexpr int CHM = 128;    // cached rows per chunk of the MFMA kernel (4 wavefronts x 32)
+constexpr int MW = 2;                // wavefronts per block of the MFMA kernel
+constexpr int CHM = 32 * MW;        // cached rows per chunk of the MFMA kernel
 
 // Column of key k (0..31) in a wavefront's V^T tile: within each 16-key
 // group bits 2 and 3 swap, so that 8 consecutive columns hold the keys a
@@ -279,15 +280,15 @@ constexpr int CHM = 128;    // cached rows per chunk of the MFMA kernel (4 wavef
 DEV int vt_key_col(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 template <int HD>
-__global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
+__global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
     constexpr int KS = HD / 16;          // k-steps of K Q^T
     constexpr int DT = HD / 32;          // 32-row dim tiles of O^T
     constexpr int VC = HD / 16;          // 16-byte V chunks per lane (32 keys x HD/8 chunks / 64 lanes)
     static_assert(VC % 2 == 0, "two keys per lane");
     constexpr int VST = 32 + 8;          // f16 stride of a V^T row
-    __shared__ __attribute__((aligned(16))) f16 Vt[4][HD][VST];
-    __shared__ float cm[4][32], cl[4][32];
-    __shared__ __attribute__((aligned(16))) float co[4][GMAX][HD];
+    __shared__ __attribute__((aligned(16))) f16 Vt[MW][HD][VST];
+    __shared__ float cm[MW][32], cl[MW][32];
+    __shared__ __attribute__((aligned(16))) float co[MW][GMAX][HD];
     __shared__ __attribute__((aligned(16))) h8 qf[2][KS][64];   // Q^T operand fragments: value, remainder
 
     const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     // Q^T operand of lane l, k-step ks: head l%32 (zero past G), dims
     // 16 ks + 8 (l/32) .. +7, scaled by 1/sqrt(hd), as f16 value + remainder;
     // built once per block in LDS
-    for (int f = tid; f < KS * 64; f += 256) {
+    for (int f = tid; f < KS * 64; f += MW * 64) {
         const int ks = f / 64, fl = f % 64, fh = fl & 31;
         h8 vh, vl;
         if (fh < G) {
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         }
     }
 
-    // ---- combine the four wavefronts into the chunk partial ----
+    // ---- combine the block's wavefronts into the chunk partial ----
     if (hv) {
         if (lane < 32) {
             cm[w][hc] = m;
@@ -421,14 +422,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     }
     __syncthreads();
     const size_t mc = (size_t)a.max_chunks;
-    for (int i = tid; i < G * HD; i += 256) {
+    for (int i = tid; i < G * HD; i += MW * 64) {
         const int h = i / HD, d = i % HD;
         float M = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < 4; k++) M = fmaxf(M, cm[k][h]);
+        for (int k = 0; k < MW; k++) M = fmaxf(M, cm[k][h]);
         float acc = 0.f, L = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
+        for (int k = 0; k < MW; k++) {
             const float f = cm[k][h] == -INFINITY ? 0.f : __expf(cm[k][h] - M);
             acc += co[k][h][d] * f;
             L += cl[k][h] * f;
@@ -443,7 +444,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 }
 
 // Chunk size of the path launch_attention takes for this cache.
-int chunk_for(int kvtype, int hd) { return kvtype == T_F16 && (hd == 64 || hd == 128) ? CHM : CH; }
+bool mfma_path(int kvtype, int hd) { return kvtype == T_F16 && (hd == 64 || hd == 128); }
+int chunk_for(int kvtype, int hd) { return mfma_path(kvtype, hd) ? CHM : CH; }
 
 template <int HD, int KVT>
 bool launch_part(const AttnArgs &a, int T, hipStream_t s) {
@@ -460,10 +462,10 @@ bool launch_part(const AttnArgs &a, int T, hipStream_t s) {
 template <int HD>
 bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
     bool ok;
-    if (a.chunk == CHM) {
+    if (mfma_path(a.kv.kvtype, HD)) {
         if constexpr (HD <= 128) {
             if (a.H / a.kv.n_kv > GMAX) return false;
-            launch(k_attn_mfma<HD>, dim3(a.max_chunks, a.kv.n_kv, T), dim3(256), 0, s, a);
+            launch(k_attn_mfma<HD>, dim3(a.max_chunks, a.kv.n_kv, T), dim3(MW * 64), 0, s, a);
             ok = true;
         } else {
             return false;
