@@ -1,4 +1,4 @@
-"""Parity at the workloads' full shapes (8B Q4_0, 1B Q8_0, 7B MHA Q4_0).
+"""Parity at the workloads' full shapes (8B Q4_0, 8B Q8_0, 1B Q8_0, 7B MHA Q4_0).
 
 The oracle cannot run a 4096-token prefill in test time, so at full size
 the GPU is checked three ways:
@@ -161,3 +161,83 @@ def test_7b_mha_batched_decode(dec):
     for k in range(n_dec):
         for s in (0, 1):
             assert_logits_close(b_rows[k][s], oc.eval(s, int(feeds[k][s])), f"oracle step {k} seq {s}")
+
+
+def test_8b_q8_long_prefill(dec):
+    """8B shape with Q8_0 weights: an 8192-token prefill in 16 ubatches of 512
+    with logits for the last token only.  Checked against the oracle on a
+    short run at the same shape (and sampled blocks bit-exact), and at full
+    length through properties: the same prompt in ubatches of 1024 gives the
+    same last logits, and decoding after the prefill equals a fresh prefill
+    of the extended prompt."""
+    import torch
+
+    import oracle
+    W = synth.WORKLOADS["8b_q8_long"]
+    hp = synth.hparams(W)
+    w = synth.weights_torch(hp, W["seed"], "cuda")
+    torch.cuda.synchronize()
+    gm = dec.Model(hp, w)
+    for name, layer in (("tok_embd", 0), ("wq", 3), ("wv", 30), ("ffn_down", 17), ("output", 0)):
+        t = w[name] if name in ("tok_embd", "output") else w[name][layer]
+        ref = oracle.quantize(t.cpu().numpy(), oracle.T_Q8_0)
+        assert np.array_equal(gm.tensor_blocks(name, layer), ref), (name, layer)
+    # short run against the oracle
+    om = oracle.Model(hp, _host(w))
+    del w
+    torch.cuda.empty_cache()
+    prompt_s = synth.prompt(hp["n_vocab"], 6, 2014)
+    o_toks, o_rows = oracle.run_greedy(om, prompt_s, 3, 64)
+    del om
+    ctx = dec.Context(gm, n_ctx=64, n_ubatch=512)
+    g_toks, g_rows = gpu_greedy(ctx, prompt_s, 3, teacher=o_toks)
+    for k, (g, o) in enumerate(zip(g_rows, o_rows)):
+        assert_logits_close(g, o, f"8b q8 step {k}")
+    ctx.close()
+    # full length: 8192 tokens in ubatches of 512 vs 1024
+    n = W["n_prompt"]
+    prompt = synth.prompt(hp["n_vocab"], n, 2004)
+    a = dec.Context(gm, n_ctx=n + 16, n_batch=n, n_ubatch=W["n_ubatch"])
+    toks, rows = gpu_greedy(a, prompt, 3)
+    b = dec.Context(gm, n_ctx=n + 16, n_batch=n + 16, n_ubatch=1024)
+    assert b.prefill(prompt, 0) == 0
+    ma, _ = logit_err(b.logits(-1), rows[0])
+    assert ma <= ABS_TOL, ma
+    assert b.argmax(-1) == toks[0]
+    b.clear(0)
+    full = np.concatenate([prompt, np.array(toks[:-1], np.int32)])
+    assert b.prefill(full, 0) == 0
+    ma, _ = logit_err(b.logits(-1), rows[-1])
+    assert ma <= ABS_TOL, ma
+    assert b.argmax(-1) == toks[-1]
+
+
+def test_7b_batched_decode_full_caches(dec):
+    """32 sequences, each with a 2048-token prompt in its own cache (the
+    batched workload's cache size), decoded together; three of them decoded
+    alone in a second context must give the same logits."""
+    import torch
+    W = synth.WORKLOADS["7b_q4_b32"]
+    hp = synth.hparams(W)
+    w = synth.weights_torch(hp, W["seed"], "cuda")
+    torch.cuda.synchronize()
+    gm = dec.Model(hp, w)
+    del w
+    torch.cuda.empty_cache()
+    S, n_p, n_dec = W["n_seq"], W["n_prompt"], 3
+    picked = (0, 17, 31)
+    prompts = [synth.prompt(hp["n_vocab"], n_p, 3000 + s) for s in range(S)]
+    feeds = synth.prompt(hp["n_vocab"], n_dec * S, 3200).reshape(n_dec, S)
+    batched = dec.Context(gm, n_ctx=n_p + 8, n_batch=n_p, n_ubatch=W["n_ubatch"], n_seq_max=S)
+    single = dec.Context(gm, n_ctx=n_p + 8, n_batch=n_p, n_ubatch=W["n_ubatch"], n_seq_max=S)
+    for s in range(S):
+        assert batched.prefill(prompts[s], s) == 0
+    for s in picked:
+        assert single.prefill(prompts[s], s) == 0
+    for k in range(n_dec):
+        assert batched.decode(feeds[k], np.arange(S)) == 0
+        for s in picked:
+            assert single.decode([feeds[k][s]], [s]) == 0
+            assert_logits_close(single.logits(0), batched.logits(s), f"step {k} seq {s}")
+            assert single.argmax(0) == batched.argmax(s)
+    assert batched.pos_max(31) == n_p + n_dec - 1
