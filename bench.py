@@ -50,6 +50,37 @@ def algorithmic(hp, n_prompt, steps):
                 prefill_flops=lin_flops + attn_flops + out_flops)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_matvec_gate_up__8b_q4_decode_bs1__hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_amd", "csrc", f) for f in ("matvec.hip", "common.h", "epilogue.h", "kernels.h")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up mat-vec from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factor), or
+    None when the summary is missing or was taken on different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(l.split(":", 1) for l in fh.read().splitlines() if l.startswith("- ") and ":" in l)
+    except OSError:
+        return None
+    kv = {k[2:].strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(hp, weights_dev, prompt, n_prompt_tokens, n_decode_tokens):
     """The oracle (f64 build, as it stands) on a bounded sample of the same
     workload: n_prompt_tokens prompt tokens, then n_decode_tokens decode
@@ -88,6 +119,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prompt", type=int, default=3)
     ap.add_argument("--cpu-decode", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (4 times), the reference kernel for "
+                         "scaling the HBM fetch/write counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on exactly one GPU (the decode step of one sequence "
@@ -171,10 +205,14 @@ def main():
     roofline = None
     if gu_avg_s:
         ach = gu_bytes / gu_avg_s / 1e9
+        traffic = measured_traffic()
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": None if traffic is None else int(traffic),
                     "kernel": "k_matvec (gate/up, Q4_0 mat-vec + RMSNorm prologue + SwiGLU epilogue)",
                     "bytes_per_launch": gu_bytes, "avg_us": round(gu_avg_s * 1e6, 2),
+                    "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                    "kernel_source_sha256_16": kernel_source_hash(),
                     "launches_timed": dc_probe[1]}
     pf_roof = None
     if pf_probe and pf_probe[1]:
@@ -186,6 +224,15 @@ def main():
                    "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
                    "kernel": "k_gemm_mfma (gate/up, ubatch 512)", "avg_us": round(avg * 1e6, 1)}
     step_gbs = alg["token_bytes"] / (decode_s / steps) / 1e9
+
+    if args.copy_calibration:
+        with torch.cuda.stream(stream):
+            src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(4):
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
