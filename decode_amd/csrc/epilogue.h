@@ -84,3 +84,63 @@ DEV void epi_pair(const EpiArgs &e, int t, int p, int r0, int r1, float a, float
     }
     }
 }
+
+// Memory inputs of an epilogue, read ahead of the arithmetic so that a
+// kernel can request them at entry: the old residual values (RESID) or the
+// RoPE factors, position and sequence of the pair (QKV).
+struct EpiPre {
+    float y0 = 0.f, y1 = 0.f;
+    float2 cs = make_float2(1.f, 0.f);
+    int pos = 0, seq = 0;
+};
+
+template <int EPI>
+DEV EpiPre epi_prefetch(const EpiArgs &e, int t, int r0, int r1) {
+    EpiPre pre;
+    if (EPI == EPI_RESID) {
+        const float *y = e.y + (size_t)t * e.ldy;
+        pre.y0 = y[r0];
+        pre.y1 = y[r1];
+    } else if (EPI == EPI_QKV) {
+        const int hd = e.kv.hd;
+        pre.pos = e.tok.pos[t];
+        pre.seq = e.tok.seq[t];
+        if (r0 < e.qd + e.kd) {
+            const int rr = r0 < e.qd ? r0 : r0 - e.qd;
+            pre.cs = *(const float2 *)(e.rope_cs + ((size_t)pre.pos * (hd >> 1) + ((rr % hd) >> 1)) * 2);
+        }
+    }
+    return pre;
+}
+
+// epi_pair with the memory inputs taken from epi_prefetch (same results).
+template <int EPI>
+DEV void epi_pair_pre(const EpiArgs &e, int t, int p, int r0, int r1, float a, float b, const EpiPre &pre) {
+    if (EPI == EPI_RESID) {
+        float *y = e.y + (size_t)t * e.ldy;
+        y[r0] = pre.y0 + a;
+        y[r1] = pre.y1 + b;
+    } else if (EPI == EPI_QKV) {
+        const int hd = e.kv.hd;
+        if (r0 < e.qd + e.kd) {
+            const int rr = r0 < e.qd ? r0 : r0 - e.qd;
+            const float ra = a * pre.cs.x - b * pre.cs.y;
+            const float rb = a * pre.cs.y + b * pre.cs.x;
+            if (r0 < e.qd) {
+                *(float2 *)(e.qout + (size_t)t * e.qd + r0) = make_float2(ra, rb);
+            } else {
+                const int g = rr / hd, el = rr % hd;
+                const size_t idx = (((size_t)pre.seq * e.kv.n_kv + g) * e.kv.n_ctx + pre.pos) * hd + el;
+                store_kv_pair(e.kv.k, e.kv.kvtype, idx, ra, rb);
+            }
+        } else {
+            const int rr = r0 - e.qd - e.kd;
+            const int g = rr / hd, el = rr % hd;
+            const size_t idx = (((size_t)pre.seq * e.kv.n_kv + g) * e.kv.n_ctx + pre.pos) * hd + el;
+            store_kv_pair(e.kv.v, e.kv.kvtype, idx, a, b);
+        }
+    } else {
+        epi_pair<EPI>(e, t, p, r0, r1, a, b);
+    }
+}
+

@@ -258,6 +258,19 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
     };
 #pragma unroll
     for (int k = 0; k < D; k++) issue(L[k], k);
+    // with a split K, thread i finishes item i (group, pair) after the last
+    // pair: its epilogue inputs are requested now
+    int fin_p = -1, fin_r0 = 0, fin_r1 = 1;
+    EpiPre fin_pre;
+    if (S > 1 && tid < G * iters) {
+        const int g = tid / iters, it = tid % iters;
+        const int p = blockIdx.x * G + g + it * stride;
+        if (p < npairs) {
+            fin_p = p;
+            pair_rows(pair_mode, p, fin_r0, fin_r1);
+            fin_pre = epi_prefetch<EPI>(ep, t, fin_r0, fin_r1);
+        }
+    }
 
     // ---- LDS image of the input row, once per block ----
     {
@@ -338,21 +351,18 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         for (int k = 0; k < D; k++) step(L[k], it + k);
     }
     if (S > 1) {
-        // partial sums of the S slices, added in slice order
+        // partial sums of the S slices, added in slice order (G * iters <= the
+        // block's threads: MV_MAXIT * G <= 16 * 64)
         __syncthreads();
-        for (int i = tid; i < G * iters; i += NW * 64) {
-            const int g = i / iters, it = i % iters;
-            const int p = blockIdx.x * G + g + it * stride;
-            if (p >= npairs) continue;
+        if (fin_p >= 0) {
+            const int g = tid / iters, it = tid % iters;
             float s0 = 0.f, s1 = 0.f;
 #pragma unroll
             for (int j = 0; j < S; j++) {
                 s0 += part[((g * MV_MAXIT + it) * S + j) * 2];
                 s1 += part[((g * MV_MAXIT + it) * S + j) * 2 + 1];
             }
-            int r0, r1;
-            pair_rows(pair_mode, p, r0, r1);
-            epi_pair<EPI>(ep, t, p, r0, r1, s0, s1);
+            epi_pair_pre<EPI>(ep, t, fin_p, fin_r0, fin_r1, s0, s1, fin_pre);
         }
     }
 }
