@@ -99,6 +99,9 @@ def load(kind: str = "f64") -> C.CDLL:
         "orc_eval": (i32, [vp, i32, i32, vp]),
         "orc_eval_tap": (i32, [vp, i32, i32, vp, i32, vp]),
         "orc_kv_row": (i32, [vp, i32, i32, i32, i32, i32, vp]),
+        "orc_splitmix64": (C.c_uint64, [C.c_uint64, C.c_uint64]),
+        "orc_uniform24": (f32, [C.c_uint64, C.c_uint64]),
+        "orc_sample": (i32, [vp, i32, vp, i32, vp, C.c_uint64, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -206,6 +209,39 @@ def swiglu(u, v, kind="f64"):
 def argmax(x, kind="f64"):
     x = np.ascontiguousarray(x, real_dtype(kind))
     return int(load(kind).orc_argmax(_p(x), x.size))
+
+
+# ------------------------------------------------------------------- sampler
+class SamplerParams(C.Structure):
+    """Mirror of orc_sampler_params (article, step 15: the sampler list)."""
+    _fields_ = [("top_k", C.c_int32), ("top_p", C.c_float), ("min_p", C.c_float), ("temp", C.c_float),
+                ("repeat_penalty", C.c_float), ("penalty_last_n", C.c_int32), ("seed", C.c_uint64)]
+
+
+def splitmix64(seed: int, index: int) -> int:
+    return int(load().orc_splitmix64(seed, index))
+
+
+def uniform24(seed: int, index: int) -> float:
+    return float(load().orc_uniform24(seed, index))
+
+
+def sample(logits, hist=(), top_k=40, top_p=1.0, min_p=0.0, temp=1.0, repeat_penalty=1.0,
+           penalty_last_n=64, seed=0, draw=0, detail=False):
+    """The sampler chain on one fp32 logits row.  Returns the token, or with
+    detail=True (token, candidate ids, inclusive cumulative weights, target)."""
+    x = np.ascontiguousarray(logits, np.float32)
+    h = np.ascontiguousarray(np.asarray(hist, np.int32))
+    prm = SamplerParams(top_k, top_p, min_p, temp, repeat_penalty, penalty_last_n, seed)
+    ids = np.zeros(x.size, np.int32)
+    cum = np.zeros(x.size, np.float32)
+    nk = C.c_int32(0)
+    tg = C.c_float(0.0)
+    tok = load().orc_sample(_p(x), x.size, _p(h) if h.size else None, h.size, C.byref(prm), draw,
+                            _p(ids), _p(cum), C.byref(nk), C.byref(tg))
+    if not detail:
+        return int(tok)
+    return int(tok), ids[:nk.value].copy(), cum[:nk.value].copy(), float(tg.value)
 
 
 # ------------------------------------------------------------------- decoder

@@ -607,3 +607,112 @@ int32_t orc_kv_row(const orc_ctx *c, int32_t which, int32_t layer, int32_t seq, 
         out[i] = (float)kv_at(base, c->m->hp.kvtype, (int64_t)pos * kd + (int64_t)kv_head * hd + i);
     return 0;
 }
+
+/* ======================================================================== */
+/* Sampler chain (article, step 15: the sampler list and its order)         */
+/* ======================================================================== */
+
+/* SplitMix64 (Steele, Lea, Flood: "Fast splittable pseudorandom number
+   generators", 2014): state advances by the golden-ratio increment, the
+   output is the state passed through two xor-shift-multiply rounds. */
+uint64_t orc_splitmix64(uint64_t seed, uint64_t index)
+{
+    uint64_t z = seed + (index + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+float orc_uniform24(uint64_t seed, uint64_t index)
+{
+    return (float)(orc_splitmix64(seed, index) >> 40) * (1.0f / 16777216.0f);
+}
+
+typedef struct { float l; int32_t id; } orc_cand;
+
+/* chain order: larger logit first, the lower token id first on equal logits */
+static int cand_cmp(const void *a, const void *b)
+{
+    const orc_cand *x = (const orc_cand *)a, *y = (const orc_cand *)b;
+    if (x->l > y->l) return -1;
+    if (x->l < y->l) return 1;
+    return (x->id > y->id) - (x->id < y->id);
+}
+
+int32_t orc_sample(const float *logits, int32_t n_vocab, const int32_t *hist, int32_t n_hist,
+                   const orc_sampler_params *p, uint64_t draw, int32_t *ids, float *cum,
+                   int32_t *n_kept, float *target)
+{
+    if (!logits || !p || n_vocab <= 0 || n_hist < 0 || (n_hist > 0 && !hist)) return -1;
+    orc_cand *c = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)n_vocab);
+    if (!c) return -1;
+    for (int32_t i = 0; i < n_vocab; i++) { c[i].l = logits[i]; c[i].id = i; }
+
+    /* repeat penalty: once per distinct token of the last penalty_last_n;
+       positive logits are divided by the penalty, negative ones multiplied */
+    if (p->repeat_penalty != 1.0f && p->penalty_last_n > 0) {
+        const int32_t w = n_hist < p->penalty_last_n ? n_hist : p->penalty_last_n;
+        for (int32_t j = n_hist - w; j < n_hist; j++) {
+            const int32_t t = hist[j];
+            if (t < 0 || t >= n_vocab) continue;
+            int seen = 0;
+            for (int32_t k = n_hist - w; k < j; k++) seen |= hist[k] == t;
+            if (seen) continue;
+            c[t].l = c[t].l > 0.0f ? c[t].l / p->repeat_penalty : c[t].l * p->repeat_penalty;
+        }
+    }
+    qsort(c, (size_t)n_vocab, sizeof(orc_cand), cand_cmp);
+
+    /* top-k */
+    int32_t n = (p->top_k > 0 && p->top_k < n_vocab) ? p->top_k : n_vocab;
+    const float m = c[0].l;   /* the leader stays first through every cut */
+
+    /* top-p: the shortest prefix whose weight reaches p of the total */
+    if (p->top_p < 1.0f) {
+        float s = 0.0f;
+        for (int32_t i = 0; i < n; i++) s += expf(c[i].l - m);
+        const float lim = p->top_p * s;
+        float a = 0.0f;
+        int32_t keep = n;
+        for (int32_t i = 0; i < n; i++) {
+            a += expf(c[i].l - m);
+            if (a >= lim) { keep = i + 1; break; }
+        }
+        n = keep;
+    }
+    /* min-p: weight relative to the leader */
+    if (p->min_p > 0.0f) {
+        int32_t keep = 1;
+        for (int32_t i = 1; i < n; i++)
+            if (expf(c[i].l - m) >= p->min_p) keep = i + 1;
+        n = keep;
+    }
+
+    int32_t tok;
+    if (p->temp <= 0.0f) {
+        tok = c[0].id;
+        if (n_kept) *n_kept = 0;
+        if (target) *target = 0.0f;
+    } else {
+        /* temperature, then the draw: the first candidate whose inclusive
+           cumulative weight exceeds u times the total */
+        float s = 0.0f;
+        for (int32_t i = 0; i < n; i++) {
+            s += expf(c[i].l / p->temp - m / p->temp);
+            if (cum) cum[i] = s;
+            if (ids) ids[i] = c[i].id;
+        }
+        const float t = orc_uniform24(p->seed, draw) * s;
+        float a = 0.0f;
+        tok = c[n - 1].id;
+        for (int32_t i = 0; i < n; i++) {
+            a += expf(c[i].l / p->temp - m / p->temp);
+            if (a > t) { tok = c[i].id; break; }
+        }
+        if (n_kept) *n_kept = n;
+        if (target) *target = t;
+    }
+    free(c);
+    return tok;
+}
+

@@ -136,6 +136,36 @@ int32_t orc_eval_tap(orc_ctx *c, int32_t seq, int32_t token, orc_real *logits,
 int32_t orc_kv_row(const orc_ctx *c, int32_t which, int32_t layer, int32_t seq,
                    int32_t pos, int32_t kv_head, float *out);
 
+/* ---- sampler chain (the article's step 15 sampler list) ----------------
+   Order as the article gives it: repeat penalty, top-k, top-p, min-p,
+   temperature, then one token drawn from the softmax of what is left.
+   Probabilities are computed in fp32, the precision the device uses for the
+   same decisions. */
+typedef struct {
+    int32_t  top_k;            /* keep the k largest (<= 0: all) */
+    float    top_p;            /* nucleus threshold in (0, 1]; 1 disables */
+    float    min_p;            /* relative floor in [0, 1); 0 disables */
+    float    temp;             /* > 0; <= 0 selects the leader (greedy) */
+    float    repeat_penalty;   /* >= 1; 1 disables */
+    int32_t  penalty_last_n;   /* history window for the penalty */
+    uint64_t seed;             /* seed of the draw stream */
+} orc_sampler_params;
+
+/* Output number `index` (0-based) of SplitMix64 started at state `seed`,
+   and its top 24 bits as a float in [0, 1). */
+uint64_t orc_splitmix64(uint64_t seed, uint64_t index);
+float    orc_uniform24(uint64_t seed, uint64_t index);
+
+/* Runs the chain on n_vocab fp32 logits with the token history hist[n_hist]
+   (oldest first) and draw number `draw`.  Returns the token, or -1 on bad
+   arguments.  When ids/cum are not NULL (capacity n_vocab) they receive the
+   surviving candidates in chain order and their inclusive cumulative
+   weights; *n_kept, *target receive their count and the draw's target
+   u * sum (both 0 for greedy). */
+int32_t orc_sample(const float *logits, int32_t n_vocab, const int32_t *hist, int32_t n_hist,
+                   const orc_sampler_params *p, uint64_t draw, int32_t *ids, float *cum,
+                   int32_t *n_kept, float *target);
+
 #ifdef __cplusplus
 }
 #endif
