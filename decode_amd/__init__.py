@@ -106,6 +106,13 @@ def lib() -> C.CDLL:
         "dec_get_probe": (i32, [vp, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
         "dec_set_use_graphs": (i32, [vp, i32]),
         "dec_version": (C.c_char_p, []),
+        "dec_sampler_new": (vp, [vp]),
+        "dec_sampler_accept": (i32, [vp, i32]),
+        "dec_sampler_sample": (i32, [vp, vp, i32]),
+        "dec_sampler_sample_row": (i32, [vp, vp, i32, vp]),
+        "dec_sampler_reset": (None, [vp]),
+        "dec_sampler_draws": (i64, [vp]),
+        "dec_sampler_free": (None, [vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -190,6 +197,53 @@ class Model:
     def close(self):
         if getattr(self, "ptr", None):
             self.L.dec_model_free(self.ptr)
+            self.ptr = None
+
+    def __del__(self):
+        self.close()
+
+
+class SamplerParams(C.Structure):
+    """Mirror of dec_sampler_params."""
+    _fields_ = [("top_k", C.c_int32), ("top_p", C.c_float), ("min_p", C.c_float), ("temp", C.c_float),
+                ("repeat_penalty", C.c_float), ("penalty_last_n", C.c_int32), ("seed", C.c_uint64)]
+
+
+class Sampler:
+    """The device sampler chain (dec_sampler_*)."""
+
+    def __init__(self, top_k=40, top_p=1.0, min_p=0.0, temp=1.0, repeat_penalty=1.0, penalty_last_n=64,
+                 seed=0):
+        self.L = lib()
+        p = SamplerParams(top_k, top_p, min_p, temp, repeat_penalty, penalty_last_n, seed)
+        self.ptr = self.L.dec_sampler_new(C.byref(p))
+        if not self.ptr:
+            raise DecodeError("dec_sampler_new rejected the parameters")
+
+    def accept(self, tokens) -> None:
+        for t in np.atleast_1d(np.asarray(tokens, np.int64)):
+            if self.L.dec_sampler_accept(self.ptr, int(t)) != 0:
+                raise DecodeError("dec_sampler_accept failed")
+
+    def sample(self, ctx, i: int = -1) -> int:
+        return int(self.L.dec_sampler_sample(self.ptr, ctx.ptr, i))
+
+    def sample_row(self, logits, stream=None) -> int:
+        """logits: float32 numpy array (host) or contiguous torch float32 tensor."""
+        if isinstance(logits, np.ndarray):
+            a = np.ascontiguousarray(logits, np.float32)
+            return int(self.L.dec_sampler_sample_row(self.ptr, a.ctypes.data, a.size, stream))
+        return int(self.L.dec_sampler_sample_row(self.ptr, _ptr(logits), logits.numel(), stream))
+
+    def reset(self) -> None:
+        self.L.dec_sampler_reset(self.ptr)
+
+    def draws(self) -> int:
+        return int(self.L.dec_sampler_draws(self.ptr))
+
+    def close(self):
+        if getattr(self, "ptr", None):
+            self.L.dec_sampler_free(self.ptr)
             self.ptr = None
 
     def __del__(self):

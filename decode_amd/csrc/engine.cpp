@@ -16,6 +16,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <new>
 #include <vector>
 
 #include "kernels.h"
@@ -931,6 +932,120 @@ extern "C" int32_t dec_argmax_all(dec_ctx *c, int32_t *out, int32_t cap) {
     if (!fetch_amax(c)) return -1;
     memcpy(out, c->host_amax.data(), (size_t)c->n_out * 4);
     return c->n_out;
+}
+
+// ---- sampler chain ---------------------------------------------------------
+struct dec_sampler {
+    dec_sampler_params p{};
+    std::vector<int32_t> hist;     // accepted tokens, at most the window kept
+    uint64_t draws = 0;
+    int32_t *d_hist = nullptr;     // device copy of the window
+    int32_t *d_out = nullptr;      // device token
+    int32_t *h_buf = nullptr;      // pinned: window [64] + token [1]
+    float *d_row = nullptr;        // device copy of a host logits row
+    size_t row_cap = 0;
+    hipStream_t own = nullptr;     // stream for rows given without one
+};
+
+extern "C" dec_sampler *dec_sampler_new(const dec_sampler_params *p) {
+    if (!p || p->top_k < 1 || p->top_k > 1024 || !(p->top_p > 0.0f && p->top_p <= 1.0f) ||
+        !(p->min_p >= 0.0f && p->min_p < 1.0f) || !(p->repeat_penalty >= 1.0f) || p->penalty_last_n < 0 ||
+        p->penalty_last_n > 64 || p->temp != p->temp)
+        return nullptr;
+    dec_sampler *s = new (std::nothrow) dec_sampler;
+    if (!s) return nullptr;
+    s->p = *p;
+    bool ok = true;
+    HIP_OK(hipMalloc((void **)&s->d_hist, 64 * 4), ok = false);
+    if (ok) HIP_OK(hipMalloc((void **)&s->d_out, 4), ok = false);
+    if (ok) HIP_OK(hipHostMalloc((void **)&s->h_buf, 65 * 4, 0), ok = false);
+    if (ok) HIP_OK(hipStreamCreateWithFlags(&s->own, hipStreamNonBlocking), ok = false);
+    if (!ok) {
+        dec_sampler_free(s);
+        return nullptr;
+    }
+    return s;
+}
+
+extern "C" int32_t dec_sampler_accept(dec_sampler *s, int32_t token) {
+    if (!s || token < 0) return -1;
+    s->hist.push_back(token);
+    if (s->hist.size() > 64) s->hist.erase(s->hist.begin(), s->hist.end() - 64);
+    return 0;
+}
+
+// Runs the chain on a device logits row on stream st; accepts the token.
+static int32_t sampler_run(dec_sampler *s, const float *row, int V, hipStream_t st) {
+    SampleArgs a;
+    const int w = (int)std::min<size_t>(s->hist.size(), (size_t)s->p.penalty_last_n);
+    a.n_hist = s->p.repeat_penalty != 1.0f ? w : 0;
+    a.n_vocab = V;
+    a.top_k = s->p.top_k;
+    a.top_p = s->p.top_p;
+    a.min_p = s->p.min_p;
+    a.temp = s->p.temp;
+    a.repeat_penalty = s->p.repeat_penalty;
+    a.seed = s->p.seed;
+    a.draw = s->draws;
+    a.hist = s->d_hist;
+    a.out = s->d_out;
+    if (a.n_hist > 0) {
+        memcpy(s->h_buf, s->hist.data() + (s->hist.size() - a.n_hist), (size_t)a.n_hist * 4);
+        HIP_OK(hipMemcpyAsync(s->d_hist, s->h_buf, (size_t)a.n_hist * 4, hipMemcpyHostToDevice, st), return -3);
+    }
+    if (!launch_sample(row, a, st)) return -1;
+    HIP_OK(hipGetLastError(), return -3);
+    HIP_OK(hipMemcpyAsync(s->h_buf + 64, s->d_out, 4, hipMemcpyDeviceToHost, st), return -3);
+    HIP_OK(hipStreamSynchronize(st), return -3);    // also frees h_buf for the next call
+    const int32_t tok = s->h_buf[64];
+    if (tok < 0 || tok >= V) return -3;
+    s->draws++;
+    dec_sampler_accept(s, tok);
+    return tok;
+}
+
+extern "C" int32_t dec_sampler_sample(dec_sampler *s, dec_ctx *c, int32_t i) {
+    if (!s || !c) return -1;
+    const int r = resolve_row(c, i);
+    if (r < 0) return -1;
+    const int V = c->m->hp.n_vocab;
+    return sampler_run(s, c->logits + (size_t)r * V, V, c->s);
+}
+
+extern "C" int32_t dec_sampler_sample_row(dec_sampler *s, const float *logits, int32_t n_vocab, void *hip_stream) {
+    if (!s || !logits || n_vocab <= 0) return -1;
+    hipStream_t st = hip_stream ? (hipStream_t)hip_stream : s->own;
+    const float *row = logits;
+    if (!is_device_ptr(logits)) {
+        if (s->row_cap < (size_t)n_vocab) {
+            if (s->d_row) (void)hipFree(s->d_row);
+            s->d_row = nullptr;
+            s->row_cap = 0;
+            HIP_OK(hipMalloc((void **)&s->d_row, (size_t)n_vocab * 4), return -3);
+            s->row_cap = (size_t)n_vocab;
+        }
+        HIP_OK(hipMemcpyAsync(s->d_row, logits, (size_t)n_vocab * 4, hipMemcpyHostToDevice, st), return -3);
+        row = s->d_row;
+    }
+    return sampler_run(s, row, n_vocab, st);
+}
+
+extern "C" void dec_sampler_reset(dec_sampler *s) {
+    if (!s) return;
+    s->hist.clear();
+    s->draws = 0;
+}
+
+extern "C" int64_t dec_sampler_draws(const dec_sampler *s) { return s ? (int64_t)s->draws : -1; }
+
+extern "C" void dec_sampler_free(dec_sampler *s) {
+    if (!s) return;
+    if (s->d_hist) (void)hipFree(s->d_hist);
+    if (s->d_out) (void)hipFree(s->d_out);
+    if (s->h_buf) (void)hipHostFree(s->h_buf);
+    if (s->d_row) (void)hipFree(s->d_row);
+    if (s->own) (void)hipStreamDestroy(s->own);
+    delete s;
 }
 
 extern "C" int32_t dec_seq_pos_max(const dec_ctx *c, int32_t seq) {

@@ -158,3 +158,18 @@ struct FlashArgs {
 bool launch_flash_prefill(const FlashArgs &a, hipStream_t s);
 
 // f16 -> (rows of) GGUF-style export helpers are host code in engine.cpp.
+
+// The sampler chain on one logits row (device): repeat penalty over the
+// distinct tokens of hist[0..n_hist), top-k (1..1024), top-p, min-p,
+// temperature (<= 0: the leader), then the draw with u from SplitMix64(seed,
+// draw).  Writes the token to out[0].  Returns false (nothing launched) when
+// the sizes are not covered (n_vocab <= 32768, n_hist <= 64).
+struct SampleArgs {
+    const int32_t *hist = nullptr;
+    int n_hist = 0, n_vocab = 0, top_k = 0;
+    float top_p = 1.f, min_p = 0.f, temp = 1.f, repeat_penalty = 1.f;
+    uint64_t seed = 0, draw = 0;
+    int32_t *out = nullptr;
+};
+bool launch_sample(const float *logits, const SampleArgs &a, hipStream_t s);
+

@@ -168,6 +168,61 @@ int32_t dec_argmax(dec_ctx *c, int32_t i);
  * (n = the value returned); returns -1 if cap is too small. */
 int32_t dec_argmax_all(dec_ctx *c, int32_t *out, int32_t cap);
 
+/* ---- sampler chain (article step 15: the sampler list) ------------------
+ * Applied in the article's order: repeat penalty on the recent history,
+ * top-k, top-p, min-p, temperature, then one token drawn from the softmax of
+ * the survivors.  Readings where the article gives only the idea: the
+ * penalty divides a positive logit and multiplies a negative one, once per
+ * distinct token of the last penalty_last_n accepted tokens; candidates are
+ * ordered by logit, the lower token id first on ties; top-p keeps the
+ * shortest prefix whose weight exp(l - leader) reaches top_p of the total;
+ * min-p keeps weights >= min_p; the temperature divides the survivors'
+ * logits; the draw takes the first candidate whose inclusive cumulative
+ * weight exceeds u times the total, with u the top 24 bits of output number
+ * `draws` of SplitMix64(seed) (Steele, Lea, Flood 2014), draws counting the
+ * sampler's draws so far.  All weights are fp32. */
+typedef struct {
+    int32_t  top_k;            /* 1..1024 candidates kept by top-k */
+    float    top_p;            /* (0, 1]; 1 disables */
+    float    min_p;            /* [0, 1); 0 disables */
+    float    temp;             /* > 0; <= 0 picks the leader (greedy) */
+    float    repeat_penalty;   /* >= 1; 1 disables */
+    int32_t  penalty_last_n;   /* 0..64 accepted tokens the penalty looks at */
+    uint64_t seed;             /* seed of the draw stream */
+} dec_sampler_params;
+
+typedef struct dec_sampler dec_sampler;
+
+/* A sampler with its own token history and draw count (the chain of the
+ * article's llama_sampler_chain_init / _add: parameters are fixed when it is
+ * built).  Allocates small device buffers (and a stream) on the current
+ * device.  NULL on parameters out of range or allocation failure. */
+dec_sampler *dec_sampler_new(const dec_sampler_params *p);
+
+/* Appends token (>= 0) to the history, e.g. the prompt.  0, or -1. */
+int32_t dec_sampler_accept(dec_sampler *s, int32_t token);
+
+/* Samples from output row i of ctx's last call (indexing as dec_get_logits)
+ * on the device, on ctx's stream; accepts the token and counts the draw.
+ * Synchronizes the stream.  Returns the token, -1 for an invalid row or a
+ * vocabulary over 32768 / below top_k, -3 on a device error. */
+int32_t dec_sampler_sample(dec_sampler *s, dec_ctx *c, int32_t i);
+
+/* The same chain on a logits row given by the caller (the article's chain
+ * applied to an arbitrary candidate array): n_vocab floats in device memory
+ * or host memory (copied to the device first), sampled on hip_stream (NULL:
+ * the sampler's own stream).  Accepts the token and counts the draw.
+ * Returns the token, -1 for bad arguments, -3 on a device error. */
+int32_t dec_sampler_sample_row(dec_sampler *s, const float *logits, int32_t n_vocab, void *hip_stream);
+
+/* Forgets the history and restarts the draw stream at draw 0. */
+void dec_sampler_reset(dec_sampler *s);
+
+/* Number of draws made (the index of the next one). */
+int64_t dec_sampler_draws(const dec_sampler *s);
+
+void dec_sampler_free(dec_sampler *s);
+
 /* Largest cached position of a sequence, -1 when empty (the memory module's
  * seq_pos_max, KV-cache appendix). */
 int32_t dec_seq_pos_max(const dec_ctx *c, int32_t seq);
