@@ -160,7 +160,8 @@ def main():
         torch.cuda.empty_cache()
 
     prompt = synth.prompt(hp["n_vocab"], n_prompt, 2000 + W["seed"] % 1000)
-    n_ctx = n_prompt + steps + warm + 8
+    n_sampled = 64                      # decode steps run with the sampler chain after the timed loop
+    n_ctx = n_prompt + steps + warm + n_sampled + 8
     ctx = dec.Context(model, n_ctx=n_ctx, n_batch=n_prompt, n_ubatch=W["n_ubatch"], stream=sp)
     probe_layer = hp["n_layer"] // 2
     ctx.set_probe(dec.K_FFN_GU, probe_layer)
@@ -197,6 +198,33 @@ def main():
     dc_probe = ctx.probe()
     st = ctx.stats()
     log(f"prefill {n_prompt / prefill_s:.0f} tok/s, decode {steps / decode_s:.1f} tok/s")
+
+    # the sampler chain in the generation loop (after, and outside, the timed region):
+    # penalty over the last 64 tokens, top-k 40, top-p 0.95, min-p 0.05, temperature 0.8
+    sprm = dict(top_k=40, top_p=0.95, min_p=0.05, temp=0.8, repeat_penalty=1.1, penalty_last_n=64, seed=1234)
+    smp = dec.Sampler(**sprm)
+    smp.accept(prompt[-64:])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_sampled):
+        tok = smp.sample(ctx, 0)
+        if tok < 0 or ctx.decode([tok], [0]) != 0:
+            raise RuntimeError("sampled decode step failed")
+    torch.cuda.synchronize()
+    sampled_s = time.perf_counter() - t0
+    n_calls = 256
+    t0 = time.perf_counter()
+    for _ in range(n_calls):
+        if smp.sample(ctx, 0) < 0:
+            raise RuntimeError("dec_sampler_sample failed")
+    call_s = (time.perf_counter() - t0) / n_calls
+    smp.close()
+    sampler = {"chain": sprm, "n_vocab": hp["n_vocab"],
+               "decode_tokens_per_s_sampled": round(n_sampled / sampled_s, 2),
+               "us_per_call": round(call_s * 1e6, 2),
+               "note": "us_per_call = one dec_sampler_sample on a resident logits row: history upload, "
+                       "the k_sample kernel, token download and stream synchronisation"}
+    log(f"sampled decode {n_sampled / sampled_s:.1f} tok/s, sampler call {call_s * 1e6:.1f} us")
 
     alg = algorithmic(hp, n_prompt, steps)
     F, d = hp["n_ff"], hp["n_embd"]
@@ -271,6 +299,7 @@ def main():
         "roofline": roofline,
         "prefill_roofline": pf_roof,
         "graph_replays": st["n_graph_replays"],
+        "sampler": sampler,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -939,9 +939,8 @@ struct dec_sampler {
     dec_sampler_params p{};
     std::vector<int32_t> hist;     // accepted tokens, at most the window kept
     uint64_t draws = 0;
-    int32_t *d_hist = nullptr;     // device copy of the window
-    int32_t *d_out = nullptr;      // device token
-    int32_t *h_buf = nullptr;      // pinned: window [64] + token [1]
+    int32_t *h_buf = nullptr;      // mapped pinned: window [64] + token [1]
+    int32_t *g_buf = nullptr;      // device address of h_buf
     float *d_row = nullptr;        // device copy of a host logits row
     size_t row_cap = 0;
     hipStream_t own = nullptr;     // stream for rows given without one
@@ -956,9 +955,8 @@ extern "C" dec_sampler *dec_sampler_new(const dec_sampler_params *p) {
     if (!s) return nullptr;
     s->p = *p;
     bool ok = true;
-    HIP_OK(hipMalloc((void **)&s->d_hist, 64 * 4), ok = false);
-    if (ok) HIP_OK(hipMalloc((void **)&s->d_out, 4), ok = false);
-    if (ok) HIP_OK(hipHostMalloc((void **)&s->h_buf, 65 * 4, 0), ok = false);
+    HIP_OK(hipHostMalloc((void **)&s->h_buf, 65 * 4, hipHostMallocMapped), ok = false);
+    if (ok) HIP_OK(hipHostGetDevicePointer((void **)&s->g_buf, s->h_buf, 0), ok = false);
     if (ok) HIP_OK(hipStreamCreateWithFlags(&s->own, hipStreamNonBlocking), ok = false);
     if (!ok) {
         dec_sampler_free(s);
@@ -987,16 +985,16 @@ static int32_t sampler_run(dec_sampler *s, const float *row, int V, hipStream_t 
     a.repeat_penalty = s->p.repeat_penalty;
     a.seed = s->p.seed;
     a.draw = s->draws;
-    a.hist = s->d_hist;
-    a.out = s->d_out;
-    if (a.n_hist > 0) {
+    // the window and the token travel through mapped pinned memory: the kernel
+    // reads the one and writes the other directly, visible at the stream sync
+    a.hist = s->g_buf;
+    a.out = s->g_buf + 64;
+    if (a.n_hist > 0)
         memcpy(s->h_buf, s->hist.data() + (s->hist.size() - a.n_hist), (size_t)a.n_hist * 4);
-        HIP_OK(hipMemcpyAsync(s->d_hist, s->h_buf, (size_t)a.n_hist * 4, hipMemcpyHostToDevice, st), return -3);
-    }
+    s->h_buf[64] = -1;
     if (!launch_sample(row, a, st)) return -1;
     HIP_OK(hipGetLastError(), return -3);
-    HIP_OK(hipMemcpyAsync(s->h_buf + 64, s->d_out, 4, hipMemcpyDeviceToHost, st), return -3);
-    HIP_OK(hipStreamSynchronize(st), return -3);    // also frees h_buf for the next call
+    HIP_OK(hipStreamSynchronize(st), return -3);
     const int32_t tok = s->h_buf[64];
     if (tok < 0 || tok >= V) return -3;
     s->draws++;
@@ -1040,8 +1038,6 @@ extern "C" int64_t dec_sampler_draws(const dec_sampler *s) { return s ? (int64_t
 
 extern "C" void dec_sampler_free(dec_sampler *s) {
     if (!s) return;
-    if (s->d_hist) (void)hipFree(s->d_hist);
-    if (s->d_out) (void)hipFree(s->d_out);
     if (s->h_buf) (void)hipHostFree(s->h_buf);
     if (s->d_row) (void)hipFree(s->d_row);
     if (s->own) (void)hipStreamDestroy(s->own);

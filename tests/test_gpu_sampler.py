@@ -158,6 +158,23 @@ def test_penalty_hits_the_leader(dec, orc):
     run_case(dec, orc, rows, prm, hist0=[0, 0, 0, 1, 2, 2])
 
 
+def test_dense_ties_and_minus_inf(dec, orc):
+    """Rows whose nearest logits are too many to compact (all equal, a few
+    integer values over 32000 tokens) take the exact radix-select path; -inf
+    entries must never be drawn unless nothing else is left."""
+    r = np.random.default_rng(9)
+    rows = [np.zeros(32000, np.float32),
+            r.integers(-3, 4, 32000).astype(np.float32),
+            r.integers(0, 2, 32000).astype(np.float32)]
+    x = (r.standard_normal(32000) * 3).astype(np.float32)
+    x[r.integers(0, 32000, 20000)] = -np.inf
+    rows.append(x)
+    for prm in (dict(top_k=40, top_p=0.9, min_p=0.0, temp=1.0, repeat_penalty=1.0, penalty_last_n=64, seed=13),
+                dict(top_k=1024, top_p=1.0, min_p=0.0, temp=1.0, repeat_penalty=1.3, penalty_last_n=64, seed=14),
+                dict(top_k=7, top_p=1.0, min_p=0.2, temp=0.0, repeat_penalty=1.0, penalty_last_n=64, seed=15)):
+        run_case(dec, orc, rows * 3, prm, hist0=[0, 1, 2, 31999])
+
+
 @pytest.mark.parametrize("V", [1, 2, 1023, 32768])
 def test_vocab_edges(dec, orc, V):
     k = min(V, 1024)
