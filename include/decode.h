@@ -7,8 +7,9 @@
  * create a context that owns the KV cache and every work buffer (step 7),
  * run a prompt as a batch split into ubatches (steps 10-13), run one new
  * token per step (the generation loop of step 8 and the KV-cache appendix),
- * read the logits (step 14) and take the greedy token (step 15).
- * Tokenization, text and sampler chains are not part of this library.
+ * read the logits (step 14) and take the greedy token or run the sampler
+ * chain on the device (step 15).  Tokenization and text are not part of
+ * this library.
  *
  * Conventions for every call:
  *  - Handles are opaque and owned by the library.
@@ -195,8 +196,12 @@ typedef struct dec_sampler dec_sampler;
 
 /* A sampler with its own token history and draw count (the chain of the
  * article's llama_sampler_chain_init / _add: parameters are fixed when it is
- * built).  Allocates small device buffers (and a stream) on the current
- * device.  NULL on parameters out of range or allocation failure. */
+ * built).  Allocates 260 bytes of mapped pinned host memory (the history
+ * window and the drawn token pass through it, read and written by the
+ * kernel directly) and a stream on the current device.  Not thread-safe: one
+ * caller at a time per sampler.  NULL on parameters out of range or
+ * allocation failure.  Logits must not be NaN (the drawn token is then
+ * unspecified, or -3). */
 dec_sampler *dec_sampler_new(const dec_sampler_params *p);
 
 /* Appends token (>= 0) to the history, e.g. the prompt.  0, or -1. */
