@@ -15,25 +15,27 @@
 //   2. per head: m = max_j s, e_j = exp(s_j - m), l = sum_j e_j;
 //   3. acc[h][d] = sum_j e_j V_j[d]: HD/2 threads per row, 2 elements each.
 // The block writes (m, l, acc) for its chunk.  A second kernel merges the
-// chunks of each (token, head) in chunk order,
+// chunks of each (token, head),
 //   M = max_c m_c, L = sum_c l_c e^(m_c - M), o = sum_c acc_c e^(m_c - M) / L,
-// with the chunk weights computed once per block and the HD-wide sums split
-// over chunk groups, and writes o in f16 for the output projection.  The
-// grid covers the context's largest chunk count; blocks past a token's last
-// chunk exit at once, so one captured launch serves every decode step.
+// with the chunk statistics and the partial rows all requested at entry, and
+// writes o in f16 (value + remainder) for the output projection.  The grid
+// covers the context's largest chunk count; blocks past a token's last chunk
+// exit at once, so one captured launch serves every decode step.
 //
 // f16 cache, head_dim 64 / 128: the chunk partials come from matrix cores
-// instead (k_attn_mfma, 128-key chunks, same partial format).  Each
-// wavefront takes 32 keys:
-//   S^T[key][head] = K Q^T   v_mfma_f32_32x32x16_f16, K rows loaded straight
-//                            into the A operand, Q (scaled by 1/sqrt(hd)) as
-//                            f16 value + remainder fragments built once per
-//                            block in LDS, so every product is exact;
+// instead (k_attn_mfma, 64-key chunks, same partial format).  Each
+// wavefront takes 32 keys and loads everything at entry:
+//   S^T[key][head] = K Q^T   v_mfma_f32_32x32x16_f16, K rows straight into
+//                            the A operand, Q / sqrt(hd) as f16 value +
+//                            remainder (written so by the QKV epilogue) as B,
+//                            so every product is exact;
 //   softmax per head column over the wavefront's keys;
-//   O^T[dim][head] += V^T P^T  with P (value + remainder) taken from the S^T
-//                            accumulators and V^T staged in LDS, its keys
-//                            permuted to match the accumulator order.
-// The block's wavefronts are then combined into one chunk partial.
+//   O[head][dim] = P V       A = P (value + remainder) taken from the S^T
+//                            accumulators as they lie; B = V read straight
+//                            from the cache, each lane gathering the 16 keys
+//                            its accumulators hold for one dim (2-byte loads
+//                            that 32 lanes turn into one 64-byte row segment).
+// The block's two wavefronts are then combined into one chunk partial.
 #include "common.h"
 #include "kernels.h"
 
@@ -208,22 +210,33 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
     }
 }
 
-// Merge of the chunk partials of one (head, token): 256 threads = HD/2
-// element pairs x (512/HD) chunk groups.
+// Merge of the chunk partials of one (head, token).  Every load is issued
+// at once -- the chunk statistics into LDS, each thread's partial rows
+// (4 elements of up to MPT chunks) into registers -- then
+//   M = max_c m_c, w_c = e^(m_c - M), L = sum_c l_c w_c, o = sum_c acc_c w_c / L.
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
-    constexpr int TPR = HD / 2, CG = 256 / TPR;
+    constexpr int TPR = HD / 4;          // threads per partial row
+    constexpr int CG = 256 / TPR;        // chunk groups
+    constexpr int MPT = 16;              // chunks per thread per round
+    __shared__ float2 mls[1024];
     __shared__ float wgt[1024];
     __shared__ float red[4];
-    __shared__ float2 part2[CG][TPR];
+    __shared__ f4 sum4[CG][TPR];
     const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nch = a.tok.pos[t] / a.chunk + 1;
     const size_t hh = (size_t)t * a.H + h;
     const float *ml = a.ml + hh * a.max_chunks * 2;
     const float *pa = a.part + hh * a.max_chunks * HD;
-    // chunk weights e^(m_c - M) and L
+    const int dq = tid % TPR, cg = tid / TPR;
+    // first round of partial rows (clamped to the last chunk; weighted 0 past it)
+    f4 v[MPT];
+#pragma unroll
+    for (int i = 0; i < MPT; i++) v[i] = *(const f4 *)(pa + (size_t)min(cg + CG * i, nch - 1) * HD + 4 * dq);
+    for (int cc = tid; cc < nch; cc += 256) mls[cc] = *(const float2 *)(ml + 2 * cc);
+    __syncthreads();
     float mloc = -INFINITY;
-    for (int cc = tid; cc < nch; cc += 256) mloc = fmaxf(mloc, ml[2 * cc]);
+    for (int cc = tid; cc < nch; cc += 256) mloc = fmaxf(mloc, mls[cc].x);
     mloc = row16_max(mloc);
     mloc = fmaxf(fmaxf(readlane_f(mloc, 0), readlane_f(mloc, 16)), fmaxf(readlane_f(mloc, 32), readlane_f(mloc, 48)));
     if (lane == 0) red[w] = mloc;
@@ -232,67 +245,57 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     __syncthreads();
     float lsum = 0.f;
     for (int cc = tid; cc < nch; cc += 256) {
-        const float f = __expf(ml[2 * cc] - M);
+        const float f = mls[cc].x == -INFINITY ? 0.f : __expf(mls[cc].x - M);
         wgt[cc] = f;
-        lsum += ml[2 * cc + 1] * f;
+        lsum += mls[cc].y * f;
     }
     lsum = wave_sum_dpp(lsum);
     if (lane == 0) red[w] = lsum;
     __syncthreads();
     const float L = (red[0] + red[1]) + (red[2] + red[3]);
-    // element pair dp, chunk group cg: chunks cg, cg + CG, ...
-    const int dp = tid % TPR, cg = tid / TPR;
-    float2 acc = make_float2(0.f, 0.f);
-#pragma unroll 4
-    for (int cc = cg; cc < nch; cc += CG) {
-        const float2 v = *(const float2 *)(pa + (size_t)cc * HD + 2 * dp);
-        const float f = wgt[cc];
-        acc.x += v.x * f;
-        acc.y += v.y * f;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < MPT; i++)
+        if (cg + CG * i < nch) acc += v[i] * wgt[cg + CG * i];
+    for (int c0 = CG * MPT; c0 < nch; c0 += CG * MPT) {      // contexts past CG*MPT chunks
+#pragma unroll
+        for (int i = 0; i < MPT; i++) v[i] = *(const f4 *)(pa + (size_t)min(c0 + cg + CG * i, nch - 1) * HD + 4 * dq);
+#pragma unroll
+        for (int i = 0; i < MPT; i++)
+            if (c0 + cg + CG * i < nch) acc += v[i] * wgt[c0 + cg + CG * i];
     }
-    part2[cg][dp] = acc;
+    sum4[cg][dq] = acc;
     __syncthreads();
     if (cg == 0) {
-        float2 s = part2[0][dp];
+        f4 s4 = sum4[0][dq];
 #pragma unroll
-        for (int k = 1; k < CG; k++) {
-            s.x += part2[k][dp].x;
-            s.y += part2[k][dp].y;
+        for (int k = 1; k < CG; k++) s4 += sum4[k][dq];
+        h2 o[2], ol[2];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float ov = s4[e] / L;
+            const f16 oh = (f16)ov;
+            o[e >> 1][e & 1] = oh;
+            ol[e >> 1][e & 1] = (f16)(ov - (float)oh);
         }
-        const float ox = s.x / L, oy = s.y / L;
-        h2 o, ol;
-        o.x = (f16)ox;
-        o.y = (f16)oy;
-        ol.x = (f16)(ox - (float)o.x);
-        ol.y = (f16)(oy - (float)o.y);
-        const size_t off = (size_t)t * a.H * HD + (size_t)h * HD + 2 * dp;
-        *(h2 *)((f16 *)a.o + off) = o;
-        if (a.o_lo) *(h2 *)((f16 *)a.o_lo + off) = ol;
+        const size_t off = (size_t)t * a.H * HD + (size_t)h * HD + 4 * dq;
+        *(uint2 *)((f16 *)a.o + off) = make_uint2(h2_bits(o[0]), h2_bits(o[1]));
+        if (a.o_lo) *(uint2 *)((f16 *)a.o_lo + off) = make_uint2(h2_bits(ol[0]), h2_bits(ol[1]));
     }
 }
 
 constexpr int MW = 2;                // wavefronts per block of the MFMA kernel
 constexpr int CHM = 32 * MW;        // cached rows per chunk of the MFMA kernel
 
-// Column of key k (0..31) in a wavefront's V^T tile: within each 16-key
-// group bits 2 and 3 swap, so that 8 consecutive columns hold the keys a
-// lane's accumulators r = 8s..8s+7 belong to (keys 16s + 8(r/4 % 2) + 4(lane/32) + r%4).
-DEV int vt_key_col(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
-
 template <int HD>
 __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
-    constexpr int KS = HD / 16;          // k-steps of K Q^T
-    constexpr int DT = HD / 32;          // 32-row dim tiles of O^T
-    constexpr int VC = HD / 16;          // 16-byte V chunks per lane (32 keys x HD/8 chunks / 64 lanes)
-    static_assert(VC % 2 == 0, "two keys per lane");
-    constexpr int VST = 32 + 8;          // f16 stride of a V^T row
-    __shared__ __attribute__((aligned(16))) f16 Vt[MW][HD][VST];
+    constexpr int KS = HD / 16;          // k-steps of S^T = K Q^T
+    constexpr int DT = HD / 32;          // 32-dim tiles of O = P V
     __shared__ float cm[MW][32], cl[MW][32];
     __shared__ __attribute__((aligned(16))) float co[MW][GMAX][HD];
-    __shared__ __attribute__((aligned(16))) h8 qf[2][KS][64];   // Q^T operand fragments: value, remainder
 
     const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, ln = lane & 31;
     const int pos = a.tok.pos[t], seq = a.tok.seq[t];
     const int G = a.H / a.kv.n_kv;
     const int c0 = c * CHM;
@@ -302,48 +305,34 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
     const f16 *Kb = (const f16 *)a.kv.k + base;
     const f16 *Vb = (const f16 *)a.kv.v + base;
 
-    // ---- loads: K rows in A-operand layout, V rows for the transpose, Q ----
-    // rows past pos are replaced by row pos (finite data; their weights are 0)
-    const int kr = min(k0 + (lane & 31), pos);
+    // ---- every load at entry; rows past pos are replaced by row pos (finite
+    // data whose weights are 0) ----
+    // A operand of S^T: key k0 + lane%32, dims 16 ks + 8 (lane/32) .. + 7
     h8 kf[KS];
+    const int kr = min(k0 + ln, pos);
 #pragma unroll
-    for (int ks = 0; ks < KS; ks++) kf[ks] = *(const h8 *)(Kb + (size_t)kr * HD + 16 * ks + 8 * (lane >> 5));
-    // V: lane l holds keys 2(l%16), 2(l%16)+1 at dims 8 d8 .. 8 d8 + 7 with
-    // d8 = l/16 + 4i, so that its LDS writes pack two keys per dword
-    const int vj = lane & 15, vg = lane >> 4;
-    h8 va[VC / 2], vb[VC / 2];
+    for (int ks = 0; ks < KS; ks++) kf[ks] = *(const h8 *)(Kb + (size_t)kr * HD + 16 * ks + 8 * hf);
+    // B operand of S^T: head lane%32 (clamped to the group; the extra columns
+    // are ignored), the same dims, q / sqrt(hd) as value + remainder
+    h8 qa[KS], qb[KS];
+    const size_t qo = ((size_t)t * a.H + g * G + min(ln, G - 1)) * HD + 8 * hf;
 #pragma unroll
-    for (int i = 0; i < VC / 2; i++) {
-        const int d8 = vg + 4 * i;
-        va[i] = *(const h8 *)(Vb + (size_t)min(k0 + 2 * vj, pos) * HD + 8 * d8);
-        vb[i] = *(const h8 *)(Vb + (size_t)min(k0 + 2 * vj + 1, pos) * HD + 8 * d8);
+    for (int ks = 0; ks < KS; ks++) {
+        qa[ks] = *(const h8 *)((const f16 *)a.qh + qo + 16 * ks);
+        qb[ks] = *(const h8 *)((const f16 *)a.ql + qo + 16 * ks);
     }
-    const int hc = lane & 31;                          // this lane's head column
-    const bool hv = hc < G;
-    // Q^T operand of lane l, k-step ks: head l%32 (zero past G), dims
-    // 16 ks + 8 (l/32) .. +7, scaled by 1/sqrt(hd), as f16 value + remainder;
-    // built once per block in LDS
-    for (int f = tid; f < KS * 64; f += MW * 64) {
-        const int ks = f / 64, fl = f % 64, fh = fl & 31;
-        h8 vh, vl;
-        if (fh < G) {
-            const float qs = 1.0f / sqrtf((float)HD);
-            const float *qr = a.q + ((size_t)t * a.H + g * G + fh) * HD + 16 * ks + 8 * (fl >> 5);
-            const f4 lo = *(const f4 *)qr, hi = *(const f4 *)(qr + 4);
+    // B operand of O = P V for k-step s: element e of lane l is key
+    // 16 s + 8 (e/4) + 4 (l/32) + e%4 -- the keys whose probabilities the lane
+    // holds in its S^T accumulators 8 s + e -- at dim 32 dt + l%32
+    h8 vb[DT][2];
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const float y = (e < 4 ? lo[e] : hi[e - 4]) * qs;
-                vh[e] = (f16)y;
-                vl[e] = (f16)(y - (float)vh[e]);
-            }
-        } else {
+    for (int s = 0; s < 2; s++)
 #pragma unroll
-            for (int e = 0; e < 8; e++) vh[e] = vl[e] = (f16)0.f;
+        for (int e = 0; e < 8; e++) {
+            const int key = min(k0 + 16 * s + 8 * (e >> 2) + 4 * hf + (e & 3), pos);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) vb[dt][s][e] = Vb[(size_t)key * HD + 32 * dt + ln];
         }
-        qf[0][ks][fl] = vh;
-        qf[1][ks][fl] = vl;
-    }
-    __syncthreads();
 
     // ---- S^T = K Q^T (exact products, fp32 accumulation) ----
     f16x sacc;
@@ -351,15 +340,15 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
     for (int r = 0; r < 16; r++) sacc[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[0][ks][lane], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[1][ks][lane], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qa[ks], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qb[ks], sacc, 0, 0, 0);
     }
 
     // ---- causal mask and this wavefront's softmax statistics per head ----
     float m = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-        const int key = k0 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int key = k0 + (r >> 2) * 8 + 4 * hf + (r & 3);
         if (key > pos) sacc[r] = -INFINITY;
         m = fmaxf(m, sacc[r]);
     }
@@ -376,49 +365,31 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
     }
     l += __shfl_xor(l, 32, 64);
 
-    // ---- V^T of this wavefront's keys into LDS ----
-    // (keys 2j and 2j+1 land in adjacent columns; the element order is
-    // rotated per lane group so the four groups of a store use different banks)
-    {
-        const int col = vt_key_col(2 * vj);
-#pragma unroll
-        for (int i = 0; i < VC / 2; i++) {
-            const int d8 = vg + 4 * i;
-#pragma unroll
-            for (int e0 = 0; e0 < 8; e0++) {
-                const int e = (e0 + 2 * vg) & 7;
-                *(h2 *)&Vt[w][8 * d8 + e][col] = h2{va[i][e], vb[i][e]};
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- O^T = V^T P^T ----
+    // ---- O = P V: A = P (value + remainder) straight from the accumulators ----
     f16x o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
 #pragma unroll
         for (int r = 0; r < 16; r++) o[dt][r] = 0.f;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; s2++) {
-            const h8 vf = *(const h8 *)(&Vt[w][32 * dt + (lane & 31)][16 * s2 + 8 * (lane >> 5)]);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, ph[s2], o[dt], 0, 0, 0);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pl[s2], o[dt], 0, 0, 0);
+        for (int s = 0; s < 2; s++) {
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ph[s], vb[dt][s], o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pl[s], vb[dt][s], o[dt], 0, 0, 0);
         }
     }
 
     // ---- combine the block's wavefronts into the chunk partial ----
-    if (hv) {
-        if (lane < 32) {
-            cm[w][hc] = m;
-            cl[w][hc] = l;
-        }
+    // O row (head) of accumulator r < 4 is 4 (lane/32) + r, column lane%32
+    if (lane < 32) {
+        cm[w][ln] = m;
+        cl[w][ln] = l;
+    }
 #pragma unroll
-        for (int dt = 0; dt < DT; dt++)
+    for (int r = 0; r < 4; r++) {
+        const int hh = 4 * hf + r;
+        if (hh < G)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; q4++)
-                *(f4 *)&co[w][hc][32 * dt + q4 * 8 + (lane >> 5) * 4] =
-                    f4{o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]};
+            for (int dt = 0; dt < DT; dt++) co[w][hh][32 * dt + ln] = o[dt][r];
     }
     __syncthreads();
     const size_t mc = (size_t)a.max_chunks;
@@ -464,7 +435,7 @@ bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
     bool ok;
     if (mfma_path(a.kv.kvtype, HD)) {
         if constexpr (HD <= 128) {
-            if (a.H / a.kv.n_kv > GMAX) return false;
+            if (a.H / a.kv.n_kv > GMAX || !a.qh || !a.ql) return false;
             launch(k_attn_mfma<HD>, dim3(a.max_chunks, a.kv.n_kv, T), dim3(MW * 64), 0, s, a);
             ok = true;
         } else {

@@ -347,8 +347,10 @@ struct dec_ctx {
     std::vector<KVLayer> kv;
     float *rope_cs = nullptr;
     float *x = nullptr, *q = nullptr, *part = nullptr, *ml = nullptr, *logits = nullptr;
+    float *ssp = nullptr;   // [Tmax][SS_SLOTS] partial sums of squares of the rows of x
     float *gws = nullptr;      // K-split partial tiles of the ubatch GEMMs
     size_t gws_bytes = 0;
+    uint16_t *qh = nullptr, *ql = nullptr;   // q / sqrt(hd) as f16 value + remainder
     uint16_t *xn = nullptr, *xn_lo = nullptr, *o = nullptr, *h = nullptr, *o_lo = nullptr,
              *h_lo = nullptr;
     int32_t *amax = nullptr, *dev_step = nullptr, *host_step = nullptr;
@@ -509,7 +511,10 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
         c->x = (float *)c->mem.get(T * d * 4);
         c->xn = (uint16_t *)c->mem.get(T * d * 2);
         c->xn_lo = (uint16_t *)c->mem.get(T * d * 2);
+        c->ssp = (float *)c->mem.get(T * SS_SLOTS * 4);
         c->q = (float *)c->mem.get(T * qd * 4);
+        c->qh = (uint16_t *)c->mem.get(T * qd * 2);
+        c->ql = (uint16_t *)c->mem.get(T * qd * 2);
         c->o = (uint16_t *)c->mem.get(T * qd * 2);
         c->h = (uint16_t *)c->mem.get(T * Fp * 2);
         c->o_lo = (uint16_t *)c->mem.get(T * qd * 2);
@@ -526,7 +531,7 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
         c->logits = (float *)c->mem.get((size_t)c->n_out_cap * V * 4);
         c->amax = (int32_t *)c->mem.get((size_t)c->n_out_cap * 4);
         c->dev_step = (int32_t *)c->mem.get((size_t)c->step_cap * 3 * 4);
-        ok = c->rope_cs && c->x && c->xn && c->xn_lo && c->q && c->o && c->h && c->o_lo && c->h_lo && c->part && c->ml && c->logits &&
+        ok = c->rope_cs && c->x && c->ssp && c->xn && c->xn_lo && c->q && c->qh && c->ql && c->o && c->h && c->o_lo && c->h_lo && c->part && c->ml && c->logits &&
              (c->gws || !c->gws_bytes) &&
              c->amax && c->dev_step;
     }
@@ -633,7 +638,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
     c->seg_cur = SEG_PRE;
 
     ok = stage(c, -1, -1, [&] {
-        launch_embed(m->tok, tok, T, c->x, d, s);
+        launch_embed(m->tok, tok, T, c->x, d, c->ssp, s);
         return true;
     });
     for (int l = 0; ok && l < h.n_layer; l++) {
@@ -641,6 +646,9 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         EpiArgs eq;
         eq.epi = EPI_QKV;
         eq.qout = c->q;
+        eq.qh = c->qh;
+        eq.ql = c->ql;
+        eq.qscale = 1.0f / sqrtf((float)h.head_dim);
         eq.qd = qd;
         eq.kd = m->kd;
         eq.kv = c->kv[l];
@@ -651,6 +659,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 InArgs in;
                 in.x32 = c->x;
                 in.norm_g = L.attn_norm;
+                in.ss_part = c->ssp;
                 in.eps = h.rms_eps;
                 in.ldx = d;
                 return launch_matvec(L.wqkv, in, eq, T, s);
@@ -660,6 +669,8 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         });
         AttnArgs at;
         at.q = c->q;
+        at.qh = c->qh;
+        at.ql = c->ql;
         at.kv = c->kv[l];
         at.tok = ti;
         at.H = h.n_head;
@@ -688,6 +699,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         er.epi = EPI_RESID;
         er.y = c->x;
         er.ldy = d;
+        er.ss_out = c->ssp;
         ok = ok && stage(c, DEC_K_WO, l, [&] {
             if (mv) {
                 InArgs in;
@@ -708,6 +720,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 InArgs in;
                 in.x32 = c->x;
                 in.norm_g = L.ffn_norm;
+                in.ss_part = c->ssp;
                 in.eps = h.rms_eps;
                 in.ldx = d;
                 return launch_matvec(L.wgu, in, eg, T, s);
@@ -736,6 +749,9 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 InArgs in;
                 in.x32 = c->x + (size_t)row0 * d;
                 in.norm_g = m->out_norm;
+                // the layers' residual adds left the sums of squares only when
+                // they ran as mat-vecs
+                in.ss_part = mv ? c->ssp + (size_t)row0 * SS_SLOTS : nullptr;
                 in.eps = h.rms_eps;
                 in.ldx = d;
                 return launch_matvec(m->out, in, eo, n_rows, s);

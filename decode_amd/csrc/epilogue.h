@@ -21,6 +21,22 @@ DEV void pair_rows(int mode, int p, int &r0, int &r1) {
     }
 }
 
+// q after RoPE: f32, and when asked, q * qscale as f16 value + remainder
+// (the exact operand form the decode attention's matrix cores take).
+DEV void store_q_pair(const EpiArgs &e, int t, int r0, float ra, float rb) {
+    *(float2 *)(e.qout + (size_t)t * e.qd + r0) = make_float2(ra, rb);
+    if (e.qh) {
+        const float ya = ra * e.qscale, yb = rb * e.qscale;
+        h2 vh, vl;
+        vh.x = (f16)ya;
+        vh.y = (f16)yb;
+        vl.x = (f16)(ya - (float)vh.x);
+        vl.y = (f16)(yb - (float)vh.y);
+        *(h2 *)(e.qh + (size_t)t * e.qd + r0) = vh;
+        *(h2 *)(e.ql + (size_t)t * e.qd + r0) = vl;
+    }
+}
+
 DEV void store_kv_pair(void *base, int kvtype, size_t idx, float a, float b) {
     if (kvtype == T_F16) {
         h2 v;
@@ -67,8 +83,7 @@ DEV void epi_pair(const EpiArgs &e, int t, int p, int r0, int r1, float a, float
             const float ra = a * cs.x - b * cs.y;
             const float rb = a * cs.y + b * cs.x;
             if (r0 < e.qd) {
-                float *q = e.qout + (size_t)t * e.qd;
-                *(float2 *)(q + r0) = make_float2(ra, rb);
+                store_q_pair(e, t, r0, ra, rb);
             } else {
                 const int g = rr / hd, el = rr % hd;
                 const size_t idx = (((size_t)e.tok.seq[t] * e.kv.n_kv + g) * e.kv.n_ctx + pos) * hd + el;
@@ -127,7 +142,7 @@ DEV void epi_pair_pre(const EpiArgs &e, int t, int p, int r0, int r1, float a, f
             const float ra = a * pre.cs.x - b * pre.cs.y;
             const float rb = a * pre.cs.y + b * pre.cs.x;
             if (r0 < e.qd) {
-                *(float2 *)(e.qout + (size_t)t * e.qd + r0) = make_float2(ra, rb);
+                store_q_pair(e, t, r0, ra, rb);
             } else {
                 const int g = rr / hd, el = rr % hd;
                 const size_t idx = (((size_t)pre.seq * e.kv.n_kv + g) * e.kv.n_ctx + pre.pos) * hd + el;

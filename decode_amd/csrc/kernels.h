@@ -63,14 +63,24 @@ struct KVLayer {
     int n_ctx = 0, n_kv = 0, hd = 0;
 };
 
+// Partial sums of squares of a residual row: the kernels that write x (the
+// embedding, the residual-add mat-vecs) leave one per block in slots
+// [row][0..SS_SLOTS) (unused slots 0), and the next RMSNorm prologue adds
+// them in slot order instead of re-reading the row.
+constexpr int SS_SLOTS = 256;
+
 struct EpiArgs {
     int epi = EPI_STORE;
+    float *ss_out = nullptr;   // RESID (mat-vec), optional: [T][SS_SLOTS] sums of squares of the new rows
     float *y = nullptr;        // STORE / RESID: [T][ldy]
     int ldy = 0;
     uint16_t *h = nullptr;     // SWIGLU: f16 [T][ldh]
     uint16_t *h_lo = nullptr;  // SWIGLU: optional f16 rounding remainder of h
     int ldh = 0;
     float *qout = nullptr;     // QKV: f32 [T][qd]
+    uint16_t *qh = nullptr;    // QKV, optional: f16 [T][qd] of q * qscale (value) ...
+    uint16_t *ql = nullptr;    // ... and its rounding remainder
+    float qscale = 1.f;        // 1 / sqrt(head_dim)
     int qd = 0, kd = 0;
     KVLayer kv;
     TokInfo tok;
@@ -83,6 +93,7 @@ struct InArgs {
     const float *x32 = nullptr;      // [T][ldx] f32; used when norm_g != nullptr
     const float *norm_g = nullptr;
     float eps = 0.f;
+    const float *ss_part = nullptr;  // optional: [rows][SS_SLOTS] partial sums of squares of x32 rows
     const uint16_t *x16 = nullptr;   // [T][ldx] f16 when no prologue
     const uint16_t *x16lo = nullptr; // [T][ldx] f16 remainder: the row is x16 + x16lo
     int ldx = 0;
@@ -119,7 +130,7 @@ size_t gemm_workspace_bytes(const QMat &W, int T);
 void gemm_set_num_cu(int n);
 
 // x[t] = dequantized row tok[t] of the embedding table (f32).
-void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, hipStream_t s);
+void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, float *ss_out, hipStream_t s);
 // y = rmsnorm(x[row_idx ? row_idx[t] : t]) * g as f16 value xn[t] and f16
 // rounding remainder xl[t] (y = xn + xl to about 22 bits)
 void launch_rmsnorm(const float *x, int ldx, const float *g, int d, float eps,
@@ -133,6 +144,8 @@ void launch_rope_table(float *cs, int n_ctx, int hd, float base, hipStream_t s);
 // (positions 0..pos[t]), split over key chunks of `chunk` rows, then merged.
 struct AttnArgs {
     const float *q = nullptr;     // [T][H*hd] f32 (after RoPE)
+    const uint16_t *qh = nullptr; // [T][H*hd] f16 q / sqrt(hd): value (f16 cache, hd 64/128) ...
+    const uint16_t *ql = nullptr; // ... and remainder
     KVLayer kv;
     TokInfo tok;
     int H = 0;
@@ -149,6 +162,8 @@ bool launch_attention(const AttnArgs &a, int T, hipStream_t s);
 // (nothing launched) when the shape is not covered.
 struct FlashArgs {
     const float *q = nullptr;     // [T][H*hd] f32 (after RoPE)
+    const uint16_t *qh = nullptr; // [T][H*hd] f16 q / sqrt(hd): value (f16 cache, hd 64/128) ...
+    const uint16_t *ql = nullptr; // ... and remainder
     KVLayer kv;
     TokInfo tok;
     int H = 0, T = 0;

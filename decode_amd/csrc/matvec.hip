@@ -143,76 +143,35 @@ constexpr int XROW = 36;   // dwords per LDS image row: 32 pairs + 4 pad (confli
 // LDS image of the input row, built once per block: per 32-element quant
 // block, 16 value pairs then 16 remainder pairs (f16x2) in the order the code
 // extraction consumes them (the pair order above), padded to XROW dwords,
-// plus the block's offset sum.  Built 8 elements at a time.
+// plus the block's offset sum.
 DEV uint32_t pk(f16 a, f16 b) { return h2_bits(h2{a, b}); }
 
-// Value/remainder split of elements k..k+3 and k2..k2+3: with NORM, fp32 x
-// times the RMSNorm factor and gain; otherwise the stored f16 value and
-// remainder.
-template <bool NORM>
-DEV void get8(const InArgs &in, const float *xr, const uint16_t *xh, const uint16_t *xl, float rs, int k,
-              int k2, f16 *hv, f16 *lv) {
-    const int ks[2] = {k, k2};
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-        if (NORM) {
-            const f4 v = *(const f4 *)(xr + ks[h]);
-            const f4 g = *(const f4 *)(in.norm_g + ks[h]);
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const float y = v[e] * rs * g[e];
-                hv[4 * h + e] = (f16)y;
-                lv[4 * h + e] = (f16)(y - (float)hv[4 * h + e]);
-            }
-        } else {
-            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-            const h4 a = *(const h4 *)(xh + ks[h]);
-            const h4 c = *(const h4 *)(xl + ks[h]);
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                hv[4 * h + e] = a[e];
-                lv[4 * h + e] = c[e];
-            }
-        }
-    }
-}
-
-// Quarter i of block b: elements 4i..4i+3 and 16+4i..16+4i+3 (Q4_0) or
-// 8i..8i+7 (Q8_0) -> image dwords 4i..4i+3 (values) and 16+4i.. (remainders).
-// The block's offset sum is the sum over its four quarters, which sit in
-// four consecutive lanes.
-template <int WT, bool NORM>
-DEV void put_quarter(uint32_t *img, float *bsum, int b, int i, const InArgs &in, const float *xr,
-                     const uint16_t *xh, const uint16_t *xl, float rs) {
+// Elements 4g..4g+3 of block b (value hv, remainder lv) -> their image
+// pairs, and their share of the block's offset sum.  Q4_0: a group of the
+// low half (g < 4) gives pairs 4g and 4g+2, of the high half (g = 4 + i)
+// pairs 4i+1 and 4i+3; Q8_0: pairs 2g and 2g+1.  The offsets are removed once
+// per block: Q4_0 keeps 1024 + q on codes 0..15 and (1024 + 16 q) / 16 on
+// codes 16..31, so sum (q - 8) x needs 1032 * sum(x[0..15]) + 72 *
+// sum(x[16..31]) subtracted; Q8_0 keeps 1024 + 128 + q everywhere.
+template <int WT>
+DEV float put_group(uint32_t *img, int b, int g, const f16 *hv, const f16 *lv) {
     uint32_t *row = img + (size_t)b * XROW;
-    f16 hv[8], lv[8];
-    float s_lo = 0.f, s_hi = 0.f;
+    int p0, p1;
     if (WT == T_Q4_0) {
-        // pairs 4i..4i+3 = (a0,a2) (c0,c2) (a1,a3) (c1,c3): a = x[4i..], c = x[16+4i..]
-        get8<NORM>(in, xr, xh, xl, rs, 32 * b + 4 * i, 32 * b + 16 + 4 * i, hv, lv);
-        *(u32x4 *)(row + 4 * i) = u32x4{pk(hv[0], hv[2]), pk(hv[4], hv[6]), pk(hv[1], hv[3]), pk(hv[5], hv[7])};
-        *(u32x4 *)(row + 16 + 4 * i) = u32x4{pk(lv[0], lv[2]), pk(lv[4], lv[6]), pk(lv[1], lv[3]), pk(lv[5], lv[7])};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            s_lo += (float)hv[e] + (float)lv[e];
-            s_hi += (float)hv[4 + e] + (float)lv[4 + e];
-        }
+        p0 = g < 4 ? 4 * g : 4 * (g - 4) + 1;
+        p1 = p0 + 2;
     } else {
-        // pairs 4i..4i+3 = (0,2) (1,3) (4,6) (5,7) of x[8i..8i+7]
-        get8<NORM>(in, xr, xh, xl, rs, 32 * b + 8 * i, 32 * b + 8 * i + 4, hv, lv);
-        *(u32x4 *)(row + 4 * i) = u32x4{pk(hv[0], hv[2]), pk(hv[1], hv[3]), pk(hv[4], hv[6]), pk(hv[5], hv[7])};
-        *(u32x4 *)(row + 16 + 4 * i) = u32x4{pk(lv[0], lv[2]), pk(lv[1], lv[3]), pk(lv[4], lv[6]), pk(lv[5], lv[7])};
-#pragma unroll
-        for (int e = 0; e < 8; e++) s_lo += (float)hv[e] + (float)lv[e];
+        p0 = 2 * g;
+        p1 = p0 + 1;
     }
-    // offsets removed once per block: Q4_0 keeps 1024 + q on codes 0..15 and
-    // (1024 + 16 q) / 16 on codes 16..31, so sum (q - 8) x needs
-    // 1032 * sum(x[0..15]) + 72 * sum(x[16..31]) subtracted; Q8_0 keeps
-    // 1024 + 128 + q everywhere.
-    float v = WT == T_Q4_0 ? 1032.f * s_lo + 72.f * s_hi : 1152.f * s_lo;
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    if (i == 0) bsum[b] = v;
+    row[p0] = pk(hv[0], hv[2]);
+    row[p1] = pk(hv[1], hv[3]);
+    row[16 + p0] = pk(lv[0], lv[2]);
+    row[16 + p1] = pk(lv[1], lv[3]);
+    float sx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; e++) sx += (float)hv[e] + (float)lv[e];
+    return sx * (WT == T_Q8_0 ? 1152.f : (g < 4 ? 1032.f : 72.f));
 }
 
 // NW = 16 wavefronts per block, one block per CU.  The K dimension is cut
@@ -220,9 +179,9 @@ DEV void put_quarter(uint32_t *img, float *bsum, int b, int i, const InArgs &in,
 // b0 + l of its slice, and keeps that block's activations (value and
 // remainder pairs, from the block's LDS image of the input row) in
 // registers.  S wavefronts share one row pair, one slice each.  A wavefront
-// keeps D row pairs of codes in flight: the first D are requested before the
-// input row is read, and each computed pair's registers are refilled with
-// the pair D ahead.  Row sums end with a DPP reduction; for S > 1 the
+// keeps D row pairs of codes in flight: the first D are requested right
+// after the inputs of the row's LDS image, and each computed pair's
+// registers are refilled with the pair D ahead.  Row sums end with a DPP reduction; for S > 1 the
 // partial sums of all pairs meet in LDS once, after the last pair, and are
 // added in slice order.
 constexpr int MV_MAXIT = 16;   // row pairs per wavefront when K is split
@@ -248,7 +207,7 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
     const int first = blockIdx.x * G + grp;
     const int iters = (npairs + stride - 1) / stride;    // same for every wavefront of the grid
 
-    // ---- code loads of the first D pairs (independent of the input row) ----
+    // ---- code loads: D row pairs in flight per wavefront ----
     PairLoad<WT, 1> L[D];
     auto issue = [&](PairLoad<WT, 1> &dst, int it) __attribute__((always_inline)) {
         const int p = min(first + it * stride, npairs - 1);   // past the end: re-read the last pair
@@ -256,8 +215,6 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         pair_rows(pair_mode, p, r0, r1);
         load_pair<WT, 1>(W, r0, r1, b0, b1, lane, dst);
     };
-#pragma unroll
-    for (int k = 0; k < D; k++) issue(L[k], k);
     // with a split K, thread i finishes item i (group, pair) after the last
     // pair: its epilogue inputs are requested now
     int fin_p = -1, fin_r0 = 0, fin_r1 = 1;
@@ -273,29 +230,77 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
     }
 
     // ---- LDS image of the input row, once per block ----
+    // Every input of the image is requested at once (one memory latency,
+    // overlapping the first code loads): thread i builds element groups
+    // i, i + 1024, ... (4 elements each); the 8 groups of a quant block sit in
+    // 8 consecutive lanes.  The RMSNorm factor comes from the partial sums of
+    // squares left by the kernel that wrote the row (added in slot order, the
+    // same in every wavefront), else from the row itself (one barrier).
     {
-        const float *xr = in.x32 + (size_t)xrow * in.ldx;
-        const uint16_t *xh = in.x16 + (size_t)xrow * in.ldx;
-        const uint16_t *xl = in.x16lo + (size_t)xrow * in.ldx;
+        constexpr int GPT = MV_KMAX / 4 / (NW * 64);
+        const int n4 = K >> 2;
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        f4 xv[GPT], gv[GPT];
+        h4 hv4[GPT], lv4[GPT];
+        f4 sp = {0.f, 0.f, 0.f, 0.f};
+        if (NORM && in.ss_part) sp = *(const f4 *)(in.ss_part + (size_t)xrow * SS_SLOTS + 4 * lane);
+#pragma unroll
+        for (int j = 0; j < GPT; j++) {
+            if (j * NW * 64 >= n4) break;                 // uniform
+            const int q = min(tid + j * NW * 64, n4 - 1);
+            if (NORM) {
+                xv[j] = *(const f4 *)(in.x32 + (size_t)xrow * in.ldx + 4 * q);
+                gv[j] = *(const f4 *)(in.norm_g + 4 * q);
+            } else {
+                hv4[j] = *(const h4 *)(in.x16 + (size_t)xrow * in.ldx + 4 * q);
+                lv4[j] = *(const h4 *)(in.x16lo + (size_t)xrow * in.ldx + 4 * q);
+            }
+        }
+        // the first D code pairs go out after the image inputs, so that waiting
+        // for the inputs (loads complete in issue order) never waits for them
+#pragma unroll
+        for (int k = 0; k < D; k++) issue(L[k], k);
         float rs = 0.f;
         if (NORM) {
-            float ss = 0.f;
-            for (int k = tid * 4; k < K; k += NW * 256) {
-                const f4 v = *(const f4 *)(xr + k);
-                ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-            }
-            ss = wave_sum_dpp(ss);
-            if (lane == 0) red[w] = ss;
-            __syncthreads();
-            float tot = 0.f;
+            float ss;
+            if (in.ss_part) {
+                ss = wave_sum_dpp((sp[0] + sp[1]) + (sp[2] + sp[3]));
+            } else {
+                float loc = 0.f;
 #pragma unroll
-            for (int i = 0; i < NW; i++) tot += red[i];
-            rs = 1.0f / sqrtf(tot / (float)K + in.eps);
+                for (int j = 0; j < GPT; j++)
+                    if (tid + j * NW * 64 < n4) loc += xv[j][0] * xv[j][0] + xv[j][1] * xv[j][1] + xv[j][2] * xv[j][2] + xv[j][3] * xv[j][3];
+                loc = wave_sum_dpp(loc);
+                if (lane == 0) red[w] = loc;
+                __syncthreads();
+                ss = 0.f;
+#pragma unroll
+                for (int i = 0; i < NW; i++) ss += red[i];
+            }
+            rs = 1.0f / sqrtf(ss / (float)K + in.eps);
         }
-        // every 4 consecutive threads build one block (whole wavefronts stay in the loop)
-        for (int q = tid; q < ((4 * nb + 63) & ~63); q += NW * 64) {
-            const int b = min(q >> 2, nb - 1);
-            if (q < 4 * nb) put_quarter<WT, NORM>(img, bsum, b, q & 3, in, xr, xh, xl, rs);
+#pragma unroll
+        for (int j = 0; j < GPT; j++) {
+            const int q = tid + j * NW * 64;
+            if (j * NW * 64 >= n4) break;                 // uniform: no group of this round
+            f16 hv[4], lv[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                if (NORM) {
+                    const float y = xv[j][e] * rs * gv[j][e];
+                    hv[e] = (f16)y;
+                    lv[e] = (f16)(y - (float)hv[e]);
+                } else {
+                    hv[e] = hv4[j][e];
+                    lv[e] = lv4[j][e];
+                }
+            }
+            float v = 0.f;
+            if (q < n4) v = put_group<WT>(img, q >> 3, q & 7, hv, lv);
+            v += __shfl_xor(v, 1, 64);
+            v += __shfl_xor(v, 2, 64);
+            v += __shfl_xor(v, 4, 64);
+            if (q < n4 && (q & 7) == 0) bsum[q >> 3] = v;
         }
     }
     __syncthreads();
@@ -318,6 +323,7 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
 
     // ---- stream row pairs ----
     const Masks mk = make_masks();
+    float ssq = 0.f;   // RESID: sum of squares of the rows this thread finished
     auto step = [&](PairLoad<WT, 1> &cur, int it) __attribute__((always_inline)) {
         if (it >= iters) return;
         const int p = first + it * stride;
@@ -338,7 +344,15 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
             if (S == 1) {
                 int r0, r1;
                 pair_rows(pair_mode, p, r0, r1);
-                epi_pair<EPI>(ep, t, p, r0, r1, a0, a1);
+                if (EPI == EPI_RESID) {
+                    float *y = ep.y + (size_t)t * ep.ldy;
+                    const float v0 = y[r0] + a0, v1 = y[r1] + a1;
+                    y[r0] = v0;
+                    y[r1] = v1;
+                    ssq += v0 * v0 + v1 * v1;
+                } else {
+                    epi_pair<EPI>(ep, t, p, r0, r1, a0, a1);
+                }
             } else {
                 float *pp = part + ((grp * MV_MAXIT + it) * S + slice) * 2;
                 pp[0] = a0;
@@ -363,7 +377,23 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
                 s1 += part[((g * MV_MAXIT + it) * S + j) * 2 + 1];
             }
             epi_pair_pre<EPI>(ep, t, fin_p, fin_r0, fin_r1, s0, s1, fin_pre);
+            if (EPI == EPI_RESID) ssq += (fin_pre.y0 + s0) * (fin_pre.y0 + s0) + (fin_pre.y1 + s1) * (fin_pre.y1 + s1);
         }
+    }
+    if (EPI == EPI_RESID && ep.ss_out) {
+        // this block's share of the new rows' sum of squares -> slot blockIdx.x
+        ssq = wave_sum_dpp(ssq);           // (the residual add reads no normalized row: red[] is free)
+        if (lane == 0) red[w] = ssq;
+        __syncthreads();
+        float *so = ep.ss_out + (size_t)t * SS_SLOTS;
+        if (tid == 0) {
+            float tot = 0.f;
+#pragma unroll
+            for (int i = 0; i < NW; i++) tot += red[i];
+            so[blockIdx.x] = tot;
+        }
+        if (blockIdx.x == 0)
+            for (int i = (int)gridDim.x + tid; i < SS_SLOTS; i += NW * 64) so[i] = 0.f;
     }
 }
 
@@ -376,6 +406,7 @@ bool launch_epi(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int p
     const int npairs = W.N / 2;
     int blocks = (npairs + G - 1) / G;
     if (blocks > g_num_cu) blocks = g_num_cu;
+    if (blocks > SS_SLOTS) blocks = SS_SLOTS;
     if (S > 1 && (npairs + blocks * G - 1) / (blocks * G) > MV_MAXIT) return false;
     launch((k_matvec<WT, S, EPI, D>), dim3(blocks, T), dim3(NW * 64), 0, s, W, in, ep, pair_mode);
     return true;

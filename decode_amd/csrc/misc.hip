@@ -101,8 +101,10 @@ __global__ __launch_bounds__(256) void k_copy_f32(const float *src, int rows, in
 }
 
 // ---- embedding: x[t] = dequantized row tok[t] (the article's get_rows) -----
-__global__ __launch_bounds__(256) void k_embed(QMat E, const int32_t *tok, float *x, int ldx) {
+__global__ __launch_bounds__(256) void k_embed(QMat E, const int32_t *tok, float *x, int ldx, float *ss_out) {
+    __shared__ float red[4];
     const int t = blockIdx.x;
+    float ss = 0.f;
     const int row = tok[t];
     const int K = E.K, nb = K >> 5;
     float *xr = x + (size_t)t * ldx;
@@ -122,6 +124,13 @@ __global__ __launch_bounds__(256) void k_embed(QMat E, const int32_t *tok, float
             }
         }
         xr[j] = v;
+        ss += v * v;
+    }
+    // sum of squares of the row for the first RMSNorm: slot 0, other slots 0
+    if (ss_out) {
+        ss = block_sum256(ss, red);
+        float *so = ss_out + (size_t)t * SS_SLOTS;
+        for (int j = threadIdx.x; j < SS_SLOTS; j += 256) so[j] = j == 0 ? ss : 0.f;
     }
 }
 
@@ -211,8 +220,8 @@ void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, i
                        m, mode, row_off);
 }
 
-void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, hipStream_t s) {
-    launch(k_embed, dim3(T), dim3(256), 0, s, E, tok, x, ldx);
+void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, float *ss_out, hipStream_t s) {
+    launch(k_embed, dim3(T), dim3(256), 0, s, E, tok, x, ldx, ss_out);
 }
 
 void launch_rmsnorm(const float *x, int ldx, const float *g, int d, float eps,
