@@ -106,11 +106,14 @@ constexpr int MV_KMAX = 16384;   // longest input row (elements); its LDS image 
 template <int WT, int KB>
 struct PairLoad {
     u32x4 q[2][KB][WT == T_Q4_0 ? 1 : 2];
-    uint32_t d[2][KB];
+    uint32_t d[2][KB];   // the aligned dword holding the block's f16 scale (half b & 1)
 };
 
 // Blocks b0 + lane + 64*i (i < KB) of rows r0, r1; lanes past the slice end
-// b1 re-read its last block and get scale 0, so every load is unconditional.
+// b1 re-read its last block (their activations are zero), so every load is
+// unconditional and nothing here waits for a load: a select
+// on a loaded value at issue time would make the wavefront wait for the
+// loads it has just requested.
 template <int WT, int KB>
 DEV void load_pair(const QMat &W, int r0, int r1, int b0, int b1, int lane, PairLoad<WT, KB> &L) {
     const int K = W.K, nb = K >> 5;
@@ -132,8 +135,7 @@ DEV void load_pair(const QMat &W, int r0, int r1, int b0, int b1, int lane, Pair
                 L.q[r][i][0] = __builtin_nontemporal_load(qr + 2 * b);
                 L.q[r][i][WT == T_Q4_0 ? 0 : 1] = __builtin_nontemporal_load(qr + 2 * b + 1);
             }
-            const uint32_t dv = dr[b];
-            L.d[r][i] = bw < b1 ? dv : 0u;
+            L.d[r][i] = ((const uint32_t *)dr)[b >> 1];   // rows of scales start 4-byte aligned (nb even)
         }
     }
 }
@@ -320,6 +322,7 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         }
     }
     const float xs = lane_ok ? bsum[bl] : 0.f;
+    const int dsh = (min(bl, b1 - 1) & 1) * 16;   // this lane's scale half in its loaded dword
 
     // ---- stream row pairs ----
     const Masks mk = make_masks();
@@ -335,9 +338,16 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
             bd0 = blockdot_q8(cur.q[0][0][0], cur.q[0][0][WT == T_Q4_0 ? 0 : 1], xp, mk);
             bd1 = blockdot_q8(cur.q[1][0][0], cur.q[1][0][WT == T_Q4_0 ? 0 : 1], xp, mk);
         }
-        float a0 = f16_bits_to_f32(cur.d[0][0]) * (bd0 - xs);
-        float a1 = f16_bits_to_f32(cur.d[1][0]) * (bd1 - xs);
+        // (lanes past the slice hold zero activations and offset sum, and the
+        // scale of a real block of the row: their products are 0)
+        float a0 = f16_bits_to_f32((uint16_t)(cur.d[0][0] >> dsh)) * (bd0 - xs);
+        float a1 = f16_bits_to_f32((uint16_t)(cur.d[1][0] >> dsh)) * (bd1 - xs);
+        // everything read from this pair's registers is consumed above the
+        // refill: a use below it would wait for the refill too (loads complete
+        // in issue order), which would leave one pair in flight instead of D
+        __builtin_amdgcn_sched_barrier(0);
         issue(cur, it + D);                              // refill with the pair D ahead
+        __builtin_amdgcn_sched_barrier(0);
         a0 = wave_sum_dpp(a0);
         a1 = wave_sum_dpp(a1);
         if (p < npairs && lane == 0) {
