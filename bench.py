@@ -118,7 +118,7 @@ def main():
     ap.add_argument("--workload", default="8b_q4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prompt", type=int, default=3)
-    ap.add_argument("--cpu-decode", type=int, default=3)
+    ap.add_argument("--cpu-decode", type=int, default=30)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (4 times), the reference kernel for "
                          "scaling the HBM fetch/write counters")
