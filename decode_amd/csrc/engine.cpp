@@ -63,6 +63,11 @@ struct Mem {
         void *p = nullptr;
         if (custom) {
             p = a.alloc(bytes, a.ud);
+            if (p && ((uintptr_t)p & 255)) {   // the kernels rely on the 256-byte alignment the contract states
+                LOGE("allocator returned memory not aligned to 256 bytes");
+                a.free(p, a.ud);
+                p = nullptr;
+            }
         } else if (hipMalloc(&p, bytes) != hipSuccess) {
             (void)hipGetLastError();
             p = nullptr;

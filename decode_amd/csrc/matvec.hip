@@ -106,7 +106,8 @@ constexpr int MV_KMAX = 16384;   // longest input row (elements); its LDS image 
 template <int WT, int KB>
 struct PairLoad {
     u32x4 q[2][KB][WT == T_Q4_0 ? 1 : 2];
-    uint32_t d[2][KB];   // the aligned dword holding the block's f16 scale (half b & 1)
+    uint32_t d[2][KB];     // the aligned dword holding the block's f16 scale ...
+    uint32_t dsh[2][KB];   // ... at this bit offset
 };
 
 // Blocks b0 + lane + 64*i (i < KB) of rows r0, r1; lanes past the slice end
@@ -120,7 +121,6 @@ DEV void load_pair(const QMat &W, int r0, int r1, int b0, int b1, int lane, Pair
     const int rows[2] = {r0, r1};
 #pragma unroll
     for (int r = 0; r < 2; r++) {
-        const uint16_t *dr = W.d + (size_t)rows[r] * nb;
         const u32x4 *qr = WT == T_Q4_0
                               ? (const u32x4 *)((const uint8_t *)W.qs + (size_t)rows[r] * (K >> 1))
                               : (const u32x4 *)((const int8_t *)W.qs + (size_t)rows[r] * K);
@@ -135,7 +135,9 @@ DEV void load_pair(const QMat &W, int r0, int r1, int b0, int b1, int lane, Pair
                 L.q[r][i][0] = __builtin_nontemporal_load(qr + 2 * b);
                 L.q[r][i][WT == T_Q4_0 ? 0 : 1] = __builtin_nontemporal_load(qr + 2 * b + 1);
             }
-            L.d[r][i] = ((const uint32_t *)dr)[b >> 1];   // rows of scales start 4-byte aligned (nb even)
+            const size_t e = (size_t)rows[r] * nb + b;   // W.d is 256-byte aligned
+            L.d[r][i] = *(const uint32_t *)(W.d + (e & ~(size_t)1));
+            L.dsh[r][i] = (uint32_t)(e & 1) * 16;
         }
     }
 }
@@ -322,7 +324,6 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         }
     }
     const float xs = lane_ok ? bsum[bl] : 0.f;
-    const int dsh = (min(bl, b1 - 1) & 1) * 16;   // this lane's scale half in its loaded dword
 
     // ---- stream row pairs ----
     const Masks mk = make_masks();
@@ -340,8 +341,8 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         }
         // (lanes past the slice hold zero activations and offset sum, and the
         // scale of a real block of the row: their products are 0)
-        float a0 = f16_bits_to_f32((uint16_t)(cur.d[0][0] >> dsh)) * (bd0 - xs);
-        float a1 = f16_bits_to_f32((uint16_t)(cur.d[1][0] >> dsh)) * (bd1 - xs);
+        float a0 = f16_bits_to_f32((uint16_t)(cur.d[0][0] >> cur.dsh[0][0])) * (bd0 - xs);
+        float a1 = f16_bits_to_f32((uint16_t)(cur.d[1][0] >> cur.dsh[1][0])) * (bd1 - xs);
         // everything read from this pair's registers is consumed above the
         // refill: a use below it would wait for the refill too (loads complete
         // in issue order), which would leave one pair in flight instead of D
