@@ -11,8 +11,8 @@
 // A 256-thread block computes BN = 128 output features x BM tokens; each
 // wavefront owns a 64 x BM/2 sub-tile.  Pipeline per K block (32 k):
 //   * global loads of codes, scale and both activation parts go to
-//     registers two K blocks ahead (two register sets, the loop unrolled by
-//     two so that each set has fixed registers);
+//     registers three K blocks ahead (three register sets, the loop unrolled
+//     by six so that each set has fixed registers);
 //   * a K block is converted (codes -> f16) and written to one of two LDS
 //     stages while the other stage feeds the MFMAs; one barrier per K block.
 // Rows of an LDS tile are 40 f16 (80 bytes) apart, so the 16-byte fragment
@@ -216,23 +216,49 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
 
     // Loads past the last K block re-read the last one (their data is never
     // used), so no load sits behind a branch: the compiler can then wait for
-    // exactly the register set a store needs and leave the other in flight.
-    Stage<WT, XC> r0, r1;
+    // exactly the register set a store needs and leave the others in flight.
+    // Three register sets rotate over two LDS stages (period 6): a K block's
+    // loads are issued three compute steps before its LDS store, which covers
+    // a loaded memory latency at the MFMA rate of a step.
+    Stage<WT, XC> r0, r1, r2;
     gload(r0, 0);
     gload(r1, min(1, nb - 1));
+    gload(r2, min(2, nb - 1));
     lstore(r0, 0);
     __syncthreads();
-    gload(r0, min(2, nb - 1));
-    for (int kb = 0; kb < nb; kb += 2) {
-        compute(0);                                     // K block kb from stage 0
+    gload(r0, min(3, nb - 1));
+    // top of an iteration: LDS stage 0 holds kb; r1, r2, r0 carry kb+1..kb+3
+    for (int kb = 0; kb < nb; kb += 6) {
+        compute(0);                                     // kb
         if (kb + 1 >= nb) break;
-        lstore(r1, 1);                                  // K block kb+1 -> stage 1
+        lstore(r1, 1);
         __syncthreads();
-        gload(r1, min(kb + 3, nb - 1));
-        compute(1);                                     // K block kb+1
-        lstore(r0, 0);                                  // K block kb+2 -> stage 0 (unused past the end)
+        gload(r1, min(kb + 4, nb - 1));
+        compute(1);                                     // kb+1
+        if (kb + 2 >= nb) break;
+        lstore(r2, 0);
         __syncthreads();
-        gload(r0, min(kb + 4, nb - 1));
+        gload(r2, min(kb + 5, nb - 1));
+        compute(0);                                     // kb+2
+        if (kb + 3 >= nb) break;
+        lstore(r0, 1);
+        __syncthreads();
+        gload(r0, min(kb + 6, nb - 1));
+        compute(1);                                     // kb+3
+        if (kb + 4 >= nb) break;
+        lstore(r1, 0);
+        __syncthreads();
+        gload(r1, min(kb + 7, nb - 1));
+        compute(0);                                     // kb+4
+        if (kb + 5 >= nb) break;
+        lstore(r2, 1);
+        __syncthreads();
+        gload(r2, min(kb + 8, nb - 1));
+        compute(1);                                     // kb+5
+        if (kb + 6 >= nb) break;
+        lstore(r0, 0);
+        __syncthreads();
+        gload(r0, min(kb + 9, nb - 1));
     }
 
     // ---- epilogue ----
