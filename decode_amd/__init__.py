@@ -91,6 +91,9 @@ def lib() -> C.CDLL:
         "dec_model_load": (vp, [vp, vp, vp, vp]),
         "dec_model_tensor_blocks": (i64, [vp, i32, i32, vp, C.c_size_t]),
         "dec_model_free": (None, [vp]),
+        "dec_gguf_inspect": (i32, [C.c_char_p, vp]),
+        "dec_model_load_gguf": (vp, [C.c_char_p, i32, vp, vp]),
+        "dec_model_save_gguf": (i32, [vp, C.c_char_p]),
         "dec_ctx_new": (vp, [vp, vp]),
         "dec_prefill": (i32, [vp, vp, i32, i32, i32]),
         "dec_decode": (i32, [vp, vp, vp, i32]),
@@ -159,7 +162,36 @@ class TorchAllocator:
         self._live.pop(p, None)
 
 
+def gguf_inspect(path) -> tuple[int, dict | None]:
+    """dec_gguf_inspect: (tensor count or negative status, hyper-parameters)."""
+    h = Hparams()
+    n = int(lib().dec_gguf_inspect(str(path).encode(), C.byref(h)))
+    if n < 0:
+        return n, None
+    return n, {f: getattr(h, f) for f, _ in Hparams._fields_}
+
+
 class Model:
+    @classmethod
+    def from_gguf(cls, path, kvtype: int = 1, stream=None, allocator: "TorchAllocator | None" = None) -> "Model":
+        """dec_model_load_gguf."""
+        self = cls.__new__(cls)
+        self.L = lib()
+        self.allocator = allocator
+        al = C.byref(allocator.struct) if allocator else None
+        self.ptr = self.L.dec_model_load_gguf(str(path).encode(), kvtype, al, stream)
+        if not self.ptr:
+            raise DecodeError(f"dec_model_load_gguf rejected {path}")
+        n, hp = gguf_inspect(path)
+        hp["kvtype"] = kvtype
+        self.hp = hp
+        return self
+
+    def save_gguf(self, path) -> None:
+        rc = self.L.dec_model_save_gguf(self.ptr, str(path).encode())
+        if rc != 0:
+            raise DecodeError(f"dec_model_save_gguf returned {rc}")
+
     def __init__(self, hp: dict, weights: dict, stream=None, allocator: TorchAllocator | None = None):
         L = lib()
         self.L = L

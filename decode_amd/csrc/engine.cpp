@@ -7,6 +7,7 @@
 // step of the decoder runs in the kernels of this directory; this file only
 // moves bytes and launches work.
 #include "../../include/decode.h"
+#include "gguf.h"
 
 #include <hip/hip_runtime.h>
 
@@ -17,6 +18,7 @@
 #include <cstring>
 #include <map>
 #include <new>
+#include <string>
 #include <vector>
 
 #include "kernels.h"
@@ -338,6 +340,231 @@ extern "C" int64_t dec_model_tensor_blocks(const dec_model *m, int32_t id, int32
         }
     }
     return (int64_t)total;
+}
+
+// --------------------------------------------------------------- GGUF files
+// The llama tensor names of the article's weight set (step 6) and the
+// llama.* hyper-parameter keys of step 4.
+static std::string layer_name(int l, const char *what) { return "blk." + std::to_string(l) + "." + what + ".weight"; }
+
+static int file_type_of(int wtype) {
+    return wtype == DEC_Q4_0 ? gguf::T_Q4_0 : wtype == DEC_Q8_0 ? gguf::T_Q8_0 : gguf::T_F32;
+}
+
+// Hyper-parameters and tensor checks of a parsed file; returns a gguf status.
+static int gguf_model_params(const gguf::File &f, int32_t kvtype, dec_hparams &h) {
+    const gguf::Value *arch = f.find("general.architecture");
+    if (!arch || arch->type != gguf::V_STR || arch->s != "llama") return gguf::E_SHAPE;
+    auto get_u = [&](const char *key, uint64_t &v, bool required, uint64_t dflt) {
+        const gguf::Value *x = f.find(key);
+        if (!x) {
+            v = dflt;
+            return !required;
+        }
+        return x->as_u64(v) && v > 0 && v < (1u << 30);
+    };
+    auto get_f = [&](const char *key, double &v, double dflt) {
+        const gguf::Value *x = f.find(key);
+        if (!x) {
+            v = dflt;
+            return true;
+        }
+        return x->as_f64(v);
+    };
+    uint64_t d, nl, ff, nh, nkv, hd;
+    double eps, base;
+    if (!get_u("llama.embedding_length", d, true, 0) || !get_u("llama.block_count", nl, true, 0) ||
+        !get_u("llama.feed_forward_length", ff, true, 0) || !get_u("llama.attention.head_count", nh, true, 0) ||
+        !get_u("llama.attention.head_count_kv", nkv, false, nh))
+        return gguf::E_SHAPE;
+    uint64_t rope_dims;
+    if (!get_u("llama.rope.dimension_count", rope_dims, false, d / nh) ||
+        !get_u("llama.attention.key_length", hd, false, rope_dims) ||
+        !get_f("llama.attention.layer_norm_rms_epsilon", eps, 1e-5) || !get_f("llama.rope.freq_base", base, 10000.0))
+        return gguf::E_SHAPE;
+    const gguf::Tensor *emb = f.tensor("token_embd.weight");
+    if (!emb || emb->n_dims != 2 || emb->dims[0] != d) return gguf::E_SHAPE;
+    const uint32_t wt = emb->type;
+    if (wt != gguf::T_F32 && wt != gguf::T_Q4_0 && wt != gguf::T_Q8_0) return gguf::E_TYPE;
+    h = dec_hparams{};
+    h.n_layer = (int32_t)nl;
+    h.n_embd = (int32_t)d;
+    h.n_head = (int32_t)nh;
+    h.n_head_kv = (int32_t)nkv;
+    h.head_dim = (int32_t)hd;
+    h.n_ff = (int32_t)ff;
+    h.n_vocab = (int32_t)emb->dims[1];
+    h.rms_eps = (float)eps;
+    h.rope_base = (float)base;
+    h.wtype = wt == gguf::T_Q4_0 ? DEC_Q4_0 : wt == gguf::T_Q8_0 ? DEC_Q8_0 : DEC_F32;
+    h.kvtype = kvtype;
+    if (!valid_hparams(h)) return gguf::E_SHAPE;
+    const uint64_t qd = nh * hd, kd = nkv * hd, V = (uint64_t)h.n_vocab;
+    auto mat = [&](const std::string &name, uint64_t in, uint64_t out) {
+        const gguf::Tensor *t = f.tensor(name);
+        return t && t->n_dims == 2 && t->dims[0] == in && t->dims[1] == out && t->type == wt;
+    };
+    auto vec = [&](const std::string &name) {
+        const gguf::Tensor *t = f.tensor(name);
+        return t && t->n_dims == 1 && t->dims[0] == d && t->type == gguf::T_F32;
+    };
+    // the output matrix may be absent (tied to the embedding, step 6)
+    if ((f.tensor("output.weight") && !mat("output.weight", d, V)) || !vec("output_norm.weight")) return gguf::E_SHAPE;
+    for (int l = 0; l < h.n_layer; l++)
+        if (!vec(layer_name(l, "attn_norm")) || !mat(layer_name(l, "attn_q"), d, qd) ||
+            !mat(layer_name(l, "attn_k"), d, kd) || !mat(layer_name(l, "attn_v"), d, kd) ||
+            !mat(layer_name(l, "attn_output"), qd, d) || !vec(layer_name(l, "ffn_norm")) ||
+            !mat(layer_name(l, "ffn_gate"), d, ff) || !mat(layer_name(l, "ffn_up"), d, ff) ||
+            !mat(layer_name(l, "ffn_down"), ff, d))
+            return gguf::E_SHAPE;
+    return gguf::OK;
+}
+
+extern "C" int32_t dec_gguf_inspect(const char *path, dec_hparams *hp) {
+    if (!path || !hp) return -1;
+    gguf::File f;
+    int st = f.open(path);
+    if (st == gguf::OK) st = gguf_model_params(f, DEC_F16, *hp);
+    return st == gguf::OK ? (int32_t)f.tensors.size() : st;
+}
+
+extern "C" dec_model *dec_model_load_gguf(const char *path, int32_t kvtype, const dec_allocator *alloc,
+                                          void *hip_stream) {
+    if (alloc && (!alloc->alloc || !alloc->free)) {
+        LOGE("dec_model_load_gguf: allocator needs both callbacks");
+        return nullptr;
+    }
+    gguf::File f;
+    dec_hparams h{};
+    int st = f.open(path);
+    if (st == gguf::OK) st = gguf_model_params(f, kvtype, h);
+    if (st != gguf::OK) {
+        LOGE("dec_model_load_gguf: %s rejected (status %d)", path ? path : "(null)", st);
+        return nullptr;
+    }
+    dec_model *m = new dec_model();
+    m->hp = h;
+    if (alloc) {
+        m->mem.a = *alloc;
+        m->mem.custom = true;
+    }
+    m->stream = (hipStream_t)hip_stream;
+    m->qd = h.n_head * h.head_dim;
+    m->kd = h.n_head_kv * h.head_dim;
+    m->F = h.n_ff;
+    m->Fp = (h.n_ff + 31) / 32 * 32;
+    const int d = h.n_embd, V = h.n_vocab, qd = m->qd, kd = m->kd, F = m->F, Fp = m->Fp;
+    bool ok = alloc_qmat(m->mem, m->tok, h.wtype, V, d) && alloc_qmat(m->mem, m->out, h.wtype, V, d);
+    m->layers.resize(h.n_layer);
+    for (int l = 0; ok && l < h.n_layer; l++) {
+        Layer &L = m->layers[l];
+        ok = alloc_qmat(m->mem, L.wqkv, h.wtype, qd + 2 * kd, d) && alloc_qmat(m->mem, L.wo, h.wtype, d, qd) &&
+             alloc_qmat(m->mem, L.wgu, h.wtype, 2 * Fp, d) && alloc_qmat(m->mem, L.wdown, h.wtype, d, Fp);
+    }
+    // one device staging buffer for the largest tensor; each tensor's bytes go
+    // there straight from the file mapping, then split into codes and scales
+    uint64_t largest = 0;
+    for (const gguf::Tensor &t : f.tensors) largest = std::max(largest, t.nbytes);
+    void *stage = ok ? m->mem.get((size_t)largest) : nullptr;
+    ok = ok && stage;
+    hipStream_t s = m->stream;
+    auto put = [&](const std::string &name, int rows, int K_src, QMat &q, int mode, int row_off) {
+        const gguf::Tensor *t = f.tensor(name);
+        HIP_OK(hipMemcpyAsync(stage, t->data, (size_t)t->nbytes, hipMemcpyHostToDevice, s), return false);
+        if (q.wtype == DEC_F32)
+            launch_copy_f32((const float *)stage, rows, K_src, q, mode, row_off, s);
+        else
+            launch_put_blocks(stage, rows, K_src, q, mode, row_off, s);
+        HIP_OK(hipGetLastError(), return false);
+        HIP_OK(hipStreamSynchronize(s), return false);   // the staging buffer is reused next
+        return true;
+    };
+    auto vec = [&](const std::string &name, float **dst) {
+        *dst = (float *)m->mem.get((size_t)d * 4);
+        if (!*dst) return false;
+        HIP_OK(hipMemcpyAsync(*dst, f.tensor(name)->data, (size_t)d * 4, hipMemcpyHostToDevice, s), return false);
+        return true;
+    };
+    const bool tied = f.tensor("output.weight") == nullptr;
+    ok = ok && put("token_embd.weight", V, d, m->tok, 0, 0) &&
+         put(tied ? "token_embd.weight" : "output.weight", V, d, m->out, 0, 0) && vec("output_norm.weight", &m->out_norm);
+    for (int l = 0; ok && l < h.n_layer; l++) {
+        Layer &L = m->layers[l];
+        ok = put(layer_name(l, "attn_q"), qd, d, L.wqkv, 0, 0) && put(layer_name(l, "attn_k"), kd, d, L.wqkv, 0, qd) &&
+             put(layer_name(l, "attn_v"), kd, d, L.wqkv, 0, qd + kd) && put(layer_name(l, "attn_output"), d, qd, L.wo, 0, 0) &&
+             put(layer_name(l, "ffn_gate"), F, d, L.wgu, 1, 0) && put(layer_name(l, "ffn_up"), F, d, L.wgu, 2, 0) &&
+             put(layer_name(l, "ffn_down"), d, F, L.wdown, 0, 0) && vec(layer_name(l, "attn_norm"), &L.attn_norm) &&
+             vec(layer_name(l, "ffn_norm"), &L.ffn_norm);
+    }
+    if (ok) HIP_OK(hipStreamSynchronize(s), ok = false);
+    if (!ok) {
+        LOGE("dec_model_load_gguf failed");
+        m->mem.release();
+        delete m;
+        return nullptr;
+    }
+    LOGI("model loaded from %s: %d layers, d=%d, wtype=%d", path, h.n_layer, d, h.wtype);
+    return m;
+}
+
+extern "C" int32_t dec_model_save_gguf(const dec_model *m, const char *path) {
+    if (!m || !path) return -1;
+    const dec_hparams &h = m->hp;
+    std::vector<std::pair<std::string, gguf::Value>> kv = {
+        {"general.architecture", gguf::str_value("llama")},
+        {"general.alignment", gguf::u32_value(32)},
+        {"llama.embedding_length", gguf::u32_value((uint32_t)h.n_embd)},
+        {"llama.block_count", gguf::u32_value((uint32_t)h.n_layer)},
+        {"llama.feed_forward_length", gguf::u32_value((uint32_t)h.n_ff)},
+        {"llama.attention.head_count", gguf::u32_value((uint32_t)h.n_head)},
+        {"llama.attention.head_count_kv", gguf::u32_value((uint32_t)h.n_head_kv)},
+        {"llama.attention.key_length", gguf::u32_value((uint32_t)h.head_dim)},
+        {"llama.attention.value_length", gguf::u32_value((uint32_t)h.head_dim)},
+        {"llama.rope.dimension_count", gguf::u32_value((uint32_t)h.head_dim)},
+        {"llama.rope.freq_base", gguf::f32_value(h.rope_base)},
+        {"llama.attention.layer_norm_rms_epsilon", gguf::f32_value(h.rms_eps)},
+        {"llama.vocab_size", gguf::u32_value((uint32_t)h.n_vocab)},
+    };
+    const uint32_t wt = (uint32_t)file_type_of(h.wtype);
+    const uint64_t d = (uint64_t)h.n_embd, V = (uint64_t)h.n_vocab, qd = (uint64_t)m->qd, kd = (uint64_t)m->kd,
+                   ff = (uint64_t)h.n_ff;
+    std::vector<gguf::OutTensor> ts;
+    auto mat = [&](const std::string &name, int id, int layer, uint64_t in, uint64_t out) {
+        ts.push_back({name, wt, {in, out}, [m, id, layer](std::vector<uint8_t> &b) {
+                          const int64_t need = -dec_model_tensor_blocks(m, id, layer, nullptr, 0);
+                          if (need <= 0) return false;
+                          b.resize((size_t)need);
+                          return dec_model_tensor_blocks(m, id, layer, b.data(), b.size()) == need;
+                      }});
+    };
+    auto vec = [&](const std::string &name, const float *src) {
+        ts.push_back({name, gguf::T_F32, {d}, [src, d](std::vector<uint8_t> &b) {
+                          b.resize((size_t)d * 4);
+                          return hipMemcpy(b.data(), src, b.size(), hipMemcpyDeviceToHost) == hipSuccess;
+                      }});
+    };
+    mat("token_embd.weight", DEC_T_TOK_EMBD, 0, d, V);
+    vec("output_norm.weight", m->out_norm);
+    mat("output.weight", DEC_T_OUTPUT, 0, d, V);
+    for (int l = 0; l < h.n_layer; l++) {
+        const Layer &L = m->layers[l];
+        vec(layer_name(l, "attn_norm"), L.attn_norm);
+        mat(layer_name(l, "attn_q"), DEC_T_WQ, l, d, qd);
+        mat(layer_name(l, "attn_k"), DEC_T_WK, l, d, kd);
+        mat(layer_name(l, "attn_v"), DEC_T_WV, l, d, kd);
+        mat(layer_name(l, "attn_output"), DEC_T_WO, l, qd, d);
+        vec(layer_name(l, "ffn_norm"), L.ffn_norm);
+        mat(layer_name(l, "ffn_gate"), DEC_T_FFN_GATE, l, d, ff);
+        mat(layer_name(l, "ffn_up"), DEC_T_FFN_UP, l, d, ff);
+        mat(layer_name(l, "ffn_down"), DEC_T_FFN_DOWN, l, ff, d);
+    }
+    if (hipStreamSynchronize(m->stream) != hipSuccess) return -3;
+    const int st = gguf::write(path, kv, ts, 32);
+    if (st != gguf::OK) {
+        LOGE("dec_model_save_gguf: writing %s failed (status %d)", path, st);
+        return -3;
+    }
+    return 0;
 }
 
 // --------------------------------------------------------------- context

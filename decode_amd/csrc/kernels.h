@@ -107,6 +107,9 @@ struct InArgs {
 void launch_quantize(const float *src, int rows, int K, QMat &m, int mode, int row_off,
                      hipStream_t s);
 // fp32 copy into a (possibly padded) F32 matrix: src [rows][K_src] -> m rows
+// GGUF-style blocks (f16 scale + codes, 18 / 34 bytes, 2-byte aligned) of a
+// rows x K Q4_0 / Q8_0 tensor -> scales and codes of rows dst_row(r) of m.
+void launch_put_blocks(const void *src, int rows, int K, QMat &m, int mode, int row_off, hipStream_t s);
 // dst_row(r), columns [0, K_src); the caller zero-fills padding beforehand.
 void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, int row_off,
                      hipStream_t s);

@@ -100,6 +100,25 @@ __global__ __launch_bounds__(256) void k_copy_f32(const float *src, int rows, in
     ((float *)m.qs)[(size_t)dst_row(mode, r, row_off) * m.K + k] = src[idx];
 }
 
+// ---- file blocks -> stored layout ------------------------------------------
+// One thread per 32-weight block of a GGUF-style tensor (f16 scale, then 16
+// bytes of Q4_0 nibbles or 32 Q8_0 codes): the scale goes to m.d and the
+// codes to m.qs, in row dst_row(mode, r, row_off).  Blocks are 2-byte aligned
+// (18 / 34 bytes each), so they are moved 16 bits at a time.
+__global__ __launch_bounds__(256) void k_put_blocks(const uint16_t *src, int rows, int K, QMat m, int mode,
+                                                    int row_off) {
+    const int nb = K >> 5, nbd = m.K >> 5;              // source / stored blocks per row
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)rows * nb) return;
+    const int r = (int)(idx / nb), b = (int)(idx % nb);
+    const int dr = dst_row(mode, r, row_off);
+    const int cw = m.wtype == T_Q8_0 ? 16 : 8;          // 16-bit words of codes per block
+    const uint16_t *blk = src + (size_t)idx * (1 + cw);
+    m.d[(size_t)dr * nbd + b] = blk[0];
+    uint16_t *q = (uint16_t *)m.qs + ((size_t)dr * nbd + b) * cw;
+    for (int j = 0; j < cw; j++) q[j] = blk[1 + j];
+}
+
 // ---- embedding: x[t] = dequantized row tok[t] (the article's get_rows) -----
 __global__ __launch_bounds__(256) void k_embed(QMat E, const int32_t *tok, float *x, int ldx, float *ss_out) {
     __shared__ float red[4];
@@ -218,6 +237,12 @@ void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, i
     const long long n = (long long)rows * K_src;
     launch(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows, K_src,
                        m, mode, row_off);
+}
+
+void launch_put_blocks(const void *src, int rows, int K, QMat &m, int mode, int row_off, hipStream_t s) {
+    const long long n = (long long)rows * (K / 32);
+    launch(k_put_blocks, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const uint16_t *)src, rows, K, m,
+           mode, row_off);
 }
 
 void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, float *ss_out, hipStream_t s) {

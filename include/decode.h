@@ -106,6 +106,41 @@ int64_t dec_model_tensor_blocks(const dec_model *m, int32_t tensor_id, int32_t l
  * weights are released together with the last of them. */
 void dec_model_free(dec_model *m);
 
+/* ---- GGUF v3 model files (article steps 2b-2c and its GGUF reference
+ * section; tensor names of step 6, hyper-parameter keys of step 4) ---------
+ * Layout: magic "GGUF", version 3, tensor count, key/value count; the
+ * key/value pairs; one record per tensor (name, dimensions with the row
+ * length first, element type, data offset); the data section at the next
+ * multiple of general.alignment (32 when absent).  Matrices are Q4_0 (18-byte
+ * blocks), Q8_0 (34-byte blocks) or F32, all of one type; norm vectors F32.
+ * Keys read: general.architecture ("llama"), llama.embedding_length,
+ * llama.block_count, llama.feed_forward_length, llama.attention.head_count
+ * (required); llama.attention.head_count_kv (default head_count),
+ * llama.attention.key_length or llama.rope.dimension_count (default
+ * embedding_length / head_count), llama.attention.layer_norm_rms_epsilon
+ * (1e-5), llama.rope.freq_base (10000).  Unknown keys and extra tensors are
+ * ignored; output.weight may be absent (tied to token_embd.weight). */
+
+/* Validates a file without loading it and fills *hp (kvtype = DEC_F16).
+ * Returns the tensor count, or: -1 cannot open / bad arguments, -4 not GGUF,
+ * -5 a version other than 3, -6 malformed or truncated records, -7 a
+ * duplicated tensor name, -8 tensor data outside the file, -9 a missing key
+ * or tensor, or one of the wrong shape or type mix, -10 an element type not
+ * handled.  Touches no device. */
+int32_t dec_gguf_inspect(const char *path, dec_hparams *hp);
+
+/* Loads a file that dec_gguf_inspect accepts.  The file is memory-mapped;
+ * each tensor's bytes are copied from the mapping straight to the device,
+ * where its blocks are split into codes and scales and placed in the fused
+ * matrices.  kvtype: the cache type (DEC_F16 or DEC_F32).  NULL on any error
+ * (the reason is logged). */
+dec_model *dec_model_load_gguf(const char *path, int32_t kvtype, const dec_allocator *alloc, void *hip_stream);
+
+/* Writes the model as a GGUF v3 file in the layout above (its stored type,
+ * the exact blocks of dec_model_tensor_blocks).  0, -1 bad arguments, -3 an
+ * I/O or device error. */
+int32_t dec_model_save_gguf(const dec_model *m, const char *path);
+
 /* Context parameters (article step 7).  n_ctx: positions per sequence,
  * rounded up to a multiple of 256 (0 -> 4096).  n_batch: most tokens one
  * prefill call may take (0 -> n_ctx, clamped to n_ctx).  n_ubatch: most
