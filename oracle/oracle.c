@@ -261,10 +261,24 @@ void orc_rope(orc_real *v, int32_t n_heads, int32_t hd, int32_t pos, float base)
     }
 }
 
+/* Element idx of a cached array.  Q8_0 cache: 34-byte blocks of 32         */
+/* consecutive row elements (scale, then codes), value = code * scale.      */
 static orc_real kv_at(const void *base, int32_t kvtype, int64_t idx)
 {
     if (kvtype == ORC_T_F16) return (orc_real)orc_f16_to_f32(((const uint16_t *)base)[idx]);
+    if (kvtype == ORC_T_Q8_0) {
+        const uint8_t *b = (const uint8_t *)base + (idx / 32) * 34;
+        const orc_real d = (orc_real)orc_f16_to_f32(rd_u16(b));
+        return (orc_real)(int8_t)b[2 + idx % 32] * d;
+    }
     return (orc_real)((const float *)base)[idx];
+}
+
+/* Byte offset of element idx (a multiple of 32 for a Q8_0 cache). */
+static size_t kv_bytes(int32_t kvtype, int64_t idx)
+{
+    if (kvtype == ORC_T_Q8_0) return (size_t)(idx / 32) * 34;
+    return (size_t)idx * (kvtype == ORC_T_F16 ? 2 : 4);
 }
 
 /* Attention of step 13b: scores = Q x K^T, causal mask, softmax, weighted  */
@@ -348,7 +362,6 @@ struct orc_ctx {
     int32_t n_seq, n_ctx;
     int32_t *pos_max;
     void **K, **V;                /* [layer*n_seq + seq] -> [n_ctx][Hkv*hd] */
-    size_t esz;
 };
 
 static int64_t enc_bytes(int32_t wtype, int64_t rows, int64_t cols)
@@ -393,7 +406,9 @@ orc_model *orc_model_new(const orc_hparams *hp, const orc_weights *w)
         h.n_ff <= 0 || h.n_vocab <= 0 || h.head_dim % 2 || h.n_head % h.n_head_kv)
         return NULL;
     if (h.wtype != ORC_T_F32 && h.wtype != ORC_T_Q8_0 && h.wtype != ORC_T_Q4_0) return NULL;
-    if (h.kvtype != ORC_T_F32 && h.kvtype != ORC_T_F16) return NULL;
+    if (h.kvtype != ORC_T_F32 && h.kvtype != ORC_T_F16 && h.kvtype != ORC_T_Q8_0) return NULL;
+    /* a Q8_0 cache row splits into whole 32-element blocks within each head */
+    if (h.kvtype == ORC_T_Q8_0 && h.head_dim % 32) return NULL;
     const int32_t qd = h.n_head * h.head_dim, kd = h.n_head_kv * h.head_dim;
     if (h.wtype != ORC_T_F32 && (h.n_embd % 32 || qd % 32 || h.n_ff % 32)) return NULL;
 
@@ -465,11 +480,10 @@ orc_ctx *orc_ctx_new(const orc_model *m, int32_t n_seq, int32_t n_ctx)
     c->m = m;
     c->n_seq = n_seq;
     c->n_ctx = n_ctx;
-    c->esz = m->hp.kvtype == ORC_T_F16 ? 2 : 4;
     c->pos_max = (int32_t *)malloc(sizeof(int32_t) * (size_t)n_seq);
     for (int32_t s = 0; s < n_seq; s++) c->pos_max[s] = -1;
     const size_t n = (size_t)m->hp.n_layer * (size_t)n_seq;
-    const size_t bytes = (size_t)n_ctx * (size_t)m->hp.n_head_kv * (size_t)m->hp.head_dim * c->esz;
+    const size_t bytes = kv_bytes(m->hp.kvtype, (int64_t)n_ctx * m->hp.n_head_kv * m->hp.head_dim);
     c->K = (void **)calloc(n, sizeof(void *));
     c->V = (void **)calloc(n, sizeof(void *));
     for (size_t i = 0; i < n; i++) {
@@ -504,9 +518,17 @@ void orc_seq_clear(orc_ctx *c, int32_t seq)
 
 /* Store one cached row (KV appendix: one row per position holds the keys   */
 /* or values of every KV head of the layer).  F16 cache: one RNE rounding.  */
+/* Q8_0 cache (the -ctk / -ctv cache types of the KV-cache appendix):       */
+/* READING: the row is rounded to fp32, the codec's input type, and coded   */
+/* with the weights' Q8_0 codec in blocks of 32 consecutive row elements.   */
 static void kv_store(void *base, int32_t kvtype, int64_t off, const orc_real *v, int32_t n)
 {
-    if (kvtype == ORC_T_F16) {
+    if (kvtype == ORC_T_Q8_0) {
+        float *t = (float *)malloc(sizeof(float) * (size_t)n);
+        for (int32_t i = 0; i < n; i++) t[i] = (float)v[i];
+        orc_q8_0_quantize(t, n, (uint8_t *)base + kv_bytes(kvtype, off));
+        free(t);
+    } else if (kvtype == ORC_T_F16) {
         uint16_t *d = (uint16_t *)base + off;
         for (int32_t i = 0; i < n; i++) d[i] = orc_f16_from_f64((double)v[i]);
     } else {
@@ -562,8 +584,8 @@ int32_t orc_eval_tap(orc_ctx *c, int32_t seq, int32_t token, orc_real *logits, i
 #pragma omp parallel for schedule(static)
         for (int32_t hq = 0; hq < H; hq++) {
             const int32_t kvh = hq / group;
-            const uint8_t *kb = (const uint8_t *)Kc + (size_t)kvh * hd * c->esz;
-            const uint8_t *vb = (const uint8_t *)Vc + (size_t)kvh * hd * c->esz;
+            const uint8_t *kb = (const uint8_t *)Kc + kv_bytes(h.kvtype, (int64_t)kvh * hd);
+            const uint8_t *vb = (const uint8_t *)Vc + kv_bytes(h.kvtype, (int64_t)kvh * hd);
             orc_attend(q + (int64_t)hq * hd, kb, vb, h.kvtype, kd, NULL, p + 1, hd, p,
                        o + (int64_t)hq * hd, NULL);
         }

@@ -74,7 +74,9 @@ void orc_matvec(int32_t wtype, const void *w, int32_t rows, int32_t cols,
 /* rotate n_heads consecutive head vectors of size hd in place, position pos */
 void orc_rope(orc_real *v, int32_t n_heads, int32_t hd, int32_t pos, float base);
 /* one query head against n cached rows: row j of K and of V starts at
-   element j*ld and holds hd elements of type kvtype (F32 float / F16 uint16).
+   element j*ld and holds hd elements of type kvtype (F32 float / F16 uint16 /
+   Q8_0 34-byte blocks of 32 elements; then ld, hd and the start of K and V
+   are whole blocks).
    Row j sits at position row_pos[j] (row_pos == NULL: position j); rows whose
    position exceeds pos are masked.  Writes o[hd]; if w != NULL also the n
    softmax weights (exactly 0 for masked rows). */
@@ -89,7 +91,7 @@ typedef struct {
     int32_t n_layer, n_embd, n_head, n_head_kv, head_dim, n_ff, n_vocab;
     float   rms_eps, rope_base;
     int32_t wtype;   /* F32, Q8_0 or Q4_0: every 2-D matrix                  */
-    int32_t kvtype;  /* F32 or F16                                           */
+    int32_t kvtype;  /* F32, F16 or Q8_0 (Q8_0 needs head_dim % 32 == 0)     */
 } orc_hparams;
 
 /* fp32 source tensors, row-major [out][in]; per-layer entries are arrays of

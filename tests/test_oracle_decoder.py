@@ -71,10 +71,15 @@ def dense_forward(orc, hp, w, tokens):
         Q = rope(Xn @ _deq(orc, w["wq"][l], wt).T, H)
         K = rope(Xn @ _deq(orc, w["wk"][l], wt).T, Hkv)
         Vv = Xn @ _deq(orc, w["wv"][l], wt).T
-        # the cache stores K and V in its element type (f32 or f16)
-        ct = np.float16 if hp["kvtype"] == synth.F16 else np.float32
-        K = K.astype(ct).astype(np.float64)
-        Vv = Vv.astype(ct).astype(np.float64)
+        # the cache stores K and V in its element type (f32, f16, or Q8_0 blocks
+        # of 32 consecutive elements of a position's row, coded from fp32)
+        if hp["kvtype"] == synth.Q8_0:
+            K = _deq(orc, K.astype(np.float32), synth.Q8_0)
+            Vv = _deq(orc, Vv.astype(np.float32), synth.Q8_0)
+        else:
+            ct = np.float16 if hp["kvtype"] == synth.F16 else np.float32
+            K = K.astype(ct).astype(np.float64)
+            Vv = Vv.astype(ct).astype(np.float64)
         O = np.zeros((T, H * hd))
         for h in range(H):
             g = h // (H // Hkv)
@@ -102,9 +107,11 @@ def _oracle_all_logits(orc, hp, w, tokens, kind="f64", n_ctx=64):
 
 
 @pytest.mark.parametrize("wtype,kvtype", [(synth.F32, synth.F32), (synth.F32, synth.F16),
-                                          (synth.Q8_0, synth.F16), (synth.Q4_0, synth.F16)])
+                                          (synth.Q8_0, synth.F16), (synth.Q4_0, synth.F16),
+                                          (synth.F32, synth.Q8_0), (synth.Q4_0, synth.Q8_0)])
 def test_cache_equals_full_recompute(orc, wtype, kvtype):
-    hp = _hp(wtype=wtype, kvtype=kvtype)
+    # a Q8_0 cache needs whole 32-element blocks per head
+    hp = _hp(wtype=wtype, kvtype=kvtype, head_dim=32 if kvtype == synth.Q8_0 else 16)
     w = _weights(hp, 5)
     toks = synth.prompt(hp["n_vocab"], 21, 6)
     got = _oracle_all_logits(orc, hp, w, toks)
@@ -211,3 +218,44 @@ def test_kv_rows_hold_rotated_keys(orc):
     assert np.allclose(c.kv_row(0, 0, 0, 2, 1), ref, rtol=1e-6, atol=1e-6)
     assert np.allclose(c.kv_row(1, 0, 0, 2, 1),
                        (w["wv"][0].astype(np.float64) @ xn)[hd:2 * hd], rtol=1e-6, atol=1e-6)
+
+
+def test_q8_0_cache_rows_within_half_step(orc):
+    """Layer-0 K/V rows depend on the token only, so a Q8_0 cache and an f32
+    cache of the same run hold the same rows up to the codec's error: at most
+    half a step of the block's fp32 scale amax/127, plus the f16 rounding of
+    the stored scale times the largest code."""
+    hp32 = _hp(head_dim=32)
+    w = _weights(hp32, 17)
+    toks = [3, 41, 7, 7, 19]
+    ctx = {}
+    for kvt in (synth.F32, synth.Q8_0):
+        m = orc.Model(dict(hp32, kvtype=kvt), w)
+        c = orc.Context(m, 1, 8)
+        for t in toks:
+            c.eval(0, t)
+        ctx[kvt] = (m, c)
+    hd = hp32["head_dim"]
+    worst = 0.0
+    for which in (0, 1):
+        for p in range(len(toks)):
+            for g in range(hp32["n_head_kv"]):
+                x = ctx[synth.F32][1].kv_row(which, 0, 0, p, g).astype(np.float64)
+                y = ctx[synth.Q8_0][1].kv_row(which, 0, 0, p, g).astype(np.float64)
+                for b in range(hd // 32):
+                    xb, yb = x[32 * b:32 * b + 32], y[32 * b:32 * b + 32]
+                    d = np.abs(xb).max() / 127
+                    bound = d * (0.5 + 127 * 2.0 ** -11) * (1 + 1e-6)
+                    err = np.abs(xb - yb).max()
+                    assert err <= bound, (which, p, g, b, err, bound)
+                    worst = max(worst, err / d)
+    assert worst > 0.3          # the cache really is quantized
+    # the codes themselves: the stored row re-coded from its fp32 source
+    x = ctx[synth.F32][1].kv_row(0, 0, 0, 2, 1)
+    blocks = orc.quantize(x, synth.Q8_0)
+    assert np.array_equal(orc.dequantize(blocks, hd, synth.Q8_0), ctx[synth.Q8_0][1].kv_row(0, 0, 0, 2, 1))
+
+
+def test_q8_0_cache_rejects_partial_blocks(orc):
+    with pytest.raises(ValueError):
+        orc.Model(_hp(kvtype=synth.Q8_0, head_dim=16), _weights(_hp(head_dim=16), 1))

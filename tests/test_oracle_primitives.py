@@ -94,7 +94,16 @@ def _dense_attention(q, K, V, row_pos, pos):
     return w @ V.astype(np.float64), w
 
 
-@pytest.mark.parametrize("kvtype", ["f32", "f16"])
+def _q8_blocks_to_f64(b):
+    """Q8_0 block bytes -> values, read straight from the block format (f16
+    little-endian scale, then 32 int8 codes)."""
+    blk = np.frombuffer(np.ascontiguousarray(b, np.uint8).tobytes(), np.uint8).reshape(-1, 34)
+    d = blk[:, :2].copy().view("<f2").astype(np.float64)
+    codes = blk[:, 2:].view(np.int8).astype(np.float64)
+    return (codes * d).ravel()
+
+
+@pytest.mark.parametrize("kvtype", ["f32", "f16", "q8_0"])
 def test_attention_brute_force(orc, kvtype):
     rng = np.random.default_rng(5)
     n, hd = 37, 64
@@ -103,12 +112,16 @@ def test_attention_brute_force(orc, kvtype):
     V = rng.standard_normal((n, hd)).astype(np.float32)
     rp = rng.permutation(n).astype(np.int32)          # cells in any order
     pos = 20
+    ld = None
     if kvtype == "f16":
         Kb, Vb, t = orc.f16_from_f32(K), orc.f16_from_f32(V), orc.T_F16
         K, V = orc.f16_to_f32(Kb), orc.f16_to_f32(Vb)
+    elif kvtype == "q8_0":
+        Kb, Vb, t, ld = orc.quantize(K, orc.T_Q8_0), orc.quantize(V, orc.T_Q8_0), orc.T_Q8_0, hd
+        K, V = _q8_blocks_to_f64(Kb).reshape(n, hd), _q8_blocks_to_f64(Vb).reshape(n, hd)
     else:
         Kb, Vb, t = K, V, orc.T_F32
-    o, w = orc.attend(q, Kb, Vb, t, pos, row_pos=rp)
+    o, w = orc.attend(q, Kb, Vb, t, pos, row_pos=rp, ld=ld, n=n)
     o_ref, w_ref = _dense_attention(q, K, V, rp, pos)
     assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-13)
     assert np.allclose(w, w_ref, rtol=1e-12, atol=0)
@@ -131,6 +144,14 @@ def test_attention_single_row_and_stride(orc):
     o_s, _ = orc.attend(q, KK.ravel()[hd:], VV.ravel()[hd:], orc.T_F32, n, ld=3 * hd, n=n)
     o_ref, _ = _dense_attention(q, KK[:, hd:2 * hd], VV[:, hd:2 * hd], np.arange(n), n)
     assert np.allclose(o_s, o_ref, rtol=1e-12)
+    # the same with a Q8_0 cache: the middle head starts hd/32 blocks into each row
+    Kq, Vq = orc.quantize(KK, orc.T_Q8_0), orc.quantize(VV, orc.T_Q8_0)
+    skip = hd // 32 * 34
+    o_q, _ = orc.attend(q, Kq[skip:], Vq[skip:], orc.T_Q8_0, n, ld=3 * hd, n=n)
+    Kd = _q8_blocks_to_f64(Kq).reshape(n, 3 * hd)
+    Vd = _q8_blocks_to_f64(Vq).reshape(n, 3 * hd)
+    o_ref, _ = _dense_attention(q, Kd[:, hd:2 * hd], Vd[:, hd:2 * hd], np.arange(n), n)
+    assert np.allclose(o_q, o_ref, rtol=1e-12)
 
 
 def test_attention_f32_build_sums_to_one(orc):
