@@ -1,4 +1,4 @@
-// attn.hip -- causal GQA attention over the f16 / f32 KV cache (gfx950).
+// attn.hip -- causal GQA attention over the f16 / f32 / Q8_0 KV cache (gfx950).
 //
 // Each query token attends to the cached rows 0..pos of its own sequence
 // (the token's own K,V row was appended by the QKV epilogue before this
@@ -44,32 +44,57 @@ namespace {
 constexpr int CH = 64;      // cached rows per chunk
 constexpr int GMAX = 8;     // query heads per KV head handled by one block
 
-template <int KVT>
+// Element reads of cached rows: row j (of HD elements) of a chunk whose
+// first row is at `base`; `sc` is that row's block scales (Q8_0 only).
+template <int KVT, int HD>
 struct KVRow;
-template <>
-struct KVRow<T_F16> {
+template <int HD>
+struct KVRow<T_F16, HD> {
     typedef uint16_t E;
-    // 8 consecutive elements as float
-    DEV void load8(const uint16_t *p, float *o) {
-        const uint4 v = *(const uint4 *)p;
+    // 8 consecutive elements e0..e0+7 as float
+    DEV void load8(const uint16_t *base, const uint16_t *, int j, int e0, float *o) {
+        const uint4 v = *(const uint4 *)(base + (size_t)j * HD + e0);
         const h2 a = as_h2(v.x), b = as_h2(v.y), c = as_h2(v.z), d = as_h2(v.w);
         o[0] = (float)a.x; o[1] = (float)a.y; o[2] = (float)b.x; o[3] = (float)b.y;
         o[4] = (float)c.x; o[5] = (float)c.y; o[6] = (float)d.x; o[7] = (float)d.y;
     }
-    DEV float2 load2(const uint16_t *p) {
-        const h2 a = *(const h2 *)p;
+    DEV float2 load2(const uint16_t *base, const uint16_t *, int j, int e0) {
+        const h2 a = *(const h2 *)(base + (size_t)j * HD + e0);
         return make_float2((float)a.x, (float)a.y);
     }
 };
-template <>
-struct KVRow<T_F32> {
+template <int HD>
+struct KVRow<T_F32, HD> {
     typedef float E;
-    DEV void load8(const float *p, float *o) {
+    DEV void load8(const float *base, const uint16_t *, int j, int e0, float *o) {
+        const float *p = base + (size_t)j * HD + e0;
         const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
         o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
         o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
     }
-    DEV float2 load2(const float *p) { return *(const float2 *)p; }
+    DEV float2 load2(const float *base, const uint16_t *, int j, int e0) {
+        return *(const float2 *)(base + (size_t)j * HD + e0);
+    }
+};
+// Q8_0 cache: value = code * block scale, exact in fp32 (an int8 code times
+// an f16 scale needs at most 19 significand bits).
+template <int HD>
+struct KVRow<T_Q8_0, HD> {
+    typedef int8_t E;
+    DEV void load8(const int8_t *base, const uint16_t *sc, int j, int e0, float *o) {
+        const uint2 c = *(const uint2 *)(base + (size_t)j * HD + e0);
+        const float d = f16_bits_to_f32(sc[(size_t)j * (HD / 32) + (e0 >> 5)]);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            o[k] = (float)(int8_t)(c.x >> (8 * k)) * d;
+            o[4 + k] = (float)(int8_t)(c.y >> (8 * k)) * d;
+        }
+    }
+    DEV float2 load2(const int8_t *base, const uint16_t *sc, int j, int e0) {
+        const uint16_t c = *(const uint16_t *)(base + (size_t)j * HD + e0);
+        const float d = f16_bits_to_f32(sc[(size_t)j * (HD / 32) + (e0 >> 5)]);
+        return make_float2((float)(int8_t)(c & 0xff) * d, (float)(int8_t)(c >> 8) * d);
+    }
 };
 
 // Sum over groups of N consecutive lanes (N = 8, 16 or 32); every lane of a
@@ -91,7 +116,8 @@ DEV float group_sum(float v) {
 template <int HD, int KVT, int G>
 __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
     static_assert(CH == 64, "softmax statistics assume one cached row per lane");
-    typedef typename KVRow<KVT>::E E;
+    typedef KVRow<KVT, HD> R;
+    typedef typename R::E E;
     constexpr int TPK = HD / 8;          // threads per key row (scores)
     constexpr int KPP = 256 / TPK;       // key rows per pass
     constexpr int NP = CH / KPP;         // passes
@@ -112,9 +138,11 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
     const int n_kv = a.kv.n_kv;
     const float scale = 1.0f / sqrtf((float)HD);
 
-    const size_t rowbase = (((size_t)seq * n_kv + g) * a.kv.n_ctx + c0) * HD;
-    const E *Kb = (const E *)a.kv.k + rowbase;
-    const E *Vb = (const E *)a.kv.v + rowbase;
+    const size_t cell0 = ((size_t)seq * n_kv + g) * a.kv.n_ctx + c0;
+    const E *Kb = (const E *)a.kv.k + cell0 * HD;
+    const E *Vb = (const E *)a.kv.v + cell0 * HD;
+    const uint16_t *Ks = KVT == T_Q8_0 ? a.kv.k_scale + cell0 * (HD / 32) : nullptr;
+    const uint16_t *Vs = KVT == T_Q8_0 ? a.kv.v_scale + cell0 * (HD / 32) : nullptr;
     const int part = tid % TPK, krow = tid / TPK;
     const int dp = tid % TPR, kg = tid / TPR;
 
@@ -124,7 +152,7 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
     for (int ps = 0; ps < NP; ps++) {
         const int j = ps * KPP + krow;
         if (j < nk)
-            KVRow<KVT>::load8(Kb + (size_t)j * HD + part * 8, kv8[ps]);
+            R::load8(Kb, Ks, j, part * 8, kv8[ps]);
         else
 #pragma unroll
             for (int e = 0; e < 8; e++) kv8[ps][e] = 0.f;
@@ -133,7 +161,7 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < VPT; i++) {
         const int j = kg + KG * i;
-        vv[i] = j < nk ? KVRow<KVT>::load2(Vb + (size_t)j * HD + 2 * dp) : make_float2(0.f, 0.f);
+        vv[i] = j < nk ? R::load2(Vb, Vs, j, 2 * dp) : make_float2(0.f, 0.f);
     }
     float qv[G][8];
     const float *qb = a.q + ((size_t)t * a.H + g * G) * HD + part * 8;
@@ -442,7 +470,9 @@ bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
             return false;
         }
     } else {
-        ok = a.kv.kvtype == T_F16 ? launch_part<HD, T_F16>(a, T, s) : launch_part<HD, T_F32>(a, T, s);
+        ok = a.kv.kvtype == T_F16    ? launch_part<HD, T_F16>(a, T, s)
+             : a.kv.kvtype == T_Q8_0 ? launch_part<HD, T_Q8_0>(a, T, s)
+                                     : launch_part<HD, T_F32>(a, T, s);
     }
     if (!ok) return false;
     launch((k_attn_merge<HD>), dim3(a.H, T), dim3(256), 0, s, a);

@@ -189,7 +189,7 @@ static bool valid_hparams(const dec_hparams &h) {
     if (h.head_dim != 64 && h.head_dim != 128 && h.head_dim != 256) return false;
     if (h.n_head % h.n_head_kv || h.n_head / h.n_head_kv > 8) return false;
     if (h.wtype != DEC_F32 && h.wtype != DEC_Q8_0 && h.wtype != DEC_Q4_0) return false;
-    if (h.kvtype != DEC_F32 && h.kvtype != DEC_F16) return false;
+    if (h.kvtype != DEC_F32 && h.kvtype != DEC_F16 && h.kvtype != DEC_Q8_0) return false;
     if (h.n_embd % 32 || (h.n_head * h.head_dim) % 32) return false;
     if (h.wtype != DEC_F32 && h.n_ff % 32) return false;
     if (!(h.rms_eps >= 0.f) || !(h.rope_base > 0.f)) return false;
@@ -721,9 +721,13 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
         c->own_stream = true;
     }
     const int d = h.n_embd, qd = m->qd, Fp = m->Fp, V = h.n_vocab, hd = h.head_dim;
-    const size_t esz = h.kvtype == DEC_F16 ? 2 : 4;
+    // Q8_0: one int8 code per element plus one f16 scale per 32 elements, and
+    // f32 staging rows for the new K / V of a ubatch (shared by the layers)
+    const bool q8 = h.kvtype == DEC_Q8_0;
+    const size_t esz = h.kvtype == DEC_F32 ? 4 : q8 ? 1 : 2;
     const size_t kv_elems = (size_t)n_seq * h.n_head_kv * n_ctx * hd;
-    bool ok = true;
+    float *kv_stage = q8 ? (float *)c->mem.get((size_t)c->Tmax * 2 * m->kd * 4) : nullptr;
+    bool ok = !q8 || kv_stage;
     c->kv.resize(h.n_layer);
     for (int l = 0; ok && l < h.n_layer; l++) {
         KVLayer &L = c->kv[l];
@@ -734,6 +738,12 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
         L.k = c->mem.get(kv_elems * esz);
         L.v = c->mem.get(kv_elems * esz);
         ok = L.k && L.v;
+        if (ok && q8) {
+            L.k_scale = (uint16_t *)c->mem.get(kv_elems / 32 * 2);
+            L.v_scale = (uint16_t *)c->mem.get(kv_elems / 32 * 2);
+            L.stage = kv_stage;
+            ok = L.k_scale && L.v_scale;
+        }
     }
     c->chunk = attention_chunk(h.kvtype, hd);
     c->max_chunks = (int)((n_ctx + c->chunk - 1) / c->chunk);
@@ -899,6 +909,11 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
             launch_rmsnorm(c->x, d, L.attn_norm, d, h.rms_eps, nullptr, T, c->xn, c->xn_lo, d, s);
             return launch_gemm(L.wqkv, c->xn, c->xn_lo, d, eq, T, c->gws, c->gws_bytes, s);
         });
+        if (h.kvtype == DEC_Q8_0)
+            ok = ok && stage(c, -1, l, [&] {
+                launch_kv_quant(c->kv[l], ti, T, s);
+                return true;
+            });
         AttnArgs at;
         at.q = c->q;
         at.qh = c->qh;

@@ -48,6 +48,19 @@ DEV void store_kv_pair(void *base, int kvtype, size_t idx, float a, float b) {
     }
 }
 
+// The pair (a, b) at row rr of the token's new K (which = 0) or V (1) row:
+// into its cell of an f16 / f32 cache, or into the f32 staging rows that
+// launch_kv_quant codes for a Q8_0 cache.
+DEV void append_kv_pair(const EpiArgs &e, int which, int t, int seq, int pos, int rr, float a, float b) {
+    if (e.kv.kvtype == T_Q8_0) {
+        *(float2 *)(e.kv.stage + ((size_t)t * 2 + which) * e.kd + rr) = make_float2(a, b);
+        return;
+    }
+    const int hd = e.kv.hd, g = rr / hd, el = rr % hd;
+    const size_t idx = (((size_t)seq * e.kv.n_kv + g) * e.kv.n_ctx + pos) * hd + el;
+    store_kv_pair(which ? e.kv.v : e.kv.k, e.kv.kvtype, idx, a, b);
+}
+
 // Applies epilogue EPI to the pair (r0, r1) = values (a, b) of token t.
 // p is the pair index (the feature index for SWIGLU).
 template <int EPI>
@@ -82,18 +95,12 @@ DEV void epi_pair(const EpiArgs &e, int t, int p, int r0, int r1, float a, float
             const float2 cs = *(const float2 *)(e.rope_cs + ((size_t)pos * (hd >> 1) + i) * 2);
             const float ra = a * cs.x - b * cs.y;
             const float rb = a * cs.y + b * cs.x;
-            if (r0 < e.qd) {
+            if (r0 < e.qd)
                 store_q_pair(e, t, r0, ra, rb);
-            } else {
-                const int g = rr / hd, el = rr % hd;
-                const size_t idx = (((size_t)e.tok.seq[t] * e.kv.n_kv + g) * e.kv.n_ctx + pos) * hd + el;
-                store_kv_pair(e.kv.k, e.kv.kvtype, idx, ra, rb);
-            }
+            else
+                append_kv_pair(e, 0, t, e.tok.seq[t], pos, rr, ra, rb);
         } else {
-            const int rr = r0 - e.qd - e.kd;
-            const int g = rr / hd, el = rr % hd;
-            const size_t idx = (((size_t)e.tok.seq[t] * e.kv.n_kv + g) * e.kv.n_ctx + pos) * hd + el;
-            store_kv_pair(e.kv.v, e.kv.kvtype, idx, a, b);
+            append_kv_pair(e, 1, t, e.tok.seq[t], pos, r0 - e.qd - e.kd, a, b);
         }
         break;
     }
@@ -136,23 +143,16 @@ DEV void epi_pair_pre(const EpiArgs &e, int t, int p, int r0, int r1, float a, f
         y[r0] = pre.y0 + a;
         y[r1] = pre.y1 + b;
     } else if (EPI == EPI_QKV) {
-        const int hd = e.kv.hd;
         if (r0 < e.qd + e.kd) {
             const int rr = r0 < e.qd ? r0 : r0 - e.qd;
             const float ra = a * pre.cs.x - b * pre.cs.y;
             const float rb = a * pre.cs.y + b * pre.cs.x;
-            if (r0 < e.qd) {
+            if (r0 < e.qd)
                 store_q_pair(e, t, r0, ra, rb);
-            } else {
-                const int g = rr / hd, el = rr % hd;
-                const size_t idx = (((size_t)pre.seq * e.kv.n_kv + g) * e.kv.n_ctx + pre.pos) * hd + el;
-                store_kv_pair(e.kv.k, e.kv.kvtype, idx, ra, rb);
-            }
+            else
+                append_kv_pair(e, 0, t, pre.seq, pre.pos, rr, ra, rb);
         } else {
-            const int rr = r0 - e.qd - e.kd;
-            const int g = rr / hd, el = rr % hd;
-            const size_t idx = (((size_t)pre.seq * e.kv.n_kv + g) * e.kv.n_ctx + pre.pos) * hd + el;
-            store_kv_pair(e.kv.v, e.kv.kvtype, idx, a, b);
+            append_kv_pair(e, 1, t, pre.seq, pre.pos, r0 - e.qd - e.kd, a, b);
         }
     } else {
         epi_pair<EPI>(e, t, p, r0, r1, a, b);

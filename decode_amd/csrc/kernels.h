@@ -46,7 +46,7 @@ enum PairMode { PAIR_ADJ = 0, PAIR_GU = 1 };
 enum Epi {
     EPI_STORE = 0,   // y[t][n] = acc                         (f32)
     EPI_RESID = 1,   // y[t][n] += acc                        (f32 residual stream)
-    EPI_QKV = 2,     // RoPE on q,k; q -> qout f32; k,v -> cache (kvtype)
+    EPI_QKV = 2,     // RoPE on q,k; q -> qout f32; k,v -> cache (kvtype; Q8_0: -> kv.stage)
     EPI_SWIGLU = 3,  // rows interleaved 32 gate / 32 up; h[t][j] = f16(silu(g) * u)
 };
 
@@ -56,9 +56,15 @@ struct TokInfo {
     const int32_t *seq = nullptr;   // sequence id
 };
 
-// KV cache of one layer: [n_seq][n_head_kv][n_ctx][head_dim], kvtype elements.
+// One layer's cache, [seq][kv head][position][hd] elements of kvtype.  A
+// Q8_0 cache holds int8 codes in k / v and the f16 scale of each 32-element
+// block in k_scale / v_scale ([seq][kv head][position][hd/32]); the QKV
+// epilogue leaves the new rows in `stage` as f32 ([token][K, V][n_kv*hd]) and
+// launch_kv_quant codes them into their cells.
 struct KVLayer {
     void *k = nullptr, *v = nullptr;
+    uint16_t *k_scale = nullptr, *v_scale = nullptr;
+    float *stage = nullptr;
     int kvtype = 0;
     int n_ctx = 0, n_kv = 0, hd = 0;
 };
@@ -107,12 +113,15 @@ struct InArgs {
 void launch_quantize(const float *src, int rows, int K, QMat &m, int mode, int row_off,
                      hipStream_t s);
 // fp32 copy into a (possibly padded) F32 matrix: src [rows][K_src] -> m rows
-// GGUF-style blocks (f16 scale + codes, 18 / 34 bytes, 2-byte aligned) of a
-// rows x K Q4_0 / Q8_0 tensor -> scales and codes of rows dst_row(r) of m.
-void launch_put_blocks(const void *src, int rows, int K, QMat &m, int mode, int row_off, hipStream_t s);
 // dst_row(r), columns [0, K_src); the caller zero-fills padding beforehand.
 void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, int row_off,
                      hipStream_t s);
+// GGUF-style blocks (f16 scale + codes, 18 / 34 bytes, 2-byte aligned) of a
+// rows x K Q4_0 / Q8_0 tensor -> scales and codes of rows dst_row(r) of m.
+void launch_put_blocks(const void *src, int rows, int K, QMat &m, int mode, int row_off, hipStream_t s);
+// Q8_0 cache: codes the T staged K and V rows (kv.stage) into the cells at
+// (tok.seq[t], tok.pos[t]), with the weights' Q8_0 block definition.
+void launch_kv_quant(const KVLayer &kv, TokInfo tok, int T, hipStream_t s);
 
 // Number of compute units the mat-vec grid is sized for (default 256).
 void matvec_set_num_cu(int n);

@@ -17,6 +17,31 @@ DEV int dst_row(int mode, int r, int row_off) {
 // fp32 arithmetic with no contraction, so codes match any IEEE fp32
 // implementation of the same steps bit for bit; the scale is stored as f16
 // (round to nearest even).
+// Q8_0 coding of 32 values: the scale's f16 bits and the 32 codes packed
+// little-endian into 8 dwords.
+DEV uint16_t q8_block(const float *v, uint32_t *packed) {
+#pragma clang fp contract(off)
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
+    float d = amax / 127.0f;
+    // keep the f16 rounding a separate step: a fused multiply-add form of
+    // the conversion would turn a -0 scale into +0
+    asm volatile("" : "+v"(d));
+    const float id = d != 0.f ? 1.0f / d : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int q = (int)roundf(v[4 * i + e] * id);
+            w |= ((uint32_t)(q & 0xff)) << (8 * e);
+        }
+        packed[i] = w;
+    }
+    return f32_to_f16_bits(d);
+}
+
 __global__ __launch_bounds__(256) void k_quantize(const float *src, int rows, int K, QMat m,
                                                   int mode, int row_off) {
 #pragma clang fp contract(off)
@@ -33,26 +58,8 @@ __global__ __launch_bounds__(256) void k_quantize(const float *src, int rows, in
     }
     const int dr = dst_row(mode, r, row_off);
     if (m.wtype == T_Q8_0) {
-        float amax = 0.f;
-#pragma unroll
-        for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
-        float d = amax / 127.0f;
-        // keep the f16 rounding a separate step: a fused multiply-add form of
-        // the conversion would turn a -0 scale into +0
-        asm volatile("" : "+v"(d));
-        const float id = d != 0.f ? 1.0f / d : 0.f;
-        m.d[(size_t)dr * nb + b] = f32_to_f16_bits(d);
         uint32_t packed[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int q = (int)roundf(v[4 * i + e] * id);
-                w |= ((uint32_t)(q & 0xff)) << (8 * e);
-            }
-            packed[i] = w;
-        }
+        m.d[(size_t)dr * nb + b] = q8_block(v, packed);
         uint4 *dst = (uint4 *)((int8_t *)m.qs + (size_t)dr * K + b * 32);
         dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
         dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
@@ -98,6 +105,31 @@ __global__ __launch_bounds__(256) void k_copy_f32(const float *src, int rows, in
     if (idx >= (long long)rows * K_src) return;
     const int r = (int)(idx / K_src), k = (int)(idx % K_src);
     ((float *)m.qs)[(size_t)dst_row(mode, r, row_off) * m.K + k] = src[idx];
+}
+
+// ---- Q8_0 KV cache: staged f32 rows -> coded cells -------------------------
+// One thread per 32-element block of the T new K and V rows (the same coding
+// as the Q8_0 weights); block b of row (t, which) covers kv head b / (hd/32).
+__global__ __launch_bounds__(256) void k_kv_quant(KVLayer kv, TokInfo tok, int T) {
+    const int hd = kv.hd, bph = hd >> 5, kd = kv.n_kv * hd, nbr = kd >> 5;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)T * 2 * nbr) return;
+    const int b = (int)(idx % nbr), which = (int)((idx / nbr) & 1), t = (int)(idx / (2 * nbr));
+    const float *x = kv.stage + ((size_t)t * 2 + which) * kd + (size_t)b * 32;
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 32; j += 4) {
+        const float4 f = *(const float4 *)(x + j);
+        v[j] = f.x; v[j + 1] = f.y; v[j + 2] = f.z; v[j + 3] = f.w;
+    }
+    uint32_t packed[8];
+    const uint16_t dbits = q8_block(v, packed);
+    const int g = b / bph, bl = b % bph;
+    const size_t cell = ((size_t)tok.seq[t] * kv.n_kv + g) * kv.n_ctx + tok.pos[t];
+    (which ? kv.v_scale : kv.k_scale)[cell * bph + bl] = dbits;
+    uint4 *dst = (uint4 *)((int8_t *)(which ? kv.v : kv.k) + cell * hd + bl * 32);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
 }
 
 // ---- file blocks -> stored layout ------------------------------------------
@@ -243,6 +275,11 @@ void launch_put_blocks(const void *src, int rows, int K, QMat &m, int mode, int 
     const long long n = (long long)rows * (K / 32);
     launch(k_put_blocks, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const uint16_t *)src, rows, K, m,
            mode, row_off);
+}
+
+void launch_kv_quant(const KVLayer &kv, TokInfo tok, int T, hipStream_t s) {
+    const long long n = (long long)T * 2 * (kv.n_kv * kv.hd / 32);
+    launch(k_kv_quant, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kv, tok, T);
 }
 
 void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, float *ss_out, hipStream_t s) {

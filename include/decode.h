@@ -43,9 +43,12 @@ typedef enum { DEC_F32 = 0, DEC_F16 = 1, DEC_Q8_0 = 2, DEC_Q4_0 = 3 } dec_type;
 /* Hyper-parameters (the article's step 4: embedding length, block count,
  * feed-forward length, head count, KV head count, RoPE frequency base).
  * wtype applies to every 2-D matrix (F32, Q8_0 or Q4_0); kvtype is the
- * cache element type (F32 or F16).  Quantized types need n_embd, n_ff and
- * n_head*head_dim to be multiples of 32; head_dim must be even and at most
- * 256, and n_head a multiple of n_head_kv. */
+ * cache element type (F32, F16, or Q8_0: the KV-cache appendix's separately
+ * typed key / value cache, here one type for both; each cached head row is
+ * coded in 32-element Q8_0 blocks as it is appended, from the fp32 K / V
+ * values, and attention reads code * scale).  Quantized weight types need
+ * n_embd, n_ff and n_head*head_dim to be multiples of 32; head_dim must be
+ * 64, 128 or 256, and n_head a multiple of n_head_kv. */
 typedef struct {
     int32_t n_layer, n_embd, n_head, n_head_kv, head_dim, n_ff, n_vocab;
     float   rms_eps;     /* 1e-5 */
@@ -132,7 +135,7 @@ int32_t dec_gguf_inspect(const char *path, dec_hparams *hp);
 /* Loads a file that dec_gguf_inspect accepts.  The file is memory-mapped;
  * each tensor's bytes are copied from the mapping straight to the device,
  * where its blocks are split into codes and scales and placed in the fused
- * matrices.  kvtype: the cache type (DEC_F16 or DEC_F32).  NULL on any error
+ * matrices.  kvtype: the cache type (DEC_F16, DEC_F32 or DEC_Q8_0).  NULL on any error
  * (the reason is logged). */
 dec_model *dec_model_load_gguf(const char *path, int32_t kvtype, const dec_allocator *alloc, void *hip_stream);
 
