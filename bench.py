@@ -110,6 +110,63 @@ def cpu_baseline(hp, weights_dev, prompt, n_prompt_tokens, n_decode_tokens):
                       f"{n_prompt_tokens + n_decode_tokens} ({dt:.1f} s)"}
 
 
+def kv_bytes_per_elem(kvtype: int) -> float:
+    return {0: 4.0, 1: 2.0, 2: 34.0 / 32.0}[kvtype]
+
+
+def attention_roofline(hp, kvtype, probe, ctx_len):
+    """Achieved bandwidth of one layer's decode attention (partials + merge)
+    from its probe: the K and V rows of ctx_len cached positions are the
+    algorithmic bytes (codes and scales for Q8_0)."""
+    if not probe or not probe[1]:
+        return None
+    kd = hp["n_head_kv"] * hp["head_dim"]
+    nbytes = ctx_len * 2 * kd * kv_bytes_per_elem(kvtype)
+    avg = probe[0] / 1e3 / probe[1]
+    ach = nbytes / avg / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": int(nbytes),
+            "mean_context": ctx_len, "avg_us": round(avg * 1e6, 2), "launches_timed": probe[1]}
+
+
+def kv_q8_leg(dec, torch, model, hp, prompt, n_ctx, n_ubatch, sp, warm, steps, probe_layer, log):
+    """The generation loop again with a Q8_0 KV cache: timed prefill, then
+    `steps` timed greedy decode steps; attention of the probed layer timed
+    live over the same steps."""
+    ctx = dec.Context(model, n_ctx=n_ctx, n_batch=len(prompt), n_ubatch=n_ubatch, stream=sp)
+    ctx.set_probe(dec.K_ATTN, probe_layer)
+    assert ctx.prefill(prompt, 0) == 0
+    tok = ctx.argmax(-1)
+    for _ in range(warm):
+        assert ctx.decode([tok], [0]) == 0
+        tok = ctx.argmax(0)
+    ctx.clear(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    assert ctx.prefill(prompt, 0) == 0
+    tok = ctx.argmax(-1)
+    prefill_s = time.perf_counter() - t0
+    ctx.set_probe(dec.K_ATTN, probe_layer)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if ctx.decode([tok], [0]) != 0:
+            raise RuntimeError("Q8_0-cache decode step failed")
+        tok = ctx.argmax(0)
+    torch.cuda.synchronize()
+    decode_s = time.perf_counter() - t0
+    probe = ctx.probe()
+    mean_ctx = len(prompt) + (steps + 1) / 2.0
+    ctx.close()
+    log(f"Q8_0 KV cache: prefill {len(prompt) / prefill_s:.0f} tok/s, decode {steps / decode_s:.1f} tok/s")
+    return {"decode_tokens_per_s": round(steps / decode_s, 2), "steps": steps,
+            "prefill_tokens_per_s": round(len(prompt) / prefill_s, 1),
+            "kv_bytes_per_position": int(hp["n_layer"] * 2 * hp["n_head_kv"] * hp["head_dim"] * 34 / 32),
+            "attention": attention_roofline(hp, 2, probe, mean_ctx),
+            "note": "same weights and prompt, K/V cached as Q8_0 blocks; attention = split-K partials "
+                    "+ merge of one layer, timed live; prefill attention takes the split-K kernel"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +176,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prompt", type=int, default=3)
     ap.add_argument("--cpu-decode", type=int, default=30)
+    ap.add_argument("--no-kv-q8", action="store_true",
+                    help="skip the leg that reruns the decode loop with a Q8_0 KV cache")
+    ap.add_argument("--kv-q8-steps", type=int, default=128)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (4 times), the reference kernel for "
                          "scaling the HBM fetch/write counters")
@@ -155,13 +215,18 @@ def main():
     model = dec.Model(hp, weights, stream=sp)
     torch.cuda.synchronize()
     log(f"model loaded (quantized on device) in {time.perf_counter() - t0:.1f} s")
+    model_q8 = None
+    if not args.no_kv_q8:
+        # same weights, Q8_0 KV cache (the KV-cache appendix's quantized cache types)
+        model_q8 = dec.Model(dict(hp, kvtype=synth.Q8_0), weights, stream=sp)
+        torch.cuda.synchronize()
     if args.no_cpu_baseline:
         del weights
         torch.cuda.empty_cache()
 
     prompt = synth.prompt(hp["n_vocab"], n_prompt, 2000 + W["seed"] % 1000)
     n_sampled = 64                      # decode steps run with the sampler chain after the timed loop
-    n_ctx = n_prompt + steps + warm + n_sampled + 8
+    n_ctx = n_prompt + steps + warm + n_sampled + 32 + 8   # + the 32 attention-probe steps
     ctx = dec.Context(model, n_ctx=n_ctx, n_batch=n_prompt, n_ubatch=W["n_ubatch"], stream=sp)
     probe_layer = hp["n_layer"] // 2
     ctx.set_probe(dec.K_FFN_GU, probe_layer)
@@ -199,6 +264,7 @@ def main():
     st = ctx.stats()
     log(f"prefill {n_prompt / prefill_s:.0f} tok/s, decode {steps / decode_s:.1f} tok/s")
 
+
     # the sampler chain in the generation loop (after, and outside, the timed region):
     # penalty over the last 64 tokens, top-k 40, top-p 0.95, min-p 0.05, temperature 0.8
     sprm = dict(top_k=40, top_p=0.95, min_p=0.05, temp=0.8, repeat_penalty=1.1, penalty_last_n=64, seed=1234)
@@ -225,6 +291,24 @@ def main():
                "note": "us_per_call = one dec_sampler_sample on a resident logits row: history upload, "
                        "the k_sample kernel, token download and stream synchronisation"}
     log(f"sampled decode {n_sampled / sampled_s:.1f} tok/s, sampler call {call_s * 1e6:.1f} us")
+
+    # attention (split-K partials + merge) of the probed layer after the
+    # sampled steps, over a few more steps outside the timed regions
+    ctx.set_probe(dec.K_ATTN, probe_layer)
+    n_attn = 32
+    for _ in range(n_attn):
+        assert ctx.decode([tok], [0]) == 0
+        tok = ctx.argmax(0)
+    at_probe = ctx.probe()
+    attn_ctx = ctx.pos_max(0) + 1 - (n_attn - 1) / 2.0
+    ctx.set_probe(-1, 0)
+
+    kv_q8 = None
+    if model_q8 is not None:
+        kv_q8 = kv_q8_leg(dec, torch, model_q8, hp, prompt, n_ctx, W["n_ubatch"], sp, warm,
+                          args.kv_q8_steps, probe_layer, log)
+        kv_q8["f16_attention"] = attention_roofline(hp, 1, at_probe, attn_ctx)
+        model_q8.close()
 
     alg = algorithmic(hp, n_prompt, steps)
     F, d = hp["n_ff"], hp["n_embd"]
@@ -300,6 +384,7 @@ def main():
         "prefill_roofline": pf_roof,
         "graph_replays": st["n_graph_replays"],
         "sampler": sampler,
+        "kv_q8_0": kv_q8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

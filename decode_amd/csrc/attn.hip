@@ -315,6 +315,48 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 constexpr int MW = 2;                // wavefronts per block of the MFMA kernel
 constexpr int CHM = 32 * MW;        // cached rows per chunk of the MFMA kernel
 
+// The block's wavefronts combined into the chunk partial (m, l, acc per head)
+// of an MFMA kernel: O row (head) of accumulator r < 4 is 4 (lane/32) + r,
+// column lane%32; m, l are per head lane%32.
+template <int HD>
+DEV void mfma_combine(const AttnArgs &a, int c, int g, int t, int G, float m, float l, const f16x *o,
+                      float (*cm)[32], float (*cl)[32], float (*co)[GMAX][HD]) {
+    constexpr int DT = HD / 32;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, ln = lane & 31;
+    if (lane < 32) {
+        cm[w][ln] = m;
+        cl[w][ln] = l;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int hh = 4 * hf + r;
+        if (hh < G)
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) co[w][hh][32 * dt + ln] = o[dt][r];
+    }
+    __syncthreads();
+    const size_t mc = (size_t)a.max_chunks;
+    for (int i = tid; i < G * HD; i += MW * 64) {
+        const int h = i / HD, d = i % HD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < MW; k++) M = fmaxf(M, cm[k][h]);
+        float acc = 0.f, L = 0.f;
+#pragma unroll
+        for (int k = 0; k < MW; k++) {
+            const float f = cm[k][h] == -INFINITY ? 0.f : __expf(cm[k][h] - M);
+            acc += co[k][h][d] * f;
+            L += cl[k][h] * f;
+        }
+        const size_t hh = (size_t)t * a.H + g * G + h;
+        a.part[(hh * mc + c) * HD + d] = acc;
+        if (d == 0) {
+            a.ml[(hh * mc + c) * 2 + 0] = M;
+            a.ml[(hh * mc + c) * 2 + 1] = L;
+        }
+    }
+}
+
 template <int HD>
 __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
     constexpr int KS = HD / 16;          // k-steps of S^T = K Q^T
@@ -406,44 +448,162 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
         }
     }
 
-    // ---- combine the block's wavefronts into the chunk partial ----
-    // O row (head) of accumulator r < 4 is 4 (lane/32) + r, column lane%32
-    if (lane < 32) {
-        cm[w][ln] = m;
-        cl[w][ln] = l;
+    mfma_combine<HD>(a, c, g, t, G, m, l, o, cm, cl, co);
+}
+
+// Q8_0 cache: the same chunk partials from matrix cores on exact codes.
+//   S^T = K Q^T   each 32-dim block b is its own temporary tile T_b (codes as
+//                 f16, exact, against q / sqrt(hd) value + remainder), then
+//                 S^T[key] += d_K(key, b) T_b[key] in fp32.  The dims of
+//                 block b are split by lane half (16 contiguous code bytes
+//                 per lane, k-step 2b taking the first 8, 2b+1 the last 8);
+//                 q is read in the same order.
+//   O = P V       output tile dt (32 dims) is exactly V block dt, so its
+//                 scale d_V(key, dt) varies only along the keys and folds
+//                 into P: A = P d_V as f16 value + remainder, B = the codes.
+template <int NB>
+struct ScaleVec;
+template <>
+struct ScaleVec<2> {
+    typedef uint32_t T;
+    DEV uint16_t get(T v, int b) { return (uint16_t)(v >> (16 * b)); }
+};
+template <>
+struct ScaleVec<4> {
+    typedef uint2 T;
+    DEV uint16_t get(T v, int b) { return (uint16_t)((b < 2 ? v.x : v.y) >> (16 * (b & 1))); }
+};
+
+DEV h8 codes_to_h8(uint32_t lo, uint32_t hi) {
+    h8 r;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        r[k] = (f16)(float)(int8_t)(lo >> (8 * k));
+        r[4 + k] = (f16)(float)(int8_t)(hi >> (8 * k));
     }
+    return r;
+}
+
+template <int HD>
+__global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
+    constexpr int KS = HD / 16;          // k-steps of S^T = K Q^T
+    constexpr int NB = HD / 32;          // blocks per row = 32-dim tiles of O
+    typedef ScaleVec<NB> SV;
+    typedef typename SV::T ST;
+    __shared__ float cm[MW][32], cl[MW][32];
+    __shared__ __attribute__((aligned(16))) float co[MW][GMAX][HD];
+
+    const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, ln = lane & 31;
+    const int pos = a.tok.pos[t], seq = a.tok.seq[t];
+    const int G = a.H / a.kv.n_kv;
+    const int c0 = c * CHM;
+    if (c0 > pos) return;                              // uniform per block
+    const int k0 = c0 + 32 * w;                        // this wavefront's first key
+    const size_t cell0 = ((size_t)seq * a.kv.n_kv + g) * a.kv.n_ctx;
+    const int8_t *Kc = (const int8_t *)a.kv.k + cell0 * HD;
+    const int8_t *Vc = (const int8_t *)a.kv.v + cell0 * HD;
+    const ST *Ks = (const ST *)(a.kv.k_scale + cell0 * NB);
+    const ST *Vs = (const ST *)(a.kv.v_scale + cell0 * NB);
+
+    // ---- every load at entry; rows past pos are replaced by row pos ----
+    // K codes of key k0 + lane%32: block b, dims 32 b + 16 (lane/32) .. + 15
+    uint4 kc[NB];
+    const int kr = min(k0 + ln, pos);
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const int hh = 4 * hf + r;
-        if (hh < G)
+    for (int b = 0; b < NB; b++) kc[b] = *(const uint4 *)(Kc + (size_t)kr * HD + 32 * b + 16 * hf);
+    // q / sqrt(hd) (value + remainder) of head lane%32 in the same dim order
+    h8 qa[KS], qb[KS];
+    const size_t qo = ((size_t)t * a.H + g * G + min(ln, G - 1)) * HD + 16 * hf;
 #pragma unroll
-            for (int dt = 0; dt < DT; dt++) co[w][hh][32 * dt + ln] = o[dt][r];
+    for (int ks = 0; ks < KS; ks++) {
+        const int off = 32 * (ks >> 1) + 8 * (ks & 1);
+        qa[ks] = *(const h8 *)((const f16 *)a.qh + qo + off);
+        qb[ks] = *(const h8 *)((const f16 *)a.ql + qo + off);
     }
-    __syncthreads();
-    const size_t mc = (size_t)a.max_chunks;
-    for (int i = tid; i < G * HD; i += MW * 64) {
-        const int h = i / HD, d = i % HD;
-        float M = -INFINITY;
+    // block scales of the keys of accumulator register r: k0 + 8 (r/4) + 4 (lane/32) + r%4
+    ST ksv[16], vsv[16];
 #pragma unroll
-        for (int k = 0; k < MW; k++) M = fmaxf(M, cm[k][h]);
-        float acc = 0.f, L = 0.f;
+    for (int r = 0; r < 16; r++) {
+        const int key = min(k0 + 8 * (r >> 2) + 4 * hf + (r & 3), pos);
+        ksv[r] = Ks[key];
+        vsv[r] = Vs[key];
+    }
+    // V codes, B operand of O = P V for k-step s: element e of lane l is key
+    // 16 s + 8 (e/4) + 4 (l/32) + e%4 at dim 32 dt + l%32
+    int8_t vc[NB][2][8];
 #pragma unroll
-        for (int k = 0; k < MW; k++) {
-            const float f = cm[k][h] == -INFINITY ? 0.f : __expf(cm[k][h] - M);
-            acc += co[k][h][d] * f;
-            L += cl[k][h] * f;
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const int key = min(k0 + 16 * s + 8 * (e >> 2) + 4 * hf + (e & 3), pos);
+#pragma unroll
+            for (int dt = 0; dt < NB; dt++) vc[dt][s][e] = Vc[(size_t)key * HD + 32 * dt + ln];
         }
-        const size_t hh = (size_t)t * a.H + g * G + h;
-        a.part[(hh * mc + c) * HD + d] = acc;
-        if (d == 0) {
-            a.ml[(hh * mc + c) * 2 + 0] = M;
-            a.ml[(hh * mc + c) * 2 + 1] = L;
+
+    // ---- S^T = K Q^T, one exact tile per block, scaled per key ----
+    f16x sacc;
+#pragma unroll
+    for (int r = 0; r < 16; r++) sacc[r] = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        const h8 klo = codes_to_h8(kc[b].x, kc[b].y), khi = codes_to_h8(kc[b].z, kc[b].w);
+        f16x tb;
+#pragma unroll
+        for (int r = 0; r < 16; r++) tb[r] = 0.f;
+        tb = __builtin_amdgcn_mfma_f32_32x32x16_f16(klo, qa[2 * b], tb, 0, 0, 0);
+        tb = __builtin_amdgcn_mfma_f32_32x32x16_f16(klo, qb[2 * b], tb, 0, 0, 0);
+        tb = __builtin_amdgcn_mfma_f32_32x32x16_f16(khi, qa[2 * b + 1], tb, 0, 0, 0);
+        tb = __builtin_amdgcn_mfma_f32_32x32x16_f16(khi, qb[2 * b + 1], tb, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; r++) sacc[r] += f16_bits_to_f32(SV::get(ksv[r], b)) * tb[r];
+    }
+
+    // ---- causal mask and this wavefront's softmax statistics per head ----
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        const int key = k0 + (r >> 2) * 8 + 4 * hf + (r & 3);
+        if (key > pos) sacc[r] = -INFINITY;
+        m = fmaxf(m, sacc[r]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    float l = 0.f, p[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        p[r] = m == -INFINITY ? 0.f : __expf(sacc[r] - m);
+        l += p[r];
+    }
+    l += __shfl_xor(l, 32, 64);
+
+    // ---- O = P V: tile dt takes A = P d_V(key, dt) (value + remainder) ----
+    f16x o[NB];
+#pragma unroll
+    for (int dt = 0; dt < NB; dt++) {
+        h8 ph[2], pl[2];
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const float pv = p[r] * f16_bits_to_f32(SV::get(vsv[r], dt));
+            const f16 p16 = (f16)pv;
+            ph[r >> 3][r & 7] = p16;
+            pl[r >> 3][r & 7] = (f16)(pv - (float)p16);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++) o[dt][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            h8 vb;
+#pragma unroll
+            for (int e = 0; e < 8; e++) vb[e] = (f16)(float)vc[dt][s][e];
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ph[s], vb, o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pl[s], vb, o[dt], 0, 0, 0);
         }
     }
+    mfma_combine<HD>(a, c, g, t, G, m, l, o, cm, cl, co);
 }
 
 // Chunk size of the path launch_attention takes for this cache.
-bool mfma_path(int kvtype, int hd) { return kvtype == T_F16 && (hd == 64 || hd == 128); }
+bool mfma_path(int kvtype, int hd) { return (kvtype == T_F16 || kvtype == T_Q8_0) && (hd == 64 || hd == 128); }
 int chunk_for(int kvtype, int hd) { return mfma_path(kvtype, hd) ? CHM : CH; }
 
 template <int HD, int KVT>
@@ -464,7 +624,10 @@ bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
     if (mfma_path(a.kv.kvtype, HD)) {
         if constexpr (HD <= 128) {
             if (a.H / a.kv.n_kv > GMAX || !a.qh || !a.ql) return false;
-            launch(k_attn_mfma<HD>, dim3(a.max_chunks, a.kv.n_kv, T), dim3(MW * 64), 0, s, a);
+            if (a.kv.kvtype == T_Q8_0)
+                launch(k_attn_mfma_q8<HD>, dim3(a.max_chunks, a.kv.n_kv, T), dim3(MW * 64), 0, s, a);
+            else
+                launch(k_attn_mfma<HD>, dim3(a.max_chunks, a.kv.n_kv, T), dim3(MW * 64), 0, s, a);
             ok = true;
         } else {
             return false;
