@@ -461,6 +461,41 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
 //   O = P V       output tile dt (32 dims) is exactly V block dt, so its
 //                 scale d_V(key, dt) varies only along the keys and folds
 //                 into P: A = P d_V as f16 value + remainder, B = the codes.
+// A code c becomes an f16 with byte permutes: the byte c + 128 under the
+// exponent of 1024 is the f16 1152 + c, and one packed subtraction of 1152
+// leaves c (all exact).  Each wavefront's 32 block scales of K and V go
+// through LDS as f32, one global load per lane.
+constexpr uint32_t F16_1024_BYTES = 0x64646464u;   // every byte the high byte of f16 1024
+constexpr uint32_t H2_1152 = 0x64806480u;          // f16 pair (1152, 1152)
+
+DEV h2 h2_minus_1152(uint32_t v) { return as_h2(v) - as_h2(H2_1152); }
+
+// Four codes (one dword, code k in byte k) -> f16 pairs (c0, c1), (c2, c3).
+DEV void codes4_to_h2(uint32_t w, h2 &a, h2 &b) {
+    const uint32_t x = w ^ 0x80808080u;
+    a = h2_minus_1152(__builtin_amdgcn_perm(F16_1024_BYTES, x, 0x04010400u));
+    b = h2_minus_1152(__builtin_amdgcn_perm(F16_1024_BYTES, x, 0x04030402u));
+}
+
+DEV h8 codes8_to_h8(uint32_t lo, uint32_t hi) {
+    h2 p[4];
+    codes4_to_h2(lo, p[0], p[1]);
+    codes4_to_h2(hi, p[2], p[3]);
+    h8 r;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        r[2 * k] = p[k].x;
+        r[2 * k + 1] = p[k].y;
+    }
+    return r;
+}
+
+// Two codes held in the low bytes of separate registers -> f16 pair.
+DEV h2 codes2_to_h2(uint32_t c0, uint32_t c1) {
+    // bytes [c0, 0, c1, 0], then c + 128 under the exponent of 1024
+    return h2_minus_1152(__builtin_amdgcn_perm(c1, c0, 0x0c040c00u) ^ H2_1152);
+}
+
 template <int NB>
 struct ScaleVec;
 template <>
@@ -474,16 +509,6 @@ struct ScaleVec<4> {
     DEV uint16_t get(T v, int b) { return (uint16_t)((b < 2 ? v.x : v.y) >> (16 * (b & 1))); }
 };
 
-DEV h8 codes_to_h8(uint32_t lo, uint32_t hi) {
-    h8 r;
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        r[k] = (f16)(float)(int8_t)(lo >> (8 * k));
-        r[4 + k] = (f16)(float)(int8_t)(hi >> (8 * k));
-    }
-    return r;
-}
-
 template <int HD>
 __global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
     constexpr int KS = HD / 16;          // k-steps of S^T = K Q^T
@@ -492,6 +517,7 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
     typedef typename SV::T ST;
     __shared__ float cm[MW][32], cl[MW][32];
     __shared__ __attribute__((aligned(16))) float co[MW][GMAX][HD];
+    __shared__ __attribute__((aligned(16))) float sks[MW][2][32][NB];   // [wave][K, V][key][block]
 
     const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, ln = lane & 31;
@@ -501,10 +527,8 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
     if (c0 > pos) return;                              // uniform per block
     const int k0 = c0 + 32 * w;                        // this wavefront's first key
     const size_t cell0 = ((size_t)seq * a.kv.n_kv + g) * a.kv.n_ctx;
-    const int8_t *Kc = (const int8_t *)a.kv.k + cell0 * HD;
-    const int8_t *Vc = (const int8_t *)a.kv.v + cell0 * HD;
-    const ST *Ks = (const ST *)(a.kv.k_scale + cell0 * NB);
-    const ST *Vs = (const ST *)(a.kv.v_scale + cell0 * NB);
+    const uint8_t *Kc = (const uint8_t *)a.kv.k + cell0 * HD;
+    const uint8_t *Vc = (const uint8_t *)a.kv.v + cell0 * HD;
 
     // ---- every load at entry; rows past pos are replaced by row pos ----
     // K codes of key k0 + lane%32: block b, dims 32 b + 16 (lane/32) .. + 15
@@ -512,6 +536,8 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
     const int kr = min(k0 + ln, pos);
 #pragma unroll
     for (int b = 0; b < NB; b++) kc[b] = *(const uint4 *)(Kc + (size_t)kr * HD + 32 * b + 16 * hf);
+    // block scales of key k0 + lane%32: K from the low half-wave, V from the high
+    const ST sc = *((const ST *)((hf ? a.kv.v_scale : a.kv.k_scale) + cell0 * NB) + kr);
     // q / sqrt(hd) (value + remainder) of head lane%32 in the same dim order
     h8 qa[KS], qb[KS];
     const size_t qo = ((size_t)t * a.H + g * G + min(ln, G - 1)) * HD + 16 * hf;
@@ -521,17 +547,9 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
         qa[ks] = *(const h8 *)((const f16 *)a.qh + qo + off);
         qb[ks] = *(const h8 *)((const f16 *)a.ql + qo + off);
     }
-    // block scales of the keys of accumulator register r: k0 + 8 (r/4) + 4 (lane/32) + r%4
-    ST ksv[16], vsv[16];
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-        const int key = min(k0 + 8 * (r >> 2) + 4 * hf + (r & 3), pos);
-        ksv[r] = Ks[key];
-        vsv[r] = Vs[key];
-    }
     // V codes, B operand of O = P V for k-step s: element e of lane l is key
     // 16 s + 8 (e/4) + 4 (l/32) + e%4 at dim 32 dt + l%32
-    int8_t vc[NB][2][8];
+    uint32_t vc[NB][2][8];
 #pragma unroll
     for (int s = 0; s < 2; s++)
 #pragma unroll
@@ -540,14 +558,18 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
 #pragma unroll
             for (int dt = 0; dt < NB; dt++) vc[dt][s][e] = Vc[(size_t)key * HD + 32 * dt + ln];
         }
+#pragma unroll
+    for (int b = 0; b < NB; b++) sks[w][hf][ln][b] = f16_bits_to_f32(SV::get(sc, b));
+    __syncthreads();
 
     // ---- S^T = K Q^T, one exact tile per block, scaled per key ----
+    // accumulator register r holds key 8 (r/4) + 4 (lane/32) + r%4 of the wavefront
     f16x sacc;
 #pragma unroll
     for (int r = 0; r < 16; r++) sacc[r] = 0.f;
 #pragma unroll
     for (int b = 0; b < NB; b++) {
-        const h8 klo = codes_to_h8(kc[b].x, kc[b].y), khi = codes_to_h8(kc[b].z, kc[b].w);
+        const h8 klo = codes8_to_h8(kc[b].x, kc[b].y), khi = codes8_to_h8(kc[b].z, kc[b].w);
         f16x tb;
 #pragma unroll
         for (int r = 0; r < 16; r++) tb[r] = 0.f;
@@ -556,7 +578,7 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
         tb = __builtin_amdgcn_mfma_f32_32x32x16_f16(khi, qa[2 * b + 1], tb, 0, 0, 0);
         tb = __builtin_amdgcn_mfma_f32_32x32x16_f16(khi, qb[2 * b + 1], tb, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; r++) sacc[r] += f16_bits_to_f32(SV::get(ksv[r], b)) * tb[r];
+        for (int r = 0; r < 16; r++) sacc[r] += sks[w][0][8 * (r >> 2) + 4 * hf + (r & 3)][b] * tb[r];
     }
 
     // ---- causal mask and this wavefront's softmax statistics per head ----
@@ -583,7 +605,7 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
         h8 ph[2], pl[2];
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-            const float pv = p[r] * f16_bits_to_f32(SV::get(vsv[r], dt));
+            const float pv = p[r] * sks[w][1][8 * (r >> 2) + 4 * hf + (r & 3)][dt];
             const f16 p16 = (f16)pv;
             ph[r >> 3][r & 7] = p16;
             pl[r >> 3][r & 7] = (f16)(pv - (float)p16);
@@ -594,7 +616,11 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
         for (int s = 0; s < 2; s++) {
             h8 vb;
 #pragma unroll
-            for (int e = 0; e < 8; e++) vb[e] = (f16)(float)vc[dt][s][e];
+            for (int k = 0; k < 4; k++) {
+                const h2 v2 = codes2_to_h2(vc[dt][s][2 * k], vc[dt][s][2 * k + 1]);
+                vb[2 * k] = v2.x;
+                vb[2 * k + 1] = v2.y;
+            }
             o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ph[s], vb, o[dt], 0, 0, 0);
             o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pl[s], vb, o[dt], 0, 0, 0);
         }
