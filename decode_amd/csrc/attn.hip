@@ -38,6 +38,7 @@
 // The block's two wavefronts are then combined into one chunk partial.
 #include "common.h"
 #include "kernels.h"
+#include "q8.h"
 
 namespace {
 
@@ -526,6 +527,10 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
     const int c0 = c * CHM;
     if (c0 > pos) return;                              // uniform per block
     const int k0 = c0 + 32 * w;                        // this wavefront's first key
+    if (a.code_new_rows && pos < c0 + CHM) {           // uniform: the chunk holding the new row
+        if (tid < 2 * NB) kv_code_block(a.kv, t, tid / NB, g * NB + tid % NB, seq, pos);
+        __syncthreads();
+    }
     const size_t cell0 = ((size_t)seq * a.kv.n_kv + g) * a.kv.n_ctx;
     const uint8_t *Kc = (const uint8_t *)a.kv.k + cell0 * HD;
     const uint8_t *Vc = (const uint8_t *)a.kv.v + cell0 * HD;
@@ -672,6 +677,7 @@ bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
 
 bool launch_attention(const AttnArgs &a, int T, hipStream_t s) {
     if (T <= 0 || a.max_chunks > 1024 || a.chunk != chunk_for(a.kv.kvtype, a.kv.hd)) return false;
+    if (a.code_new_rows && !attention_codes_rows(a.kv.kvtype, a.kv.hd)) return false;
     switch (a.kv.hd) {
     case 64: return launch_hd<64>(a, T, s);
     case 128: return launch_hd<128>(a, T, s);
@@ -681,3 +687,5 @@ bool launch_attention(const AttnArgs &a, int T, hipStream_t s) {
 }
 
 int attention_chunk(int kvtype, int hd) { return chunk_for(kvtype, hd); }
+
+bool attention_codes_rows(int kvtype, int hd) { return kvtype == T_Q8_0 && mfma_path(kvtype, hd); }

@@ -909,7 +909,12 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
             launch_rmsnorm(c->x, d, L.attn_norm, d, h.rms_eps, nullptr, T, c->xn, c->xn_lo, d, s);
             return launch_gemm(L.wqkv, c->xn, c->xn_lo, d, eq, T, c->gws, c->gws_bytes, s);
         });
-        if (h.kvtype == DEC_Q8_0)
+        // Q8_0 cache: a decode call's tokens are of distinct sequences, so the
+        // attention block holding each new row codes it; a prefill ubatch's
+        // later tokens read earlier ones' rows, so they are coded first
+        const bool code_in_attn = h.kvtype == DEC_Q8_0 && !c->prefill_mode &&
+                                  attention_codes_rows(h.kvtype, h.head_dim);
+        if (h.kvtype == DEC_Q8_0 && !code_in_attn)
             ok = ok && stage(c, -1, l, [&] {
                 launch_kv_quant(c->kv[l], ti, T, s);
                 return true;
@@ -927,6 +932,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         at.chunk = c->chunk;
         at.o = c->o;
         at.o_lo = c->o_lo;
+        at.code_new_rows = code_in_attn ? 1 : 0;
         ok = ok && stage(c, DEC_K_ATTN, l, [&] {
             if (c->prefill_mode && c->flash_prefill && T > 1) {
                 FlashArgs fa;

@@ -164,10 +164,16 @@ struct AttnArgs {
     float *part = nullptr;        // [T][H][max_chunks][hd] partial outputs
     float *ml = nullptr;          // [T][H][max_chunks][2] running max / sum
     int max_chunks = 0, chunk = 0;
+    // Q8_0 cache, every token of its own sequence (decode): the block whose
+    // chunk holds a token's position first codes the token's staged K / V
+    // rows of its KV head into the cache (no launch_kv_quant needed)
+    int code_new_rows = 0;
     uint16_t *o = nullptr;        // [T][H*hd] f16 output
     uint16_t *o_lo = nullptr;     // [T][H*hd] f16 rounding remainder of the output
 };
 bool launch_attention(const AttnArgs &a, int T, hipStream_t s);
+// Whether launch_attention can take code_new_rows for this cache.
+bool attention_codes_rows(int kvtype, int hd);
 
 // Causal attention of a prefill ubatch: T tokens of sequence tok.seq[0] at
 // positions tok.pos[0] + t, f16 cache, MFMA flash attention.  Returns false

@@ -1,5 +1,6 @@
 // misc.hip -- small kernels of the decoder step and of weight loading (gfx950).
 #include "common.h"
+#include "q8.h"
 #include "kernels.h"
 
 namespace {
@@ -17,31 +18,6 @@ DEV int dst_row(int mode, int r, int row_off) {
 // fp32 arithmetic with no contraction, so codes match any IEEE fp32
 // implementation of the same steps bit for bit; the scale is stored as f16
 // (round to nearest even).
-// Q8_0 coding of 32 values: the scale's f16 bits and the 32 codes packed
-// little-endian into 8 dwords.
-DEV uint16_t q8_block(const float *v, uint32_t *packed) {
-#pragma clang fp contract(off)
-    float amax = 0.f;
-#pragma unroll
-    for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
-    float d = amax / 127.0f;
-    // keep the f16 rounding a separate step: a fused multiply-add form of
-    // the conversion would turn a -0 scale into +0
-    asm volatile("" : "+v"(d));
-    const float id = d != 0.f ? 1.0f / d : 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int q = (int)roundf(v[4 * i + e] * id);
-            w |= ((uint32_t)(q & 0xff)) << (8 * e);
-        }
-        packed[i] = w;
-    }
-    return f32_to_f16_bits(d);
-}
-
 __global__ __launch_bounds__(256) void k_quantize(const float *src, int rows, int K, QMat m,
                                                   int mode, int row_off) {
 #pragma clang fp contract(off)
@@ -111,25 +87,11 @@ __global__ __launch_bounds__(256) void k_copy_f32(const float *src, int rows, in
 // One thread per 32-element block of the T new K and V rows (the same coding
 // as the Q8_0 weights); block b of row (t, which) covers kv head b / (hd/32).
 __global__ __launch_bounds__(256) void k_kv_quant(KVLayer kv, TokInfo tok, int T) {
-    const int hd = kv.hd, bph = hd >> 5, kd = kv.n_kv * hd, nbr = kd >> 5;
+    const int nbr = kv.n_kv * kv.hd >> 5;
     const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (long long)T * 2 * nbr) return;
     const int b = (int)(idx % nbr), which = (int)((idx / nbr) & 1), t = (int)(idx / (2 * nbr));
-    const float *x = kv.stage + ((size_t)t * 2 + which) * kd + (size_t)b * 32;
-    float v[32];
-#pragma unroll
-    for (int j = 0; j < 32; j += 4) {
-        const float4 f = *(const float4 *)(x + j);
-        v[j] = f.x; v[j + 1] = f.y; v[j + 2] = f.z; v[j + 3] = f.w;
-    }
-    uint32_t packed[8];
-    const uint16_t dbits = q8_block(v, packed);
-    const int g = b / bph, bl = b % bph;
-    const size_t cell = ((size_t)tok.seq[t] * kv.n_kv + g) * kv.n_ctx + tok.pos[t];
-    (which ? kv.v_scale : kv.k_scale)[cell * bph + bl] = dbits;
-    uint4 *dst = (uint4 *)((int8_t *)(which ? kv.v : kv.k) + cell * hd + bl * 32);
-    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    kv_code_block(kv, t, which, b, tok.seq[t], tok.pos[t]);
 }
 
 // ---- file blocks -> stored layout ------------------------------------------
