@@ -9,7 +9,8 @@
 // g*G + hz*Gb + w%Gb and a tile of 32 tokens (w/Gb picks the tile when a
 // group has fewer than 4 heads).  Per 64-key tile, K (row-major) and V
 // (transposed, keys permuted as below) are staged in LDS once for all four
-// wavefronts, then each wavefront runs
+// wavefronts (the next tile's loads are in flight meanwhile), then each
+// wavefront runs
 //   S^T[key][q] = K Q^T     v_mfma_f32_32x32x16_f16, 2 key tiles x hd/16 steps
 //   online softmax per query column (a lane holds 16 keys of one query; the
 //   other 16 are in lane l^32), base-2 with log2(e)/sqrt(hd) folded into Q
@@ -86,28 +87,52 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
     constexpr int CPT = CHUNKS / 256;
 
     const int ntiles = (n_keys + BKEY - 1) / BKEY;
-    for (int kt = 0; kt < ntiles; kt++) {
-        const int k0 = kt * BKEY;
-        // ---- stage K and V^T of keys k0 .. k0+63 (rows past n_keys read as 0) ----
-        uint4 kr[CPT], vr[CPT];
+    // K and V of keys k0 .. k0+63 into registers (rows past n_keys read as 0).
+    // K: chunk ch = 8 dims d8 of key ch / (hd/8).  V: pair chunk pc = 8 dims
+    // d8 = pc / 32 of the keys 2 (pc%32) and 2 (pc%32) + 1, whose V^T columns
+    // are adjacent (vt_col keeps bit 0 of the key), so each of the 8 dims is
+    // one 4-byte LDS store, and a wavefront's 64 stores hit 64 different banks.
+    constexpr int PPT = CPT / 2;                            // V pair chunks per thread
+    uint4 kr[CPT], vr[PPT][2];
+    auto load_tile = [&](int k0) {
 #pragma unroll
         for (int c = 0; c < CPT; c++) {
             const int ch = tid + c * 256, key = ch / (HD / 8), d8 = ch % (HD / 8);
             const bool ok = k0 + key < n_keys;
             kr[c] = ok ? *(const uint4 *)(Kg + (size_t)(k0 + key) * HD + d8 * 8) : make_uint4(0, 0, 0, 0);
-            vr[c] = ok ? *(const uint4 *)(Vg + (size_t)(k0 + key) * HD + d8 * 8) : make_uint4(0, 0, 0, 0);
         }
+#pragma unroll
+        for (int c = 0; c < PPT; c++) {
+            const int pc = tid + c * 256, key = 2 * (pc & 31), d8 = pc >> 5;
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const bool ok = k0 + key + j < n_keys;
+                vr[c][j] = ok ? *(const uint4 *)(Vg + (size_t)(k0 + key + j) * HD + d8 * 8) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    load_tile(0);
+    for (int kt = 0; kt < ntiles; kt++) {
+        const int k0 = kt * BKEY;
+        // ---- stage K and V^T of this tile; the next tile's loads then run
+        // during this tile's arithmetic ----
         __syncthreads();                                    // previous tile fully consumed
 #pragma unroll
         for (int c = 0; c < CPT; c++) {
             const int ch = tid + c * 256, key = ch / (HD / 8), d8 = ch % (HD / 8);
             *(uint4 *)&Ks[key][d8 * 8] = kr[c];
-            const f16 *v = (const f16 *)&vr[c];
-            const int col = vt_col(key);
+        }
 #pragma unroll
-            for (int e = 0; e < 8; e++) Vt[d8 * 8 + e][col] = v[e];
+        for (int c = 0; c < PPT; c++) {
+            const int pc = tid + c * 256, key = 2 * (pc & 31), d8 = pc >> 5;
+            const uint16_t *v0 = (const uint16_t *)&vr[c][0], *v1 = (const uint16_t *)&vr[c][1];
+            const int col = vt_col(key);                    // even; key + 1 sits at col + 1
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                *(uint32_t *)&Vt[d8 * 8 + e][col] = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
         }
         __syncthreads();
+        if (kt + 1 < ntiles) load_tile(k0 + BKEY);
 
         // ---- S^T = K Q^T for two 32-key halves ----
         f16x s[2];
