@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libdecode.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "decode.h")
 
 F32, F16, Q8_0, Q4_0 = 0, 1, 2, 3
-K_QKV, K_ATTN, K_WO, K_FFN_GU, K_FFN_DOWN, K_OUTPUT = 0, 1, 2, 3, 4, 5
+K_QKV, K_ATTN, K_WO, K_FFN_GU, K_FFN_DOWN, K_OUTPUT, K_STEP = 0, 1, 2, 3, 4, 5, 6
 TENSOR_IDS = {"tok_embd": 0, "output": 1, "wq": 2, "wk": 3, "wv": 4, "wo": 5,
               "ffn_gate": 6, "ffn_up": 7, "ffn_down": 8}
 
@@ -108,6 +108,7 @@ def lib() -> C.CDLL:
         "dec_set_probe": (i32, [vp, i32, i32]),
         "dec_get_probe": (i32, [vp, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
         "dec_set_use_graphs": (i32, [vp, i32]),
+        "dec_set_step_kernel": (i32, [vp, i32]),
         "dec_version": (C.c_char_p, []),
         "dec_sampler_new": (vp, [vp]),
         "dec_sampler_accept": (i32, [vp, i32]),
@@ -341,6 +342,12 @@ class Context:
 
     def use_graphs(self, on: bool) -> bool:
         return bool(self.L.dec_set_use_graphs(self.ptr, int(on)))
+
+    def step_kernel(self, on: int = -1) -> int:
+        """One-token decode steps as one persistent kernel: 1 on, 0 off, -1
+        query.  Returns the setting before the call, or -1 when the context
+        cannot use it."""
+        return int(self.L.dec_set_step_kernel(self.ptr, int(on)))
 
     def close(self):
         if getattr(self, "ptr", None):

@@ -12,6 +12,17 @@ typedef float f16x __attribute__((ext_vector_type(16)));
 
 #define DEV static __device__ __forceinline__
 
+// Global address space: pointers read from memory (not kernel arguments) are
+// generic to the compiler, and generic (flat) accesses need a 64-bit address
+// register each; casting them makes every access a global one with a scalar base.
+#ifdef __HIP_DEVICE_COMPILE__
+#define GLB __attribute__((address_space(1)))
+#else
+#define GLB
+#endif
+template <class T>
+DEV GLB T *gl(T *p) { return (GLB T *)p; }
+
 // Element type codes (same values as dec_type in include/decode.h).
 enum { T_F32 = 0, T_F16 = 1, T_Q8_0 = 2, T_Q4_0 = 3 };
 

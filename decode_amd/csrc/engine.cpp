@@ -616,6 +616,13 @@ struct dec_ctx {
     // launches run_tokens emits; seg_cur tracks where the sequence is.
     int seg_req = 0, seg_cur = 1;
     std::map<int, hipGraphExec_t> graphs_post;
+    // one-token decode steps as one persistent kernel (dec_set_step_kernel)
+    bool step_ok = false, step_on = false;
+    int step_grid = 0;
+    StepArgs *step_args = nullptr;     // argument block (device memory)
+    uint32_t *step_sync = nullptr;     // its barrier memory
+    uint32_t step_n0 = 0;              // grid barriers of earlier launches
+    bool step_ran = false;             // the last decode call ran the step kernel
 };
 
 thread_local LaunchProbe g_launch_probe;
@@ -671,6 +678,99 @@ static void probe_end(dec_ctx *c, int role, int layer) {
         c->pr_used++;
     }
     c->seg_cur = SEG_POST;
+}
+
+// Prepares the one-token step kernel when the shapes allow it: the layer
+// table and argument block in device memory, the barrier memory zeroed.
+static void step_setup(dec_ctx *c) {
+    const dec_model *m = c->m;
+    const dec_hparams &h = m->hp;
+    int dev = 0, ncu = 0, coop = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return;
+    }
+    const int grid = ncu;
+    StepArgs a;
+    a.n_layer = h.n_layer;
+    a.tok = m->tok;
+    a.out = m->out;
+    a.out_norm = m->out_norm;
+    a.d = h.n_embd;
+    a.qd = m->qd;
+    a.kd = m->kd;
+    a.Fp = m->Fp;
+    a.H = h.n_head;
+    a.Hkv = h.n_head_kv;
+    a.hd = h.head_dim;
+    a.V = h.n_vocab;
+    a.n_ctx = c->n_ctx;
+    a.eps = h.rms_eps;
+    a.qscale = 1.0f / sqrtf((float)h.head_dim);
+    a.bpg = a.Hkv > 0 ? std::min(grid / a.Hkv, STEP_BPG_MAX) : 0;
+    a.S_qkv = step_slices(a.qd + 2 * a.kd, a.d, grid);
+    a.S_o = step_slices(a.d, a.qd, grid);
+    a.S_gu = step_slices(2 * a.Fp, a.d, grid);
+    a.S_down = step_slices(a.d, a.Fp, grid);
+    a.S_out = step_slices(a.V, a.d, grid);
+    const char *why = nullptr;
+    if (!coop) why = "no cooperative launch";
+    else if (!step_supported(a, h.wtype, h.kvtype, grid, &why)) {
+    } else if (step_blocks_per_cu(h.wtype, h.head_dim) < 1) why = "kernel does not fit a compute unit";
+    if (why) {
+        LOGI("one-token step kernel not used: %s", why);
+        return;
+    }
+    std::vector<StepLayer> layers(h.n_layer);
+    for (int l = 0; l < h.n_layer; l++) {
+        const Layer &L = m->layers[l];
+        StepLayer &S = layers[l];
+        S.wqkv = L.wqkv;
+        S.wo = L.wo;
+        S.wgu = L.wgu;
+        S.wdown = L.wdown;
+        S.attn_norm = L.attn_norm;
+        S.ffn_norm = L.ffn_norm;
+        S.k = (uint16_t *)c->kv[l].k;
+        S.v = (uint16_t *)c->kv[l].v;
+    }
+    StepLayer *dl = (StepLayer *)c->mem.get(layers.size() * sizeof(StepLayer));
+    c->step_args = (StepArgs *)c->mem.get(sizeof(StepArgs));
+    c->step_sync = (uint32_t *)c->mem.get(STEP_SYNC_WORDS * 4);
+    a.apart = (float *)c->mem.get((size_t)a.H * a.bpg * a.hd * 4);
+    a.aml = (float *)c->mem.get((size_t)a.H * a.bpg * 2 * 4);
+    a.bmax = (float *)c->mem.get((size_t)grid * 4);
+    a.bidx = (int32_t *)c->mem.get((size_t)grid * 4);
+    if (!dl || !c->step_args || !c->step_sync || !a.apart || !a.aml || !a.bmax || !a.bidx) return;
+    a.layers = dl;
+    a.step = c->dev_step;
+    a.rope_cs = c->rope_cs;
+    a.x = c->x;
+    a.ss = c->ssp;
+    a.qh = c->qh;
+    a.ql = c->ql;
+    a.o = c->o;
+    a.o_lo = c->o_lo;
+    a.h = c->h;
+    a.h_lo = c->h_lo;
+    a.logits = c->logits;
+    a.amax = c->amax;
+    a.sync = c->step_sync;
+    if (hipMemcpy(dl, layers.data(), layers.size() * sizeof(StepLayer), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(c->step_args, &a, sizeof(StepArgs), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemset(c->step_sync, 0, STEP_SYNC_WORDS * 4) != hipSuccess) {
+        (void)hipGetLastError();
+        return;
+    }
+    c->step_grid = grid;
+    c->step_n0 = 0;
+    c->step_ok = true;
+    // off unless asked for: on one MI355X the per-layer graph is faster (the
+    // step's 5 grid barriers per layer cost more than the kernel boundaries)
+    const char *e = getenv("DECODE_STEP_KERNEL");
+    c->step_on = e && strcmp(e, "1") == 0;
 }
 
 extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
@@ -784,6 +884,7 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
         if (ok) HIP_OK(hipEventCreate(&c->pr_e1[i]), ok = false);
     }
 
+    if (ok) step_setup(c);
     if (ok) {
         launch_rope_table(c->rope_cs, (int)n_ctx, hd, h.rope_base, c->s);
         HIP_OK(hipGetLastError(), ok = false);
@@ -1116,6 +1217,29 @@ extern "C" int32_t dec_decode(dec_ctx *c, const int32_t *tokens, const int32_t *
         c->host_step[2 * n + i] = seq_ids[i];
     }
     if (!stage_step(c, n)) return -3;
+    c->step_ran = false;
+    if (n == 1 && c->step_on && c->use_graphs && (c->pr_role < 0 || c->pr_role == DEC_K_STEP)) {
+        // the whole step as one persistent kernel
+        const bool probe = c->pr_role == DEC_K_STEP;
+        if (probe) {
+            if (c->pr_used == dec_ctx::NPROBE) probe_collect(c);
+            HIP_OK(hipEventRecord(c->pr_e0[c->pr_used], c->s), return -3);
+        }
+        if (!launch_step(c->step_args, c->m->hp.wtype, c->m->hp.head_dim, c->step_n0, c->step_grid, c->s)) {
+            LOGE("dec_decode: step kernel launch failed (%s)", hipGetErrorString(hipGetLastError()));
+            return -3;
+        }
+        if (probe) {
+            HIP_OK(hipEventRecord(c->pr_e1[c->pr_used], c->s), return -3);
+            c->pr_used++;
+        }
+        c->step_n0 += step_barriers(c->m->hp.n_layer);
+        c->step_ran = true;
+        c->pos_max[seq_ids[0]]++;
+        c->st.n_decode_calls++;
+        reset_outputs(c, 1);
+        return 0;
+    }
     // The first step of a shape runs kernel by kernel: every kernel it uses is
     // then loaded, so the capture of the second step only records launches
     // (graph reuse applies to repeated shapes, as in the article's step 13b).
@@ -1123,7 +1247,7 @@ extern "C" int32_t dec_decode(dec_ctx *c, const int32_t *tokens, const int32_t *
         c->seg_req = SEG_ALL;
         if (!run_tokens(c, 0, n, 0, n, 0)) return -3;
     } else {
-        const bool split = c->pr_role >= 0;
+        const bool split = c->pr_role >= 0 && c->pr_role != DEC_K_STEP;
         auto it = c->graphs.find(n);
         if (it == c->graphs.end()) {
             hipGraphExec_t pre = capture_step(c, n, split ? SEG_PRE : SEG_ALL);
@@ -1185,6 +1309,13 @@ static bool fetch_amax(dec_ctx *c) {
            return false);
     HIP_OK(hipStreamSynchronize(c->s), return false);
     c->amax_fetched = true;
+    if (c->step_ran && c->host_amax[0] < 0) {
+        // a bounded wait of the step kernel gave up: clean barrier state for the next step
+        LOGE("decode step kernel: a grid barrier timed out; the step's results are invalid");
+        c->step_n0 = 0;
+        HIP_OK(hipMemsetAsync(c->step_sync, 0, STEP_SYNC_WORDS * 4, c->s), return true);
+        HIP_OK(hipStreamSynchronize(c->s), return true);
+    }
     return true;
 }
 
@@ -1330,14 +1461,14 @@ extern "C" void dec_get_stats(const dec_ctx *c, dec_stats *out) {
 }
 
 extern "C" int32_t dec_set_probe(dec_ctx *c, int32_t role, int32_t layer) {
-    if (!c || role > DEC_K_OUTPUT) return -1;
-    if (role >= 0 && role != DEC_K_OUTPUT && (layer < 0 || layer >= c->m->hp.n_layer)) return -1;
+    if (!c || role > DEC_K_STEP) return -1;
+    if (role >= 0 && role < DEC_K_OUTPUT && (layer < 0 || layer >= c->m->hp.n_layer)) return -1;
     (void)hipStreamSynchronize(c->s);
     c->pr_used = 0;
     c->pr_ms = 0.0;
     c->pr_n = 0;
     const int r = role < 0 ? -1 : role;
-    if (r != c->pr_role || (r >= 0 && r != DEC_K_OUTPUT && layer != c->pr_layer)) {
+    if (r != c->pr_role || (r >= 0 && r < DEC_K_OUTPUT && layer != c->pr_layer)) {
         c->pr_role = r;
         c->pr_layer = layer;
         drop_graphs(c);   // captured graphs hold (or lack) the probe's event nodes
@@ -1357,6 +1488,13 @@ extern "C" int32_t dec_set_use_graphs(dec_ctx *c, int32_t on) {
     if (!c) return -1;
     const int32_t prev = c->use_graphs ? 1 : 0;
     c->use_graphs = on != 0;
+    return prev;
+}
+
+extern "C" int32_t dec_set_step_kernel(dec_ctx *c, int32_t on) {
+    if (!c || !c->step_ok) return -1;
+    const int32_t prev = c->step_on ? 1 : 0;
+    if (on >= 0) c->step_on = on != 0;
     return prev;
 }
 

@@ -125,6 +125,9 @@ void launch_kv_quant(const KVLayer &kv, TokInfo tok, int T, hipStream_t s);
 
 // Number of compute units the mat-vec grid is sized for (default 256).
 void matvec_set_num_cu(int n);
+// K slices per row pair the mat-vec uses for an N x K matrix on a grid of
+// num_cu blocks (num_cu <= 0: the grid matvec_set_num_cu set).
+int matvec_slices(int N, int K, int num_cu);
 // y = W x for T tokens (decode).  Q8_0 / Q4_0 only.  The input row is
 // RMS-normalized (in.norm_g) for every epilogue but EPI_RESID, which takes
 // the f16 row as is.
@@ -206,3 +209,57 @@ struct SampleArgs {
 };
 bool launch_sample(const float *logits, const SampleArgs &a, hipStream_t s);
 
+
+// ---- one decode step of one token as a single persistent kernel ----------
+// One layer's weights and f16 cache as the step kernel reads them (a device
+// array of n_layer entries, built once per context).
+struct StepLayer {
+    QMat wqkv, wo, wgu, wdown;
+    const float *attn_norm = nullptr, *ffn_norm = nullptr;
+    uint16_t *k = nullptr, *v = nullptr;   // [seq][n_kv][n_ctx][hd] f16
+};
+
+// Barrier and merge-counter memory of the step kernel (uint32 words, zeroed
+// once; the kernel keeps it consistent from launch to launch).
+constexpr int STEP_SYNC_WORDS = 64 * 96;
+// Word index of the failure flag (a bounded wait timed out) in that memory.
+constexpr int STEP_SYNC_FAIL = 64 * 17;
+// Most blocks that share one KV head's attention (their partials meet in one merge).
+constexpr int STEP_BPG_MAX = 64;
+
+struct StepArgs {
+    const StepLayer *layers = nullptr;
+    int n_layer = 0;
+    QMat tok, out;
+    const float *out_norm = nullptr;
+    int d = 0, qd = 0, kd = 0, Fp = 0, H = 0, Hkv = 0, hd = 0, V = 0, n_ctx = 0;
+    float eps = 0.f, qscale = 1.f;
+    const int32_t *step = nullptr;    // the token: id, position, sequence
+    const float *rope_cs = nullptr;   // [n_ctx][hd/2][2]
+    float *x = nullptr;               // [d] residual row
+    float *ss = nullptr;              // [SS_SLOTS] partial sums of squares of x
+    uint16_t *qh = nullptr, *ql = nullptr;   // [qd] q / sqrt(hd), f16 value + remainder
+    uint16_t *o = nullptr, *o_lo = nullptr;  // [qd] attention output
+    uint16_t *h = nullptr, *h_lo = nullptr;  // [Fp] SwiGLU output
+    float *apart = nullptr;           // [Hkv][bpg][G][hd] attention partials of the blocks
+    float *aml = nullptr;             // [Hkv][bpg][G][2] their running max / sum
+    int bpg = 0;                      // blocks per KV head in the attention phase
+    float *logits = nullptr;          // [V]
+    int32_t *amax = nullptr;          // greedy token, -1 when a wait timed out
+    float *bmax = nullptr;            // [grid] per-block argmax candidates
+    int32_t *bidx = nullptr;
+    uint32_t *sync = nullptr;         // STEP_SYNC_WORDS
+    int S_qkv = 1, S_o = 1, S_gu = 1, S_down = 1, S_out = 1;   // K slices per phase
+};
+// Grid barriers one launch performs.
+inline uint32_t step_barriers(int n_layer) { return 2u + 5u * (uint32_t)n_layer; }
+// Whether the step kernel covers this shape; `why` names the first reason it does not.
+bool step_supported(const StepArgs &a, int wtype, int kvtype, int grid, const char **why);
+// K slices per row pair the step kernel uses for an N x K matrix on `grid` blocks.
+int step_slices(int N, int K, int grid);
+// Blocks of the step kernel one compute unit holds (0: not launchable).
+int step_blocks_per_cu(int wtype, int hd);
+// Launches the step (cooperative launch of `grid` blocks of 512 threads) with
+// the argument block at dev_args (device memory, as checked by step_supported)
+// after n0 grid barriers of earlier launches on the same sync memory.
+bool launch_step(const StepArgs *dev_args, int wtype, int hd, uint32_t n0, int grid, hipStream_t s);

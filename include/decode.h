@@ -284,15 +284,18 @@ void dec_get_stats(const dec_ctx *c, dec_stats *out);
 /* Kernel roles of one layer (and the final output projection) for the
  * timing probe. */
 enum { DEC_K_QKV = 0, DEC_K_ATTN = 1, DEC_K_WO = 2, DEC_K_FFN_GU = 3, DEC_K_FFN_DOWN = 4,
-       DEC_K_OUTPUT = 5 };
+       DEC_K_OUTPUT = 5, DEC_K_STEP = 6 };
 
 /* Timing probe (the article's per-node evaluation callback, step 13b, in
  * measuring form): the launch(es) of kernel `role` in layer `layer` (layer
- * ignored for DEC_K_OUTPUT) go through hipExtLaunchKernel with a pair of HIP
+ * ignored for DEC_K_OUTPUT and DEC_K_STEP) go through hipExtLaunchKernel with a pair of HIP
  * events, which take the start time of the first kernel and the end time of
  * the last one.  Applies to prefill ubatches and to decode steps; a probed
  * decode step replays its graph in two parts around the directly launched
- * probed kernel.  role < 0 disables.  Setting the probe resets the totals;
+ * probed kernel.  DEC_K_STEP times the whole one-token decode step kernel
+ * (see dec_set_step_kernel) between two events recorded around its launch;
+ * any other role makes one-token decode steps take the per-layer kernels.
+ * role < 0 disables.  Setting the probe resets the totals;
  * choosing a different role or layer also drops captured decode graphs.
  * Returns 0, or -1 on bad arguments. */
 int32_t dec_set_probe(dec_ctx *c, int32_t role, int32_t layer);
@@ -305,6 +308,26 @@ int32_t dec_get_probe(dec_ctx *c, double *total_ms, int64_t *count);
 /* Decode steps are captured as HIP graphs and replayed (on, the default) or
  * launched kernel by kernel (off).  Returns the previous setting. */
 int32_t dec_set_use_graphs(dec_ctx *c, int32_t on);
+
+/* One-token decode steps (dec_decode with n = 1) as one persistent kernel:
+ * every layer of the step (RMSNorm, QKV, RoPE, K/V append, attention,
+ * output projection, SwiGLU FFN; then the output projection and the greedy
+ * token), one block per compute unit, with grid barriers between the
+ * layers' stages instead of kernel boundaries (graph reuse, step 13b, taken
+ * to its limit).  Available where the context supports it: Q8_0 / Q4_0
+ * weights, an f16 cache, head_dim 64 or 128, at most 8 query heads per KV
+ * head, d_model and n_head * head_dim at most 4096, n_ff at most 16384, and
+ * a cooperative launch of one block per compute unit.  Off by default (on
+ * one MI355X the per-layer graph is faster); the environment variable
+ * DECODE_STEP_KERNEL=1 turns the default on.  It is used only while
+ * graphs are on and no probe role other than DEC_K_STEP is set.  Results
+ * agree with the per-layer kernels within rounding (the attention merges
+ * its partial sums in another order).  If a wait inside the kernel times out
+ * (blocks not co-resident), the step's greedy token reads -1, its logits are
+ * undefined, and the next step starts from clean barrier state.
+ * on: 1 use, 0 do not use, -1 query.  Returns the setting before the call
+ * (0 or 1), or -1 when the context cannot use the kernel (nothing changes). */
+int32_t dec_set_step_kernel(dec_ctx *c, int32_t on);
 
 void dec_ctx_free(dec_ctx *c);
 
