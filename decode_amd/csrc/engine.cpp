@@ -599,6 +599,7 @@ struct dec_ctx {
     std::map<int, int> seen;   // decode steps run per token count (capture from the second on)
     bool use_graphs = true;
     bool prefill_mode = false; // run_tokens is running one sequence's consecutive positions
+    int prefill_p0 = 0;        // ... starting at this position
     bool flash_prefill = true; // DECODE_PREFILL_ATTN=splitk selects the split-K kernel instead
     bool registered = false;   // counted in m->n_ctx_refs
     dec_stats st{};
@@ -1044,6 +1045,10 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 fa.T = T;
                 fa.o = c->o;
                 fa.o_lo = c->o_lo;
+                fa.part = c->part;
+                fa.ml = c->ml;
+                fa.max_chunks = c->max_chunks;
+                fa.tok_pos0_max = c->prefill_p0;
                 if (launch_flash_prefill(fa, s)) return true;
             }
             return launch_attention(at, T, s);
@@ -1167,6 +1172,7 @@ extern "C" int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int
             n_rows = 1;
         }
         c->prefill_mode = true;
+        c->prefill_p0 = p0 + u;
         const bool ok = run_tokens(c, u, T, row0, n_rows, output_all ? u : 0);
         c->prefill_mode = false;
         if (!ok) return -3;

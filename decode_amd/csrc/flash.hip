@@ -7,7 +7,12 @@
 //
 // Block = 4 wavefronts sharing one KV head g.  Wavefront w takes query head
 // g*G + hz*Gb + w%Gb and a tile of 32 tokens (w/Gb picks the tile when a
-// group has fewer than 4 heads).  Per 64-key tile, K (row-major) and V
+// group has fewer than 4 heads).  The keys a token tile reads are cut into
+// NS ranges of `chunk` keys, one block each, so that the grid fills the chip
+// (a ubatch has only T/32 token tiles per head); a block whose tile needs
+// one range writes o itself, otherwise it leaves its unnormalized output and
+// (max, sum) per query, and k_flash_merge combines the ranges in order.
+// Per 64-key tile, K (row-major) and V
 // (transposed, keys permuted as below) are staged in LDS once for all four
 // wavefronts (the next tile's loads are in flight meanwhile), then each
 // wavefront runs
@@ -21,6 +26,8 @@
 // 16s + 8h + e of its 16-key group, and each lane reads 16 contiguous bytes.
 #include "common.h"
 #include "kernels.h"
+
+int g_flash_blocks = 512;       // blocks the key split aims for (2 per compute unit)
 
 namespace {
 
@@ -44,7 +51,8 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
     const int G = a.H / a.kv.n_kv, Gb = G < 4 ? G : 4, Tb = 4 / Gb;
     const int g = blockIdx.y;
     const int head = g * G + blockIdx.z * Gb + (w % Gb);
-    const int tok0 = blockIdx.x * 32 * Tb;                  // first token of the block
+    const int split = blockIdx.x % a.ns;
+    const int tok0 = (blockIdx.x / a.ns) * 32 * Tb;         // first token of the block
     const int tw = tok0 + (w / Gb) * 32;                    // first token of this wavefront
     const int q_t = tw + (lane & 31);                       // this lane's query column
     const int p0 = a.tok.pos[0], seq = a.tok.seq[0];
@@ -52,7 +60,11 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
     const bool q_ok = q_t < T;
     const int qpos = p0 + q_t;
     const int last_tok = min(T - 1, tok0 + 32 * Tb - 1);
-    const int n_keys = p0 + last_tok + 1;                   // keys any query of the block reads
+    const int n_keys_tile = p0 + last_tok + 1;              // keys any query of the tile reads
+    const int nsplit = (n_keys_tile + a.chunk - 1) / a.chunk;
+    if (split >= nsplit) return;                            // uniform: this tile needs fewer ranges
+    const int kbeg = split * a.chunk;
+    const int n_keys = min(n_keys_tile, kbeg + a.chunk);    // keys of this block: kbeg .. n_keys-1
     const float qscale = 1.4426950408889634f / sqrtf((float)HD);
 
     // Q^T operand: lane supplies Q[q][16 ks + 8 (lane/32) + e]
@@ -86,7 +98,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
     constexpr int CHUNKS = BKEY * HD / 8;                   // 16-byte chunks per tile
     constexpr int CPT = CHUNKS / 256;
 
-    const int ntiles = (n_keys + BKEY - 1) / BKEY;
+    const int ntiles = (n_keys - kbeg + BKEY - 1) / BKEY;
     // K and V of keys k0 .. k0+63 into registers (rows past n_keys read as 0).
     // K: chunk ch = 8 dims d8 of key ch / (hd/8).  V: pair chunk pc = 8 dims
     // d8 = pc / 32 of the keys 2 (pc%32) and 2 (pc%32) + 1, whose V^T columns
@@ -111,9 +123,9 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
             }
         }
     };
-    load_tile(0);
+    load_tile(kbeg);
     for (int kt = 0; kt < ntiles; kt++) {
-        const int k0 = kt * BKEY;
+        const int k0 = kbeg + kt * BKEY;
         // ---- stage K and V^T of this tile; the next tile's loads then run
         // during this tile's arithmetic ----
         __syncthreads();                                    // previous tile fully consumed
@@ -187,6 +199,23 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
         }
     }
 
+    if (nsplit > 1) {
+        // this range's unnormalized output and statistics (base 2), merged later
+        if (q_ok) {
+            const size_t hh = (size_t)q_t * a.H + head;
+            float *pp = a.part + (hh * a.max_chunks + split) * HD;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; r4++) {
+                    const int d = dt * 32 + r4 * 8 + (lane >> 5) * 4;
+                    *(float4 *)(pp + d) = make_float4(acc[dt][r4 * 4], acc[dt][r4 * 4 + 1], acc[dt][r4 * 4 + 2],
+                                                      acc[dt][r4 * 4 + 3]);
+                }
+            if (lane < 32) *(float2 *)(a.ml + (hh * a.max_chunks + split) * 2) = make_float2(m_run, l_run);
+        }
+        return;
+    }
     // ---- O = O^T / l, f16 ----
     if (q_ok) {
         const float inv = 1.0f / l_run;
@@ -209,17 +238,78 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
     }
 }
 
+// Token t (row of the ubatch), all heads: combines the key ranges of its
+// tile in range order, M = max m_s, L = sum l_s 2^(m_s - M),
+// o = sum acc_s 2^(m_s - M) / L.  Tiles that needed one range are skipped.
+template <int HD>
+__global__ __launch_bounds__(256) void k_flash_merge(FlashArgs a, int tile_tokens) {
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const int last_tok = min(a.T - 1, (t / tile_tokens) * tile_tokens + tile_tokens - 1);
+    const int nsplit = (a.tok.pos[0] + last_tok + 1 + a.chunk - 1) / a.chunk;
+    if (nsplit <= 1) return;
+    for (int i = tid; i < a.H * HD / 4; i += 256) {
+        const int head = i / (HD / 4), d = (i % (HD / 4)) * 4;
+        const size_t hh = (size_t)t * a.H + head;
+        float M = -INFINITY;
+        for (int sp = 0; sp < nsplit; sp++) M = fmaxf(M, a.ml[(hh * a.max_chunks + sp) * 2]);
+        float L = 0.f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int sp = 0; sp < nsplit; sp++) {
+            const float2 ml = *(const float2 *)(a.ml + (hh * a.max_chunks + sp) * 2);
+            const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+            L += ml.y * f;
+            const float4 v = *(const float4 *)(a.part + (hh * a.max_chunks + sp) * HD + d);
+            o.x += v.x * f;
+            o.y += v.y * f;
+            o.z += v.z * f;
+            o.w += v.w * f;
+        }
+        const float inv = 1.0f / L;
+        const float y[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+        f16 hv[4], lv[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            hv[e] = (f16)y[e];
+            lv[e] = (f16)(y[e] - (float)hv[e]);
+        }
+        const size_t ob = hh * HD + d;
+        *(uint2 *)((f16 *)a.o + ob) = *(const uint2 *)hv;
+        if (a.o_lo) *(uint2 *)((f16 *)a.o_lo + ob) = *(const uint2 *)lv;
+    }
+}
+
 }  // namespace
 
-bool launch_flash_prefill(const FlashArgs &a, hipStream_t s) {
+bool launch_flash_prefill(const FlashArgs &a_in, hipStream_t s) {
+    FlashArgs a = a_in;
     if (a.kv.kvtype != T_F16 || a.T <= 0) return false;
     const int G = a.H / a.kv.n_kv;
     if (G != 1 && G != 2 && G != 4 && G != 8) return false;
     const int Gb = G < 4 ? G : 4, Tb = 4 / Gb;
-    const dim3 grid((a.T + 32 * Tb - 1) / (32 * Tb), a.kv.n_kv, G / Gb);
+    const int tiles = (a.T + 32 * Tb - 1) / (32 * Tb);
+    // key ranges per token tile: enough blocks for two wavefronts per SIMD
+    // (512 blocks of 4 on 256 compute units), ranges of whole 64-key tiles
+    const long long blocks = (long long)tiles * a.kv.n_kv * (G / Gb);
+    int ns = (int)((g_flash_blocks + blocks - 1) / blocks);
+    ns = ns < 1 ? 1 : ns > 8 ? 8 : ns;
+    if (!a.part || !a.ml) ns = 1;
+    if (ns > a.max_chunks) ns = a.max_chunks > 0 ? a.max_chunks : 1;
+    const int max_keys = a.tok_pos0_max + a.T;            // keys of the last tile (host-side bound)
+    int chunk = (max_keys + ns - 1) / ns;
+    chunk = (chunk + 63) / 64 * 64;
+    if (ns == 1) chunk = max_keys + 64;
+    a.ns = ns;
+    a.chunk = chunk;
+    const dim3 grid(tiles * ns, a.kv.n_kv, G / Gb);
     switch (a.kv.hd) {
-    case 64: launch(k_flash_prefill<64>, grid, dim3(256), 0, s, a); return true;
-    case 128: launch(k_flash_prefill<128>, grid, dim3(256), 0, s, a); return true;
+    case 64:
+        launch(k_flash_prefill<64>, grid, dim3(256), 0, s, a);
+        if (ns > 1) launch(k_flash_merge<64>, dim3(a.T), dim3(256), 0, s, a, 32 * Tb);
+        return true;
+    case 128:
+        launch(k_flash_prefill<128>, grid, dim3(256), 0, s, a);
+        if (ns > 1) launch(k_flash_merge<128>, dim3(a.T), dim3(256), 0, s, a, 32 * Tb);
+        return true;
     default: return false;
     }
 }

@@ -190,6 +190,12 @@ struct FlashArgs {
     int H = 0, T = 0;
     uint16_t *o = nullptr;        // [T][H*hd] f16 output
     uint16_t *o_lo = nullptr;     // [T][H*hd] f16 rounding remainder of the output
+    // key split: per-range unnormalized outputs [T][H][max_chunks][hd] and
+    // (max, sum) [T][H][max_chunks][2]; null: no split
+    float *part = nullptr, *ml = nullptr;
+    int max_chunks = 0;
+    int tok_pos0_max = 0;         // host-side upper bound of tok.pos[0] (sizes the key ranges)
+    int ns = 1, chunk = 0;        // set by the launcher
 };
 bool launch_flash_prefill(const FlashArgs &a, hipStream_t s);
 
