@@ -33,8 +33,9 @@ def block_bytes(wtype: int) -> float:
 
 
 def algorithmic(hp, n_prompt, steps):
-    """Bytes per decode token (weights once + KV rows read at the mean context)
-    and FLOPs of the prefill, counted as in the design doc."""
+    """Bytes per decode token (weights once, the embedding as one row, and the
+    K/V rows of every layer at the mean context) and FLOPs of the prefill
+    (2 per MAC; causal attention counts unmasked pairs only)."""
     d, L, F, V = hp["n_embd"], hp["n_layer"], hp["n_ff"], hp["n_vocab"]
     qd, kd = hp["n_head"] * hp["head_dim"], hp["n_head_kv"] * hp["head_dim"]
     per_layer = d * (qd + 2 * kd) + qd * d + 3 * F * d
@@ -51,7 +52,8 @@ def algorithmic(hp, n_prompt, steps):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_matvec_gate_up__8b_q4_decode_bs1__hbm_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "decode_amd", "csrc", f) for f in ("matvec.hip", "common.h", "epilogue.h", "kernels.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_amd", "csrc", f)
+                  for f in ("matvec.hip", "mvcore.h", "common.h", "epilogue.h", "kernels.h")]
 
 
 def kernel_source_hash() -> str:
@@ -179,6 +181,8 @@ def main():
     ap.add_argument("--no-kv-q8", action="store_true",
                     help="skip the leg that reruns the decode loop with a Q8_0 KV cache")
     ap.add_argument("--kv-q8-steps", type=int, default=128)
+    ap.add_argument("--no-step-kernel", action="store_true",
+                    help="skip the leg that runs decode steps through the one-launch step kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (4 times), the reference kernel for "
                          "scaling the HBM fetch/write counters")
@@ -226,7 +230,8 @@ def main():
 
     prompt = synth.prompt(hp["n_vocab"], n_prompt, 2000 + W["seed"] % 1000)
     n_sampled = 64                      # decode steps run with the sampler chain after the timed loop
-    n_ctx = n_prompt + steps + warm + n_sampled + 32 + 8   # + the 32 attention-probe steps
+    n_step_leg = 64                     # decode steps through the one-launch step kernel
+    n_ctx = n_prompt + steps + warm + n_sampled + 32 + n_step_leg + 8   # + the 32 attention-probe steps
     ctx = dec.Context(model, n_ctx=n_ctx, n_batch=n_prompt, n_ubatch=W["n_ubatch"], stream=sp)
     probe_layer = hp["n_layer"] // 2
     ctx.set_probe(dec.K_FFN_GU, probe_layer)
@@ -302,6 +307,40 @@ def main():
     at_probe = ctx.probe()
     attn_ctx = ctx.pos_max(0) + 1 - (n_attn - 1) / 2.0
     ctx.set_probe(-1, 0)
+
+    # the same generation loop through the persistent one-launch step kernel
+    # (opt-in; reported beside the default per-layer graph)
+    step_leg = None
+    if not args.no_step_kernel and ctx.step_kernel(1) >= 0:
+        ctx.set_probe(dec.K_STEP, 0)
+        for _ in range(4):
+            assert ctx.decode([tok], [0]) == 0
+            tok = ctx.argmax(0)
+        ctx.set_probe(dec.K_STEP, 0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_step_leg - 4):
+            if ctx.decode([tok], [0]) != 0:
+                raise RuntimeError("step-kernel decode step failed")
+            tok = ctx.argmax(0)
+            if tok < 0:
+                raise RuntimeError("step kernel: a grid barrier timed out")
+        torch.cuda.synchronize()
+        sk_s = time.perf_counter() - t0
+        sk_probe = ctx.probe()
+        ctx.set_probe(-1, 0)
+        ctx.step_kernel(0)
+        sk_ctx = ctx.pos_max(0) + 1 - (n_step_leg - 4 - 1) / 2.0
+        sk_bytes = algorithmic(hp, 0, 0)["weight_bytes"] + algorithmic(hp, 0, 0)["kv_row_bytes"] * sk_ctx
+        sk_us = sk_probe[0] * 1e3 / sk_probe[1] if sk_probe and sk_probe[1] else None
+        step_leg = {"decode_tokens_per_s": round((n_step_leg - 4) / sk_s, 2), "steps": n_step_leg - 4,
+                    "kernel_us": round(sk_us, 1) if sk_us else None,
+                    "achieved_GBs": round(sk_bytes / (sk_us * 1e-6) / 1e9, 1) if sk_us else None,
+                    "frac": round(sk_bytes / (sk_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if sk_us else None,
+                    "bytes_per_token": int(sk_bytes), "mean_context": sk_ctx,
+                    "note": "whole decode step as one cooperative launch with grid barriers between the "
+                            "layer stages (dec_set_step_kernel); kernel_us from events around the launch"}
+        log(f"step kernel: {step_leg['decode_tokens_per_s']} tok/s, {step_leg['kernel_us']} us per launch")
 
     kv_q8 = None
     if model_q8 is not None:
@@ -385,6 +424,7 @@ def main():
         "graph_replays": st["n_graph_replays"],
         "sampler": sampler,
         "kv_q8_0": kv_q8,
+        "step_kernel": step_leg,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
