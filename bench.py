@@ -169,6 +169,155 @@ def kv_q8_leg(dec, torch, model, hp, prompt, n_ctx, n_ubatch, sp, warm, steps, p
                     "+ merge of one layer, timed live; prefill attention takes the split-K kernel"}
 
 
+def prefill_flops(hp, n_prompt, n_out=1):
+    """FLOPs of a prefill of n_prompt tokens: the layers' projections for
+    every token, causal attention over the unmasked pairs, and the output
+    projection for the n_out rows whose logits are asked for."""
+    d, L, F, V = hp["n_embd"], hp["n_layer"], hp["n_ff"], hp["n_vocab"]
+    qd, kd = hp["n_head"] * hp["head_dim"], hp["n_head_kv"] * hp["head_dim"]
+    per_layer = d * (qd + 2 * kd) + qd * d + 3 * F * d
+    lin = 2.0 * L * per_layer * n_prompt
+    attn = 4.0 * hp["head_dim"] * hp["n_head"] * L * n_prompt * (n_prompt + 1) / 2.0
+    return lin + attn + 2.0 * V * d * n_out
+
+
+def prefill_workload(args, dec, torch, W, hp, log):
+    """A prefill-only workload (the 8B Q8_0 8192-token prompt in ubatches of
+    512, logits for the last token): prefill tokens/s against the f16 MFMA
+    peak, with the gate/up GEMM of the middle layer timed live."""
+    import synth
+    stream = torch.cuda.Stream()
+    sp = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        weights = synth.weights_torch(hp, W["seed"], "cuda")
+    torch.cuda.synchronize()
+    model = dec.Model(hp, weights, stream=sp)
+    torch.cuda.synchronize()
+    del weights
+    torch.cuda.empty_cache()
+    n = W["n_prompt"]
+    prompt = synth.prompt(hp["n_vocab"], n, 2000 + W["seed"] % 1000)
+    ctx = dec.Context(model, n_ctx=n + 64, n_batch=n, n_ubatch=W["n_ubatch"], stream=sp)
+    layer = hp["n_layer"] // 2
+    assert ctx.prefill(prompt, 0) == 0                       # warm-up
+    times = []
+    probe = None
+    for rep in range(max(1, args.prefill_reps)):
+        ctx.clear(0)
+        ctx.set_probe(dec.K_FFN_GU, layer)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        assert ctx.prefill(prompt, 0) == 0
+        tok = ctx.argmax(-1)
+        times.append(time.perf_counter() - t0)
+        probe = ctx.probe()
+        log(f"prefill {n} tokens: {n / times[-1]:.0f} tok/s (token {tok})")
+    ctx.close()
+    model.close()
+    t = sorted(times)[len(times) // 2]
+    flops = prefill_flops(hp, n)
+    gu = None
+    if probe and probe[1]:
+        avg = probe[0] / 1e3 / probe[1]
+        gflop = 2.0 * W["n_ubatch"] * 2 * hp["n_ff"] * hp["n_embd"]
+        gu = {"bound": "mfma", "achieved": round(gflop / avg / 1e12, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+              "unit": "TFLOP/s", "frac": round(gflop / avg / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+              "kernel": "k_gemm_mfma (gate/up, ubatch 512)", "avg_us": round(avg * 1e6, 1),
+              "launches_timed": probe[1]}
+    out = {"metric": "prefill tokens/s (8B-shape Q8_0, 8192-token prompt, ubatches of 512)",
+           "value": round(n / t, 1), "unit": "tokens/s", "n_gpus": 1, "steps": len(times), "warmup": 1,
+           "ms_per_step": round(t * 1e3, 2), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f16", "data": "synthetic",
+           "config": {"workload": f"8B-shape decoder, {'Q8_0' if hp['wtype'] == 2 else 'Q4_0'} weights "
+                                  f"N(0,0.02), f16 KV cache: {n}-token random prompt in ubatches of "
+                                  f"{W['n_ubatch']}, logits for the last token", "n_layer": hp["n_layer"],
+                      "d_model": hp["n_embd"], "heads": hp["n_head"], "kv_heads": hp["n_head_kv"],
+                      "head_dim": hp["head_dim"], "ffn": hp["n_ff"], "vocab": hp["n_vocab"]},
+           "prefill_mfma": {"flops": flops, "achieved_TFLOPs": round(flops / t / 1e12, 1),
+                            "frac": round(flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+           "roofline": gu, "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
+def batched_workload(args, dec, torch, W, hp, log):
+    """Batched decode of independent sequences (the 7B MHA Q4_0 workload: 32
+    sequences of 2048 prompt tokens, then decode calls of one token per
+    sequence): aggregate tokens/s and the decode step's HBM fraction, with
+    the attention of the middle layer timed live, on an f16 and then on a
+    Q8_0 cache."""
+    import numpy as np
+
+    import synth
+    stream = torch.cuda.Stream()
+    sp = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        weights = synth.weights_torch(hp, W["seed"], "cuda")
+    torch.cuda.synchronize()
+    S, n = W["n_seq"], W["n_prompt"]
+    steps, warm = min(args.steps, W["n_decode"]), args.warmup
+    prompts = [synth.prompt(hp["n_vocab"], n, 3000 + s) for s in range(S)]
+    layer = hp["n_layer"] // 2
+    legs = {}
+    for kvt, name in ((synth.F16, "f16"), (synth.Q8_0, "q8_0")):
+        hpk = dict(hp, kvtype=kvt)
+        model = dec.Model(hpk, weights, stream=sp)
+        ctx = dec.Context(model, n_ctx=n + steps + warm + 8, n_batch=n, n_ubatch=W["n_ubatch"],
+                          n_seq_max=S, stream=sp)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(S):
+            assert ctx.prefill(prompts[s], s) == 0
+        torch.cuda.synchronize()
+        prefill_s = time.perf_counter() - t0
+        seqs = np.arange(S, dtype=np.int32)
+        toks = np.asarray(synth.prompt(hp["n_vocab"], S, 4000), np.int32)
+        for _ in range(warm):
+            assert ctx.decode(toks, seqs) == 0
+            toks = ctx.argmax_all().astype(np.int32)
+        ctx.set_probe(dec.K_ATTN, layer)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            if ctx.decode(toks, seqs) != 0:
+                raise RuntimeError("batched decode step failed")
+            toks = ctx.argmax_all().astype(np.int32)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        probe = ctx.probe()
+        mean_ctx = n + warm + (steps + 1) / 2.0
+        wbytes = algorithmic(hpk, 0, 0)["weight_bytes"]
+        kv_row = hp["n_layer"] * 2 * hp["n_head_kv"] * hp["head_dim"] * kv_bytes_per_elem(kvt)
+        step_bytes = wbytes + S * kv_row * mean_ctx
+        gbs = step_bytes / (dt / steps) / 1e9
+        attn = None
+        if probe and probe[1]:
+            avg = probe[0] / 1e3 / probe[1]
+            ab = S * mean_ctx * 2 * hp["n_head_kv"] * hp["head_dim"] * kv_bytes_per_elem(kvt)
+            attn = {"bound": "hbm", "achieved": round(ab / avg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ab / avg / 1e9 / HBM_PEAK_GBS, 4), "avg_us": round(avg * 1e6, 2),
+                    "bytes_per_launch": int(ab), "launches_timed": probe[1]}
+        legs[name] = {"decode_tokens_per_s": round(S * steps / dt, 1), "ms_per_step": round(dt / steps * 1e3, 3),
+                      "prefill_tokens_per_s": round(S * n / prefill_s, 1),
+                      "step_hbm": {"bytes_per_step": int(step_bytes), "achieved_GBs": round(gbs, 1),
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                      "attention": attn}
+        log(f"{name} cache: decode {S * steps / dt:.0f} tok/s, prefill {S * n / prefill_s:.0f} tok/s")
+        ctx.close()
+        model.close()
+    f = legs["f16"]
+    out = {"metric": "aggregate decode tokens/s (7B-shape Q4_0 MHA, 32 sequences)",
+           "value": f["decode_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+           "ms_per_step": f["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f16", "data": "synthetic",
+           "config": {"workload": f"7B-shape decoder, Q4_0 weights N(0,0.02), MHA: {S} sequences with their "
+                                  f"own caches, {n}-token random prompts, decode calls of one token per "
+                                  f"sequence", "n_layer": hp["n_layer"], "d_model": hp["n_embd"],
+                      "heads": hp["n_head"], "kv_heads": hp["n_head_kv"], "head_dim": hp["head_dim"],
+                      "ffn": hp["n_ff"], "vocab": hp["n_vocab"], "sequences": S},
+           "decode_step_hbm": f["step_hbm"], "roofline": f["attention"], "legs": legs, "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +330,7 @@ def main():
     ap.add_argument("--no-kv-q8", action="store_true",
                     help="skip the leg that reruns the decode loop with a Q8_0 KV cache")
     ap.add_argument("--kv-q8-steps", type=int, default=128)
+    ap.add_argument("--prefill-reps", type=int, default=3, help="timed prefills of a prefill-only workload")
     ap.add_argument("--no-step-kernel", action="store_true",
                     help="skip the leg that runs decode steps through the one-launch step kernel")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -201,6 +351,17 @@ def main():
     W = synth.WORKLOADS[args.workload]
     hp = synth.hparams(W)
     n_prompt = W["n_prompt"]
+    if W["n_decode"] == 0 or W["n_seq"] > 1:
+        torch.cuda.set_device(0)
+        dec.lib()
+
+        def log(msg):
+            print(f"[bench] {msg}", file=sys.stderr, flush=True)
+        if W["n_decode"] == 0:
+            prefill_workload(args, dec, torch, W, hp, log)
+        else:
+            batched_workload(args, dec, torch, W, hp, log)
+        return
     steps, warm = args.steps, args.warmup
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
