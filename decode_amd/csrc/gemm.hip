@@ -33,6 +33,11 @@
 //
 // Fallback path (fp32 weights, or shapes the MFMA tiling does not cover):
 // one thread per (row pair, token), plain fp32 FMA.
+#include <stdlib.h>
+#include <string.h>
+
+#include <type_traits>
+
 #include "common.h"
 #include "epilogue.h"
 #include "kernels.h"
@@ -85,7 +90,16 @@ struct Stage {
     u32x4 xh[XC], xl[XC];
 };
 
-template <int WT, int BM, int EPI, bool SPLIT>
+// F16W (opt-in, DECODE_GEMM_F16=1, ubatches of more than 64 tokens): the
+// weights enter the matrix cores as f16(d * code) (the block's dequantized
+// values rounded to f16) and the activations as their f16 value part only,
+// with fp32 accumulation: one MFMA per 16 k and tile and no per-block
+// scaling, and from 256 tokens on a block covers 256 tokens with two register
+// stages.  This is the precision of a dequantize-then-f16-GEMM path; at the
+// 8B shape it leaves the prefill logits about 3.5e-2 from the fp64 result,
+// over the 2e-2 acceptance bound, so it is not the default.  Otherwise
+// (exact operands) as described above.
+template <int WT, int BM, int EPI, bool SPLIT, bool F16W>
 __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh, const uint16_t *Xl,
                                                       int ldx, EpiArgs ep, int M, int pair_mode, int NT,
                                                       int nsplit, float *part) {
@@ -94,8 +108,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
     constexpr bool XALL = BM * 4 >= 256;                // every thread loads activations
     __shared__ __attribute__((aligned(16))) f16 As[2][BN * LDS_STRIDE];
     __shared__ __attribute__((aligned(16))) f16 Bh[2][BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) f16 Bl[2][BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) float Sc[2][BN];
+    __shared__ __attribute__((aligned(16))) f16 Bl[2][F16W ? 8 : BM * LDS_STRIDE];
+    __shared__ __attribute__((aligned(16))) float Sc[2][F16W ? 1 : BN];
 
     // block -> (feature tile, token tile, K split); the tiles of one feature
     // tile (all token tiles and splits) share an XCD
@@ -143,28 +157,36 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
 #pragma unroll
             for (int c = 0; c < XC; c++) {
                 r.xh[c] = *(const u32x4 *)(xh_src[c] + k * 32);
-                r.xl[c] = *(const u32x4 *)(xl_src[c] + k * 32);
+                if (!F16W) r.xl[c] = *(const u32x4 *)(xl_src[c] + k * 32);
             }
         }
     };
     auto lstore = [&](const Stage<WT, XC> &r, int st) __attribute__((always_inline)) {
         h8 c0, c1;
         f16 *arow = &As[st][a_row * LDS_STRIDE];
-        if (WT == T_Q4_0) {
+        if (WT == T_Q4_0)
             q4_codes(u32x2{r.a.x, r.a.y}, c0, c1);
+        else
+            q8_codes(r.a, c0, c1);
+        if (F16W) {
+            const f16 dv = __builtin_bit_cast(f16, (uint16_t)r.d);
+            const h8 dd = h8{dv, dv, dv, dv, dv, dv, dv, dv};
+            c0 *= dd;
+            c1 *= dd;
+        }
+        if (WT == T_Q4_0) {
             *(h8 *)(arow + 8 * a_half) = c0;           // codes 8h .. 8h+7
             *(h8 *)(arow + 16 + 8 * a_half) = c1;      // codes 16+8h .. 16+8h+7
         } else {
-            q8_codes(r.a, c0, c1);
             *(h8 *)(arow + 16 * a_half) = c0;          // codes 16h .. 16h+7
             *(h8 *)(arow + 16 * a_half + 8) = c1;      // codes 16h+8 .. 16h+15
         }
-        if (a_half == 0) Sc[st][a_row] = f16_bits_to_f32((uint16_t)r.d);
+        if (!F16W && a_half == 0) Sc[st][a_row] = f16_bits_to_f32((uint16_t)r.d);
         if (x_loader) {
 #pragma unroll
             for (int c = 0; c < XC; c++) {
                 *(u32x4 *)(&Bh[st][x_lds[c]]) = r.xh[c];
-                *(u32x4 *)(&Bl[st][x_lds[c]]) = r.xl[c];
+                if (!F16W) *(u32x4 *)(&Bl[st][x_lds[c]]) = r.xl[c];
             }
         }
     };
@@ -178,6 +200,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
             for (int r = 0; r < 16; r++) acc[a][b][r] = 0.f;
 
     auto compute = [&](int st) __attribute__((always_inline)) {
+        if constexpr (F16W) {
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                h8 cf[2], xh[MT];
+#pragma unroll
+                for (int a = 0; a < 2; a++)
+                    cf[a] = *(const h8 *)(&As[st][(wn + 32 * a + (lane & 31)) * LDS_STRIDE + 16 * h + 8 * (lane >> 5)]);
+#pragma unroll
+                for (int b = 0; b < MT; b++)
+                    xh[b] = *(const h8 *)(&Bh[st][(wm + 32 * b + (lane & 31)) * LDS_STRIDE + 16 * h + 8 * (lane >> 5)]);
+#pragma unroll
+                for (int a = 0; a < 2; a++)
+#pragma unroll
+                    for (int b = 0; b < MT; b++)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[b], cf[a], acc[a][b], 0, 0, 0);
+            }
+        } else {
         f16x tmp[2][MT];
 #pragma unroll
         for (int kk = 0; kk < 32; kk += 16) {
@@ -212,6 +251,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
 #pragma unroll
                 for (int r = 0; r < 16; r++) acc[a][b][r] += sc * tmp[a][b][r];
         }
+        }
     };
 
     // Loads past the last K block re-read the last one (their data is never
@@ -220,6 +260,34 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
     // Three register sets rotate over two LDS stages (period 6): a K block's
     // loads are issued three compute steps before its LDS store, which covers
     // a loaded memory latency at the MFMA rate of a step.
+    if constexpr (F16W && BM == 256) {
+        // two register sets (the accumulators leave no room for a third): a
+        // K block's loads are issued two steps before its LDS store
+        Stage<WT, XC> r0, r1;
+        gload(r0, 0);
+        gload(r1, min(1, nb - 1));
+        lstore(r0, 0);
+        __syncthreads();
+        gload(r0, min(2, nb - 1));
+        // top: LDS stage 0 holds kb; r1, r0 carry kb+1, kb+2
+        int kb = 0;
+        for (; kb + 3 <= nb; kb += 2) {
+            compute(0);                                 // kb
+            lstore(r1, 1);
+            __syncthreads();
+            gload(r1, min(kb + 3, nb - 1));
+            compute(1);                                 // kb+1
+            lstore(r0, 0);
+            __syncthreads();
+            gload(r0, min(kb + 4, nb - 1));
+        }
+        compute(0);                                     // last 1 or 2 K blocks
+        if (kb + 1 < nb) {
+            lstore(r1, 1);
+            __syncthreads();
+            compute(1);
+        }
+    } else {
     Stage<WT, XC> r0, r1, r2;
     gload(r0, 0);
     gload(r1, min(1, nb - 1));
@@ -228,37 +296,109 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
     __syncthreads();
     gload(r0, min(3, nb - 1));
     // top of an iteration: LDS stage 0 holds kb; r1, r2, r0 carry kb+1..kb+3
-    for (int kb = 0; kb < nb; kb += 6) {
+    if constexpr (F16W) {
+    // Step i of a period: compute K block kb+i, store kb+i+1 to the other
+    // LDS stage, load kb+i+4.  Full periods run unguarded (the compiler can
+    // then count exactly which loads a store waits for); the last period's
+    // steps are guarded by uniform conditions rather than early exits, so the
+    // accumulators stay in the same registers on every path.
+    int kb = 0;
+    for (; kb + 7 <= nb; kb += 6) {
         compute(0);                                     // kb
-        if (kb + 1 >= nb) break;
         lstore(r1, 1);
         __syncthreads();
         gload(r1, min(kb + 4, nb - 1));
         compute(1);                                     // kb+1
-        if (kb + 2 >= nb) break;
         lstore(r2, 0);
         __syncthreads();
         gload(r2, min(kb + 5, nb - 1));
         compute(0);                                     // kb+2
-        if (kb + 3 >= nb) break;
         lstore(r0, 1);
         __syncthreads();
         gload(r0, min(kb + 6, nb - 1));
         compute(1);                                     // kb+3
-        if (kb + 4 >= nb) break;
         lstore(r1, 0);
         __syncthreads();
         gload(r1, min(kb + 7, nb - 1));
         compute(0);                                     // kb+4
-        if (kb + 5 >= nb) break;
         lstore(r2, 1);
         __syncthreads();
         gload(r2, min(kb + 8, nb - 1));
         compute(1);                                     // kb+5
-        if (kb + 6 >= nb) break;
         lstore(r0, 0);
         __syncthreads();
         gload(r0, min(kb + 9, nb - 1));
+    }
+    // last 1 .. 6 K blocks (r1 and r2 still take kb+4 and kb+5)
+    compute(0);                                         // kb
+    if (kb + 1 < nb) {
+        lstore(r1, 1);
+        __syncthreads();
+        gload(r1, min(kb + 4, nb - 1));
+        compute(1);
+    }
+    if (kb + 2 < nb) {
+        lstore(r2, 0);
+        __syncthreads();
+        gload(r2, min(kb + 5, nb - 1));
+        compute(0);
+    }
+    if (kb + 3 < nb) {
+        lstore(r0, 1);
+        __syncthreads();
+        compute(1);
+    }
+    if (kb + 4 < nb) {
+        lstore(r1, 0);
+        __syncthreads();
+        compute(0);
+    }
+    if (kb + 5 < nb) {
+        lstore(r2, 1);
+        __syncthreads();
+        compute(1);
+    }
+    } else {
+    // exact operands: every step guarded by a uniform condition
+    for (int kb = 0; kb < nb; kb += 6) {
+        compute(0);                                     // kb
+        if (kb + 1 < nb) {
+            lstore(r1, 1);
+            __syncthreads();
+            gload(r1, min(kb + 4, nb - 1));
+            compute(1);                                 // kb+1
+        }
+        if (kb + 2 < nb) {
+            lstore(r2, 0);
+            __syncthreads();
+            gload(r2, min(kb + 5, nb - 1));
+            compute(0);                                 // kb+2
+        }
+        if (kb + 3 < nb) {
+            lstore(r0, 1);
+            __syncthreads();
+            gload(r0, min(kb + 6, nb - 1));
+            compute(1);                                 // kb+3
+        }
+        if (kb + 4 < nb) {
+            lstore(r1, 0);
+            __syncthreads();
+            gload(r1, min(kb + 7, nb - 1));
+            compute(0);                                 // kb+4
+        }
+        if (kb + 5 < nb) {
+            lstore(r2, 1);
+            __syncthreads();
+            gload(r2, min(kb + 8, nb - 1));
+            compute(1);                                 // kb+5
+        }
+        if (kb + 6 < nb) {
+            lstore(r0, 0);
+            __syncthreads();
+            gload(r0, min(kb + 9, nb - 1));
+        }
+    }
+    }
     }
 
     // ---- epilogue ----
@@ -280,8 +420,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
             }
         return;
     }
-#pragma unroll
-    for (int b = 0; b < MT; b++) {
+    // one copy of the epilogue per token tile (b a constant: the tile's
+    // accumulators stay in registers)
+    auto epi_tile = [&](auto bc) __attribute__((always_inline)) {
+        constexpr int b = decltype(bc)::value;
         const int mb = m0 + wm + 32 * b + (lane >> 5) * 4;
         if (EPI == EPI_STORE || EPI == EPI_RESID) {
 #pragma unroll
@@ -325,7 +467,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
                     if (m < M) epi_pair<EPI>(ep, m, f >> 1, f, f + 1, va, vb);
                 }
         }
-    }
+    };
+    epi_tile(std::integral_constant<int, 0>{});
+    if constexpr (MT > 1) epi_tile(std::integral_constant<int, 1>{});
+    if constexpr (MT > 2) epi_tile(std::integral_constant<int, 2>{});
+    if constexpr (MT > 3) epi_tile(std::integral_constant<int, 3>{});
+    static_assert(MT <= 4, "epilogue covers four token tiles");
 }
 
 // Sums the K-split partial tiles in split order and applies the epilogue;
@@ -370,6 +517,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(QMat W, const uint16_t *X, con
 }
 
 int g_gemm_cu = 256;
+int g_gemm_f16w = 0;   // f16 operands for ubatches of more than 64 tokens (opt-in)
 
 bool mfma_shape(const QMat &W, int ldx) {
     return (W.wtype == T_Q4_0 || W.wtype == T_Q8_0) && W.N % BN == 0 && W.K % 32 == 0 && ldx % 8 == 0;
@@ -379,8 +527,11 @@ bool mfma_shape(const QMat &W, int ldx) {
 // (2 per CU) empty, the largest of 2 and 4 that still fits one round of
 // slots, each split keeping >= 16 K blocks.  (Splitting a grid that already
 // fills the chip only adds partial-tile traffic.)
+// Token tile: 256 with f16 operands from 256 tokens on, else 128 above 64 tokens, else 64.
+int tile_m(int M) { return g_gemm_f16w && M >= 256 ? 256 : M > 64 ? 128 : 64; }
+
 int split_for(const QMat &W, int M) {
-    const int bm = M > 64 ? 128 : 64;
+    const int bm = tile_m(M);
     const long tiles = (long)(W.N / BN) * ((M + bm - 1) / bm);
     const long slots = 2L * g_gemm_cu;
     const int nb = W.K / 32;
@@ -390,27 +541,42 @@ int split_for(const QMat &W, int M) {
     return best;
 }
 
+template <int WT, int EPI, int BM, bool SPLIT>
+void launch_mfma_tile(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
+                      int M, int pair_mode, int S, float *ws, dim3 grid, bool f16w, hipStream_t s) {
+    const int NT = W.N / BN;
+    float *part = SPLIT ? ws : nullptr;
+    if (f16w)
+        launch((k_gemm_mfma<WT, BM, EPI, SPLIT, true>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode,
+               NT, S, part);
+    else if constexpr (BM <= 128)   // exact operands: tiles of up to 128 tokens
+        launch((k_gemm_mfma<WT, BM, EPI, SPLIT, false>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode,
+               NT, S, part);
+}
+
 template <int WT, int EPI>
 void launch_mfma_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
                      int M, int pair_mode, int S, float *ws, hipStream_t s) {
     const int NT = W.N / BN, NT8 = (NT + 7) / 8 * 8;
-    const int bm = M > 64 ? 128 : 64;
+    const int bm = tile_m(M);
     const dim3 grid(NT8 * ((M + bm - 1) / bm) * S);
+    // f16 operands for ubatches of more than 64 tokens; exact operands below
+    const bool f16w = g_gemm_f16w && bm >= 128;
     if (S > 1) {
-        if (bm == 128)
-            launch((k_gemm_mfma<WT, 128, EPI, true>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode,
-                   NT, S, ws);
+        if (bm == 256)
+            launch_mfma_tile<WT, EPI, 256, true>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, grid, true, s);
+        else if (bm == 128)
+            launch_mfma_tile<WT, EPI, 128, true>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, grid, f16w, s);
         else
-            launch((k_gemm_mfma<WT, 64, EPI, true>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode,
-                   NT, S, ws);
+            launch_mfma_tile<WT, EPI, 64, true>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, grid, false, s);
         launch(k_gemm_splitk_sum<EPI>, dim3((W.N / 2 + 255) / 256, M), dim3(256), 0, s, (const float *)ws, S,
                W.N, M, ep, pair_mode);
+    } else if (bm == 256) {
+        launch_mfma_tile<WT, EPI, 256, false>(W, Xh, Xl, ldx, ep, M, pair_mode, 1, ws, grid, true, s);
     } else if (bm == 128) {
-        launch((k_gemm_mfma<WT, 128, EPI, false>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT,
-               1, (float *)nullptr);
+        launch_mfma_tile<WT, EPI, 128, false>(W, Xh, Xl, ldx, ep, M, pair_mode, 1, ws, grid, f16w, s);
     } else {
-        launch((k_gemm_mfma<WT, 64, EPI, false>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT,
-               1, (float *)nullptr);
+        launch_mfma_tile<WT, EPI, 64, false>(W, Xh, Xl, ldx, ep, M, pair_mode, 1, ws, grid, false, s);
     }
 }
 
@@ -434,7 +600,11 @@ void launch_f32_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int l
 
 }  // namespace
 
-void gemm_set_num_cu(int n) { g_gemm_cu = n > 0 ? n : 256; }
+void gemm_set_num_cu(int n) {
+    g_gemm_cu = n > 0 ? n : 256;
+    const char *e = getenv("DECODE_GEMM_F16");
+    g_gemm_f16w = e && strcmp(e, "1") == 0;
+}
 
 size_t gemm_workspace_bytes(const QMat &W, int M) {
     if (M <= 0 || !mfma_shape(W, 8)) return 0;

@@ -1,0 +1,88 @@
+"""Operand modes of the ubatch GEMM (prefill and batched decode) against the oracle.
+
+By default every ubatch takes exact operands (integer codes, activations as
+f16 value + remainder, per-block scale applied in fp32).  With
+DECODE_GEMM_F16=1 (read when a context is created) ubatches of more than 64
+tokens take f16 operands instead: each weight enters the matrix cores as its
+dequantized value d * code rounded to f16 and each activation as its f16
+value, with fp32 accumulation; from 256 tokens on a block covers 256 tokens.
+At this small shape both modes meet the oracle bar on every output row of a
+300-token ubatch (a full 256-token tile and a ragged 44-token tile), and they
+differ, which shows that the switch took effect.  (At the 8B shape the f16
+mode does not meet the bar, which is why it is opt-in.)
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import assert_logits_close, logit_err, small_hp
+
+pytestmark = pytest.mark.gpu
+
+ROWS = (0, 1, 63, 64, 255, 256, 257, 299)
+
+
+@pytest.fixture(scope="module")
+def dec():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_amd
+    decode_amd.lib()
+    return decode_amd
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.load("f64")
+    return oracle
+
+
+def _rows(dec, gm, prompt, n_ubatch):
+    ctx = dec.Context(gm, n_ctx=512, n_batch=len(prompt), n_ubatch=n_ubatch)
+    assert ctx.prefill(prompt, 0, output_all=True) == 0
+    rows = {i: np.array(ctx.logits(i)) for i in ROWS}
+    am = {i: ctx.argmax(i) for i in ROWS}
+    ctx.close()
+    return rows, am
+
+
+@pytest.mark.parametrize("wtype", [synth.Q4_0, synth.Q8_0])
+def test_both_operand_modes_match_oracle(dec, orc, wtype, monkeypatch):
+    hp = small_hp(wtype, synth.F16)
+    w = synth.weights_numpy(hp, 900 + wtype, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 300, 901)
+    oc = orc.Context(orc.Model(hp, w), 1, 512)
+    o_rows = {}
+    for i, t in enumerate(prompt):
+        r = oc.eval(0, int(t))
+        if i in ROWS:
+            o_rows[i] = r
+    gm = dec.Model(hp, w)
+    got = {}
+    for exact in (False, True):
+        monkeypatch.setenv("DECODE_GEMM_F16", "0" if exact else "1")
+        rows, am = _rows(dec, gm, prompt, 300)
+        for i in ROWS:
+            assert_logits_close(rows[i], o_rows[i], f"exact={exact} row {i}")
+            assert am[i] == int(np.argmax(rows[i]))
+        got[exact] = rows
+    monkeypatch.delenv("DECODE_GEMM_F16")
+    diff = max(logit_err(got[False][i], got[True][i])[0] for i in ROWS)
+    assert 0.0 < diff < 1e-2, f"modes differ by {diff:.3e}"
+
+
+def test_small_ubatch_exact_in_both_modes(dec, monkeypatch):
+    """Ubatches of at most 64 tokens take exact operands whatever the switch says."""
+    hp = small_hp(synth.Q4_0, synth.F16)
+    w = synth.weights_numpy(hp, 910, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 300, 911)
+    gm = dec.Model(hp, w)
+    got = []
+    for exact in (False, True):
+        monkeypatch.setenv("DECODE_GEMM_F16", "0" if exact else "1")
+        got.append(_rows(dec, gm, prompt, 64)[0])
+    monkeypatch.delenv("DECODE_GEMM_F16")
+    for i in ROWS:
+        assert np.array_equal(got[0][i], got[1][i]), f"row {i}"
