@@ -144,7 +144,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
         x_lds[c] = mr * LDS_STRIDE + kc * 8;
     }
 
-    auto gload = [&](Stage<WT, XC> &r, int kb) __attribute__((always_inline)) {
+    // kb may run past the last K block: the last one is re-read with a zero
+    // scale, so that block adds nothing
+    auto gload = [&](Stage<WT, XC> &r, int kb_raw) __attribute__((always_inline)) {
+        const int kb = min(kb_raw, nb - 1);
         const int k = kb0 + kb;
         if (WT == T_Q4_0) {
             const u32x2 v = *(const u32x2 *)(qbase + (size_t)k * 16);
@@ -152,7 +155,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
         } else {
             r.a = *(const u32x4 *)(qbase + (size_t)k * 32);
         }
-        r.d = dbase[k];
+        const uint32_t dv = dbase[k];
+        r.d = kb_raw < nb ? dv : 0u;
         if (x_loader) {
 #pragma unroll
             for (int c = 0; c < XC; c++) {
@@ -260,41 +264,46 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
     // Three register sets rotate over two LDS stages (period 6): a K block's
     // loads are issued three compute steps before its LDS store, which covers
     // a loaded memory latency at the MFMA rate of a step.
-    if constexpr (F16W && BM == 256) {
+    if constexpr (F16W ? BM == 256 : BM == 64) {
         // two register sets (the accumulators leave no room for a third): a
         // K block's loads are issued two steps before its LDS store
         Stage<WT, XC> r0, r1;
         gload(r0, 0);
-        gload(r1, min(1, nb - 1));
+        gload(r1, 1);
         lstore(r0, 0);
         __syncthreads();
-        gload(r0, min(2, nb - 1));
+        gload(r0, 2);
         // top: LDS stage 0 holds kb; r1, r0 carry kb+1, kb+2
         int kb = 0;
-        for (; kb + 3 <= nb; kb += 2) {
+        // exact operands: K blocks past the last one take zero scales, so the
+        // loop runs whole periods and has no guarded tail
+        const int nbl = F16W ? nb - 2 : (nb + 1) / 2 * 2;
+        for (; kb < nbl; kb += 2) {
             compute(0);                                 // kb
             lstore(r1, 1);
             __syncthreads();
-            gload(r1, min(kb + 3, nb - 1));
+            gload(r1, kb + 3);
             compute(1);                                 // kb+1
             lstore(r0, 0);
             __syncthreads();
-            gload(r0, min(kb + 4, nb - 1));
+            gload(r0, kb + 4);
         }
-        compute(0);                                     // last 1 or 2 K blocks
-        if (kb + 1 < nb) {
-            lstore(r1, 1);
-            __syncthreads();
-            compute(1);
+        if constexpr (F16W) {
+            compute(0);                                 // last 1 or 2 K blocks
+            if (kb + 1 < nb) {
+                lstore(r1, 1);
+                __syncthreads();
+                compute(1);
+            }
         }
     } else {
     Stage<WT, XC> r0, r1, r2;
     gload(r0, 0);
-    gload(r1, min(1, nb - 1));
-    gload(r2, min(2, nb - 1));
+    gload(r1, 1);
+    gload(r2, 2);
     lstore(r0, 0);
     __syncthreads();
-    gload(r0, min(3, nb - 1));
+    gload(r0, 3);
     // top of an iteration: LDS stage 0 holds kb; r1, r2, r0 carry kb+1..kb+3
     if constexpr (F16W) {
     // Step i of a period: compute K block kb+i, store kb+i+1 to the other
