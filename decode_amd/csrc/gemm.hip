@@ -36,6 +36,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -87,6 +88,7 @@ template <int WT, int XC>
 struct Stage {
     u32x4 a;          // Q4_0: .x,.y = 8 bytes; Q8_0: 16 bytes
     uint32_t d;       // f16 scale bits of row t/2 (even threads)
+    bool live;        // false: a K block past the last one (scale taken as 0)
     u32x4 xh[XC], xl[XC];
 };
 
@@ -155,8 +157,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
         } else {
             r.a = *(const u32x4 *)(qbase + (size_t)k * 32);
         }
-        const uint32_t dv = dbase[k];
-        r.d = kb_raw < nb ? dv : 0u;
+        r.d = dbase[k];
+        r.live = kb_raw < nb;   // applied at the store: a select here would wait for the load
         if (x_loader) {
 #pragma unroll
             for (int c = 0; c < XC; c++) {
@@ -172,8 +174,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
             q4_codes(u32x2{r.a.x, r.a.y}, c0, c1);
         else
             q8_codes(r.a, c0, c1);
+        const uint32_t dbits = r.live ? r.d : 0u;
         if (F16W) {
-            const f16 dv = __builtin_bit_cast(f16, (uint16_t)r.d);
+            const f16 dv = __builtin_bit_cast(f16, (uint16_t)dbits);
             const h8 dd = h8{dv, dv, dv, dv, dv, dv, dv, dv};
             c0 *= dd;
             c1 *= dd;
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
             *(h8 *)(arow + 16 * a_half) = c0;          // codes 16h .. 16h+7
             *(h8 *)(arow + 16 * a_half + 8) = c1;      // codes 16h+8 .. 16h+15
         }
-        if (!F16W && a_half == 0) Sc[st][a_row] = f16_bits_to_f32((uint16_t)r.d);
+        if (!F16W && a_half == 0) Sc[st][a_row] = f16_bits_to_f32((uint16_t)dbits);
         if (x_loader) {
 #pragma unroll
             for (int c = 0; c < XC; c++) {
@@ -525,8 +528,151 @@ __global__ __launch_bounds__(256) void k_gemm_f32(QMat W, const uint16_t *X, con
     epi_pair<EPI>(ep, m, p, r0, r1, a, b);
 }
 
+
+// ---- skinny form: ubatches of at most 32 tokens (batched decode) ----------
+//
+// The same exact operands as above, without LDS staging or a barrier per K
+// block.  A wavefront owns FT tiles of 32 features and every token (one
+// 32-row tile; rows past M repeat row M-1 and are dropped), and streams its
+// own weight rows straight into B operands: lane l takes feature l%32 and the
+// 8 bytes of the block that hold codes 8(l/32)..+7 (low nibbles: k-half 0)
+// and 16+8(l/32)..+7 (high nibbles: k-half 1) for Q4_0, or those two 8-byte
+// runs for Q8_0.  The activation fragments (token l%32, k 8(l/32)..+7 of each
+// k-half, value and remainder) come from global memory, shared through L2.
+// The four wavefronts of a block take interleaved K blocks of the block's K
+// range and meet once in LDS; blocks of different K ranges write fp32 partial
+// tiles that k_gemm_splitk_sum adds in order and finishes with the epilogue.
+// Each wavefront reads its activation fragments itself (4 KB per K block for
+// 64 features), so the form pays in L2 traffic what it saves in barriers: it
+// is taken for matrices of at most 4096 features, where the tiled grid has
+// too few blocks (32 tokens, d = 4096: O 13 vs 18 µs, down 29 vs 41 µs; the
+// wider gate/up and QKV matrices are faster on the tiles).
+// Loads run D_W K blocks ahead for weights and D_X for activations; K blocks
+// past the wavefront's last one re-read it with a zero scale, so the loop has
+// one body and no guards.
+template <int WT, int FT>
+__global__ __launch_bounds__(256) void k_gemm_skinny(QMat W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
+                                                     int M, int nsplit, float *part) {
+    constexpr int D_W = 4, D_X = 2;
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    __shared__ __attribute__((aligned(16))) float red[3][FT][16][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane >> 5, fl = lane & 31;
+    const int ngroups = W.N / (32 * FT);
+    const int grp = blockIdx.x % ngroups, split = blockIdx.x / ngroups;
+    const int nb = W.K >> 5;
+    const int kb_lo = (int)((long)nb * split / nsplit), kb_hi = (int)((long)nb * (split + 1) / nsplit);
+    // this wavefront's K blocks: kb_lo + w + 4 i, i < nblk
+    const int nblk = kb_hi - kb_lo > w ? (kb_hi - kb_lo - w + 3) / 4 : 0;
+    const int nblkp = (nblk + D_W - 1) / D_W * D_W;
+    const int n0 = grp * 32 * FT;
+
+    const size_t rowb = WT == T_Q4_0 ? (size_t)(W.K >> 1) : (size_t)W.K;
+    const uint8_t *qrow[FT];
+    const uint16_t *drow[FT];
+#pragma unroll
+    for (int t = 0; t < FT; t++) {
+        const int row = n0 + 32 * t + fl;
+        qrow[t] = (const uint8_t *)W.qs + (size_t)row * rowb + 8 * c;
+        drow[t] = W.d + (size_t)row * nb;
+    }
+    const int tok = min(fl, M - 1);
+    const uint16_t *xh_row = Xh + (size_t)tok * ldx + 8 * c;
+    const uint16_t *xl_row = Xl + (size_t)tok * ldx + 8 * c;
+
+    // (clamped into the block's range: a wavefront with no K block re-reads
+    // the range's last one, with a zero scale)
+    auto kb_of = [&](int i) __attribute__((always_inline)) {
+        return min(kb_lo + w + 4 * min(i, max(nblk - 1, 0)), kb_hi - 1);
+    };
+    struct WSlot { u32x2v q[FT][WT == T_Q4_0 ? 1 : 2]; uint32_t d[FT]; };
+    struct XSlot { u32x4 h[2], l[2]; };
+    auto wload = [&](WSlot &sl, int i) __attribute__((always_inline)) {
+        const int kb = kb_of(i);
+#pragma unroll
+        for (int t = 0; t < FT; t++) {
+            if (WT == T_Q4_0) {
+                sl.q[t][0] = *(const u32x2v *)(qrow[t] + (size_t)kb * 16);
+            } else {
+                sl.q[t][0] = *(const u32x2v *)(qrow[t] + (size_t)kb * 32);
+                sl.q[t][WT == T_Q4_0 ? 0 : 1] = *(const u32x2v *)(qrow[t] + (size_t)kb * 32 + 16);
+            }
+            sl.d[t] = drow[t][kb];
+        }
+    };
+    auto xload = [&](XSlot &sl, int i) __attribute__((always_inline)) {
+        const int kb = kb_of(i);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            sl.h[h] = *(const u32x4 *)(xh_row + (size_t)kb * 32 + 16 * h);
+            sl.l[h] = *(const u32x4 *)(xl_row + (size_t)kb * 32 + 16 * h);
+        }
+    };
+
+    f16x acc[FT];
+#pragma unroll
+    for (int t = 0; t < FT; t++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[t][r] = 0.f;
+
+    WSlot ws[D_W];
+    XSlot xs[D_X];
+#pragma unroll
+    for (int j = 0; j < D_W; j++) wload(ws[j], j);
+#pragma unroll
+    for (int j = 0; j < D_X; j++) xload(xs[j], j);
+
+    for (int i0 = 0; i0 < nblkp; i0 += D_W) {
+#pragma unroll
+        for (int j = 0; j < D_W; j++) {
+            const int i = i0 + j;
+            const XSlot &x = xs[j % D_X];
+            const h8 xh0 = __builtin_bit_cast(h8, x.h[0]), xh1 = __builtin_bit_cast(h8, x.h[1]);
+            const h8 xl0 = __builtin_bit_cast(h8, x.l[0]), xl1 = __builtin_bit_cast(h8, x.l[1]);
+#pragma unroll
+            for (int t = 0; t < FT; t++) {
+                h8 b0, b1;
+                if (WT == T_Q4_0)
+                    q4_codes(ws[j].q[t][0], b0, b1);
+                else
+                    q8_codes(u32x4{ws[j].q[t][0].x, ws[j].q[t][0].y, ws[j].q[t][WT == T_Q4_0 ? 0 : 1].x,
+                                   ws[j].q[t][WT == T_Q4_0 ? 0 : 1].y}, b0, b1);
+                f16x tmp = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh0, b0, f16x{}, 0, 0, 0);
+                tmp = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl0, b0, tmp, 0, 0, 0);
+                tmp = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh1, b1, tmp, 0, 0, 0);
+                tmp = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl1, b1, tmp, 0, 0, 0);
+                // past the last block: no contribution (the select is on the
+                // index, so it does not wait for the scale's load)
+                const float sc = f16_bits_to_f32((uint16_t)ws[j].d[t]) * (i < nblk ? 1.f : 0.f);
+#pragma unroll
+                for (int r = 0; r < 16; r++) acc[t][r] += sc * tmp[r];
+            }
+            xload(xs[j % D_X], i + D_X);
+            wload(ws[j], i + D_W);
+        }
+    }
+
+    // the four wavefronts' partial tiles meet in LDS; wavefront 0 writes
+    if (w > 0) {
+#pragma unroll
+        for (int t = 0; t < FT; t++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) red[w - 1][t][r][lane] = acc[t][r];
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int t = 0; t < FT; t++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const float v = acc[t][r] + red[0][t][r][lane] + red[1][t][r][lane] + red[2][t][r][lane];
+            const int m = (r >> 2) * 8 + c * 4 + (r & 3);
+            if (m < M) part[((size_t)split * M + m) * W.N + n0 + 32 * t + fl] = v;
+        }
+}
+
 int g_gemm_cu = 256;
 int g_gemm_f16w = 0;   // f16 operands for ubatches of more than 64 tokens (opt-in)
+int g_gemm_skinny = 1; // skinny form for ubatches of at most 32 tokens
 
 bool mfma_shape(const QMat &W, int ldx) {
     return (W.wtype == T_Q4_0 || W.wtype == T_Q8_0) && W.N % BN == 0 && W.K % 32 == 0 && ldx % 8 == 0;
@@ -538,6 +684,16 @@ bool mfma_shape(const QMat &W, int ldx) {
 // fills the chip only adds partial-tile traffic.)
 // Token tile: 256 with f16 operands from 256 tokens on, else 128 above 64 tokens, else 64.
 int tile_m(int M) { return g_gemm_f16w && M >= 256 ? 256 : M > 64 ? 128 : 64; }
+
+// Skinny form: 64 features per block; K ranges so that the grid has about
+// two blocks per compute unit and each wavefront at least 4 K blocks.
+constexpr int SK_FT = 2;
+int skinny_splits(const QMat &W) {
+    const int groups = W.N / (32 * SK_FT), nb = W.K / 32;
+    int S = (2 * g_gemm_cu + groups - 1) / groups;
+    S = std::min(S, std::max(1, nb / 16));
+    return std::max(1, std::min(S, 64));
+}
 
 int split_for(const QMat &W, int M) {
     const int bm = tile_m(M);
@@ -613,12 +769,17 @@ void gemm_set_num_cu(int n) {
     g_gemm_cu = n > 0 ? n : 256;
     const char *e = getenv("DECODE_GEMM_F16");
     g_gemm_f16w = e && strcmp(e, "1") == 0;
+    const char *k = getenv("DECODE_GEMM_SKINNY");
+    g_gemm_skinny = !(k && strcmp(k, "0") == 0);
 }
 
 size_t gemm_workspace_bytes(const QMat &W, int M) {
     if (M <= 0 || !mfma_shape(W, 8)) return 0;
     const int S = split_for(W, M);
-    return S > 1 ? (size_t)S * M * W.N * 4 : 0;
+    const size_t tile = S > 1 ? (size_t)S * M * W.N * 4 : 0;
+    // the skinny form, for any ubatch of at most min(M, 32) tokens
+    const int ms = M < 32 ? M : 32;
+    return W.N <= 4096 ? std::max(tile, (size_t)skinny_splits(W) * ms * W.N * 4) : tile;
 }
 
 bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
@@ -626,6 +787,28 @@ bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
     if (M <= 0 || W.N % 2 || !Xh || !Xl) return false;
     const int pair_mode = ep.epi == EPI_SWIGLU ? PAIR_GU : PAIR_ADJ;
     if (pair_mode == PAIR_GU && W.N % 64) return false;
+    // skinny form for at most 32 tokens and at most 4096 features: there the
+    // tiled grid is too small to spread over the chip (wider matrices stay
+    // on the tiles, whose LDS-shared activations cost less L2 traffic)
+    if (mfma_shape(W, ldx) && M <= 32 && W.N <= 4096 && g_gemm_skinny && W.N % (32 * SK_FT) == 0) {
+        const int S = skinny_splits(W);
+        if (ws && (size_t)S * M * W.N * 4 <= ws_bytes) {
+            const int groups = W.N / (32 * SK_FT);
+            if (W.wtype == T_Q4_0)
+                launch((k_gemm_skinny<T_Q4_0, SK_FT>), dim3(groups * S), dim3(256), 0, s, W, Xh, Xl, ldx, M, S, ws);
+            else
+                launch((k_gemm_skinny<T_Q8_0, SK_FT>), dim3(groups * S), dim3(256), 0, s, W, Xh, Xl, ldx, M, S, ws);
+            const dim3 g((W.N / 2 + 255) / 256, M);
+            switch (ep.epi) {
+            case EPI_STORE: launch(k_gemm_splitk_sum<EPI_STORE>, g, dim3(256), 0, s, (const float *)ws, S, W.N, M, ep, pair_mode); break;
+            case EPI_RESID: launch(k_gemm_splitk_sum<EPI_RESID>, g, dim3(256), 0, s, (const float *)ws, S, W.N, M, ep, pair_mode); break;
+            case EPI_QKV: launch(k_gemm_splitk_sum<EPI_QKV>, g, dim3(256), 0, s, (const float *)ws, S, W.N, M, ep, pair_mode); break;
+            case EPI_SWIGLU: launch(k_gemm_splitk_sum<EPI_SWIGLU>, g, dim3(256), 0, s, (const float *)ws, S, W.N, M, ep, pair_mode); break;
+            default: return false;
+            }
+            return true;
+        }
+    }
     if (mfma_shape(W, ldx)) {
         int S = split_for(W, M);
         while (S > 1 && (!ws || (size_t)S * M * W.N * 4 > ws_bytes)) S >>= 1;

@@ -86,3 +86,30 @@ def test_small_ubatch_exact_in_both_modes(dec, monkeypatch):
     monkeypatch.delenv("DECODE_GEMM_F16")
     for i in ROWS:
         assert np.array_equal(got[0][i], got[1][i]), f"row {i}"
+
+
+@pytest.mark.parametrize("wtype", [synth.Q4_0, synth.Q8_0])
+def test_skinny_form_matches_tiles_and_oracle(dec, orc, wtype, monkeypatch):
+    """Ubatches of at most 32 tokens take the skinny form (wavefronts stream
+    their own weight rows, K ranges over blocks); DECODE_GEMM_SKINNY=0 sends
+    them through the tiled kernel instead.  Same exact operands, different
+    summation order: rows within 1e-3 of each other and within the oracle bar,
+    on a 45-token prompt in ubatches of 32 (a full and a ragged 13-token one)."""
+    hp = small_hp(wtype, synth.F16, n_embd=512, n_head=8, n_ff=1024)
+    w = synth.weights_numpy(hp, 920 + wtype, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 45, 921)
+    oc = orc.Context(orc.Model(hp, w), 1, 256)
+    o_rows = [oc.eval(0, int(t)) for t in prompt]
+    gm = dec.Model(hp, w)
+    got = {}
+    for skinny in (True, False):
+        monkeypatch.setenv("DECODE_GEMM_SKINNY", "1" if skinny else "0")
+        ctx = dec.Context(gm, n_ctx=256, n_batch=45, n_ubatch=32)
+        assert ctx.prefill(prompt, 0, output_all=True) == 0
+        got[skinny] = [np.array(ctx.logits(i)) for i in range(45)]
+        ctx.close()
+    monkeypatch.delenv("DECODE_GEMM_SKINNY")
+    for i in (0, 1, 31, 32, 44):
+        assert_logits_close(got[True][i], o_rows[i], f"skinny row {i}")
+        ma, _ = logit_err(got[True][i], got[False][i])
+        assert ma <= 1e-3, f"row {i}: skinny vs tiles {ma:.3e}"
