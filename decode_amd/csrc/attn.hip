@@ -364,6 +364,7 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
     constexpr int DT = HD / 32;          // 32-dim tiles of O = P V
     __shared__ float cm[MW][32], cl[MW][32];
     __shared__ __attribute__((aligned(16))) float co[MW][GMAX][HD];
+    __shared__ __attribute__((aligned(16))) f16 vtile[MW][32 * (HD + 8)];
 
     const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, ln = lane & 31;
@@ -395,15 +396,16 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
     // B operand of O = P V for k-step s: element e of lane l is key
     // 16 s + 8 (e/4) + 4 (l/32) + e%4 -- the keys whose probabilities the lane
     // holds in its S^T accumulators 8 s + e -- at dim 32 dt + l%32
-    h8 vb[DT][2];
+    // The wavefront's 32 V rows are requested as 16-byte pieces (8 KB at hd
+    // 128: HD/8 pieces per row, 64 lanes per round) and pass through a
+    // wavefront-private LDS tile, from which the transposed operand is read.
+    constexpr int VP = HD / 8, VR = 32 * VP / 64;      // pieces per row, rounds
+    u32x4 vraw[VR];
 #pragma unroll
-    for (int s = 0; s < 2; s++)
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const int key = min(k0 + 16 * s + 8 * (e >> 2) + 4 * hf + (e & 3), pos);
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++) vb[dt][s][e] = Vb[(size_t)key * HD + 32 * dt + ln];
-        }
+    for (int u = 0; u < VR; u++) {
+        const int pc = u * 64 + lane, key = min(k0 + pc / VP, pos);
+        vraw[u] = *(const u32x4 *)(Vb + (size_t)key * HD + 8 * (pc % VP));
+    }
 
     // ---- S^T = K Q^T (exact products, fp32 accumulation) ----
     f16x sacc;
@@ -435,6 +437,24 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
         pl[r >> 3][r & 7] = (f16)(p - (float)p16);
     }
     l += __shfl_xor(l, 32, 64);
+
+    // ---- V tile through LDS (rows padded by 16 bytes) ----
+    f16 *vt = &vtile[w][0];
+#pragma unroll
+    for (int u = 0; u < VR; u++) {
+        const int pc = u * 64 + lane;
+        *(u32x4 *)(vt + (pc / VP) * (HD + 8) + 8 * (pc % VP)) = vraw[u];
+    }
+    // (a wavefront's LDS accesses complete in order: no wait or barrier)
+    h8 vb[DT][2];
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const int key = 16 * s + 8 * (e >> 2) + 4 * hf + (e & 3);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) vb[dt][s][e] = vt[key * (HD + 8) + 32 * dt + ln];
+        }
 
     // ---- O = P V: A = P (value + remainder) straight from the accumulators ----
     f16x o[DT];
