@@ -164,7 +164,20 @@ typedef struct {
  * (n_layer x n_seq_max x n_ctx positions), the activation buffers for
  * n_ubatch tokens, and the logits buffer (n_batch rows).  Nothing is
  * allocated afterwards (the article's worst-case reservation, step 7 / 13b).
- * Returns NULL on invalid parameters or allocation failure. */
+ * Returns NULL on invalid parameters or allocation failure.
+ *
+ * Environment switches, read here and applied to every context of the
+ * process from then on (tuning and measurement aids; the defaults are the
+ * paths the library is validated on):
+ *   DECODE_GEMM_F16=1     ubatches of more than 64 tokens take f16 GEMM
+ *                         operands (weights f16(d*q), activations f16): about
+ *                         1.65x faster prefill, but at the 8B shape the
+ *                         logits move about 3.5e-2 from the exact result
+ *   DECODE_GEMM_SKINNY=0  ubatches of at most 32 tokens use the tiled GEMM
+ *                         on every matrix (same exact operands)
+ *   DECODE_PREFILL_ATTN=splitk  prefill attention through the split-K
+ *                         decode kernels instead of the flash kernel
+ *   DECODE_STEP_KERNEL=1  see dec_set_step_kernel */
 dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *p);
 
 /* Runs n prompt tokens of one sequence, continuing at seq_pos_max(seq)+1
