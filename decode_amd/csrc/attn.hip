@@ -36,6 +36,7 @@
 //                            its accumulators hold for one dim (2-byte loads
 //                            that 32 lanes turn into one 64-byte row segment).
 // The block's two wavefronts are then combined into one chunk partial.
+#include "../../include/decode.h"
 #include "common.h"
 #include "kernels.h"
 #include "q8.h"
@@ -707,5 +708,8 @@ bool launch_attention(const AttnArgs &a, int T, hipStream_t s) {
 }
 
 int attention_chunk(int kvtype, int hd) { return chunk_for(kvtype, hd); }
+
+static_assert(CH == 64 && CHM == 64 && 1024 * CH == DEC_MAX_CTX,
+              "the public context limit is 1024 chunks of every attention kernel");
 
 bool attention_codes_rows(int kvtype, int hd) { return kvtype == T_Q8_0 && mfma_path(kvtype, hd); }

@@ -78,6 +78,17 @@ struct Mem {
         else LOGE("device allocation of %zu bytes failed", bytes);
         return p;
     }
+    // Returns one allocation of this owner before the others.
+    void drop(void *p) {
+        if (!p) return;
+        for (size_t i = 0; i < owned.size(); i++)
+            if (owned[i] == p) {
+                if (custom) a.free(p, a.ud);
+                else (void)hipFree(p);
+                owned.erase(owned.begin() + (long)i);
+                return;
+            }
+    }
     void release() {
         for (void *p : owned) {
             if (custom) a.free(p, a.ud);
@@ -192,6 +203,11 @@ static bool valid_hparams(const dec_hparams &h) {
     if (h.kvtype != DEC_F32 && h.kvtype != DEC_F16 && h.kvtype != DEC_Q8_0) return false;
     if (h.n_embd % 32 || (h.n_head * h.head_dim) % 32) return false;
     if (h.wtype != DEC_F32 && h.n_ff % 32) return false;
+    // the decode mat-vec holds a whole input row in LDS: every K of a
+    // quantized matrix (d, H*hd, n_ff) is at most MV_KMAX elements
+    if (h.wtype != DEC_F32 &&
+        (h.n_embd > DEC_MAX_ROW || h.n_head * h.head_dim > DEC_MAX_ROW || h.n_ff > DEC_MAX_ROW))
+        return false;
     if (!(h.rms_eps >= 0.f) || !(h.rope_base > 0.f)) return false;
     return true;
 }
@@ -264,6 +280,7 @@ extern "C" dec_model *dec_model_load(const dec_hparams *hp, const dec_weights *w
              ld.vec(w->ffn_norm[l], d, &L.ffn_norm);
     }
     if (ok) HIP_OK(hipStreamSynchronize(m->stream), ok = false);
+    m->mem.drop(ld.stage);   // host weights are staged during the load only
     if (!ok) {
         LOGE("dec_model_load failed");
         m->mem.release();
@@ -497,6 +514,7 @@ extern "C" dec_model *dec_model_load_gguf(const char *path, int32_t kvtype, cons
              vec(layer_name(l, "ffn_norm"), &L.ffn_norm);
     }
     if (ok) HIP_OK(hipStreamSynchronize(s), ok = false);
+    m->mem.drop(stage);   // the file's tensors pass through it during the load only
     if (!ok) {
         LOGE("dec_model_load_gguf failed");
         m->mem.release();
@@ -624,9 +642,13 @@ struct dec_ctx {
     uint32_t *step_sync = nullptr;     // its barrier memory
     uint32_t step_n0 = 0;              // grid barriers of earlier launches
     bool step_ran = false;             // the last decode call ran the step kernel
+    bool step_unchecked = false;       // ... and its failure word has not been read yet
+    int step_seq = -1;                 // the sequence that step advanced
 };
 
 thread_local LaunchProbe g_launch_probe;
+
+static int step_settle(dec_ctx *c);
 
 enum { SEG_ALL = 0, SEG_PRE = 1, SEG_MID = 2, SEG_POST = 3 };
 static bool emit(const dec_ctx *c) { return c->seg_req == SEG_ALL || c->seg_req == c->seg_cur; }
@@ -795,6 +817,12 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
     if (n_ubatch > n_batch) n_ubatch = n_batch;
     const uint32_t n_seq = p.n_seq_max ? p.n_seq_max : 1;
     if (n_seq > 256) {
+        delete c;
+        return nullptr;
+    }
+    // split-K attention keeps at most 1024 chunks of a row's positions
+    if (n_ctx > (uint32_t)DEC_MAX_CTX) {
+        LOGE("dec_ctx_new: n_ctx %u above the supported %d positions", n_ctx, DEC_MAX_CTX);
         delete c;
         return nullptr;
     }
@@ -1137,6 +1165,7 @@ static void reset_outputs(dec_ctx *c, int n_out) {
 extern "C" int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int32_t seq,
                                int32_t output_all) {
     if (!c || !tokens || n <= 0 || n > c->n_batch || seq < 0 || seq >= c->n_seq) return -1;
+    if (step_settle(c) != 0) return -3;
     const int V = c->m->hp.n_vocab;
     for (int i = 0; i < n; i++)
         if (tokens[i] < 0 || tokens[i] >= V) {
@@ -1206,8 +1235,31 @@ static hipGraphExec_t capture_step(dec_ctx *c, int n, int seg) {
     return ex;
 }
 
+// After a step-kernel launch: reads the kernel's failure word (a bounded
+// grid-barrier wait gave up).  On failure the step is undone: its position
+// is free again (its cache row holds no valid K / V), its outputs are
+// dropped, and the barrier memory is cleared for the next launch.  Returns
+// 0, or -3 once for the failed step.
+static int step_settle(dec_ctx *c) {
+    if (!c->step_unchecked) return 0;
+    c->step_unchecked = false;
+    uint32_t fail = 0;
+    HIP_OK(hipMemcpyAsync(&fail, c->step_sync + STEP_SYNC_FAIL, 4, hipMemcpyDeviceToHost, c->s), return -3);
+    HIP_OK(hipStreamSynchronize(c->s), return -3);
+    if (!fail) return 0;
+    LOGE("decode step kernel: a grid barrier timed out; the step is rolled back");
+    if (c->step_seq >= 0 && c->pos_max[c->step_seq] >= 0) c->pos_max[c->step_seq]--;
+    c->step_n0 = 0;
+    c->step_ran = false;
+    reset_outputs(c, 0);
+    HIP_OK(hipMemsetAsync(c->step_sync, 0, STEP_SYNC_WORDS * 4, c->s), return -3);
+    HIP_OK(hipStreamSynchronize(c->s), return -3);
+    return -3;
+}
+
 extern "C" int32_t dec_decode(dec_ctx *c, const int32_t *tokens, const int32_t *seq_ids, int32_t n) {
     if (!c || !tokens || !seq_ids || n <= 0 || n > c->n_seq || n > c->Tmax) return -1;
+    if (step_settle(c) != 0) return -3;
     const int V = c->m->hp.n_vocab;
     std::vector<char> seen(c->n_seq, 0);
     for (int i = 0; i < n; i++) {
@@ -1241,6 +1293,8 @@ extern "C" int32_t dec_decode(dec_ctx *c, const int32_t *tokens, const int32_t *
         }
         c->step_n0 += step_barriers(c->m->hp.n_layer);
         c->step_ran = true;
+        c->step_unchecked = true;
+        c->step_seq = seq_ids[0];
         c->pos_max[seq_ids[0]]++;
         c->st.n_decode_calls++;
         reset_outputs(c, 1);
@@ -1294,7 +1348,7 @@ static int resolve_row(const dec_ctx *c, int i) {
 }
 
 extern "C" const float *dec_get_logits(dec_ctx *c, int32_t i) {
-    if (!c) return nullptr;
+    if (!c || step_settle(c) != 0) return nullptr;
     const int r = resolve_row(c, i);
     if (r < 0) return nullptr;
     const size_t V = (size_t)c->m->hp.n_vocab;
@@ -1309,31 +1363,26 @@ extern "C" const float *dec_get_logits(dec_ctx *c, int32_t i) {
 }
 
 static bool fetch_amax(dec_ctx *c) {
+    if (step_settle(c) != 0) return false;
     if (c->amax_fetched) return true;
     c->host_amax.resize(c->n_out);
     HIP_OK(hipMemcpyAsync(c->host_amax.data(), c->amax, (size_t)c->n_out * 4, hipMemcpyDeviceToHost, c->s),
            return false);
     HIP_OK(hipStreamSynchronize(c->s), return false);
     c->amax_fetched = true;
-    if (c->step_ran && c->host_amax[0] < 0) {
-        // a bounded wait of the step kernel gave up: clean barrier state for the next step
-        LOGE("decode step kernel: a grid barrier timed out; the step's results are invalid");
-        c->step_n0 = 0;
-        HIP_OK(hipMemsetAsync(c->step_sync, 0, STEP_SYNC_WORDS * 4, c->s), return true);
-        HIP_OK(hipStreamSynchronize(c->s), return true);
-    }
     return true;
 }
 
 extern "C" int32_t dec_argmax(dec_ctx *c, int32_t i) {
-    if (!c) return -1;
+    if (!c || step_settle(c) != 0) return -1;
     const int r = resolve_row(c, i);
     if (r < 0 || !fetch_amax(c)) return -1;
     return c->host_amax[r];
 }
 
 extern "C" int32_t dec_argmax_all(dec_ctx *c, int32_t *out, int32_t cap) {
-    if (!c || c->n_out <= 0) return 0;
+    if (!c || step_settle(c) != 0) return -1;
+    if (c->n_out <= 0) return 0;
     if (!out || cap < c->n_out) return -1;
     if (!fetch_amax(c)) return -1;
     memcpy(out, c->host_amax.data(), (size_t)c->n_out * 4);
@@ -1410,6 +1459,7 @@ static int32_t sampler_run(dec_sampler *s, const float *row, int V, hipStream_t 
 
 extern "C" int32_t dec_sampler_sample(dec_sampler *s, dec_ctx *c, int32_t i) {
     if (!s || !c) return -1;
+    if (step_settle(c) != 0) return -3;
     const int r = resolve_row(c, i);
     if (r < 0) return -1;
     const int V = c->m->hp.n_vocab;
@@ -1457,6 +1507,7 @@ extern "C" int32_t dec_seq_pos_max(const dec_ctx *c, int32_t seq) {
 
 extern "C" int32_t dec_seq_clear(dec_ctx *c, int32_t seq) {
     if (!c || seq < 0 || seq >= c->n_seq) return -1;
+    (void)step_settle(c);   // a failed step's rollback does not matter to a cleared sequence
     c->pos_max[seq] = -1;
     return 0;
 }

@@ -24,10 +24,13 @@
 // Optional prologue: RMSNorm of the f32 residual row (sum of squares reduced
 // over the block, then x * rstd * g rounded to f16), so the normalization of
 // the article's per-layer graph costs no extra launch.
+#include "../../include/decode.h"
 #include "common.h"
 #include "epilogue.h"
 #include "kernels.h"
 #include "mvcore.h"
+
+static_assert(MV_KMAX == DEC_MAX_ROW, "the public row limit is the mat-vec's LDS image");
 
 namespace {
 

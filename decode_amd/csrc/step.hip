@@ -725,14 +725,7 @@ DEV void attn_phase(const StepArgs &a, const StepLayer &Ly, int pos, int seq, ui
 
 // ---- the step ------------------------------------------------------------------
 // The argument block lives in device memory; each phase re-reads the fields
-// it uses (scalar loads through a pointer the compiler cannot track), so no
-// argument stays in registers across the whole step.
-DEV const StepArgs *launder(const StepArgs *p) {
-#ifdef LAUNDER
-    asm volatile("" : "+s"(p));
-#endif
-    return p;
-}
+// it uses, so no argument stays in registers across the whole step.
 
 template <int WT, int HD>
 __global__ __launch_bounds__(NT) void k_step(const StepArgs *ap, uint32_t n0) {
@@ -749,16 +742,16 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs *ap, uint32_t n0) {
     uint32_t *const sync = ap->sync;
     const int n_layer = ap->n_layer;
     Pre<WT> pf;
-    embed_phase(*launder(ap), tok, sm);
+    embed_phase(*ap, tok, sm);
     wait_vm();
     {
-        const StepArgs &a = *launder(ap);
+        const StepArgs &a = *ap;
         mv_prefetch<WT>(a.layers[0].wqkv, a.S_qkv, PAIR_ADJ, pf);
     }
     grid_barrier(sync, n0, nbar, sh);
     for (int l = 0; l < n_layer; l++) {
         {
-            const StepArgs &a = *launder(ap);
+            const StepArgs &a = *ap;
             const StepLayer &Ly = a.layers[l];
             MvIn in;
             in.x32 = a.x;
@@ -769,17 +762,17 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs *ap, uint32_t n0) {
         wait_vm();
         grid_barrier(sync, n0, nbar, sh);
         {
-            const StepArgs &a = *launder(ap);
+            const StepArgs &a = *ap;
             attn_phase<HD>(a, a.layers[l], pos, seq, sm, sh);
         }
         wait_vm();
         {
-            const StepArgs &a = *launder(ap);
+            const StepArgs &a = *ap;
             mv_prefetch<WT>(a.layers[l].wo, a.S_o, PAIR_ADJ, pf);
         }
         grid_barrier(sync, n0, nbar, sh);
         {
-            const StepArgs &a = *launder(ap);
+            const StepArgs &a = *ap;
             const StepLayer &Ly = a.layers[l];
             MvIn io;
             io.xh = a.o;
@@ -788,12 +781,12 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs *ap, uint32_t n0) {
         }
         wait_vm();
         {
-            const StepArgs &a = *launder(ap);
+            const StepArgs &a = *ap;
             mv_prefetch<WT>(a.layers[l].wgu, a.S_gu, PAIR_GU, pf);
         }
         grid_barrier(sync, n0, nbar, sh);
         {
-            const StepArgs &a = *launder(ap);
+            const StepArgs &a = *ap;
             const StepLayer &Ly = a.layers[l];
             MvIn ig;
             ig.x32 = a.x;
@@ -803,12 +796,12 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs *ap, uint32_t n0) {
         }
         wait_vm();
         {
-            const StepArgs &a = *launder(ap);
+            const StepArgs &a = *ap;
             mv_prefetch<WT>(a.layers[l].wdown, a.S_down, PAIR_ADJ, pf);
         }
         grid_barrier(sync, n0, nbar, sh);
         {
-            const StepArgs &a = *launder(ap);
+            const StepArgs &a = *ap;
             const StepLayer &Ly = a.layers[l];
             MvIn ih;
             ih.xh = a.h;
@@ -817,7 +810,7 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs *ap, uint32_t n0) {
         }
         wait_vm();
         {
-            const StepArgs &a = *launder(ap);
+            const StepArgs &a = *ap;
             if (l + 1 < n_layer)
                 mv_prefetch<WT>(a.layers[l + 1].wqkv, a.S_qkv, PAIR_ADJ, pf);
             else
@@ -826,7 +819,7 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs *ap, uint32_t n0) {
         grid_barrier(sync, n0, nbar, sh);
     }
     {
-        const StepArgs &a = *launder(ap);
+        const StepArgs &a = *ap;
         MvIn iout;
         iout.x32 = a.x;
         iout.g = a.out_norm;
@@ -836,7 +829,7 @@ __global__ __launch_bounds__(NT) void k_step(const StepArgs *ap, uint32_t n0) {
     wait_vm();
     grid_barrier(sync, n0, nbar, sh);
     if (blockIdx.x == 0) {
-        const StepArgs &a = *launder(ap);
+        const StepArgs &a = *ap;
         Amax am;
         for (int b = tid; b < (int)gridDim.x; b += NT) amax_take(am, ldcf(a.bmax + b), (int)ldc32(a.bidx + b));
 #pragma unroll

@@ -40,6 +40,13 @@ extern "C" {
  * fixed-size blocks sharing one scale (step 2c). */
 typedef enum { DEC_F32 = 0, DEC_F16 = 1, DEC_Q8_0 = 2, DEC_Q4_0 = 3 } dec_type;
 
+/* Shape limits.  With Q8_0 / Q4_0 weights every matrix row (n_embd,
+ * n_head * head_dim, n_ff) holds at most DEC_MAX_ROW elements: a decode step
+ * keeps one whole input row on chip.  A context holds at most DEC_MAX_CTX
+ * positions per sequence (split-K attention takes at most 1024 chunks of 64
+ * positions).  Larger shapes are rejected at load / context creation. */
+enum { DEC_MAX_ROW = 16384, DEC_MAX_CTX = 65536 };
+
 /* Hyper-parameters (the article's step 4: embedding length, block count,
  * feed-forward length, head count, KV head count, RoPE frequency base).
  * wtype applies to every 2-D matrix (F32, Q8_0 or Q4_0); kvtype is the
@@ -47,8 +54,9 @@ typedef enum { DEC_F32 = 0, DEC_F16 = 1, DEC_Q8_0 = 2, DEC_Q4_0 = 3 } dec_type;
  * typed key / value cache, here one type for both; each cached head row is
  * coded in 32-element Q8_0 blocks as it is appended, from the fp32 K / V
  * values, and attention reads code * scale).  Quantized weight types need
- * n_embd, n_ff and n_head*head_dim to be multiples of 32; head_dim must be
- * 64, 128 or 256, and n_head a multiple of n_head_kv. */
+ * n_embd, n_ff and n_head*head_dim to be multiples of 32 and at most
+ * DEC_MAX_ROW; head_dim must be 64, 128 or 256, and n_head a multiple of
+ * n_head_kv with at most 8 query heads per KV head. */
 typedef struct {
     int32_t n_layer, n_embd, n_head, n_head_kv, head_dim, n_ff, n_vocab;
     float   rms_eps;     /* 1e-5 */
@@ -105,8 +113,10 @@ enum { DEC_T_TOK_EMBD = 0, DEC_T_OUTPUT = 1, DEC_T_WQ = 2, DEC_T_WK = 3, DEC_T_W
 int64_t dec_model_tensor_blocks(const dec_model *m, int32_t tensor_id, int32_t layer,
                                 void *dst, size_t cap);
 
-/* Frees the model.  When contexts created from it are still alive, the
- * weights are released together with the last of them. */
+/* Frees the model (the caller owns what the load entry returned, article
+ * step 2a, where a half-built model is freed before nullptr is returned).
+ * When contexts created from it are still alive, the weights are released
+ * together with the last of them. */
 void dec_model_free(dec_model *m);
 
 /* ---- GGUF v3 model files (article steps 2b-2c and its GGUF reference
@@ -145,7 +155,7 @@ dec_model *dec_model_load_gguf(const char *path, int32_t kvtype, const dec_alloc
 int32_t dec_model_save_gguf(const dec_model *m, const char *path);
 
 /* Context parameters (article step 7).  n_ctx: positions per sequence,
- * rounded up to a multiple of 256 (0 -> 4096).  n_batch: most tokens one
+ * rounded up to a multiple of 256 (0 -> 4096), at most DEC_MAX_CTX.  n_batch: most tokens one
  * prefill call may take (0 -> n_ctx, clamped to n_ctx).  n_ubatch: most
  * tokens run through the layers at once (0 -> 512, clamped to n_batch).
  * n_seq_max: independent sequences, each with its own n_ctx cells
@@ -283,8 +293,10 @@ void dec_sampler_free(dec_sampler *s);
  * seq_pos_max, KV-cache appendix). */
 int32_t dec_seq_pos_max(const dec_ctx *c, int32_t seq);
 
-/* Forgets every cached position of a sequence.  Returns 0, or -1 for a bad
- * seq. */
+/* Forgets every cached position of a sequence: the memory module's cells
+ * of that sequence are free again, and its next token starts at position 0
+ * (KV-cache appendix: seq_pos_max decides where a batch continues).
+ * Returns 0, or -1 for a bad seq. */
 int32_t dec_seq_clear(dec_ctx *c, int32_t seq);
 
 /* Counters since creation (the article's "graphs reused" count, step 13b). */
@@ -319,7 +331,9 @@ int32_t dec_set_probe(dec_ctx *c, int32_t role, int32_t layer);
 int32_t dec_get_probe(dec_ctx *c, double *total_ms, int64_t *count);
 
 /* Decode steps are captured as HIP graphs and replayed (on, the default) or
- * launched kernel by kernel (off).  Returns the previous setting. */
+ * launched kernel by kernel (off): the article's graph reuse (step 13b,
+ * can_reuse / graph_reuse_disable) as a switch.  Returns the previous
+ * setting. */
 int32_t dec_set_use_graphs(dec_ctx *c, int32_t on);
 
 /* One-token decode steps (dec_decode with n = 1) as one persistent kernel:
@@ -335,17 +349,27 @@ int32_t dec_set_use_graphs(dec_ctx *c, int32_t on);
  * DECODE_STEP_KERNEL=1 turns the default on.  It is used only while
  * graphs are on and no probe role other than DEC_K_STEP is set.  Results
  * agree with the per-layer kernels within rounding (the attention merges
- * its partial sums in another order).  If a wait inside the kernel times out
- * (blocks not co-resident), the step's greedy token reads -1, its logits are
- * undefined, and the next step starts from clean barrier state.
+ * its partial sums in another order).  Every wait inside the kernel is
+ * bounded.  If one times out (blocks not co-resident), the step failed: the
+ * next call on the context that reads results or runs work (dec_get_logits
+ * returns NULL, dec_argmax / dec_argmax_all -1, dec_sampler_sample,
+ * dec_decode and dec_prefill -3) reports it once and undoes the step (the
+ * sequence's position returns to what it was before, so the cache row it
+ * wrote is free again, and the call's outputs are dropped); barrier state is
+ * reset, and later calls work normally.
  * on: 1 use, 0 do not use, -1 query.  Returns the setting before the call
  * (0 or 1), or -1 when the context cannot use the kernel (nothing changes). */
 int32_t dec_set_step_kernel(dec_ctx *c, int32_t on);
 
+/* Frees a context: its KV cache, work buffers, captured graphs and (if it
+ * made one) its stream, everything reserved at creation (article step 7).
+ * Waits for the context's queued work first. */
 void dec_ctx_free(dec_ctx *c);
 
-/* Log sink: level 0 debug, 1 info, 2 warning, 3 error.  NULL restores the
- * default (errors to stderr). */
+/* Log sink: level 0 debug, 1 info, 2 warning, 3 error (the library's form
+ * of the LLAMA_LOG_* messages the article's code emits, e.g. the load and
+ * decode error reports of steps 2a and 11).  Process-wide.  NULL restores
+ * the default (errors to stderr). */
 void dec_set_log_callback(void (*cb)(int level, const char *msg, void *ud), void *ud);
 
 /* Library build string (target, version). */
