@@ -117,6 +117,7 @@ def lib() -> C.CDLL:
         "dec_sampler_reset": (None, [vp]),
         "dec_sampler_draws": (i64, [vp]),
         "dec_sampler_free": (None, [vp]),
+        "dec_sample_row_noalloc": (i32, [vp, vp, i32, C.c_uint64, vp, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -281,6 +282,28 @@ class Sampler:
 
     def __del__(self):
         self.close()
+
+
+NOALLOC_MAX_VOCAB = 32768
+
+
+def sample_row_noalloc(logits, token_out, hist=(), draw=0, stream=None, top_k=40, top_p=1.0, min_p=0.0,
+                       temp=1.0, repeat_penalty=1.0, penalty_last_n=64, seed=0) -> int:
+    """dec_sample_row_noalloc: enqueue one draw of the chain on ``logits``
+    (float32 numpy array or contiguous torch tensor, host or device); the token
+    is written to ``token_out`` (an int32 torch tensor on the device).  Returns
+    the call's status (0 enqueued)."""
+    p = SamplerParams(top_k, top_p, min_p, temp, repeat_penalty, penalty_last_n, seed)
+    h = np.ascontiguousarray(np.asarray(hist, np.int32))
+    if isinstance(logits, np.ndarray):
+        row = np.ascontiguousarray(logits, np.float32)
+        rp, n = row.ctypes.data, row.size
+    else:
+        rp, n = _ptr(logits), logits.numel()
+    if str(token_out.dtype) != "torch.int32" or not token_out.is_contiguous():
+        raise ValueError("token_out must be a contiguous int32 tensor")
+    return int(lib().dec_sample_row_noalloc(C.byref(p), h.ctypes.data if h.size else None, h.size, int(draw),
+                                            rp, n, token_out.data_ptr(), stream))
 
 
 class Context:

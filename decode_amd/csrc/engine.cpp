@@ -29,7 +29,7 @@ int attention_chunk(int kvtype, int hd);
 static void (*g_log_cb)(int, const char *, void *) = nullptr;
 static void *g_log_ud = nullptr;
 
-static void logf(int level, const char *fmt, ...) {
+void log_message(int level, const char *fmt, ...) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
@@ -40,9 +40,9 @@ static void logf(int level, const char *fmt, ...) {
     else if (level >= 3)
         fprintf(stderr, "libdecode: %s\n", buf);
 }
-#define LOGE(...) logf(3, __VA_ARGS__)
-#define LOGW(...) logf(2, __VA_ARGS__)
-#define LOGI(...) logf(1, __VA_ARGS__)
+#define LOGE(...) log_message(3, __VA_ARGS__)
+#define LOGW(...) log_message(2, __VA_ARGS__)
+#define LOGI(...) log_message(1, __VA_ARGS__)
 
 #define HIP_OK(expr, onfail)                                                          \
     do {                                                                              \

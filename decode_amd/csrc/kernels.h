@@ -215,6 +215,9 @@ struct SampleArgs {
 };
 bool launch_sample(const float *logits, const SampleArgs &a, hipStream_t s);
 
+// The library's log sink (level 0 debug .. 3 error; see dec_set_log_callback).
+void log_message(int level, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
 
 // ---- one decode step of one token as a single persistent kernel ----------
 // One layer's weights and f16 cache as the step kernel reads them (a device

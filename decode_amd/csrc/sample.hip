@@ -29,8 +29,11 @@
 //      those sums.
 // The draw is u = top 24 bits of SplitMix64(seed, draw index) (Steele et al.
 // 2014), so a run is reproducible from (seed, number of draws).
+#include "../../include/decode.h"
 #include "common.h"
 #include "kernels.h"
+
+#include <mutex>
 
 namespace {
 
@@ -471,4 +474,122 @@ bool launch_sample(const float *logits, const SampleArgs &a, hipStream_t s) {
         return false;
     launch(k_sample, dim3(1), dim3(1024), 0, s, logits, a);
     return true;
+}
+
+// ---- the sampler chain without allocation (dec_sample_row_noalloc) -----------
+// Device memory the call needs beyond its inputs and outputs -- the penalty
+// window, and the device copy of a logits row given in host memory -- lives
+// in one file-scope array, so the call allocates nothing.  Each GPU the
+// library runs on holds its own copy until the process ends; host code reaches
+// it only through the address hipGetSymbolAddress returns for the current
+// device (the array's name is a host-side stand-in, not a device address).
+namespace {
+constexpr size_t NA_HIST_BYTES = (size_t)SH_MAX * 4;                 // window, int32
+constexpr size_t NA_SCRATCH_BYTES = NA_HIST_BYTES + (size_t)SV_MAX * 4;   // + one logits row
+static_assert(NA_HIST_BYTES % 256 == 0, "the row starts 256-byte aligned");
+static_assert(SV_MAX == DEC_NOALLOC_MAX_VOCAB, "public limit of the no-allocation sampler");
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[NA_SCRATCH_BYTES];
+
+namespace {
+constexpr int NA_MAX_DEV = 64;
+std::mutex g_na_mu;
+uint8_t *g_na_ptr[NA_MAX_DEV] = {};
+
+// The scratch array's device address on the current device (looked up once
+// per device, with that device current), or null.
+uint8_t *na_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NA_MAX_DEV) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(g_na_mu);
+    if (!g_na_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            log_message(3, "dec_sample_row_noalloc: hipGetSymbolAddress failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+            return nullptr;
+        }
+        g_na_ptr[dev] = (uint8_t *)p;
+    }
+    return g_na_ptr[dev];
+}
+
+// Device-visible address of p (device memory, or pinned host memory mapped
+// into the device's address space), or null when the device cannot use it.
+const void *na_device_view(const void *p, bool *is_host) {
+    hipPointerAttribute_t at;
+    *is_host = true;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (at.type == hipMemoryTypeDevice) {
+        *is_host = false;
+        return p;
+    }
+    return at.devicePointer;
+}
+}  // namespace
+
+
+extern "C" int32_t dec_sample_row_noalloc(const dec_sampler_params *p, const int32_t *hist, int32_t n_hist,
+                                          uint64_t draw, const float *logits, int32_t n_vocab,
+                                          int32_t *token_out, void *hip_stream) {
+    if (!p || p->top_k < 1 || p->top_k > SK_MAX || !(p->top_p > 0.0f && p->top_p <= 1.0f) ||
+        !(p->min_p >= 0.0f && p->min_p < 1.0f) || !(p->repeat_penalty >= 1.0f) || p->penalty_last_n < 0 ||
+        p->penalty_last_n > SH_MAX || p->temp != p->temp)
+        return -1;
+    if (!logits || !token_out || n_vocab < p->top_k || n_hist < 0 || n_hist > SH_MAX || (n_hist > 0 && !hist))
+        return -1;
+    if (n_vocab > SV_MAX) {
+        log_message(3, "dec_sample_row_noalloc: n_vocab %d above the %d logits its static buffer holds", n_vocab,
+                    SV_MAX);
+        return -4;
+    }
+    bool out_host = false, row_host = false;
+    int32_t *out = (int32_t *)na_device_view(token_out, &out_host);
+    if (!out) {
+        log_message(3, "dec_sample_row_noalloc: token_out is neither device memory nor mapped host memory");
+        return -1;
+    }
+    (void)na_device_view(logits, &row_host);
+    uint8_t *sc = na_scratch();
+    if (!sc) return -3;
+    hipStream_t st = (hipStream_t)hip_stream;
+    SampleArgs a;
+    const int w = n_hist < p->penalty_last_n ? n_hist : p->penalty_last_n;
+    a.n_hist = p->repeat_penalty != 1.0f ? w : 0;
+    a.n_vocab = n_vocab;
+    a.top_k = p->top_k;
+    a.top_p = p->top_p;
+    a.min_p = p->min_p;
+    a.temp = p->temp;
+    a.repeat_penalty = p->repeat_penalty;
+    a.seed = p->seed;
+    a.draw = draw;
+    a.hist = (const int32_t *)sc;
+    a.out = out;
+    if (a.n_hist > 0 && hipMemcpyAsync(sc, hist + (n_hist - a.n_hist), (size_t)a.n_hist * 4, hipMemcpyDefault,
+                                       st) != hipSuccess) {
+        (void)hipGetLastError();
+        return -3;
+    }
+    const float *row = logits;
+    if (row_host) {
+        if (hipMemcpyAsync(sc + NA_HIST_BYTES, logits, (size_t)n_vocab * 4, hipMemcpyHostToDevice, st) != hipSuccess) {
+            (void)hipGetLastError();
+            return -3;
+        }
+        row = (const float *)(sc + NA_HIST_BYTES);
+    }
+    if (!launch_sample(row, a, st)) return -1;
+    if (hipGetLastError() != hipSuccess) return -3;
+    return 0;
 }

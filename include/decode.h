@@ -289,6 +289,30 @@ int64_t dec_sampler_draws(const dec_sampler *s);
 
 void dec_sampler_free(dec_sampler *s);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the chain
+ * of dec_sampler_sample_row as one stateless call that allocates nothing.
+ * p: the chain (same ranges as dec_sampler_new).  hist: the n_hist (0..64)
+ * most recently accepted tokens, oldest first, host or device memory; the
+ * penalty looks at the last penalty_last_n of them.  draw: the index of this
+ * draw in the seed's stream (dec_sampler_draws before the equivalent
+ * dec_sampler_sample_row call).  logits: n_vocab floats (top_k <= n_vocab <=
+ * DEC_NOALLOC_MAX_VOCAB), device memory or host memory.  token_out: one
+ * int32 in device memory or in mapped pinned host memory; the token is
+ * written there by the kernel.  Enqueued on hip_stream (NULL: the null
+ * stream) without synchronizing: the token is valid once the stream reaches
+ * this point.  The window and a host row are staged in a fixed device buffer
+ * of the library (about 128 KiB per GPU, held until the process ends), so
+ * calls on one GPU must be ordered on one stream: calls that overlap on one
+ * GPU race on that buffer.  Nothing is kept between calls; the caller keeps
+ * the history and the draw count.  Returns 0 when enqueued, -1 for bad
+ * arguments (token_out the device cannot write, ranges), -4 when n_vocab
+ * exceeds DEC_NOALLOC_MAX_VOCAB (the reason is logged), -3 on a device
+ * error. */
+enum { DEC_NOALLOC_MAX_VOCAB = 32768 };
+int32_t dec_sample_row_noalloc(const dec_sampler_params *p, const int32_t *hist, int32_t n_hist, uint64_t draw,
+                               const float *logits, int32_t n_vocab, int32_t *token_out, void *hip_stream);
+
 /* Largest cached position of a sequence, -1 when empty (the memory module's
  * seq_pos_max, KV-cache appendix). */
 int32_t dec_seq_pos_max(const dec_ctx *c, int32_t seq);

@@ -64,3 +64,30 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 src = open(os.path.join(dirpath, f), errors="ignore").read()
                 assert not re.search(r"\boracle\b|liboracle|orc_", src), f
+
+
+def test_shape_limits_rejected_before_the_device(dec):
+    L = dec.lib()
+    w = dec.Weights()
+    wide = dec.Hparams(2, 16384 + 32, 4, 4, 64, 512, 1024, 1e-5, 1e4, dec.Q4_0, dec.F16)
+    assert not L.dec_model_load(C.byref(wide), C.byref(w), None, None)
+    wide_ff = dec.Hparams(2, 256, 4, 4, 64, 16384 + 32, 1024, 1e-5, 1e4, dec.Q8_0, dec.F16)
+    assert not L.dec_model_load(C.byref(wide_ff), C.byref(w), None, None)
+    gqa16 = dec.Hparams(2, 256, 16, 1, 64, 512, 1024, 1e-5, 1e4, dec.Q8_0, dec.F16)
+    assert not L.dec_model_load(C.byref(gqa16), C.byref(w), None, None)
+
+
+def test_noalloc_sampler_rejects_arguments_before_the_device(dec):
+    L = dec.lib()
+    p = dec.SamplerParams(40, 1.0, 0.0, 1.0, 1.0, 64, 0)
+    buf = (C.c_float * 8)()
+    tok = (C.c_int32 * 1)()
+    addr, taddr = C.addressof(buf), C.addressof(tok)
+    assert L.dec_sample_row_noalloc(None, None, 0, 0, addr, 100, taddr, None) == -1
+    assert L.dec_sample_row_noalloc(C.byref(p), None, 0, 0, None, 100, taddr, None) == -1
+    assert L.dec_sample_row_noalloc(C.byref(p), None, 0, 0, addr, 100, None, None) == -1
+    assert L.dec_sample_row_noalloc(C.byref(p), None, 0, 0, addr, 39, taddr, None) == -1      # below top_k
+    assert L.dec_sample_row_noalloc(C.byref(p), None, 3, 0, addr, 100, taddr, None) == -1     # hist missing
+    assert L.dec_sample_row_noalloc(C.byref(p), None, 65, 0, addr, 100, taddr, None) == -1
+    big = dec.NOALLOC_MAX_VOCAB + 1
+    assert L.dec_sample_row_noalloc(C.byref(p), None, 0, 0, addr, big, taddr, None) == -4
