@@ -83,33 +83,71 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(hp, weights_dev, prompt, n_prompt_tokens, n_decode_tokens):
-    """The oracle (f64 build, as it stands) on a bounded sample of the same
-    workload: n_prompt_tokens prompt tokens, then n_decode_tokens decode
-    steps; decode tokens/s over the decode steps."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _omp_set_threads(n: int) -> None:
+    """Thread count of the oracle's later parallel regions (libgomp of this process)."""
+    import ctypes
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
+def cpu_baseline(hp, weights_dev, prompt, n_prompt_tokens, n_decode_tokens, n_decode_1t, gpu_ctx):
+    """The oracle (its fp32 build, as it stands) on a bounded sample of the
+    same workload: n_prompt_tokens prompt tokens, then greedy decode steps,
+    timed with all host threads and then with one thread."""
     import numpy as np
 
     import oracle
     host = {}
     for k, v in weights_dev.items():
         host[k] = [t.cpu().numpy() for t in v] if isinstance(v, list) else v.cpu().numpy()
-    om = oracle.Model(hp, host, "f64")
+    om = oracle.Model(hp, host, "f32")
     del host
-    ctx = oracle.Context(om, 1, n_prompt_tokens + n_decode_tokens + 1)
+    ctx = oracle.Context(om, 1, n_prompt_tokens + n_decode_tokens + n_decode_1t + 2)
     for t in prompt[:n_prompt_tokens - 1]:
         ctx.eval(0, int(t), want_logits=False)
     lg = ctx.eval(0, int(prompt[n_prompt_tokens - 1]))
-    tok = oracle.argmax(lg)
-    t0 = time.perf_counter()
-    for _ in range(n_decode_tokens):
-        lg = ctx.eval(0, tok)
-        tok = oracle.argmax(lg)
-    dt = time.perf_counter() - t0
+    tok = oracle.argmax(lg, "f32")
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    _omp_set_threads(threads)
+
+    def run(n):
+        nonlocal tok
+        t0 = time.perf_counter()
+        for _ in range(n):
+            lg = ctx.eval(0, tok)
+            tok = oracle.argmax(lg, "f32")
+        return time.perf_counter() - t0
+    dt = run(n_decode_tokens)
+    _omp_set_threads(1)
+    dt1 = run(n_decode_1t)
+    _omp_set_threads(threads)
+    c_end = n_prompt_tokens + n_decode_tokens + n_decode_1t
     return {"value": n_decode_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"f64 oracle, same weights: {n_prompt_tokens}-token prompt then "
-                      f"{n_decode_tokens} greedy decode steps at context <= "
-                      f"{n_prompt_tokens + n_decode_tokens} ({dt:.1f} s)"}
+            "value_1_thread": n_decode_1t / dt1, "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "sample": f"fp32 oracle build, same weights: {n_prompt_tokens}-token prompt, then "
+                      f"{n_decode_tokens} greedy decode steps on {threads} threads ({dt:.1f} s) and "
+                      f"{n_decode_1t} on 1 thread ({dt1:.1f} s), at contexts {n_prompt_tokens + 1}.."
+                      f"{c_end}; the GPU line decodes at context ~{gpu_ctx:.0f} (attention is about "
+                      f"{100 * attention_share(hp, gpu_ctx):.0f}% of a step's multiply-adds there)"}
+
+
+def attention_share(hp, ctx_len):
+    """Fraction of a decode step's multiply-adds spent in attention at ctx_len."""
+    d, L, F, V = hp["n_embd"], hp["n_layer"], hp["n_ff"], hp["n_vocab"]
+    qd, kd = hp["n_head"] * hp["head_dim"], hp["n_head_kv"] * hp["head_dim"]
+    lin = L * (d * (qd + 2 * kd) + qd * d + 3 * F * d) + V * d
+    att = L * 2 * qd * ctx_len
+    return att / (lin + att)
 
 
 def kv_bytes_per_elem(kvtype: int) -> float:
@@ -326,7 +364,11 @@ def main():
     ap.add_argument("--workload", default="8b_q4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prompt", type=int, default=3)
-    ap.add_argument("--cpu-decode", type=int, default=30)
+    ap.add_argument("--cpu-decode", type=int, default=24, help="oracle decode steps on all host threads")
+    ap.add_argument("--cpu-decode-1t", type=int, default=2, help="oracle decode steps on one thread")
+    ap.add_argument("--reps", type=int, default=5, help="timed repetitions (prefill + steps decode steps)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the attainable stream-read / MFMA measurements")
     ap.add_argument("--no-kv-q8", action="store_true",
                     help="skip the leg that reruns the decode loop with a Q8_0 KV cache")
     ap.add_argument("--kv-q8-steps", type=int, default=128)
@@ -362,7 +404,7 @@ def main():
         else:
             batched_workload(args, dec, torch, W, hp, log)
         return
-    steps, warm = args.steps, args.warmup
+    steps, warm, reps = args.steps, args.warmup, max(1, args.reps)
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     sp = stream.cuda_stream
@@ -390,12 +432,14 @@ def main():
         torch.cuda.empty_cache()
 
     prompt = synth.prompt(hp["n_vocab"], n_prompt, 2000 + W["seed"] % 1000)
-    n_sampled = 64                      # decode steps run with the sampler chain after the timed loop
+    n_probe = 16                        # decode steps per probed kernel role, after the timed loops
+    roles = [("qkv", dec.K_QKV), ("attention", dec.K_ATTN), ("o", dec.K_WO), ("gate_up", dec.K_FFN_GU),
+             ("down", dec.K_FFN_DOWN), ("output", dec.K_OUTPUT)]
+    n_sampled = 64                      # decode steps run with the sampler chain
     n_step_leg = 64                     # decode steps through the one-launch step kernel
-    n_ctx = n_prompt + steps + warm + n_sampled + 32 + n_step_leg + 8   # + the 32 attention-probe steps
+    n_ctx = n_prompt + max(steps, warm) + n_probe * len(roles) + n_sampled + n_step_leg + 32
     ctx = dec.Context(model, n_ctx=n_ctx, n_batch=n_prompt, n_ubatch=W["n_ubatch"], stream=sp)
     probe_layer = hp["n_layer"] // 2
-    ctx.set_probe(dec.K_FFN_GU, probe_layer)
 
     # warm-up: prefill + decode steps (captures the decode graph)
     assert ctx.prefill(prompt, 0) == 0
@@ -403,35 +447,78 @@ def main():
     for _ in range(warm):
         assert ctx.decode([tok], [0]) == 0
         tok = ctx.argmax(0)
-    ctx.clear(0)
-    ctx.set_probe(dec.K_FFN_GU, probe_layer)
     torch.cuda.synchronize()
     log("warm-up done")
 
-    # timed prefill
-    t0 = time.perf_counter()
-    assert ctx.prefill(prompt, 0) == 0
-    tok = ctx.argmax(-1)
-    prefill_s = time.perf_counter() - t0
-    pf_probe = ctx.probe()
-    ctx.set_probe(dec.K_FFN_GU, probe_layer)
-
-    # timed decode: the generation loop, one token per step
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        rc = ctx.decode([tok], [0])
-        if rc != 0:
-            raise RuntimeError(f"dec_decode returned {rc}")
-        tok = ctx.argmax(0)
-    torch.cuda.synchronize()
-    decode_s = time.perf_counter() - t0
-    dc_probe = ctx.probe()
+    # timed repetitions, no probe set: each clears the cache, prefills the
+    # prompt (timed to its greedy token on the host), then times exactly
+    # `steps` decode steps, each a decode call + greedy token readback
+    pf_s, dc_s = [], []
+    for r in range(reps):
+        ctx.clear(0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        assert ctx.prefill(prompt, 0) == 0
+        tok = ctx.argmax(-1)
+        pf_s.append(time.perf_counter() - t0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            rc = ctx.decode([tok], [0])
+            if rc != 0:
+                raise RuntimeError(f"dec_decode returned {rc}")
+            tok = ctx.argmax(0)
+        torch.cuda.synchronize()
+        dc_s.append(time.perf_counter() - t0)
+        log(f"rep {r}: prefill {n_prompt / pf_s[-1]:.0f} tok/s, decode {steps / dc_s[-1]:.1f} tok/s")
     st = ctx.stats()
-    log(f"prefill {n_prompt / prefill_s:.0f} tok/s, decode {steps / decode_s:.1f} tok/s")
+    decode_s = sorted(dc_s)[len(dc_s) // 2]
+    prefill_s = sorted(pf_s)[len(pf_s) // 2]
 
+    # probe pass (outside the timed repetitions): each kernel role of the middle
+    # layer timed live over n_probe further decode steps, then one more prefill
+    # with its gate/up GEMM and its attention probed
+    per_kernel = {}
+    alg0 = algorithmic(hp, 0, 0)
+    F, d, V = hp["n_ff"], hp["n_embd"], hp["n_vocab"]
+    qd, kd = hp["n_head"] * hp["head_dim"], hp["n_head_kv"] * hp["head_dim"]
+    bb = block_bytes(hp["wtype"])
+    role_bytes = {"qkv": (qd + 2 * kd) * d * bb, "o": d * qd * bb, "gate_up": 2 * F * d * bb,
+                  "down": d * F * bb, "output": V * d * bb}
+    dc_probe = None
+    for name, role in roles:
+        ctx.set_probe(role, probe_layer)
+        c0 = ctx.pos_max(0) + 1
+        for _ in range(n_probe):
+            assert ctx.decode([tok], [0]) == 0
+            tok = ctx.argmax(0)
+        pr = ctx.probe()
+        if not pr or not pr[1]:
+            continue
+        avg = pr[0] / 1e3 / pr[1]
+        nb = role_bytes.get(name)
+        if name == "attention":
+            nb = (c0 + (n_probe - 1) / 2.0) * 2 * kd * kv_bytes_per_elem(hp["kvtype"])
+        ach = nb / avg / 1e9
+        per_kernel[name] = {"avg_us": round(avg * 1e6, 2), "bytes": int(nb), "achieved_GBs": round(ach, 1),
+                            "frac": round(ach / HBM_PEAK_GBS, 4), "launches": pr[1]}
+        if name == "gate_up":
+            dc_probe = pr
+    ctx.set_probe(-1, 0)
+    pf_probe = pf_attn = None
+    ctx2 = dec.Context(model, n_ctx=n_prompt + 8, n_batch=n_prompt, n_ubatch=W["n_ubatch"], stream=sp)
+    for role in (dec.K_FFN_GU, dec.K_ATTN):
+        ctx2.clear(0)
+        ctx2.set_probe(role, probe_layer)
+        assert ctx2.prefill(prompt, 0) == 0
+        if role == dec.K_FFN_GU:
+            pf_probe = ctx2.probe()
+        else:
+            pf_attn = ctx2.probe()
+    ctx2.close()
+    log("probe pass done")
 
-    # the sampler chain in the generation loop (after, and outside, the timed region):
+    # the sampler chain in the generation loop (outside the timed region):
     # penalty over the last 64 tokens, top-k 40, top-p 0.95, min-p 0.05, temperature 0.8
     sprm = dict(top_k=40, top_p=0.95, min_p=0.05, temp=0.8, repeat_penalty=1.1, penalty_last_n=64, seed=1234)
     smp = dec.Sampler(**sprm)
@@ -457,17 +544,7 @@ def main():
                "note": "us_per_call = one dec_sampler_sample on a resident logits row: history upload, "
                        "the k_sample kernel, token download and stream synchronisation"}
     log(f"sampled decode {n_sampled / sampled_s:.1f} tok/s, sampler call {call_s * 1e6:.1f} us")
-
-    # attention (split-K partials + merge) of the probed layer after the
-    # sampled steps, over a few more steps outside the timed regions
-    ctx.set_probe(dec.K_ATTN, probe_layer)
-    n_attn = 32
-    for _ in range(n_attn):
-        assert ctx.decode([tok], [0]) == 0
-        tok = ctx.argmax(0)
-    at_probe = ctx.probe()
-    attn_ctx = ctx.pos_max(0) + 1 - (n_attn - 1) / 2.0
-    ctx.set_probe(-1, 0)
+    tok = ctx.argmax(0)
 
     # the same generation loop through the persistent one-launch step kernel
     # (opt-in; reported beside the default per-layer graph)
@@ -492,7 +569,7 @@ def main():
         ctx.set_probe(-1, 0)
         ctx.step_kernel(0)
         sk_ctx = ctx.pos_max(0) + 1 - (n_step_leg - 4 - 1) / 2.0
-        sk_bytes = algorithmic(hp, 0, 0)["weight_bytes"] + algorithmic(hp, 0, 0)["kv_row_bytes"] * sk_ctx
+        sk_bytes = alg0["weight_bytes"] + alg0["kv_row_bytes"] * sk_ctx
         sk_us = sk_probe[0] * 1e3 / sk_probe[1] if sk_probe and sk_probe[1] else None
         step_leg = {"decode_tokens_per_s": round((n_step_leg - 4) / sk_s, 2), "steps": n_step_leg - 4,
                     "kernel_us": round(sk_us, 1) if sk_us else None,
@@ -502,17 +579,19 @@ def main():
                     "note": "whole decode step as one cooperative launch with grid barriers between the "
                             "layer stages (dec_set_step_kernel); kernel_us from events around the launch"}
         log(f"step kernel: {step_leg['decode_tokens_per_s']} tok/s, {step_leg['kernel_us']} us per launch")
+    ctx.close()
 
     kv_q8 = None
     if model_q8 is not None:
         kv_q8 = kv_q8_leg(dec, torch, model_q8, hp, prompt, n_ctx, W["n_ubatch"], sp, warm,
                           args.kv_q8_steps, probe_layer, log)
-        kv_q8["f16_attention"] = attention_roofline(hp, 1, at_probe, attn_ctx)
+        if "attention" in per_kernel:
+            kv_q8["f16_attention"] = per_kernel["attention"]
         model_q8.close()
+    model.close()
 
     alg = algorithmic(hp, n_prompt, steps)
-    F, d = hp["n_ff"], hp["n_embd"]
-    gu_bytes = 2 * F * d * block_bytes(hp["wtype"])
+    gu_bytes = role_bytes["gate_up"]
     gu_avg_s = dc_probe[0] / 1e3 / max(dc_probe[1], 1) if dc_probe and dc_probe[1] else None
     roofline = None
     if gu_avg_s:
@@ -534,7 +613,10 @@ def main():
         ach = flops / avg / 1e12
         pf_roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                    "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
-                   "kernel": "k_gemm_mfma (gate/up, ubatch 512)", "avg_us": round(avg * 1e6, 1)}
+                   "kernel": "k_gemm_mfma (gate/up, ubatch 512)", "avg_us": round(avg * 1e6, 1),
+                   "launches_timed": pf_probe[1]}
+        if pf_attn and pf_attn[1]:
+            pf_roof["attention_avg_us_per_ubatch"] = round(pf_attn[0] * 1e3 / pf_attn[1], 1)
     step_gbs = alg["token_bytes"] / (decode_s / steps) / 1e9
 
     if args.copy_calibration:
@@ -546,12 +628,30 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    ceilings = None
+    if not args.no_ceilings:
+        rd = dec.measure_stream_read(2 << 30, 10, sp)
+        mf = dec.measure_mfma_f16(20000, 5, sp)
+        ceilings = {"hbm_stream_read_GBs": round(rd, 1), "mfma_f16_TFLOPs": round(mf, 1),
+                    "decode_step_frac_of_attainable": round(step_gbs / rd, 4),
+                    "note": "dec_measure_stream_read (2 GiB read with 16-byte loads) and "
+                            "dec_measure_mfma_f16 (independent 32x32x16 f16 MFMAs, 8 wavefronts per CU), "
+                            "measured in this run"}
+        if roofline:
+            roofline["frac_of_attainable"] = round(roofline["achieved"] / rd, 4)
+        if pf_roof:
+            pf_roof["frac_of_attainable"] = round(pf_roof["achieved"] / mf, 4)
+        log(f"ceilings: stream read {rd:.0f} GB/s, f16 MFMA {mf:.0f} TFLOP/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores")
-        cpu = cpu_baseline(hp, weights, prompt, args.cpu_prompt, args.cpu_decode)
+        cpu = cpu_baseline(hp, weights, prompt, args.cpu_prompt, args.cpu_decode, args.cpu_decode_1t,
+                           alg["mean_ctx"])
         del weights
 
+    wname = "Q8_0" if hp["wtype"] == synth.Q8_0 else "Q4_0"
+    kvname = {0: "f32", 1: "f16", 2: "Q8_0"}[hp["kvtype"]]
     out = {
         "metric": METRIC,
         "value": round(steps / decode_s, 2),
@@ -565,14 +665,22 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "8B-shape decoder, Q4_0 weights N(0,0.02), f16 KV cache, batch 1: "
-                               f"{n_prompt}-token random prompt in ubatches of {W['n_ubatch']}, "
-                               f"then {steps} greedy decode steps",
+        "repetitions": {"n": reps, "decode_tokens_per_s": [round(steps / t, 2) for t in dc_s],
+                        "decode_min_tokens_per_s": round(steps / max(dc_s), 2),
+                        "decode_max_tokens_per_s": round(steps / min(dc_s), 2),
+                        "prefill_tokens_per_s": [round(n_prompt / t, 1) for t in pf_s],
+                        "note": "value and prefill_tokens_per_s are the medians; no probe is set during "
+                                "these repetitions"},
+        "config": {"workload": f"{args.workload}: {hp['n_layer']}-layer decoder (d {d}, {hp['n_head']} heads / "
+                               f"{hp['n_head_kv']} KV heads of {hp['head_dim']}, FFN {F}, vocab {V}), {wname} "
+                               f"weights N(0,0.02), {kvname} KV cache, batch 1: {n_prompt}-token random prompt "
+                               f"in ubatches of {W['n_ubatch']}, then {steps} greedy decode steps",
                    "n_layer": hp["n_layer"], "d_model": d, "heads": hp["n_head"],
                    "kv_heads": hp["n_head_kv"], "head_dim": hp["head_dim"], "ffn": F,
-                   "vocab": hp["n_vocab"], "prefill_tokens": n_prompt, "n_ubatch": W["n_ubatch"],
+                   "vocab": V, "prefill_tokens": n_prompt, "n_ubatch": W["n_ubatch"],
                    "mean_decode_context": alg["mean_ctx"]},
-        "precision": {"weights": "q4_0", "activations": "f16", "accumulate": "f32", "kv": "f16"},
+        "precision": {"weights": wname.lower(), "activations": "f16 value + f16 remainder", "accumulate": "f32",
+                      "kv": kvname},
         "prefill_tokens_per_s": round(n_prompt / prefill_s, 1),
         "prefill_ms": round(prefill_s * 1e3, 2),
         "decode_step_hbm": {"bytes_per_token": int(alg["token_bytes"]), "achieved_GBs": round(step_gbs, 1),
@@ -582,12 +690,17 @@ def main():
                          "frac": round(alg["prefill_flops"] / prefill_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
         "roofline": roofline,
         "prefill_roofline": pf_roof,
+        "decode_kernels": {"layer": probe_layer, "steps_each": n_probe, "kernels": per_kernel,
+                           "note": "per kernel role of one layer (output: the final projection), timed live "
+                                   "in a probe pass after the timed repetitions; bytes are algorithmic"},
+        "ceilings": ceilings,
         "graph_replays": st["n_graph_replays"],
         "sampler": sampler,
         "kv_q8_0": kv_q8,
         "step_kernel": step_leg,
         "cpu_baseline": cpu,
     }
+    torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
 
 

@@ -118,6 +118,8 @@ def lib() -> C.CDLL:
         "dec_sampler_draws": (i64, [vp]),
         "dec_sampler_free": (None, [vp]),
         "dec_sample_row_noalloc": (i32, [vp, vp, i32, C.c_uint64, vp, i32, vp, vp]),
+        "dec_measure_stream_read": (i32, [C.c_size_t, i32, vp, C.POINTER(C.c_double)]),
+        "dec_measure_mfma_f16": (i32, [i32, i32, vp, C.POINTER(C.c_double)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -282,6 +284,24 @@ class Sampler:
 
     def __del__(self):
         self.close()
+
+
+def measure_stream_read(nbytes: int = 2 << 30, reps: int = 10, stream=None) -> float:
+    """dec_measure_stream_read: attainable HBM read GB/s on the current device."""
+    v = C.c_double()
+    rc = lib().dec_measure_stream_read(nbytes, reps, stream, C.byref(v))
+    if rc != 0:
+        raise DecodeError(f"dec_measure_stream_read returned {rc}")
+    return float(v.value)
+
+
+def measure_mfma_f16(iters: int = 20000, reps: int = 5, stream=None) -> float:
+    """dec_measure_mfma_f16: attainable f16 MFMA TFLOP/s on the current device."""
+    v = C.c_double()
+    rc = lib().dec_measure_mfma_f16(iters, reps, stream, C.byref(v))
+    if rc != 0:
+        raise DecodeError(f"dec_measure_mfma_f16 returned {rc}")
+    return float(v.value)
 
 
 NOALLOC_MAX_VOCAB = 32768

@@ -354,6 +354,21 @@ int32_t dec_set_probe(dec_ctx *c, int32_t role, int32_t layer);
  * Returns 0, or -1 when no probe is set. */
 int32_t dec_get_probe(dec_ctx *c, double *total_ms, int64_t *count);
 
+/* Attainable ceilings of the current device, the measured counterparts of
+ * the datasheet peaks that roofline fractions are taken against (the
+ * article's point that prefill loads the compute units and decode loads
+ * memory, KV-cache appendix, made quantitative).  Measurement aids: each
+ * allocates, runs and frees its own buffers on hip_stream and synchronizes.
+ *   dec_measure_stream_read: GB/s of a plain streaming read of `bytes`
+ *     (>= 1 MiB; use several times the 256 MiB last-level cache) with 16-byte
+ *     loads, averaged over `reps` passes after one untimed pass.
+ *   dec_measure_mfma_f16: TFLOP/s of independent v_mfma_f32_32x32x16_f16 on
+ *     register operands, 8 wavefronts per compute unit, `iters` loop
+ *     iterations of 8 instructions each, over `reps` launches.
+ * Return 0, -1 bad arguments, -2 allocation failure, -3 device error. */
+int32_t dec_measure_stream_read(size_t bytes, int32_t reps, void *hip_stream, double *gbs);
+int32_t dec_measure_mfma_f16(int32_t iters, int32_t reps, void *hip_stream, double *tflops);
+
 /* Decode steps are captured as HIP graphs and replayed (on, the default) or
  * launched kernel by kernel (off): the article's graph reuse (step 13b,
  * can_reuse / graph_reuse_disable) as a switch.  Returns the previous
