@@ -16,10 +16,11 @@
 // (transposed, keys permuted as below) are staged in LDS once for all four
 // wavefronts (the next tile's loads are in flight meanwhile), then each
 // wavefront runs
-//   S^T[key][q] = K Q^T     v_mfma_f32_32x32x16_f16, 2 key tiles x hd/16 steps
+//   S^T[key][q] = K Q^T     v_mfma_f32_32x32x16_f16, 2 key tiles x hd/16 steps,
+//                           Q as f16 value + f16 remainder (two MFMAs a step)
 //   online softmax per query column (a lane holds 16 keys of one query; the
 //   other 16 are in lane l^32), base-2 with log2(e)/sqrt(hd) folded into Q
-//   O^T[d][q] += V^T P^T    4 key steps x hd/32 dim tiles
+//   O^T[d][q] += V^T P^T    4 key steps x hd/32 dim tiles, P as value + remainder
 // The P operand comes straight from the S^T accumulators: for key step s the
 // lane's eight values r = 8s'..8s'+7 are keys 16s + 8(e>>2) + 4h + (e&3)
 // (h = lane/32, e = 0..7), so V^T is stored with key k at column
@@ -67,8 +68,10 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
     const int n_keys = min(n_keys_tile, kbeg + a.chunk);    // keys of this block: kbeg .. n_keys-1
     const float qscale = 1.4426950408889634f / sqrtf((float)HD);
 
-    // Q^T operand: lane supplies Q[q][16 ks + 8 (lane/32) + e]
-    h8 qf[KS];
+    // Q^T operand: lane supplies Q[q][16 ks + 8 (lane/32) + e], as an f16
+    // value qf and its f16 rounding remainder ql (about 22 significant bits:
+    // one f16 would put an error of 2^-11 of each score into the softmax)
+    h8 qf[KS], ql[KS];
     {
         const float *qr = a.q + ((size_t)(q_ok ? q_t : 0) * a.H + head) * HD + 8 * (lane >> 5);
 #pragma unroll
@@ -78,10 +81,13 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
                 lo = *(const float4 *)(qr + 16 * ks);
                 hi = *(const float4 *)(qr + 16 * ks + 4);
             }
-            qf[ks][0] = (f16)(lo.x * qscale); qf[ks][1] = (f16)(lo.y * qscale);
-            qf[ks][2] = (f16)(lo.z * qscale); qf[ks][3] = (f16)(lo.w * qscale);
-            qf[ks][4] = (f16)(hi.x * qscale); qf[ks][5] = (f16)(hi.y * qscale);
-            qf[ks][6] = (f16)(hi.z * qscale); qf[ks][7] = (f16)(hi.w * qscale);
+            const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float y = v[e] * qscale;
+                qf[ks][e] = (f16)y;
+                ql[ks][e] = (f16)(y - (float)qf[ks][e]);
+            }
         }
     }
 
@@ -156,6 +162,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
             for (int ks = 0; ks < KS; ks++) {
                 const h8 kf = *(const h8 *)&Ks[mt * 32 + (lane & 31)][16 * ks + 8 * (lane >> 5)];
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[mt], 0, 0, 0);
+                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, ql[ks], s[mt], 0, 0, 0);
             }
         }
         // ---- causal mask + online softmax over this query column ----
@@ -172,14 +179,16 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
         const float m_new = fmaxf(m_run, mt_max);
         const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
         float psum = 0.f;
-        h8 pf[4];
+        h8 pf[4], pl[4];   // P as f16 value + remainder, like Q
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const float p = m_new == -INFINITY ? 0.f : exp2f(s[mt][r] - m_new);
                 psum += p;
-                pf[mt * 2 + (r >> 3)][r & 7] = (f16)p;
+                const f16 ph = (f16)p;
+                pf[mt * 2 + (r >> 3)][r & 7] = ph;
+                pl[mt * 2 + (r >> 3)][r & 7] = (f16)(p - (float)ph);
             }
         psum += __shfl_xor(psum, 32, 64);
         l_run = l_run * alpha + psum;
@@ -195,6 +204,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
             for (int dt = 0; dt < DT; dt++) {
                 const h8 vf = *(const h8 *)&Vt[dt * 32 + (lane & 31)][16 * ss + 8 * (lane >> 5)];
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ss], acc[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pl[ss], acc[dt], 0, 0, 0);
             }
         }
     }
