@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libdecode.so")
 BUILD = os.path.join(HERE, "_build")
 
-SOURCES = ["engine.cpp", "gguf.cpp", "matvec.hip", "gemm.hip", "attn.hip", "flash.hip", "misc.hip", "sample.hip", "step.hip", "ceiling.hip"]
+SOURCES = ["engine.cpp", "gguf.cpp", "matvec.hip", "gemm.hip", "gemm_dl.hip", "attn.hip", "flash.hip", "misc.hip", "sample.hip", "step.hip", "ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

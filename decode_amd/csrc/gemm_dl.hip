@@ -1,0 +1,453 @@
+// gemm_dl.hip -- ubatch GEMM Y = X W^T with direct-to-LDS operand loads (gfx950).
+//
+// The arithmetic is that of k_gemm_mfma's exact form: weights enter the
+// matrix cores as their integer codes (exact in f16), activations as an f16
+// value and its f16 rounding remainder, and per 32-wide quant block the four
+// v_mfma_f32_32x32x16_f16 of a 32x32 tile (2 k-halves x value/remainder)
+// fill a temporary tile that is scaled by the row's block scale and added to
+// the fp32 result, C += d[n][kb] * T.  With the same K split the results are
+// bitwise those of k_gemm_mfma.
+//
+// What changes is how operands reach the matrix cores.  Every byte goes from
+// global memory straight into LDS (global_load_lds_dwordx4, no register
+// staging, no wait at a store): per K block a stage holds the block tile's
+// activation values and remainders (128 tokens x 64 bytes each), its raw
+// codes (256 rows x 16 or 32 bytes) and its scales (256 x 4 bytes, the f16
+// in the low half).  NS
+// stages form a ring; K block kb+NS-1 is requested while kb is computed, and
+// a wavefront waits only for its own loads of block kb (a constant vmcnt:
+// past the last K block the last one is requested again) before the one
+// barrier per K block.  Each stage is its own LDS array, so the compiler sees
+// that reading one stage does not depend on the loads into another.
+// The codes are converted to f16 operands when read (each wavefront converts
+// the rows it uses).  Activation rows are 4 chunks of 16 bytes; chunk c of
+// token m sits at slot 4m + (c ^ swz(m)), which spreads the 16-byte reads of
+// 16 consecutive tokens over distinct bank groups; the direct loads write
+// slots in lane order, so each lane simply fetches the chunk its slot holds.
+//
+// Block: 256 threads, 256 features x 128 tokens; wavefront w covers features
+// 128 (w & 1) .. +127 (four 32-feature tiles a) and tokens 64 (w >> 1) .. +63
+// (two 32-token tiles b).  Operand layouts as in k_gemm_mfma: lane l supplies
+// A[l%32][8(l/32)+e] (tokens) and B[8(l/32)+e][l%32] (features); accumulator r
+// of lane l is C[(r/4)*8+(l/32)*4+r%4][l%32], so a lane's 16 accumulators of a
+// tile are 16 tokens of one feature and the block scale is one value per tile.
+// Feature tiles of one block tile share an XCD (round-robin block placement),
+// as in k_gemm_mfma; K splits write fp32 partial tiles summed in order by
+// k_gemm_splitk_sum.
+#include <type_traits>
+
+#include "common.h"
+#include "epilogue.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int DBN = 256;    // features per block
+constexpr int DBM = 128;    // tokens per block
+constexpr int DWN = 128;    // features per wavefront
+constexpr int DWM = 64;     // tokens per wavefront
+
+#define AS1 __attribute__((address_space(1)))
+#define AS3 __attribute__((address_space(3)))
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int WT>
+struct Geo {
+    static constexpr int CB = WT == T_Q4_0 ? 16 : 32;    // code bytes per row and K block
+    static constexpr int ACT = DBM * 64;                 // one activation part per K block
+    static constexpr int OFF_LO = ACT;
+    static constexpr int OFF_CODES = 2 * ACT;
+    static constexpr int OFF_SC = 2 * ACT + DBN * CB;
+    static constexpr int STAGE = OFF_SC + DBN * 4;      // a 2-byte direct load fills one dword per lane
+    // direct loads per wavefront and K block: 4 activation, 1 or 2 code, 1 scale
+    static constexpr int LOADS = 4 + DBN * CB / 4096 + 1;
+};
+
+// Slot of chunk c of token row m (see the header).
+DEV int swz(int m) { return ((m >> 1) ^ (m >> 3)) & 3; }
+
+DEV h2 magic_lo(uint32_t v) { return as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04010400u)); }
+DEV h2 magic_hi(uint32_t v) { return as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04030402u)); }
+
+// Q4_0: 8 bytes holding codes 8c..8c+7 (low nibbles) and 16+8c..16+8c+7 (high
+// nibbles) -> exact f16 values q - 8 of the two k-halves.
+DEV void q4_pair(u32x2 raw, h8 &k0, h8 &k1) {
+    const h2 off = h2{(f16)1032.f, (f16)1032.f};
+    const uint32_t l0 = raw.x & 0x0F0F0F0Fu, l1 = raw.y & 0x0F0F0F0Fu;
+    const uint32_t u0 = (raw.x >> 4) & 0x0F0F0F0Fu, u1 = (raw.y >> 4) & 0x0F0F0F0Fu;
+    const h2 a0 = magic_lo(l0) - off, a1 = magic_hi(l0) - off, a2 = magic_lo(l1) - off, a3 = magic_hi(l1) - off;
+    const h2 b0 = magic_lo(u0) - off, b1 = magic_hi(u0) - off, b2 = magic_lo(u1) - off, b3 = magic_hi(u1) - off;
+    k0 = h8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+    k1 = h8{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+}
+
+// Q8_0: 8 signed byte codes -> exact f16 values.
+DEV h8 q8_eight(u32x2 raw) {
+    const h2 off = h2{(f16)1152.f, (f16)1152.f};
+    const uint32_t w0 = raw.x ^ 0x80808080u, w1 = raw.y ^ 0x80808080u;
+    const h2 a0 = magic_lo(w0) - off, a1 = magic_hi(w0) - off, a2 = magic_lo(w1) - off, a3 = magic_hi(w1) - off;
+    return h8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+}
+
+// s_waitcnt with vmcnt(N), lgkmcnt(0), expcnt untouched (gfx9 encoding),
+// fenced against compiler reordering of memory accesses.
+template <int N>
+DEV void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+    asm volatile("" ::: "memory");
+}
+
+DEV void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Direct load of 16 bytes per lane from src into LDS at lds + 16 * lane, or
+// of 2 bytes into the low half of the dword at lds + 4 * lane (zero-extended;
+// both placements checked on the device); lds is wave-uniform.  Written as an instruction the
+// compiler does not interpret: it produces no register, and the loop's own
+// vmcnt waits order the LDS reads after it (the compiler, unable to tell the
+// stages apart, would otherwise wait for every load in flight before each
+// LDS read).  The asm sets m0 itself; the compiler uses m0 nowhere else in
+// these kernels (it is a reserved register that an asm clobber cannot name).
+DEV void dma16(const void *src, const void AS3 *lds) {
+    const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m) : "memory");
+}
+DEV void dma2(const void *src, const void AS3 *lds) {
+    const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(src), "s"(m) : "memory");
+}
+
+template <int WT, int EPI, bool SPLIT, int NS, int MF>
+__global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const uint16_t *Xh, const uint16_t *Xl,
+                                                                  int ldx, EpiArgs ep, int M, int pair_mode, int NT,
+                                                                  int nsplit, float *part) {
+    using G = Geo<WT>;
+    __shared__ __attribute__((aligned(16))) uint8_t S0[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t S1[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t S2[NS > 2 ? G::STAGE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t S3[NS > 3 ? G::STAGE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t S4[NS > 4 ? G::STAGE : 16];
+    static_assert(NS >= 3 && NS <= 5, "stages");
+
+    // block -> (feature tile, token tile, K split); the tiles of one feature
+    // tile share an XCD
+    const int mtiles = (M + DBM - 1) / DBM;
+    const int per_nt = mtiles * nsplit;
+    const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
+    const int nt = (j / per_nt) * 8 + xcd, rem = j % per_nt;
+    const int mtile = rem % mtiles, split = rem / mtiles;
+    if (nt >= NT) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n0 = nt * DBN, m0 = mtile * DBM;
+    const int nb_all = W.K >> 5, nb = nb_all / nsplit, kb0 = split * nb;
+    const int wn = (w & 1) * DWN, wm = (w >> 1) * DWM;
+
+    // ---- per-lane global sources of the direct loads (K block 0 of the range) ----
+    // activations: instructions j = w, w + 4 of each part cover slots 64j .. 64j+63
+    const uint16_t *xa[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int slot = 64 * (w + 4 * i) + lane, m = slot >> 2, c = (slot & 3) ^ swz(slot >> 2);
+        const int row = min(m0 + m, M - 1);            // rows past M repeat row M-1; their outputs are dropped
+        xa[0][i] = Xh + (size_t)row * ldx + (size_t)kb0 * 32 + c * 8;
+        xa[1][i] = Xl + (size_t)row * ldx + (size_t)kb0 * 32 + c * 8;
+    }
+    // codes: Q4_0 one row of 16 bytes per lane (rows 64w + lane); Q8_0 two
+    // instructions of 32 rows x 2 halves
+    const size_t row_bytes = WT == T_Q4_0 ? (size_t)(W.K >> 1) : (size_t)W.K;
+    const uint8_t *ca[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        if (WT == T_Q4_0) {
+            ca[i] = (const uint8_t *)W.qs + (size_t)(n0 + 64 * w + lane) * row_bytes + (size_t)kb0 * 16;
+        } else {
+            const int slot = 64 * (w + 4 * i) + lane, r = slot >> 1, half = slot & 1;
+            ca[i] = (const uint8_t *)W.qs + (size_t)(n0 + r) * row_bytes + (size_t)kb0 * 32 + half * 16;
+        }
+    }
+    const uint16_t *sa = W.d + (size_t)(n0 + 64 * w + lane) * nb_all + kb0;
+
+    auto stage_ptr = [&](auto sc) -> uint8_t * {
+        constexpr int s = decltype(sc)::value;
+        if constexpr (s == 0) return S0;
+        else if constexpr (s == 1) return S1;
+        else if constexpr (s == 2) return S2;
+        else if constexpr (s == 3) return S3;
+        else return S4;
+    };
+
+    // requests K block kb (clamped to the range) into stage s
+    auto issue = [&](auto sc, int kb) __attribute__((always_inline)) {
+        uint8_t *st = stage_ptr(sc);
+        const int k = min(kb, nb - 1);
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            dma16(xa[0][i] + (size_t)k * 32, (const void AS3 *)(st + 1024 * (w + 4 * i)));
+            dma16(xa[1][i] + (size_t)k * 32, (const void AS3 *)(st + G::OFF_LO + 1024 * (w + 4 * i)));
+        }
+        if (WT == T_Q4_0) {
+            dma16(ca[0] + (size_t)k * 16, (const void AS3 *)(st + G::OFF_CODES + 1024 * w));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+                dma16(ca[i] + (size_t)k * 32, (const void AS3 *)(st + G::OFF_CODES + 1024 * (w + 4 * i)));
+        }
+        dma2(sa + k, (const void AS3 *)(st + G::OFF_SC + 256 * w));
+    };
+
+    // MF = 32: 32x32 tiles, 4 feature x 2 token tiles per wavefront;
+    // MF = 16: 16x16 tiles, 8 x 4 (one v_mfma_f32_16x16x32_f16 covers a whole
+    // 32-wide quant block: each tile's block is a chain of two MFMAs)
+    constexpr int TA = DWN / MF, TB = DWM / MF, NR = MF == 32 ? 16 : 4;
+    typedef float accv __attribute__((ext_vector_type(NR)));
+    accv acc[TA][TB];
+#pragma unroll
+    for (int a = 0; a < TA; a++)
+#pragma unroll
+        for (int b = 0; b < TB; b++)
+#pragma unroll
+            for (int r = 0; r < NR; r++) acc[a][b][r] = 0.f;
+
+    // (each body is dependent on the lambda's argument, so only the variant
+    // this instance uses is compiled)
+    auto compute16 = [&](auto sc) __attribute__((always_inline)) {
+        if constexpr (MF == 16 && decltype(sc)::value >= 0) {
+        typedef float f4v __attribute__((ext_vector_type(4)));
+        const uint8_t *st = stage_ptr(sc);
+        const int g = lane >> 4;          // k group: this lane supplies k = 8g .. 8g+7
+        h8 xh[TB], xl[TB];
+#pragma unroll
+        for (int b = 0; b < TB; b++) {
+            const int m = wm + 16 * b + (lane & 15);
+            const int slot = 4 * m + (g ^ swz(m));
+            xh[b] = *(const h8 *)(st + 16 * slot);
+            xl[b] = *(const h8 *)(st + G::OFF_LO + 16 * slot);
+        }
+#pragma unroll
+        for (int a = 0; a < TA; a++) {
+            const int f = wn + 16 * a + (lane & 15);
+            h8 cf;
+            if (WT == T_Q4_0) {
+                // codes 8g .. 8g+7: the low (g < 2) or high (g >= 2) nibbles of
+                // bytes 8(g & 1) .. 8(g & 1)+7
+                const u32x2 raw = *(const u32x2 *)(st + G::OFF_CODES + 16 * f + 8 * (g & 1));
+                const int sh = (g >> 1) * 4;
+                const uint32_t v0 = (raw.x >> sh) & 0x0F0F0F0Fu, v1 = (raw.y >> sh) & 0x0F0F0F0Fu;
+                const h2 off = h2{(f16)1032.f, (f16)1032.f};
+                const h2 a0 = magic_lo(v0) - off, a1 = magic_hi(v0) - off, a2 = magic_lo(v1) - off,
+                         a3 = magic_hi(v1) - off;
+                cf = h8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+            } else {
+                cf = q8_eight(*(const u32x2 *)(st + G::OFF_CODES + 32 * f + 8 * g));
+            }
+            const float d = f16_bits_to_f32(*(const uint16_t *)(st + G::OFF_SC + 4 * f));
+#pragma unroll
+            for (int b = 0; b < TB; b++) {
+                f4v t = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[b], cf, f4v{}, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[b], cf, t, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc[a][b][r] += d * t[r];
+            }
+        }
+        }
+    };
+
+    auto compute32 = [&](auto sc) __attribute__((always_inline)) {
+        if constexpr (MF == 32 && decltype(sc)::value >= 0) {
+        const uint8_t *st = stage_ptr(sc);
+        // activation fragments: token tile b, k-half h, value / remainder
+        h8 xh[2][2], xl[2][2];
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+            const int m = wm + 32 * b + (lane & 31);
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int slot = 4 * m + ((2 * h + (lane >> 5)) ^ swz(m));
+                xh[b][h] = *(const h8 *)(st + 16 * slot);
+                xl[b][h] = *(const h8 *)(st + G::OFF_LO + 16 * slot);
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < 4; a++) {
+            const int f = wn + 32 * a + (lane & 31);
+            h8 c0, c1;
+            if (WT == T_Q4_0) {
+                q4_pair(*(const u32x2 *)(st + G::OFF_CODES + 16 * f + 8 * (lane >> 5)), c0, c1);
+            } else {
+                c0 = q8_eight(*(const u32x2 *)(st + G::OFF_CODES + 32 * f + 8 * (lane >> 5)));
+                c1 = q8_eight(*(const u32x2 *)(st + G::OFF_CODES + 32 * f + 16 + 8 * (lane >> 5)));
+            }
+            const float d = f16_bits_to_f32(*(const uint16_t *)(st + G::OFF_SC + 4 * f));
+#pragma unroll
+            for (int b = 0; b < 2; b++) {
+                f16x t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[b][0], c0, f16x{}, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[b][0], c0, t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[b][1], c1, t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[b][1], c1, t, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; r++) acc[a][b][r] += d * t[r];
+            }
+        }
+        }
+    };
+
+    // one step: K block kb is in stage S; wait for it, then refill the stage
+    // computed in the previous step with K block kb + NS - 1
+    auto step = [&](auto sc, int kb) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        wait_vm_lgkm0<(NS - 2) * G::LOADS>();
+        block_barrier();
+        issue(std::integral_constant<int, (s + NS - 1) % NS>{}, kb + NS - 1);
+        if constexpr (MF == 16) compute16(sc);
+        else compute32(sc);
+    };
+
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, 1);
+    if constexpr (NS > 3) issue(std::integral_constant<int, 2>{}, 2);
+    if constexpr (NS > 4) issue(std::integral_constant<int, 3>{}, 3);
+    // whole periods of NS steps; K blocks past the last are clamped re-reads
+    // whose stages are never computed
+    for (int kb = 0; kb < nb; kb += NS) {
+        step(std::integral_constant<int, 0>{}, kb);
+        if (kb + 1 < nb) step(std::integral_constant<int, 1>{}, kb + 1);
+        if (kb + 2 < nb) step(std::integral_constant<int, 2>{}, kb + 2);
+        if constexpr (NS > 3)
+            if (kb + 3 < nb) step(std::integral_constant<int, 3>{}, kb + 3);
+        if constexpr (NS > 4)
+            if (kb + 4 < nb) step(std::integral_constant<int, 4>{}, kb + 4);
+    }
+    // drain the requests past the last K block before the block can exit
+    wait_vm_lgkm0<0>();
+
+    // ---- epilogue.  MF = 32: lane holds feature n0 + wn + 32a + (lane & 31)
+    // and, in accumulator r, token m0 + wm + 32b + (r/4)*8 + (lane/32)*4 + r%4.
+    // MF = 16: feature n0 + wn + 16a + (lane & 15), token m0 + wm + 16b +
+    // 4(lane/16) + r. ----
+    const int fl = lane & (MF - 1);
+    auto tok_of = [&](int b, int r) __attribute__((always_inline)) {
+        return MF == 32 ? m0 + wm + 32 * b + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)
+                        : m0 + wm + 16 * b + 4 * (lane >> 4) + r;
+    };
+    if (SPLIT) {
+        const int N = W.N;
+#pragma unroll
+        for (int b = 0; b < TB; b++)
+#pragma unroll
+            for (int r = 0; r < NR; r++) {
+                const int m = tok_of(b, r);
+                if (m >= M) continue;
+                float *dst = part + ((size_t)split * M + m) * N + n0 + wn + fl;
+#pragma unroll
+                for (int a = 0; a < TA; a++) dst[MF * a] = acc[a][b][r];
+            }
+        return;
+    }
+#pragma unroll
+    for (int b = 0; b < TB; b++) {
+        if (EPI == EPI_STORE || EPI == EPI_RESID) {
+#pragma unroll
+            for (int r = 0; r < NR; r++) {
+                const int m = tok_of(b, r);
+                if (m >= M) continue;
+                float *y = ep.y + (size_t)m * ep.ldy + n0 + wn + fl;
+#pragma unroll
+                for (int a = 0; a < TA; a++) {
+                    if (EPI == EPI_STORE) y[MF * a] = acc[a][b][r];
+                    else y[MF * a] += acc[a][b][r];
+                }
+            }
+        } else if (pair_mode == PAIR_GU) {
+            // gate rows 64g .. 64g+31 and their up rows 64g+32 .. 64g+63: in
+            // feature tiles a and a + 32/MF of the same 64-row group
+            constexpr int UP = 32 / MF;
+#pragma unroll
+            for (int a = 0; a < TA; a++) {
+                if ((a / UP) % 2) continue;                      // an up tile
+                const int rr = n0 + wn + MF * a + fl;            // gate row
+                const int g = rr >> 6;
+#pragma unroll
+                for (int r = 0; r < NR; r++) {
+                    const int m = tok_of(b, r);
+                    if (m >= M) continue;
+                    epi_pair<EPI>(ep, m, (g << 5) + (rr & 31), rr, rr + 32, acc[a][b][r], acc[a + UP][b][r]);
+                }
+            }
+        } else {
+            // adjacent features f (even lane) and f+1 (odd lane): the even lane
+            // takes the first half of the pair's tokens, the odd lane the second
+            const bool odd = lane & 1;
+            constexpr int HR = NR / 2;
+#pragma unroll
+            for (int a = 0; a < TA; a++)
+#pragma unroll
+                for (int r = 0; r < HR; r++) {
+                    const float send = odd ? acc[a][b][r] : acc[a][b][r + HR];
+                    const float recv = __shfl_xor(send, 1, 64);
+                    const int rr = odd ? r + HR : r;
+                    const int m = tok_of(b, rr);
+                    const int f = n0 + wn + MF * a + (fl & ~1);
+                    const float va = odd ? recv : acc[a][b][r];
+                    const float vb = odd ? acc[a][b][r + HR] : recv;
+                    if (m < M) epi_pair<EPI>(ep, m, f >> 1, f, f + 1, va, vb);
+                }
+        }
+    }
+}
+
+template <int WT, int EPI, bool SPLIT>
+void launch_dl_ns(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                  int pair_mode, int S, float *part, hipStream_t s) {
+    const int NT = W.N / DBN, NT8 = (NT + 7) / 8 * 8;
+    const dim3 grid(NT8 * ((M + DBM - 1) / DBM) * S);
+    // ns: LDS stages, plus 10 for the 16x16x32 tiles
+    switch (ns) {
+    case 3: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
+    case 5: launch((k_gemm_dl<WT, EPI, SPLIT, 5, 32>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
+    case 13: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 16>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
+    case 14: launch((k_gemm_dl<WT, EPI, SPLIT, 4, 16>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
+    default: launch((k_gemm_dl<WT, EPI, SPLIT, 4, 32>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
+    }
+}
+
+template <int WT, int EPI>
+void launch_dl_epi(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                   int pair_mode, int S, float *ws, hipStream_t s) {
+    if (S > 1) {
+        launch_dl_ns<WT, EPI, true>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+        launch_splitk_sum(EPI, ws, S, W.N, M, ep, pair_mode, s);
+    } else {
+        launch_dl_ns<WT, EPI, false>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, 1, nullptr, s);
+    }
+}
+
+template <int WT>
+void launch_dl_wt(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                  int pair_mode, int S, float *ws, hipStream_t s) {
+    switch (ep.epi) {
+    case EPI_STORE: launch_dl_epi<WT, EPI_STORE>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_RESID: launch_dl_epi<WT, EPI_RESID>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_QKV: launch_dl_epi<WT, EPI_QKV>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_SWIGLU: launch_dl_epi<WT, EPI_SWIGLU>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    }
+}
+
+}  // namespace
+
+int gemm_dl_tile_features() { return DBN; }
+int gemm_dl_tile_tokens() { return DBM; }
+
+void launch_gemm_dl(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
+                    int M, int pair_mode, int S, float *ws, hipStream_t s) {
+    if (W.wtype == T_Q4_0)
+        launch_dl_wt<T_Q4_0>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+    else
+        launch_dl_wt<T_Q8_0>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+}

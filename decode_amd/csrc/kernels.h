@@ -141,6 +141,16 @@ bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
                  int T, float *ws, size_t ws_bytes, hipStream_t s);
 // Workspace launch_gemm uses for W at T tokens (0 when it does not split K).
 size_t gemm_workspace_bytes(const QMat &W, int T);
+// The direct-to-LDS form of the ubatch GEMM (gemm_dl.hip): a block tile of
+// gemm_dl_tile_features() x gemm_dl_tile_tokens(), `ns` LDS stages (3, 4 or
+// 5), K split S (fp32 partial tiles in ws, summed by launch_splitk_sum).
+void launch_gemm_dl(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
+                    int M, int pair_mode, int S, float *ws, hipStream_t s);
+int gemm_dl_tile_features();
+int gemm_dl_tile_tokens();
+// Sums S fp32 partial tiles [S][M][N] in split order and applies epilogue epi.
+void launch_splitk_sum(int epi, const float *ws, int S, int N, int M, const EpiArgs &ep, int pair_mode,
+                       hipStream_t s);
 // Number of compute units the GEMM grid is sized for (default 256).
 void gemm_set_num_cu(int n);
 

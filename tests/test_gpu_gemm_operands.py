@@ -113,3 +113,37 @@ def test_skinny_form_matches_tiles_and_oracle(dec, orc, wtype, monkeypatch):
         assert_logits_close(got[True][i], o_rows[i], f"skinny row {i}")
         ma, _ = logit_err(got[True][i], got[False][i])
         assert ma <= 1e-3, f"row {i}: skinny vs tiles {ma:.3e}"
+
+
+@pytest.mark.parametrize("wtype", [synth.Q4_0, synth.Q8_0])
+def test_direct_load_form_bitwise_equals_staged_tiles(dec, orc, wtype, monkeypatch):
+    """Ubatches of more than 64 tokens on matrices of whole 256-feature tiles
+    take the direct-to-LDS form (DECODE_GEMM_DL = 3, 4 or 5 stages on 32x32
+    tiles, 13 or 14 on 16x16 tiles; 0 keeps the register-staged tiles).  On
+    32x32 tiles both forms feed the matrix cores the same operands in the same
+    order and, at this shape, split K the same way (not at all), so every
+    logits row of a 300-token ubatch (token tiles of 128, 128 and a ragged 44)
+    is bitwise equal across them; the 16x16x32 MFMA sums a quant block in one
+    instruction, so there the rows agree to rounding.  All meet the oracle bar."""
+    hp = small_hp(wtype, synth.F16)
+    w = synth.weights_numpy(hp, 930 + wtype, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 300, 931)
+    oc = orc.Context(orc.Model(hp, w), 1, 512)
+    o_rows = {}
+    for i, t in enumerate(prompt):
+        r = oc.eval(0, int(t))
+        if i in ROWS:
+            o_rows[i] = r
+    gm = dec.Model(hp, w)
+    got = {}
+    for ns in ("0", "3", "4", "5", "13", "14"):
+        monkeypatch.setenv("DECODE_GEMM_DL", ns)
+        got[ns] = _rows(dec, gm, prompt, 300)[0]
+    monkeypatch.delenv("DECODE_GEMM_DL")
+    for i in ROWS:
+        for ns in ("3", "13"):
+            assert_logits_close(got[ns][i], o_rows[i], f"direct-load {ns} row {i}")
+        for ns in ("3", "4", "5"):
+            assert np.array_equal(got[ns][i], got["0"][i]), f"{ns} stages, row {i}"
+        for ns in ("13", "14"):
+            assert logit_err(got[ns][i], got["0"][i])[0] <= 1e-4, f"16x16 tiles ({ns}), row {i}"
