@@ -673,7 +673,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(QMat W, const uint16_t *Xh,
 int g_gemm_cu = 256;
 int g_gemm_f16w = 0;   // f16 operands for ubatches of more than 64 tokens (opt-in)
 int g_gemm_skinny = 1; // skinny form for ubatches of at most 32 tokens
-int g_gemm_dl = 3;     // direct-to-LDS form: LDS stages (+10: 16x16 tiles; 0: off)
+int g_gemm_dl = 23;    // direct-to-LDS form variant (0: off)
 
 bool mfma_shape(const QMat &W, int ldx) {
     return (W.wtype == T_Q4_0 || W.wtype == T_Q8_0) && W.N % BN == 0 && W.K % 32 == 0 && ldx % 8 == 0;
@@ -766,14 +766,17 @@ void launch_f32_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int l
 
 // Direct-to-LDS form (gemm_dl.hip): ubatches of more than 64 tokens with the
 // exact operands, feature counts that are whole 256-feature tiles.
-bool dl_shape(const QMat &W, int M) {
-    return g_gemm_dl > 0 && !g_gemm_f16w && M > 64 && W.N % gemm_dl_tile_features() == 0;
+bool dl_shape(const QMat &W, int M, int ldx) {
+    // the direct loads address operands by 32-bit byte offsets from a base
+    const size_t row_bytes = W.wtype == T_Q4_0 ? (size_t)W.K / 2 : (size_t)W.K;
+    return g_gemm_dl > 0 && !g_gemm_f16w && M > 64 && W.N % gemm_dl_tile_features() == 0 &&
+           (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * row_bytes < ((size_t)1 << 31);
 }
 
 int dl_split(const QMat &W, int M) {
     const long tiles = (long)(W.N / gemm_dl_tile_features()) *
                        ((M + gemm_dl_tile_tokens() - 1) / gemm_dl_tile_tokens());
-    const long slots = (g_gemm_dl % 10 <= 3 ? 2L : 1L) * g_gemm_cu;
+    const long slots = (g_gemm_dl == 4 ? 1L : 2L) * g_gemm_cu;
     const int nb = W.K / 32;
     int best = 1;
     for (int S = 2; S <= 8; S *= 2)
@@ -789,14 +792,15 @@ void gemm_set_num_cu(int n) {
     g_gemm_f16w = e && strcmp(e, "1") == 0;
     const char *k = getenv("DECODE_GEMM_SKINNY");
     g_gemm_skinny = !(k && strcmp(k, "0") == 0);
-    // DECODE_GEMM_DL: 0 keeps the register-staged tiles; 3, 4 or 5 picks the
-    // direct-to-LDS form with that many stages on 32x32 tiles, 13 or 14 with 3
-    // or 4 stages on 16x16 tiles (default 3)
+    // DECODE_GEMM_DL: 0 keeps the register-staged tiles; 3 or 4 picks the
+    // direct-to-LDS form with that many stages on 32x32 tiles, 13 three stages
+    // on 16x16 tiles, 23 three stages with 64-feature wavefront tiles
+    // (default 23)
     const char *dl = getenv("DECODE_GEMM_DL");
-    g_gemm_dl = 3;
+    g_gemm_dl = 23;
     if (dl) {
         const int v = atoi(dl);
-        g_gemm_dl = (v == 0 || v == 3 || v == 4 || v == 5 || v == 13 || v == 14) ? v : 3;
+        g_gemm_dl = (v == 0 || v == 3 || v == 4 || v == 13 || v == 23) ? v : 23;
     }
 }
 
@@ -815,7 +819,7 @@ size_t gemm_workspace_bytes(const QMat &W, int M) {
     if (M <= 0 || !mfma_shape(W, 8)) return 0;
     const int S = split_for(W, M);
     size_t tile = S > 1 ? (size_t)S * M * W.N * 4 : 0;
-    if (dl_shape(W, M)) {
+    if (dl_shape(W, M, W.K)) {
         const int Sd = dl_split(W, M);
         tile = std::max(tile, Sd > 1 ? (size_t)Sd * M * W.N * 4 : (size_t)0);
     }
@@ -851,7 +855,7 @@ bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
             return true;
         }
     }
-    if (mfma_shape(W, ldx) && dl_shape(W, M)) {
+    if (mfma_shape(W, ldx) && dl_shape(W, M, ldx)) {
         int S = dl_split(W, M);
         while (S > 1 && (!ws || (size_t)S * M * W.N * 4 > ws_bytes)) S >>= 1;
         launch_gemm_dl(g_gemm_dl, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);

@@ -24,6 +24,9 @@
 // token m sits at slot 4m + (c ^ swz(m)), which spreads the 16-byte reads of
 // 16 consecutive tokens over distinct bank groups; the direct loads write
 // slots in lane order, so each lane simply fetches the chunk its slot holds.
+// Code rows are read 16 bytes at a time (conflict-free, where 8-byte reads at
+// a 16-byte stride conflict); a Q8_0 row's two 16-byte chunks are swapped in
+// rows 8..15 of every 16, for the same reason.
 //
 // Block: 256 threads, 256 features x 128 tokens; wavefront w covers features
 // 128 (w & 1) .. +127 (four 32-feature tiles a) and tokens 64 (w >> 1) .. +63
@@ -44,8 +47,6 @@ namespace {
 
 constexpr int DBN = 256;    // features per block
 constexpr int DBM = 128;    // tokens per block
-constexpr int DWN = 128;    // features per wavefront
-constexpr int DWM = 64;     // tokens per wavefront
 
 #define AS1 __attribute__((address_space(1)))
 #define AS3 __attribute__((address_space(3)))
@@ -64,8 +65,11 @@ struct Geo {
     static constexpr int LOADS = 4 + DBN * CB / 4096 + 1;
 };
 
-// Slot of chunk c of token row m (see the header).
-DEV int swz(int m) { return ((m >> 1) ^ (m >> 3)) & 3; }
+// Slot of chunk c of token row m (see the header): the 16-byte reads of a
+// quarter wavefront (16 consecutive tokens, one chunk each) then fall into 16
+// distinct groups of 4 banks (checked with the bank-conflict counter: no
+// conflicts, against 75% of LDS cycles without the swizzle).
+DEV int swz(int m) { return (m >> 2) & 3; }
 
 DEV h2 magic_lo(uint32_t v) { return as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04010400u)); }
 DEV h2 magic_hi(uint32_t v) { return as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04030402u)); }
@@ -114,6 +118,17 @@ DEV void block_barrier() {
 // stages apart, would otherwise wait for every load in flight before each
 // LDS read).  The asm sets m0 itself; the compiler uses m0 nowhere else in
 // these kernels (it is a reserved register that an asm clobber cannot name).
+// Same, with the address split into a wave-uniform base (SGPRs) and a
+// 32-bit per-lane byte offset, so that advancing to the next K block changes
+// only the base: no per-lane address arithmetic per load.
+DEV void dma16s(const void *base, uint32_t off, const void AS3 *lds) {
+    const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m) : "memory");
+}
+DEV void dma2s(const void *base, uint32_t off, const void AS3 *lds) {
+    const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(off), "s"(base), "s"(m) : "memory");
+}
 DEV void dma16(const void *src, const void AS3 *lds) {
     const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m) : "memory");
@@ -123,7 +138,7 @@ DEV void dma2(const void *src, const void AS3 *lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(src), "s"(m) : "memory");
 }
 
-template <int WT, int EPI, bool SPLIT, int NS, int MF>
+template <int WT, int EPI, bool SPLIT, int NS, int MF, int WL>
 __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const uint16_t *Xh, const uint16_t *Xl,
                                                                   int ldx, EpiArgs ep, int M, int pair_mode, int NT,
                                                                   int nsplit, float *part) {
@@ -144,35 +159,45 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
     const int mtile = rem % mtiles, split = rem / mtiles;
     if (nt >= NT) return;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wavefront index as a wave-uniform value: the LDS addresses of the
+    // direct loads then live in scalar registers
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n0 = nt * DBN, m0 = mtile * DBM;
     const int nb_all = W.K >> 5, nb = nb_all / nsplit, kb0 = split * nb;
-    const int wn = (w & 1) * DWN, wm = (w >> 1) * DWM;
+    // WL 0: wavefront w covers features 128 (w & 1) .. +127 and tokens
+    // 64 (w >> 1) .. +63; WL 1: features 64 w .. +63 and all 128 tokens (each
+    // code converted by one wavefront only)
+    constexpr int DWN = WL ? 64 : 128, DWM = WL ? 128 : 64;
+    const int wn = WL ? 64 * w : (w & 1) * DWN, wm = WL ? 0 : (w >> 1) * DWM;
 
-    // ---- per-lane global sources of the direct loads (K block 0 of the range) ----
+    // ---- per-lane byte offsets of the direct loads (from a base that moves
+    // with the K block; every offset below 2^31, checked by the launcher) ----
     // activations: instructions j = w, w + 4 of each part cover slots 64j .. 64j+63
-    const uint16_t *xa[2][2];
+    uint32_t xo[2];
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int slot = 64 * (w + 4 * i) + lane, m = slot >> 2, c = (slot & 3) ^ swz(slot >> 2);
         const int row = min(m0 + m, M - 1);            // rows past M repeat row M-1; their outputs are dropped
-        xa[0][i] = Xh + (size_t)row * ldx + (size_t)kb0 * 32 + c * 8;
-        xa[1][i] = Xl + (size_t)row * ldx + (size_t)kb0 * 32 + c * 8;
+        xo[i] = (uint32_t)(((size_t)row * ldx + c * 8) * 2);
     }
     // codes: Q4_0 one row of 16 bytes per lane (rows 64w + lane); Q8_0 two
     // instructions of 32 rows x 2 halves
     const size_t row_bytes = WT == T_Q4_0 ? (size_t)(W.K >> 1) : (size_t)W.K;
-    const uint8_t *ca[2];
+    uint32_t co[2];
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         if (WT == T_Q4_0) {
-            ca[i] = (const uint8_t *)W.qs + (size_t)(n0 + 64 * w + lane) * row_bytes + (size_t)kb0 * 16;
+            co[i] = (uint32_t)((size_t)(64 * w + lane) * row_bytes);
         } else {
-            const int slot = 64 * (w + 4 * i) + lane, r = slot >> 1, half = slot & 1;
-            ca[i] = (const uint8_t *)W.qs + (size_t)(n0 + r) * row_bytes + (size_t)kb0 * 32 + half * 16;
+            const int slot = 64 * (w + 4 * i) + lane, r = slot >> 1, half = (slot & 1) ^ ((r >> 3) & 1);
+            co[i] = (uint32_t)((size_t)r * row_bytes + half * 16);
         }
     }
-    const uint16_t *sa = W.d + (size_t)(n0 + 64 * w + lane) * nb_all + kb0;
+    const uint32_t so = (uint32_t)((size_t)(64 * w + lane) * nb_all * 2);
+    const uint8_t *xh_base = (const uint8_t *)Xh + (size_t)kb0 * 64;
+    const uint8_t *xl_base = (const uint8_t *)Xl + (size_t)kb0 * 64;
+    const uint8_t *c_base = (const uint8_t *)W.qs + (size_t)n0 * row_bytes + (size_t)kb0 * (WT == T_Q4_0 ? 16 : 32);
+    const uint8_t *s_base = (const uint8_t *)W.d + ((size_t)n0 * nb_all + kb0) * 2;
 
     auto stage_ptr = [&](auto sc) -> uint8_t * {
         constexpr int s = decltype(sc)::value;
@@ -186,20 +211,20 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
     // requests K block kb (clamped to the range) into stage s
     auto issue = [&](auto sc, int kb) __attribute__((always_inline)) {
         uint8_t *st = stage_ptr(sc);
-        const int k = min(kb, nb - 1);
+        const size_t k = (size_t)min(kb, nb - 1);
 #pragma unroll
         for (int i = 0; i < 2; i++) {
-            dma16(xa[0][i] + (size_t)k * 32, (const void AS3 *)(st + 1024 * (w + 4 * i)));
-            dma16(xa[1][i] + (size_t)k * 32, (const void AS3 *)(st + G::OFF_LO + 1024 * (w + 4 * i)));
+            dma16s(xh_base + k * 64, xo[i], (const void AS3 *)(st + 1024 * (w + 4 * i)));
+            dma16s(xl_base + k * 64, xo[i], (const void AS3 *)(st + G::OFF_LO + 1024 * (w + 4 * i)));
         }
         if (WT == T_Q4_0) {
-            dma16(ca[0] + (size_t)k * 16, (const void AS3 *)(st + G::OFF_CODES + 1024 * w));
+            dma16s(c_base + k * 16, co[0], (const void AS3 *)(st + G::OFF_CODES + 1024 * w));
         } else {
 #pragma unroll
             for (int i = 0; i < 2; i++)
-                dma16(ca[i] + (size_t)k * 32, (const void AS3 *)(st + G::OFF_CODES + 1024 * (w + 4 * i)));
+                dma16s(c_base + k * 32, co[i], (const void AS3 *)(st + G::OFF_CODES + 1024 * (w + 4 * i)));
         }
-        dma2(sa + k, (const void AS3 *)(st + G::OFF_SC + 256 * w));
+        dma2s(s_base + k * 2, so, (const void AS3 *)(st + G::OFF_SC + 256 * w));
     };
 
     // MF = 32: 32x32 tiles, 4 feature x 2 token tiles per wavefront;
@@ -237,7 +262,8 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
             if (WT == T_Q4_0) {
                 // codes 8g .. 8g+7: the low (g < 2) or high (g >= 2) nibbles of
                 // bytes 8(g & 1) .. 8(g & 1)+7
-                const u32x2 raw = *(const u32x2 *)(st + G::OFF_CODES + 16 * f + 8 * (g & 1));
+                const u32x4 v = *(const u32x4 *)(st + G::OFF_CODES + 16 * f);
+                const u32x2 raw = (g & 1) ? u32x2{v.z, v.w} : u32x2{v.x, v.y};
                 const int sh = (g >> 1) * 4;
                 const uint32_t v0 = (raw.x >> sh) & 0x0F0F0F0Fu, v1 = (raw.y >> sh) & 0x0F0F0F0Fu;
                 const h2 off = h2{(f16)1032.f, (f16)1032.f};
@@ -245,7 +271,10 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
                          a3 = magic_hi(v1) - off;
                 cf = h8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
             } else {
-                cf = q8_eight(*(const u32x2 *)(st + G::OFF_CODES + 32 * f + 8 * g));
+                // k 8g .. 8g+7: chunk g >> 1 (stored at position (g >> 1) ^ sw), half g & 1
+                const int sw = (f >> 3) & 1;
+                const u32x4 v = *(const u32x4 *)(st + G::OFF_CODES + 32 * f + 16 * ((g >> 1) ^ sw));
+                cf = q8_eight((g & 1) ? u32x2{v.z, v.w} : u32x2{v.x, v.y});
             }
             const float d = f16_bits_to_f32(*(const uint16_t *)(st + G::OFF_SC + 4 * f));
 #pragma unroll
@@ -262,37 +291,46 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
     auto compute32 = [&](auto sc) __attribute__((always_inline)) {
         if constexpr (MF == 32 && decltype(sc)::value >= 0) {
         const uint8_t *st = stage_ptr(sc);
-        // activation fragments: token tile b, k-half h, value / remainder
-        h8 xh[2][2], xl[2][2];
+        // the wavefront's feature tiles: codes of both k-halves and the scale
+        h8 c0[TA], c1[TA];
+        float d[TA];
 #pragma unroll
-        for (int b = 0; b < 2; b++) {
+        for (int a = 0; a < TA; a++) {
+            const int f = wn + 32 * a + (lane & 31);
+            const bool hi8 = lane >> 5;      // this lane's 8 bytes of a 16-byte chunk
+            if (WT == T_Q4_0) {
+                const u32x4 v = *(const u32x4 *)(st + G::OFF_CODES + 16 * f);
+                q4_pair(hi8 ? u32x2{v.z, v.w} : u32x2{v.x, v.y}, c0[a], c1[a]);
+            } else {
+                const int sw = (f >> 3) & 1;
+                const u32x4 v0 = *(const u32x4 *)(st + G::OFF_CODES + 32 * f + 16 * sw);
+                const u32x4 v1 = *(const u32x4 *)(st + G::OFF_CODES + 32 * f + 16 * (1 - sw));
+                c0[a] = q8_eight(hi8 ? u32x2{v0.z, v0.w} : u32x2{v0.x, v0.y});
+                c1[a] = q8_eight(hi8 ? u32x2{v1.z, v1.w} : u32x2{v1.x, v1.y});
+            }
+            d[a] = f16_bits_to_f32(*(const uint16_t *)(st + G::OFF_SC + 4 * f));
+        }
+        // (keeps the token tiles' fragment reads below: hoisted above, they
+        // would hold registers the codes need)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < TB; b++) {
+            h8 xh[2], xl[2];
             const int m = wm + 32 * b + (lane & 31);
 #pragma unroll
             for (int h = 0; h < 2; h++) {
                 const int slot = 4 * m + ((2 * h + (lane >> 5)) ^ swz(m));
-                xh[b][h] = *(const h8 *)(st + 16 * slot);
-                xl[b][h] = *(const h8 *)(st + G::OFF_LO + 16 * slot);
+                xh[h] = *(const h8 *)(st + 16 * slot);
+                xl[h] = *(const h8 *)(st + G::OFF_LO + 16 * slot);
             }
-        }
 #pragma unroll
-        for (int a = 0; a < 4; a++) {
-            const int f = wn + 32 * a + (lane & 31);
-            h8 c0, c1;
-            if (WT == T_Q4_0) {
-                q4_pair(*(const u32x2 *)(st + G::OFF_CODES + 16 * f + 8 * (lane >> 5)), c0, c1);
-            } else {
-                c0 = q8_eight(*(const u32x2 *)(st + G::OFF_CODES + 32 * f + 8 * (lane >> 5)));
-                c1 = q8_eight(*(const u32x2 *)(st + G::OFF_CODES + 32 * f + 16 + 8 * (lane >> 5)));
-            }
-            const float d = f16_bits_to_f32(*(const uint16_t *)(st + G::OFF_SC + 4 * f));
+            for (int a = 0; a < TA; a++) {
+                f16x t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[0], c0[a], f16x{}, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[0], c0[a], t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[1], c1[a], t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[1], c1[a], t, 0, 0, 0);
 #pragma unroll
-            for (int b = 0; b < 2; b++) {
-                f16x t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[b][0], c0, f16x{}, 0, 0, 0);
-                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[b][0], c0, t, 0, 0, 0);
-                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[b][1], c1, t, 0, 0, 0);
-                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[b][1], c1, t, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 16; r++) acc[a][b][r] += d * t[r];
+                for (int r = 0; r < 16; r++) acc[a][b][r] += d[a] * t[r];
             }
         }
         }
@@ -407,13 +445,14 @@ void launch_dl_ns(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl,
                   int pair_mode, int S, float *part, hipStream_t s) {
     const int NT = W.N / DBN, NT8 = (NT + 7) / 8 * 8;
     const dim3 grid(NT8 * ((M + DBM - 1) / DBM) * S);
-    // ns: LDS stages, plus 10 for the 16x16x32 tiles
+    // ns: 3 or 4 LDS stages on 32x32 tiles (wavefront tile 128 features x 64
+    // tokens); 13: 3 stages on 16x16 tiles; 23: 3 stages, 32x32 tiles,
+    // wavefront tile 64 features x 128 tokens
     switch (ns) {
-    case 3: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
-    case 5: launch((k_gemm_dl<WT, EPI, SPLIT, 5, 32>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
-    case 13: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 16>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
-    case 14: launch((k_gemm_dl<WT, EPI, SPLIT, 4, 16>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
-    default: launch((k_gemm_dl<WT, EPI, SPLIT, 4, 32>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
+    case 4: launch((k_gemm_dl<WT, EPI, SPLIT, 4, 32, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
+    case 13: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 16, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
+    case 23: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 1>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
+    default: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
     }
 }
 
