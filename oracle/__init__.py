@@ -22,7 +22,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 
-T_F32, T_F16, T_Q8_0, T_Q4_0 = 0, 1, 2, 3
+T_F32, T_F16, T_Q8_0, T_Q4_0, T_Q4_K = 0, 1, 2, 3, 4
 TENSOR_IDS = {"tok_embd": 0, "output": 1, "wq": 2, "wk": 3, "wv": 4, "wo": 5,
               "ffn_gate": 6, "ffn_up": 7, "ffn_down": 8}
 
@@ -83,6 +83,9 @@ def load(kind: str = "f64") -> C.CDLL:
         "orc_q4_0_quantize": (i64, [vp, i64, vp]),
         "orc_q8_0_dequantize": (None, [vp, i64, vp]),
         "orc_q4_0_dequantize": (None, [vp, i64, vp]),
+        "orc_q4_k_quantize": (i64, [vp, i64, vp]),
+        "orc_q4_k_dequantize": (None, [vp, i64, vp]),
+        "orc_q4_k_scales": (None, [vp, vp, vp]),
         "orc_rmsnorm": (None, [vp, vp, i32, f32, vp]),
         "orc_matvec": (None, [i32, vp, i32, i32, vp, vp]),
         "orc_rope": (None, [vp, i32, i32, i32, f32]),
@@ -134,24 +137,39 @@ def f16_to_f32(h: np.ndarray) -> np.ndarray:
     return x
 
 
+# block elements and bytes per block of each quantized type
+BLOCK = {T_Q8_0: (32, 34), T_Q4_0: (32, 18), T_Q4_K: (256, 144)}
+
+
 def quantize(x: np.ndarray, wtype: int) -> np.ndarray:
-    """fp32 array (size multiple of 32) -> GGUF-style block bytes."""
+    """fp32 array (size a multiple of the block) -> GGUF-style block bytes."""
     x = np.ascontiguousarray(x, dtype=np.float32).ravel()
-    bsz = {T_Q8_0: 34, T_Q4_0: 18}[wtype]
-    out = np.empty(x.size // 32 * bsz, np.uint8)
-    fn = load().orc_q8_0_quantize if wtype == T_Q8_0 else load().orc_q4_0_quantize
+    be, bsz = BLOCK[wtype]
+    out = np.empty(x.size // be * bsz, np.uint8)
+    L = load()
+    fn = {T_Q8_0: L.orc_q8_0_quantize, T_Q4_0: L.orc_q4_0_quantize, T_Q4_K: L.orc_q4_k_quantize}[wtype]
     n = fn(_p(x), x.size, _p(out))
     if n < 0:
-        raise ValueError("size must be a multiple of 32")
+        raise ValueError(f"size must be a multiple of {be}")
     return out
 
 
 def dequantize(blocks: np.ndarray, n: int, wtype: int) -> np.ndarray:
     blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
     y = np.empty(n, np.float32)
-    fn = load().orc_q8_0_dequantize if wtype == T_Q8_0 else load().orc_q4_0_dequantize
+    L = load()
+    fn = {T_Q8_0: L.orc_q8_0_dequantize, T_Q4_0: L.orc_q4_0_dequantize, T_Q4_K: L.orc_q4_k_dequantize}[wtype]
     fn(_p(blocks), n, _p(y))
     return y
+
+
+def q4_k_scales(block: np.ndarray):
+    """The eight six-bit (scale, min) pairs of one 144-byte Q4_K block."""
+    b = np.ascontiguousarray(block, dtype=np.uint8)
+    sc = np.empty(8, np.int32)
+    m = np.empty(8, np.int32)
+    load().orc_q4_k_scales(_p(b), _p(sc), _p(m))
+    return sc, m
 
 
 def rmsnorm(x, g, eps, kind="f64"):

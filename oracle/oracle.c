@@ -198,6 +198,132 @@ void orc_q4_0_dequantize(const uint8_t *blocks, int64_t n, float *y)
 }
 
 /* ======================================================================== */
+/* Q4_K.  The article names Q4_K among the GGUF tensor types (step 2c and   */
+/* its GGUF reference section) without defining it.                         */
+/* READING, layout (the GGUF super-block, so that blocks are interchangeable */
+/* with GGUF files): 256 elements along a row in 8 sub-blocks of 32, stored */
+/* in 144 bytes: d (f16), dmin (f16), 12 bytes s[] holding a six-bit scale  */
+/* sc_j and a six-bit min m_j per sub-block, 128 bytes of 4-bit codes q.    */
+/*   x = f32(d) * sc_j * q - f32(dmin) * m_j   (element of sub-block j)     */
+/*   j < 4 : sc_j = s[j] & 63,  m_j = s[j+4] & 63                            */
+/*   j >= 4: sc_j = (s[j+4] & 15) | (s[j-4] >> 6) << 4,                      */
+/*           m_j  = (s[j+4] >> 4) | (s[j]   >> 6) << 4                       */
+/*   code byte 32g + l (g = 0..3, l = 0..31): low nibble = element 64g + l, */
+/*   high nibble = element 64g + 32 + l.                                     */
+/* READING, quantizer (none is given; the plainest min-max form that keeps  */
+/* every element within half a step of its code): per sub-block, lo and hi  */
+/* its smallest and largest element;                                         */
+/*   mn_j = max(0, -lo_j); dmin = f16(max_j mn_j / 63) (0 if that is 0);    */
+/*   m_j = min(63, ceil(mn_j / dmin)); mf_j = m_j * dmin;                    */
+/*   s_j = max(0, (hi_j + mf_j) / 15); d = f16(max_j s_j / 63);             */
+/*   sc_j = min(63, ceil(s_j / d)); step_j = d * sc_j;                       */
+/*   q = min(15, round-half-away((x + mf_j) * (1 / step_j)))  (0 if step 0). */
+/* All in fp32 with d and dmin taken as their f16 values.                   */
+/* ======================================================================== */
+
+void orc_q4_k_scales(const uint8_t *ib, int32_t *sc, int32_t *m)
+{
+    const uint8_t *s = ib + 4;
+    for (int j = 0; j < 8; j++) {
+        if (j < 4) {
+            sc[j] = s[j] & 63;
+            m[j] = s[j + 4] & 63;
+        } else {
+            sc[j] = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+            m[j] = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+        }
+    }
+}
+
+int64_t orc_q4_k_quantize(const float *x, int64_t n, uint8_t *out)
+{
+    if (n < 0 || n % 256) return -1;
+    for (int64_t b = 0; b < n / 256; b++) {
+        const float *xb = x + b * 256;
+        uint8_t *ob = out + b * 144;
+        float lo[8], hi[8], mn[8], sv[8], mf[8], step[8];
+        int32_t sc[8], m[8];
+        for (int j = 0; j < 8; j++) {
+            lo[j] = hi[j] = xb[32 * j];
+            for (int i = 1; i < 32; i++) {
+                const float v = xb[32 * j + i];
+                if (v < lo[j]) lo[j] = v;
+                if (v > hi[j]) hi[j] = v;
+            }
+            mn[j] = lo[j] < 0.0f ? -lo[j] : 0.0f;
+        }
+        float mmax = 0.0f;
+        for (int j = 0; j < 8; j++) if (mn[j] > mmax) mmax = mn[j];
+        const uint16_t dminh = orc_f16_from_f32(mmax / 63.0f);
+        const float dmin = orc_f16_to_f32(dminh);
+        for (int j = 0; j < 8; j++) {
+            int mj = 0;
+            if (dmin > 0.0f) {
+                const float r = ceilf(mn[j] / dmin);
+                mj = r > 63.0f ? 63 : (int)r;
+            }
+            m[j] = mj;
+            mf[j] = (float)mj * dmin;
+            const float t = (hi[j] + mf[j]) / 15.0f;
+            sv[j] = t > 0.0f ? t : 0.0f;
+        }
+        float smax = 0.0f;
+        for (int j = 0; j < 8; j++) if (sv[j] > smax) smax = sv[j];
+        const uint16_t dh = orc_f16_from_f32(smax / 63.0f);
+        const float d = orc_f16_to_f32(dh);
+        for (int j = 0; j < 8; j++) {
+            int sj = 0;
+            if (d > 0.0f) {
+                const float r = ceilf(sv[j] / d);
+                sj = r > 63.0f ? 63 : (int)r;
+            }
+            sc[j] = sj;
+            step[j] = d * (float)sj;
+        }
+        wr_u16(ob, dh);
+        wr_u16(ob + 2, dminh);
+        uint8_t *s = ob + 4;
+        for (int j = 0; j < 4; j++) {
+            s[j] = (uint8_t)(sc[j] | ((sc[j + 4] >> 4) << 6));
+            s[j + 4] = (uint8_t)(m[j] | ((m[j + 4] >> 4) << 6));
+            s[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((m[j + 4] & 15) << 4));
+        }
+        int code[256];
+        for (int j = 0; j < 8; j++) {
+            const float inv = step[j] > 0.0f ? 1.0f / step[j] : 0.0f;
+            for (int i = 0; i < 32; i++) {
+                const float t = (xb[32 * j + i] + mf[j]) * inv;
+                int c = (int)roundf(t);      /* half away from zero */
+                if (c > 15) c = 15;
+                if (c < 0) c = 0;
+                code[32 * j + i] = c;
+            }
+        }
+        for (int g = 0; g < 4; g++)
+            for (int l = 0; l < 32; l++)
+                ob[16 + 32 * g + l] = (uint8_t)(code[64 * g + l] | (code[64 * g + 32 + l] << 4));
+    }
+    return n / 256 * 144;
+}
+
+void orc_q4_k_dequantize(const uint8_t *blocks, int64_t n, float *y)
+{
+    for (int64_t b = 0; b < n / 256; b++) {
+        const uint8_t *ib = blocks + b * 144;
+        const float d = orc_f16_to_f32(rd_u16(ib)), dmin = orc_f16_to_f32(rd_u16(ib + 2));
+        int32_t sc[8], m[8];
+        orc_q4_k_scales(ib, sc, m);
+        for (int g = 0; g < 4; g++)
+            for (int l = 0; l < 32; l++) {
+                const uint8_t byte = ib[16 + 32 * g + l];
+                const int e0 = 64 * g + l, e1 = 64 * g + 32 + l;
+                y[b * 256 + e0] = d * (float)sc[e0 / 32] * (float)(byte & 15) - dmin * (float)m[e0 / 32];
+                y[b * 256 + e1] = d * (float)sc[e1 / 32] * (float)(byte >> 4) - dmin * (float)m[e1 / 32];
+            }
+    }
+}
+
+/* ======================================================================== */
 /* Primitives                                                               */
 /* ======================================================================== */
 
@@ -219,6 +345,8 @@ static void deq_row(int32_t wtype, const void *w, int64_t row, int32_t cols, flo
         memcpy(dst, (const float *)w + row * cols, sizeof(float) * (size_t)cols);
     } else if (wtype == ORC_T_Q8_0) {
         orc_q8_0_dequantize((const uint8_t *)w + row * (cols / 32) * 34, cols, dst);
+    } else if (wtype == ORC_T_Q4_K) {
+        orc_q4_k_dequantize((const uint8_t *)w + row * (cols / 256) * 144, cols, dst);
     } else {
         orc_q4_0_dequantize((const uint8_t *)w + row * (cols / 32) * 18, cols, dst);
     }
@@ -368,6 +496,7 @@ static int64_t enc_bytes(int32_t wtype, int64_t rows, int64_t cols)
 {
     if (wtype == ORC_T_F32) return rows * cols * 4;
     if (wtype == ORC_T_Q8_0) return rows * (cols / 32) * 34;
+    if (wtype == ORC_T_Q4_K) return rows * (cols / 256) * 144;
     return rows * (cols / 32) * 18;
 }
 
@@ -385,6 +514,8 @@ static void *encode(int32_t wtype, const float *src, int64_t rows, int64_t cols)
     for (int64_t r = 0; r < rows; r++) {
         if (wtype == ORC_T_Q8_0)
             orc_q8_0_quantize(src + r * cols, cols, dst + r * rb);
+        else if (wtype == ORC_T_Q4_K)
+            orc_q4_k_quantize(src + r * cols, cols, dst + r * rb);
         else
             orc_q4_0_quantize(src + r * cols, cols, dst + r * rb);
     }
@@ -405,12 +536,14 @@ orc_model *orc_model_new(const orc_hparams *hp, const orc_weights *w)
     if (h.n_layer <= 0 || h.n_embd <= 0 || h.n_head <= 0 || h.n_head_kv <= 0 || h.head_dim <= 0 ||
         h.n_ff <= 0 || h.n_vocab <= 0 || h.head_dim % 2 || h.n_head % h.n_head_kv)
         return NULL;
-    if (h.wtype != ORC_T_F32 && h.wtype != ORC_T_Q8_0 && h.wtype != ORC_T_Q4_0) return NULL;
+    if (h.wtype != ORC_T_F32 && h.wtype != ORC_T_Q8_0 && h.wtype != ORC_T_Q4_0 && h.wtype != ORC_T_Q4_K) return NULL;
     if (h.kvtype != ORC_T_F32 && h.kvtype != ORC_T_F16 && h.kvtype != ORC_T_Q8_0) return NULL;
     /* a Q8_0 cache row splits into whole 32-element blocks within each head */
     if (h.kvtype == ORC_T_Q8_0 && h.head_dim % 32) return NULL;
     const int32_t qd = h.n_head * h.head_dim, kd = h.n_head_kv * h.head_dim;
     if (h.wtype != ORC_T_F32 && (h.n_embd % 32 || qd % 32 || h.n_ff % 32)) return NULL;
+    /* Q4_K rows are whole 256-element super-blocks */
+    if (h.wtype == ORC_T_Q4_K && (h.n_embd % 256 || qd % 256 || h.n_ff % 256)) return NULL;
 
     orc_model *m = (orc_model *)calloc(1, sizeof *m);
     m->hp = h;

@@ -25,7 +25,10 @@
  * Parity pins: every function here is pinned by tests/test_oracle_*.py
  * against closed forms, brute force, library routines or hand-computed
  * fixtures (tests/golden/).  No function is "parity unpinned" except the
- * end-to-end equality with llama.cpp itself, which cannot be checked here.
+ * end-to-end equality with llama.cpp itself, which cannot be checked here
+ * (for Q4_K also its quantizer: the article gives none, so the min-max
+ * quantizer in oracle.c is a reading; the block layout and decode rule are
+ * pinned by a hand-worked block).
  */
 #ifndef DECODE_ORACLE_H
 #define DECODE_ORACLE_H
@@ -43,7 +46,7 @@ extern "C" {
 typedef ORC_REAL orc_real;
 
 /* Element types.  Values chosen by this file alone. */
-enum { ORC_T_F32 = 0, ORC_T_F16 = 1, ORC_T_Q8_0 = 2, ORC_T_Q4_0 = 3 };
+enum { ORC_T_F32 = 0, ORC_T_F16 = 1, ORC_T_Q8_0 = 2, ORC_T_Q4_0 = 3, ORC_T_Q4_K = 4 };
 
 /* sizeof(orc_real): 8 for the f64 build, 4 for the f32 build. */
 int32_t orc_real_size(void);
@@ -64,11 +67,18 @@ int64_t orc_q8_0_quantize(const float *x, int64_t n, uint8_t *blocks);
 int64_t orc_q4_0_quantize(const float *x, int64_t n, uint8_t *blocks);
 void    orc_q8_0_dequantize(const uint8_t *blocks, int64_t n, float *y);
 void    orc_q4_0_dequantize(const uint8_t *blocks, int64_t n, float *y);
+/* Q4_K super-block = 256 elements in 144 bytes: f16 d, f16 dmin, 12 bytes of
+ * six-bit sub-block scales and mins, 128 bytes of 4-bit codes (see
+ * oracle.c).  n must be a multiple of 256. */
+int64_t orc_q4_k_quantize(const float *x, int64_t n, uint8_t *blocks);
+void    orc_q4_k_dequantize(const uint8_t *blocks, int64_t n, float *y);
+/* The eight (scale, min) six-bit pairs of one super-block, unpacked. */
+void    orc_q4_k_scales(const uint8_t *block, int32_t *sc, int32_t *m);
 
 /* ---- primitives (exposed for the pins) ---------------------------------- */
 void orc_rmsnorm(const orc_real *x, const float *g, int32_t n, float eps, orc_real *y);
 /* y[r] = sum_k deq(W)[r][k] * x[k]; W row-major [rows][cols] of type wtype
-   (F32: float array; Q8_0/Q4_0: block bytes as above). */
+   (F32: float array; Q8_0/Q4_0/Q4_K: block bytes as above). */
 void orc_matvec(int32_t wtype, const void *w, int32_t rows, int32_t cols,
                 const orc_real *x, orc_real *y);
 /* rotate n_heads consecutive head vectors of size hd in place, position pos */
@@ -90,7 +100,7 @@ int32_t orc_argmax(const orc_real *x, int32_t n);   /* lowest index on ties */
 typedef struct {
     int32_t n_layer, n_embd, n_head, n_head_kv, head_dim, n_ff, n_vocab;
     float   rms_eps, rope_base;
-    int32_t wtype;   /* F32, Q8_0 or Q4_0: every 2-D matrix                  */
+    int32_t wtype;   /* F32, Q8_0, Q4_0 or Q4_K: every 2-D matrix            */
     int32_t kvtype;  /* F32, F16 or Q8_0 (Q8_0 needs head_dim % 32 == 0)     */
 } orc_hparams;
 

@@ -23,7 +23,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 # element types (same numbering as the library's public header)
-F32, F16, Q8_0, Q4_0 = 0, 1, 2, 3
+F32, F16, Q8_0, Q4_0, Q4_K = 0, 1, 2, 3, 4
 
 WORKLOADS = {
     # 2 layers, d 256, 4 heads (hd 64, no GQA), FFN 688, vocab 1024, fp32

@@ -1,4 +1,4 @@
-"""Pins for the oracle's f16 conversion and Q8_0 / Q4_0 block codecs.
+"""Pins for the oracle's f16 conversion and Q8_0 / Q4_0 / Q4_K block codecs.
 
 Each pin checks the oracle against something other than itself: numpy's own
 IEEE half conversion, exhaustive enumeration, hand-worked blocks under
@@ -169,8 +169,105 @@ def test_q4_0_properties(orc):
     assert ok.all()
 
 
+# ------------------------------------------------------------------ Q4_K
+def test_q4_k_golden(orc):
+    (blk,) = _fixture("q4_k_block.txt")
+    x = np.array(blk["x"], np.float32)
+    b = orc.quantize(x, orc.T_Q4_K)
+    assert b.size == 144
+    assert b[:16].tolist() == [int(v, 16) for v in blk["header"]]
+    assert b[16:].tolist() == [int(v, 16) for v in blk["codes"]]
+    sc, m = orc.q4_k_scales(b)
+    assert sc.tolist() == [10, 63, 1, 30, 16, 47, 2, 55]
+    assert m.tolist() == [63, 0, 5, 17, 33, 48, 1, 20]
+    y = orc.dequantize(b, 256, orc.T_Q4_K)
+    assert y.tolist() == [float(v) for v in blk["y"]]
+
+
+def _q4_k_fields(orc, b):
+    """Per super-block d, dmin (as fp64), sub-block sc, m and the 256 codes."""
+    b = b.reshape(-1, 144)
+    d = b[:, 0:2].copy().view(np.float16)[:, 0].astype(np.float64)
+    dmin = b[:, 2:4].copy().view(np.float16)[:, 0].astype(np.float64)
+    sc = np.empty((len(b), 8), np.int64)
+    m = np.empty((len(b), 8), np.int64)
+    for i in range(len(b)):
+        s_, m_ = orc.q4_k_scales(b[i])
+        sc[i], m[i] = s_, m_
+    qs = b[:, 16:].reshape(-1, 4, 32)
+    code = np.empty((len(b), 4, 2, 32), np.int64)
+    code[:, :, 0, :] = qs & 15
+    code[:, :, 1, :] = qs >> 4
+    return d, dmin, sc, m, code.reshape(-1, 8, 32)
+
+
+def test_q4_k_properties(orc):
+    rng = np.random.default_rng(21)
+    nb = 1500
+    x = rng.standard_normal((nb, 8, 32)) * rng.uniform(1e-3, 10, (nb, 1, 1))
+    x *= rng.uniform(0.05, 1.0, (nb, 8, 1))                # uneven sub-block ranges
+    x += rng.uniform(-1, 1, (nb, 8, 1)) * np.abs(x).max((1, 2), keepdims=True) * 0.5
+    x[3] = 0.0                                             # zero super-block
+    x[4] = np.abs(x[4])                                    # no negative element
+    x[5] = -np.abs(x[5])                                   # no positive element
+    x[6, :, :] = 0.25                                      # constant
+    x = x.astype(np.float32)
+    b = orc.quantize(x, orc.T_Q4_K)
+    y = orc.dequantize(b, x.size, orc.T_Q4_K).reshape(x.shape).astype(np.float64)
+    d, dmin, sc, m, code = _q4_k_fields(orc, b)
+    xd = x.astype(np.float64)
+    # (i) an all-zero super-block encodes to 144 zero bytes and decodes to zeros
+    assert (b.reshape(-1, 144)[3] == 0).all() and (y[3] == 0).all()
+    # (ii) a super-block without negative elements needs no min
+    assert (m[4] == 0).all() and dmin[4] == 0
+    # (iii) the decode rule, element by element, from the unpacked fields
+    step = d[:, None] * sc
+    mf = dmin[:, None] * m
+    assert np.allclose(y, code * step[..., None] - mf[..., None], rtol=0, atol=1e-6 * np.abs(xd).max())
+    # (iv) the largest sub-block scale and min use the six-bit range (62 or 63;
+    # 62 when the f16 rounding of d or dmin went up)
+    nzr = np.abs(x).max((1, 2)) > 0
+    assert (sc.max(1)[nzr] >= 62).all()
+    neg = x.min((1, 2)) < 0
+    assert (m.max(1)[neg] >= 62).all()
+    # (v) every element within half a step of its decoded value, apart from the
+    # slack that a clamped six-bit scale or min leaves (s_j > step_j, mn_j > mf_j)
+    lo, hi = xd.min(2), xd.max(2)
+    s_need = np.maximum(0, (hi + mf) / 15)
+    mn_need = np.maximum(0, -lo)
+    slack = 15 * np.maximum(0, s_need - step) + np.maximum(0, mn_need - mf)
+    bound = step / 2 + slack + 1e-6 * np.maximum(np.abs(xd).max(2), 1e-30)
+    assert (np.abs(xd - y) <= bound[..., None]).all()
+    # (vi) brute force: each code is the nearest of the 16 levels c*step - mf
+    # (away from exact ties)
+    lev = np.arange(16)[None, None, None, :] * step[..., None, None] - mf[..., None, None]
+    dist = np.abs(xd[..., None] - lev)
+    best = dist.argmin(-1)
+    srt = np.sort(dist, -1)
+    tie = (srt[..., 1] - srt[..., 0]) <= 1e-5 * np.maximum(step[..., None], 1e-30)
+    zero_step = (step == 0)[..., None]
+    assert ((best == code) | tie | zero_step).all()
+
+
+def test_q4_k_sub_block_addressing(orc):
+    # each sub-block's scale/min must land on its own 32 elements: a block whose
+    # sub-block j is the constant j+1 (all others untouched) decodes sub-block
+    # j to within half a step of j+1 and the rest to zero
+    for j in range(8):
+        x = np.zeros(256, np.float32)
+        x[32 * j:32 * j + 32] = j + 1
+        b = orc.quantize(x, orc.T_Q4_K)
+        y = orc.dequantize(b, 256, orc.T_Q4_K)
+        sc, m = orc.q4_k_scales(b)
+        assert sc[j] == 63 and (np.delete(sc, j) == 0).all() and (m == 0).all()
+        assert np.abs(y[32 * j:32 * j + 32] - (j + 1)).max() <= (j + 1) / 15 / 2 * 1.01
+        assert (np.delete(y, np.s_[32 * j:32 * j + 32]) == 0).all()
+
+
 def test_codecs_reject_ragged(orc):
     L = orc.load()
     x = np.zeros(33, np.float32)
     assert L.orc_q8_0_quantize(x.ctypes.data, 33, None) == -1
     assert L.orc_q4_0_quantize(x.ctypes.data, 33, None) == -1
+    x = np.zeros(288, np.float32)
+    assert L.orc_q4_k_quantize(x.ctypes.data, 288, None) == -1

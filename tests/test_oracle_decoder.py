@@ -123,6 +123,20 @@ def test_cache_equals_full_recompute(orc, wtype, kvtype):
     assert np.abs(got - ref).max() <= tol * np.abs(ref).max()
 
 
+def test_q4_k_weights_equal_full_recompute(orc):
+    # Q4_K rows are whole 256-element super-blocks: d, H*hd and F multiples of 256
+    hp = _hp(wtype=synth.Q4_K, kvtype=synth.F16, n_embd=256, head_dim=64, n_ff=512)
+    w = _weights(hp, 6)
+    toks = synth.prompt(hp["n_vocab"], 9, 7)
+    got = _oracle_all_logits(orc, hp, w, toks)
+    ref = dense_forward(orc, hp, w, toks)
+    assert np.abs(ref).max() > 1.0
+    assert np.abs(got - ref).max() <= 1e-6 * np.abs(ref).max()
+    # and the Q4_K model is not the F32 one: the codes moved the logits
+    f32 = _oracle_all_logits(orc, dict(hp, wtype=synth.F32), w, toks)
+    assert np.abs(f32 - got).max() > 1e-3 * np.abs(ref).max()
+
+
 def test_gqa_equals_mha_with_repeated_heads(orc):
     hp = _hp()
     w = _weights(hp, 7)
@@ -196,6 +210,9 @@ def test_return_codes(orc):
         assert L.orc_eval(c.ptr, 0, 1, None) == 0
     assert L.orc_eval(c.ptr, 0, 1, None) == 1                   # context full
     assert c.pos_max(0) == 3
+    # Q4_K needs rows of whole 256-element super-blocks
+    with pytest.raises(ValueError):
+        orc.Model(_hp(wtype=synth.Q4_K), _weights(_hp(), 15))
 
 
 def test_kv_rows_hold_rotated_keys(orc):
