@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdecode.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "decode.h")
 
-F32, F16, Q8_0, Q4_0 = 0, 1, 2, 3
+F32, F16, Q8_0, Q4_0, Q4_K = 0, 1, 2, 3, 4
 K_QKV, K_ATTN, K_WO, K_FFN_GU, K_FFN_DOWN, K_OUTPUT, K_STEP = 0, 1, 2, 3, 4, 5, 6
 TENSOR_IDS = {"tok_embd": 0, "output": 1, "wq": 2, "wk": 3, "wv": 4, "wo": 5,
               "ffn_gate": 6, "ffn_up": 7, "ffn_down": 8}

@@ -24,7 +24,7 @@ template <class T>
 DEV GLB T *gl(T *p) { return (GLB T *)p; }
 
 // Element type codes (same values as dec_type in include/decode.h).
-enum { T_F32 = 0, T_F16 = 1, T_Q8_0 = 2, T_Q4_0 = 3 };
+enum { T_F32 = 0, T_F16 = 1, T_Q8_0 = 2, T_Q4_0 = 3, T_Q4_K = 4 };
 
 DEV h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 DEV uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }

@@ -147,6 +147,10 @@ static bool alloc_qmat(Mem &mem, QMat &m, int wtype, int N, int K) {
     } else if (hipMemset(m.qs, 0, qbytes) != hipSuccess) {   // padding must read as zero
         return false;
     }
+    if (wtype == DEC_Q4_K) {
+        m.dm = (uint32_t *)mem.get((size_t)N * (K / 256) * 4);
+        if (!m.dm) return false;
+    }
     return true;
 }
 
@@ -199,10 +203,12 @@ static bool valid_hparams(const dec_hparams &h) {
         return false;
     if (h.head_dim != 64 && h.head_dim != 128 && h.head_dim != 256) return false;
     if (h.n_head % h.n_head_kv || h.n_head / h.n_head_kv > 8) return false;
-    if (h.wtype != DEC_F32 && h.wtype != DEC_Q8_0 && h.wtype != DEC_Q4_0) return false;
+    if (h.wtype != DEC_F32 && h.wtype != DEC_Q8_0 && h.wtype != DEC_Q4_0 && h.wtype != DEC_Q4_K) return false;
     if (h.kvtype != DEC_F32 && h.kvtype != DEC_F16 && h.kvtype != DEC_Q8_0) return false;
     if (h.n_embd % 32 || (h.n_head * h.head_dim) % 32) return false;
     if (h.wtype != DEC_F32 && h.n_ff % 32) return false;
+    // Q4_K rows are whole 256-weight super-blocks
+    if (h.wtype == DEC_Q4_K && (h.n_embd % 256 || (h.n_head * h.head_dim) % 256 || h.n_ff % 256)) return false;
     // the decode mat-vec holds a whole input row in LDS: every K of a
     // quantized matrix (d, H*hd, n_ff) is at most MV_KMAX elements
     if (h.wtype != DEC_F32 &&
@@ -324,7 +330,9 @@ extern "C" int64_t dec_model_tensor_blocks(const dec_model *m, int32_t id, int32
     }
     const int wt = src->wtype;
     const int nb = cols / 32;
-    const size_t row_bytes = wt == DEC_F32 ? (size_t)cols * 4 : (size_t)nb * (wt == DEC_Q8_0 ? 34 : 18);
+    const size_t row_bytes = wt == DEC_F32    ? (size_t)cols * 4
+                             : wt == DEC_Q4_K ? (size_t)(cols / 256) * 144
+                                              : (size_t)nb * (wt == DEC_Q8_0 ? 34 : 18);
     const size_t total = row_bytes * rows;
     if (!dst || cap < total) return -(int64_t)total;
     if (hipStreamSynchronize(m->stream) != hipSuccess) return 0;
@@ -336,6 +344,9 @@ extern "C" int64_t dec_model_tensor_blocks(const dec_model *m, int32_t id, int32
     if (hipMemcpy(q.data(), src->qs, q.size(), hipMemcpyDeviceToHost) != hipSuccess) return 0;
     if (!sc.empty() && hipMemcpy(sc.data(), src->d, sc.size() * 2, hipMemcpyDeviceToHost) != hipSuccess)
         return 0;
+    std::vector<uint32_t> dmv(wt == DEC_Q4_K ? (size_t)src->N * (src->K / 256) : 0);
+    if (!dmv.empty() && hipMemcpy(dmv.data(), src->dm, dmv.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+        return 0;
     uint8_t *o = (uint8_t *)dst;
     for (int r = 0; r < rows; r++) {
         int sr = r + row_off;
@@ -345,6 +356,37 @@ extern "C" int64_t dec_model_tensor_blocks(const dec_model *m, int32_t id, int32
         if (wt == DEC_F32) {
             memcpy(o, qr, (size_t)cols * 4);
             o += (size_t)cols * 4;
+            continue;
+        }
+        if (wt == DEC_Q4_K) {
+            // stored (Q4_0-layout codes, sc | m << 8 per sub-block, d | dmin << 16)
+            // -> the 144-byte super-block of the public layout
+            const uint16_t *sm = sc.data() + (size_t)sr * (src->K / 32);
+            for (int sb = 0; sb < cols / 256; sb++) {
+                const uint32_t dd = dmv[(size_t)sr * (src->K / 256) + sb];
+                memcpy(o, &dd, 4);
+                int scj[8], mj[8];
+                for (int j = 0; j < 8; j++) {
+                    scj[j] = sm[8 * sb + j] & 63;
+                    mj[j] = (sm[8 * sb + j] >> 8) & 63;
+                }
+                for (int j = 0; j < 4; j++) {
+                    o[4 + j] = (uint8_t)(scj[j] | ((scj[j + 4] >> 4) << 6));
+                    o[8 + j] = (uint8_t)(mj[j] | ((mj[j + 4] >> 4) << 6));
+                    o[12 + j] = (uint8_t)((scj[j + 4] & 15) | ((mj[j + 4] & 15) << 4));
+                }
+                // sub-block pair (2g, 2g+1): stored byte k of sub-block j holds its
+                // weights k (low) and k+16 (high); file byte 32g + l holds weight
+                // l of sub-block 2g (low) and of sub-block 2g+1 (high)
+                const uint8_t *q = qr + (size_t)sb * 128;
+                for (int g = 0; g < 4; g++)
+                    for (int l = 0; l < 32; l++) {
+                        const uint8_t a = q[32 * g + (l & 15)], b = q[32 * g + 16 + (l & 15)];
+                        const int lo = l < 16 ? (a & 15) : (a >> 4), hi = l < 16 ? (b & 15) : (b >> 4);
+                        o[16 + 32 * g + l] = (uint8_t)(lo | (hi << 4));
+                    }
+                o += 144;
+            }
             continue;
         }
         const int qb = wt == DEC_Q8_0 ? 32 : 16;
@@ -365,7 +407,10 @@ extern "C" int64_t dec_model_tensor_blocks(const dec_model *m, int32_t id, int32
 static std::string layer_name(int l, const char *what) { return "blk." + std::to_string(l) + "." + what + ".weight"; }
 
 static int file_type_of(int wtype) {
-    return wtype == DEC_Q4_0 ? gguf::T_Q4_0 : wtype == DEC_Q8_0 ? gguf::T_Q8_0 : gguf::T_F32;
+    return wtype == DEC_Q4_0   ? gguf::T_Q4_0
+           : wtype == DEC_Q8_0 ? gguf::T_Q8_0
+           : wtype == DEC_Q4_K ? gguf::T_Q4_K
+                               : gguf::T_F32;
 }
 
 // Hyper-parameters and tensor checks of a parsed file; returns a gguf status.
@@ -402,7 +447,7 @@ static int gguf_model_params(const gguf::File &f, int32_t kvtype, dec_hparams &h
     const gguf::Tensor *emb = f.tensor("token_embd.weight");
     if (!emb || emb->n_dims != 2 || emb->dims[0] != d) return gguf::E_SHAPE;
     const uint32_t wt = emb->type;
-    if (wt != gguf::T_F32 && wt != gguf::T_Q4_0 && wt != gguf::T_Q8_0) return gguf::E_TYPE;
+    if (wt != gguf::T_F32 && wt != gguf::T_Q4_0 && wt != gguf::T_Q8_0 && wt != gguf::T_Q4_K) return gguf::E_TYPE;
     h = dec_hparams{};
     h.n_layer = (int32_t)nl;
     h.n_embd = (int32_t)d;
@@ -413,7 +458,7 @@ static int gguf_model_params(const gguf::File &f, int32_t kvtype, dec_hparams &h
     h.n_vocab = (int32_t)emb->dims[1];
     h.rms_eps = (float)eps;
     h.rope_base = (float)base;
-    h.wtype = wt == gguf::T_Q4_0 ? DEC_Q4_0 : wt == gguf::T_Q8_0 ? DEC_Q8_0 : DEC_F32;
+    h.wtype = wt == gguf::T_Q4_0 ? DEC_Q4_0 : wt == gguf::T_Q8_0 ? DEC_Q8_0 : wt == gguf::T_Q4_K ? DEC_Q4_K : DEC_F32;
     h.kvtype = kvtype;
     if (!valid_hparams(h)) return gguf::E_SHAPE;
     const uint64_t qd = nh * hd, kd = nkv * hd, V = (uint64_t)h.n_vocab;

@@ -32,7 +32,8 @@
 // RoPE pairs (adjacent features) sit in lanes l and l^1 and are exchanged.
 //
 // Fallback path (fp32 weights, or shapes the MFMA tiling does not cover):
-// one thread per (row pair, token), plain fp32 FMA.
+// one thread per (row pair, token), plain fp32 FMA.  Q4_K weights take the
+// direct-to-LDS form (gemm_dl.hip) or such a plain kernel.
 #include <stdlib.h>
 #include <string.h>
 
@@ -528,6 +529,63 @@ __global__ __launch_bounds__(256) void k_gemm_f32(QMat W, const uint16_t *X, con
     epi_pair<EPI>(ep, m, p, r0, r1, a, b);
 }
 
+// Q4_K weights (any N): one thread per (row pair, token); per sub-block
+// (d sc) sum q x - (dmin m) sum x in fp32.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_q4k(QMat W, const uint16_t *X, const uint16_t *Xl, int ldx,
+                                                  EpiArgs ep, int M, int pair_mode) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    const int m = blockIdx.y;
+    if (p >= W.N / 2 || m >= M) return;
+    int r0, r1;
+    pair_rows(pair_mode, p, r0, r1);
+    const f16 *x = (const f16 *)X + (size_t)m * ldx;
+    const f16 *xl = (const f16 *)Xl + (size_t)m * ldx;
+    const int nb = W.K >> 5;
+    float out[2];
+    const int rows[2] = {r0, r1};
+    for (int i = 0; i < 2; i++) {
+        const int row = rows[i];
+        const uint8_t *q = (const uint8_t *)W.qs + (size_t)row * (W.K >> 1);
+        float a = 0.f;
+        for (int b = 0; b < nb; b++) {
+            const uint32_t dd = W.dm[(size_t)row * (W.K >> 8) + (b >> 3)];
+            const uint16_t sm = W.d[(size_t)row * nb + b];
+            float t = 0.f, xs = 0.f;
+            for (int k = 0; k < 32; k++) {
+                const uint8_t byte = q[b * 16 + (k & 15)];
+                const int c = k < 16 ? (byte & 15) : (byte >> 4);
+                const float xv = (float)x[b * 32 + k] + (float)xl[b * 32 + k];
+                t += (float)c * xv;
+                xs += xv;
+            }
+            a += f16_bits_to_f32((uint16_t)dd) * (float)(sm & 63) * t -
+                 f16_bits_to_f32((uint16_t)(dd >> 16)) * (float)((sm >> 8) & 63) * xs;
+        }
+        out[i] = a;
+    }
+    epi_pair<EPI>(ep, m, p, r0, r1, out[0], out[1]);
+}
+
+// xs[m][kb] = sum of (Xh + Xl)[m][32 kb .. 32 kb + 31], in order.
+__global__ __launch_bounds__(256) void k_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, int K,
+                                                    float *xs) {
+    const int nb = K >> 5;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)M * nb) return;
+    const int m = (int)(idx / nb), kb = (int)(idx % nb);
+    const h8 *h = (const h8 *)(Xh + (size_t)m * ldx + kb * 32);
+    const h8 *l = (const h8 *)(Xl + (size_t)m * ldx + kb * 32);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        const h8 hv = h[c], lv = l[c];
+#pragma unroll
+        for (int e = 0; e < 8; e++) s += (float)hv[e] + (float)lv[e];
+    }
+    xs[idx] = s;
+}
+
 
 // ---- skinny form: ubatches of at most 32 tokens (batched decode) ----------
 //
@@ -765,18 +823,24 @@ void launch_f32_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int l
 }
 
 // Direct-to-LDS form (gemm_dl.hip): ubatches of more than 64 tokens with the
-// exact operands, feature counts that are whole 256-feature tiles.
+// exact operands (Q4_K: any ubatch, it has no other MFMA form), feature
+// counts that are whole 256-feature tiles.
 bool dl_shape(const QMat &W, int M, int ldx) {
     // the direct loads address operands by 32-bit byte offsets from a base
-    const size_t row_bytes = W.wtype == T_Q4_0 ? (size_t)W.K / 2 : (size_t)W.K;
-    return g_gemm_dl > 0 && !g_gemm_f16w && M > 64 && W.N % gemm_dl_tile_features() == 0 &&
-           (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * row_bytes < ((size_t)1 << 31);
+    const size_t row_bytes = W.wtype == T_Q8_0 ? (size_t)W.K : (size_t)W.K / 2;
+    const bool k4 = W.wtype == T_Q4_K;
+    return g_gemm_dl > 0 && (k4 || (!g_gemm_f16w && M > 64)) && W.N % gemm_dl_tile_features() == 0 &&
+           (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * row_bytes < ((size_t)1 << 31) &&
+           (size_t)M * (W.K / 32) * 4 < ((size_t)1 << 31);
 }
+
+// Bytes of the Q4_K block sums at the start of the workspace.
+size_t q4k_sums_bytes(const QMat &W, int M) { return ((size_t)M * (W.K / 32) * 4 + 255) / 256 * 256; }
 
 int dl_split(const QMat &W, int M) {
     const long tiles = (long)(W.N / gemm_dl_tile_features()) *
                        ((M + gemm_dl_tile_tokens() - 1) / gemm_dl_tile_tokens());
-    const long slots = (g_gemm_dl == 4 ? 1L : 2L) * g_gemm_cu;
+    const long slots = (g_gemm_dl == 4 && W.wtype != T_Q4_K ? 1L : 2L) * g_gemm_cu;
     const int nb = W.K / 32;
     int best = 1;
     for (int S = 2; S <= 8; S *= 2)
@@ -804,6 +868,11 @@ void gemm_set_num_cu(int n) {
     }
 }
 
+void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, int K, float *xs, hipStream_t s) {
+    const long long n = (long long)M * (K / 32);
+    launch(k_block_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, Xh, Xl, ldx, M, K, xs);
+}
+
 void launch_splitk_sum(int epi, const float *ws, int S, int N, int M, const EpiArgs &ep, int pair_mode,
                        hipStream_t s) {
     const dim3 g((N / 2 + 255) / 256, M);
@@ -816,6 +885,11 @@ void launch_splitk_sum(int epi, const float *ws, int S, int N, int M, const EpiA
 }
 
 size_t gemm_workspace_bytes(const QMat &W, int M) {
+    if (M > 0 && W.wtype == T_Q4_K) {
+        if (!dl_shape(W, M, W.K)) return 0;
+        const int Sd = dl_split(W, M);
+        return q4k_sums_bytes(W, M) + (Sd > 1 ? (size_t)Sd * M * W.N * 4 : (size_t)0);
+    }
     if (M <= 0 || !mfma_shape(W, 8)) return 0;
     const int S = split_for(W, M);
     size_t tile = S > 1 ? (size_t)S * M * W.N * 4 : 0;
@@ -833,6 +907,26 @@ bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
     if (M <= 0 || W.N % 2 || !Xh || !Xl) return false;
     const int pair_mode = ep.epi == EPI_SWIGLU ? PAIR_GU : PAIR_ADJ;
     if (pair_mode == PAIR_GU && W.N % 64) return false;
+    if (W.wtype == T_Q4_K) {
+        const size_t xsb = q4k_sums_bytes(W, M);
+        if (ldx % 8 == 0 && dl_shape(W, M, ldx) && ws && ws_bytes >= xsb) {
+            float *part = ws + xsb / 4;
+            int S = dl_split(W, M);
+            while (S > 1 && (size_t)S * M * W.N * 4 > ws_bytes - xsb) S >>= 1;
+            launch_block_sums(Xh, Xl, ldx, M, W.K, ws, s);
+            launch_gemm_dl(23, W, Xh, Xl, ldx, ep, M, pair_mode, S, part, ws, s);
+            return true;
+        }
+        const dim3 g((W.N / 2 + 255) / 256, M);
+        switch (ep.epi) {
+        case EPI_STORE: launch(k_gemm_q4k<EPI_STORE>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
+        case EPI_RESID: launch(k_gemm_q4k<EPI_RESID>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
+        case EPI_QKV: launch(k_gemm_q4k<EPI_QKV>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
+        case EPI_SWIGLU: launch(k_gemm_q4k<EPI_SWIGLU>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
+        default: return false;
+        }
+        return true;
+    }
     // skinny form for at most 32 tokens and at most 4096 features: there the
     // tiled grid is too small to spread over the chip (wider matrices stay
     // on the tiles, whose LDS-shared activations cost less L2 traffic)
@@ -858,7 +952,7 @@ bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
     if (mfma_shape(W, ldx) && dl_shape(W, M, ldx)) {
         int S = dl_split(W, M);
         while (S > 1 && (!ws || (size_t)S * M * W.N * 4 > ws_bytes)) S >>= 1;
-        launch_gemm_dl(g_gemm_dl, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+        launch_gemm_dl(g_gemm_dl, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, nullptr, s);
         return true;
     }
     if (mfma_shape(W, ldx)) {

@@ -37,6 +37,15 @@
 // Feature tiles of one block tile share an XCD (round-robin block placement),
 // as in k_gemm_mfma; K splits write fp32 partial tiles summed in order by
 // k_gemm_splitk_sum.
+//
+// Q4_K (256-weight super-blocks of eight 32-weight sub-blocks; weight = d sc q
+// - dmin m): the K block is a sub-block.  Its codes (stored in the Q4_0
+// nibble layout) enter the matrix cores as exact f16 values q = 0..15, the
+// temporary tile T = sum q x is scaled by d sc, and the min term is
+// dmin m times the token's block sum of x, which a small kernel writes
+// beforehand ([M][K/32] fp32): C += (d sc) T - (dmin m) X.  The sc | m word
+// is loaded where the f16 scale goes, plus one dword of d | dmin per row and
+// one x sum per token.
 #include <type_traits>
 
 #include "common.h"
@@ -53,16 +62,24 @@ constexpr int DBM = 128;    // tokens per block
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Q4_K adds per stage the rows' super-block factors (d | dmin << 16, one
+// dword per row) and the tokens' block sums of x (one fp32 per token; the
+// sc | m word of a sub-block takes the scale's place).
 template <int WT>
 struct Geo {
-    static constexpr int CB = WT == T_Q4_0 ? 16 : 32;    // code bytes per row and K block
+    static constexpr bool K4 = WT == T_Q4_K;
+    static constexpr int CB = WT == T_Q8_0 ? 32 : 16;    // code bytes per row and K block
     static constexpr int ACT = DBM * 64;                 // one activation part per K block
     static constexpr int OFF_LO = ACT;
     static constexpr int OFF_CODES = 2 * ACT;
     static constexpr int OFF_SC = 2 * ACT + DBN * CB;
-    static constexpr int STAGE = OFF_SC + DBN * 4;      // a 2-byte direct load fills one dword per lane
+    static constexpr int OFF_DM = OFF_SC + DBN * 4;     // a 2-byte direct load fills one dword per lane
+    static constexpr int OFF_XS = OFF_DM + (K4 ? DBN * 4 : 0);
+    // (x sums: waves 0, 1 load the 128 tokens, waves 2, 3 the same into a spare 512 bytes)
+    static constexpr int STAGE = OFF_XS + (K4 ? 1024 : 0);
     // direct loads per wavefront and K block: 4 activation, 1 or 2 code, 1 scale
-    static constexpr int LOADS = 4 + DBN * CB / 4096 + 1;
+    // (Q4_K: + 1 factor, 1 x sum)
+    static constexpr int LOADS = 4 + DBN * CB / 4096 + 1 + (K4 ? 2 : 0);
 };
 
 // Slot of chunk c of token row m (see the header): the 16-byte reads of a
@@ -78,6 +95,17 @@ DEV h2 magic_hi(uint32_t v) { return as_h2(__builtin_amdgcn_perm(0x64646464u, v,
 // nibbles) -> exact f16 values q - 8 of the two k-halves.
 DEV void q4_pair(u32x2 raw, h8 &k0, h8 &k1) {
     const h2 off = h2{(f16)1032.f, (f16)1032.f};
+    const uint32_t l0 = raw.x & 0x0F0F0F0Fu, l1 = raw.y & 0x0F0F0F0Fu;
+    const uint32_t u0 = (raw.x >> 4) & 0x0F0F0F0Fu, u1 = (raw.y >> 4) & 0x0F0F0F0Fu;
+    const h2 a0 = magic_lo(l0) - off, a1 = magic_hi(l0) - off, a2 = magic_lo(l1) - off, a3 = magic_hi(l1) - off;
+    const h2 b0 = magic_lo(u0) - off, b1 = magic_hi(u0) - off, b2 = magic_lo(u1) - off, b3 = magic_hi(u1) - off;
+    k0 = h8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+    k1 = h8{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+}
+
+// Q4_K: the same bytes -> exact f16 values q (codes 0..15, no shift).
+DEV void q4k_pair(u32x2 raw, h8 &k0, h8 &k1) {
+    const h2 off = h2{(f16)1024.f, (f16)1024.f};
     const uint32_t l0 = raw.x & 0x0F0F0F0Fu, l1 = raw.y & 0x0F0F0F0Fu;
     const uint32_t u0 = (raw.x >> 4) & 0x0F0F0F0Fu, u1 = (raw.y >> 4) & 0x0F0F0F0Fu;
     const h2 a0 = magic_lo(l0) - off, a1 = magic_hi(l0) - off, a2 = magic_lo(l1) - off, a3 = magic_hi(l1) - off;
@@ -125,6 +153,10 @@ DEV void dma16s(const void *base, uint32_t off, const void AS3 *lds) {
     const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m) : "memory");
 }
+DEV void dma4s(const void *base, uint32_t off, const void AS3 *lds) {
+    const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(m) : "memory");
+}
 DEV void dma2s(const void *base, uint32_t off, const void AS3 *lds) {
     const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(off), "s"(base), "s"(m) : "memory");
@@ -141,8 +173,9 @@ DEV void dma2(const void *src, const void AS3 *lds) {
 template <int WT, int EPI, bool SPLIT, int NS, int MF, int WL>
 __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const uint16_t *Xh, const uint16_t *Xl,
                                                                   int ldx, EpiArgs ep, int M, int pair_mode, int NT,
-                                                                  int nsplit, float *part) {
+                                                                  int nsplit, float *part, const float *xs) {
     using G = Geo<WT>;
+    constexpr bool Q4L = WT != T_Q8_0;    // 16 code bytes per row and K block
     __shared__ __attribute__((aligned(16))) uint8_t S0[G::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t S1[G::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t S2[NS > 2 ? G::STAGE : 16];
@@ -182,11 +215,11 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
     }
     // codes: Q4_0 one row of 16 bytes per lane (rows 64w + lane); Q8_0 two
     // instructions of 32 rows x 2 halves
-    const size_t row_bytes = WT == T_Q4_0 ? (size_t)(W.K >> 1) : (size_t)W.K;
+    const size_t row_bytes = Q4L ? (size_t)(W.K >> 1) : (size_t)W.K;
     uint32_t co[2];
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-        if (WT == T_Q4_0) {
+        if (Q4L) {
             co[i] = (uint32_t)((size_t)(64 * w + lane) * row_bytes);
         } else {
             const int slot = 64 * (w + 4 * i) + lane, r = slot >> 1, half = (slot & 1) ^ ((r >> 3) & 1);
@@ -196,8 +229,14 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
     const uint32_t so = (uint32_t)((size_t)(64 * w + lane) * nb_all * 2);
     const uint8_t *xh_base = (const uint8_t *)Xh + (size_t)kb0 * 64;
     const uint8_t *xl_base = (const uint8_t *)Xl + (size_t)kb0 * 64;
-    const uint8_t *c_base = (const uint8_t *)W.qs + (size_t)n0 * row_bytes + (size_t)kb0 * (WT == T_Q4_0 ? 16 : 32);
+    const uint8_t *c_base = (const uint8_t *)W.qs + (size_t)n0 * row_bytes + (size_t)kb0 * (Q4L ? 16 : 32);
     const uint8_t *s_base = (const uint8_t *)W.d + ((size_t)n0 * nb_all + kb0) * 2;
+    // Q4_K: factors of rows 64w + lane (super-block (kb0 + k) / 8) and x sums
+    // of tokens m0 + 64 (w & 1) + lane (rows past M repeat row M-1)
+    const uint32_t dmo = G::K4 ? (uint32_t)((size_t)(64 * w + lane) * (nb_all >> 3) * 4) : 0u;
+    const uint32_t xso = G::K4 ? (uint32_t)((size_t)min(m0 + 64 * (w & 1) + lane, M - 1) * nb_all * 4) : 0u;
+    const uint8_t *dm_base = G::K4 ? (const uint8_t *)W.dm + (size_t)n0 * (nb_all >> 3) * 4 : nullptr;
+    const uint8_t *xs_base = G::K4 ? (const uint8_t *)xs + (size_t)kb0 * 4 : nullptr;
 
     auto stage_ptr = [&](auto sc) -> uint8_t * {
         constexpr int s = decltype(sc)::value;
@@ -217,7 +256,7 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
             dma16s(xh_base + k * 64, xo[i], (const void AS3 *)(st + 1024 * (w + 4 * i)));
             dma16s(xl_base + k * 64, xo[i], (const void AS3 *)(st + G::OFF_LO + 1024 * (w + 4 * i)));
         }
-        if (WT == T_Q4_0) {
+        if (Q4L) {
             dma16s(c_base + k * 16, co[0], (const void AS3 *)(st + G::OFF_CODES + 1024 * w));
         } else {
 #pragma unroll
@@ -225,6 +264,10 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
                 dma16s(c_base + k * 32, co[i], (const void AS3 *)(st + G::OFF_CODES + 1024 * (w + 4 * i)));
         }
         dma2s(s_base + k * 2, so, (const void AS3 *)(st + G::OFF_SC + 256 * w));
+        if constexpr (G::K4) {
+            dma4s(dm_base + ((kb0 + k) >> 3) * 4, dmo, (const void AS3 *)(st + G::OFF_DM + 256 * w));
+            dma4s(xs_base + k * 4, xso, (const void AS3 *)(st + G::OFF_XS + 256 * w));
+        }
     };
 
     // MF = 32: 32x32 tiles, 4 feature x 2 token tiles per wavefront;
@@ -292,8 +335,9 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
         if constexpr (MF == 32 && decltype(sc)::value >= 0) {
         const uint8_t *st = stage_ptr(sc);
         // the wavefront's feature tiles: codes of both k-halves and the scale
+        // (Q4_K: d sc and dmin m of the sub-block)
         h8 c0[TA], c1[TA];
-        float d[TA];
+        float d[TA], mf[TA];
 #pragma unroll
         for (int a = 0; a < TA; a++) {
             const int f = wn + 32 * a + (lane & 31);
@@ -301,6 +345,9 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
             if (WT == T_Q4_0) {
                 const u32x4 v = *(const u32x4 *)(st + G::OFF_CODES + 16 * f);
                 q4_pair(hi8 ? u32x2{v.z, v.w} : u32x2{v.x, v.y}, c0[a], c1[a]);
+            } else if (WT == T_Q4_K) {
+                const u32x4 v = *(const u32x4 *)(st + G::OFF_CODES + 16 * f);
+                q4k_pair(hi8 ? u32x2{v.z, v.w} : u32x2{v.x, v.y}, c0[a], c1[a]);
             } else {
                 const int sw = (f >> 3) & 1;
                 const u32x4 v0 = *(const u32x4 *)(st + G::OFF_CODES + 32 * f + 16 * sw);
@@ -308,7 +355,14 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
                 c0[a] = q8_eight(hi8 ? u32x2{v0.z, v0.w} : u32x2{v0.x, v0.y});
                 c1[a] = q8_eight(hi8 ? u32x2{v1.z, v1.w} : u32x2{v1.x, v1.y});
             }
-            d[a] = f16_bits_to_f32(*(const uint16_t *)(st + G::OFF_SC + 4 * f));
+            if constexpr (G::K4) {
+                const uint32_t sm = *(const uint32_t *)(st + G::OFF_SC + 4 * f);
+                const uint32_t dd = *(const uint32_t *)(st + G::OFF_DM + 4 * f);
+                d[a] = f16_bits_to_f32((uint16_t)dd) * (float)(sm & 63);
+                mf[a] = f16_bits_to_f32((uint16_t)(dd >> 16)) * (float)((sm >> 8) & 63);
+            } else {
+                d[a] = f16_bits_to_f32(*(const uint16_t *)(st + G::OFF_SC + 4 * f));
+            }
         }
         // (keeps the token tiles' fragment reads below: hoisted above, they
         // would hold registers the codes need)
@@ -323,14 +377,27 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
                 xh[h] = *(const h8 *)(st + 16 * slot);
                 xl[h] = *(const h8 *)(st + G::OFF_LO + 16 * slot);
             }
+            // Q4_K: block sums of x of this lane's 16 tokens (accumulator r:
+            // token 32b + (r/4)*8 + (lane/32)*4 + r%4)
+            f4 xsv[G::K4 ? 4 : 1];
+            if constexpr (G::K4) {
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    xsv[i] = *(const f4 *)(st + G::OFF_XS + 4 * (wm + 32 * b + 8 * i + 4 * (lane >> 5)));
+            }
 #pragma unroll
             for (int a = 0; a < TA; a++) {
                 f16x t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[0], c0[a], f16x{}, 0, 0, 0);
                 t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[0], c0[a], t, 0, 0, 0);
                 t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[1], c1[a], t, 0, 0, 0);
                 t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[1], c1[a], t, 0, 0, 0);
+                if constexpr (G::K4) {
 #pragma unroll
-                for (int r = 0; r < 16; r++) acc[a][b][r] += d[a] * t[r];
+                    for (int r = 0; r < 16; r++) acc[a][b][r] += d[a] * t[r] - mf[a] * xsv[r >> 2][r & 3];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; r++) acc[a][b][r] += d[a] * t[r];
+                }
             }
         }
         }
@@ -442,39 +509,45 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
 
 template <int WT, int EPI, bool SPLIT>
 void launch_dl_ns(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
-                  int pair_mode, int S, float *part, hipStream_t s) {
+                  int pair_mode, int S, float *part, const float *xs, hipStream_t s) {
     const int NT = W.N / DBN, NT8 = (NT + 7) / 8 * 8;
     const dim3 grid(NT8 * ((M + DBM - 1) / DBM) * S);
+    if constexpr (WT == T_Q4_K) {   // one form: 3 stages, 32x32 tiles, 64-feature wavefront tiles
+        launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 1>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S,
+               part, xs);
+        return;
+    } else {
     // ns: 3 or 4 LDS stages on 32x32 tiles (wavefront tile 128 features x 64
     // tokens); 13: 3 stages on 16x16 tiles; 23: 3 stages, 32x32 tiles,
     // wavefront tile 64 features x 128 tokens
     switch (ns) {
-    case 4: launch((k_gemm_dl<WT, EPI, SPLIT, 4, 32, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
-    case 13: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 16, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
-    case 23: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 1>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
-    default: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part); break;
+    case 4: launch((k_gemm_dl<WT, EPI, SPLIT, 4, 32, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
+    case 13: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 16, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
+    case 23: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 1>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
+    default: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
+    }
     }
 }
 
 template <int WT, int EPI>
 void launch_dl_epi(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
-                   int pair_mode, int S, float *ws, hipStream_t s) {
+                   int pair_mode, int S, float *ws, const float *xs, hipStream_t s) {
     if (S > 1) {
-        launch_dl_ns<WT, EPI, true>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+        launch_dl_ns<WT, EPI, true>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s);
         launch_splitk_sum(EPI, ws, S, W.N, M, ep, pair_mode, s);
     } else {
-        launch_dl_ns<WT, EPI, false>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, 1, nullptr, s);
+        launch_dl_ns<WT, EPI, false>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, 1, nullptr, xs, s);
     }
 }
 
 template <int WT>
 void launch_dl_wt(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
-                  int pair_mode, int S, float *ws, hipStream_t s) {
+                  int pair_mode, int S, float *ws, const float *xs, hipStream_t s) {
     switch (ep.epi) {
-    case EPI_STORE: launch_dl_epi<WT, EPI_STORE>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
-    case EPI_RESID: launch_dl_epi<WT, EPI_RESID>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
-    case EPI_QKV: launch_dl_epi<WT, EPI_QKV>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
-    case EPI_SWIGLU: launch_dl_epi<WT, EPI_SWIGLU>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_STORE: launch_dl_epi<WT, EPI_STORE>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
+    case EPI_RESID: launch_dl_epi<WT, EPI_RESID>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
+    case EPI_QKV: launch_dl_epi<WT, EPI_QKV>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
+    case EPI_SWIGLU: launch_dl_epi<WT, EPI_SWIGLU>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
     }
 }
 
@@ -484,9 +557,11 @@ int gemm_dl_tile_features() { return DBN; }
 int gemm_dl_tile_tokens() { return DBM; }
 
 void launch_gemm_dl(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
-                    int M, int pair_mode, int S, float *ws, hipStream_t s) {
+                    int M, int pair_mode, int S, float *ws, const float *xs, hipStream_t s) {
     if (W.wtype == T_Q4_0)
-        launch_dl_wt<T_Q4_0>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+        launch_dl_wt<T_Q4_0>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, nullptr, s);
+    else if (W.wtype == T_Q4_K)
+        launch_dl_wt<T_Q4_K>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s);
     else
-        launch_dl_wt<T_Q8_0>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+        launch_dl_wt<T_Q8_0>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, nullptr, s);
 }

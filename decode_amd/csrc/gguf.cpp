@@ -135,6 +135,7 @@ uint64_t type_bytes(uint32_t type, uint64_t ne0, uint64_t rows) {
     case T_F16: return ne0 * rows * 2;
     case T_Q4_0: return ne0 % 32 ? 0 : ne0 / 32 * 18 * rows;
     case T_Q8_0: return ne0 % 32 ? 0 : ne0 / 32 * 34 * rows;
+    case T_Q4_K: return ne0 % 256 ? 0 : ne0 / 256 * 144 * rows;
     default: return 0;
     }
 }
@@ -205,7 +206,8 @@ int File::parse() {
             rows *= T.dims[j];
         }
         if (T.dims[0] > (1ull << 42) / rows) return E_MALFORMED;   // keeps the byte counts below 2^46
-        if (T.type != T_F32 && T.type != T_F16 && T.type != T_Q4_0 && T.type != T_Q8_0) return E_TYPE;
+        if (T.type != T_F32 && T.type != T_F16 && T.type != T_Q4_0 && T.type != T_Q8_0 && T.type != T_Q4_K)
+            return E_TYPE;
         T.nbytes = type_bytes(T.type, T.dims[0], rows);
         if (T.nbytes == 0) return E_MALFORMED;
         if (T.offset % alignment) return E_MALFORMED;

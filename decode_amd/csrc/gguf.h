@@ -27,7 +27,7 @@ enum ValueType : uint32_t {
 };
 
 // element types this library reads and writes (ggml numbering)
-enum TensorType : uint32_t { T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q8_0 = 8 };
+enum TensorType : uint32_t { T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12 };
 
 // result codes (negative = rejected)
 enum Status {

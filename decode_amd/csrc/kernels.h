@@ -32,11 +32,16 @@ inline void launch(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s,
 //   Q8_0: qs = int8 codes [N][K],           d = f16 scales [N][K/32]
 //   Q4_0: qs = packed nibbles [N][K/2]      d = f16 scales [N][K/32]
 //         (16 bytes per 32-weight block, byte k = code k | code k+16 << 4)
+//   Q4_K: qs = packed nibbles [N][K/2] in the Q4_0 layout (codes 0..15 of
+//         each 32-weight sub-block), d = sub-block scale | min << 8 [N][K/32]
+//         (six-bit integers), dm = f16 d | f16 dmin << 16 [N][K/256]
+//         (super-block factors): weight = f(d) * sc * q - f(dmin) * m
 struct QMat {
     int wtype = 0;
     int N = 0, K = 0;
     void *qs = nullptr;
     uint16_t *d = nullptr;
+    uint32_t *dm = nullptr;
 };
 
 // How output rows of a matrix pair up in an epilogue.
@@ -117,7 +122,8 @@ void launch_quantize(const float *src, int rows, int K, QMat &m, int mode, int r
 void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, int row_off,
                      hipStream_t s);
 // GGUF-style blocks (f16 scale + codes, 18 / 34 bytes, 2-byte aligned) of a
-// rows x K Q4_0 / Q8_0 tensor -> scales and codes of rows dst_row(r) of m.
+// rows x K Q4_0 / Q8_0 tensor, or 144-byte Q4_K super-blocks (16-byte
+// aligned), -> scales and codes of rows dst_row(r) of m.
 void launch_put_blocks(const void *src, int rows, int K, QMat &m, int mode, int row_off, hipStream_t s);
 // Q8_0 cache: codes the T staged K and V rows (kv.stage) into the cells at
 // (tok.seq[t], tok.pos[t]), with the weights' Q8_0 block definition.
@@ -134,9 +140,10 @@ int matvec_slices(int N, int K, int num_cu);
 bool launch_matvec(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, hipStream_t s);
 // Y = X W^T for T tokens (prefill / batched decode), X = Xh + Xl given as two
 // f16 arrays [T][ldx] (value and rounding remainder): MFMA for Q8_0 / Q4_0
-// with N % 128 == 0, a plain fp32 kernel otherwise.  `ws` (ws_bytes) holds
-// the fp32 partial tiles of a K split; with too little workspace (or none)
-// the GEMM splits K less (or not at all).
+// with N % 128 == 0 and Q4_K with N % 256 == 0, a plain fp32 kernel
+// otherwise.  `ws` (ws_bytes) holds the fp32 partial tiles of a K split (and
+// for Q4_K first the tokens' block sums); with too little workspace (or none)
+// the GEMM splits K less (or not at all; Q4_K then takes the plain kernel).
 bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
                  int T, float *ws, size_t ws_bytes, hipStream_t s);
 // Workspace launch_gemm uses for W at T tokens (0 when it does not split K).
@@ -144,8 +151,12 @@ size_t gemm_workspace_bytes(const QMat &W, int T);
 // The direct-to-LDS form of the ubatch GEMM (gemm_dl.hip): a block tile of
 // gemm_dl_tile_features() x gemm_dl_tile_tokens(), `ns` LDS stages (3, 4 or
 // 5), K split S (fp32 partial tiles in ws, summed by launch_splitk_sum).
+// Q4_K also reads xs, the tokens' block sums of x ([M][K/32] fp32, written by
+// launch_block_sums).
 void launch_gemm_dl(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
-                    int M, int pair_mode, int S, float *ws, hipStream_t s);
+                    int M, int pair_mode, int S, float *ws, const float *xs, hipStream_t s);
+// xs[m][kb] = sum over the 32 elements of block kb of (Xh + Xl)[m] (fp32, in order).
+void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, int K, float *xs, hipStream_t s);
 int gemm_dl_tile_features();
 int gemm_dl_tile_tokens();
 // Sums S fp32 partial tiles [S][M][N] in split order and applies epilogue epi.

@@ -1,6 +1,6 @@
 // matvec.hip -- dequant-fused block-quantized mat-vec for decode (gfx950).
 //
-// y = W x with W in Q8_0 / Q4_0 blocks and x an activation row.  This is the
+// y = W x with W in Q8_0 / Q4_0 blocks (or Q4_K sub-blocks) and x an activation row.  This is the
 // memory-bound heart of a decode step: every weight byte is read once per
 // step, so the kernel is built around streaming the code bytes with 16-byte
 // coalesced loads and keeping the arithmetic per weight small.
@@ -52,6 +52,7 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
     constexpr bool NORM = EPI != EPI_RESID;   // every epilogue except the residual add reads a normalized row
     __shared__ __attribute__((aligned(16))) uint32_t img[(MV_KMAX / 32) * XROW];
     __shared__ float bsum[MV_KMAX / 32];
+    __shared__ float xsum[WT == T_Q4_K ? MV_KMAX / 32 : 1];   // Q4_K: plain block sums of x
     __shared__ float red[NW];
     __shared__ float part[S > 1 ? G * MV_MAXIT * S * 2 : 1];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -155,12 +156,18 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
                     lv[e] = lv4[j][e];
                 }
             }
-            float v = 0.f;
-            if (q < n4) v = put_group<WT>(img, q >> 3, q & 7, hv, lv);
+            float v = 0.f, pl = 0.f;
+            if (q < n4) v = put_group<WT>(img, q >> 3, q & 7, hv, lv, &pl);
             v += __shfl_xor(v, 1, 64);
             v += __shfl_xor(v, 2, 64);
             v += __shfl_xor(v, 4, 64);
             if (q < n4 && (q & 7) == 0) bsum[q >> 3] = v;
+            if constexpr (WT == T_Q4_K) {
+                pl += __shfl_xor(pl, 1, 64);
+                pl += __shfl_xor(pl, 2, 64);
+                pl += __shfl_xor(pl, 4, 64);
+                if (q < n4 && (q & 7) == 0) xsum[q >> 3] = pl;
+            }
         }
     }
     __syncthreads();
@@ -180,6 +187,7 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         }
     }
     const float xs = lane_ok ? bsum[bl] : 0.f;
+    const float xp_sum = WT == T_Q4_K && lane_ok ? xsum[bl] : 0.f;
 
     // ---- stream row pairs ----
     const Masks mk = make_masks();
@@ -188,17 +196,28 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         if (it >= iters) return;
         const int p = first + it * stride;
         float bd0, bd1;
-        if (WT == T_Q4_0) {
+        if (WT != T_Q8_0) {
             bd0 = blockdot_q4(cur.q[0][0][0], xp, mk);
             bd1 = blockdot_q4(cur.q[1][0][0], xp, mk);
         } else {
-            bd0 = blockdot_q8(cur.q[0][0][0], cur.q[0][0][WT == T_Q4_0 ? 0 : 1], xp, mk);
-            bd1 = blockdot_q8(cur.q[1][0][0], cur.q[1][0][WT == T_Q4_0 ? 0 : 1], xp, mk);
+            bd0 = blockdot_q8(cur.q[0][0][0], cur.q[0][0][WT == T_Q8_0 ? 1 : 0], xp, mk);
+            bd1 = blockdot_q8(cur.q[1][0][0], cur.q[1][0][WT == T_Q8_0 ? 1 : 0], xp, mk);
         }
         // (lanes past the slice hold zero activations and offset sum, and the
         // scale of a real block of the row: their products are 0)
-        float a0 = f16_bits_to_f32((uint16_t)(cur.d[0][0] >> cur.dsh[0][0])) * (bd0 - xs);
-        float a1 = f16_bits_to_f32((uint16_t)(cur.d[1][0] >> cur.dsh[1][0])) * (bd1 - xs);
+        float a0, a1;
+        if constexpr (WT == T_Q4_K) {
+            // d sc (q . x) - dmin m (sum x), with q . x = bd - offsets
+            const uint32_t s0 = cur.d[0][0] >> cur.dsh[0][0], s1 = cur.d[1][0] >> cur.dsh[1][0];
+            const uint32_t e0 = cur.dm[0][0], e1 = cur.dm[1][0];
+            a0 = f16_bits_to_f32((uint16_t)e0) * (float)(s0 & 63) * (bd0 - xs) -
+                 f16_bits_to_f32((uint16_t)(e0 >> 16)) * (float)((s0 >> 8) & 63) * xp_sum;
+            a1 = f16_bits_to_f32((uint16_t)e1) * (float)(s1 & 63) * (bd1 - xs) -
+                 f16_bits_to_f32((uint16_t)(e1 >> 16)) * (float)((s1 >> 8) & 63) * xp_sum;
+        } else {
+            a0 = f16_bits_to_f32((uint16_t)(cur.d[0][0] >> cur.dsh[0][0])) * (bd0 - xs);
+            a1 = f16_bits_to_f32((uint16_t)(cur.d[1][0] >> cur.dsh[1][0])) * (bd1 - xs);
+        }
         // everything read from this pair's registers is consumed above the
         // refill: a use below it would wait for the refill too (loads complete
         // in issue order), which would leave one pair in flight instead of D
@@ -269,7 +288,7 @@ int g_num_cu = 256;
 template <int WT, int S, int EPI>
 bool launch_epi(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, int pair_mode, hipStream_t s) {
     constexpr int NW = 16, G = NW / S;
-    constexpr int D = WT == T_Q4_0 ? 2 : 3;   // row pairs in flight per wavefront (deeper measured slower)
+    constexpr int D = WT != T_Q8_0 ? 2 : 3;   // row pairs in flight per wavefront (deeper measured slower)
     const int npairs = W.N / 2;
     int blocks = (npairs + G - 1) / G;
     if (blocks > g_num_cu) blocks = g_num_cu;
@@ -330,5 +349,6 @@ bool launch_matvec(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, hi
     if (pair_mode == PAIR_GU && W.N % 64) return false;
     if (W.wtype == T_Q4_0) return launch_wt<T_Q4_0>(W, in, ep, T, pair_mode, s);
     if (W.wtype == T_Q8_0) return launch_wt<T_Q8_0>(W, in, ep, T, pair_mode, s);
+    if (W.wtype == T_Q4_K) return launch_wt<T_Q4_K>(W, in, ep, T, pair_mode, s);
     return false;
 }

@@ -75,6 +75,87 @@ __global__ __launch_bounds__(256) void k_quantize(const float *src, int rows, in
     }
 }
 
+// Q4_K (super-blocks of 256 = 8 sub-blocks of 32; eight consecutive threads
+// take one super-block, a sub-block each): per sub-block j with smallest and
+// largest element lo_j, hi_j:
+//   mn_j = max(0, -lo_j); dmin = f16(max_j mn_j / 63); m_j = min(63, ceil(mn_j / dmin));
+//   s_j = max(0, (hi_j + m_j dmin) / 15); d = f16(max_j s_j / 63); sc_j = min(63, ceil(s_j / d));
+//   q = min(15, round-half-away((x + m_j dmin) * (1 / (d sc_j))))   (0 when d sc_j = 0)
+// in fp32 without contraction (d, dmin as their f16 values).  The maxima over
+// the super-block are exact whatever the order, so the eight threads meet by
+// lane exchange.
+__global__ __launch_bounds__(256) void k_quantize_q4k(const float *src, int rows, int K, QMat m, int mode,
+                                                      int row_off) {
+#pragma clang fp contract(off)
+    const int nb = K >> 5;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    // rows * nb is a multiple of 8 and each super-block's threads are 8
+    // aligned lanes, so a super-block is wholly in range or wholly out
+    if (idx >= (long long)rows * nb) return;
+    const int r = (int)(idx / nb), b = (int)(idx % nb);
+    const float *x = src + (size_t)r * K + b * 32;
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 32; j += 4) {
+        const float4 t = *(const float4 *)(x + j);
+        v[j] = t.x; v[j + 1] = t.y; v[j + 2] = t.z; v[j + 3] = t.w;
+    }
+    float lo = v[0], hi = v[0];
+#pragma unroll
+    for (int j = 1; j < 32; j++) {
+        if (v[j] < lo) lo = v[j];
+        if (v[j] > hi) hi = v[j];
+    }
+    const float mn = lo < 0.f ? -lo : 0.f;
+    float mmax = mn;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, o, 64));
+    const uint16_t dminh = f32_to_f16_bits(mmax / 63.0f);
+    const float dmin = f16_bits_to_f32(dminh);
+    int mj = 0;
+    if (dmin > 0.f) {
+        const float c = ceilf(mn / dmin);
+        mj = c > 63.f ? 63 : (int)c;
+    }
+    const float mf = (float)mj * dmin;
+    const float t = (hi + mf) / 15.0f;
+    const float sv = t > 0.f ? t : 0.f;
+    float smax = sv;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) smax = fmaxf(smax, __shfl_xor(smax, o, 64));
+    const uint16_t dh = f32_to_f16_bits(smax / 63.0f);
+    const float d = f16_bits_to_f32(dh);
+    int sj = 0;
+    if (d > 0.f) {
+        const float c = ceilf(sv / d);
+        sj = c > 63.f ? 63 : (int)c;
+    }
+    const float step = d * (float)sj;
+    const float inv = step > 0.f ? 1.0f / step : 0.f;
+    int code[32];
+#pragma unroll
+    for (int j = 0; j < 32; j++) {
+        const float u = (v[j] + mf) * inv;
+        int c = (int)roundf(u);
+        code[j] = c > 15 ? 15 : (c < 0 ? 0 : c);
+    }
+    uint32_t packed[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int k = 4 * i + e;
+            w |= (uint32_t)(code[k] | (code[k + 16] << 4)) << (8 * e);
+        }
+        packed[i] = w;
+    }
+    const int dr = dst_row(mode, r, row_off);
+    *(uint4 *)((uint8_t *)m.qs + (size_t)dr * (K >> 1) + b * 16) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    m.d[(size_t)dr * nb + b] = (uint16_t)(sj | (mj << 8));
+    if ((b & 7) == 0) m.dm[(size_t)dr * (K >> 8) + (b >> 3)] = (uint32_t)dh | ((uint32_t)dminh << 16);
+}
+
 __global__ __launch_bounds__(256) void k_copy_f32(const float *src, int rows, int K_src, QMat m,
                                                   int mode, int row_off) {
     const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -113,6 +194,41 @@ __global__ __launch_bounds__(256) void k_put_blocks(const uint16_t *src, int row
     for (int j = 0; j < cw; j++) q[j] = blk[1 + j];
 }
 
+// One thread per 144-byte Q4_K super-block of a file tensor (16-byte aligned:
+// the staging buffer is, and 144 = 9 x 16): header -> m.d (sc | m << 8 per
+// sub-block) and m.dm; codes -> the Q4_0 nibble layout per sub-block (file
+// byte 32g + l holds weight l of sub-blocks 2g (low nibble) and 2g+1 (high)).
+__global__ __launch_bounds__(256) void k_put_blocks_q4k(const uint4 *src, int rows, int K, QMat m, int mode,
+                                                        int row_off) {
+    const int ns = K >> 8;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)rows * ns) return;
+    const int r = (int)(idx / ns), sb = (int)(idx % ns);
+    const int dr = dst_row(mode, r, row_off);
+    union { uint4 v[9]; uint8_t b[144]; } blk;
+#pragma unroll
+    for (int i = 0; i < 9; i++) blk.v[i] = src[(size_t)idx * 9 + i];
+    const uint8_t *s = blk.b + 4;
+    m.dm[(size_t)dr * ns + sb] = (uint32_t)blk.b[0] | ((uint32_t)blk.b[1] << 8) | ((uint32_t)blk.b[2] << 16) |
+                                 ((uint32_t)blk.b[3] << 24);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const int sc = j < 4 ? (s[j] & 63) : ((s[j + 4] & 15) | ((s[j - 4] >> 6) << 4));
+        const int mn = j < 4 ? (s[j + 4] & 63) : ((s[j + 4] >> 4) | ((s[j] >> 6) << 4));
+        m.d[(size_t)dr * (K >> 5) + 8 * sb + j] = (uint16_t)(sc | (mn << 8));
+    }
+    const uint8_t *q = blk.b + 16;
+    uint8_t *dst = (uint8_t *)m.qs + (size_t)dr * (K >> 1) + (size_t)sb * 128;
+#pragma unroll
+    for (int g = 0; g < 4; g++)
+#pragma unroll
+        for (int k = 0; k < 16; k++) {
+            const uint8_t a = q[32 * g + k], c = q[32 * g + 16 + k];
+            dst[32 * g + k] = (uint8_t)((a & 15) | ((c & 15) << 4));         // sub-block 2g
+            dst[32 * g + 16 + k] = (uint8_t)((a >> 4) | (c & 0xF0));         // sub-block 2g+1
+        }
+}
+
 // ---- embedding: x[t] = dequantized row tok[t] (the article's get_rows) -----
 __global__ __launch_bounds__(256) void k_embed(QMat E, const int32_t *tok, float *x, int ldx, float *ss_out) {
     __shared__ float red[4];
@@ -125,6 +241,15 @@ __global__ __launch_bounds__(256) void k_embed(QMat E, const int32_t *tok, float
         float v;
         if (E.wtype == T_F32) {
             v = ((const float *)E.qs)[(size_t)row * K + j];
+        } else if (E.wtype == T_Q4_K) {
+#pragma clang fp contract(off)
+            const int b = j >> 5, e = j & 31;
+            const uint32_t dd = E.dm[(size_t)row * (K >> 8) + (b >> 3)];
+            const uint16_t sm = E.d[(size_t)row * nb + b];
+            const uint8_t byte = ((const uint8_t *)E.qs)[(size_t)row * (K >> 1) + b * 16 + (e & 15)];
+            const int c = e < 16 ? (byte & 15) : (byte >> 4);
+            v = f16_bits_to_f32((uint16_t)dd) * (float)(sm & 63) * (float)c -
+                f16_bits_to_f32((uint16_t)(dd >> 16)) * (float)(sm >> 8);
         } else {
             const int b = j >> 5, e = j & 31;
             const float d = f16_bits_to_f32(E.d[(size_t)row * nb + b]);
@@ -222,8 +347,10 @@ __global__ __launch_bounds__(256) void k_rope_table(float *cs, int n_ctx, int hd
 void launch_quantize(const float *src, int rows, int K, QMat &m, int mode, int row_off,
                      hipStream_t s) {
     const long long n = (long long)rows * (K / 32);
-    launch(k_quantize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows, K, m,
-                       mode, row_off);
+    if (m.wtype == T_Q4_K)
+        launch(k_quantize_q4k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows, K, m, mode, row_off);
+    else
+        launch(k_quantize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows, K, m, mode, row_off);
 }
 
 void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, int row_off,
@@ -234,6 +361,12 @@ void launch_copy_f32(const float *src, int rows, int K_src, QMat &m, int mode, i
 }
 
 void launch_put_blocks(const void *src, int rows, int K, QMat &m, int mode, int row_off, hipStream_t s) {
+    if (m.wtype == T_Q4_K) {
+        const long long n = (long long)rows * (K / 256);
+        launch(k_put_blocks_q4k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const uint4 *)src, rows, K, m,
+               mode, row_off);
+        return;
+    }
     const long long n = (long long)rows * (K / 32);
     launch(k_put_blocks, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const uint16_t *)src, rows, K, m,
            mode, row_off);

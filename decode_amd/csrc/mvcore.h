@@ -81,12 +81,15 @@ DEV float blockdot_q8(const u32x4 q0, const u32x4 q1, const h2 *xp, const Masks 
 
 constexpr int MV_KMAX = 16384;   // longest input row (elements); its LDS image holds 512 blocks
 
-// Code bytes + scales of one pair of rows for this lane's blocks.
+// Code bytes + scales of one pair of rows for this lane's blocks.  Q4_K
+// blocks are sub-blocks: codes as in Q4_0, `d` holds the six-bit scale and
+// min (sc | m << 8), `dm` the super-block's f16 d and dmin.
 template <int WT, int KB>
 struct PairLoad {
-    u32x4 q[2][KB][WT == T_Q4_0 ? 1 : 2];
+    u32x4 q[2][KB][WT == T_Q8_0 ? 2 : 1];
     uint32_t d[2][KB];     // the aligned dword holding the block's f16 scale ...
     uint32_t dsh[2][KB];   // ... at this bit offset
+    uint32_t dm[2][WT == T_Q4_K ? KB : 1];
 };
 
 // Blocks b0 + lane + 64*i (i < KB) of rows r0, r1; lanes past the slice end
@@ -100,7 +103,7 @@ DEV void load_pair(const QMat &W, int r0, int r1, int b0, int b1, int lane, Pair
     const int rows[2] = {r0, r1};
 #pragma unroll
     for (int r = 0; r < 2; r++) {
-        const GLB u32x4 *qr = WT == T_Q4_0
+        const GLB u32x4 *qr = WT != T_Q8_0
                                   ? (const GLB u32x4 *)((const GLB uint8_t *)gl(W.qs) + (size_t)rows[r] * (K >> 1))
                                   : (const GLB u32x4 *)((const GLB int8_t *)gl(W.qs) + (size_t)rows[r] * K);
 #pragma unroll
@@ -108,15 +111,16 @@ DEV void load_pair(const QMat &W, int r0, int r1, int b0, int b1, int lane, Pair
             const int bw = b0 + lane + 64 * i;
             const int b = bw < b1 ? bw : b1 - 1;
             // streaming loads: the weights are read once per step
-            if (WT == T_Q4_0) {
+            if (WT != T_Q8_0) {
                 L.q[r][i][0] = __builtin_nontemporal_load(qr + b);
             } else {
                 L.q[r][i][0] = __builtin_nontemporal_load(qr + 2 * b);
-                L.q[r][i][WT == T_Q4_0 ? 0 : 1] = __builtin_nontemporal_load(qr + 2 * b + 1);
+                L.q[r][i][WT == T_Q8_0 ? 1 : 0] = __builtin_nontemporal_load(qr + 2 * b + 1);
             }
             const size_t e = (size_t)rows[r] * nb + b;   // W.d is 256-byte aligned
             L.d[r][i] = *(const GLB uint32_t *)(gl(W.d) + (e & ~(size_t)1));
             L.dsh[r][i] = (uint32_t)(e & 1) * 16;
+            if constexpr (WT == T_Q4_K) L.dm[r][i] = gl(W.dm)[(size_t)rows[r] * (K >> 8) + (b >> 3)];
         }
     }
 }
@@ -136,11 +140,14 @@ DEV uint32_t pk(f16 a, f16 b) { return h2_bits(h2{a, b}); }
 // per block: Q4_0 keeps 1024 + q on codes 0..15 and (1024 + 16 q) / 16 on
 // codes 16..31, so sum (q - 8) x needs 1032 * sum(x[0..15]) + 72 *
 // sum(x[16..31]) subtracted; Q8_0 keeps 1024 + 128 + q everywhere.
+// Q4_K sub-blocks take the Q4_0 image with offsets 1024 (low nibbles) and
+// 64 (high nibbles) only, since their codes are 0..15 without a shift; their
+// min term needs the plain sum of the block's x, returned in *plain.
 template <int WT>
-DEV float put_group(uint32_t *img, int b, int g, const f16 *hv, const f16 *lv) {
+DEV float put_group(uint32_t *img, int b, int g, const f16 *hv, const f16 *lv, float *plain = nullptr) {
     uint32_t *row = img + (size_t)b * XROW;
     int p0, p1;
-    if (WT == T_Q4_0) {
+    if (WT != T_Q8_0) {
         p0 = g < 4 ? 4 * g : 4 * (g - 4) + 1;
         p1 = p0 + 2;
     } else {
@@ -154,6 +161,8 @@ DEV float put_group(uint32_t *img, int b, int g, const f16 *hv, const f16 *lv) {
     float sx = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; e++) sx += (float)hv[e] + (float)lv[e];
+    if (plain) *plain = sx;
+    if (WT == T_Q4_K) return sx * (g < 4 ? 1024.f : 64.f);
     return sx * (WT == T_Q8_0 ? 1152.f : (g < 4 ? 1032.f : 72.f));
 }
 

@@ -37,10 +37,22 @@ extern "C" {
  * (34 bytes).  Q4_0: blocks of 32 weights = f16 scale + 16 bytes of 4-bit
  * codes offset by 8; byte k holds code k (low nibble) and code k+16 (high
  * nibble) (18 bytes).  The article names these as GGUF tensor types of
- * fixed-size blocks sharing one scale (step 2c). */
-typedef enum { DEC_F32 = 0, DEC_F16 = 1, DEC_Q8_0 = 2, DEC_Q4_0 = 3 } dec_type;
+ * fixed-size blocks sharing one scale (step 2c).
+ * Q4_K (named there among the k-quant types, not defined): super-blocks of
+ * 256 weights in 144 bytes = f16 d, f16 dmin, 12 bytes of six-bit sub-block
+ * scales sc_j and mins m_j (j = 0..7, 32 weights each), 128 bytes of 4-bit
+ * codes q; a weight of sub-block j is d * sc_j * q - dmin * m_j.  For j < 4,
+ * sc_j and m_j are the low six bits of bytes j and j + 4 of the 12; for j >= 4
+ * they are the low / high nibble of byte j + 4 with the top two bits of bytes
+ * j - 4 / j above.  Code byte 32g + l holds weight 64g + l (low nibble) and
+ * 64g + 32 + l (high nibble).  This is the GGUF super-block, so files carry
+ * it unchanged.  The library quantizes fp32 weights to it with a min-max
+ * rule (per sub-block: the min maps to code 0 and the max to code 15, up to
+ * the six-bit rounding of sc_j and m_j, rounded up; codes rounded half away
+ * from zero), not with llama.cpp's scale search. */
+typedef enum { DEC_F32 = 0, DEC_F16 = 1, DEC_Q8_0 = 2, DEC_Q4_0 = 3, DEC_Q4_K = 4 } dec_type;
 
-/* Shape limits.  With Q8_0 / Q4_0 weights every matrix row (n_embd,
+/* Shape limits.  With quantized weights every matrix row (n_embd,
  * n_head * head_dim, n_ff) holds at most DEC_MAX_ROW elements: a decode step
  * keeps one whole input row on chip.  A context holds at most DEC_MAX_CTX
  * positions per sequence (split-K attention takes at most 1024 chunks of 64
@@ -49,13 +61,13 @@ enum { DEC_MAX_ROW = 16384, DEC_MAX_CTX = 65536 };
 
 /* Hyper-parameters (the article's step 4: embedding length, block count,
  * feed-forward length, head count, KV head count, RoPE frequency base).
- * wtype applies to every 2-D matrix (F32, Q8_0 or Q4_0); kvtype is the
+ * wtype applies to every 2-D matrix (F32, Q8_0, Q4_0 or Q4_K); kvtype is the
  * cache element type (F32, F16, or Q8_0: the KV-cache appendix's separately
  * typed key / value cache, here one type for both; each cached head row is
  * coded in 32-element Q8_0 blocks as it is appended, from the fp32 K / V
  * values, and attention reads code * scale).  Quantized weight types need
- * n_embd, n_ff and n_head*head_dim to be multiples of 32 and at most
- * DEC_MAX_ROW; head_dim must be 64, 128 or 256, and n_head a multiple of
+ * n_embd, n_ff and n_head*head_dim to be multiples of 32 (of 256 for Q4_K)
+ * and at most DEC_MAX_ROW; head_dim must be 64, 128 or 256, and n_head a multiple of
  * n_head_kv with at most 8 query heads per KV head. */
 typedef struct {
     int32_t n_layer, n_embd, n_head, n_head_kv, head_dim, n_ff, n_vocab;
@@ -92,7 +104,7 @@ typedef struct {
 typedef struct dec_model dec_model;
 typedef struct dec_ctx   dec_ctx;
 
-/* Loads (copies, and for Q8_0/Q4_0 quantizes on the device) every weight.
+/* Loads (copies, and for Q8_0 / Q4_0 / Q4_K quantizes on the device) every weight.
  * Returns a model handle, or NULL on invalid hyper-parameters, a NULL
  * weight pointer, allocation failure or a device error (article step 2a:
  * the load entry returns the model or nullptr).  The allocator struct is
@@ -105,8 +117,8 @@ enum { DEC_T_TOK_EMBD = 0, DEC_T_OUTPUT = 1, DEC_T_WQ = 2, DEC_T_WK = 3, DEC_T_W
        DEC_T_WO = 5, DEC_T_FFN_GATE = 6, DEC_T_FFN_UP = 7, DEC_T_FFN_DOWN = 8 };
 
 /* Copies one stored matrix to host memory dst in its file form: GGUF-style
- * blocks (34 or 18 bytes each, row-major, scale first) for Q8_0 / Q4_0, or
- * fp32 rows for F32.  `layer` is ignored for tok_embd and output.  Returns
+ * blocks (34 or 18 bytes each, row-major, scale first) for Q8_0 / Q4_0,
+ * 144-byte super-blocks for Q4_K, or fp32 rows for F32.  `layer` is ignored for tok_embd and output.  Returns
  * the byte count; when dst is NULL or cap is too small returns minus the
  * needed size (the article's size-probe convention, step 9); 0 on a bad id
  * or layer.  Synchronizes the load stream. */
@@ -125,7 +137,8 @@ void dec_model_free(dec_model *m);
  * key/value pairs; one record per tensor (name, dimensions with the row
  * length first, element type, data offset); the data section at the next
  * multiple of general.alignment (32 when absent).  Matrices are Q4_0 (18-byte
- * blocks), Q8_0 (34-byte blocks) or F32, all of one type; norm vectors F32.
+ * blocks, file type 2), Q8_0 (34-byte blocks, type 8), Q4_K (144-byte
+ * super-blocks, type 12) or F32, all of one type; norm vectors F32.
  * Keys read: general.architecture ("llama"), llama.embedding_length,
  * llama.block_count, llama.feed_forward_length, llama.attention.head_count
  * (required); llama.attention.head_count_kv (default head_count),

@@ -43,6 +43,10 @@ WORKLOADS = {
     "8b_q8_long": dict(n_layer=32, n_embd=4096, n_head=32, n_head_kv=8, head_dim=128,
                        n_ff=14336, n_vocab=32000, wtype=Q8_0, kvtype=F16, n_prompt=8192,
                        n_ubatch=512, n_decode=0, n_seq=1, seed=1004),
+    # 8B shape with Q4_K super-block weights, f16 KV; 4096 prompt, 256 decode steps.
+    "8b_q4k": dict(n_layer=32, n_embd=4096, n_head=32, n_head_kv=8, head_dim=128, n_ff=14336,
+                   n_vocab=32000, wtype=Q4_K, kvtype=F16, n_prompt=4096, n_ubatch=512,
+                   n_decode=256, n_seq=1, seed=1006),
     # 7B shape (MHA), Q4_0; 32 sequences x 2048 prompt, 128 steps of 32 tokens.
     "7b_q4_b32": dict(n_layer=32, n_embd=4096, n_head=32, n_head_kv=32, head_dim=128,
                       n_ff=11008, n_vocab=32000, wtype=Q4_0, kvtype=F16, n_prompt=2048,

@@ -13,7 +13,7 @@ from __future__ import annotations
 import struct
 
 U8, I8, U16, I16, U32, I32, F32, BOOL, STR, ARR, U64, I64, F64 = range(13)
-T_F32, T_F16, T_Q4_0, T_Q8_0 = 0, 1, 2, 8
+T_F32, T_F16, T_Q4_0, T_Q8_0, T_Q4_K = 0, 1, 2, 8, 12
 _SCALAR = {U8: "<B", I8: "<b", U16: "<H", I16: "<h", U32: "<I", I32: "<i", F32: "<f", BOOL: "<?",
            U64: "<Q", I64: "<q", F64: "<d"}
 
@@ -45,6 +45,8 @@ def tensor_nbytes(ttype: int, dims) -> int:
         return n // 32 * 18
     if ttype == T_Q8_0:
         return n // 32 * 34
+    if ttype == T_Q4_K:
+        return n // 256 * 144
     raise ValueError(ttype)
 
 

@@ -22,6 +22,10 @@ CASES = {
     # 1B shape, Q8_0: the workload's own 512-token ubatch, then 8 decode steps
     "1b_q8_512": dict(workload="1b_q8", n_prompt=512, prompt_seed=4002, n_ubatch=512,
                       rows=(0, 63, 64, 255, 256, 511), n_decode=8),
+    # 8B shape, Q4_K super-block weights: a full ubatch of 256 and a ragged
+    # one of 8 tokens, then 3 decode steps
+    "8b_q4k_264": dict(workload="8b_q4k", n_prompt=264, prompt_seed=4006, n_ubatch=256,
+                       rows=(0, 127, 128, 255, 256, 263), n_decode=3),
     # narrow and long: d 512, 2 layers, head_dim 128, 8 query / 2 KV heads
     # (GQA 4), Q4_0; a 4200-token prompt in ubatches of 512 (attention over
     # up to 4200 cached positions: many split-K chunks and flash key ranges)

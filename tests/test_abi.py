@@ -75,6 +75,10 @@ def test_shape_limits_rejected_before_the_device(dec):
     assert not L.dec_model_load(C.byref(wide_ff), C.byref(w), None, None)
     gqa16 = dec.Hparams(2, 256, 16, 1, 64, 512, 1024, 1e-5, 1e4, dec.Q8_0, dec.F16)
     assert not L.dec_model_load(C.byref(gqa16), C.byref(w), None, None)
+    # Q4_K rows are whole 256-weight super-blocks (d, n_head * head_dim, n_ff)
+    for d, nh, ff in ((288, 4, 512), (256, 2, 512), (256, 4, 544)):
+        k4 = dec.Hparams(2, d, nh, nh, 64, ff, 1024, 1e-5, 1e4, dec.Q4_K, dec.F16)
+        assert not L.dec_model_load(C.byref(k4), C.byref(w), None, None)
 
 
 def test_noalloc_sampler_rejects_arguments_before_the_device(dec):

@@ -50,7 +50,7 @@ def test_helper_round_trip():
     assert p["kv"]["llama.block_count"] == HP["n_layer"]
 
 
-@pytest.mark.parametrize("ttype,wt", [(G.T_Q4_0, 3), (G.T_Q8_0, 2), (G.T_F32, 0)])
+@pytest.mark.parametrize("ttype,wt", [(G.T_Q4_0, 3), (G.T_Q8_0, 2), (G.T_F32, 0), (G.T_Q4_K, 4)])
 def test_valid_file(dec, tmp_path, ttype, wt):
     ts = tensors(ttype=ttype)
     n, hp = inspect(dec, write(tmp_path, G.build(G.llama_kv(HP), ts)))
@@ -93,7 +93,7 @@ def test_alignment_key(dec, tmp_path):
 @pytest.mark.parametrize("case,code", [
     ("magic", -4), ("version2", -5), ("version4", -5), ("truncated_header", -6), ("truncated_data", -8),
     ("duplicate", -7), ("unknown_type", -10), ("missing_key", -9), ("missing_tensor", -9), ("wrong_dims", -9),
-    ("mixed_types", -9), ("arch", -9), ("bad_string", -6), ("empty", -6)])
+    ("mixed_types", -9), ("arch", -9), ("bad_string", -6), ("empty", -6), ("q4_k_partial_superblock", -6)])
 def test_rejected(dec, tmp_path, case, code):
     kv, ts = G.llama_kv(HP), tensors()
     if case == "magic":
@@ -109,7 +109,7 @@ def test_rejected(dec, tmp_path, case, code):
     elif case == "duplicate":
         b = G.build(kv, ts + [ts[3]])
     elif case == "unknown_type":
-        b = G.build(kv, ts + [("extra.weight", 12, [256, 4], bytes(144 * 4))])
+        b = G.build(kv, ts + [("extra.weight", 14, [256, 4], bytes(210 * 4))])
     elif case == "missing_key":
         b = G.build([x for x in kv if x[0] != "llama.block_count"], ts)
     elif case == "missing_tensor":
@@ -123,6 +123,10 @@ def test_rejected(dec, tmp_path, case, code):
                          for n, t, d, x in ts])
     elif case == "arch":
         b = G.build([("general.architecture", G.STR, "gptx")] + kv[1:], ts)
+    elif case == "q4_k_partial_superblock":
+        # Q4_K rows are whole 256-weight super-blocks: ffn_down rows of 288 are not
+        hp = dict(HP, n_ff=288)
+        b = G.build(G.llama_kv(hp), tensors(hp, ttype=G.T_Q4_K))
     elif case == "bad_string":
         good = G.build(kv, ts)
         # the first key's length field claims more bytes than the file holds

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 MATS = {"tok_embd": "token_embd.weight", "output": "output.weight"}
 LAYER_MATS = {"wq": "attn_q", "wk": "attn_k", "wv": "attn_v", "wo": "attn_output", "ffn_gate": "ffn_gate",
               "ffn_up": "ffn_up", "ffn_down": "ffn_down"}
-FILE_TYPE = {synth.Q4_0: G.T_Q4_0, synth.Q8_0: G.T_Q8_0, synth.F32: G.T_F32}
+FILE_TYPE = {synth.Q4_0: G.T_Q4_0, synth.Q8_0: G.T_Q8_0, synth.F32: G.T_F32, synth.Q4_K: G.T_Q4_K}
 
 
 @pytest.fixture(scope="module")
@@ -50,7 +50,7 @@ def weights(hp, seed):
     return w
 
 
-@pytest.mark.parametrize("wtype", [synth.Q4_0, synth.Q8_0, synth.F32])
+@pytest.mark.parametrize("wtype", [synth.Q4_0, synth.Q8_0, synth.F32, synth.Q4_K])
 def test_saved_file_layout_and_bytes(dec, orc, tmp_path, wtype):
     hp = model_hp(wtype)
     w = weights(hp, 51 + wtype)
@@ -82,7 +82,7 @@ def test_saved_file_layout_and_bytes(dec, orc, tmp_path, wtype):
         assert np.array_equal(blocks, om.tensor_bytes(key, layer or 0)), name
 
 
-@pytest.mark.parametrize("wtype,n_ff", [(synth.Q4_0, 512), (synth.Q8_0, 512), (synth.F32, 688)])
+@pytest.mark.parametrize("wtype,n_ff", [(synth.Q4_0, 512), (synth.Q8_0, 512), (synth.F32, 688), (synth.Q4_K, 512)])
 def test_load_round_trip_is_bitwise(dec, tmp_path, wtype, n_ff):
     """n_ff 688 with fp32 weights leaves the stored FFN rows / columns padded
     to 704: the loader must place the file's 688 and leave the rest zero."""
@@ -111,12 +111,13 @@ def test_load_round_trip_is_bitwise(dec, tmp_path, wtype, n_ff):
     gm.close()
 
 
-def test_foreign_file_tied_output_matches_oracle(dec, orc, tmp_path):
+@pytest.mark.parametrize("wtype", [synth.Q8_0, synth.Q4_K])
+def test_foreign_file_tied_output_matches_oracle(dec, orc, tmp_path, wtype):
     """Blocks quantized by the oracle, written by the test writer in shuffled
     order with extra keys and tensors, no output.weight (tied): the loaded
     model runs within tolerance of the oracle, and bit for bit like a model
     loaded from the same fp32 weights."""
-    hp = model_hp(synth.Q8_0)
+    hp = model_hp(wtype)
     w = weights(hp, 71)
     w["output"] = w["tok_embd"].copy()               # tied output
     om = orc.Model(hp, w)
@@ -128,7 +129,7 @@ def test_foreign_file_tied_output_matches_oracle(dec, orc, tmp_path):
             src = w[key] if layer is None else w[key][layer]
             ts.append((name, G.T_F32, dims, np.asarray(src, np.float32).tobytes()))
         else:
-            ts.append((name, G.T_Q8_0, dims, om.tensor_bytes(key, layer or 0).tobytes()))
+            ts.append((name, FILE_TYPE[wtype], dims, om.tensor_bytes(key, layer or 0).tobytes()))
     order = np.random.default_rng(3).permutation(len(ts))
     ts = [ts[i] for i in order] + [("rope_freqs.weight", G.T_F32, [32], bytes(128))]
     kv = [("general.name", G.STR, "synthetic")] + G.llama_kv(hp)[::-1] + [
