@@ -29,7 +29,8 @@ METRIC = "decode tokens/s + % HBM roofline (8B-shape Q4_0, bs=1); prefill tokens
 
 
 def block_bytes(wtype: int) -> float:
-    return {2: 34.0, 3: 18.0}.get(wtype, 128.0) / 32.0
+    """Bytes per weight of the file form: Q8_0 34 / 32, Q4_0 18 / 32, Q4_K 144 / 256, F32 4."""
+    return {2: 34.0 / 32, 3: 18.0 / 32, 4: 144.0 / 256}.get(wtype, 4.0)
 
 
 def algorithmic(hp, n_prompt, steps):
@@ -207,6 +208,72 @@ def kv_q8_leg(dec, torch, model, hp, prompt, n_ctx, n_ubatch, sp, warm, steps, p
                     "+ merge of one layer, timed live; prefill attention takes the split-K kernel"}
 
 
+def q4k_leg(dec, torch, model, hp, prompt, n_ctx, n_ubatch, sp, warm, steps, probe_layer, log):
+    """The generation loop with the same fp32 weights quantized to Q4_K
+    super-blocks: timed prefill (median of 3) and `steps` timed greedy decode
+    steps, then the gate/up mat-vec of the probed layer timed live over 16
+    decode steps and the gate/up GEMM of one prefill."""
+    ctx = dec.Context(model, n_ctx=n_ctx, n_batch=len(prompt), n_ubatch=n_ubatch, stream=sp)
+    assert ctx.prefill(prompt, 0) == 0
+    tok = ctx.argmax(-1)
+    for _ in range(warm):
+        assert ctx.decode([tok], [0]) == 0
+        tok = ctx.argmax(0)
+    pf = []
+    for _ in range(3):
+        ctx.clear(0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        assert ctx.prefill(prompt, 0) == 0
+        tok = ctx.argmax(-1)
+        pf.append(time.perf_counter() - t0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if ctx.decode([tok], [0]) != 0:
+            raise RuntimeError("Q4_K decode step failed")
+        tok = ctx.argmax(0)
+    torch.cuda.synchronize()
+    decode_s = time.perf_counter() - t0
+    ctx.set_probe(dec.K_FFN_GU, probe_layer)
+    for _ in range(16):
+        assert ctx.decode([tok], [0]) == 0
+        tok = ctx.argmax(0)
+    mv = ctx.probe()
+    ctx.set_probe(-1, 0)
+    ctx.clear(0)
+    ctx.set_probe(dec.K_FFN_GU, probe_layer)
+    assert ctx.prefill(prompt, 0) == 0
+    gm = ctx.probe()
+    ctx.close()
+    F, d = hp["n_ff"], hp["n_embd"]
+    prefill_s = sorted(pf)[1]
+    alg = algorithmic(hp, len(prompt), steps)
+    step_gbs = alg["token_bytes"] / (decode_s / steps) / 1e9
+    out = {"decode_tokens_per_s": round(steps / decode_s, 2), "steps": steps,
+           "prefill_tokens_per_s": round(len(prompt) / prefill_s, 1),
+           "decode_step_hbm": {"bytes_per_token": int(alg["token_bytes"]), "achieved_GBs": round(step_gbs, 1),
+                               "frac": round(step_gbs / HBM_PEAK_GBS, 4)}}
+    if mv and mv[1]:
+        avg = mv[0] / 1e3 / mv[1]
+        nb = 2 * F * d * block_bytes(4)
+        out["gate_up_matvec"] = {"bound": "hbm", "avg_us": round(avg * 1e6, 2), "bytes": int(nb),
+                                 "achieved": round(nb / avg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(nb / avg / 1e9 / HBM_PEAK_GBS, 4), "launches": mv[1]}
+    if gm and gm[1]:
+        avg = gm[0] / 1e3 / gm[1]
+        fl = 2.0 * n_ubatch * 2 * F * d
+        out["gate_up_gemm"] = {"bound": "mfma", "avg_us": round(avg * 1e6, 1),
+                               "achieved": round(fl / avg / 1e12, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(fl / avg / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                               "launches": gm[1]}
+    out["note"] = ("same fp32 weights quantized to Q4_K super-blocks (144 bytes per 256 weights; the "
+                   "library stores 148: codes, a 2-byte scale/min word per 32 and d/dmin per 256); "
+                   "algorithmic bytes count 144 per 256")
+    log(f"Q4_K weights: prefill {out['prefill_tokens_per_s']:.0f} tok/s, decode {out['decode_tokens_per_s']} tok/s")
+    return out
+
+
 def prefill_flops(hp, n_prompt, n_out=1):
     """FLOPs of a prefill of n_prompt tokens: the layers' projections for
     every token, causal attention over the unmasked pairs, and the output
@@ -372,6 +439,9 @@ def main():
     ap.add_argument("--no-kv-q8", action="store_true",
                     help="skip the leg that reruns the decode loop with a Q8_0 KV cache")
     ap.add_argument("--kv-q8-steps", type=int, default=128)
+    ap.add_argument("--no-q4k", action="store_true",
+                    help="skip the leg that reruns the generation loop with Q4_K weights")
+    ap.add_argument("--q4k-steps", type=int, default=128)
     ap.add_argument("--prefill-reps", type=int, default=3, help="timed prefills of a prefill-only workload")
     ap.add_argument("--no-step-kernel", action="store_true",
                     help="skip the leg that runs decode steps through the one-launch step kernel")
@@ -426,6 +496,11 @@ def main():
     if not args.no_kv_q8:
         # same weights, Q8_0 KV cache (the KV-cache appendix's quantized cache types)
         model_q8 = dec.Model(dict(hp, kvtype=synth.Q8_0), weights, stream=sp)
+        torch.cuda.synchronize()
+    model_k4 = None
+    if not args.no_q4k and hp["wtype"] != synth.Q4_K:
+        # same weights as Q4_K super-blocks (the k-quant type of the GGUF type list)
+        model_k4 = dec.Model(dict(hp, wtype=synth.Q4_K), weights, stream=sp)
         torch.cuda.synchronize()
     if args.no_cpu_baseline:
         del weights
@@ -588,6 +663,11 @@ def main():
         if "attention" in per_kernel:
             kv_q8["f16_attention"] = per_kernel["attention"]
         model_q8.close()
+    q4k = None
+    if model_k4 is not None:
+        q4k = q4k_leg(dec, torch, model_k4, dict(hp, wtype=synth.Q4_K), prompt, n_ctx, W["n_ubatch"], sp, warm,
+                      args.q4k_steps, probe_layer, log)
+        model_k4.close()
     model.close()
 
     alg = algorithmic(hp, n_prompt, steps)
@@ -600,7 +680,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4),
                     "traffic": None if traffic is None else int(traffic),
-                    "kernel": "k_matvec (gate/up, Q4_0 mat-vec + RMSNorm prologue + SwiGLU epilogue)",
+                    "kernel": "k_matvec (gate/up block-quantized mat-vec + RMSNorm prologue + SwiGLU epilogue)",
                     "bytes_per_launch": gu_bytes, "avg_us": round(gu_avg_s * 1e6, 2),
                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                     "kernel_source_sha256_16": kernel_source_hash(),
@@ -650,7 +730,7 @@ def main():
                            alg["mean_ctx"])
         del weights
 
-    wname = "Q8_0" if hp["wtype"] == synth.Q8_0 else "Q4_0"
+    wname = {synth.Q8_0: "Q8_0", synth.Q4_0: "Q4_0", synth.Q4_K: "Q4_K"}.get(hp["wtype"], "F32")
     kvname = {0: "f32", 1: "f16", 2: "Q8_0"}[hp["kvtype"]]
     out = {
         "metric": METRIC,
@@ -697,6 +777,7 @@ def main():
         "graph_replays": st["n_graph_replays"],
         "sampler": sampler,
         "kv_q8_0": kv_q8,
+        "q4_k": q4k,
         "step_kernel": step_leg,
         "cpu_baseline": cpu,
     }

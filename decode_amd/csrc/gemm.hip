@@ -32,8 +32,9 @@
 // RoPE pairs (adjacent features) sit in lanes l and l^1 and are exchanged.
 //
 // Fallback path (fp32 weights, or shapes the MFMA tiling does not cover):
-// one thread per (row pair, token), plain fp32 FMA.  Q4_K weights take the
-// direct-to-LDS form (gemm_dl.hip) or such a plain kernel.
+// one thread per (row pair, token), plain fp32 FMA (for quantized weights on
+// the codes, block by block).  Q4_K weights take the direct-to-LDS form
+// (gemm_dl.hip) or such a plain kernel.
 #include <stdlib.h>
 #include <string.h>
 
@@ -529,11 +530,13 @@ __global__ __launch_bounds__(256) void k_gemm_f32(QMat W, const uint16_t *X, con
     epi_pair<EPI>(ep, m, p, r0, r1, a, b);
 }
 
-// Q4_K weights (any N): one thread per (row pair, token); per sub-block
-// (d sc) sum q x - (dmin m) sum x in fp32.
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_q4k(QMat W, const uint16_t *X, const uint16_t *Xl, int ldx,
-                                                  EpiArgs ep, int M, int pair_mode) {
+// Block-quantized weights of any N (shapes the MFMA forms do not cover):
+// one thread per (row pair, token); per 32-weight block d * sum(c x) with c
+// the signed code (Q4_0: q - 8, Q8_0: q), or for a Q4_K sub-block
+// (d sc) sum q x - (dmin m) sum x, in fp32.
+template <int WT, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_plainq(QMat W, const uint16_t *X, const uint16_t *Xl, int ldx,
+                                                     EpiArgs ep, int M, int pair_mode) {
     const int p = blockIdx.x * 256 + threadIdx.x;
     const int m = blockIdx.y;
     if (p >= W.N / 2 || m >= M) return;
@@ -546,21 +549,30 @@ __global__ __launch_bounds__(256) void k_gemm_q4k(QMat W, const uint16_t *X, con
     const int rows[2] = {r0, r1};
     for (int i = 0; i < 2; i++) {
         const int row = rows[i];
-        const uint8_t *q = (const uint8_t *)W.qs + (size_t)row * (W.K >> 1);
+        const uint8_t *q = (const uint8_t *)W.qs + (size_t)row * (WT == T_Q8_0 ? W.K : W.K >> 1);
         float a = 0.f;
         for (int b = 0; b < nb; b++) {
-            const uint32_t dd = W.dm[(size_t)row * (W.K >> 8) + (b >> 3)];
-            const uint16_t sm = W.d[(size_t)row * nb + b];
             float t = 0.f, xs = 0.f;
             for (int k = 0; k < 32; k++) {
-                const uint8_t byte = q[b * 16 + (k & 15)];
-                const int c = k < 16 ? (byte & 15) : (byte >> 4);
+                int c;
+                if (WT == T_Q8_0) {
+                    c = (int)(int8_t)q[b * 32 + k];
+                } else {
+                    const uint8_t byte = q[b * 16 + (k & 15)];
+                    c = (k < 16 ? (byte & 15) : (byte >> 4)) - (WT == T_Q4_0 ? 8 : 0);
+                }
                 const float xv = (float)x[b * 32 + k] + (float)xl[b * 32 + k];
                 t += (float)c * xv;
                 xs += xv;
             }
-            a += f16_bits_to_f32((uint16_t)dd) * (float)(sm & 63) * t -
-                 f16_bits_to_f32((uint16_t)(dd >> 16)) * (float)((sm >> 8) & 63) * xs;
+            if (WT == T_Q4_K) {
+                const uint32_t dd = W.dm[(size_t)row * (W.K >> 8) + (b >> 3)];
+                const uint16_t sm = W.d[(size_t)row * nb + b];
+                a += f16_bits_to_f32((uint16_t)dd) * (float)(sm & 63) * t -
+                     f16_bits_to_f32((uint16_t)(dd >> 16)) * (float)((sm >> 8) & 63) * xs;
+            } else {
+                a += f16_bits_to_f32(W.d[(size_t)row * nb + b]) * t;
+            }
         }
         out[i] = a;
     }
@@ -732,6 +744,10 @@ int g_gemm_cu = 256;
 int g_gemm_f16w = 0;   // f16 operands for ubatches of more than 64 tokens (opt-in)
 int g_gemm_skinny = 1; // skinny form for ubatches of at most 32 tokens
 int g_gemm_dl = 23;    // direct-to-LDS form variant (0: off)
+int g_gemm_dls = 1;    // direct-to-LDS form with 32-token tiles for at most 32 tokens (0: skinny / tiles)
+int g_gemm_dls_ns = 4; // its LDS stages
+int g_gemm_dls_fill = 4; // its K split aims at this many blocks per 4 compute units
+int g_gemm_ws = 2;     // weight-streaming form for Q4_0 at most 32 tokens: K blocks per stage (0: off)
 
 bool mfma_shape(const QMat &W, int ldx) {
     return (W.wtype == T_Q4_0 || W.wtype == T_Q8_0) && W.N % BN == 0 && W.K % 32 == 0 && ldx % 8 == 0;
@@ -822,6 +838,20 @@ void launch_f32_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int l
                        ep, M, pair_mode);
 }
 
+template <int WT>
+bool launch_plainq(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                   int pair_mode, hipStream_t s) {
+    const dim3 g((W.N / 2 + 255) / 256, M);
+    switch (ep.epi) {
+    case EPI_STORE: launch(k_gemm_plainq<WT, EPI_STORE>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
+    case EPI_RESID: launch(k_gemm_plainq<WT, EPI_RESID>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
+    case EPI_QKV: launch(k_gemm_plainq<WT, EPI_QKV>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
+    case EPI_SWIGLU: launch(k_gemm_plainq<WT, EPI_SWIGLU>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
+    default: return false;
+    }
+    return true;
+}
+
 // Direct-to-LDS form (gemm_dl.hip): ubatches of more than 64 tokens with the
 // exact operands (Q4_K: any ubatch, it has no other MFMA form), feature
 // counts that are whole 256-feature tiles.
@@ -832,6 +862,48 @@ bool dl_shape(const QMat &W, int M, int ldx) {
     return g_gemm_dl > 0 && (k4 || (!g_gemm_f16w && M > 64)) && W.N % gemm_dl_tile_features() == 0 &&
            (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * row_bytes < ((size_t)1 << 31) &&
            (size_t)M * (W.K / 32) * 4 < ((size_t)1 << 31);
+}
+
+// The 32-token direct-to-LDS form: at most 32 tokens, whole 256-feature tiles.
+bool dls_shape(const QMat &W, int M, int ldx) {
+    const size_t row_bytes = W.wtype == T_Q8_0 ? (size_t)W.K : (size_t)W.K / 2;
+    return (g_gemm_dls || W.wtype == T_Q4_K) && g_gemm_dl > 0 && M > 0 && M <= gemm_dls_tile_tokens() &&
+           W.wtype != T_F32 && W.N % gemm_dl_tile_features() == 0 && ldx % 8 == 0 &&
+           (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * row_bytes < ((size_t)1 << 31);
+}
+
+// Its K split: doubled while the grid holds fewer than g_gemm_dls_fill blocks
+// per 4 compute units and every split keeps at least 4 K blocks (splits may
+// be uneven).
+int dls_split(const QMat &W, int M) {
+    const long tiles = (long)(W.N / gemm_dl_tile_features()) *
+                       ((M + gemm_dls_tile_tokens() - 1) / gemm_dls_tile_tokens());
+    const int nb = W.K / 32;
+    int S = 1;
+    while (S < 64 && tiles * S * 4 < (long)g_gemm_dls_fill * g_gemm_cu && nb / (2 * S) >= 4) S *= 2;
+    return S;
+}
+
+// The weight-streaming form (Q4_0, at most 32 tokens, K and N whole 256s).
+bool ws_shape(const QMat &W, int M, int ldx) {
+    return g_gemm_ws && g_gemm_dls && W.wtype == T_Q4_0 && M > 0 && M <= 32 && W.K % 256 == 0 &&
+           W.N % gemm_dl_tile_features() == 0 && ldx % 8 == 0 && (size_t)M * ldx * 2 < ((size_t)1 << 31) &&
+           (size_t)W.N * (W.K / 2) < ((size_t)1 << 31);
+}
+
+// Its K split, in whole octets of K blocks with at most
+// gemm_ws_max_blocks_per_split() K blocks per split: the fewest splits whose
+// grid fills half the resident block slots (2 per compute unit with 2 K
+// blocks per stage, 1 with 4).  More splits shorten each block's stream but
+// add fp32 partial tiles (S x M x N x 4 bytes written and read back), which
+// at 32 tokens weigh as much as the codes of several K blocks.
+int ws_split(const QMat &W, int M) {
+    const long tiles = (long)(W.N / gemm_dl_tile_features()) * ((M + 31) / 32);
+    const int no = W.K / 256, per = gemm_ws_max_blocks_per_split() / 8;
+    const long slots = (long)(g_gemm_ws == 2 ? 2 : 1) * g_gemm_cu;
+    int S = (no + per - 1) / per;
+    while (S < no && tiles * S * 2 < slots) S++;
+    return S;
 }
 
 // Bytes of the Q4_K block sums at the start of the workspace.
@@ -866,6 +938,26 @@ void gemm_set_num_cu(int n) {
         const int v = atoi(dl);
         g_gemm_dl = (v == 0 || v == 3 || v == 4 || v == 13 || v == 23) ? v : 23;
     }
+    // DECODE_GEMM_SMALL: "tiles" keeps the skinny form / register-staged
+    // tiles for ubatches of at most 32 tokens; else the 32-token direct-to-LDS
+    // form with DECODE_GEMM_DLS_NS stages (4, 6 or 8; default 4) and a K
+    // split for DECODE_GEMM_DLS_FILL blocks per 4 compute units (default 4)
+    const char *sm = getenv("DECODE_GEMM_SMALL");
+    g_gemm_dls = !(sm && strcmp(sm, "tiles") == 0);
+    const char *ns = getenv("DECODE_GEMM_DLS_NS");
+    g_gemm_dls_ns = 4;
+    if (ns) {
+        const int v = atoi(ns);
+        g_gemm_dls_ns = (v == 4 || v == 6 || v == 8) ? v : 4;
+    }
+    const char *fl = getenv("DECODE_GEMM_DLS_FILL");
+    g_gemm_dls_fill = fl && atoi(fl) > 0 ? atoi(fl) : 4;
+    // DECODE_GEMM_WS: K blocks per stage of the weight-streaming form (2 or 4,
+    // default 2); 0 leaves Q4_0 ubatches of at most 32 tokens to the 32-token
+    // direct-to-LDS form
+    const char *wsv = getenv("DECODE_GEMM_WS");
+    g_gemm_ws = 2;
+    if (wsv) g_gemm_ws = atoi(wsv) == 0 ? 0 : atoi(wsv) == 4 ? 4 : 2;
 }
 
 void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, int K, float *xs, hipStream_t s) {
@@ -885,10 +977,20 @@ void launch_splitk_sum(int epi, const float *ws, int S, int N, int M, const EpiA
 }
 
 size_t gemm_workspace_bytes(const QMat &W, int M) {
+    const int ms = M < gemm_dls_tile_tokens() ? M : gemm_dls_tile_tokens();
+    size_t small = 0;   // the 32-token forms, for any ubatch of at most min(M, 32) tokens
+    if (M > 0 && dls_shape(W, ms, W.K)) {
+        const int Ss = dls_split(W, ms);
+        small = Ss > 1 ? (size_t)Ss * ms * W.N * 4 : 0;
+    }
+    if (M > 0 && ws_shape(W, ms, W.K)) {
+        const int Sw = ws_split(W, ms);
+        small = std::max(small, Sw > 1 ? (size_t)Sw * ms * W.N * 4 : (size_t)0);
+    }
     if (M > 0 && W.wtype == T_Q4_K) {
         if (!dl_shape(W, M, W.K)) return 0;
         const int Sd = dl_split(W, M);
-        return q4k_sums_bytes(W, M) + (Sd > 1 ? (size_t)Sd * M * W.N * 4 : (size_t)0);
+        return q4k_sums_bytes(W, M) + std::max(small, Sd > 1 ? (size_t)Sd * M * W.N * 4 : (size_t)0);
     }
     if (M <= 0 || !mfma_shape(W, 8)) return 0;
     const int S = split_for(W, M);
@@ -897,8 +999,8 @@ size_t gemm_workspace_bytes(const QMat &W, int M) {
         const int Sd = dl_split(W, M);
         tile = std::max(tile, Sd > 1 ? (size_t)Sd * M * W.N * 4 : (size_t)0);
     }
+    tile = std::max(tile, small);
     // the skinny form, for any ubatch of at most min(M, 32) tokens
-    const int ms = M < 32 ? M : 32;
     return W.N <= 4096 ? std::max(tile, (size_t)skinny_splits(W) * ms * W.N * 4) : tile;
 }
 
@@ -911,20 +1013,31 @@ bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
         const size_t xsb = q4k_sums_bytes(W, M);
         if (ldx % 8 == 0 && dl_shape(W, M, ldx) && ws && ws_bytes >= xsb) {
             float *part = ws + xsb / 4;
-            int S = dl_split(W, M);
+            const bool small = dls_shape(W, M, ldx);
+            int S = small ? dls_split(W, M) : dl_split(W, M);
             while (S > 1 && (size_t)S * M * W.N * 4 > ws_bytes - xsb) S >>= 1;
             launch_block_sums(Xh, Xl, ldx, M, W.K, ws, s);
-            launch_gemm_dl(23, W, Xh, Xl, ldx, ep, M, pair_mode, S, part, ws, s);
+            if (small)
+                launch_gemm_dls(g_gemm_dls_ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, part, ws, s);
+            else
+                launch_gemm_dl(23, W, Xh, Xl, ldx, ep, M, pair_mode, S, part, ws, s);
             return true;
         }
-        const dim3 g((W.N / 2 + 255) / 256, M);
-        switch (ep.epi) {
-        case EPI_STORE: launch(k_gemm_q4k<EPI_STORE>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
-        case EPI_RESID: launch(k_gemm_q4k<EPI_RESID>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
-        case EPI_QKV: launch(k_gemm_q4k<EPI_QKV>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
-        case EPI_SWIGLU: launch(k_gemm_q4k<EPI_SWIGLU>, g, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode); break;
-        default: return false;
+        return launch_plainq<T_Q4_K>(W, Xh, Xl, ldx, ep, M, pair_mode, s);
+    }
+    // weight-streaming form (Q4_0), else the 32-token direct-to-LDS form, for
+    // at most 32 tokens
+    if (ws_shape(W, M, ldx)) {
+        const int S = ws_split(W, M);
+        if (S == 1 || (ws && (size_t)S * M * W.N * 4 <= ws_bytes)) {
+            launch_gemm_ws(g_gemm_ws, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+            return true;
         }
+    }
+    if (mfma_shape(W, ldx) && dls_shape(W, M, ldx) && g_gemm_dls) {
+        int S = dls_split(W, M);
+        while (S > 1 && (!ws || (size_t)S * M * W.N * 4 > ws_bytes)) S >>= 1;
+        launch_gemm_dls(g_gemm_dls_ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, nullptr, s);
         return true;
     }
     // skinny form for at most 32 tokens and at most 4096 features: there the
@@ -964,6 +1077,8 @@ bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
             launch_mfma<T_Q8_0>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
         return true;
     }
+    if (W.wtype == T_Q4_0) return launch_plainq<T_Q4_0>(W, Xh, Xl, ldx, ep, M, pair_mode, s);
+    if (W.wtype == T_Q8_0) return launch_plainq<T_Q8_0>(W, Xh, Xl, ldx, ep, M, pair_mode, s);
     if (W.wtype != T_F32) return false;
     switch (ep.epi) {
     case EPI_STORE: launch_f32_epi<EPI_STORE>(W, Xh, Xl, ldx, ep, M, pair_mode, s); break;

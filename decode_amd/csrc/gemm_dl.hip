@@ -55,7 +55,8 @@
 namespace {
 
 constexpr int DBN = 256;    // features per block
-constexpr int DBM = 128;    // tokens per block
+constexpr int DBM = 128;    // tokens per block (prefill form)
+constexpr int DBM_S = 32;   // tokens per block (small-ubatch form)
 
 #define AS1 __attribute__((address_space(1)))
 #define AS3 __attribute__((address_space(3)))
@@ -65,11 +66,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Q4_K adds per stage the rows' super-block factors (d | dmin << 16, one
 // dword per row) and the tokens' block sums of x (one fp32 per token; the
 // sc | m word of a sub-block takes the scale's place).
-template <int WT>
+template <int WT, int TM>
 struct Geo {
     static constexpr bool K4 = WT == T_Q4_K;
     static constexpr int CB = WT == T_Q8_0 ? 32 : 16;    // code bytes per row and K block
-    static constexpr int ACT = DBM * 64;                 // one activation part per K block
+    static constexpr int ACT = TM * 64;                  // one activation part per K block
     static constexpr int OFF_LO = ACT;
     static constexpr int OFF_CODES = 2 * ACT;
     static constexpr int OFF_SC = 2 * ACT + DBN * CB;
@@ -77,9 +78,9 @@ struct Geo {
     static constexpr int OFF_XS = OFF_DM + (K4 ? DBN * 4 : 0);
     // (x sums: waves 0, 1 load the 128 tokens, waves 2, 3 the same into a spare 512 bytes)
     static constexpr int STAGE = OFF_XS + (K4 ? 1024 : 0);
-    // direct loads per wavefront and K block: 4 activation, 1 or 2 code, 1 scale
-    // (Q4_K: + 1 factor, 1 x sum)
-    static constexpr int LOADS = 4 + DBN * CB / 4096 + 1 + (K4 ? 2 : 0);
+    // direct loads per wavefront and K block: 4 activation (128 tokens) or 1
+    // (32 tokens), 1 or 2 code, 1 scale (Q4_K: + 1 factor, 1 x sum)
+    static constexpr int LOADS = TM / 32 + DBN * CB / 4096 + 1 + (K4 ? 2 : 0);
 };
 
 // Slot of chunk c of token row m (see the header): the 16-byte reads of a
@@ -170,22 +171,31 @@ DEV void dma2(const void *src, const void AS3 *lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(src), "s"(m) : "memory");
 }
 
-template <int WT, int EPI, bool SPLIT, int NS, int MF, int WL>
-__global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const uint16_t *Xh, const uint16_t *Xl,
-                                                                  int ldx, EpiArgs ep, int M, int pair_mode, int NT,
-                                                                  int nsplit, float *part, const float *xs) {
-    using G = Geo<WT>;
+// TM = 128 tokens per block tile (prefill) or 32 (ubatches of at most 32
+// tokens, batched decode: one activation load per wavefront and K block,
+// each wavefront 64 features x 32 tokens, more stages in flight).
+template <int WT, int EPI, bool SPLIT, int NS, int MF, int WL, int TM>
+__global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(QMat W, const uint16_t *Xh,
+                                                                                const uint16_t *Xl, int ldx, EpiArgs ep,
+                                                                                int M, int pair_mode, int NT,
+                                                                                int nsplit, float *part,
+                                                                                const float *xs) {
+    using G = Geo<WT, TM>;
     constexpr bool Q4L = WT != T_Q8_0;    // 16 code bytes per row and K block
     __shared__ __attribute__((aligned(16))) uint8_t S0[G::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t S1[G::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t S2[NS > 2 ? G::STAGE : 16];
     __shared__ __attribute__((aligned(16))) uint8_t S3[NS > 3 ? G::STAGE : 16];
     __shared__ __attribute__((aligned(16))) uint8_t S4[NS > 4 ? G::STAGE : 16];
-    static_assert(NS >= 3 && NS <= 5, "stages");
+    __shared__ __attribute__((aligned(16))) uint8_t S5[NS > 5 ? G::STAGE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t S6[NS > 6 ? G::STAGE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t S7[NS > 7 ? G::STAGE : 16];
+    static_assert(NS >= 3 && NS <= 8, "stages");
+    static_assert(TM == 128 || (TM == 32 && MF == 32 && WL == 1), "token tile");
 
     // block -> (feature tile, token tile, K split); the tiles of one feature
     // tile share an XCD
-    const int mtiles = (M + DBM - 1) / DBM;
+    const int mtiles = (M + TM - 1) / TM;
     const int per_nt = mtiles * nsplit;
     const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
     const int nt = (j / per_nt) * 8 + xcd, rem = j % per_nt;
@@ -195,21 +205,26 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
     // the wavefront index as a wave-uniform value: the LDS addresses of the
     // direct loads then live in scalar registers
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n0 = nt * DBN, m0 = mtile * DBM;
-    const int nb_all = W.K >> 5, nb = nb_all / nsplit, kb0 = split * nb;
+    const int n0 = nt * DBN, m0 = mtile * TM;
+    // K split `split` of nsplit: K blocks [nb_all * split / nsplit, nb_all * (split + 1) / nsplit)
+    const int nb_all = W.K >> 5, kb0 = (int)((long)nb_all * split / nsplit);
+    const int nb = (int)((long)nb_all * (split + 1) / nsplit) - kb0;
     // WL 0: wavefront w covers features 128 (w & 1) .. +127 and tokens
-    // 64 (w >> 1) .. +63; WL 1: features 64 w .. +63 and all 128 tokens (each
+    // 64 (w >> 1) .. +63; WL 1: features 64 w .. +63 and all TM tokens (each
     // code converted by one wavefront only)
-    constexpr int DWN = WL ? 64 : 128, DWM = WL ? 128 : 64;
+    constexpr int DWN = WL ? 64 : 128, DWM = WL ? TM : 64;
     const int wn = WL ? 64 * w : (w & 1) * DWN, wm = WL ? 0 : (w >> 1) * DWM;
 
     // ---- per-lane byte offsets of the direct loads (from a base that moves
     // with the K block; every offset below 2^31, checked by the launcher) ----
-    // activations: instructions j = w, w + 4 of each part cover slots 64j .. 64j+63
+    // activations: TM 128: instructions j = w, w + 4 of each part cover
+    // slots 64j .. 64j+63; TM 32: wavefront w loads slots 64 (w & 1) .. +63 of
+    // part w >> 1 (value, remainder)
     uint32_t xo[2];
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-        const int slot = 64 * (w + 4 * i) + lane, m = slot >> 2, c = (slot & 3) ^ swz(slot >> 2);
+        const int slot = TM == 128 ? 64 * (w + 4 * i) + lane : 64 * (w & 1) + lane;
+        const int m = slot >> 2, c = (slot & 3) ^ swz(slot >> 2);
         const int row = min(m0 + m, M - 1);            // rows past M repeat row M-1; their outputs are dropped
         xo[i] = (uint32_t)(((size_t)row * ldx + c * 8) * 2);
     }
@@ -234,7 +249,8 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
     // Q4_K: factors of rows 64w + lane (super-block (kb0 + k) / 8) and x sums
     // of tokens m0 + 64 (w & 1) + lane (rows past M repeat row M-1)
     const uint32_t dmo = G::K4 ? (uint32_t)((size_t)(64 * w + lane) * (nb_all >> 3) * 4) : 0u;
-    const uint32_t xso = G::K4 ? (uint32_t)((size_t)min(m0 + 64 * (w & 1) + lane, M - 1) * nb_all * 4) : 0u;
+    const uint32_t xso =
+        G::K4 ? (uint32_t)((size_t)min(m0 + (TM == 128 ? 64 * (w & 1) + lane : lane & 31), M - 1) * nb_all * 4) : 0u;
     const uint8_t *dm_base = G::K4 ? (const uint8_t *)W.dm + (size_t)n0 * (nb_all >> 3) * 4 : nullptr;
     const uint8_t *xs_base = G::K4 ? (const uint8_t *)xs + (size_t)kb0 * 4 : nullptr;
 
@@ -244,17 +260,25 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
         else if constexpr (s == 1) return S1;
         else if constexpr (s == 2) return S2;
         else if constexpr (s == 3) return S3;
-        else return S4;
+        else if constexpr (s == 4) return S4;
+        else if constexpr (s == 5) return S5;
+        else if constexpr (s == 6) return S6;
+        else return S7;
     };
 
     // requests K block kb (clamped to the range) into stage s
     auto issue = [&](auto sc, int kb) __attribute__((always_inline)) {
         uint8_t *st = stage_ptr(sc);
         const size_t k = (size_t)min(kb, nb - 1);
+        if constexpr (TM == 128) {
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            dma16s(xh_base + k * 64, xo[i], (const void AS3 *)(st + 1024 * (w + 4 * i)));
-            dma16s(xl_base + k * 64, xo[i], (const void AS3 *)(st + G::OFF_LO + 1024 * (w + 4 * i)));
+            for (int i = 0; i < 2; i++) {
+                dma16s(xh_base + k * 64, xo[i], (const void AS3 *)(st + 1024 * (w + 4 * i)));
+                dma16s(xl_base + k * 64, xo[i], (const void AS3 *)(st + G::OFF_LO + 1024 * (w + 4 * i)));
+            }
+        } else {
+            dma16s((w >> 1 ? xl_base : xh_base) + k * 64, xo[0],
+                   (const void AS3 *)(st + (w >> 1 ? G::OFF_LO : 0) + 1024 * (w & 1)));
         }
         if (Q4L) {
             dma16s(c_base + k * 16, co[0], (const void AS3 *)(st + G::OFF_CODES + 1024 * w));
@@ -418,6 +442,9 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
     issue(std::integral_constant<int, 1>{}, 1);
     if constexpr (NS > 3) issue(std::integral_constant<int, 2>{}, 2);
     if constexpr (NS > 4) issue(std::integral_constant<int, 3>{}, 3);
+    if constexpr (NS > 5) issue(std::integral_constant<int, 4>{}, 4);
+    if constexpr (NS > 6) issue(std::integral_constant<int, 5>{}, 5);
+    if constexpr (NS > 7) issue(std::integral_constant<int, 6>{}, 6);
     // whole periods of NS steps; K blocks past the last are clamped re-reads
     // whose stages are never computed
     for (int kb = 0; kb < nb; kb += NS) {
@@ -428,6 +455,12 @@ __global__ __launch_bounds__(256, NS <= 3 ? 2 : 1) void k_gemm_dl(QMat W, const 
             if (kb + 3 < nb) step(std::integral_constant<int, 3>{}, kb + 3);
         if constexpr (NS > 4)
             if (kb + 4 < nb) step(std::integral_constant<int, 4>{}, kb + 4);
+        if constexpr (NS > 5)
+            if (kb + 5 < nb) step(std::integral_constant<int, 5>{}, kb + 5);
+        if constexpr (NS > 6)
+            if (kb + 6 < nb) step(std::integral_constant<int, 6>{}, kb + 6);
+        if constexpr (NS > 7)
+            if (kb + 7 < nb) step(std::integral_constant<int, 7>{}, kb + 7);
     }
     // drain the requests past the last K block before the block can exit
     wait_vm_lgkm0<0>();
@@ -513,7 +546,7 @@ void launch_dl_ns(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl,
     const int NT = W.N / DBN, NT8 = (NT + 7) / 8 * 8;
     const dim3 grid(NT8 * ((M + DBM - 1) / DBM) * S);
     if constexpr (WT == T_Q4_K) {   // one form: 3 stages, 32x32 tiles, 64-feature wavefront tiles
-        launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 1>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S,
+        launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 1, 128>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S,
                part, xs);
         return;
     } else {
@@ -521,11 +554,51 @@ void launch_dl_ns(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl,
     // tokens); 13: 3 stages on 16x16 tiles; 23: 3 stages, 32x32 tiles,
     // wavefront tile 64 features x 128 tokens
     switch (ns) {
-    case 4: launch((k_gemm_dl<WT, EPI, SPLIT, 4, 32, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
-    case 13: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 16, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
-    case 23: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 1>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
-    default: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 0>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
+    case 4: launch((k_gemm_dl<WT, EPI, SPLIT, 4, 32, 0, 128>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
+    case 13: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 16, 0, 128>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
+    case 23: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 1, 128>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
+    default: launch((k_gemm_dl<WT, EPI, SPLIT, 3, 32, 0, 128>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
     }
+    }
+}
+
+// The 32-token form: NS stages (4, 6 or 8).
+template <int WT, int EPI, bool SPLIT>
+void launch_dls_ns(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                   int pair_mode, int S, float *part, const float *xs, hipStream_t s) {
+    const int NT = W.N / DBN, NT8 = (NT + 7) / 8 * 8;
+    const dim3 grid(NT8 * ((M + DBM_S - 1) / DBM_S) * S);
+    switch (ns) {
+    case 8:   // (8 stages fit two blocks per compute unit for Q4_0 only)
+        if constexpr (WT == T_Q4_0) {
+            launch((k_gemm_dl<WT, EPI, SPLIT, 8, 32, 1, 32>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs);
+            break;
+        }
+        [[fallthrough]];
+    case 6: launch((k_gemm_dl<WT, EPI, SPLIT, 6, 32, 1, 32>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
+    default: launch((k_gemm_dl<WT, EPI, SPLIT, 4, 32, 1, 32>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, part, xs); break;
+    }
+}
+
+template <int WT, int EPI>
+void launch_dls_epi(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                    int pair_mode, int S, float *ws, const float *xs, hipStream_t s) {
+    if (S > 1) {
+        launch_dls_ns<WT, EPI, true>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s);
+        launch_splitk_sum(EPI, ws, S, W.N, M, ep, pair_mode, s);
+    } else {
+        launch_dls_ns<WT, EPI, false>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, 1, nullptr, xs, s);
+    }
+}
+
+template <int WT>
+void launch_dls_wt(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                   int pair_mode, int S, float *ws, const float *xs, hipStream_t s) {
+    switch (ep.epi) {
+    case EPI_STORE: launch_dls_epi<WT, EPI_STORE>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
+    case EPI_RESID: launch_dls_epi<WT, EPI_RESID>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
+    case EPI_QKV: launch_dls_epi<WT, EPI_QKV>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
+    case EPI_SWIGLU: launch_dls_epi<WT, EPI_SWIGLU>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
     }
 }
 
@@ -551,10 +624,303 @@ void launch_dl_wt(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl,
     }
 }
 
+
+// ---- weight-streaming form: Q4_0, at most 32 tokens (batched decode) --------
+//
+// With 32 tokens a weight byte feeds only 64 products, so the kernel has to
+// stream codes at the HBM rate.  Where the forms above request one K block per
+// stage (each load instruction then touches 64 rows, 16 bytes of each, and
+// each scale is a 2-byte request), here a stage is KS = 2 or 4 consecutive
+// K blocks: a load instruction covers 1024 / (16 KS) rows x 16 KS contiguous
+// bytes of codes, or 1024 / (64 KS) tokens x 64 KS contiguous bytes of
+// activations, and the scales of the block's whole K range (at most WS_RMAX
+// blocks) are loaded once at entry.
+// Everything else is the direct-to-LDS scheme: a ring of WS_NS stages, a
+// constant vmcnt per wavefront, one barrier per stage.  Block tile: 256
+// features x 32 tokens, wavefront w owning features 64 w .. +63 (two 32x32
+// tiles, the same MFMA operands and per-block scaling as k_gemm_dl).
+// LDS stage (16 or 32 KB): activation values [32 tokens][4 KS chunks of 16 B]
+// (chunk q = 4 j + c: K block j of the stage, 16-byte piece c), remainders
+// likewise, codes [256 rows][KS K blocks of 16 B], each stored at an XOR slot
+// (ws_xslot, ws_cslot) that spreads a quarter wavefront's 16-byte reads over
+// distinct bank groups.  With KS = 2 a block takes 80 KB of LDS, so two fit a
+// compute unit.  K splits are whole octets of K blocks.
+constexpr int WS_NS = 4;                      // stages
+constexpr int WS_RMAX = 32;                   // K blocks per split at most
+
+// Stage geometry for KS K blocks per stage (KS = 2 or 4).
+template <int KS>
+struct WsGeo {
+    static constexpr int XPART = 32 * KS * 64;            // one activation part
+    static constexpr int STAGE = 2 * XPART + DBN * KS * 16;
+    static constexpr int XI = XPART / 1024;               // activation instructions per part
+    static constexpr int CI = DBN * KS * 16 / 1024;       // code instructions
+    static constexpr int LOADS = (2 * XI + CI) / 4;       // per wavefront and stage
+    static constexpr int TOKB = KS * 64;                  // bytes of one token's row in a part
+};
+// chunk slot of activation chunk q (of KS*4) of token m; K-block slot of code
+// chunk j of row f: XOR patterns that put 16 consecutive lanes' 16-byte reads
+// in distinct bank groups (KS = 4: 256-byte token rows, 64-byte code rows;
+// KS = 2: 128-byte token rows, 32-byte code rows)
+template <int KS>
+DEV int ws_xslot(int q, int m) { return KS == 4 ? q ^ (m & 15) : q ^ ((m >> 1) & 7); }
+template <int KS>
+DEV int ws_cslot(int j, int f) { return KS == 4 ? j ^ ((f >> 2) & 3) : j ^ ((f >> 3) & 1); }
+
+template <int EPI, bool SPLIT, int KS>
+__global__ __launch_bounds__(256, KS == 2 ? 2 : 1) void k_gemm_ws(QMat W, const uint16_t *Xh, const uint16_t *Xl,
+                                                                   int ldx, EpiArgs ep, int M, int pair_mode, int NT,
+                                                                   int nsplit, float *part) {
+    using G = WsGeo<KS>;
+    __shared__ __attribute__((aligned(16))) uint8_t S0[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t S1[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t S2[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t S3[G::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t SC[DBN * WS_RMAX * 2];
+    static_assert(WS_NS == 4, "four stage buffers");
+    static_assert(G::LOADS * 4 == 2 * G::XI + G::CI && G::XI % 2 == 0 && G::CI % 4 == 0, "loads per wavefront");
+    const int mtiles = (M + 31) / 32;
+    const int per_nt = mtiles * nsplit;
+    const int L = blockIdx.x, xcd = L & 7, jj = L >> 3;
+    const int nt = (jj / per_nt) * 8 + xcd, rem = jj % per_nt;
+    const int mtile = rem % mtiles, split = rem / mtiles;
+    if (nt >= NT) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = nt * DBN, m0 = mtile * 32;
+    const int nb_all = W.K >> 5, no = W.K >> 8;            // K blocks, octets of K blocks
+    const int kb0 = 8 * (int)((long)no * split / nsplit);
+    const int nb = 8 * (int)((long)no * (split + 1) / nsplit) - kb0;   // multiple of 8, <= WS_RMAX
+    const int nst = nb / KS;
+    const size_t row_bytes = (size_t)(W.K >> 1);
+
+    // activations: wavefront w fills part w >> 1, instruction i the 1 KB at
+    // 1024 ib, ib = (XW w + i) mod XI (XW = XI / 2 instructions per wavefront):
+    // token ib * (1024 / TOKB) + lane / (TOKB / 16), stored slot lane % (TOKB / 16)
+    constexpr int XW = G::XI / 2, SPT = G::TOKB / 16;
+    uint32_t xo[XW];
+#pragma unroll
+    for (int i = 0; i < XW; i++) {
+        const int ib = (XW * w + i) % G::XI, m = ib * (1024 / G::TOKB) + lane / SPT;
+        const int q = ws_xslot<KS>(lane % SPT, m);     // (the XOR pattern is its own inverse)
+        const int row = min(m0 + m, M - 1);            // rows past M repeat row M-1; their outputs are dropped
+        xo[i] = (uint32_t)(((size_t)row * ldx + (q >> 2) * 32 + (q & 3) * 8) * 2);
+    }
+    const uint8_t *xbase = (const uint8_t *)(w >> 1 ? Xl : Xh) + (size_t)kb0 * 64;
+    // codes: instruction i of wavefront w fills the 1 KB at 1024 (CW w + i)
+    // (CW = CI / 4): rows of KS 16-byte chunks, KS lanes per row
+    constexpr int CW = G::CI / 4;
+    uint32_t co[CW];
+#pragma unroll
+    for (int i = 0; i < CW; i++) {
+        const int f = (1024 / (16 * KS)) * (CW * w + i) + lane / KS, j = ws_cslot<KS>(lane % KS, f);
+        co[i] = (uint32_t)((size_t)f * row_bytes + j * 16);
+    }
+    const uint8_t *cbase = (const uint8_t *)W.qs + (size_t)n0 * row_bytes + (size_t)kb0 * 16;
+
+    // the f16 scales of the block's K range: row f at SC + 2 nb f, 16 bytes
+    // (8 K blocks) per lane and instruction
+    {
+        const int nchunk = nb >> 3;                    // 16-byte pieces per row
+        for (int n = w; n < nb >> 1; n += 4) {         // nb / 2 instructions of 64 pieces
+            const int g = 64 * n + lane, f = g / nchunk, c = g % nchunk;
+            dma16(W.d + (size_t)(n0 + f) * nb_all + kb0 + 8 * c, (const void AS3 *)(SC + 1024 * n));
+        }
+    }
+
+    auto stage_ptr = [&](auto sc) -> uint8_t * {
+        constexpr int s = decltype(sc)::value;
+        if constexpr (s == 0) return S0;
+        else if constexpr (s == 1) return S1;
+        else if constexpr (s == 2) return S2;
+        else return S3;
+    };
+    auto issue = [&](auto sc, int sg) __attribute__((always_inline)) {
+        uint8_t *st = stage_ptr(sc);
+        const size_t k = (size_t)min(sg, nst - 1) * KS;
+#pragma unroll
+        for (int i = 0; i < XW; i++)
+            dma16s(xbase + k * 64, xo[i], (const void AS3 *)(st + (w >> 1) * G::XPART + 1024 * ((XW * w + i) % G::XI)));
+#pragma unroll
+        for (int i = 0; i < CW; i++)
+            dma16s(cbase + k * 16, co[i], (const void AS3 *)(st + 2 * G::XPART + 1024 * (CW * w + i)));
+    };
+
+    f16x acc[2];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[a][r] = 0.f;
+
+    auto compute = [&](auto sc, int sg) __attribute__((always_inline)) {
+        const uint8_t *st = stage_ptr(sc);
+        const int m = lane & 31;
+        const bool hi8 = lane >> 5;
+        float d[2][KS];
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+            const int f = 64 * w + 32 * a + m;
+            const uint8_t *sp = SC + 2 * ((size_t)f * nb + KS * sg);
+            if constexpr (KS == 4) {
+                const u32x2 sv = *(const u32x2 *)sp;
+                d[a][0] = f16_bits_to_f32((uint16_t)sv.x);
+                d[a][1] = f16_bits_to_f32((uint16_t)(sv.x >> 16));
+                d[a][2] = f16_bits_to_f32((uint16_t)sv.y);
+                d[a][3] = f16_bits_to_f32((uint16_t)(sv.y >> 16));
+            } else {
+                const uint32_t sv = *(const uint32_t *)sp;
+                d[a][0] = f16_bits_to_f32((uint16_t)sv);
+                d[a][1] = f16_bits_to_f32((uint16_t)(sv >> 16));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KS; j++) {
+            h8 xh[2], xl[2];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int q = 4 * j + 2 * h + (lane >> 5);
+                const int pos = G::TOKB * m + 16 * ws_xslot<KS>(q, m);
+                xh[h] = *(const h8 *)(st + pos);
+                xl[h] = *(const h8 *)(st + G::XPART + pos);
+            }
+#pragma unroll
+            for (int a = 0; a < 2; a++) {
+                const int f = 64 * w + 32 * a + m;
+                const u32x4 v = *(const u32x4 *)(st + 2 * G::XPART + 16 * KS * f + 16 * ws_cslot<KS>(j, f));
+                h8 c0, c1;
+                q4_pair(hi8 ? u32x2{v.z, v.w} : u32x2{v.x, v.y}, c0, c1);
+                f16x t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[0], c0, f16x{}, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[0], c0, t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[1], c1, t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[1], c1, t, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; r++) acc[a][r] += d[a][j] * t[r];
+            }
+        }
+    };
+
+    auto step = [&](auto sc, int sg) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        wait_vm_lgkm0<(WS_NS - 2) * G::LOADS>();
+        block_barrier();
+        issue(std::integral_constant<int, (s + WS_NS - 1) % WS_NS>{}, sg + WS_NS - 1);
+        compute(sc, sg);
+    };
+
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, 1);
+    issue(std::integral_constant<int, 2>{}, 2);
+    for (int sg = 0; sg < nst; sg += WS_NS) {
+        step(std::integral_constant<int, 0>{}, sg);
+        if (sg + 1 < nst) step(std::integral_constant<int, 1>{}, sg + 1);
+        if (sg + 2 < nst) step(std::integral_constant<int, 2>{}, sg + 2);
+        if (sg + 3 < nst) step(std::integral_constant<int, 3>{}, sg + 3);
+    }
+    wait_vm_lgkm0<0>();
+
+    // ---- epilogue: lane holds feature n0 + 64w + 32a + (lane & 31) and, in
+    // accumulator r, token m0 + (r/4)*8 + (lane/32)*4 + r%4 ----
+    const int fl = lane & 31;
+    auto tok_of = [&](int r) __attribute__((always_inline)) { return m0 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); };
+    if (SPLIT) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int m = tok_of(r);
+            if (m >= M) continue;
+            float *dst = part + ((size_t)split * M + m) * W.N + n0 + 64 * w + fl;
+            dst[0] = acc[0][r];
+            dst[32] = acc[1][r];
+        }
+        return;
+    }
+    if (EPI == EPI_STORE || EPI == EPI_RESID) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int m = tok_of(r);
+            if (m >= M) continue;
+            float *y = ep.y + (size_t)m * ep.ldy + n0 + 64 * w + fl;
+#pragma unroll
+            for (int a = 0; a < 2; a++) {
+                if (EPI == EPI_STORE) y[32 * a] = acc[a][r];
+                else y[32 * a] += acc[a][r];
+            }
+        }
+    } else if (pair_mode == PAIR_GU) {
+        // gate rows 64g .. +31 (tile 0) and their up rows 64g + 32 .. (tile 1)
+        const int rr = n0 + 64 * w + fl, g = rr >> 6;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int m = tok_of(r);
+            if (m < M) epi_pair<EPI>(ep, m, (g << 5) + (rr & 31), rr, rr + 32, acc[0][r], acc[1][r]);
+        }
+    } else {
+        // adjacent features f (even lane) and f+1 (odd lane), exchanged by lane pairs
+        const bool odd = lane & 1;
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+#pragma unroll
+            for (int r = 0; r < 8; r++) {
+                const float send = odd ? acc[a][r] : acc[a][r + 8];
+                const float recv = __shfl_xor(send, 1, 64);
+                const int rr = odd ? r + 8 : r;
+                const int m = tok_of(rr);
+                const int f = n0 + 64 * w + 32 * a + (fl & ~1);
+                const float va = odd ? recv : acc[a][r];
+                const float vb = odd ? acc[a][r + 8] : recv;
+                if (m < M) epi_pair<EPI>(ep, m, f >> 1, f, f + 1, va, vb);
+            }
+    }
+}
+
+template <int EPI, int KS>
+void launch_ws_ks(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                  int pair_mode, int S, float *ws, hipStream_t s) {
+    const int NT = W.N / DBN, NT8 = (NT + 7) / 8 * 8;
+    const dim3 grid(NT8 * ((M + 31) / 32) * S);
+    if (S > 1) {
+        launch((k_gemm_ws<EPI, true, KS>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, ws);
+        launch_splitk_sum(EPI, ws, S, W.N, M, ep, pair_mode, s);
+    } else {
+        launch((k_gemm_ws<EPI, false, KS>), grid, dim3(256), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, 1,
+               (float *)nullptr);
+    }
+}
+
+template <int EPI>
+void launch_ws_epi(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                   int pair_mode, int S, float *ws, hipStream_t s) {
+    if (ks == 4)
+        launch_ws_ks<EPI, 4>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+    else
+        launch_ws_ks<EPI, 2>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+}
+
 }  // namespace
 
 int gemm_dl_tile_features() { return DBN; }
 int gemm_dl_tile_tokens() { return DBM; }
+int gemm_dls_tile_tokens() { return DBM_S; }
+int gemm_ws_max_blocks_per_split() { return WS_RMAX; }
+
+void launch_gemm_ws(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                    int pair_mode, int S, float *ws, hipStream_t s) {
+    switch (ep.epi) {
+    case EPI_STORE: launch_ws_epi<EPI_STORE>(ks, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_RESID: launch_ws_epi<EPI_RESID>(ks, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_QKV: launch_ws_epi<EPI_QKV>(ks, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_SWIGLU: launch_ws_epi<EPI_SWIGLU>(ks, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    }
+}
+
+void launch_gemm_dls(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
+                     int M, int pair_mode, int S, float *ws, const float *xs, hipStream_t s) {
+    if (W.wtype == T_Q4_0)
+        launch_dls_wt<T_Q4_0>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, nullptr, s);
+    else if (W.wtype == T_Q4_K)
+        launch_dls_wt<T_Q4_K>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s);
+    else
+        launch_dls_wt<T_Q8_0>(ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, nullptr, s);
+}
 
 void launch_gemm_dl(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
                     int M, int pair_mode, int S, float *ws, const float *xs, hipStream_t s) {

@@ -141,7 +141,7 @@ bool launch_matvec(const QMat &W, const InArgs &in, const EpiArgs &ep, int T, hi
 // Y = X W^T for T tokens (prefill / batched decode), X = Xh + Xl given as two
 // f16 arrays [T][ldx] (value and rounding remainder): MFMA for Q8_0 / Q4_0
 // with N % 128 == 0 and Q4_K with N % 256 == 0, a plain fp32 kernel
-// otherwise.  `ws` (ws_bytes) holds the fp32 partial tiles of a K split (and
+// otherwise (on the codes for quantized weights).  `ws` (ws_bytes) holds the fp32 partial tiles of a K split (and
 // for Q4_K first the tokens' block sums); with too little workspace (or none)
 // the GEMM splits K less (or not at all; Q4_K then takes the plain kernel).
 bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
@@ -159,6 +159,17 @@ void launch_gemm_dl(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *X
 void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, int K, float *xs, hipStream_t s);
 int gemm_dl_tile_features();
 int gemm_dl_tile_tokens();
+// The same form with 32-token block tiles for ubatches of at most 32 tokens
+// (batched decode): `ns` stages (4, 6 or 8), K split S (uneven splits allowed).
+void launch_gemm_dls(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
+                     int M, int pair_mode, int S, float *ws, const float *xs, hipStream_t s);
+int gemm_dls_tile_tokens();
+// Weight-streaming form for Q4_0 at most 32 tokens (K % 256 == 0, N % 256 ==
+// 0): K split S in whole octets of K blocks, at most
+// gemm_ws_max_blocks_per_split() K blocks per split.
+void launch_gemm_ws(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                    int pair_mode, int S, float *ws, hipStream_t s);
+int gemm_ws_max_blocks_per_split();
 // Sums S fp32 partial tiles [S][M][N] in split order and applies epilogue epi.
 void launch_splitk_sum(int epi, const float *ws, int S, int N, int M, const EpiArgs &ep, int pair_mode,
                        hipStream_t s);

@@ -90,11 +90,12 @@ def test_small_ubatch_exact_in_both_modes(dec, monkeypatch):
 
 @pytest.mark.parametrize("wtype", [synth.Q4_0, synth.Q8_0])
 def test_skinny_form_matches_tiles_and_oracle(dec, orc, wtype, monkeypatch):
-    """Ubatches of at most 32 tokens take the skinny form (wavefronts stream
-    their own weight rows, K ranges over blocks); DECODE_GEMM_SKINNY=0 sends
-    them through the tiled kernel instead.  Same exact operands, different
-    summation order: rows within 1e-3 of each other and within the oracle bar,
-    on a 45-token prompt in ubatches of 32 (a full and a ragged 13-token one)."""
+    """With DECODE_GEMM_SMALL=tiles, ubatches of at most 32 tokens take the
+    skinny form (wavefronts stream their own weight rows, K ranges over
+    blocks); DECODE_GEMM_SKINNY=0 sends them through the tiled kernel instead.
+    Same exact operands, different summation order: rows within 1e-3 of each
+    other and within the oracle bar, on a 45-token prompt in ubatches of 32 (a
+    full and a ragged 13-token one)."""
     hp = small_hp(wtype, synth.F16, n_embd=512, n_head=8, n_ff=1024)
     w = synth.weights_numpy(hp, 920 + wtype, threads=4)
     prompt = synth.prompt(hp["n_vocab"], 45, 921)
@@ -102,6 +103,7 @@ def test_skinny_form_matches_tiles_and_oracle(dec, orc, wtype, monkeypatch):
     o_rows = [oc.eval(0, int(t)) for t in prompt]
     gm = dec.Model(hp, w)
     got = {}
+    monkeypatch.setenv("DECODE_GEMM_SMALL", "tiles")
     for skinny in (True, False):
         monkeypatch.setenv("DECODE_GEMM_SKINNY", "1" if skinny else "0")
         ctx = dec.Context(gm, n_ctx=256, n_batch=45, n_ubatch=32)
@@ -109,6 +111,7 @@ def test_skinny_form_matches_tiles_and_oracle(dec, orc, wtype, monkeypatch):
         got[skinny] = [np.array(ctx.logits(i)) for i in range(45)]
         ctx.close()
     monkeypatch.delenv("DECODE_GEMM_SKINNY")
+    monkeypatch.delenv("DECODE_GEMM_SMALL")
     for i in (0, 1, 31, 32, 44):
         assert_logits_close(got[True][i], o_rows[i], f"skinny row {i}")
         ma, _ = logit_err(got[True][i], got[False][i])
@@ -148,3 +151,90 @@ def test_direct_load_form_bitwise_equals_staged_tiles(dec, orc, wtype, monkeypat
             assert np.array_equal(got[ns][i], got["0"][i]), f"variant {ns}, row {i}"
         for ns in ("13",):
             assert logit_err(got[ns][i], got["0"][i])[0] <= 1e-4, f"16x16 tiles ({ns}), row {i}"
+
+
+@pytest.mark.parametrize("wtype", [synth.Q4_0, synth.Q8_0])
+def test_small_direct_load_form_matches_tiles_and_oracle(dec, orc, wtype, monkeypatch):
+    """Ubatches of at most 32 tokens on matrices of whole 256-feature tiles
+    take the direct-to-LDS form with 32-token block tiles (4, 6 or 8 stages,
+    DECODE_GEMM_DLS_NS; K split into possibly uneven ranges: the down matrix
+    here has 41 K blocks).  Against the skinny / tiled kernels
+    (DECODE_GEMM_SMALL=tiles): the same exact operands in another summation
+    order, so rows agree to 1e-3; every form meets the oracle bar on a
+    45-token prompt in ubatches of 32 (a full and a ragged 13-token one)."""
+    hp = small_hp(wtype, synth.F16, n_embd=512, n_head=8, n_ff=1312, n_vocab=1024)
+    w = synth.weights_numpy(hp, 940 + wtype, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 45, 941)
+    oc = orc.Context(orc.Model(hp, w), 1, 256)
+    o_rows = [oc.eval(0, int(t)) for t in prompt]
+    gm = dec.Model(hp, w)
+    got = {}
+    monkeypatch.setenv("DECODE_GEMM_WS", "0")
+    for form in ("tiles", "4", "6", "8"):
+        if form == "tiles":
+            monkeypatch.setenv("DECODE_GEMM_SMALL", "tiles")
+        else:
+            monkeypatch.delenv("DECODE_GEMM_SMALL", raising=False)
+            monkeypatch.setenv("DECODE_GEMM_DLS_NS", form)
+        ctx = dec.Context(gm, n_ctx=256, n_batch=45, n_ubatch=32)
+        assert ctx.prefill(prompt, 0, output_all=True) == 0
+        got[form] = [np.array(ctx.logits(i)) for i in range(45)]
+        ctx.close()
+    monkeypatch.delenv("DECODE_GEMM_SMALL", raising=False)
+    monkeypatch.delenv("DECODE_GEMM_DLS_NS", raising=False)
+    monkeypatch.delenv("DECODE_GEMM_WS", raising=False)
+    for i in (0, 1, 12, 31, 32, 44):
+        for form in ("tiles", "4", "6", "8"):
+            assert_logits_close(got[form][i], o_rows[i], f"{form} row {i}")
+        for form in ("4", "6", "8"):
+            ma, _ = logit_err(got[form][i], got["tiles"][i])
+            assert ma <= 1e-3, f"row {i}: 32-token direct-load ({form} stages) vs tiles {ma:.3e}"
+        # the stage count changes only the pipelining, not the arithmetic
+        assert np.array_equal(got["4"][i], got["6"][i]) and np.array_equal(got["4"][i], got["8"][i])
+
+
+def test_weight_streaming_form_matches_oracle(dec, orc, monkeypatch):
+    """Q4_0 ubatches of at most 32 tokens on matrices of whole 256-feature
+    tiles with K a multiple of 256 take the weight-streaming form (2 K blocks
+    per stage by default, DECODE_GEMM_WS=4 for 4; the split's scales loaded
+    once; K split in whole octets of K blocks, unevenly where K = 768 is three
+    octets).  Against the 32-token direct-to-LDS form (DECODE_GEMM_WS=0): the
+    same operands and per-block scaling in another K split, so rows agree to
+    1e-3; every form meets the oracle bar on a 45-token prompt in ubatches of
+    32, and on five sequences decoded in one call."""
+    hp = small_hp(synth.Q4_0, synth.F16, n_embd=768, n_head=12, n_head_kv=4, n_ff=1024, n_vocab=1024)
+    w = synth.weights_numpy(hp, 950, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 45, 951)
+    om = orc.Model(hp, w)
+    oc = orc.Context(om, 1, 256)
+    o_rows = [oc.eval(0, int(t)) for t in prompt]
+    gm = dec.Model(hp, w)
+    got = {}
+    for form in ("0", "2", "4"):
+        monkeypatch.setenv("DECODE_GEMM_WS", form)
+        ctx = dec.Context(gm, n_ctx=256, n_batch=45, n_ubatch=32)
+        assert ctx.prefill(prompt, 0, output_all=True) == 0
+        got[form] = [np.array(ctx.logits(i)) for i in range(45)]
+        ctx.close()
+    for i in (0, 1, 12, 31, 32, 44):
+        for form in ("0", "2", "4"):
+            assert_logits_close(got[form][i], o_rows[i], f"form {form} row {i}")
+        for form in ("2", "4"):
+            ma, _ = logit_err(got[form][i], got["0"][i])
+            assert ma <= 1e-3, f"row {i}: streaming ({form} K blocks per stage) vs 32-token direct-load {ma:.3e}"
+    # five sequences, one decode call of five tokens (M = 5)
+    monkeypatch.setenv("DECODE_GEMM_WS", "2")
+    S = 5
+    prompts = [synth.prompt(hp["n_vocab"], 10 + 2 * s, 960 + s) for s in range(S)]
+    feeds = synth.prompt(hp["n_vocab"], S, 970)
+    ctx = dec.Context(gm, n_ctx=128, n_batch=32, n_ubatch=32, n_seq_max=S)
+    for s in range(S):
+        assert ctx.prefill(prompts[s], s) == 0
+    assert ctx.decode([int(t) for t in feeds], list(range(S))) == 0
+    for s in range(S):
+        oc = orc.Context(om, 1, 128)
+        for t in prompts[s]:
+            oc.eval(0, int(t))
+        assert_logits_close(ctx.logits(s), oc.eval(0, int(feeds[s])), f"sequence {s}")
+    ctx.close()
+    monkeypatch.delenv("DECODE_GEMM_WS")
