@@ -149,7 +149,9 @@ static bool alloc_qmat(Mem &mem, QMat &m, int wtype, int N, int K) {
     }
     if (wtype == DEC_Q4_K) {
         m.dm = (uint32_t *)mem.get((size_t)N * (K / 256) * 4);
-        if (!m.dm) return false;
+        m.mfq = (uint32_t *)mem.get((size_t)N * (K / 32) * 4);
+        m.sf = (float *)mem.get((size_t)N * (K / 32) * 4);
+        if (!m.dm || !m.mfq || !m.sf) return false;
     }
     return true;
 }
@@ -196,6 +198,15 @@ struct Loader {
         return true;
     }
 };
+
+// Q4_K: the GEMM's min-term operand of every matrix, once all rows are stored.
+static void finish_q4k(dec_model *m, hipStream_t s) {
+    if (m->hp.wtype != DEC_Q4_K) return;
+    launch_q4k_mins(m->tok, s);
+    launch_q4k_mins(m->out, s);
+    for (Layer &L : m->layers)
+        for (QMat *q : {&L.wqkv, &L.wo, &L.wgu, &L.wdown}) launch_q4k_mins(*q, s);
+}
 
 static bool valid_hparams(const dec_hparams &h) {
     if (h.n_layer <= 0 || h.n_embd <= 0 || h.n_head <= 0 || h.n_head_kv <= 0 || h.head_dim <= 0 ||
@@ -285,6 +296,7 @@ extern "C" dec_model *dec_model_load(const dec_hparams *hp, const dec_weights *w
              ld.put(w->ffn_down[l], d, F, L.wdown, 0, 0) && ld.vec(w->attn_norm[l], d, &L.attn_norm) &&
              ld.vec(w->ffn_norm[l], d, &L.ffn_norm);
     }
+    if (ok) finish_q4k(m, m->stream);
     if (ok) HIP_OK(hipStreamSynchronize(m->stream), ok = false);
     m->mem.drop(ld.stage);   // host weights are staged during the load only
     if (!ok) {
@@ -558,6 +570,7 @@ extern "C" dec_model *dec_model_load_gguf(const char *path, int32_t kvtype, cons
              put(layer_name(l, "ffn_down"), d, F, L.wdown, 0, 0) && vec(layer_name(l, "attn_norm"), &L.attn_norm) &&
              vec(layer_name(l, "ffn_norm"), &L.ffn_norm);
     }
+    if (ok) finish_q4k(m, s);
     if (ok) HIP_OK(hipStreamSynchronize(s), ok = false);
     m->mem.drop(stage);   // the file's tensors pass through it during the load only
     if (!ok) {

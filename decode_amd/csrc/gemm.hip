@@ -595,7 +595,25 @@ __global__ __launch_bounds__(256) void k_block_sums(const uint16_t *Xh, const ui
 #pragma unroll
         for (int e = 0; e < 8; e++) s += (float)hv[e] + (float)lv[e];
     }
-    xs[idx] = s;
+    const f16 sh = (f16)s, sl = (f16)(s - (float)sh);
+    // octet-major [K/256][M][8]: the 8 sums of one K-block octet of a token are contiguous
+    ((uint32_t *)xs)[((size_t)(kb >> 3) * M + m) * 8 + (kb & 7)] =
+        (uint32_t)__builtin_bit_cast(uint16_t, sh) | ((uint32_t)__builtin_bit_cast(uint16_t, sl) << 16);
+}
+
+// mfq = -f(dmin) m of sub-block kb of row n as f16 value | remainder << 16,
+// octet-major ([K/256][N][8]); sf[n][kb] = f(d) sc (exact in fp32: an 11-bit
+// significand times a six-bit integer).
+__global__ __launch_bounds__(256) void k_q4k_mins(QMat W) {
+    const int nb = W.K >> 5;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)W.N * nb) return;
+    const int r = (int)(idx / nb), b = (int)(idx % nb);
+    const uint32_t dd = W.dm[(size_t)r * (W.K >> 8) + (b >> 3)];
+    W.sf[idx] = f16_bits_to_f32((uint16_t)dd) * (float)(W.d[idx] & 63);
+    const float v = -f16_bits_to_f32((uint16_t)(dd >> 16)) * (float)((W.d[idx] >> 8) & 63);
+    const f16 vh = (f16)v, vl = (f16)(v - (float)vh);
+    W.mfq[((size_t)(b >> 3) * W.N + r) * 8 + (b & 7)] = (uint32_t)__builtin_bit_cast(uint16_t, vh) | ((uint32_t)__builtin_bit_cast(uint16_t, vl) << 16);
 }
 
 
@@ -916,7 +934,7 @@ int dl_split(const QMat &W, int M) {
     const int nb = W.K / 32;
     int best = 1;
     for (int S = 2; S <= 8; S *= 2)
-        if (tiles * S <= slots && nb % S == 0 && nb / S >= 16) best = S;
+        if (tiles * S <= slots && nb % S == 0 && nb / S >= 16 && (W.wtype != T_Q4_K || (nb / S) % 8 == 0)) best = S;
     return best;
 }
 
@@ -958,6 +976,11 @@ void gemm_set_num_cu(int n) {
     const char *wsv = getenv("DECODE_GEMM_WS");
     g_gemm_ws = 2;
     if (wsv) g_gemm_ws = atoi(wsv) == 0 ? 0 : atoi(wsv) == 4 ? 4 : 2;
+}
+
+void launch_q4k_mins(QMat &m, hipStream_t s) {
+    const long long n = (long long)m.N * (m.K / 32);
+    launch(k_q4k_mins, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, m);
 }
 
 void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, int K, float *xs, hipStream_t s) {

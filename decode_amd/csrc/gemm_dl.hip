@@ -41,11 +41,11 @@
 // Q4_K (256-weight super-blocks of eight 32-weight sub-blocks; weight = d sc q
 // - dmin m): the K block is a sub-block.  Its codes (stored in the Q4_0
 // nibble layout) enter the matrix cores as exact f16 values q = 0..15, the
-// temporary tile T = sum q x is scaled by d sc, and the min term is
-// dmin m times the token's block sum of x, which a small kernel writes
-// beforehand ([M][K/32] fp32): C += (d sc) T - (dmin m) X.  The sc | m word
-// is loaded where the f16 scale goes, plus one dword of d | dmin per row and
-// one x sum per token.
+// temporary tile T = sum q x is scaled by d sc (an fp32 array derived at load,
+// loaded where the f16 scale goes), and the min
+// term sum over K blocks of (dmin m) X, with X the token's block sum of x
+// (written beforehand by a small kernel), is a product of its own over K/32,
+// run on the matrix cores after the main loop straight into the accumulators.
 #include <type_traits>
 
 #include "common.h"
@@ -63,9 +63,8 @@ constexpr int DBM_S = 32;   // tokens per block (small-ubatch form)
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Q4_K adds per stage the rows' super-block factors (d | dmin << 16, one
-// dword per row) and the tokens' block sums of x (one fp32 per token; the
-// sc | m word of a sub-block takes the scale's place).
+// Q4_K loads its fp32 sub-block scale d sc (one dword per row) where the f16
+// scale goes.
 template <int WT, int TM>
 struct Geo {
     static constexpr bool K4 = WT == T_Q4_K;
@@ -74,13 +73,10 @@ struct Geo {
     static constexpr int OFF_LO = ACT;
     static constexpr int OFF_CODES = 2 * ACT;
     static constexpr int OFF_SC = 2 * ACT + DBN * CB;
-    static constexpr int OFF_DM = OFF_SC + DBN * 4;     // a 2-byte direct load fills one dword per lane
-    static constexpr int OFF_XS = OFF_DM + (K4 ? DBN * 4 : 0);
-    // (x sums: waves 0, 1 load the 128 tokens, waves 2, 3 the same into a spare 512 bytes)
-    static constexpr int STAGE = OFF_XS + (K4 ? 1024 : 0);
+    static constexpr int STAGE = OFF_SC + DBN * 4;      // a 2-byte direct load fills one dword per lane
     // direct loads per wavefront and K block: 4 activation (128 tokens) or 1
-    // (32 tokens), 1 or 2 code, 1 scale (Q4_K: + 1 factor, 1 x sum)
-    static constexpr int LOADS = TM / 32 + DBN * CB / 4096 + 1 + (K4 ? 2 : 0);
+    // (32 tokens), 1 or 2 code, 1 scale
+    static constexpr int LOADS = TM / 32 + DBN * CB / 4096 + 1;
 };
 
 // Slot of chunk c of token row m (see the header): the 16-byte reads of a
@@ -246,13 +242,9 @@ __global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(
     const uint8_t *xl_base = (const uint8_t *)Xl + (size_t)kb0 * 64;
     const uint8_t *c_base = (const uint8_t *)W.qs + (size_t)n0 * row_bytes + (size_t)kb0 * (Q4L ? 16 : 32);
     const uint8_t *s_base = (const uint8_t *)W.d + ((size_t)n0 * nb_all + kb0) * 2;
-    // Q4_K: factors of rows 64w + lane (super-block (kb0 + k) / 8) and x sums
-    // of tokens m0 + 64 (w & 1) + lane (rows past M repeat row M-1)
-    const uint32_t dmo = G::K4 ? (uint32_t)((size_t)(64 * w + lane) * (nb_all >> 3) * 4) : 0u;
-    const uint32_t xso =
-        G::K4 ? (uint32_t)((size_t)min(m0 + (TM == 128 ? 64 * (w & 1) + lane : lane & 31), M - 1) * nb_all * 4) : 0u;
-    const uint8_t *dm_base = G::K4 ? (const uint8_t *)W.dm + (size_t)n0 * (nb_all >> 3) * 4 : nullptr;
-    const uint8_t *xs_base = G::K4 ? (const uint8_t *)xs + (size_t)kb0 * 4 : nullptr;
+    // Q4_K: fp32 scales of rows 64w + lane
+    const uint32_t sfo = G::K4 ? (uint32_t)((size_t)(64 * w + lane) * nb_all * 4) : 0u;
+    const uint8_t *sf_base = G::K4 ? (const uint8_t *)W.sf + ((size_t)n0 * nb_all + kb0) * 4 : nullptr;
 
     auto stage_ptr = [&](auto sc) -> uint8_t * {
         constexpr int s = decltype(sc)::value;
@@ -287,11 +279,10 @@ __global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(
             for (int i = 0; i < 2; i++)
                 dma16s(c_base + k * 32, co[i], (const void AS3 *)(st + G::OFF_CODES + 1024 * (w + 4 * i)));
         }
-        dma2s(s_base + k * 2, so, (const void AS3 *)(st + G::OFF_SC + 256 * w));
-        if constexpr (G::K4) {
-            dma4s(dm_base + ((kb0 + k) >> 3) * 4, dmo, (const void AS3 *)(st + G::OFF_DM + 256 * w));
-            dma4s(xs_base + k * 4, xso, (const void AS3 *)(st + G::OFF_XS + 256 * w));
-        }
+        if constexpr (G::K4)
+            dma4s(sf_base + k * 4, sfo, (const void AS3 *)(st + G::OFF_SC + 256 * w));
+        else
+            dma2s(s_base + k * 2, so, (const void AS3 *)(st + G::OFF_SC + 256 * w));
     };
 
     // MF = 32: 32x32 tiles, 4 feature x 2 token tiles per wavefront;
@@ -359,9 +350,9 @@ __global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(
         if constexpr (MF == 32 && decltype(sc)::value >= 0) {
         const uint8_t *st = stage_ptr(sc);
         // the wavefront's feature tiles: codes of both k-halves and the scale
-        // (Q4_K: d sc and dmin m of the sub-block)
+        // (Q4_K: d sc of the sub-block)
         h8 c0[TA], c1[TA];
-        float d[TA], mf[TA];
+        float d[TA];
 #pragma unroll
         for (int a = 0; a < TA; a++) {
             const int f = wn + 32 * a + (lane & 31);
@@ -380,10 +371,7 @@ __global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(
                 c1[a] = q8_eight(hi8 ? u32x2{v1.z, v1.w} : u32x2{v1.x, v1.y});
             }
             if constexpr (G::K4) {
-                const uint32_t sm = *(const uint32_t *)(st + G::OFF_SC + 4 * f);
-                const uint32_t dd = *(const uint32_t *)(st + G::OFF_DM + 4 * f);
-                d[a] = f16_bits_to_f32((uint16_t)dd) * (float)(sm & 63);
-                mf[a] = f16_bits_to_f32((uint16_t)(dd >> 16)) * (float)((sm >> 8) & 63);
+                d[a] = *(const float *)(st + G::OFF_SC + 4 * f);
             } else {
                 d[a] = f16_bits_to_f32(*(const uint16_t *)(st + G::OFF_SC + 4 * f));
             }
@@ -401,27 +389,14 @@ __global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(
                 xh[h] = *(const h8 *)(st + 16 * slot);
                 xl[h] = *(const h8 *)(st + G::OFF_LO + 16 * slot);
             }
-            // Q4_K: block sums of x of this lane's 16 tokens (accumulator r:
-            // token 32b + (r/4)*8 + (lane/32)*4 + r%4)
-            f4 xsv[G::K4 ? 4 : 1];
-            if constexpr (G::K4) {
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    xsv[i] = *(const f4 *)(st + G::OFF_XS + 4 * (wm + 32 * b + 8 * i + 4 * (lane >> 5)));
-            }
 #pragma unroll
             for (int a = 0; a < TA; a++) {
                 f16x t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[0], c0[a], f16x{}, 0, 0, 0);
                 t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[0], c0[a], t, 0, 0, 0);
                 t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[1], c1[a], t, 0, 0, 0);
                 t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[1], c1[a], t, 0, 0, 0);
-                if constexpr (G::K4) {
 #pragma unroll
-                    for (int r = 0; r < 16; r++) acc[a][b][r] += d[a] * t[r] - mf[a] * xsv[r >> 2][r & 3];
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 16; r++) acc[a][b][r] += d[a] * t[r];
-                }
+                for (int r = 0; r < 16; r++) acc[a][b][r] += d[a] * t[r];
             }
         }
         }
@@ -464,6 +439,112 @@ __global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(
     }
     // drain the requests past the last K block before the block can exit
     wait_vm_lgkm0<0>();
+
+    // Q4_K min term, on the matrix cores: acc += X (-M)^T over this split's K
+    // blocks, with A = the tokens' block sums of x and B = the rows' negated
+    // sub-block mins -dmin m, both as f16 value | remainder << 16 per K block
+    // and stored octet-major ([K/256][rows][8]), so an octet of the block's
+    // rows is one contiguous run.  16 K blocks per MFMA step (each lane half
+    // takes one octet), three MFMAs per step (value x value, remainder x value,
+    // value x remainder).  K blocks past the split enter as zeros.
+    if constexpr (G::K4 && MF == 32) {
+        const uint32_t *xq = (const uint32_t *)xs;
+        const int kend = kb0 + nb, hf = lane >> 5;
+        auto unpack = [](const u32x4 &p0, const u32x4 &p1, h8 &hi, h8 &lo) __attribute__((always_inline)) {
+            const uint32_t v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                hi[e] = __builtin_bit_cast(f16, (uint16_t)v[e]);
+                lo[e] = __builtin_bit_cast(f16, (uint16_t)(v[e] >> 16));
+            }
+        };
+        if constexpr (TM == 128) {   // (the launcher splits K in whole octets for Q4_K)
+            // whole octets, 16 K blocks per chunk: the chunk's mins (2 octets x
+            // 256 rows x 32 B, contiguous per octet) go by direct loads into
+            // stage 0 and its sums (2 octets x 128 tokens x 32 B) into stage 1,
+            // then each lane reads its row's and token's 32 bytes from LDS
+            static_assert(TM != 128 || (G::STAGE >= 16384), "stage holds a chunk of mins");
+            const int oend = kend >> 3;
+            block_barrier();                               // every wavefront is done with the stages
+            for (int k16 = kb0; k16 < kend; k16 += 16) {
+                const int ob = k16 >> 3;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int j = 4 * w + i, oc = min(ob + (j >> 3), oend - 1);
+                    const int row = (j & 7) * 32 + (lane >> 1);
+                    dma16(W.mfq + ((size_t)oc * W.N + n0 + row) * 8 + 4 * (lane & 1),
+                          (const void AS3 *)(S0 + 1024 * j));
+                }
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    const int j = 2 * w + i, oc = min(ob + (j >> 2), oend - 1);
+                    const int row = min(m0 + (j & 3) * 32 + (lane >> 1), M - 1);
+                    dma16(xq + ((size_t)oc * M + row) * 8 + 4 * (lane & 1), (const void AS3 *)(S1 + 1024 * j));
+                }
+                wait_vm_lgkm0<0>();
+                block_barrier();
+                const bool live = ob + hf < oend;               // this lane half's octet lies in the split
+                h8 mh[TA], ml[TA];
+#pragma unroll
+                for (int a = 0; a < TA; a++) {
+                    const uint8_t *p = S0 + 8192 * hf + 32 * (wn + 32 * a + (lane & 31));
+                    u32x4 p0 = *(const u32x4 *)p, p1 = *(const u32x4 *)(p + 16);
+                    if (!live) p0 = p1 = u32x4{0u, 0u, 0u, 0u};
+                    unpack(p0, p1, mh[a], ml[a]);
+                }
+#pragma unroll
+                for (int b = 0; b < TB; b++) {
+                    const uint8_t *p = S1 + 4096 * hf + 32 * (wm + 32 * b + (lane & 31));
+                    u32x4 p0 = *(const u32x4 *)p, p1 = *(const u32x4 *)(p + 16);
+                    if (!live) p0 = p1 = u32x4{0u, 0u, 0u, 0u};
+                    h8 xh, xl;
+                    unpack(p0, p1, xh, xl);
+#pragma unroll
+                    for (int a = 0; a < TA; a++) {
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, mh[a], acc[a][b], 0, 0, 0);
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl, mh[a], acc[a][b], 0, 0, 0);
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, ml[a], acc[a][b], 0, 0, 0);
+                    }
+                }
+                block_barrier();                               // before the next chunk overwrites the stages
+            }
+        } else {
+            // the 32-token form, whose splits need not be whole octets: element loads
+            for (int k16 = kb0; k16 < kend; k16 += 16) {
+                const int kq = k16 + 8 * hf;
+                h8 mh[TA], ml[TA];
+#pragma unroll
+                for (int a = 0; a < TA; a++) {
+                    const size_t f = n0 + wn + 32 * a + (lane & 31);
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        const int k = kq + e;
+                        const uint32_t v = k < kend ? W.mfq[((size_t)(k >> 3) * W.N + f) * 8 + (k & 7)] : 0u;
+                        mh[a][e] = __builtin_bit_cast(f16, (uint16_t)v);
+                        ml[a][e] = __builtin_bit_cast(f16, (uint16_t)(v >> 16));
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < TB; b++) {
+                    const size_t row = min(m0 + wm + 32 * b + (lane & 31), M - 1);
+                    h8 xh, xl;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        const int k = kq + e;
+                        const uint32_t v = k < kend ? xq[((size_t)(k >> 3) * M + row) * 8 + (k & 7)] : 0u;
+                        xh[e] = __builtin_bit_cast(f16, (uint16_t)v);
+                        xl[e] = __builtin_bit_cast(f16, (uint16_t)(v >> 16));
+                    }
+#pragma unroll
+                    for (int a = 0; a < TA; a++) {
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, mh[a], acc[a][b], 0, 0, 0);
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl, mh[a], acc[a][b], 0, 0, 0);
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, ml[a], acc[a][b], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
 
     // ---- epilogue.  MF = 32: lane holds feature n0 + wn + 32a + (lane & 31)
     // and, in accumulator r, token m0 + wm + 32b + (r/4)*8 + (lane/32)*4 + r%4.

@@ -35,13 +35,19 @@ inline void launch(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s,
 //   Q4_K: qs = packed nibbles [N][K/2] in the Q4_0 layout (codes 0..15 of
 //         each 32-weight sub-block), d = sub-block scale | min << 8 [N][K/32]
 //         (six-bit integers), dm = f16 d | f16 dmin << 16 [N][K/256]
-//         (super-block factors): weight = f(d) * sc * q - f(dmin) * m
+//         (super-block factors): weight = f(d) * sc * q - f(dmin) * m;
+//         mfq = -f(dmin) * m per sub-block as f16 value | remainder << 16
+//         ([K/256][N][8]: the 8 sub-blocks of a super-block contiguous) and
+//         sf = f(d) * sc per sub-block in fp32 (exact, [N][K/32]), derived at
+//         load: the GEMM's min-term operand and block scale
 struct QMat {
     int wtype = 0;
     int N = 0, K = 0;
     void *qs = nullptr;
     uint16_t *d = nullptr;
     uint32_t *dm = nullptr;
+    uint32_t *mfq = nullptr;
+    float *sf = nullptr;
 };
 
 // How output rows of a matrix pair up in an epilogue.
@@ -151,12 +157,15 @@ size_t gemm_workspace_bytes(const QMat &W, int T);
 // The direct-to-LDS form of the ubatch GEMM (gemm_dl.hip): a block tile of
 // gemm_dl_tile_features() x gemm_dl_tile_tokens(), `ns` LDS stages (3, 4 or
 // 5), K split S (fp32 partial tiles in ws, summed by launch_splitk_sum).
-// Q4_K also reads xs, the tokens' block sums of x ([M][K/32] fp32, written by
+// Q4_K also reads xs, the tokens' block sums of x ([M][K/32], written by
 // launch_block_sums).
 void launch_gemm_dl(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,
                     int M, int pair_mode, int S, float *ws, const float *xs, hipStream_t s);
-// xs[m][kb] = sum over the 32 elements of block kb of (Xh + Xl)[m] (fp32, in order).
+// The sum over the 32 elements of block kb of (Xh + Xl)[m] (fp32, in order)
+// as f16 value | f16 remainder << 16 (uint32) at xs[((kb / 8) M + m) 8 + kb % 8].
 void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, int K, float *xs, hipStream_t s);
+// Q4_K: fills m.mfq and m.sf from m.d and m.dm (after every row of m is stored).
+void launch_q4k_mins(QMat &m, hipStream_t s);
 int gemm_dl_tile_features();
 int gemm_dl_tile_tokens();
 // The same form with 32-token block tiles for ubatches of at most 32 tokens
