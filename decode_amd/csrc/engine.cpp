@@ -1071,6 +1071,10 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         launch_embed(m->tok, tok, T, c->x, d, c->ssp, s);
         return true;
     });
+    // set where a K-split sum also wrote the next RMSNorm's output (the flags
+    // are per emission: a unit not emitted here leaves them 0, and the norm
+    // is then launched on its own)
+    int attn_normed = 0;
     for (int l = 0; ok && l < h.n_layer; l++) {
         const Layer &L = m->layers[l];
         EpiArgs eq;
@@ -1094,7 +1098,8 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 in.ldx = d;
                 return launch_matvec(L.wqkv, in, eq, T, s);
             }
-            launch_rmsnorm(c->x, d, L.attn_norm, d, h.rms_eps, nullptr, T, c->xn, c->xn_lo, d, s);
+            // (skipped where the previous down projection's K-split sum wrote it)
+            if (!attn_normed) launch_rmsnorm(c->x, d, L.attn_norm, d, h.rms_eps, nullptr, T, c->xn, c->xn_lo, d, s);
             return launch_gemm(L.wqkv, c->xn, c->xn_lo, d, eq, T, c->gws, c->gws_bytes, s);
         });
         // Q8_0 cache: a decode call's tokens are of distinct sequences, so the
@@ -1145,6 +1150,14 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         er.y = c->x;
         er.ldy = d;
         er.ss_out = c->ssp;
+        // a K-split sum ending the O projection also writes the FFN norm's input
+        int ffn_normed = 0;
+        er.nrm_g = L.ffn_norm;
+        er.nrm_eps = h.rms_eps;
+        er.nrm_h = c->xn;
+        er.nrm_l = c->xn_lo;
+        er.nrm_ld = d;
+        er.nrm_done = &ffn_normed;
         ok = ok && stage(c, DEC_K_WO, l, [&] {
             if (mv) {
                 InArgs in;
@@ -1170,9 +1183,18 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 in.ldx = d;
                 return launch_matvec(L.wgu, in, eg, T, s);
             }
-            launch_rmsnorm(c->x, d, L.ffn_norm, d, h.rms_eps, nullptr, T, c->xn, c->xn_lo, d, s);
+            if (!ffn_normed) launch_rmsnorm(c->x, d, L.ffn_norm, d, h.rms_eps, nullptr, T, c->xn, c->xn_lo, d, s);
             return launch_gemm(L.wgu, c->xn, c->xn_lo, d, eg, T, c->gws, c->gws_bytes, s);
         });
+        // and one ending the down projection, the next layer's attention norm input
+        attn_normed = 0;
+        if (l + 1 < h.n_layer) {
+            er.nrm_g = m->layers[l + 1].attn_norm;
+            er.nrm_done = &attn_normed;
+        } else {
+            er.nrm_g = nullptr;
+            er.nrm_done = nullptr;
+        }
         ok = ok && stage(c, DEC_K_FFN_DOWN, l, [&] {
             if (mv) {
                 InArgs in;

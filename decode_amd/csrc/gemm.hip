@@ -508,6 +508,60 @@ __global__ __launch_bounds__(256) void k_gemm_splitk_sum(const float *part, int 
     epi_pair<EPI>(ep, m, p, r0, r1, a, b);
 }
 
+// The K-split sum of a residual-adding GEMM fused with the RMSNorm of the
+// rows it completes: one 1024-thread block per token row; element j of the row
+// is y[j] + the sum of the S partials in split order (as k_gemm_splitk_sum adds
+// them), each thread holding its elements' sums in registers for the norm.
+constexpr int SRN_T = 1024, SRN_E = 16;      // threads, elements per thread at most (rows <= 16384)
+__global__ __launch_bounds__(SRN_T) void k_splitk_resid_norm(const float *part, int nsplit, int N, int M, EpiArgs ep) {
+    __shared__ float red[SRN_T / 64];
+    const int m = blockIdx.x, tid = threadIdx.x;
+    float *y = ep.y + (size_t)m * ep.ldy;
+    const float *pm = part + (size_t)m * N;
+    const size_t ps = (size_t)M * N;                   // between splits
+    float v[SRN_E];
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < SRN_E; u++) {
+        const int j = tid + SRN_T * u;
+        if (SRN_T * u >= N) break;                     // uniform
+        const int jc = min(j, N - 1);
+        float pv[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) pv[k] = k < nsplit ? pm[k * ps + jc] : 0.f;
+        float a = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            if (k < nsplit) a += pv[k];
+        for (int k = 8; k < nsplit; k++) a += pm[k * ps + jc];
+        v[u] = y[jc] + a;
+        if (j < N) {
+            y[j] = v[u];
+            ss += v[u] * v[u];
+        }
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < SRN_T / 64; i++) tot += red[i];
+    const float r = 1.0f / sqrtf(tot / (float)N + ep.nrm_eps);
+    f16 *o = (f16 *)ep.nrm_h + (size_t)m * ep.nrm_ld;
+    f16 *ol = (f16 *)ep.nrm_l + (size_t)m * ep.nrm_ld;
+#pragma unroll
+    for (int u = 0; u < SRN_E; u++) {
+        const int j = tid + SRN_T * u;
+        if (SRN_T * u >= N) break;
+        if (j < N) {
+            const float w = v[u] * r * ep.nrm_g[j];
+            const f16 hi = (f16)w;
+            o[j] = hi;
+            ol[j] = (f16)(w - (float)hi);
+        }
+    }
+}
+
 // fp32 weights (any K), f16 activations; one thread per (row pair, token).
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_f32(QMat W, const uint16_t *X, const uint16_t *Xl,
@@ -990,6 +1044,11 @@ void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, i
 
 void launch_splitk_sum(int epi, const float *ws, int S, int N, int M, const EpiArgs &ep, int pair_mode,
                        hipStream_t s) {
+    if (epi == EPI_RESID && ep.nrm_g && ep.nrm_done) {
+        launch(k_splitk_resid_norm, dim3(M), dim3(SRN_T), 0, s, ws, S, N, M, ep);
+        *ep.nrm_done = 1;
+        return;
+    }
     const dim3 g((N / 2 + 255) / 256, M);
     switch (epi) {
     case EPI_STORE: launch(k_gemm_splitk_sum<EPI_STORE>, g, dim3(256), 0, s, ws, S, N, M, ep, pair_mode); break;

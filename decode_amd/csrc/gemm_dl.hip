@@ -373,7 +373,11 @@ __global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(
             if constexpr (G::K4) {
                 d[a] = *(const float *)(st + G::OFF_SC + 4 * f);
             } else {
+                // (converted once here and kept opaque: the 16 scaling FMAs of a
+                // tile then issue as plain fp32 FMAs instead of f16-operand
+                // v_fma_mix_f32; measured 1.6% faster on the gate/up GEMM)
                 d[a] = f16_bits_to_f32(*(const uint16_t *)(st + G::OFF_SC + 4 * f));
+                asm volatile("" : "+v"(d[a]));
             }
         }
         // (keeps the token tiles' fragment reads below: hoisted above, they

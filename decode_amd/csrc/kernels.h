@@ -102,6 +102,14 @@ struct EpiArgs {
     KVLayer kv;
     TokInfo tok;
     const float *rope_cs = nullptr;  // [n_ctx][hd/2][2] (cos, sin)
+    // RESID, optional: when the GEMM ends with a K-split sum, that kernel also
+    // writes the new rows' RMSNorm (gain nrm_g, eps nrm_eps) as f16 value
+    // nrm_h + remainder nrm_l [T][nrm_ld] and sets *nrm_done = 1 (host flag)
+    const float *nrm_g = nullptr;
+    float nrm_eps = 0.f;
+    uint16_t *nrm_h = nullptr, *nrm_l = nullptr;
+    int nrm_ld = 0;
+    int *nrm_done = nullptr;
 };
 
 // Input of a mat-vec / GEMM: either an f32 residual row normalized on the
