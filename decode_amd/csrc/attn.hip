@@ -359,13 +359,18 @@ DEV void mfma_combine(const AttnArgs &a, int c, int g, int t, int G, float m, fl
     }
 }
 
-template <int HD>
+// KT: K rows through an LDS tile as coalesced 16-byte pieces (for calls of a
+// few tokens, where the grid is small and each load's latency is exposed);
+// else straight into the operand (many blocks: the tile's LDS would cut how
+// many are resident, which costs more than the wider loads save).
+template <int HD, bool KT>
 __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
     constexpr int KS = HD / 16;          // k-steps of S^T = K Q^T
     constexpr int DT = HD / 32;          // 32-dim tiles of O = P V
     __shared__ float cm[MW][32], cl[MW][32];
     __shared__ __attribute__((aligned(16))) float co[MW][GMAX][HD];
     __shared__ __attribute__((aligned(16))) f16 vtile[MW][32 * (HD + 8)];
+    __shared__ __attribute__((aligned(16))) f16 ktile[KT ? MW : 1][KT ? 32 * (HD + 8) : 8];
 
     const int c = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, ln = lane & 31;
@@ -380,11 +385,24 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
 
     // ---- every load at entry; rows past pos are replaced by row pos (finite
     // data whose weights are 0) ----
-    // A operand of S^T: key k0 + lane%32, dims 16 ks + 8 (lane/32) .. + 7
+    // A operand of S^T: key k0 + lane%32, dims 16 ks + 8 (lane/32) .. + 7.
+    // KT: the wavefront's 32 K rows are requested as 16-byte pieces, HD/8
+    // lanes per row (a load instruction covers 64 / (HD/8) whole rows instead
+    // of 16 bytes of 32 rows), and pass through a wavefront-private LDS tile.
+    constexpr int VP = HD / 8, VR = 32 * VP / 64;      // pieces per row, rounds
+    u32x4 kraw[KT ? VR : 1];
     h8 kf[KS];
-    const int kr = min(k0 + ln, pos);
+    if constexpr (KT) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ks++) kf[ks] = *(const h8 *)(Kb + (size_t)kr * HD + 16 * ks + 8 * hf);
+        for (int u = 0; u < VR; u++) {
+            const int pc = u * 64 + lane, key = min(k0 + pc / VP, pos);
+            kraw[u] = *(const u32x4 *)(Kb + (size_t)key * HD + 8 * (pc % VP));
+        }
+    } else {
+        const int kr = min(k0 + ln, pos);
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) kf[ks] = *(const h8 *)(Kb + (size_t)kr * HD + 16 * ks + 8 * hf);
+    }
     // B operand of S^T: head lane%32 (clamped to the group; the extra columns
     // are ignored), the same dims, q / sqrt(hd) as value + remainder
     h8 qa[KS], qb[KS];
@@ -397,15 +415,26 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
     // B operand of O = P V for k-step s: element e of lane l is key
     // 16 s + 8 (e/4) + 4 (l/32) + e%4 -- the keys whose probabilities the lane
     // holds in its S^T accumulators 8 s + e -- at dim 32 dt + l%32
-    // The wavefront's 32 V rows are requested as 16-byte pieces (8 KB at hd
-    // 128: HD/8 pieces per row, 64 lanes per round) and pass through a
-    // wavefront-private LDS tile, from which the transposed operand is read.
-    constexpr int VP = HD / 8, VR = 32 * VP / 64;      // pieces per row, rounds
+    // The wavefront's 32 V rows are requested the same way (8 KB at hd 128)
+    // and pass through their own tile, from which the transposed operand is read.
     u32x4 vraw[VR];
 #pragma unroll
     for (int u = 0; u < VR; u++) {
         const int pc = u * 64 + lane, key = min(k0 + pc / VP, pos);
         vraw[u] = *(const u32x4 *)(Vb + (size_t)key * HD + 8 * (pc % VP));
+    }
+
+    // ---- KT: K tile through LDS (rows padded by 16 bytes) ----
+    if constexpr (KT) {
+        f16 *kt = &ktile[w][0];
+#pragma unroll
+        for (int u = 0; u < VR; u++) {
+            const int pc = u * 64 + lane;
+            *(u32x4 *)(kt + (pc / VP) * (HD + 8) + 8 * (pc % VP)) = kraw[u];
+        }
+        // (a wavefront's LDS accesses complete in order: no wait or barrier)
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) kf[ks] = *(const h8 *)(kt + ln * (HD + 8) + 16 * ks + 8 * hf);
     }
 
     // ---- S^T = K Q^T (exact products, fp32 accumulation) ----
@@ -678,8 +707,10 @@ bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
             if (a.H / a.kv.n_kv > GMAX || !a.qh || !a.ql) return false;
             if (a.kv.kvtype == T_Q8_0)
                 launch(k_attn_mfma_q8<HD>, dim3(a.max_chunks, a.kv.n_kv, T), dim3(MW * 64), 0, s, a);
+            else if (T <= 4)   // (measured: batch 1 13.5 -> 12.5 us per layer; batch 32 slower)
+                launch(k_attn_mfma<HD, true>, dim3(a.max_chunks, a.kv.n_kv, T), dim3(MW * 64), 0, s, a);
             else
-                launch(k_attn_mfma<HD>, dim3(a.max_chunks, a.kv.n_kv, T), dim3(MW * 64), 0, s, a);
+                launch(k_attn_mfma<HD, false>, dim3(a.max_chunks, a.kv.n_kv, T), dim3(MW * 64), 0, s, a);
             ok = true;
         } else {
             return false;
