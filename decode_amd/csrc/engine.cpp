@@ -131,7 +131,9 @@ static void model_release(dec_model *m) {
     delete m;
 }
 
-static bool alloc_qmat(Mem &mem, QMat &m, int wtype, int N, int K) {
+// gemm: the matrix is a GEMM operand (every matrix but the token embedding),
+// which also holds the GEMM's derived scale arrays.
+static bool alloc_qmat(Mem &mem, QMat &m, int wtype, int N, int K, bool gemm = true) {
     m.wtype = wtype;
     m.N = N;
     m.K = K;
@@ -149,9 +151,15 @@ static bool alloc_qmat(Mem &mem, QMat &m, int wtype, int N, int K) {
     }
     if (wtype == DEC_Q4_K) {
         m.dm = (uint32_t *)mem.get((size_t)N * (K / 256) * 4);
-        m.mfq = (uint32_t *)mem.get((size_t)N * (K / 32) * 4);
-        m.sf = (float *)mem.get((size_t)N * (K / 32) * 4);
-        if (!m.dm || !m.mfq || !m.sf) return false;
+        if (!m.dm) return false;
+        if (gemm) {
+            m.mfq = (uint32_t *)mem.get((size_t)N * (K / 32) * 4);
+            m.sf = (float *)mem.get((size_t)N * (K / 32) * 4);
+            if (!m.mfq || !m.sf) return false;
+        }
+    } else if (gemm && (wtype == DEC_Q8_0 || wtype == DEC_Q4_0)) {
+        m.dt = (uint16_t *)mem.get((size_t)N * (K / 32) * 2);
+        if (!m.dt) return false;
     }
     return true;
 }
@@ -200,12 +208,12 @@ struct Loader {
 };
 
 // Q4_K: the GEMM's min-term operand of every matrix, once all rows are stored.
-static void finish_q4k(dec_model *m, hipStream_t s) {
-    if (m->hp.wtype != DEC_Q4_K) return;
-    launch_q4k_mins(m->tok, s);
-    launch_q4k_mins(m->out, s);
+// The GEMM operands' derived scale arrays, once every matrix is stored.
+static void finish_gemm_scales(dec_model *m, hipStream_t s) {
+    if (m->hp.wtype == DEC_F32) return;
+    launch_gemm_scales(m->out, s);
     for (Layer &L : m->layers)
-        for (QMat *q : {&L.wqkv, &L.wo, &L.wgu, &L.wdown}) launch_q4k_mins(*q, s);
+        for (QMat *q : {&L.wqkv, &L.wo, &L.wgu, &L.wdown}) launch_gemm_scales(*q, s);
 }
 
 static bool valid_hparams(const dec_hparams &h) {
@@ -253,7 +261,7 @@ extern "C" dec_model *dec_model_load(const dec_hparams *hp, const dec_weights *w
     m->Fp = (h.n_ff + 31) / 32 * 32;
     const int d = h.n_embd, V = h.n_vocab, qd = m->qd, kd = m->kd, F = m->F, Fp = m->Fp;
 
-    bool ok = alloc_qmat(m->mem, m->tok, h.wtype, V, d) && alloc_qmat(m->mem, m->out, h.wtype, V, d);
+    bool ok = alloc_qmat(m->mem, m->tok, h.wtype, V, d, false) && alloc_qmat(m->mem, m->out, h.wtype, V, d);
     m->layers.resize(h.n_layer);
     for (int l = 0; ok && l < h.n_layer; l++) {
         Layer &L = m->layers[l];
@@ -296,7 +304,7 @@ extern "C" dec_model *dec_model_load(const dec_hparams *hp, const dec_weights *w
              ld.put(w->ffn_down[l], d, F, L.wdown, 0, 0) && ld.vec(w->attn_norm[l], d, &L.attn_norm) &&
              ld.vec(w->ffn_norm[l], d, &L.ffn_norm);
     }
-    if (ok) finish_q4k(m, m->stream);
+    if (ok) finish_gemm_scales(m, m->stream);
     if (ok) HIP_OK(hipStreamSynchronize(m->stream), ok = false);
     m->mem.drop(ld.stage);   // host weights are staged during the load only
     if (!ok) {
@@ -528,7 +536,7 @@ extern "C" dec_model *dec_model_load_gguf(const char *path, int32_t kvtype, cons
     m->F = h.n_ff;
     m->Fp = (h.n_ff + 31) / 32 * 32;
     const int d = h.n_embd, V = h.n_vocab, qd = m->qd, kd = m->kd, F = m->F, Fp = m->Fp;
-    bool ok = alloc_qmat(m->mem, m->tok, h.wtype, V, d) && alloc_qmat(m->mem, m->out, h.wtype, V, d);
+    bool ok = alloc_qmat(m->mem, m->tok, h.wtype, V, d, false) && alloc_qmat(m->mem, m->out, h.wtype, V, d);
     m->layers.resize(h.n_layer);
     for (int l = 0; ok && l < h.n_layer; l++) {
         Layer &L = m->layers[l];
@@ -570,7 +578,7 @@ extern "C" dec_model *dec_model_load_gguf(const char *path, int32_t kvtype, cons
              put(layer_name(l, "ffn_down"), d, F, L.wdown, 0, 0) && vec(layer_name(l, "attn_norm"), &L.attn_norm) &&
              vec(layer_name(l, "ffn_norm"), &L.ffn_norm);
     }
-    if (ok) finish_q4k(m, s);
+    if (ok) finish_gemm_scales(m, s);
     if (ok) HIP_OK(hipStreamSynchronize(s), ok = false);
     m->mem.drop(stage);   // the file's tensors pass through it during the load only
     if (!ok) {

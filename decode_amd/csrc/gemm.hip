@@ -656,7 +656,7 @@ __global__ __launch_bounds__(256) void k_block_sums(const uint16_t *Xh, const ui
 }
 
 // mfq = -f(dmin) m of sub-block kb of row n as f16 value | remainder << 16,
-// octet-major ([K/256][N][8]); sf[n][kb] = f(d) sc (exact in fp32: an 11-bit
+// octet-major ([K/256][N][8]); sf[kb][n] = f(d) sc (exact in fp32: an 11-bit
 // significand times a six-bit integer).
 __global__ __launch_bounds__(256) void k_q4k_mins(QMat W) {
     const int nb = W.K >> 5;
@@ -664,10 +664,20 @@ __global__ __launch_bounds__(256) void k_q4k_mins(QMat W) {
     if (idx >= (long long)W.N * nb) return;
     const int r = (int)(idx / nb), b = (int)(idx % nb);
     const uint32_t dd = W.dm[(size_t)r * (W.K >> 8) + (b >> 3)];
-    W.sf[idx] = f16_bits_to_f32((uint16_t)dd) * (float)(W.d[idx] & 63);
+    W.sf[(size_t)b * W.N + r] = f16_bits_to_f32((uint16_t)dd) * (float)(W.d[idx] & 63);
     const float v = -f16_bits_to_f32((uint16_t)(dd >> 16)) * (float)((W.d[idx] >> 8) & 63);
     const f16 vh = (f16)v, vl = (f16)(v - (float)vh);
     W.mfq[((size_t)(b >> 3) * W.N + r) * 8 + (b & 7)] = (uint32_t)__builtin_bit_cast(uint16_t, vh) | ((uint32_t)__builtin_bit_cast(uint16_t, vl) << 16);
+}
+
+
+// dt[kb][n] = d[n][kb]
+__global__ __launch_bounds__(256) void k_scales_t(QMat W) {
+    const int nb = W.K >> 5;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)W.N * nb) return;
+    const int r = (int)(idx / nb), b = (int)(idx % nb);
+    W.dt[(size_t)b * W.N + r] = W.d[idx];
 }
 
 
@@ -924,6 +934,9 @@ bool launch_plainq(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ld
     return true;
 }
 
+// The transposed scale array the direct-to-LDS forms read (dt, Q4_K sf).
+static bool has_gemm_scales(const QMat &W) { return W.wtype == T_Q4_K ? W.sf != nullptr : W.dt != nullptr; }
+
 // Direct-to-LDS form (gemm_dl.hip): ubatches of more than 64 tokens with the
 // exact operands (Q4_K: any ubatch, it has no other MFMA form), feature
 // counts that are whole 256-feature tiles.
@@ -931,7 +944,8 @@ bool dl_shape(const QMat &W, int M, int ldx) {
     // the direct loads address operands by 32-bit byte offsets from a base
     const size_t row_bytes = W.wtype == T_Q8_0 ? (size_t)W.K : (size_t)W.K / 2;
     const bool k4 = W.wtype == T_Q4_K;
-    return g_gemm_dl > 0 && (k4 || (!g_gemm_f16w && M > 64)) && W.N % gemm_dl_tile_features() == 0 &&
+    return g_gemm_dl > 0 && has_gemm_scales(W) && (k4 || (!g_gemm_f16w && M > 64)) &&
+           W.N % gemm_dl_tile_features() == 0 &&
            (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * row_bytes < ((size_t)1 << 31) &&
            (size_t)M * (W.K / 32) * 4 < ((size_t)1 << 31);
 }
@@ -939,7 +953,8 @@ bool dl_shape(const QMat &W, int M, int ldx) {
 // The 32-token direct-to-LDS form: at most 32 tokens, whole 256-feature tiles.
 bool dls_shape(const QMat &W, int M, int ldx) {
     const size_t row_bytes = W.wtype == T_Q8_0 ? (size_t)W.K : (size_t)W.K / 2;
-    return (g_gemm_dls || W.wtype == T_Q4_K) && g_gemm_dl > 0 && M > 0 && M <= gemm_dls_tile_tokens() &&
+    return (g_gemm_dls || W.wtype == T_Q4_K) && g_gemm_dl > 0 && has_gemm_scales(W) && M > 0 &&
+           M <= gemm_dls_tile_tokens() &&
            W.wtype != T_F32 && W.N % gemm_dl_tile_features() == 0 && ldx % 8 == 0 &&
            (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * row_bytes < ((size_t)1 << 31);
 }
@@ -1032,9 +1047,12 @@ void gemm_set_num_cu(int n) {
     if (wsv) g_gemm_ws = atoi(wsv) == 0 ? 0 : atoi(wsv) == 4 ? 4 : 2;
 }
 
-void launch_q4k_mins(QMat &m, hipStream_t s) {
+void launch_gemm_scales(QMat &m, hipStream_t s) {
     const long long n = (long long)m.N * (m.K / 32);
-    launch(k_q4k_mins, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, m);
+    if (m.wtype == T_Q4_K)
+        launch(k_q4k_mins, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, m);
+    else if (m.dt)
+        launch(k_scales_t, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, m);
 }
 
 void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, int K, float *xs, hipStream_t s) {

@@ -237,14 +237,15 @@ __global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(
             co[i] = (uint32_t)((size_t)r * row_bytes + half * 16);
         }
     }
-    const uint32_t so = (uint32_t)((size_t)(64 * w + lane) * nb_all * 2);
+    // scales: the block's 256 rows of one K block are contiguous in the
+    // transposed arrays (f16 dt, Q4_K fp32 sf), 64 of them per wavefront
+    const uint32_t so = (uint32_t)((64 * w + lane) * (G::K4 ? 4 : 2));
     const uint8_t *xh_base = (const uint8_t *)Xh + (size_t)kb0 * 64;
     const uint8_t *xl_base = (const uint8_t *)Xl + (size_t)kb0 * 64;
     const uint8_t *c_base = (const uint8_t *)W.qs + (size_t)n0 * row_bytes + (size_t)kb0 * (Q4L ? 16 : 32);
-    const uint8_t *s_base = (const uint8_t *)W.d + ((size_t)n0 * nb_all + kb0) * 2;
-    // Q4_K: fp32 scales of rows 64w + lane
-    const uint32_t sfo = G::K4 ? (uint32_t)((size_t)(64 * w + lane) * nb_all * 4) : 0u;
-    const uint8_t *sf_base = G::K4 ? (const uint8_t *)W.sf + ((size_t)n0 * nb_all + kb0) * 4 : nullptr;
+    const size_t s_step = (size_t)W.N * (G::K4 ? 4 : 2);   // bytes per K block
+    const uint8_t *s_base = (G::K4 ? (const uint8_t *)W.sf : (const uint8_t *)W.dt) +
+                            (size_t)kb0 * s_step + (size_t)n0 * (G::K4 ? 4 : 2);
 
     auto stage_ptr = [&](auto sc) -> uint8_t * {
         constexpr int s = decltype(sc)::value;
@@ -280,9 +281,9 @@ __global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(
                 dma16s(c_base + k * 32, co[i], (const void AS3 *)(st + G::OFF_CODES + 1024 * (w + 4 * i)));
         }
         if constexpr (G::K4)
-            dma4s(sf_base + k * 4, sfo, (const void AS3 *)(st + G::OFF_SC + 256 * w));
+            dma4s(s_base + k * s_step, so, (const void AS3 *)(st + G::OFF_SC + 256 * w));
         else
-            dma2s(s_base + k * 2, so, (const void AS3 *)(st + G::OFF_SC + 256 * w));
+            dma2s(s_base + k * s_step, so, (const void AS3 *)(st + G::OFF_SC + 256 * w));
     };
 
     // MF = 32: 32x32 tiles, 4 feature x 2 token tiles per wavefront;
@@ -383,9 +384,8 @@ __global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(
         // (keeps the token tiles' fragment reads below: hoisted above, they
         // would hold registers the codes need)
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int b = 0; b < TB; b++) {
-            h8 xh[2], xl[2];
+        h8 xh[2], xl[2];
+        auto read_x = [&](int b) __attribute__((always_inline)) {
             const int m = wm + 32 * b + (lane & 31);
 #pragma unroll
             for (int h = 0; h < 2; h++) {
@@ -393,14 +393,57 @@ __global__ __launch_bounds__(256, (NS <= 3 || TM == 32) ? 2 : 1) void k_gemm_dl(
                 xh[h] = *(const h8 *)(st + 16 * slot);
                 xl[h] = *(const h8 *)(st + G::OFF_LO + 16 * slot);
             }
+        };
+        auto chain = [&](int a) __attribute__((always_inline)) {
+            f16x t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[0], c0[a], f16x{}, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[0], c0[a], t, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[1], c1[a], t, 0, 0, 0);
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[1], c1[a], t, 0, 0, 0);
+        };
+        if constexpr (WL) {
+            // Tiles i = TA b + a in order, software-pipelined: the four MFMAs
+            // of tile i go into one of two temporaries while the 16 scaling
+            // FMAs of tile i-1 read the other, and the issue order below puts
+            // four of those FMAs after each MFMA, so the matrix cores and the
+            // VALU work at the same time (with one temporary every scaling
+            // waits for its chain and the next chain for the scaling).
+            read_x(0);
+            f16x tp = chain(0);
 #pragma unroll
-            for (int a = 0; a < TA; a++) {
-                f16x t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[0], c0[a], f16x{}, 0, 0, 0);
-                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[0], c0[a], t, 0, 0, 0);
-                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[1], c1[a], t, 0, 0, 0);
-                t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[1], c1[a], t, 0, 0, 0);
+            for (int i = 1; i < TA * TB; i++) {
+                const int a = i % TA, b = i / TA, pa = (i - 1) % TA, pb = (i - 1) / TA;
+                if (a == 0) read_x(b);
+                const f16x tc = chain(a);
 #pragma unroll
-                for (int r = 0; r < 16; r++) acc[a][b][r] += d[a] * t[r];
+                for (int r = 0; r < 16; r++) acc[pa][pb][r] += d[pa] * tp[r];
+                tp = tc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[TA - 1][TB - 1][r] += d[TA - 1] * tp[r];
+            // per tile: its fragment reads (first feature tile of a token
+            // tile), then each MFMA followed by four FMAs
+#pragma unroll
+            for (int i = 0; i < TA * TB; i++) {
+                if (i % TA == 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (i > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        } else {
+            // (128-feature wavefront tiles: the pipelined order would need
+            // more registers than a wavefront has)
+#pragma unroll
+            for (int b = 0; b < TB; b++) {
+                read_x(b);
+#pragma unroll
+                for (int a = 0; a < TA; a++) {
+                    const f16x t = chain(a);
+#pragma unroll
+                    for (int r = 0; r < 16; r++) acc[a][b][r] += d[a] * t[r];
+                }
             }
         }
         }

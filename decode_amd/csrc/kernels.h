@@ -38,13 +38,18 @@ inline void launch(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s,
 //         (super-block factors): weight = f(d) * sc * q - f(dmin) * m;
 //         mfq = -f(dmin) * m per sub-block as f16 value | remainder << 16
 //         ([K/256][N][8]: the 8 sub-blocks of a super-block contiguous) and
-//         sf = f(d) * sc per sub-block in fp32 (exact, [N][K/32]), derived at
+//         sf = f(d) * sc per sub-block in fp32 (exact, [K/32][N]), derived at
 //         load: the GEMM's min-term operand and block scale
+//   Q4_0/Q8_0 matrices a GEMM reads also hold dt = d transposed ([K/32][N],
+//   derived at load): the scales of one K block of consecutive rows are then
+//   one contiguous run, which the direct-to-LDS GEMM loads with a few wide
+//   requests instead of one 2-byte request per row.
 struct QMat {
     int wtype = 0;
     int N = 0, K = 0;
     void *qs = nullptr;
     uint16_t *d = nullptr;
+    uint16_t *dt = nullptr;
     uint32_t *dm = nullptr;
     uint32_t *mfq = nullptr;
     float *sf = nullptr;
@@ -172,8 +177,9 @@ void launch_gemm_dl(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *X
 // The sum over the 32 elements of block kb of (Xh + Xl)[m] (fp32, in order)
 // as f16 value | f16 remainder << 16 (uint32) at xs[((kb / 8) M + m) 8 + kb % 8].
 void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, int K, float *xs, hipStream_t s);
-// Q4_K: fills m.mfq and m.sf from m.d and m.dm (after every row of m is stored).
-void launch_q4k_mins(QMat &m, hipStream_t s);
+// Derives the GEMM's scale arrays once every row of m is stored: Q4_0/Q8_0
+// m.dt from m.d; Q4_K m.mfq and m.sf from m.d and m.dm.
+void launch_gemm_scales(QMat &m, hipStream_t s);
 int gemm_dl_tile_features();
 int gemm_dl_tile_tokens();
 // The same form with 32-token block tiles for ubatches of at most 32 tokens
