@@ -830,6 +830,7 @@ int g_gemm_dls = 1;    // direct-to-LDS form with 32-token tiles for at most 32 
 int g_gemm_dls_ns = 4; // its LDS stages
 int g_gemm_dls_fill = 4; // its K split aims at this many blocks per 4 compute units
 int g_gemm_ws = 2;     // weight-streaming form for Q4_0 at most 32 tokens: K blocks per stage (0: off)
+int g_gemm_dw = 1;     // wide direct-to-LDS form for Q4_0 ubatches of more than 64 tokens (0: off)
 
 bool mfma_shape(const QMat &W, int ldx) {
     return (W.wtype == T_Q4_0 || W.wtype == T_Q8_0) && W.N % BN == 0 && W.K % 32 == 0 && ldx % 8 == 0;
@@ -950,6 +951,26 @@ bool dl_shape(const QMat &W, int M, int ldx) {
            (size_t)M * (W.K / 32) * 4 < ((size_t)1 << 31);
 }
 
+// The wide form (Q4_0): more than 64 tokens, whole 512-feature tiles, K in
+// whole code super-stages.
+bool dw_shape(const QMat &W, int M, int ldx) {
+    return g_gemm_dw && g_gemm_dl > 0 && !g_gemm_f16w && W.wtype == T_Q4_0 && W.dt && M > 64 &&
+           W.N % gemm_dw_tile_features() == 0 && (W.K / 32) % gemm_dw_super_blocks() == 0 &&
+           (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * (W.K / 2) < ((size_t)1 << 31);
+}
+
+// Its K split: the largest of 1, 2, 4, 8 whose grid fits one block per
+// compute unit, with equal splits of whole super-stages of at least 16 K
+// blocks.
+int dw_split(const QMat &W, int M) {
+    const long tiles = (long)(W.N / gemm_dw_tile_features()) * ((M + 127) / 128);
+    const int nb = W.K / 32;
+    int best = 1;
+    for (int S = 2; S <= 8; S *= 2)
+        if (tiles * S <= g_gemm_cu && nb % (S * gemm_dw_super_blocks()) == 0 && nb / S >= 16) best = S;
+    return best;
+}
+
 // The 32-token direct-to-LDS form: at most 32 tokens, whole 256-feature tiles.
 bool dls_shape(const QMat &W, int M, int ldx) {
     const size_t row_bytes = W.wtype == T_Q8_0 ? (size_t)W.K : (size_t)W.K / 2;
@@ -1042,6 +1063,10 @@ void gemm_set_num_cu(int n) {
     // DECODE_GEMM_WS: K blocks per stage of the weight-streaming form (2 or 4,
     // default 2); 0 leaves Q4_0 ubatches of at most 32 tokens to the 32-token
     // direct-to-LDS form
+    // DECODE_GEMM_DW=0: Q4_0 ubatches of more than 64 tokens take the
+    // 256-feature direct-to-LDS form instead of the wide one
+    const char *dwv = getenv("DECODE_GEMM_DW");
+    g_gemm_dw = !(dwv && strcmp(dwv, "0") == 0);
     const char *wsv = getenv("DECODE_GEMM_WS");
     g_gemm_ws = 2;
     if (wsv) g_gemm_ws = atoi(wsv) == 0 ? 0 : atoi(wsv) == 4 ? 4 : 2;
@@ -1098,6 +1123,10 @@ size_t gemm_workspace_bytes(const QMat &W, int M) {
     if (dl_shape(W, M, W.K)) {
         const int Sd = dl_split(W, M);
         tile = std::max(tile, Sd > 1 ? (size_t)Sd * M * W.N * 4 : (size_t)0);
+    }
+    if (dw_shape(W, M, W.K)) {
+        const int Sw = dw_split(W, M);
+        tile = std::max(tile, Sw > 1 ? (size_t)Sw * M * W.N * 4 : (size_t)0);
     }
     tile = std::max(tile, small);
     // the skinny form, for any ubatch of at most min(M, 32) tokens
@@ -1161,6 +1190,12 @@ bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
             }
             return true;
         }
+    }
+    if (mfma_shape(W, ldx) && dw_shape(W, M, ldx)) {
+        int S = dw_split(W, M);
+        while (S > 1 && (!ws || (size_t)S * M * W.N * 4 > ws_bytes)) S >>= 1;
+        launch_gemm_dw(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+        return true;
     }
     if (mfma_shape(W, ldx) && dl_shape(W, M, ldx)) {
         int S = dl_split(W, M);

@@ -1023,6 +1023,291 @@ void launch_ws_epi(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *Xl
         launch_ws_ks<EPI, 2>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
 }
 
+
+// ---- wide form: Q4_0, 512 features x 128 tokens per block -------------------
+//
+// The arithmetic and operand layouts of k_gemm_dl (exact codes, activation
+// value and remainder, per-block fp32 scaling, 64-feature wavefront tiles over
+// all 128 tokens), with the operand movement cut into fewer, wider memory
+// requests.  Measured on the direct-to-LDS form: its time follows the number
+// of requests, not the bytes (per K block of a 256 x 128 tile: 256 one-row
+// 16-byte code requests, 256 64-byte activation requests; codes alone took
+// 102 us of a 512-token gate/up GEMM, and 46 us when each request covered 4
+// K blocks of a row).  Here:
+// * codes come in super-stages of DW_CK = 4 K blocks: 64 contiguous bytes per
+//   row and request, double-buffered (super-stage s+1 is requested at the
+//   first K block of s);
+// * a block covers 512 features (8 wavefronts), so each activation request
+//   feeds twice the features;
+// * activations and scales (from the transposed dt) go through a ring of
+//   DW_A = 4 single-K-block stages, three K blocks ahead.
+// LDS (one array, 136 KB, one block of 8 wavefronts per compute unit, two
+// per SIMD): the 4 activation stages fill the first 64 KB, so every
+// activation read is a fixed register plus an immediate offset; then the
+// stages' scales and the two code stages.  A wavefront requests 3 loads per K block (2
+// activation, 1 scale) and 4 code loads every 4th; loads complete in issue
+// order, so the wait before K block kb is a constant per kb % 4: 6 loads
+// issued after its activation stage when kb % 4 == 0, else 10 (the code
+// loads of the super-stage issued in between).  The K range of a split is a
+// whole number of super-stages.
+constexpr int DW_N = 512;                       // features per block
+constexpr int DW_A = 4;                         // activation stages
+constexpr int DW_CK = 4;                        // K blocks per code super-stage
+constexpr int DW_ACT = 128 * 64;                // one activation part of a K block
+constexpr int DW_AST = 2 * DW_ACT;              // activation stage: values, remainders
+constexpr int DW_SST = DW_N * 4;                // scales of a K block, one dword per row
+constexpr int DW_CST = DW_N * 16 * DW_CK;       // codes of a super-stage: [512 rows][4 x 16 B]
+constexpr int DW_OFF_S = DW_A * DW_AST;         // (= 64 KB)
+constexpr int DW_OFF_C = DW_OFF_S + DW_A * DW_SST;
+constexpr int DW_LDS = DW_OFF_C + 2 * DW_CST;
+
+// Position of K block q (0..3) of a super-stage in row r: XOR-swizzled so that
+// the 16-byte reads of a quarter wavefront (16 consecutive rows, one K block)
+// fall into 16 distinct groups of 4 banks.
+DEV int dw_pos(int r, int q) { return q ^ ((r >> 2) & 3); }
+
+template <int EPI, bool SPLIT>
+__global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
+                                                   EpiArgs ep, int M, int pair_mode, int NT, int nsplit,
+                                                   float *part) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[DW_LDS];
+
+    // block -> (feature tile, token tile, K split); the tiles of one feature
+    // tile share an XCD
+    const int mtiles = (M + 127) / 128;
+    const int per_nt = mtiles * nsplit;
+    const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
+    const int nt = (j / per_nt) * 8 + xcd, rem = j % per_nt;
+    const int mtile = rem % mtiles, split = rem / mtiles;
+    if (nt >= NT) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = nt * DW_N, m0 = mtile * 128, wn = 64 * w;
+    // equal splits of whole super-stages (checked by the launcher)
+    const int nb_all = W.K >> 5, nb = nb_all / nsplit, kb0 = split * nb, nsup = nb / DW_CK;
+
+    // ---- per-lane byte offsets of the direct loads ----
+    // activations: wavefront w loads part w >> 2 (value, remainder), slots
+    // 64 j .. 64 j + 63 for j = 2 (w & 3) + i; slot 4m + (c ^ swz(m)) holds
+    // chunk c of token m
+    uint32_t xo[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int slot = 64 * (2 * (w & 3) + i) + lane;
+        const int m = slot >> 2, c = (slot & 3) ^ swz(slot >> 2);
+        const int row = min(m0 + m, M - 1);            // rows past M repeat row M-1; their outputs are dropped
+        xo[i] = (uint32_t)(((size_t)row * ldx + c * 8) * 2);
+    }
+    // codes: instruction i of wavefront w covers rows 64 w + 16 i + lane / 4,
+    // one 16-byte K block each (4 lanes = 64 contiguous bytes of a row)
+    const size_t row_bytes = (size_t)(W.K >> 1);
+    uint32_t co[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int r = 64 * w + 16 * i + (lane >> 2);
+        const int q = dw_pos(r, lane & 3);             // the K block that lands at position lane & 3
+        co[i] = (uint32_t)((size_t)r * row_bytes + 16 * q);
+    }
+    const uint32_t so = (uint32_t)((64 * w + lane) * 2);
+    const uint8_t *xh_base = (const uint8_t *)Xh + (size_t)kb0 * 64;
+    const uint8_t *xl_base = (const uint8_t *)Xl + (size_t)kb0 * 64;
+    const uint8_t *xp_base = (w >> 2) ? xl_base : xh_base;
+    const uint8_t *c_base = (const uint8_t *)W.qs + (size_t)n0 * row_bytes + (size_t)kb0 * 16;
+    const size_t s_step = (size_t)W.N * 2;
+    const uint8_t *s_base = (const uint8_t *)W.dt + (size_t)kb0 * s_step + (size_t)n0 * 2;
+
+    // code stage of super-stage sup: the first for even, the second for odd
+    auto cstage = [&](int sup) -> uint8_t * { return lds + DW_OFF_C + (sup & 1) * DW_CST; };
+    // K block kb (clamped) -> activation stage sc: 2 loads + 1 scale load
+    auto issue_act = [&](auto sc, int kb) __attribute__((always_inline)) {
+        constexpr int v = decltype(sc)::value;
+        const size_t k = (size_t)min(kb, nb - 1);
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+            dma16s(xp_base + k * 64, xo[i],
+                   (const void AS3 *)(lds + v * DW_AST + (w >> 2) * DW_ACT + 1024 * (2 * (w & 3) + i)));
+        dma2s(s_base + k * s_step, so, (const void AS3 *)(lds + DW_OFF_S + v * DW_SST + 256 * w));
+    };
+    // super-stage sup (clamped) -> code stage: 4 loads
+    auto issue_codes = [&](int sup) __attribute__((always_inline)) {
+        uint8_t *cs = cstage(sup);
+        const size_t k = (size_t)min(sup, nsup - 1) * DW_CK;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            dma16s(c_base + k * 16, co[i], (const void AS3 *)(cs + (64 * w + 16 * i) * 64));
+    };
+
+    f16x acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[a][b][r] = 0.f;
+
+    // K block q of the code stage cs, activations of stage st, scales ss
+    auto compute = [&](const uint8_t *st, const uint8_t *ss, const uint8_t *cs, int q) __attribute__((always_inline)) {
+        h8 c0[2], c1[2];
+        float d[2];
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+            const int f = wn + 32 * a + (lane & 31);
+            const u32x4 v = *(const u32x4 *)(cs + f * 64 + 16 * dw_pos(f, q));
+            q4_pair((lane >> 5) ? u32x2{v.z, v.w} : u32x2{v.x, v.y}, c0[a], c1[a]);
+            d[a] = f16_bits_to_f32(*(const uint16_t *)(ss + 4 * f));
+            asm volatile("" : "+v"(d[a]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        h8 xh[2], xl[2];
+        auto read_x = [&](int b) __attribute__((always_inline)) {
+            const int m = 32 * b + (lane & 31);
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int slot = 4 * m + ((2 * h + (lane >> 5)) ^ swz(m));
+                xh[h] = *(const h8 *)(st + 16 * slot);
+                xl[h] = *(const h8 *)(st + DW_ACT + 16 * slot);
+            }
+        };
+        auto chain = [&](int a) __attribute__((always_inline)) {
+            f16x t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[0], c0[a], f16x{}, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[0], c0[a], t, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh[1], c1[a], t, 0, 0, 0);
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(xl[1], c1[a], t, 0, 0, 0);
+        };
+        // tiles i = 2 b + a, each tile's MFMAs against the previous tile's
+        // scaling FMAs (as in k_gemm_dl)
+        read_x(0);
+        f16x tp = chain(0);
+#pragma unroll
+        for (int i = 1; i < 8; i++) {
+            const int a = i & 1, b = i >> 1, pa = (i - 1) & 1, pb = (i - 1) >> 1;
+            if (a == 0) read_x(b);
+            const f16x tc = chain(a);
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[pa][pb][r] += d[pa] * tp[r];
+            tp = tc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[1][3][r] += d[1] * tp[r];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            if ((i & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+    };
+
+    // step kb (stage kb % 4, code stage of super-stage kb / 4): wait for its
+    // loads, barrier, refill the stage computed at kb - 1 with kb + 3 (and at
+    // the first K block of a super-stage, the other code stage with the next
+    // super-stage), compute
+    auto step = [&](auto pc, int kb, const uint8_t *cs) __attribute__((always_inline)) {
+        constexpr int p = decltype(pc)::value;     // kb % 4
+        if constexpr (p == 0) wait_vm_lgkm0<6>();
+        else wait_vm_lgkm0<10>();
+        block_barrier();
+        issue_act(std::integral_constant<int, (p + 3) % 4>{}, kb + 3);
+        if constexpr (p == 0) issue_codes(kb / DW_CK + 1);
+        compute(lds + p * DW_AST, lds + DW_OFF_S + p * DW_SST, cs, p);
+    };
+
+    issue_codes(0);
+    issue_act(std::integral_constant<int, 0>{}, 0);
+    issue_act(std::integral_constant<int, 1>{}, 1);
+    issue_act(std::integral_constant<int, 2>{}, 2);
+    // one super-stage per period; K blocks past the last are clamped
+    // re-reads whose stages are never computed
+    for (int kb = 0; kb < nb; kb += DW_CK) {
+        const uint8_t *cs = cstage(kb / DW_CK);
+        step(std::integral_constant<int, 0>{}, kb, cs);
+        step(std::integral_constant<int, 1>{}, kb + 1, cs);
+        step(std::integral_constant<int, 2>{}, kb + 2, cs);
+        step(std::integral_constant<int, 3>{}, kb + 3, cs);
+    }
+    // drain the requests past the last K block before the block can exit
+    wait_vm_lgkm0<0>();
+
+    // ---- epilogue: lane holds feature n0 + wn + 32a + (lane & 31) and, in
+    // accumulator r, token m0 + 32b + (r/4)*8 + (lane/32)*4 + r%4 ----
+    const int fl = lane & 31;
+    auto tok_of = [&](int b, int r) __attribute__((always_inline)) {
+        return m0 + 32 * b + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+    };
+    if (SPLIT) {
+        const int N = W.N;
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = tok_of(b, r);
+                if (m >= M) continue;
+                float *dst = part + ((size_t)split * M + m) * N + n0 + wn + fl;
+#pragma unroll
+                for (int a = 0; a < 2; a++) dst[32 * a] = acc[a][b][r];
+            }
+        return;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        if (EPI == EPI_STORE || EPI == EPI_RESID) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = tok_of(b, r);
+                if (m >= M) continue;
+                float *y = ep.y + (size_t)m * ep.ldy + n0 + wn + fl;
+#pragma unroll
+                for (int a = 0; a < 2; a++) {
+                    if (EPI == EPI_STORE) y[32 * a] = acc[a][b][r];
+                    else y[32 * a] += acc[a][b][r];
+                }
+            }
+        } else if (pair_mode == PAIR_GU) {
+            // gate rows 64g .. 64g+31 (tile 0) and their up rows 64g+32 .. (tile 1)
+            const int rr = n0 + wn + fl, g = rr >> 6;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = tok_of(b, r);
+                if (m < M) epi_pair<EPI>(ep, m, (g << 5) + (rr & 31), rr, rr + 32, acc[0][b][r], acc[1][b][r]);
+            }
+        } else {
+            // adjacent features f (even lane) and f+1 (odd lane): the even lane
+            // takes the first half of the pair's tokens, the odd lane the second
+            const bool odd = lane & 1;
+#pragma unroll
+            for (int a = 0; a < 2; a++)
+#pragma unroll
+                for (int r = 0; r < 8; r++) {
+                    const float send = odd ? acc[a][b][r] : acc[a][b][r + 8];
+                    const float recv = __shfl_xor(send, 1, 64);
+                    const int rr = odd ? r + 8 : r;
+                    const int m = tok_of(b, rr);
+                    const int f = n0 + wn + 32 * a + (fl & ~1);
+                    const float va = odd ? recv : acc[a][b][r];
+                    const float vb = odd ? acc[a][b][r + 8] : recv;
+                    if (m < M) epi_pair<EPI>(ep, m, f >> 1, f, f + 1, va, vb);
+                }
+        }
+    }
+}
+
+template <int EPI>
+void launch_dw_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                   int pair_mode, int S, float *ws, hipStream_t s) {
+    const int NT = W.N / DW_N, NT8 = (NT + 7) / 8 * 8;
+    const dim3 grid(NT8 * ((M + 127) / 128) * S);
+    if (S > 1) {
+        launch((k_gemm_dw<EPI, true>), grid, dim3(512), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, ws);
+        launch_splitk_sum(EPI, ws, S, W.N, M, ep, pair_mode, s);
+    } else {
+        launch((k_gemm_dw<EPI, false>), grid, dim3(512), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, 1,
+               (float *)nullptr);
+    }
+}
+
 }  // namespace
 
 int gemm_dl_tile_features() { return DBN; }
@@ -1037,6 +1322,19 @@ void launch_gemm_ws(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *X
     case EPI_RESID: launch_ws_epi<EPI_RESID>(ks, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
     case EPI_QKV: launch_ws_epi<EPI_QKV>(ks, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
     case EPI_SWIGLU: launch_ws_epi<EPI_SWIGLU>(ks, W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    }
+}
+
+int gemm_dw_tile_features() { return DW_N; }
+int gemm_dw_super_blocks() { return DW_CK; }
+
+void launch_gemm_dw(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                    int pair_mode, int S, float *ws, hipStream_t s) {
+    switch (ep.epi) {
+    case EPI_STORE: launch_dw_epi<EPI_STORE>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_RESID: launch_dw_epi<EPI_RESID>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_QKV: launch_dw_epi<EPI_QKV>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_SWIGLU: launch_dw_epi<EPI_SWIGLU>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
     }
 }
 

@@ -123,8 +123,10 @@ def test_direct_load_form_bitwise_equals_staged_tiles(dec, orc, wtype, monkeypat
     """Ubatches of more than 64 tokens on matrices of whole 256-feature tiles
     take the direct-to-LDS form (DECODE_GEMM_DL = 3 or 4 stages on 32x32
     tiles, 23 with 64-feature wavefront tiles, 13 on 16x16 tiles; 0 keeps the
-    register-staged tiles).  On
-    32x32 tiles both forms feed the matrix cores the same operands in the same
+    register-staged tiles); Q4_0 matrices of whole 512-feature tiles take the
+    wide form unless DECODE_GEMM_DW=0 (here the gate/up and QKV matrices,
+    whose K of 8 blocks is two code super-stages).  On
+    32x32 tiles all these forms feed the matrix cores the same operands in the same
     order and, at this shape, split K the same way (not at all), so every
     logits row of a 300-token ubatch (token tiles of 128, 128 and a ragged 44)
     is bitwise equal across them; the 16x16x32 MFMA sums a quant block in one
@@ -140,14 +142,19 @@ def test_direct_load_form_bitwise_equals_staged_tiles(dec, orc, wtype, monkeypat
             o_rows[i] = r
     gm = dec.Model(hp, w)
     got = {}
+    monkeypatch.setenv("DECODE_GEMM_DW", "0")
     for ns in ("0", "3", "4", "23", "13"):
         monkeypatch.setenv("DECODE_GEMM_DL", ns)
         got[ns] = _rows(dec, gm, prompt, 300)[0]
     monkeypatch.delenv("DECODE_GEMM_DL")
+    monkeypatch.delenv("DECODE_GEMM_DW")
+    wide = ("dw",) if wtype == synth.Q4_0 else ()
+    if wide:
+        got["dw"] = _rows(dec, gm, prompt, 300)[0]
     for i in ROWS:
-        for ns in ("3", "13"):
+        for ns in ("3", "13") + wide:
             assert_logits_close(got[ns][i], o_rows[i], f"direct-load {ns} row {i}")
-        for ns in ("3", "4", "23"):
+        for ns in ("3", "4", "23") + wide:
             assert np.array_equal(got[ns][i], got["0"][i]), f"variant {ns}, row {i}"
         for ns in ("13",):
             assert logit_err(got[ns][i], got["0"][i])[0] <= 1e-4, f"16x16 tiles ({ns}), row {i}"
