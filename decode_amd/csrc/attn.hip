@@ -240,75 +240,65 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
     }
 }
 
-// Merge of the chunk partials of one (head, token).  Every load is issued
-// at once -- the chunk statistics into LDS, each thread's partial rows
-// (4 elements of up to MPT chunks) into registers -- then
+// Merge of the chunk partials of one (head, token), 32 dims per block: one
+// wavefront, so every step is a lane exchange and nothing waits at a
+// barrier.  Lane l holds dims 4 (l % 8) .. +3 of chunks l / 8 + 8 i, and the
+// statistics of chunk l; all of them are requested at entry (rounds of 64
+// chunks past the first), then
 //   M = max_c m_c, w_c = e^(m_c - M), L = sum_c l_c w_c, o = sum_c acc_c w_c / L.
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
-    constexpr int TPR = HD / 4;          // threads per partial row
-    constexpr int CG = 256 / TPR;        // chunk groups
-    constexpr int MPT = 16;              // chunks per thread per round
-    __shared__ float2 mls[1024];
-    __shared__ float wgt[1024];
-    __shared__ float red[4];
-    __shared__ f4 sum4[CG][TPR];
-    const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+__global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
+    const int h = blockIdx.x, t = blockIdx.y, d0 = 32 * blockIdx.z, lane = threadIdx.x;
+    const int dq = lane & 7, cg = lane >> 3;
     const int nch = a.tok.pos[t] / a.chunk + 1;
     const size_t hh = (size_t)t * a.H + h;
     const float *ml = a.ml + hh * a.max_chunks * 2;
-    const float *pa = a.part + hh * a.max_chunks * HD;
-    const int dq = tid % TPR, cg = tid / TPR;
-    // first round of partial rows (clamped to the last chunk; weighted 0 past it)
-    f4 v[MPT];
+    const float *pa = a.part + hh * a.max_chunks * HD + d0 + 4 * dq;
+    // chunks past nch re-read the last one; their weights are 0
+    f4 v[8];
 #pragma unroll
-    for (int i = 0; i < MPT; i++) v[i] = *(const f4 *)(pa + (size_t)min(cg + CG * i, nch - 1) * HD + 4 * dq);
-    for (int cc = tid; cc < nch; cc += 256) mls[cc] = *(const float2 *)(ml + 2 * cc);
-    __syncthreads();
-    float mloc = -INFINITY;
-    for (int cc = tid; cc < nch; cc += 256) mloc = fmaxf(mloc, mls[cc].x);
+    for (int i = 0; i < 8; i++) v[i] = *(const f4 *)(pa + (size_t)min(cg + 8 * i, nch - 1) * HD);
+    const float2 s0 = *(const float2 *)(ml + 2 * min(lane, nch - 1));
+    float mloc = lane < nch ? s0.x : -INFINITY;
+    for (int c = lane + 64; c < nch; c += 64) mloc = fmaxf(mloc, ml[2 * c]);
     mloc = row16_max(mloc);
-    mloc = fmaxf(fmaxf(readlane_f(mloc, 0), readlane_f(mloc, 16)), fmaxf(readlane_f(mloc, 32), readlane_f(mloc, 48)));
-    if (lane == 0) red[w] = mloc;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    float lsum = 0.f;
-    for (int cc = tid; cc < nch; cc += 256) {
-        const float f = mls[cc].x == -INFINITY ? 0.f : __expf(mls[cc].x - M);
-        wgt[cc] = f;
-        lsum += mls[cc].y * f;
+    const float M = fmaxf(fmaxf(readlane_f(mloc, 0), readlane_f(mloc, 16)), fmaxf(readlane_f(mloc, 32), readlane_f(mloc, 48)));
+    float wl = lane < nch && s0.x != -INFINITY ? __expf(s0.x - M) : 0.f;
+    float lloc = lane < nch ? s0.y * wl : 0.f;
+    for (int c = lane + 64; c < nch; c += 64) {
+        const float2 sc = *(const float2 *)(ml + 2 * c);
+        lloc += sc.x == -INFINITY ? 0.f : sc.y * __expf(sc.x - M);
     }
-    lsum = wave_sum_dpp(lsum);
-    if (lane == 0) red[w] = lsum;
-    __syncthreads();
-    const float L = (red[0] + red[1]) + (red[2] + red[3]);
+    const float L = wave_sum_dpp(lloc);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0;;) {
 #pragma unroll
-    for (int i = 0; i < MPT; i++)
-        if (cg + CG * i < nch) acc += v[i] * wgt[cg + CG * i];
-    for (int c0 = CG * MPT; c0 < nch; c0 += CG * MPT) {      // contexts past CG*MPT chunks
+        for (int i = 0; i < 8; i++) {
+            const float wc = __shfl(wl, cg + 8 * i, 64);
+            if (c0 + cg + 8 * i < nch) acc += v[i] * wc;
+        }
+        c0 += 64;
+        if (c0 >= nch) break;
 #pragma unroll
-        for (int i = 0; i < MPT; i++) v[i] = *(const f4 *)(pa + (size_t)min(c0 + cg + CG * i, nch - 1) * HD + 4 * dq);
-#pragma unroll
-        for (int i = 0; i < MPT; i++)
-            if (c0 + cg + CG * i < nch) acc += v[i] * wgt[c0 + cg + CG * i];
+        for (int i = 0; i < 8; i++) v[i] = *(const f4 *)(pa + (size_t)min(c0 + cg + 8 * i, nch - 1) * HD);
+        const float2 sc = *(const float2 *)(ml + 2 * min(c0 + lane, nch - 1));
+        wl = c0 + lane < nch && sc.x != -INFINITY ? __expf(sc.x - M) : 0.f;
     }
-    sum4[cg][dq] = acc;
-    __syncthreads();
-    if (cg == 0) {
-        f4 s4 = sum4[0][dq];
+    // sum over the 8 chunk groups (lane bits 3..5)
 #pragma unroll
-        for (int k = 1; k < CG; k++) s4 += sum4[k][dq];
+    for (int o = 8; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; e++) acc[e] += __shfl_xor(acc[e], o, 64);
+    if (cg == 0) {
         h2 o[2], ol[2];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const float ov = s4[e] / L;
+            const float ov = acc[e] / L;
             const f16 oh = (f16)ov;
             o[e >> 1][e & 1] = oh;
             ol[e >> 1][e & 1] = (f16)(ov - (float)oh);
         }
-        const size_t off = (size_t)t * a.H * HD + (size_t)h * HD + 4 * dq;
+        const size_t off = (size_t)t * a.H * HD + (size_t)h * HD + d0 + 4 * dq;
         *(uint2 *)((f16 *)a.o + off) = make_uint2(h2_bits(o[0]), h2_bits(o[1]));
         if (a.o_lo) *(uint2 *)((f16 *)a.o_lo + off) = make_uint2(h2_bits(ol[0]), h2_bits(ol[1]));
     }
@@ -721,7 +711,7 @@ bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
                                      : launch_part<HD, T_F32>(a, T, s);
     }
     if (!ok) return false;
-    launch((k_attn_merge<HD>), dim3(a.H, T), dim3(256), 0, s, a);
+    launch((k_attn_merge<HD>), dim3(a.H, T, HD / 32), dim3(64), 0, s, a);
     return true;
 }
 

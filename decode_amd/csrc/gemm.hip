@@ -951,12 +951,13 @@ bool dl_shape(const QMat &W, int M, int ldx) {
            (size_t)M * (W.K / 32) * 4 < ((size_t)1 << 31);
 }
 
-// The wide form (Q4_0): more than 64 tokens, whole 512-feature tiles, K in
-// whole code super-stages.
+// The wide form (Q4_0, Q8_0): more than 64 tokens, whole 512-feature tiles,
+// K in whole periods of code super-stages.
 bool dw_shape(const QMat &W, int M, int ldx) {
-    return g_gemm_dw && g_gemm_dl > 0 && !g_gemm_f16w && W.wtype == T_Q4_0 && W.dt && M > 64 &&
-           W.N % gemm_dw_tile_features() == 0 && (W.K / 32) % gemm_dw_super_blocks() == 0 &&
-           (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * (W.K / 2) < ((size_t)1 << 31);
+    const size_t row_bytes = W.wtype == T_Q8_0 ? (size_t)W.K : (size_t)W.K / 2;
+    return g_gemm_dw && g_gemm_dl > 0 && !g_gemm_f16w && (W.wtype == T_Q4_0 || W.wtype == T_Q8_0) && W.dt &&
+           M > 64 && W.N % gemm_dw_tile_features() == 0 && (W.K / 32) % gemm_dw_super_blocks() == 0 &&
+           (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * row_bytes < ((size_t)1 << 31);
 }
 
 // Its K split: the largest of 1, 2, 4, 8 whose grid fits one block per
@@ -1063,7 +1064,7 @@ void gemm_set_num_cu(int n) {
     // DECODE_GEMM_WS: K blocks per stage of the weight-streaming form (2 or 4,
     // default 2); 0 leaves Q4_0 ubatches of at most 32 tokens to the 32-token
     // direct-to-LDS form
-    // DECODE_GEMM_DW=0: Q4_0 ubatches of more than 64 tokens take the
+    // DECODE_GEMM_DW=0: Q4_0 / Q8_0 ubatches of more than 64 tokens take the
     // 256-feature direct-to-LDS form instead of the wide one
     const char *dwv = getenv("DECODE_GEMM_DW");
     g_gemm_dw = !(dwv && strcmp(dwv, "0") == 0);

@@ -1024,7 +1024,7 @@ void launch_ws_epi(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *Xl
 }
 
 
-// ---- wide form: Q4_0, 512 features x 128 tokens per block -------------------
+// ---- wide form: Q4_0 / Q8_0, 512 features x 128 tokens per block ----------
 //
 // The arithmetic and operand layouts of k_gemm_dl (exact codes, activation
 // value and remainder, per-block fp32 scaling, 64-feature wavefront tiles over
@@ -1034,9 +1034,9 @@ void launch_ws_epi(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *Xl
 // 16-byte code requests, 256 64-byte activation requests; codes alone took
 // 102 us of a 512-token gate/up GEMM, and 46 us when each request covered 4
 // K blocks of a row).  Here:
-// * codes come in super-stages of DW_CK = 4 K blocks: 64 contiguous bytes per
-//   row and request, double-buffered (super-stage s+1 is requested at the
-//   first K block of s);
+// * codes come in super-stages of 64 contiguous bytes per row and request
+//   (4 K blocks of Q4_0, 2 of Q8_0), double-buffered (super-stage s+1 is
+//   requested at the first K block of s);
 // * a block covers 512 features (8 wavefronts), so each activation request
 //   feeds twice the features;
 // * activations and scales (from the transposed dt) go through a ring of
@@ -1044,29 +1044,38 @@ void launch_ws_epi(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *Xl
 // LDS (one array, 136 KB, one block of 8 wavefronts per compute unit, two
 // per SIMD): the 4 activation stages fill the first 64 KB, so every
 // activation read is a fixed register plus an immediate offset; then the
-// stages' scales and the two code stages.  A wavefront requests 3 loads per K block (2
-// activation, 1 scale) and 4 code loads every 4th; loads complete in issue
-// order, so the wait before K block kb is a constant per kb % 4: 6 loads
-// issued after its activation stage when kb % 4 == 0, else 10 (the code
-// loads of the super-stage issued in between).  The K range of a split is a
-// whole number of super-stages.
+// stages' scales and the two code stages.  A wavefront requests 3 loads per
+// K block (2 activation, 1 scale) and, at the first K block of a super-stage,
+// 4 code loads (Q4_0 after the activation loads; Q8_0 before them, since its
+// codes are needed two K blocks later); loads complete in issue order, so the
+// wait before K block kb is a constant per kb within its super-stage
+// (dw_wait: the loads issued after the later of its activation stage and
+// its codes).  The K range of a split is whole periods of 4 K blocks.
 constexpr int DW_N = 512;                       // features per block
 constexpr int DW_A = 4;                         // activation stages
-constexpr int DW_CK = 4;                        // K blocks per code super-stage
 constexpr int DW_ACT = 128 * 64;                // one activation part of a K block
 constexpr int DW_AST = 2 * DW_ACT;              // activation stage: values, remainders
 constexpr int DW_SST = DW_N * 4;                // scales of a K block, one dword per row
-constexpr int DW_CST = DW_N * 16 * DW_CK;       // codes of a super-stage: [512 rows][4 x 16 B]
+constexpr int DW_CST = DW_N * 64;               // codes of a super-stage: [512 rows][64 B]
 constexpr int DW_OFF_S = DW_A * DW_AST;         // (= 64 KB)
 constexpr int DW_OFF_C = DW_OFF_S + DW_A * DW_SST;
 constexpr int DW_LDS = DW_OFF_C + 2 * DW_CST;
 
-// Position of K block q (0..3) of a super-stage in row r: XOR-swizzled so that
-// the 16-byte reads of a quarter wavefront (16 consecutive rows, one K block)
-// fall into 16 distinct groups of 4 banks.
+// K blocks per super-stage.
+template <int WT>
+constexpr int dw_ck() { return WT == T_Q8_0 ? 2 : 4; }
+// Loads a wavefront issued after those that K block kb needs, for kb at
+// position p of its super-stage: Q4_0 [6, 10, 10, 10], Q8_0 [6, 10].
+template <int WT>
+constexpr int dw_wait(int p) { return p == 0 ? 6 : 10; }
+
+// Position of 16-byte piece q (0..3: Q4_0 K block q, Q8_0 half q % 2 of K
+// block q / 2) of a super-stage in row r: XOR-swizzled so that the 16-byte
+// reads of a quarter wavefront (16 consecutive rows, one piece) fall into 16
+// distinct groups of 4 banks.
 DEV int dw_pos(int r, int q) { return q ^ ((r >> 2) & 3); }
 
-template <int EPI, bool SPLIT>
+template <int WT, int EPI, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
                                                    EpiArgs ep, int M, int pair_mode, int NT, int nsplit,
                                                    float *part) {
@@ -1084,7 +1093,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n0 = nt * DW_N, m0 = mtile * 128, wn = 64 * w;
     // equal splits of whole super-stages (checked by the launcher)
-    const int nb_all = W.K >> 5, nb = nb_all / nsplit, kb0 = split * nb, nsup = nb / DW_CK;
+    constexpr int CK = dw_ck<WT>();
+    const int nb_all = W.K >> 5, nb = nb_all / nsplit, kb0 = split * nb, nsup = nb / CK;
 
     // ---- per-lane byte offsets of the direct loads ----
     // activations: wavefront w loads part w >> 2 (value, remainder), slots
@@ -1099,20 +1109,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
         xo[i] = (uint32_t)(((size_t)row * ldx + c * 8) * 2);
     }
     // codes: instruction i of wavefront w covers rows 64 w + 16 i + lane / 4,
-    // one 16-byte K block each (4 lanes = 64 contiguous bytes of a row)
-    const size_t row_bytes = (size_t)(W.K >> 1);
+    // one 16-byte piece each (4 lanes = a super-stage's 64 contiguous bytes of
+    // a row)
+    const size_t row_bytes = WT == T_Q8_0 ? (size_t)W.K : (size_t)(W.K >> 1);
     uint32_t co[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int r = 64 * w + 16 * i + (lane >> 2);
-        const int q = dw_pos(r, lane & 3);             // the K block that lands at position lane & 3
+        const int q = dw_pos(r, lane & 3);             // the piece that lands at position lane & 3
         co[i] = (uint32_t)((size_t)r * row_bytes + 16 * q);
     }
     const uint32_t so = (uint32_t)((64 * w + lane) * 2);
     const uint8_t *xh_base = (const uint8_t *)Xh + (size_t)kb0 * 64;
     const uint8_t *xl_base = (const uint8_t *)Xl + (size_t)kb0 * 64;
     const uint8_t *xp_base = (w >> 2) ? xl_base : xh_base;
-    const uint8_t *c_base = (const uint8_t *)W.qs + (size_t)n0 * row_bytes + (size_t)kb0 * 16;
+    const uint8_t *c_base = (const uint8_t *)W.qs + (size_t)n0 * row_bytes + (size_t)kb0 * (64 / CK);
     const size_t s_step = (size_t)W.N * 2;
     const uint8_t *s_base = (const uint8_t *)W.dt + (size_t)kb0 * s_step + (size_t)n0 * 2;
 
@@ -1131,10 +1142,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
     // super-stage sup (clamped) -> code stage: 4 loads
     auto issue_codes = [&](int sup) __attribute__((always_inline)) {
         uint8_t *cs = cstage(sup);
-        const size_t k = (size_t)min(sup, nsup - 1) * DW_CK;
+        const size_t k = (size_t)min(sup, nsup - 1);
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            dma16s(c_base + k * 16, co[i], (const void AS3 *)(cs + (64 * w + 16 * i) * 64));
+            dma16s(c_base + k * 64, co[i], (const void AS3 *)(cs + (64 * w + 16 * i) * 64));
     };
 
     f16x acc[2][4];
@@ -1152,8 +1163,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
 #pragma unroll
         for (int a = 0; a < 2; a++) {
             const int f = wn + 32 * a + (lane & 31);
-            const u32x4 v = *(const u32x4 *)(cs + f * 64 + 16 * dw_pos(f, q));
-            q4_pair((lane >> 5) ? u32x2{v.z, v.w} : u32x2{v.x, v.y}, c0[a], c1[a]);
+            const bool hi8 = lane >> 5;      // this lane's 8 bytes of a 16-byte piece
+            if constexpr (WT == T_Q8_0) {
+                const u32x4 v0 = *(const u32x4 *)(cs + f * 64 + 16 * dw_pos(f, 2 * q));
+                const u32x4 v1 = *(const u32x4 *)(cs + f * 64 + 16 * dw_pos(f, 2 * q + 1));
+                c0[a] = q8_eight(hi8 ? u32x2{v0.z, v0.w} : u32x2{v0.x, v0.y});
+                c1[a] = q8_eight(hi8 ? u32x2{v1.z, v1.w} : u32x2{v1.x, v1.y});
+            } else {
+                const u32x4 v = *(const u32x4 *)(cs + f * 64 + 16 * dw_pos(f, q));
+                q4_pair(hi8 ? u32x2{v.z, v.w} : u32x2{v.x, v.y}, c0[a], c1[a]);
+            }
             d[a] = f16_bits_to_f32(*(const uint16_t *)(ss + 4 * f));
             asm volatile("" : "+v"(d[a]));
         }
@@ -1201,32 +1220,33 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
         __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
     };
 
-    // step kb (stage kb % 4, code stage of super-stage kb / 4): wait for its
-    // loads, barrier, refill the stage computed at kb - 1 with kb + 3 (and at
-    // the first K block of a super-stage, the other code stage with the next
-    // super-stage), compute
+    // step kb (activation stage kb % 4, position p = kb % CK of super-stage
+    // kb / CK): wait for its loads, barrier, at p = 0 request the next
+    // super-stage into the other code stage, refill the activation stage
+    // computed at kb - 1 with kb + 3, compute
     auto step = [&](auto pc, int kb, const uint8_t *cs) __attribute__((always_inline)) {
-        constexpr int p = decltype(pc)::value;     // kb % 4
-        if constexpr (p == 0) wait_vm_lgkm0<6>();
-        else wait_vm_lgkm0<10>();
+        constexpr int j = decltype(pc)::value;     // kb % 4
+        constexpr int p = j % CK;
+        wait_vm_lgkm0<dw_wait<WT>(p)>();
         block_barrier();
-        issue_act(std::integral_constant<int, (p + 3) % 4>{}, kb + 3);
-        if constexpr (p == 0) issue_codes(kb / DW_CK + 1);
-        compute(lds + p * DW_AST, lds + DW_OFF_S + p * DW_SST, cs, p);
+        if constexpr (p == 0 && WT == T_Q8_0) issue_codes(kb / CK + 1);
+        issue_act(std::integral_constant<int, (j + 3) % 4>{}, kb + 3);
+        if constexpr (p == 0 && WT != T_Q8_0) issue_codes(kb / CK + 1);
+        compute(lds + j * DW_AST, lds + DW_OFF_S + j * DW_SST, cs, p);
     };
 
     issue_codes(0);
     issue_act(std::integral_constant<int, 0>{}, 0);
     issue_act(std::integral_constant<int, 1>{}, 1);
     issue_act(std::integral_constant<int, 2>{}, 2);
-    // one super-stage per period; K blocks past the last are clamped
-    // re-reads whose stages are never computed
-    for (int kb = 0; kb < nb; kb += DW_CK) {
-        const uint8_t *cs = cstage(kb / DW_CK);
-        step(std::integral_constant<int, 0>{}, kb, cs);
-        step(std::integral_constant<int, 1>{}, kb + 1, cs);
-        step(std::integral_constant<int, 2>{}, kb + 2, cs);
-        step(std::integral_constant<int, 3>{}, kb + 3, cs);
+    // periods of four K blocks (one Q4_0 super-stage, two Q8_0 ones; a split
+    // is whole periods); K blocks past the last are clamped re-reads whose
+    // stages are never computed
+    for (int kb = 0; kb < nb; kb += 4) {
+        step(std::integral_constant<int, 0>{}, kb, cstage(kb / CK));
+        step(std::integral_constant<int, 1>{}, kb + 1, cstage(kb / CK));
+        step(std::integral_constant<int, 2>{}, kb + 2, cstage((kb + 2) / CK));
+        step(std::integral_constant<int, 3>{}, kb + 3, cstage((kb + 2) / CK));
     }
     // drain the requests past the last K block before the block can exit
     wait_vm_lgkm0<0>();
@@ -1294,17 +1314,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
     }
 }
 
-template <int EPI>
+template <int WT, int EPI>
 void launch_dw_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
                    int pair_mode, int S, float *ws, hipStream_t s) {
     const int NT = W.N / DW_N, NT8 = (NT + 7) / 8 * 8;
     const dim3 grid(NT8 * ((M + 127) / 128) * S);
     if (S > 1) {
-        launch((k_gemm_dw<EPI, true>), grid, dim3(512), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, ws);
+        launch((k_gemm_dw<WT, EPI, true>), grid, dim3(512), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, ws);
         launch_splitk_sum(EPI, ws, S, W.N, M, ep, pair_mode, s);
     } else {
-        launch((k_gemm_dw<EPI, false>), grid, dim3(512), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, 1,
+        launch((k_gemm_dw<WT, EPI, false>), grid, dim3(512), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, 1,
                (float *)nullptr);
+    }
+}
+
+template <int WT>
+void launch_dw_wt(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
+                  int pair_mode, int S, float *ws, hipStream_t s) {
+    switch (ep.epi) {
+    case EPI_STORE: launch_dw_epi<WT, EPI_STORE>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_RESID: launch_dw_epi<WT, EPI_RESID>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_QKV: launch_dw_epi<WT, EPI_QKV>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_SWIGLU: launch_dw_epi<WT, EPI_SWIGLU>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
     }
 }
 
@@ -1326,16 +1357,16 @@ void launch_gemm_ws(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *X
 }
 
 int gemm_dw_tile_features() { return DW_N; }
-int gemm_dw_super_blocks() { return DW_CK; }
+// A K split must give every split whole periods of 4 K blocks (whole
+// super-stages of either type).
+int gemm_dw_super_blocks() { return 4; }
 
 void launch_gemm_dw(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
                     int pair_mode, int S, float *ws, hipStream_t s) {
-    switch (ep.epi) {
-    case EPI_STORE: launch_dw_epi<EPI_STORE>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
-    case EPI_RESID: launch_dw_epi<EPI_RESID>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
-    case EPI_QKV: launch_dw_epi<EPI_QKV>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
-    case EPI_SWIGLU: launch_dw_epi<EPI_SWIGLU>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
-    }
+    if (W.wtype == T_Q8_0)
+        launch_dw_wt<T_Q8_0>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+    else
+        launch_dw_wt<T_Q4_0>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
 }
 
 void launch_gemm_dls(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,

@@ -180,10 +180,10 @@ void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, i
 // Derives the GEMM's scale arrays once every row of m is stored: Q4_0/Q8_0
 // m.dt from m.d; Q4_K m.mfq and m.sf from m.d and m.dm.
 void launch_gemm_scales(QMat &m, hipStream_t s);
-// The wide direct-to-LDS form (Q4_0, ubatches of more than 64 tokens):
-// gemm_dw_tile_features() x 128 block tiles, codes loaded
-// gemm_dw_super_blocks() K blocks at a time; K split S into equal ranges of
-// whole super-stages.
+// The wide direct-to-LDS form (Q4_0 / Q8_0, ubatches of more than 64
+// tokens): gemm_dw_tile_features() x 128 block tiles, codes loaded 64 bytes
+// of a row at a time; K split S into equal ranges of whole periods of
+// gemm_dw_super_blocks() K blocks.
 void launch_gemm_dw(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
                     int pair_mode, int S, float *ws, hipStream_t s);
 int gemm_dw_tile_features();

@@ -123,9 +123,9 @@ def test_direct_load_form_bitwise_equals_staged_tiles(dec, orc, wtype, monkeypat
     """Ubatches of more than 64 tokens on matrices of whole 256-feature tiles
     take the direct-to-LDS form (DECODE_GEMM_DL = 3 or 4 stages on 32x32
     tiles, 23 with 64-feature wavefront tiles, 13 on 16x16 tiles; 0 keeps the
-    register-staged tiles); Q4_0 matrices of whole 512-feature tiles take the
-    wide form unless DECODE_GEMM_DW=0 (here the gate/up and QKV matrices,
-    whose K of 8 blocks is two code super-stages).  On
+    register-staged tiles); Q4_0 and Q8_0 matrices of whole 512-feature tiles
+    take the wide form unless DECODE_GEMM_DW=0 (here the gate/up and QKV
+    matrices, whose K of 8 blocks is two periods of code super-stages).  On
     32x32 tiles all these forms feed the matrix cores the same operands in the same
     order and, at this shape, split K the same way (not at all), so every
     logits row of a 300-token ubatch (token tiles of 128, 128 and a ragged 44)
@@ -148,9 +148,8 @@ def test_direct_load_form_bitwise_equals_staged_tiles(dec, orc, wtype, monkeypat
         got[ns] = _rows(dec, gm, prompt, 300)[0]
     monkeypatch.delenv("DECODE_GEMM_DL")
     monkeypatch.delenv("DECODE_GEMM_DW")
-    wide = ("dw",) if wtype == synth.Q4_0 else ()
-    if wide:
-        got["dw"] = _rows(dec, gm, prompt, 300)[0]
+    wide = ("dw",)
+    got["dw"] = _rows(dec, gm, prompt, 300)[0]
     for i in ROWS:
         for ns in ("3", "13") + wide:
             assert_logits_close(got[ns][i], o_rows[i], f"direct-load {ns} row {i}")
