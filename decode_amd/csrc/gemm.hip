@@ -951,12 +951,13 @@ bool dl_shape(const QMat &W, int M, int ldx) {
            (size_t)M * (W.K / 32) * 4 < ((size_t)1 << 31);
 }
 
-// The wide form (Q4_0, Q8_0): more than 64 tokens, whole 512-feature tiles,
-// K in whole periods of code super-stages.
+// The wide form (Q4_0, Q8_0, Q4_K): more than 64 tokens, whole 512-feature
+// tiles, K in whole periods of code super-stages.
 bool dw_shape(const QMat &W, int M, int ldx) {
     const size_t row_bytes = W.wtype == T_Q8_0 ? (size_t)W.K : (size_t)W.K / 2;
-    return g_gemm_dw && g_gemm_dl > 0 && !g_gemm_f16w && (W.wtype == T_Q4_0 || W.wtype == T_Q8_0) && W.dt &&
-           M > 64 && W.N % gemm_dw_tile_features() == 0 && (W.K / 32) % gemm_dw_super_blocks() == 0 &&
+    return g_gemm_dw && g_gemm_dl > 0 && !g_gemm_f16w &&
+           (W.wtype == T_Q4_0 || W.wtype == T_Q8_0 || W.wtype == T_Q4_K) && has_gemm_scales(W) && M > 64 &&
+           W.N % gemm_dw_tile_features() == 0 && (W.K / 32) % gemm_dw_super_blocks() == 0 &&
            (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * row_bytes < ((size_t)1 << 31);
 }
 
@@ -967,8 +968,9 @@ int dw_split(const QMat &W, int M) {
     const long tiles = (long)(W.N / gemm_dw_tile_features()) * ((M + 127) / 128);
     const int nb = W.K / 32;
     int best = 1;
+    const int unit = W.wtype == T_Q4_K ? 8 : gemm_dw_super_blocks();   // Q4_K: whole octets
     for (int S = 2; S <= 8; S *= 2)
-        if (tiles * S <= g_gemm_cu && nb % (S * gemm_dw_super_blocks()) == 0 && nb / S >= 16) best = S;
+        if (tiles * S <= g_gemm_cu && nb % (S * unit) == 0 && nb / S >= 16) best = S;
     return best;
 }
 
@@ -1116,7 +1118,12 @@ size_t gemm_workspace_bytes(const QMat &W, int M) {
     if (M > 0 && W.wtype == T_Q4_K) {
         if (!dl_shape(W, M, W.K)) return 0;
         const int Sd = dl_split(W, M);
-        return q4k_sums_bytes(W, M) + std::max(small, Sd > 1 ? (size_t)Sd * M * W.N * 4 : (size_t)0);
+        size_t tile = Sd > 1 ? (size_t)Sd * M * W.N * 4 : (size_t)0;
+        if (dw_shape(W, M, W.K)) {
+            const int Sw = dw_split(W, M);
+            tile = std::max(tile, Sw > 1 ? (size_t)Sw * M * W.N * 4 : (size_t)0);
+        }
+        return q4k_sums_bytes(W, M) + std::max(small, tile);
     }
     if (M <= 0 || !mfma_shape(W, 8)) return 0;
     const int S = split_for(W, M);
@@ -1143,12 +1150,14 @@ bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
         const size_t xsb = q4k_sums_bytes(W, M);
         if (ldx % 8 == 0 && dl_shape(W, M, ldx) && ws && ws_bytes >= xsb) {
             float *part = ws + xsb / 4;
-            const bool small = dls_shape(W, M, ldx);
-            int S = small ? dls_split(W, M) : dl_split(W, M);
+            const bool small = dls_shape(W, M, ldx), wide = !small && dw_shape(W, M, ldx);
+            int S = small ? dls_split(W, M) : wide ? dw_split(W, M) : dl_split(W, M);
             while (S > 1 && (size_t)S * M * W.N * 4 > ws_bytes - xsb) S >>= 1;
             launch_block_sums(Xh, Xl, ldx, M, W.K, ws, s);
             if (small)
                 launch_gemm_dls(g_gemm_dls_ns, W, Xh, Xl, ldx, ep, M, pair_mode, S, part, ws, s);
+            else if (wide)
+                launch_gemm_dw(W, Xh, Xl, ldx, ep, M, pair_mode, S, part, ws, s);
             else
                 launch_gemm_dl(23, W, Xh, Xl, ldx, ep, M, pair_mode, S, part, ws, s);
             return true;
@@ -1195,7 +1204,7 @@ bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
     if (mfma_shape(W, ldx) && dw_shape(W, M, ldx)) {
         int S = dw_split(W, M);
         while (S > 1 && (!ws || (size_t)S * M * W.N * 4 > ws_bytes)) S >>= 1;
-        launch_gemm_dw(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+        launch_gemm_dw(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, nullptr, s);
         return true;
     }
     if (mfma_shape(W, ldx) && dl_shape(W, M, ldx)) {

@@ -1024,7 +1024,7 @@ void launch_ws_epi(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *Xl
 }
 
 
-// ---- wide form: Q4_0 / Q8_0, 512 features x 128 tokens per block ----------
+// ---- wide form: Q4_0 / Q8_0 / Q4_K, 512 features x 128 tokens per block ----
 //
 // The arithmetic and operand layouts of k_gemm_dl (exact codes, activation
 // value and remainder, per-block fp32 scaling, 64-feature wavefront tiles over
@@ -1050,7 +1050,11 @@ void launch_ws_epi(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *Xl
 // codes are needed two K blocks later); loads complete in issue order, so the
 // wait before K block kb is a constant per kb within its super-stage
 // (dw_wait: the loads issued after the later of its activation stage and
-// its codes).  The K range of a split is whole periods of 4 K blocks.
+// its codes).  The K range of a split is whole periods of 4 K blocks (Q4_K:
+// whole octets).  Q4_K: codes as Q4_0 (exact values 0..15), the fp32 scale
+// d sc from the transposed sf, and after the main loop the min term as in
+// k_gemm_dl, with the chunks of mins and block sums staged in the code
+// stages.
 constexpr int DW_N = 512;                       // features per block
 constexpr int DW_A = 4;                         // activation stages
 constexpr int DW_ACT = 128 * 64;                // one activation part of a K block
@@ -1078,7 +1082,8 @@ DEV int dw_pos(int r, int q) { return q ^ ((r >> 2) & 3); }
 template <int WT, int EPI, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
                                                    EpiArgs ep, int M, int pair_mode, int NT, int nsplit,
-                                                   float *part) {
+                                                   float *part, const float *xs) {
+    constexpr bool K4 = WT == T_Q4_K;
     __shared__ __attribute__((aligned(16))) uint8_t lds[DW_LDS];
 
     // block -> (feature tile, token tile, K split); the tiles of one feature
@@ -1119,13 +1124,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
         const int q = dw_pos(r, lane & 3);             // the piece that lands at position lane & 3
         co[i] = (uint32_t)((size_t)r * row_bytes + 16 * q);
     }
-    const uint32_t so = (uint32_t)((64 * w + lane) * 2);
+    // scales: f16 dt, or Q4_K fp32 sf, both [K/32][N]
+    constexpr int SB = K4 ? 4 : 2;
+    const uint32_t so = (uint32_t)((64 * w + lane) * SB);
     const uint8_t *xh_base = (const uint8_t *)Xh + (size_t)kb0 * 64;
     const uint8_t *xl_base = (const uint8_t *)Xl + (size_t)kb0 * 64;
     const uint8_t *xp_base = (w >> 2) ? xl_base : xh_base;
     const uint8_t *c_base = (const uint8_t *)W.qs + (size_t)n0 * row_bytes + (size_t)kb0 * (64 / CK);
-    const size_t s_step = (size_t)W.N * 2;
-    const uint8_t *s_base = (const uint8_t *)W.dt + (size_t)kb0 * s_step + (size_t)n0 * 2;
+    const size_t s_step = (size_t)W.N * SB;
+    const uint8_t *s_base =
+        (K4 ? (const uint8_t *)W.sf : (const uint8_t *)W.dt) + (size_t)kb0 * s_step + (size_t)n0 * SB;
 
     // code stage of super-stage sup: the first for even, the second for odd
     auto cstage = [&](int sup) -> uint8_t * { return lds + DW_OFF_C + (sup & 1) * DW_CST; };
@@ -1137,7 +1145,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
         for (int i = 0; i < 2; i++)
             dma16s(xp_base + k * 64, xo[i],
                    (const void AS3 *)(lds + v * DW_AST + (w >> 2) * DW_ACT + 1024 * (2 * (w & 3) + i)));
-        dma2s(s_base + k * s_step, so, (const void AS3 *)(lds + DW_OFF_S + v * DW_SST + 256 * w));
+        if constexpr (K4)
+            dma4s(s_base + k * s_step, so, (const void AS3 *)(lds + DW_OFF_S + v * DW_SST + 256 * w));
+        else
+            dma2s(s_base + k * s_step, so, (const void AS3 *)(lds + DW_OFF_S + v * DW_SST + 256 * w));
     };
     // super-stage sup (clamped) -> code stage: 4 loads
     auto issue_codes = [&](int sup) __attribute__((always_inline)) {
@@ -1171,9 +1182,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
                 c1[a] = q8_eight(hi8 ? u32x2{v1.z, v1.w} : u32x2{v1.x, v1.y});
             } else {
                 const u32x4 v = *(const u32x4 *)(cs + f * 64 + 16 * dw_pos(f, q));
-                q4_pair(hi8 ? u32x2{v.z, v.w} : u32x2{v.x, v.y}, c0[a], c1[a]);
+                if constexpr (K4) q4k_pair(hi8 ? u32x2{v.z, v.w} : u32x2{v.x, v.y}, c0[a], c1[a]);
+                else q4_pair(hi8 ? u32x2{v.z, v.w} : u32x2{v.x, v.y}, c0[a], c1[a]);
             }
-            d[a] = f16_bits_to_f32(*(const uint16_t *)(ss + 4 * f));
+            if constexpr (K4) d[a] = *(const float *)(ss + 4 * f);
+            else d[a] = f16_bits_to_f32(*(const uint16_t *)(ss + 4 * f));
             asm volatile("" : "+v"(d[a]));
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1251,6 +1264,65 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
     // drain the requests past the last K block before the block can exit
     wait_vm_lgkm0<0>();
 
+    // Q4_K min term: acc += X (-M)^T over the split's K blocks (see k_gemm_dl),
+    // 16 K blocks per chunk: the chunk's mins (2 octets x 512 rows x 32 B)
+    // and block sums (2 octets x 128 tokens x 32 B) go by direct loads into
+    // the code stages, then each lane reads its row's and token's 32 bytes
+    if constexpr (K4) {
+        const uint32_t *xq = (const uint32_t *)xs;
+        const int kend = kb0 + nb, oend = kend >> 3, hf = lane >> 5;
+        uint8_t *mins = lds + DW_OFF_C, *sums = lds + DW_OFF_C + 32768;
+        auto unpack = [](const u32x4 &p0, const u32x4 &p1, h8 &hi, h8 &lo) __attribute__((always_inline)) {
+            const uint32_t v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                hi[e] = __builtin_bit_cast(f16, (uint16_t)v[e]);
+                lo[e] = __builtin_bit_cast(f16, (uint16_t)(v[e] >> 16));
+            }
+        };
+        block_barrier();                               // every wavefront is done with the code stages
+        for (int k16 = kb0; k16 < kend; k16 += 16) {
+            const int ob = k16 >> 3;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int j = 4 * w + i, oc = min(ob + (j >> 4), oend - 1);
+                const int row = (j & 15) * 32 + (lane >> 1);
+                dma16(W.mfq + ((size_t)oc * W.N + n0 + row) * 8 + 4 * (lane & 1), (const void AS3 *)(mins + 1024 * j));
+            }
+            {
+                const int j = w, oc = min(ob + (j >> 2), oend - 1);
+                const int row = min(m0 + (j & 3) * 32 + (lane >> 1), M - 1);
+                dma16(xq + ((size_t)oc * M + row) * 8 + 4 * (lane & 1), (const void AS3 *)(sums + 1024 * j));
+            }
+            wait_vm_lgkm0<0>();
+            block_barrier();
+            const bool live = ob + hf < oend;               // this lane half's octet lies in the split
+            h8 mh[2], ml[2];
+#pragma unroll
+            for (int a = 0; a < 2; a++) {
+                const uint8_t *p = mins + 16384 * hf + 32 * (wn + 32 * a + (lane & 31));
+                u32x4 p0 = *(const u32x4 *)p, p1 = *(const u32x4 *)(p + 16);
+                if (!live) p0 = p1 = u32x4{0u, 0u, 0u, 0u};
+                unpack(p0, p1, mh[a], ml[a]);
+            }
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                const uint8_t *p = sums + 4096 * hf + 32 * (32 * b + (lane & 31));
+                u32x4 p0 = *(const u32x4 *)p, p1 = *(const u32x4 *)(p + 16);
+                if (!live) p0 = p1 = u32x4{0u, 0u, 0u, 0u};
+                h8 xh, xl;
+                unpack(p0, p1, xh, xl);
+#pragma unroll
+                for (int a = 0; a < 2; a++) {
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, mh[a], acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl, mh[a], acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, ml[a], acc[a][b], 0, 0, 0);
+                }
+            }
+            block_barrier();                               // before the next chunk overwrites the stages
+        }
+    }
+
     // ---- epilogue: lane holds feature n0 + wn + 32a + (lane & 31) and, in
     // accumulator r, token m0 + 32b + (r/4)*8 + (lane/32)*4 + r%4 ----
     const int fl = lane & 31;
@@ -1316,26 +1388,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
 
 template <int WT, int EPI>
 void launch_dw_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
-                   int pair_mode, int S, float *ws, hipStream_t s) {
+                   int pair_mode, int S, float *ws, const float *xs, hipStream_t s) {
     const int NT = W.N / DW_N, NT8 = (NT + 7) / 8 * 8;
     const dim3 grid(NT8 * ((M + 127) / 128) * S);
     if (S > 1) {
-        launch((k_gemm_dw<WT, EPI, true>), grid, dim3(512), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, ws);
+        launch((k_gemm_dw<WT, EPI, true>), grid, dim3(512), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, ws, xs);
         launch_splitk_sum(EPI, ws, S, W.N, M, ep, pair_mode, s);
     } else {
         launch((k_gemm_dw<WT, EPI, false>), grid, dim3(512), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, 1,
-               (float *)nullptr);
+               (float *)nullptr, xs);
     }
 }
 
 template <int WT>
 void launch_dw_wt(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
-                  int pair_mode, int S, float *ws, hipStream_t s) {
+                  int pair_mode, int S, float *ws, const float *xs, hipStream_t s) {
     switch (ep.epi) {
-    case EPI_STORE: launch_dw_epi<WT, EPI_STORE>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
-    case EPI_RESID: launch_dw_epi<WT, EPI_RESID>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
-    case EPI_QKV: launch_dw_epi<WT, EPI_QKV>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
-    case EPI_SWIGLU: launch_dw_epi<WT, EPI_SWIGLU>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s); break;
+    case EPI_STORE: launch_dw_epi<WT, EPI_STORE>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
+    case EPI_RESID: launch_dw_epi<WT, EPI_RESID>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
+    case EPI_QKV: launch_dw_epi<WT, EPI_QKV>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
+    case EPI_SWIGLU: launch_dw_epi<WT, EPI_SWIGLU>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s); break;
     }
 }
 
@@ -1362,11 +1434,13 @@ int gemm_dw_tile_features() { return DW_N; }
 int gemm_dw_super_blocks() { return 4; }
 
 void launch_gemm_dw(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
-                    int pair_mode, int S, float *ws, hipStream_t s) {
+                    int pair_mode, int S, float *ws, const float *xs, hipStream_t s) {
     if (W.wtype == T_Q8_0)
-        launch_dw_wt<T_Q8_0>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+        launch_dw_wt<T_Q8_0>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, nullptr, s);
+    else if (W.wtype == T_Q4_K)
+        launch_dw_wt<T_Q4_K>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, xs, s);
     else
-        launch_dw_wt<T_Q4_0>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, s);
+        launch_dw_wt<T_Q4_0>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, nullptr, s);
 }
 
 void launch_gemm_dls(int ns, const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep,

@@ -180,12 +180,13 @@ void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, i
 // Derives the GEMM's scale arrays once every row of m is stored: Q4_0/Q8_0
 // m.dt from m.d; Q4_K m.mfq and m.sf from m.d and m.dm.
 void launch_gemm_scales(QMat &m, hipStream_t s);
-// The wide direct-to-LDS form (Q4_0 / Q8_0, ubatches of more than 64
+// The wide direct-to-LDS form (Q4_0 / Q8_0 / Q4_K, ubatches of more than 64
 // tokens): gemm_dw_tile_features() x 128 block tiles, codes loaded 64 bytes
 // of a row at a time; K split S into equal ranges of whole periods of
-// gemm_dw_super_blocks() K blocks.
+// gemm_dw_super_blocks() K blocks (Q4_K: whole octets; it also reads xs, the
+// tokens' block sums written by launch_block_sums).
 void launch_gemm_dw(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
-                    int pair_mode, int S, float *ws, hipStream_t s);
+                    int pair_mode, int S, float *ws, const float *xs, hipStream_t s);
 int gemm_dw_tile_features();
 int gemm_dw_super_blocks();
 int gemm_dl_tile_features();

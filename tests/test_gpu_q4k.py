@@ -7,8 +7,8 @@
   oracle's greedy tokens free-running; MHA and GQA, head_dim 64 and 128.
 * A vocabulary that is not a whole number of 256-row GEMM tiles takes the
   plain kernel for the output projection and still matches.
-* The direct-to-LDS GEMM form and the plain kernel agree closely (the same
-  arithmetic in another order).
+* The wide and 256-feature direct-to-LDS GEMM forms agree bitwise, and the
+  plain kernel closely (the same arithmetic in another order).
 * Several sequences decoded in one call (a GEMM of a few tokens) equal the
   same sequences decoded one at a time.
 """
@@ -95,25 +95,32 @@ def test_q4k_odd_vocab_plain_output_kernel(dec, orc):
 
 
 def test_q4k_gemm_forms_agree(dec):
+    # wide direct-to-LDS form (512-feature tiles: the gate/up and down
+    # matrices here), the 256-feature form (DECODE_GEMM_DW=0), the plain
+    # kernel (DECODE_GEMM_DL=0)
     hp = small_hp(synth.Q4_K, synth.F16, n_embd=512, n_ff=1024, n_vocab=2048)
     w = synth.weights_numpy(hp, 160, threads=4)
     prompt = synth.prompt(hp["n_vocab"], 200, 161)
     gm = dec.Model(hp, w)
     rows = {}
-    old = os.environ.get("DECODE_GEMM_DL")
+    saved = {k: os.environ.get(k) for k in ("DECODE_GEMM_DL", "DECODE_GEMM_DW")}
     try:
-        for form in ("23", "0"):     # direct-to-LDS form, then the plain kernel
-            os.environ["DECODE_GEMM_DL"] = form
+        for form, dl, dw in (("wide", "23", "1"), ("256", "23", "0"), ("plain", "0", "1")):
+            os.environ["DECODE_GEMM_DL"] = dl
+            os.environ["DECODE_GEMM_DW"] = dw
             ctx = dec.Context(gm, n_ctx=256, n_ubatch=128)
             assert ctx.prefill(prompt, 0, output_all=True) == 0
             rows[form] = np.stack([ctx.logits(i) for i in range(len(prompt))]).astype(np.float64)
             del ctx
     finally:
-        if old is None:
-            os.environ.pop("DECODE_GEMM_DL", None)
-        else:
-            os.environ["DECODE_GEMM_DL"] = old
-    a, b = rows["23"], rows["0"]
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    # the two direct-to-LDS forms: the same operands, order and K split
+    assert np.array_equal(rows["wide"], rows["256"])
+    a, b = rows["wide"], rows["plain"]
     assert np.abs(a).max() > 1e-2
     assert np.abs(a - b).max() <= 1e-4 * np.abs(b).max(), np.abs(a - b).max()
 
