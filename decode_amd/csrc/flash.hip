@@ -42,11 +42,14 @@ DEV int vt_col(int k) {         // permuted column of key k (0..63) in V^T
 }
 
 template <int HD>
-__global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
+__global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
     constexpr int KS = HD / 16;     // k-steps of Q K^T
     constexpr int DT = HD / 32;     // 32-row dim tiles of O^T
-    __shared__ __attribute__((aligned(16))) f16 Ks[BKEY][HD + KPAD];
-    __shared__ __attribute__((aligned(16))) f16 Vt[HD][BKEY + KPAD];
+    // two buffers: tile kt is staged in buffer kt & 1, so one barrier per tile
+    // orders both its stores before the reads and the previous reads of that
+    // buffer (two tiles back) before its stores
+    __shared__ __attribute__((aligned(16))) f16 Ks[2][BKEY][HD + KPAD];
+    __shared__ __attribute__((aligned(16))) f16 Vt[2][HD][BKEY + KPAD];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int G = a.H / a.kv.n_kv, Gb = G < 4 ? G : 4, Tb = 4 / Gb;
@@ -129,16 +132,19 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
             }
         }
     };
+    // the wavefront's first query position: key tiles wholly at or below it
+    // need no causal mask (nor do full query tiles)
+    const int qpos_min = p0 + tw;
+    const bool tile_full = tw + 31 < T;
     load_tile(kbeg);
     for (int kt = 0; kt < ntiles; kt++) {
-        const int k0 = kbeg + kt * BKEY;
+        const int k0 = kbeg + kt * BKEY, buf = kt & 1;
         // ---- stage K and V^T of this tile; the next tile's loads then run
         // during this tile's arithmetic ----
-        __syncthreads();                                    // previous tile fully consumed
 #pragma unroll
         for (int c = 0; c < CPT; c++) {
             const int ch = tid + c * 256, key = ch / (HD / 8), d8 = ch % (HD / 8);
-            *(uint4 *)&Ks[key][d8 * 8] = kr[c];
+            *(uint4 *)&Ks[buf][key][d8 * 8] = kr[c];
         }
 #pragma unroll
         for (int c = 0; c < PPT; c++) {
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
             const int col = vt_col(key);                    // even; key + 1 sits at col + 1
 #pragma unroll
             for (int e = 0; e < 8; e++)
-                *(uint32_t *)&Vt[d8 * 8 + e][col] = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
+                *(uint32_t *)&Vt[buf][d8 * 8 + e][col] = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
         }
         __syncthreads();
         if (kt + 1 < ntiles) load_tile(k0 + BKEY);
@@ -160,21 +166,26 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
             for (int r = 0; r < 16; r++) s[mt][r] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ks++) {
-                const h8 kf = *(const h8 *)&Ks[mt * 32 + (lane & 31)][16 * ks + 8 * (lane >> 5)];
+                const h8 kf = *(const h8 *)&Ks[buf][mt * 32 + (lane & 31)][16 * ks + 8 * (lane >> 5)];
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[mt], 0, 0, 0);
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, ql[ks], s[mt], 0, 0, 0);
             }
         }
         // ---- causal mask + online softmax over this query column ----
         float mt_max = -INFINITY;
+        if (k0 + BKEY - 1 > qpos_min || !tile_full) {       // (uniform)
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int key = k0 + mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    if (key > qpos || !q_ok) s[mt][r] = -INFINITY;
+                }
+        }
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int key = k0 + mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (key > qpos || !q_ok) s[mt][r] = -INFINITY;
-                mt_max = fmaxf(mt_max, s[mt][r]);
-            }
+            for (int r = 0; r < 16; r++) mt_max = fmaxf(mt_max, s[mt][r]);
         mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, 64));
         const float m_new = fmaxf(m_run, mt_max);
         const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
@@ -193,16 +204,17 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
         psum += __shfl_xor(psum, 32, 64);
         l_run = l_run * alpha + psum;
         m_run = m_new;
+        if (__ballot(alpha != 1.f))                         // (uniform: skipped while no max moved)
 #pragma unroll
-        for (int dt = 0; dt < DT; dt++)
+            for (int dt = 0; dt < DT; dt++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) acc[dt][r] *= alpha;
+                for (int r = 0; r < 16; r++) acc[dt][r] *= alpha;
         // ---- O^T += V^T P^T ----
 #pragma unroll
         for (int ss = 0; ss < 4; ss++) {
 #pragma unroll
             for (int dt = 0; dt < DT; dt++) {
-                const h8 vf = *(const h8 *)&Vt[dt * 32 + (lane & 31)][16 * ss + 8 * (lane >> 5)];
+                const h8 vf = *(const h8 *)&Vt[buf][dt * 32 + (lane & 31)][16 * ss + 8 * (lane >> 5)];
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ss], acc[dt], 0, 0, 0);
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pl[ss], acc[dt], 0, 0, 0);
             }
