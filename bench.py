@@ -327,7 +327,7 @@ def prefill_workload(args, dec, torch, W, hp, log):
         gflop = 2.0 * W["n_ubatch"] * 2 * hp["n_ff"] * hp["n_embd"]
         gu = {"bound": "mfma", "achieved": round(gflop / avg / 1e12, 1), "peak": MFMA_F16_PEAK_TFLOPS,
               "unit": "TFLOP/s", "frac": round(gflop / avg / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-              "kernel": "gate/up GEMM of a 512-token ubatch (k_gemm_dl)", "avg_us": round(avg * 1e6, 1),
+              "kernel": "gate/up GEMM of a 512-token ubatch (k_gemm_dw, the wide direct-to-LDS form)", "avg_us": round(avg * 1e6, 1),
               "launches_timed": probe[1]}
     out = {"metric": "prefill tokens/s (8B-shape Q8_0, 8192-token prompt, ubatches of 512)",
            "value": round(n / t, 1), "unit": "tokens/s", "n_gpus": 1, "steps": len(times), "warmup": 1,
@@ -693,7 +693,7 @@ def main():
         ach = flops / avg / 1e12
         pf_roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                    "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
-                   "kernel": "gate/up GEMM of a 512-token ubatch (k_gemm_dl)", "avg_us": round(avg * 1e6, 1),
+                   "kernel": "gate/up GEMM of a 512-token ubatch (k_gemm_dw, the wide direct-to-LDS form)", "avg_us": round(avg * 1e6, 1),
                    "launches_timed": pf_probe[1]}
         if pf_attn and pf_attn[1]:
             pf_roof["attention_avg_us_per_ubatch"] = round(pf_attn[0] * 1e3 / pf_attn[1], 1)
