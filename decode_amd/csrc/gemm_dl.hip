@@ -1051,7 +1051,7 @@ void launch_ws_epi(int ks, const QMat &W, const uint16_t *Xh, const uint16_t *Xl
 // wait before K block kb is a constant per kb within its super-stage
 // (dw_wait: the loads issued after the later of its activation stage and
 // its codes).  The K range of a split is whole periods of 4 K blocks (Q4_K:
-// whole octets).  Q4_K: codes as Q4_0 (exact values 0..15), the fp32 scale
+// whole octets), the splits as even as that allows.  Q4_K: codes as Q4_0 (exact values 0..15), the fp32 scale
 // d sc from the transposed sf, and after the main loop the min term as in
 // k_gemm_dl, with the chunks of mins and block sums staged in the code
 // stages.
@@ -1097,9 +1097,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n0 = nt * DW_N, m0 = mtile * 128, wn = 64 * w;
-    // equal splits of whole super-stages (checked by the launcher)
-    constexpr int CK = dw_ck<WT>();
-    const int nb_all = W.K >> 5, nb = nb_all / nsplit, kb0 = split * nb, nsup = nb / CK;
+    // split `split` of nsplit: units [P split / nsplit, P (split + 1) / nsplit)
+    // of the P units of U K blocks (periods of 4; Q4_K octets), so splits may
+    // differ by one unit
+    constexpr int CK = dw_ck<WT>(), U = K4 ? 8 : 4;
+    const int nb_all = W.K >> 5, P = nb_all / U;
+    const int kb0 = U * (int)((long)P * split / nsplit), nb = U * (int)((long)P * (split + 1) / nsplit) - kb0;
+    const int nsup = nb / CK;
 
     // ---- per-lane byte offsets of the direct loads ----
     // activations: wavefront w loads part w >> 2 (value, remainder), slots
