@@ -830,7 +830,7 @@ int g_gemm_dls = 1;    // direct-to-LDS form with 32-token tiles for at most 32 
 int g_gemm_dls_ns = 4; // its LDS stages
 int g_gemm_dls_fill = 4; // its K split aims at this many blocks per 4 compute units
 int g_gemm_ws = 2;     // weight-streaming form for Q4_0 at most 32 tokens: K blocks per stage (0: off)
-int g_gemm_dw = 1;     // wide direct-to-LDS form for Q4_0 ubatches of more than 64 tokens (0: off)
+int g_gemm_dw = 1;     // wide direct-to-LDS form for Q4_0 / Q8_0 / Q4_K ubatches of more than 64 tokens (0: off)
 
 bool mfma_shape(const QMat &W, int ldx) {
     return (W.wtype == T_Q4_0 || W.wtype == T_Q8_0) && W.N % BN == 0 && W.K % 32 == 0 && ldx % 8 == 0;
@@ -1066,7 +1066,7 @@ void gemm_set_num_cu(int n) {
     // DECODE_GEMM_WS: K blocks per stage of the weight-streaming form (2 or 4,
     // default 2); 0 leaves Q4_0 ubatches of at most 32 tokens to the 32-token
     // direct-to-LDS form
-    // DECODE_GEMM_DW=0: Q4_0 / Q8_0 ubatches of more than 64 tokens take the
+    // DECODE_GEMM_DW=0: Q4_0 / Q8_0 / Q4_K ubatches of more than 64 tokens take the
     // 256-feature direct-to-LDS form instead of the wide one
     const char *dwv = getenv("DECODE_GEMM_DW");
     g_gemm_dw = !(dwv && strcmp(dwv, "0") == 0);

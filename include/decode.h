@@ -198,6 +198,10 @@ typedef struct {
  *                         logits move about 3.5e-2 from the exact result
  *   DECODE_GEMM_SKINNY=0  ubatches of at most 32 tokens use the tiled GEMM
  *                         on every matrix (same exact operands)
+ *   DECODE_GEMM_DW=0      ubatches of more than 64 tokens take the
+ *                         256-feature direct-to-LDS GEMM instead of the
+ *                         512-feature wide form (bitwise the same results;
+ *                         the wide form is faster)
  *   DECODE_PREFILL_ATTN=splitk  prefill attention through the split-K
  *                         decode kernels instead of the flash kernel
  *   DECODE_STEP_KERNEL=1  see dec_set_step_kernel */
