@@ -35,6 +35,22 @@ namespace {
 constexpr int BKEY = 64;        // keys per tile
 constexpr int KPAD = 8;         // f16 padding of an LDS row
 
+// Sum and max of a value over lanes l and l ^ 32 with one v_permlane32_swap
+// (which exchanges the upper half of one copy with the lower half of the
+// other: each lane gets back its own value and its partner's, in lane order).
+DEV uint2 swap_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return make_uint2(r[0], r[1]);
+}
+DEV float sum_halves(float v) {
+    const uint2 r = swap_halves(v);
+    return __uint_as_float(r.x) + __uint_as_float(r.y);
+}
+DEV float max_halves(float v) {
+    const uint2 r = swap_halves(v);
+    return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+}
+
 DEV int vt_col(int k) {         // permuted column of key k (0..63) in V^T
     const int s = k >> 4, rem = k & 15;
     const int h = (rem >> 2) & 1, e = ((rem >> 3) << 2) | (rem & 3);
@@ -186,22 +202,32 @@ __global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
         for (int mt = 0; mt < 2; mt++)
 #pragma unroll
             for (int r = 0; r < 16; r++) mt_max = fmaxf(mt_max, s[mt][r]);
-        mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, 64));
+        mt_max = max_halves(mt_max);
         const float m_new = fmaxf(m_run, mt_max);
-        const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+        // exponents are <= 0 here, so the plain hardware exp2 serves (results
+        // below 2^-126 flush to zero, far under what an f16 P or the fp32 sum
+        // keeps); while m_new is -inf every score is -inf and exp2(-inf) = 0
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float m_sub = m_new == -INFINITY ? 0.f : m_new;
         float psum = 0.f;
         h8 pf[4], pl[4];   // P as f16 value + remainder, like Q
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const float p = m_new == -INFINITY ? 0.f : exp2f(s[mt][r] - m_new);
-                psum += p;
-                const f16 ph = (f16)p;
-                pf[mt * 2 + (r >> 3)][r & 7] = ph;
-                pl[mt * 2 + (r >> 3)][r & 7] = (f16)(p - (float)ph);
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(s[mt][r] - m_sub);
+                const float p1 = __builtin_amdgcn_exp2f(s[mt][r + 1] - m_sub);
+                psum += p0;
+                psum += p1;
+                uint32_t pb = h2_bits(h2{(f16)p0, (f16)p1});  // one packed conversion ...
+                asm volatile("" : "+v"(pb));                  // ... whose halves the remainders reuse
+                const h2 ph = as_h2(pb);
+                pf[mt * 2 + (r >> 3)][r & 7] = ph.x;
+                pf[mt * 2 + (r >> 3)][(r & 7) + 1] = ph.y;
+                pl[mt * 2 + (r >> 3)][r & 7] = (f16)(p0 - (float)ph.x);
+                pl[mt * 2 + (r >> 3)][(r & 7) + 1] = (f16)(p1 - (float)ph.y);
             }
-        psum += __shfl_xor(psum, 32, 64);
+        psum = sum_halves(psum);
         l_run = l_run * alpha + psum;
         m_run = m_new;
         if (__ballot(alpha != 1.f))                         // (uniform: skipped while no max moved)
@@ -260,44 +286,55 @@ __global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
     }
 }
 
-// Token t (row of the ubatch), all heads: combines the key ranges of its
-// tile in range order, M = max m_s, L = sum l_s 2^(m_s - M),
+// Token t (row of the ubatch), 256 (head, 4-dim) items per block: combines the
+// key ranges of its tile in range order, M = max m_s, L = sum l_s 2^(m_s - M),
 // o = sum acc_s 2^(m_s - M) / L.  Tiles that needed one range are skipped.
+// A thread requests every range's (m, l) and partial before it adds any, so a
+// token's loads are in flight together (at most FM_MAXNS ranges).
+constexpr int FM_MAXNS = 8;
 template <int HD>
 __global__ __launch_bounds__(256) void k_flash_merge(FlashArgs a, int tile_tokens) {
-    const int t = blockIdx.x, tid = threadIdx.x;
+    const int t = blockIdx.x, i = blockIdx.y * 256 + threadIdx.x;
     const int last_tok = min(a.T - 1, (t / tile_tokens) * tile_tokens + tile_tokens - 1);
-    const int nsplit = (a.tok.pos[0] + last_tok + 1 + a.chunk - 1) / a.chunk;
-    if (nsplit <= 1) return;
-    for (int i = tid; i < a.H * HD / 4; i += 256) {
-        const int head = i / (HD / 4), d = (i % (HD / 4)) * 4;
-        const size_t hh = (size_t)t * a.H + head;
-        float M = -INFINITY;
-        for (int sp = 0; sp < nsplit; sp++) M = fmaxf(M, a.ml[(hh * a.max_chunks + sp) * 2]);
-        float L = 0.f;
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int sp = 0; sp < nsplit; sp++) {
-            const float2 ml = *(const float2 *)(a.ml + (hh * a.max_chunks + sp) * 2);
-            const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
-            L += ml.y * f;
-            const float4 v = *(const float4 *)(a.part + (hh * a.max_chunks + sp) * HD + d);
-            o.x += v.x * f;
-            o.y += v.y * f;
-            o.z += v.z * f;
-            o.w += v.w * f;
-        }
-        const float inv = 1.0f / L;
-        const float y[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
-        f16 hv[4], lv[4];
+    const int nsplit = min(a.ns, (a.tok.pos[0] + last_tok + 1 + a.chunk - 1) / a.chunk);   // a.ns <= FM_MAXNS
+    if (nsplit <= 1 || i >= a.H * HD / 4) return;
+    const int head = i / (HD / 4), d = (i % (HD / 4)) * 4;
+    const size_t hh = (size_t)t * a.H + head;
+    float2 ml[FM_MAXNS];
+    float4 v[FM_MAXNS];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            hv[e] = (f16)y[e];
-            lv[e] = (f16)(y[e] - (float)hv[e]);
+    for (int sp = 0; sp < FM_MAXNS; sp++)
+        if (sp < nsplit) {
+            ml[sp] = *(const float2 *)(a.ml + (hh * a.max_chunks + sp) * 2);
+            v[sp] = *(const float4 *)(a.part + (hh * a.max_chunks + sp) * HD + d);
         }
-        const size_t ob = hh * HD + d;
-        *(uint2 *)((f16 *)a.o + ob) = *(const uint2 *)hv;
-        if (a.o_lo) *(uint2 *)((f16 *)a.o_lo + ob) = *(const uint2 *)lv;
+    float M = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < FM_MAXNS; sp++)
+        if (sp < nsplit) M = fmaxf(M, ml[sp].x);
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int sp = 0; sp < FM_MAXNS; sp++)
+        if (sp < nsplit) {
+            const float f = ml[sp].x == -INFINITY ? 0.f : exp2f(ml[sp].x - M);
+            L += ml[sp].y * f;
+            o.x += v[sp].x * f;
+            o.y += v[sp].y * f;
+            o.z += v[sp].z * f;
+            o.w += v[sp].w * f;
+        }
+    const float inv = 1.0f / L;
+    const float y[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+    f16 hv[4], lv[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        hv[e] = (f16)y[e];
+        lv[e] = (f16)(y[e] - (float)hv[e]);
     }
+    const size_t ob = hh * HD + d;
+    *(uint2 *)((f16 *)a.o + ob) = *(const uint2 *)hv;
+    if (a.o_lo) *(uint2 *)((f16 *)a.o_lo + ob) = *(const uint2 *)lv;
 }
 
 }  // namespace
@@ -313,7 +350,7 @@ bool launch_flash_prefill(const FlashArgs &a_in, hipStream_t s) {
     // (512 blocks of 4 on 256 compute units), ranges of whole 64-key tiles
     const long long blocks = (long long)tiles * a.kv.n_kv * (G / Gb);
     int ns = (int)((g_flash_blocks + blocks - 1) / blocks);
-    ns = ns < 1 ? 1 : ns > 8 ? 8 : ns;
+    ns = ns < 1 ? 1 : ns > FM_MAXNS ? FM_MAXNS : ns;
     if (!a.part || !a.ml) ns = 1;
     if (ns > a.max_chunks) ns = a.max_chunks > 0 ? a.max_chunks : 1;
     const int max_keys = a.tok_pos0_max + a.T;            // keys of the last tile (host-side bound)
@@ -326,11 +363,11 @@ bool launch_flash_prefill(const FlashArgs &a_in, hipStream_t s) {
     switch (a.kv.hd) {
     case 64:
         launch(k_flash_prefill<64>, grid, dim3(256), 0, s, a);
-        if (ns > 1) launch(k_flash_merge<64>, dim3(a.T), dim3(256), 0, s, a, 32 * Tb);
+        if (ns > 1) launch(k_flash_merge<64>, dim3(a.T, (a.H * 16 + 255) / 256), dim3(256), 0, s, a, 32 * Tb);
         return true;
     case 128:
         launch(k_flash_prefill<128>, grid, dim3(256), 0, s, a);
-        if (ns > 1) launch(k_flash_merge<128>, dim3(a.T), dim3(256), 0, s, a, 32 * Tb);
+        if (ns > 1) launch(k_flash_merge<128>, dim3(a.T, (a.H * 32 + 255) / 256), dim3(256), 0, s, a, 32 * Tb);
         return true;
     default: return false;
     }

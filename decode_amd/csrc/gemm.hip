@@ -47,6 +47,8 @@
 
 namespace {
 
+void launch_sum(int epi, const float *ws, int S, int N, int M, const EpiArgs &ep, int pair_mode, hipStream_t s);
+
 constexpr int BN = 128;
 constexpr int LDS_STRIDE = 40;   // f16 elements per LDS row (32 + 8 pad)
 
@@ -490,7 +492,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(QMat W, const uint16_t *Xh
 }
 
 // Sums the K-split partial tiles in split order and applies the epilogue;
-// one thread per (row pair, token).
+// one thread per (row pair, token).  The epilogue's memory inputs and the
+// first 8 splits' values are requested together, then added in order.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_splitk_sum(const float *part, int nsplit, int N, int M,
                                                          EpiArgs ep, int pair_mode) {
@@ -499,45 +502,78 @@ __global__ __launch_bounds__(256) void k_gemm_splitk_sum(const float *part, int 
     if (p >= N / 2 || m >= M) return;
     int r0, r1;
     pair_rows(pair_mode, p, r0, r1);
+    const EpiPre pre = epi_prefetch<EPI>(ep, m, r0, r1);
+    const float *pm = part + (size_t)m * N;
+    const size_t ps = (size_t)M * N;                   // between splits
+    float va[8], vb[8];
+#pragma unroll
+    for (int s = 0; s < 8; s++)
+        if (s < nsplit) {
+            va[s] = pm[s * ps + r0];
+            vb[s] = pm[s * ps + r1];
+        }
     float a = 0.f, b = 0.f;
-    for (int s = 0; s < nsplit; s++) {
-        const float *row = part + ((size_t)s * M + m) * N;
-        a += row[r0];
-        b += row[r1];
+#pragma unroll
+    for (int s = 0; s < 8; s++)
+        if (s < nsplit) {
+            a += va[s];
+            b += vb[s];
+        }
+    for (int s = 8; s < nsplit; s++) {
+        a += pm[s * ps + r0];
+        b += pm[s * ps + r1];
     }
-    epi_pair<EPI>(ep, m, p, r0, r1, a, b);
+    epi_pair_pre<EPI>(ep, m, p, r0, r1, a, b, pre);
 }
 
 // The K-split sum of a residual-adding GEMM fused with the RMSNorm of the
 // rows it completes: one 1024-thread block per token row; element j of the row
 // is y[j] + the sum of the S partials in split order (as k_gemm_splitk_sum adds
 // them), each thread holding its elements' sums in registers for the norm.
+// V = 4 (N a multiple of 4) moves each split's values of a thread in one
+// 16-byte load.
 constexpr int SRN_T = 1024, SRN_E = 16;      // threads, elements per thread at most (rows <= 16384)
+template <int V>
 __global__ __launch_bounds__(SRN_T) void k_splitk_resid_norm(const float *part, int nsplit, int N, int M, EpiArgs ep) {
+    constexpr int U = SRN_E / V;                       // chunks of V elements per thread at most
     __shared__ float red[SRN_T / 64];
     const int m = blockIdx.x, tid = threadIdx.x;
     float *y = ep.y + (size_t)m * ep.ldy;
     const float *pm = part + (size_t)m * N;
     const size_t ps = (size_t)M * N;                   // between splits
-    float v[SRN_E];
+    using vec = std::conditional_t<V == 4, float4, float>;
+    auto ld = [](const float *p) __attribute__((always_inline)) { return *(const vec *)p; };
+    auto el = [](const vec &x, int e) __attribute__((always_inline)) -> float {
+        if constexpr (V == 4) return e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
+        else return x;
+    };
+    float v[U][V];
     float ss = 0.f;
 #pragma unroll
-    for (int u = 0; u < SRN_E; u++) {
-        const int j = tid + SRN_T * u;
-        if (SRN_T * u >= N) break;                     // uniform
-        const int jc = min(j, N - 1);
-        float pv[8];
-#pragma unroll
-        for (int k = 0; k < 8; k++) pv[k] = k < nsplit ? pm[k * ps + jc] : 0.f;
-        float a = 0.f;
+    for (int u = 0; u < U; u++) {
+        const int j = (tid + SRN_T * u) * V;
+        if (SRN_T * u * V >= N) break;                 // uniform
+        const int jc = min(j, N - V);
+        vec pv[8];
 #pragma unroll
         for (int k = 0; k < 8; k++)
-            if (k < nsplit) a += pv[k];
-        for (int k = 8; k < nsplit; k++) a += pm[k * ps + jc];
-        v[u] = y[jc] + a;
+            if (k < nsplit) pv[k] = ld(pm + k * ps + jc);
+        const vec yv = ld(y + jc);
+#pragma unroll
+        for (int e = 0; e < V; e++) {
+            float a = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+                if (k < nsplit) a += el(pv[k], e);
+            for (int k = 8; k < nsplit; k++) a += pm[k * ps + jc + e];
+            v[u][e] = el(yv, e) + a;
+        }
         if (j < N) {
-            y[j] = v[u];
-            ss += v[u] * v[u];
+#pragma unroll
+            for (int e = 0; e < V; e++) {
+                y[j + e] = v[u][e];
+                ss += v[u][e] * v[u][e];
+            }
         }
     }
     ss = wave_sum(ss);
@@ -550,14 +586,17 @@ __global__ __launch_bounds__(SRN_T) void k_splitk_resid_norm(const float *part, 
     f16 *o = (f16 *)ep.nrm_h + (size_t)m * ep.nrm_ld;
     f16 *ol = (f16 *)ep.nrm_l + (size_t)m * ep.nrm_ld;
 #pragma unroll
-    for (int u = 0; u < SRN_E; u++) {
-        const int j = tid + SRN_T * u;
-        if (SRN_T * u >= N) break;
+    for (int u = 0; u < U; u++) {
+        const int j = (tid + SRN_T * u) * V;
+        if (SRN_T * u * V >= N) break;
         if (j < N) {
-            const float w = v[u] * r * ep.nrm_g[j];
-            const f16 hi = (f16)w;
-            o[j] = hi;
-            ol[j] = (f16)(w - (float)hi);
+#pragma unroll
+            for (int e = 0; e < V; e++) {
+                const float w = v[u][e] * r * ep.nrm_g[j + e];
+                const f16 hi = (f16)w;
+                o[j + e] = hi;
+                ol[j + e] = (f16)(w - (float)hi);
+            }
         }
     }
 }
@@ -892,8 +931,7 @@ void launch_mfma_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int 
             launch_mfma_tile<WT, EPI, 128, true>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, grid, f16w, s);
         else
             launch_mfma_tile<WT, EPI, 64, true>(W, Xh, Xl, ldx, ep, M, pair_mode, S, ws, grid, false, s);
-        launch(k_gemm_splitk_sum<EPI>, dim3((W.N / 2 + 255) / 256, M), dim3(256), 0, s, (const float *)ws, S,
-               W.N, M, ep, pair_mode);
+        launch_sum(EPI, (const float *)ws, S, W.N, M, ep, pair_mode, s);
     } else if (bm == 256) {
         launch_mfma_tile<WT, EPI, 256, false>(W, Xh, Xl, ldx, ep, M, pair_mode, 1, ws, grid, true, s);
     } else if (bm == 128) {
@@ -1088,13 +1126,9 @@ void launch_block_sums(const uint16_t *Xh, const uint16_t *Xl, int ldx, int M, i
     launch(k_block_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, Xh, Xl, ldx, M, K, xs);
 }
 
-void launch_splitk_sum(int epi, const float *ws, int S, int N, int M, const EpiArgs &ep, int pair_mode,
-                       hipStream_t s) {
-    if (epi == EPI_RESID && ep.nrm_g && ep.nrm_done) {
-        launch(k_splitk_resid_norm, dim3(M), dim3(SRN_T), 0, s, ws, S, N, M, ep);
-        *ep.nrm_done = 1;
-        return;
-    }
+namespace {
+// The plain K-split sum + epilogue.
+void launch_sum(int epi, const float *ws, int S, int N, int M, const EpiArgs &ep, int pair_mode, hipStream_t s) {
     const dim3 g((N / 2 + 255) / 256, M);
     switch (epi) {
     case EPI_STORE: launch(k_gemm_splitk_sum<EPI_STORE>, g, dim3(256), 0, s, ws, S, N, M, ep, pair_mode); break;
@@ -1102,6 +1136,20 @@ void launch_splitk_sum(int epi, const float *ws, int S, int N, int M, const EpiA
     case EPI_QKV: launch(k_gemm_splitk_sum<EPI_QKV>, g, dim3(256), 0, s, ws, S, N, M, ep, pair_mode); break;
     case EPI_SWIGLU: launch(k_gemm_splitk_sum<EPI_SWIGLU>, g, dim3(256), 0, s, ws, S, N, M, ep, pair_mode); break;
     }
+}
+}  // namespace
+
+void launch_splitk_sum(int epi, const float *ws, int S, int N, int M, const EpiArgs &ep, int pair_mode,
+                       hipStream_t s) {
+    if (epi == EPI_RESID && ep.nrm_g && ep.nrm_done) {
+        if (N % 4 == 0)
+            launch(k_splitk_resid_norm<4>, dim3(M), dim3(SRN_T), 0, s, ws, S, N, M, ep);
+        else
+            launch(k_splitk_resid_norm<1>, dim3(M), dim3(SRN_T), 0, s, ws, S, N, M, ep);
+        *ep.nrm_done = 1;
+        return;
+    }
+    launch_sum(epi, ws, S, N, M, ep, pair_mode, s);
 }
 
 size_t gemm_workspace_bytes(const QMat &W, int M) {
@@ -1190,14 +1238,8 @@ bool launch_gemm(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx,
                 launch((k_gemm_skinny<T_Q4_0, SK_FT>), dim3(groups * S), dim3(256), 0, s, W, Xh, Xl, ldx, M, S, ws);
             else
                 launch((k_gemm_skinny<T_Q8_0, SK_FT>), dim3(groups * S), dim3(256), 0, s, W, Xh, Xl, ldx, M, S, ws);
-            const dim3 g((W.N / 2 + 255) / 256, M);
-            switch (ep.epi) {
-            case EPI_STORE: launch(k_gemm_splitk_sum<EPI_STORE>, g, dim3(256), 0, s, (const float *)ws, S, W.N, M, ep, pair_mode); break;
-            case EPI_RESID: launch(k_gemm_splitk_sum<EPI_RESID>, g, dim3(256), 0, s, (const float *)ws, S, W.N, M, ep, pair_mode); break;
-            case EPI_QKV: launch(k_gemm_splitk_sum<EPI_QKV>, g, dim3(256), 0, s, (const float *)ws, S, W.N, M, ep, pair_mode); break;
-            case EPI_SWIGLU: launch(k_gemm_splitk_sum<EPI_SWIGLU>, g, dim3(256), 0, s, (const float *)ws, S, W.N, M, ep, pair_mode); break;
-            default: return false;
-            }
+            if (ep.epi != EPI_STORE && ep.epi != EPI_RESID && ep.epi != EPI_QKV && ep.epi != EPI_SWIGLU) return false;
+            launch_sum(ep.epi, (const float *)ws, S, W.N, M, ep, pair_mode, s);
             return true;
         }
     }
