@@ -69,10 +69,19 @@ __global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int G = a.H / a.kv.n_kv, Gb = G < 4 ? G : 4, Tb = 4 / Gb;
-    const int g = blockIdx.y;
-    const int head = g * G + blockIdx.z * Gb + (w % Gb);
-    const int split = blockIdx.x % a.ns;
-    const int tok0 = (blockIdx.x / a.ns) * 32 * Tb;         // first token of the block
+    // Workgroups go to the 8 XCDs in turn (linear id mod 8), each XCD with
+    // its own L2.  The linear ids are renumbered so that an XCD's blocks form
+    // one contiguous run of (KV head, head group, range) order: the blocks
+    // that read one KV head's keys then share an L2 instead of each XCD
+    // caching every head.
+    const int X = gridDim.x, Y = gridDim.y, Z = gridDim.z;
+    const int B = X * Y * Z;
+    const int L = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
+    const int lin = B % 8 == 0 ? (L % 8) * (B / 8) + L / 8 : L;
+    const int bx = lin % X, bz = (lin / X) % Z, g = lin / (X * Z);
+    const int head = g * G + bz * Gb + (w % Gb);
+    const int split = bx % a.ns;
+    const int tok0 = (bx / a.ns) * 32 * Tb;                 // first token of the block
     const int tw = tok0 + (w / Gb) * 32;                    // first token of this wavefront
     const int q_t = tw + (lane & 31);                       // this lane's query column
     const int p0 = a.tok.pos[0], seq = a.tok.seq[0];
