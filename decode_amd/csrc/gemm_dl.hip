@@ -1086,14 +1086,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
     constexpr bool K4 = WT == T_Q4_K;
     __shared__ __attribute__((aligned(16))) uint8_t lds[DW_LDS];
 
-    // block -> (feature tile, token tile, K split); the tiles of one feature
-    // tile share an XCD
+    // block -> (feature tile, K split, token tile): the units (feature tile,
+    // K split) go to the 8 XCDs in turn (workgroup i runs on XCD i mod 8), and
+    // the token tiles of a unit, which read the same weights, run together on
+    // its XCD
     const int mtiles = (M + 127) / 128;
-    const int per_nt = mtiles * nsplit;
     const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
-    const int nt = (j / per_nt) * 8 + xcd, rem = j % per_nt;
-    const int mtile = rem % mtiles, split = rem / mtiles;
-    if (nt >= NT) return;
+    const int unit = (j / mtiles) * 8 + xcd, mtile = j % mtiles;
+    if (unit >= NT * nsplit) return;
+    const int nt = unit / nsplit, split = unit % nsplit;
 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n0 = nt * DW_N, m0 = mtile * 128, wn = 64 * w;
@@ -1393,8 +1394,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dw(QMat W, const uint16_t *Xh, 
 template <int WT, int EPI>
 void launch_dw_epi(const QMat &W, const uint16_t *Xh, const uint16_t *Xl, int ldx, const EpiArgs &ep, int M,
                    int pair_mode, int S, float *ws, const float *xs, hipStream_t s) {
-    const int NT = W.N / DW_N, NT8 = (NT + 7) / 8 * 8;
-    const dim3 grid(NT8 * ((M + 127) / 128) * S);
+    const int NT = W.N / DW_N, U8 = (NT * S + 7) / 8 * 8;
+    const dim3 grid(U8 * ((M + 127) / 128));
     if (S > 1) {
         launch((k_gemm_dw<WT, EPI, true>), grid, dim3(512), 0, s, W, Xh, Xl, ldx, ep, M, pair_mode, NT, S, ws, xs);
         launch_splitk_sum(EPI, ws, S, W.N, M, ep, pair_mode, s);
