@@ -218,10 +218,18 @@ __global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
         // keeps); while m_new is -inf every score is -inf and exp2(-inf) = 0
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-        float psum = 0.f;
-        h8 pf[4], pl[4];   // P as f16 value + remainder, like Q
+        if (__ballot(alpha != 1.f))                         // (uniform: skipped while no max moved)
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++)
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) acc[dt][r] *= alpha;
+        // ---- P and O^T += V^T P^T, one 32-key half at a time: the second
+        // half's exp2 and conversions have no operand in the first half's
+        // MFMAs, so the two overlap within the wavefront ----
+        float psum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++) {
+            h8 pf[2], pl[2];   // P as f16 value + remainder, like Q
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 const float p0 = __builtin_amdgcn_exp2f(s[mt][r] - m_sub);
@@ -231,29 +239,25 @@ __global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
                 uint32_t pb = h2_bits(h2{(f16)p0, (f16)p1});  // one packed conversion ...
                 asm volatile("" : "+v"(pb));                  // ... whose halves the remainders reuse
                 const h2 ph = as_h2(pb);
-                pf[mt * 2 + (r >> 3)][r & 7] = ph.x;
-                pf[mt * 2 + (r >> 3)][(r & 7) + 1] = ph.y;
-                pl[mt * 2 + (r >> 3)][r & 7] = (f16)(p0 - (float)ph.x);
-                pl[mt * 2 + (r >> 3)][(r & 7) + 1] = (f16)(p1 - (float)ph.y);
+                pf[r >> 3][r & 7] = ph.x;
+                pf[r >> 3][(r & 7) + 1] = ph.y;
+                pl[r >> 3][r & 7] = (f16)(p0 - (float)ph.x);
+                pl[r >> 3][(r & 7) + 1] = (f16)(p1 - (float)ph.y);
             }
+#pragma unroll
+            for (int sh = 0; sh < 2; sh++) {
+                const int ss = 2 * mt + sh;
+#pragma unroll
+                for (int dt = 0; dt < DT; dt++) {
+                    const h8 vf = *(const h8 *)&Vt[buf][dt * 32 + (lane & 31)][16 * ss + 8 * (lane >> 5)];
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[sh], acc[dt], 0, 0, 0);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pl[sh], acc[dt], 0, 0, 0);
+                }
+            }
+        }
         psum = sum_halves(psum);
         l_run = l_run * alpha + psum;
         m_run = m_new;
-        if (__ballot(alpha != 1.f))                         // (uniform: skipped while no max moved)
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) acc[dt][r] *= alpha;
-        // ---- O^T += V^T P^T ----
-#pragma unroll
-        for (int ss = 0; ss < 4; ss++) {
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++) {
-                const h8 vf = *(const h8 *)&Vt[buf][dt * 32 + (lane & 31)][16 * ss + 8 * (lane >> 5)];
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ss], acc[dt], 0, 0, 0);
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pl[ss], acc[dt], 0, 0, 0);
-            }
-        }
     }
 
     if (nsplit > 1) {
