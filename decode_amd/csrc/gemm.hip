@@ -530,8 +530,8 @@ __global__ __launch_bounds__(256) void k_gemm_splitk_sum(const float *part, int 
 // rows it completes: one 1024-thread block per token row; element j of the row
 // is y[j] + the sum of the S partials in split order (as k_gemm_splitk_sum adds
 // them), each thread holding its elements' sums in registers for the norm.
-// V = 4 (N a multiple of 4) moves each split's values of a thread in one
-// 16-byte load.
+// V = 4 (N and the row stride of y multiples of 4) moves each split's values
+// of a thread in one 16-byte load.
 constexpr int SRN_T = 1024, SRN_E = 16;      // threads, elements per thread at most (rows <= 16384)
 template <int V>
 __global__ __launch_bounds__(SRN_T) void k_splitk_resid_norm(const float *part, int nsplit, int N, int M, EpiArgs ep) {
@@ -1151,7 +1151,7 @@ void launch_sum(int epi, const float *ws, int S, int N, int M, const EpiArgs &ep
 void launch_splitk_sum(int epi, const float *ws, int S, int N, int M, const EpiArgs &ep, int pair_mode,
                        hipStream_t s) {
     if (epi == EPI_RESID && ep.nrm_g && ep.nrm_done) {
-        if (N % 4 == 0)
+        if (N % 4 == 0 && ep.ldy % 4 == 0)
             launch(k_splitk_resid_norm<4>, dim3(M), dim3(SRN_T), 0, s, ws, S, N, M, ep);
         else
             launch(k_splitk_resid_norm<1>, dim3(M), dim3(SRN_T), 0, s, ws, S, N, M, ep);
