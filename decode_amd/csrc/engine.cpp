@@ -685,6 +685,25 @@ struct dec_ctx {
     bool prefill_mode = false; // run_tokens is running one sequence's consecutive positions
     int prefill_p0 = 0;        // ... starting at this position
     bool flash_prefill = true; // DECODE_PREFILL_ATTN=splitk selects the split-K kernel instead
+    // Prefill lanes: consecutive ubatches of a prefill call alternate between
+    // two sets of activation buffers, each with its own stream, so that one
+    // ubatch's kernels fill the compute units the other's leave idle.  Lane 0
+    // is the context's own buffers and stream (the fields above while no
+    // prefill runs); ubatch u+1 attends to ubatch u's keys, so its attention
+    // at layer l waits for u's K/V of layer l (kv_ev of u's lane).
+    struct Lane {
+        hipStream_t s = nullptr;
+        float *x = nullptr, *q = nullptr, *part = nullptr, *ml = nullptr, *ssp = nullptr, *gws = nullptr;
+        uint16_t *qh = nullptr, *ql = nullptr, *xn = nullptr, *xn_lo = nullptr, *o = nullptr, *o_lo = nullptr,
+                 *h = nullptr, *h_lo = nullptr;
+        std::vector<hipEvent_t> kv_ev;   // per layer: this lane's K/V of the layer are in the cache
+        hipEvent_t done = nullptr;       // recorded when a lane hands over to the other
+    };
+    Lane lanes[2];
+    bool lanes_ok = false;     // lane 1 allocated (multi-ubatch prefill on an f16 / f32 cache)
+    int lane_cur = 0;          // lane whose buffers the fields above hold
+    int lane_wait = -1;        // lane whose K/V events the running ubatch's attention waits for
+                               // (-1: lanes unused; -2: the call's first ubatch, which only records)
     bool registered = false;   // counted in m->n_ctx_refs
     dec_stats st{};
     // timing probe: a pool of event pairs, each stamped by the kernels of one
@@ -715,6 +734,47 @@ struct dec_ctx {
 thread_local LaunchProbe g_launch_probe;
 
 static int step_settle(dec_ctx *c);
+
+// Points the context's buffer fields and stream at lane k.
+static void use_lane(dec_ctx *c, int k) {
+    const dec_ctx::Lane &L = c->lanes[k];
+    c->s = L.s;
+    c->x = L.x;
+    c->q = L.q;
+    c->part = L.part;
+    c->ml = L.ml;
+    c->ssp = L.ssp;
+    c->gws = L.gws;
+    c->qh = L.qh;
+    c->ql = L.ql;
+    c->xn = L.xn;
+    c->xn_lo = L.xn_lo;
+    c->o = L.o;
+    c->o_lo = L.o_lo;
+    c->h = L.h;
+    c->h_lo = L.h_lo;
+    c->lane_cur = k;
+}
+
+// The lane's view of the fields (lane 0 taken from the context at creation).
+static void save_lane(dec_ctx *c, int k) {
+    dec_ctx::Lane &L = c->lanes[k];
+    L.s = c->s;
+    L.x = c->x;
+    L.q = c->q;
+    L.part = c->part;
+    L.ml = c->ml;
+    L.ssp = c->ssp;
+    L.gws = c->gws;
+    L.qh = c->qh;
+    L.ql = c->ql;
+    L.xn = c->xn;
+    L.xn_lo = c->xn_lo;
+    L.o = c->o;
+    L.o_lo = c->o_lo;
+    L.h = c->h;
+    L.h_lo = c->h_lo;
+}
 
 enum { SEG_ALL = 0, SEG_PRE = 1, SEG_MID = 2, SEG_POST = 3 };
 static bool emit(const dec_ctx *c) { return c->seg_req == SEG_ALL || c->seg_req == c->seg_cur; }
@@ -972,6 +1032,40 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
              (c->gws || !c->gws_bytes) &&
              c->amax && c->dev_step;
     }
+    if (ok) save_lane(c, 0);
+    // lane 1 (prefill calls of several ubatches; an f16 / f32 cache: the Q8_0
+    // cache's staging rows are one buffer for the context)
+    const char *lv = getenv("DECODE_PREFILL_LANES");
+    if (ok && n_batch > n_ubatch && !q8 && !(lv && strcmp(lv, "1") == 0)) {
+        dec_ctx::Lane &L1 = c->lanes[1];
+        const size_t Tu = (size_t)n_ubatch;
+        L1.x = (float *)c->mem.get(Tu * d * 4);
+        L1.xn = (uint16_t *)c->mem.get(Tu * d * 2);
+        L1.xn_lo = (uint16_t *)c->mem.get(Tu * d * 2);
+        L1.ssp = (float *)c->mem.get(Tu * SS_SLOTS * 4);
+        L1.q = (float *)c->mem.get(Tu * qd * 4);
+        L1.qh = (uint16_t *)c->mem.get(Tu * qd * 2);
+        L1.ql = (uint16_t *)c->mem.get(Tu * qd * 2);
+        L1.o = (uint16_t *)c->mem.get(Tu * qd * 2);
+        L1.o_lo = (uint16_t *)c->mem.get(Tu * qd * 2);
+        L1.h = (uint16_t *)c->mem.get(Tu * Fp * 2);
+        L1.h_lo = (uint16_t *)c->mem.get(Tu * Fp * 2);
+        L1.part = (float *)c->mem.get(Tu * h.n_head * c->max_chunks * hd * 4);
+        L1.ml = (float *)c->mem.get(Tu * h.n_head * c->max_chunks * 2 * 4);
+        L1.gws = c->gws_bytes ? (float *)c->mem.get(c->gws_bytes) : nullptr;
+        bool lok = L1.x && L1.xn && L1.xn_lo && L1.ssp && L1.q && L1.qh && L1.ql && L1.o && L1.o_lo && L1.h &&
+                   L1.h_lo && L1.part && L1.ml && (L1.gws || !c->gws_bytes);
+        if (lok) HIP_OK(hipStreamCreateWithFlags(&L1.s, hipStreamNonBlocking), lok = false);
+        for (int k = 0; lok && k < 2; k++) {
+            dec_ctx::Lane &L = c->lanes[k];
+            L.kv_ev.assign(h.n_layer, nullptr);
+            for (int l = 0; lok && l < h.n_layer; l++)
+                HIP_OK(hipEventCreateWithFlags(&L.kv_ev[l], hipEventDisableTiming), lok = false);
+            if (lok) HIP_OK(hipEventCreateWithFlags(&L.done, hipEventDisableTiming), lok = false);
+        }
+        c->lanes_ok = lok;
+        if (!lok) LOGW("dec_ctx_new: no second prefill lane; ubatches run one after another");
+    }
     if (ok) HIP_OK(hipHostMalloc((void **)&c->host_step, (size_t)c->step_cap * 3 * 4, 0), ok = false);
     if (ok) HIP_OK(hipEventCreateWithFlags(&c->staged, hipEventDisableTiming), ok = false);
     for (int i = 0; ok && i < dec_ctx::NPROBE; i++) {
@@ -1006,6 +1100,13 @@ extern "C" void dec_ctx_free(dec_ctx *c) {
         if (c->pr_e1[i]) (void)hipEventDestroy(c->pr_e1[i]);
     }
 
+    if (c->lanes[1].s) (void)hipStreamSynchronize(c->lanes[1].s);
+    for (dec_ctx::Lane &L : c->lanes) {
+        for (hipEvent_t e : L.kv_ev)
+            if (e) (void)hipEventDestroy(e);
+        if (L.done) (void)hipEventDestroy(L.done);
+    }
+    if (c->lanes[1].s) (void)hipStreamDestroy(c->lanes[1].s);
     if (c->host_step) (void)hipHostFree(c->host_step);
     c->mem.release();
     if (c->own_stream) (void)hipStreamDestroy(c->s);
@@ -1120,6 +1221,14 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                 launch_kv_quant(c->kv[l], ti, T, s);
                 return true;
             });
+        // prefill lanes: this ubatch's K/V of layer l are in the cache; the
+        // previous ubatch's must be before this one attends
+        if (ok && c->lane_wait >= 0) {
+            HIP_OK(hipEventRecord(c->lanes[c->lane_cur].kv_ev[l], s), ok = false);
+            if (ok) HIP_OK(hipStreamWaitEvent(s, c->lanes[c->lane_wait].kv_ev[l], 0), ok = false);
+        } else if (ok && c->lane_wait == -2) {
+            HIP_OK(hipEventRecord(c->lanes[c->lane_cur].kv_ev[l], s), ok = false);
+        }
         AttnArgs at;
         at.q = c->q;
         at.qh = c->qh;
@@ -1274,10 +1383,29 @@ extern "C" int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int
     if (!stage_step(c, n)) return -3;
     c->st.n_prefill_calls++;
     reset_outputs(c, 0);
-    for (int u = 0; u < n; u += c->n_ubatch) {
+    // ubatches alternate between the two lanes when there are several (and
+    // no timing probe is set: a probe times kernels on the context's stream)
+    const int n_ub = (n + c->n_ubatch - 1) / c->n_ubatch;
+    const bool lanes = c->lanes_ok && n_ub > 1 && c->pr_role < 0;
+    bool lane1_used = false;
+    if (lanes) {
+        HIP_OK(hipEventRecord(c->lanes[0].done, c->lanes[0].s), return -3);
+        HIP_OK(hipStreamWaitEvent(c->lanes[1].s, c->lanes[0].done, 0), return -3);
+    }
+    // back to lane 0, whose stream then waits for lane 1's work
+    auto join = [&]() -> bool {
+        if (!lanes) return true;
+        use_lane(c, 0);
+        c->lane_wait = -1;
+        if (!lane1_used) return true;
+        HIP_OK(hipEventRecord(c->lanes[1].done, c->lanes[1].s), return false);
+        HIP_OK(hipStreamWaitEvent(c->lanes[0].s, c->lanes[1].done, 0), return false);
+        return true;
+    };
+    for (int u = 0, ub = 0; u < n; u += c->n_ubatch, ub++) {
         if (u > 0 && c->p.abort_cb && c->p.abort_cb(c->p.abort_ud)) {
             LOGW("dec_prefill: aborted after %d of %d tokens", u, n);
-            return 2;
+            return join() ? 2 : -3;
         }
         const int T = n - u < c->n_ubatch ? n - u : c->n_ubatch;
         const bool last = u + T == n;
@@ -1288,16 +1416,24 @@ extern "C" int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int
             row0 = T - 1;
             n_rows = 1;
         }
+        if (lanes) {
+            use_lane(c, ub & 1);
+            lane1_used |= (ub & 1) == 1;
+            c->lane_wait = ub == 0 ? -2 : (ub & 1) ^ 1;   // -2: record only
+        }
         c->prefill_mode = true;
         c->prefill_p0 = p0 + u;
         const bool ok = run_tokens(c, u, T, row0, n_rows, output_all ? u : 0);
         c->prefill_mode = false;
-        if (!ok) return -3;
+        if (!ok) {
+            (void)join();
+            return -3;
+        }
         c->pos_max[seq] = p0 + u + T - 1;
         c->st.n_ubatches++;
         reset_outputs(c, output_all ? u + T : (last ? 1 : 0));
     }
-    return 0;
+    return join() ? 0 : -3;
 }
 
 // Captures the decode step for n tokens (segment `seg` of it) as a graph.

@@ -1,0 +1,99 @@
+"""Prefill lanes: the ubatches of one prefill call alternate between two sets
+of activation buffers and two streams, ubatch u+1's attention at each layer
+waiting for ubatch u's K/V of that layer.  Each ubatch's arithmetic is the
+same as with one lane (DECODE_PREFILL_LANES=1), so every logits row is
+bitwise equal; rows also meet the oracle, and the decode steps that follow
+(on the context's own stream) see every ubatch's cache rows.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import assert_logits_close, small_hp
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dec():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_amd
+    decode_amd.lib()
+    return decode_amd
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.load("f64")
+    return oracle
+
+
+def _run(dec, gm, prompt, feed, n_ubatch, lanes, split_at=None):
+    key = "DECODE_PREFILL_LANES"
+    saved = os.environ.get(key)
+    try:
+        if lanes:
+            os.environ.pop(key, None)
+        else:
+            os.environ[key] = "1"
+        ctx = dec.Context(gm, n_ctx=1024, n_batch=len(prompt), n_ubatch=n_ubatch)
+    finally:
+        if saved is None:
+            os.environ.pop(key, None)
+        else:
+            os.environ[key] = saved
+    rows = []
+    parts = [prompt] if split_at is None else [prompt[:split_at], prompt[split_at:]]
+    for part in parts:
+        assert ctx.prefill(part, 0, output_all=True) == 0
+        rows += [ctx.logits(i) for i in range(len(part))]
+    steps = []
+    for t in feed:
+        assert ctx.decode([int(t)]) == 0
+        steps.append(ctx.logits(0))
+    del ctx
+    return np.stack(rows), np.stack(steps)
+
+
+@pytest.mark.parametrize("wtype", [synth.Q4_0, synth.Q8_0])
+def test_lanes_bitwise_equal_one_lane_and_match_oracle(dec, orc, wtype):
+    hp = small_hp(wtype, synth.F16, n_layer=3, n_embd=512, n_head=8, n_head_kv=2, n_ff=1024, n_vocab=1024)
+    w = synth.weights_numpy(hp, 1410 + wtype, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 600, 1411)           # ubatches 128 x 4 and a ragged 88
+    feed = synth.prompt(hp["n_vocab"], 3, 1412)
+    gm = dec.Model(hp, w)
+    one = _run(dec, gm, prompt, feed, 128, lanes=False)
+    two = _run(dec, gm, prompt, feed, 128, lanes=True)
+    assert np.array_equal(one[0], two[0])
+    assert np.array_equal(one[1], two[1])
+    # the oracle at the last row of each ubatch and at the decode steps
+    oc = orc.Context(orc.Model(hp, w), 1, 1024)
+    want = {127, 255, 383, 511, 599}
+    for i, t in enumerate(prompt):
+        r = oc.eval(0, int(t))
+        if i in want:
+            assert_logits_close(two[0][i], r, f"prefill row {i}")
+    for k, t in enumerate(feed):
+        assert_logits_close(two[1][k], oc.eval(0, int(t)), f"decode step {k}")
+
+
+def test_lanes_over_two_prefill_calls(dec):
+    # a second prefill call continues the sequence: its first ubatch attends
+    # to the first call's rows written from both lanes
+    hp = small_hp(synth.Q4_0, synth.F16, n_layer=2, n_embd=256, n_head=4, n_head_kv=2, n_vocab=640)
+    w = synth.weights_numpy(hp, 1420, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 400, 1421)
+    feed = synth.prompt(hp["n_vocab"], 2, 1422)
+    gm = dec.Model(hp, w)
+    one = _run(dec, gm, prompt, feed, 64, lanes=False, split_at=230)
+    two = _run(dec, gm, prompt, feed, 64, lanes=True, split_at=230)
+    whole = _run(dec, gm, prompt, feed, 64, lanes=True)
+    assert np.array_equal(one[0], two[0])
+    assert np.array_equal(one[1], two[1])
+    # splitting the call moves the ubatch boundaries, so rows agree to rounding
+    assert np.abs(two[0] - whole[0]).max() <= 1e-3 * np.abs(whole[0]).max()
