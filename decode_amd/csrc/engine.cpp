@@ -685,10 +685,10 @@ struct dec_ctx {
     bool prefill_mode = false; // run_tokens is running one sequence's consecutive positions
     int prefill_p0 = 0;        // ... starting at this position
     bool flash_prefill = true; // DECODE_PREFILL_ATTN=splitk selects the split-K kernel instead
-    // Prefill lanes: consecutive ubatches of a prefill call alternate between
-    // two sets of activation buffers, each with its own stream, so that one
-    // ubatch's kernels fill the compute units the other's leave idle.  Lane 0
-    // is the context's own buffers and stream (the fields above while no
+    // Prefill lanes: consecutive ubatches of a prefill call go round
+    // n_lanes sets of activation buffers, each with its own stream, so that
+    // one ubatch's kernels fill the compute units another's leave idle.  Lane
+    // 0 is the context's own buffers and stream (the fields above while no
     // prefill runs); ubatch u+1 attends to ubatch u's keys, so its attention
     // at layer l waits for u's K/V of layer l (kv_ev of u's lane).
     struct Lane {
@@ -699,8 +699,9 @@ struct dec_ctx {
         std::vector<hipEvent_t> kv_ev;   // per layer: this lane's K/V of the layer are in the cache
         hipEvent_t done = nullptr;       // recorded when a lane hands over to the other
     };
-    Lane lanes[2];
-    bool lanes_ok = false;     // lane 1 allocated (multi-ubatch prefill on an f16 / f32 cache)
+    static constexpr int MAX_LANES = 4;
+    Lane lanes[MAX_LANES];
+    int n_lanes = 1;           // lanes allocated (more than 1: multi-ubatch prefill on an f16 / f32 cache)
     int lane_cur = 0;          // lane whose buffers the fields above hold
     int lane_wait = -1;        // lane whose K/V events the running ubatch's attention waits for
                                // (-1: lanes unused; -2: the call's first ubatch, which only records)
@@ -1033,37 +1034,47 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
              c->amax && c->dev_step;
     }
     if (ok) save_lane(c, 0);
-    // lane 1 (prefill calls of several ubatches; an f16 / f32 cache: the Q8_0
-    // cache's staging rows are one buffer for the context)
-    const char *lv = getenv("DECODE_PREFILL_LANES");
-    if (ok && n_batch > n_ubatch && !q8 && !(lv && strcmp(lv, "1") == 0)) {
-        dec_ctx::Lane &L1 = c->lanes[1];
-        const size_t Tu = (size_t)n_ubatch;
-        L1.x = (float *)c->mem.get(Tu * d * 4);
-        L1.xn = (uint16_t *)c->mem.get(Tu * d * 2);
-        L1.xn_lo = (uint16_t *)c->mem.get(Tu * d * 2);
-        L1.ssp = (float *)c->mem.get(Tu * SS_SLOTS * 4);
-        L1.q = (float *)c->mem.get(Tu * qd * 4);
-        L1.qh = (uint16_t *)c->mem.get(Tu * qd * 2);
-        L1.ql = (uint16_t *)c->mem.get(Tu * qd * 2);
-        L1.o = (uint16_t *)c->mem.get(Tu * qd * 2);
-        L1.o_lo = (uint16_t *)c->mem.get(Tu * qd * 2);
-        L1.h = (uint16_t *)c->mem.get(Tu * Fp * 2);
-        L1.h_lo = (uint16_t *)c->mem.get(Tu * Fp * 2);
-        L1.part = (float *)c->mem.get(Tu * h.n_head * c->max_chunks * hd * 4);
-        L1.ml = (float *)c->mem.get(Tu * h.n_head * c->max_chunks * 2 * 4);
-        L1.gws = c->gws_bytes ? (float *)c->mem.get(c->gws_bytes) : nullptr;
-        bool lok = L1.x && L1.xn && L1.xn_lo && L1.ssp && L1.q && L1.qh && L1.ql && L1.o && L1.o_lo && L1.h &&
-                   L1.h_lo && L1.part && L1.ml && (L1.gws || !c->gws_bytes);
-        if (lok) HIP_OK(hipStreamCreateWithFlags(&L1.s, hipStreamNonBlocking), lok = false);
-        for (int k = 0; lok && k < 2; k++) {
+    // lanes 1.. (prefill calls of several ubatches; an f16 / f32 cache: the
+    // Q8_0 cache's staging rows are one buffer for the context);
+    // DECODE_PREFILL_LANES = 1..4 lanes, default 2
+    int want = 2;
+    if (const char *lv = getenv("DECODE_PREFILL_LANES")) {
+        const int v = atoi(lv);
+        want = v < 1 ? 1 : v > dec_ctx::MAX_LANES ? dec_ctx::MAX_LANES : v;
+    }
+    if (ok && n_batch > n_ubatch && !q8 && want > 1) {
+        bool lok = true;
+        int k = 1;
+        for (; lok && k < want; k++) {
             dec_ctx::Lane &L = c->lanes[k];
+            const size_t Tu = (size_t)n_ubatch;
+            L.x = (float *)c->mem.get(Tu * d * 4);
+            L.xn = (uint16_t *)c->mem.get(Tu * d * 2);
+            L.xn_lo = (uint16_t *)c->mem.get(Tu * d * 2);
+            L.ssp = (float *)c->mem.get(Tu * SS_SLOTS * 4);
+            L.q = (float *)c->mem.get(Tu * qd * 4);
+            L.qh = (uint16_t *)c->mem.get(Tu * qd * 2);
+            L.ql = (uint16_t *)c->mem.get(Tu * qd * 2);
+            L.o = (uint16_t *)c->mem.get(Tu * qd * 2);
+            L.o_lo = (uint16_t *)c->mem.get(Tu * qd * 2);
+            L.h = (uint16_t *)c->mem.get(Tu * Fp * 2);
+            L.h_lo = (uint16_t *)c->mem.get(Tu * Fp * 2);
+            L.part = (float *)c->mem.get(Tu * h.n_head * c->max_chunks * hd * 4);
+            L.ml = (float *)c->mem.get(Tu * h.n_head * c->max_chunks * 2 * 4);
+            L.gws = c->gws_bytes ? (float *)c->mem.get(c->gws_bytes) : nullptr;
+            lok = L.x && L.xn && L.xn_lo && L.ssp && L.q && L.qh && L.ql && L.o && L.o_lo && L.h && L.h_lo &&
+                  L.part && L.ml && (L.gws || !c->gws_bytes);
+            if (lok) HIP_OK(hipStreamCreateWithFlags(&L.s, hipStreamNonBlocking), lok = false);
+        }
+        const int nl = lok ? want : k - 1;               // lanes whose buffers and stream exist
+        for (int j = 0; lok && j < nl; j++) {
+            dec_ctx::Lane &L = c->lanes[j];
             L.kv_ev.assign(h.n_layer, nullptr);
             for (int l = 0; lok && l < h.n_layer; l++)
                 HIP_OK(hipEventCreateWithFlags(&L.kv_ev[l], hipEventDisableTiming), lok = false);
             if (lok) HIP_OK(hipEventCreateWithFlags(&L.done, hipEventDisableTiming), lok = false);
         }
-        c->lanes_ok = lok;
+        c->n_lanes = lok ? want : 1;
         if (!lok) LOGW("dec_ctx_new: no second prefill lane; ubatches run one after another");
     }
     if (ok) HIP_OK(hipHostMalloc((void **)&c->host_step, (size_t)c->step_cap * 3 * 4, 0), ok = false);
@@ -1100,13 +1111,15 @@ extern "C" void dec_ctx_free(dec_ctx *c) {
         if (c->pr_e1[i]) (void)hipEventDestroy(c->pr_e1[i]);
     }
 
-    if (c->lanes[1].s) (void)hipStreamSynchronize(c->lanes[1].s);
+    for (int k = 1; k < dec_ctx::MAX_LANES; k++)
+        if (c->lanes[k].s) (void)hipStreamSynchronize(c->lanes[k].s);
     for (dec_ctx::Lane &L : c->lanes) {
         for (hipEvent_t e : L.kv_ev)
             if (e) (void)hipEventDestroy(e);
         if (L.done) (void)hipEventDestroy(L.done);
     }
-    if (c->lanes[1].s) (void)hipStreamDestroy(c->lanes[1].s);
+    for (int k = 1; k < dec_ctx::MAX_LANES; k++)
+        if (c->lanes[k].s) (void)hipStreamDestroy(c->lanes[k].s);
     if (c->host_step) (void)hipHostFree(c->host_step);
     c->mem.release();
     if (c->own_stream) (void)hipStreamDestroy(c->s);
@@ -1383,23 +1396,23 @@ extern "C" int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int
     if (!stage_step(c, n)) return -3;
     c->st.n_prefill_calls++;
     reset_outputs(c, 0);
-    // ubatches alternate between the two lanes when there are several (and
-    // no timing probe is set: a probe times kernels on the context's stream)
+    // ubatches go round the lanes when there are several (and no timing
+    // probe is set: a probe times kernels on the context's stream)
     const int n_ub = (n + c->n_ubatch - 1) / c->n_ubatch;
-    const bool lanes = c->lanes_ok && n_ub > 1 && c->pr_role < 0;
-    bool lane1_used = false;
-    if (lanes) {
+    const int nl = c->pr_role < 0 ? std::min(c->n_lanes, n_ub) : 1;
+    if (nl > 1) {
         HIP_OK(hipEventRecord(c->lanes[0].done, c->lanes[0].s), return -3);
-        HIP_OK(hipStreamWaitEvent(c->lanes[1].s, c->lanes[0].done, 0), return -3);
+        for (int k = 1; k < nl; k++) HIP_OK(hipStreamWaitEvent(c->lanes[k].s, c->lanes[0].done, 0), return -3);
     }
-    // back to lane 0, whose stream then waits for lane 1's work
+    // back to lane 0, whose stream then waits for the other lanes' work
     auto join = [&]() -> bool {
-        if (!lanes) return true;
+        if (nl == 1) return true;
         use_lane(c, 0);
         c->lane_wait = -1;
-        if (!lane1_used) return true;
-        HIP_OK(hipEventRecord(c->lanes[1].done, c->lanes[1].s), return false);
-        HIP_OK(hipStreamWaitEvent(c->lanes[0].s, c->lanes[1].done, 0), return false);
+        for (int k = 1; k < nl; k++) {
+            HIP_OK(hipEventRecord(c->lanes[k].done, c->lanes[k].s), return false);
+            HIP_OK(hipStreamWaitEvent(c->lanes[0].s, c->lanes[k].done, 0), return false);
+        }
         return true;
     };
     for (int u = 0, ub = 0; u < n; u += c->n_ubatch, ub++) {
@@ -1416,10 +1429,9 @@ extern "C" int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int
             row0 = T - 1;
             n_rows = 1;
         }
-        if (lanes) {
-            use_lane(c, ub & 1);
-            lane1_used |= (ub & 1) == 1;
-            c->lane_wait = ub == 0 ? -2 : (ub & 1) ^ 1;   // -2: record only
+        if (nl > 1) {
+            use_lane(c, ub % nl);
+            c->lane_wait = ub == 0 ? -2 : (ub - 1) % nl;   // -2: record only
         }
         c->prefill_mode = true;
         c->prefill_p0 = p0 + u;

@@ -204,6 +204,12 @@ typedef struct {
  *                         the wide form is faster)
  *   DECODE_PREFILL_ATTN=splitk  prefill attention through the split-K
  *                         decode kernels instead of the flash kernel
+ *   DECODE_PREFILL_LANES=n  buffer sets and streams the ubatches of a prefill
+ *                         call go round (1..4, default 2; 1 runs them one
+ *                         after another; a Q8_0 cache always takes 1); each
+ *                         extra lane holds one ubatch's activations and
+ *                         GEMM workspace.  Results are bitwise the same for
+ *                         every n
  *   DECODE_STEP_KERNEL=1  see dec_set_step_kernel */
 dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *p);
 

@@ -1,9 +1,9 @@
-"""Prefill lanes: the ubatches of one prefill call alternate between two sets
-of activation buffers and two streams, ubatch u+1's attention at each layer
-waiting for ubatch u's K/V of that layer.  Each ubatch's arithmetic is the
-same as with one lane (DECODE_PREFILL_LANES=1), so every logits row is
-bitwise equal; rows also meet the oracle, and the decode steps that follow
-(on the context's own stream) see every ubatch's cache rows.
+"""Prefill lanes: the ubatches of one prefill call go round several sets of
+activation buffers and streams (DECODE_PREFILL_LANES, default 2), ubatch
+u+1's attention at each layer waiting for ubatch u's K/V of that layer.
+Each ubatch's arithmetic is the same as with one lane, so every logits row
+is bitwise equal; rows also meet the oracle, and the decode steps that
+follow (on the context's own stream) see every ubatch's cache rows.
 """
 import os
 
@@ -37,10 +37,7 @@ def _run(dec, gm, prompt, feed, n_ubatch, lanes, split_at=None):
     key = "DECODE_PREFILL_LANES"
     saved = os.environ.get(key)
     try:
-        if lanes:
-            os.environ.pop(key, None)
-        else:
-            os.environ[key] = "1"
+        os.environ[key] = str(lanes)
         ctx = dec.Context(gm, n_ctx=1024, n_batch=len(prompt), n_ubatch=n_ubatch)
     finally:
         if saved is None:
@@ -67,8 +64,11 @@ def test_lanes_bitwise_equal_one_lane_and_match_oracle(dec, orc, wtype):
     prompt = synth.prompt(hp["n_vocab"], 600, 1411)           # ubatches 128 x 4 and a ragged 88
     feed = synth.prompt(hp["n_vocab"], 3, 1412)
     gm = dec.Model(hp, w)
-    one = _run(dec, gm, prompt, feed, 128, lanes=False)
-    two = _run(dec, gm, prompt, feed, 128, lanes=True)
+    one = _run(dec, gm, prompt, feed, 128, lanes=1)
+    two = _run(dec, gm, prompt, feed, 128, lanes=2)
+    for k in (3, 4):
+        more = _run(dec, gm, prompt, feed, 128, lanes=k)
+        assert np.array_equal(one[0], more[0]) and np.array_equal(one[1], more[1]), f"{k} lanes"
     assert np.array_equal(one[0], two[0])
     assert np.array_equal(one[1], two[1])
     # the oracle at the last row of each ubatch and at the decode steps
@@ -90,9 +90,9 @@ def test_lanes_over_two_prefill_calls(dec):
     prompt = synth.prompt(hp["n_vocab"], 400, 1421)
     feed = synth.prompt(hp["n_vocab"], 2, 1422)
     gm = dec.Model(hp, w)
-    one = _run(dec, gm, prompt, feed, 64, lanes=False, split_at=230)
-    two = _run(dec, gm, prompt, feed, 64, lanes=True, split_at=230)
-    whole = _run(dec, gm, prompt, feed, 64, lanes=True)
+    one = _run(dec, gm, prompt, feed, 64, lanes=1, split_at=230)
+    two = _run(dec, gm, prompt, feed, 64, lanes=2, split_at=230)
+    whole = _run(dec, gm, prompt, feed, 64, lanes=2)
     assert np.array_equal(one[0], two[0])
     assert np.array_equal(one[1], two[1])
     # splitting the call moves the ubatch boundaries, so rows agree to rounding
