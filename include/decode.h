@@ -16,9 +16,14 @@
  *  - Host arrays passed in are read during the call only; the caller keeps
  *    ownership.  Pointers returned stay valid until the next prefill /
  *    decode / free on the same context.
- *  - All device work runs on one HIP stream: the one given at creation
+ *  - Device work runs on one HIP stream: the one given at creation
  *    (hip_stream, a hipStream_t); a context created with NULL makes and owns
  *    a non-blocking stream of its own (decode graphs are captured on it).
+ *    A prefill call of several ubatches also runs some of them on streams
+ *    the context owns (DECODE_PREFILL_LANES below); those first wait for the
+ *    context's stream, and before the call returns the context's stream is
+ *    made to wait for them, so work queued on it afterwards sees the whole
+ *    call.
  *  - Calls on one context must not overlap (no internal locking).
  *  - Errors are reported through return values (documented per call) and
  *    a message to the log callback; nothing aborts the process.
