@@ -999,25 +999,22 @@ bool dw_shape(const QMat &W, int M, int ldx) {
            (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * row_bytes < ((size_t)1 << 31);
 }
 
-// Its K split S (1..8): the blocks are the (feature tile, split) units times
-// the token tiles, units spread evenly over the 8 XCDs, and an XCD's share
-// must fit one block per compute unit.  Splits take whole periods (4 K
-// blocks; Q4_K octets) and at least 16 K blocks; among the S that fit, the
-// one with the shortest longest split wins (the fewest splits on a tie).
+// Its K split S (1, 2, 4 or 8): the blocks are the (feature tile, split)
+// units times the token tiles, units spread evenly over the 8 XCDs, and an
+// XCD's share must fit one block per compute unit; splits take whole periods
+// (4 K blocks; Q4_K octets) and at least 16 K blocks.  The largest such S
+// wins.  (Uneven splits that fill more compute units, e.g. 5 for the 8B QKV
+// matrix, gain alone but lose once two prefill lanes share the chip: their
+// extra fp32 partials then cost more than the idle units.)
 int dw_split(const QMat &W, int M) {
     const int NT = W.N / gemm_dw_tile_features(), mtiles = (M + 127) / 128;
     const int nb = W.K / 32;
     const int unit = W.wtype == T_Q4_K ? 8 : gemm_dw_super_blocks();
     const int P = nb / unit;
     const int per_xcd = g_gemm_cu / 8;
-    int best = 1, best_len = P;
-    for (int S = 2; S <= 8; S++) {
-        const int len = (P + S - 1) / S;           // periods of the longest split
-        if ((NT * S + 7) / 8 * mtiles <= per_xcd && P >= S && nb / S >= 16 && len < best_len) {
-            best = S;
-            best_len = len;
-        }
-    }
+    int best = 1;
+    for (int S = 2; S <= 8; S *= 2)
+        if ((NT * S + 7) / 8 * mtiles <= per_xcd && P % S == 0 && nb / S >= 16) best = S;
     return best;
 }
 
