@@ -1403,12 +1403,14 @@ extern "C" int32_t dec_prefill(dec_ctx *c, const int32_t *tokens, int32_t n, int
     if (nl > 1) {
         HIP_OK(hipEventRecord(c->lanes[0].done, c->lanes[0].s), return -3);
         for (int k = 1; k < nl; k++) HIP_OK(hipStreamWaitEvent(c->lanes[k].s, c->lanes[0].done, 0), return -3);
+        gemm_set_split_cap(4);    // the other lane fills what a smaller K split leaves idle
     }
     // back to lane 0, whose stream then waits for the other lanes' work
     auto join = [&]() -> bool {
         if (nl == 1) return true;
         use_lane(c, 0);
         c->lane_wait = -1;
+        gemm_set_split_cap(8);
         for (int k = 1; k < nl; k++) {
             HIP_OK(hipEventRecord(c->lanes[k].done, c->lanes[k].s), return false);
             HIP_OK(hipStreamWaitEvent(c->lanes[0].s, c->lanes[k].done, 0), return false);

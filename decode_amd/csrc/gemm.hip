@@ -999,13 +999,16 @@ bool dw_shape(const QMat &W, int M, int ldx) {
            (size_t)M * ldx * 2 < ((size_t)1 << 31) && (size_t)W.N * row_bytes < ((size_t)1 << 31);
 }
 
-// Its K split S (1, 2, 4 or 8): the blocks are the (feature tile, split)
+thread_local int g_dw_split_cap = 8;   // gemm_set_split_cap
+
+// Its K split S (1, 2, 4 or 8, at most g_dw_split_cap): the blocks are the (feature tile, split)
 // units times the token tiles, units spread evenly over the 8 XCDs, and an
 // XCD's share must fit one block per compute unit; splits take whole periods
 // (4 K blocks; Q4_K octets) and at least 16 K blocks.  The largest such S
 // wins.  (Uneven splits that fill more compute units, e.g. 5 for the 8B QKV
 // matrix, gain alone but lose once two prefill lanes share the chip: their
-// extra fp32 partials then cost more than the idle units.)
+// extra fp32 partials then cost more than the idle units.  For the same
+// reason the engine caps S at 4 while lanes run.)
 int dw_split(const QMat &W, int M) {
     const int NT = W.N / gemm_dw_tile_features(), mtiles = (M + 127) / 128;
     const int nb = W.K / 32;
@@ -1013,7 +1016,7 @@ int dw_split(const QMat &W, int M) {
     const int P = nb / unit;
     const int per_xcd = g_gemm_cu / 8;
     int best = 1;
-    for (int S = 2; S <= 8; S *= 2)
+    for (int S = 2; S <= g_dw_split_cap; S *= 2)
         if ((NT * S + 7) / 8 * mtiles <= per_xcd && P % S == 0 && nb / S >= 16) best = S;
     return best;
 }
@@ -1076,6 +1079,8 @@ int dl_split(const QMat &W, int M) {
 }
 
 }  // namespace
+
+void gemm_set_split_cap(int cap) { g_dw_split_cap = cap >= 8 ? 8 : cap >= 4 ? 4 : cap >= 2 ? 2 : 1; }
 
 void gemm_set_num_cu(int n) {
     g_gemm_cu = n > 0 ? n : 256;

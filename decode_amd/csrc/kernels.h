@@ -207,6 +207,11 @@ void launch_splitk_sum(int epi, const float *ws, int S, int N, int M, const EpiA
                        hipStream_t s);
 // Number of compute units the GEMM grid is sized for (default 256).
 void gemm_set_num_cu(int n);
+// Largest K split of the wide GEMM form for launches from the calling thread
+// (1, 2, 4 or 8; default 8).  While two prefill ubatches share the chip the
+// other's blocks fill the compute units a smaller split leaves idle, and the
+// fewer fp32 partials cost less.
+void gemm_set_split_cap(int cap);
 
 // x[t] = dequantized row tok[t] of the embedding table (f32).
 void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, float *ss_out, hipStream_t s);

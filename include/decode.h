@@ -213,8 +213,10 @@ typedef struct {
  *                         call go round (1..4, default 2; 1 runs them one
  *                         after another; a Q8_0 cache always takes 1); each
  *                         extra lane holds one ubatch's activations and
- *                         GEMM workspace.  Results are bitwise the same for
- *                         every n
+ *                         GEMM workspace.  With n >= 2 the wide GEMM form
+ *                         splits K at most 4 ways (8 with one lane), so rows
+ *                         can differ from one lane's in rounding; they are
+ *                         bitwise the same for every n >= 2
  *   DECODE_STEP_KERNEL=1  see dec_set_step_kernel */
 dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *p);
 

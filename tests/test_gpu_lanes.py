@@ -1,9 +1,12 @@
 """Prefill lanes: the ubatches of one prefill call go round several sets of
 activation buffers and streams (DECODE_PREFILL_LANES, default 2), ubatch
 u+1's attention at each layer waiting for ubatch u's K/V of that layer.
-Each ubatch's arithmetic is the same as with one lane, so every logits row
-is bitwise equal; rows also meet the oracle, and the decode steps that
-follow (on the context's own stream) see every ubatch's cache rows.
+Each ubatch's arithmetic is the same for any number of lanes, except that
+with two or more the wide GEMM form splits K at most 4 ways (8 alone): where
+that split is the same, every logits row is bitwise equal across lane
+counts, and where it differs the rows agree to rounding.  Rows also meet the
+oracle, and the decode steps that follow (on the context's own stream) see
+every ubatch's cache rows.
 """
 import os
 
@@ -97,3 +100,27 @@ def test_lanes_over_two_prefill_calls(dec):
     assert np.array_equal(one[1], two[1])
     # splitting the call moves the ubatch boundaries, so rows agree to rounding
     assert np.abs(two[0] - whole[0]).max() <= 1e-3 * np.abs(whole[0]).max()
+
+
+def test_lanes_split_cap_rows_agree(dec, orc):
+    # the down matrix (K 4096, 512 rows) splits 8 ways with one lane and 4
+    # ways with lanes: rows agree to rounding, lanes 2 and 3 bitwise
+    hp = small_hp(synth.Q4_0, synth.F16, n_layer=2, n_embd=512, n_head=8, n_head_kv=2, n_ff=4096, n_vocab=1024)
+    w = synth.weights_numpy(hp, 1430, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 300, 1431)          # ubatches 128, 128, 44
+    feed = synth.prompt(hp["n_vocab"], 2, 1432)
+    gm = dec.Model(hp, w)
+    one = _run(dec, gm, prompt, feed, 128, lanes=1)
+    two = _run(dec, gm, prompt, feed, 128, lanes=2)
+    three = _run(dec, gm, prompt, feed, 128, lanes=3)
+    assert np.array_equal(two[0], three[0]) and np.array_equal(two[1], three[1])
+    scale = np.abs(one[0]).max()
+    assert scale > 1e-2
+    assert np.abs(one[0] - two[0]).max() <= 1e-4 * scale
+    assert np.abs(one[1] - two[1]).max() <= 1e-4 * scale
+    oc = orc.Context(orc.Model(hp, w), 1, 1024)
+    want = {127, 255, 299}
+    for i, t in enumerate(prompt):
+        r = oc.eval(0, int(t))
+        if i in want:
+            assert_logits_close(two[0][i], r, f"prefill row {i}")
