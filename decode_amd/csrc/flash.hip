@@ -25,6 +25,11 @@
 // lane's eight values r = 8s'..8s'+7 are keys 16s + 8(e>>2) + 4h + (e&3)
 // (h = lane/32, e = 0..7), so V^T is stored with key k at column
 // 16s + 8h + e of its 16-key group, and each lane reads 16 contiguous bytes.
+// A Q8_0 cache (Q8 = true): each element is code * scale, exact in fp32, and
+// the tiles hold it as f16 value + f16 remainder (converted while staging);
+// S^T and O^T take one more MFMA a step for the remainder (K remainder x Q
+// value, V remainder x P value; remainder x remainder, about 2^-22 of a
+// product, is left out).
 #include "common.h"
 #include "kernels.h"
 
@@ -57,13 +62,17 @@ DEV int vt_col(int k) {         // permuted column of key k (0..63) in V^T
     return (s << 4) | (h << 3) | e;
 }
 
-template <int HD>
+template <int HD, bool Q8>
 __global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
     constexpr int KS = HD / 16;     // k-steps of Q K^T
     constexpr int DT = HD / 32;     // 32-row dim tiles of O^T
-    // two buffers: tile kt is staged in buffer kt & 1, so one barrier per tile
-    // orders both its stores before the reads and the previous reads of that
-    // buffer (two tiles back) before its stores
+    constexpr int NB = HD / 32;     // Q8_0 blocks per cached row
+    // f16 cache: two buffers, tile kt staged in buffer kt & 1, so one barrier
+    // per tile orders both its stores before the reads and the previous reads
+    // of that buffer (two tiles back) before its stores.  Q8_0 cache: one
+    // tile at a time, [0] its values' f16 value parts and [1] their
+    // remainders (code * scale is exact in fp32 and is exactly value +
+    // remainder), with a barrier before the stores as well.
     __shared__ __attribute__((aligned(16))) f16 Ks[2][BKEY][HD + KPAD];
     __shared__ __attribute__((aligned(16))) f16 Vt[2][HD][BKEY + KPAD];
 
@@ -157,31 +166,109 @@ __global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
             }
         }
     };
+    // Q8_0 cache: K piece p (thread p < BKEY * NB) = block p % NB of key
+    // p / NB, 32 codes and their scale; V piece p (p < 32 * HD / 16) = 16
+    // dims, half p >> 5 of the blocks, of the keys 2 (p & 31) and 2 (p & 31) + 1
+    // (adjacent V^T columns, as above).  Rows past n_keys read as code 0,
+    // scale 0.
+    const size_t cell0 = ((size_t)seq * a.kv.n_kv + g) * a.kv.n_ctx;
+    const int8_t *Kc = (const int8_t *)a.kv.k + cell0 * HD;
+    const int8_t *Vc = (const int8_t *)a.kv.v + cell0 * HD;
+    const uint16_t *Ksc = a.kv.k_scale + cell0 * NB;
+    const uint16_t *Vsc = a.kv.v_scale + cell0 * NB;
+    constexpr int KPC = BKEY * NB, VPC = 32 * (HD / 16);
+    uint4 kq[2] = {}, vq[2] = {};
+    uint16_t ksc = 0, vsc[2] = {};
+    // (a sequence's cache rows of one KV head span n_ctx * HD < 2^31 bytes)
+    auto load_q8 = [&](int k0) {
+        if (tid < KPC) {
+            const int key = tid / NB, blk = tid % NB;
+            const bool ok = k0 + key < n_keys;
+            const uint32_t e = (uint32_t)(k0 + key) * HD + 32 * blk;
+            kq[0] = ok ? *(const uint4 *)(Kc + e) : make_uint4(0, 0, 0, 0);
+            kq[1] = ok ? *(const uint4 *)(Kc + e + 16) : make_uint4(0, 0, 0, 0);
+            ksc = ok ? Ksc[e / 32] : (uint16_t)0;
+        }
+        if (tid < VPC) {
+            const int key = 2 * (tid & 31), hb = tid >> 5;
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const bool ok = k0 + key + j < n_keys;
+                const uint32_t e = (uint32_t)(k0 + key + j) * HD + 16 * hb;
+                vq[j] = ok ? *(const uint4 *)(Vc + e) : make_uint4(0, 0, 0, 0);
+                vsc[j] = ok ? Vsc[e / 32] : (uint16_t)0;
+            }
+        }
+    };
+    // code * scale (exact in fp32) as f16 value + f16 remainder
+    auto dq_split = [](int code, float sc, f16 &hi, f16 &lo) __attribute__((always_inline)) {
+        const float v = (float)code * sc;
+        hi = (f16)v;
+        lo = (f16)(v - (float)hi);
+    };
+    auto store_q8 = [&]() {
+        if (tid < KPC) {
+            const int key = tid / NB, blk = tid % NB;
+            const float sc = f16_bits_to_f32(ksc);
+            const int8_t *c8 = (const int8_t *)kq;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                f16 hv[8], lv[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) dq_split(c8[8 * i + e], sc, hv[e], lv[e]);
+                *(uint4 *)&Ks[0][key][32 * blk + 8 * i] = *(const uint4 *)hv;
+                *(uint4 *)&Ks[1][key][32 * blk + 8 * i] = *(const uint4 *)lv;
+            }
+        }
+        if (tid < VPC) {
+            const int key = 2 * (tid & 31), hb = tid >> 5;
+            const int col = vt_col(key);                    // even; key + 1 sits at col + 1
+            const float s0 = f16_bits_to_f32(vsc[0]), s1 = f16_bits_to_f32(vsc[1]);
+            const int8_t *c0 = (const int8_t *)&vq[0], *c1 = (const int8_t *)&vq[1];
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                f16 h0, l0, h1, l1;
+                dq_split(c0[e], s0, h0, l0);
+                dq_split(c1[e], s1, h1, l1);
+                *(uint32_t *)&Vt[0][16 * hb + e][col] = h2_bits(h2{h0, h1});
+                *(uint32_t *)&Vt[1][16 * hb + e][col] = h2_bits(h2{l0, l1});
+            }
+        }
+    };
     // the wavefront's first query position: key tiles wholly at or below it
     // need no causal mask (nor do full query tiles)
     const int qpos_min = p0 + tw;
     const bool tile_full = tw + 31 < T;
-    load_tile(kbeg);
+    if constexpr (Q8) load_q8(kbeg);
+    else load_tile(kbeg);
     for (int kt = 0; kt < ntiles; kt++) {
-        const int k0 = kbeg + kt * BKEY, buf = kt & 1;
+        const int k0 = kbeg + kt * BKEY, buf = Q8 ? 0 : kt & 1;
         // ---- stage K and V^T of this tile; the next tile's loads then run
         // during this tile's arithmetic ----
+        if constexpr (Q8) {
+            if (kt > 0) __syncthreads();                    // every wavefront is done with the last tile
+            store_q8();
+        } else {
 #pragma unroll
-        for (int c = 0; c < CPT; c++) {
-            const int ch = tid + c * 256, key = ch / (HD / 8), d8 = ch % (HD / 8);
-            *(uint4 *)&Ks[buf][key][d8 * 8] = kr[c];
-        }
+            for (int c = 0; c < CPT; c++) {
+                const int ch = tid + c * 256, key = ch / (HD / 8), d8 = ch % (HD / 8);
+                *(uint4 *)&Ks[buf][key][d8 * 8] = kr[c];
+            }
 #pragma unroll
-        for (int c = 0; c < PPT; c++) {
-            const int pc = tid + c * 256, key = 2 * (pc & 31), d8 = pc >> 5;
-            const uint16_t *v0 = (const uint16_t *)&vr[c][0], *v1 = (const uint16_t *)&vr[c][1];
-            const int col = vt_col(key);                    // even; key + 1 sits at col + 1
+            for (int c = 0; c < PPT; c++) {
+                const int pc = tid + c * 256, key = 2 * (pc & 31), d8 = pc >> 5;
+                const uint16_t *v0 = (const uint16_t *)&vr[c][0], *v1 = (const uint16_t *)&vr[c][1];
+                const int col = vt_col(key);                // even; key + 1 sits at col + 1
 #pragma unroll
-            for (int e = 0; e < 8; e++)
-                *(uint32_t *)&Vt[buf][d8 * 8 + e][col] = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
+                for (int e = 0; e < 8; e++)
+                    *(uint32_t *)&Vt[buf][d8 * 8 + e][col] = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
+            }
         }
         __syncthreads();
-        if (kt + 1 < ntiles) load_tile(k0 + BKEY);
+        if (kt + 1 < ntiles) {
+            if constexpr (Q8) load_q8(k0 + BKEY);
+            else load_tile(k0 + BKEY);
+        }
 
         // ---- S^T = K Q^T for two 32-key halves ----
         f16x s[2];
@@ -194,6 +281,10 @@ __global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
                 const h8 kf = *(const h8 *)&Ks[buf][mt * 32 + (lane & 31)][16 * ks + 8 * (lane >> 5)];
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[mt], 0, 0, 0);
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, ql[ks], s[mt], 0, 0, 0);
+                if constexpr (Q8) {                         // K remainder x Q value (remainder x remainder dropped)
+                    const h8 kl = *(const h8 *)&Ks[1][mt * 32 + (lane & 31)][16 * ks + 8 * (lane >> 5)];
+                    s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl, qf[ks], s[mt], 0, 0, 0);
+                }
             }
         }
         // ---- causal mask + online softmax over this query column ----
@@ -252,6 +343,10 @@ __global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
                     const h8 vf = *(const h8 *)&Vt[buf][dt * 32 + (lane & 31)][16 * ss + 8 * (lane >> 5)];
                     acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[sh], acc[dt], 0, 0, 0);
                     acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pl[sh], acc[dt], 0, 0, 0);
+                    if constexpr (Q8) {                     // V remainder x P value
+                        const h8 vl = *(const h8 *)&Vt[1][dt * 32 + (lane & 31)][16 * ss + 8 * (lane >> 5)];
+                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vl, pf[sh], acc[dt], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -354,7 +449,8 @@ __global__ __launch_bounds__(256) void k_flash_merge(FlashArgs a, int tile_token
 
 bool launch_flash_prefill(const FlashArgs &a_in, hipStream_t s) {
     FlashArgs a = a_in;
-    if (a.kv.kvtype != T_F16 || a.T <= 0) return false;
+    if ((a.kv.kvtype != T_F16 && a.kv.kvtype != T_Q8_0) || a.T <= 0) return false;
+    const bool q8 = a.kv.kvtype == T_Q8_0;
     const int G = a.H / a.kv.n_kv;
     if (G != 1 && G != 2 && G != 4 && G != 8) return false;
     const int Gb = G < 4 ? G : 4, Tb = 4 / Gb;
@@ -375,11 +471,13 @@ bool launch_flash_prefill(const FlashArgs &a_in, hipStream_t s) {
     const dim3 grid(tiles * ns, a.kv.n_kv, G / Gb);
     switch (a.kv.hd) {
     case 64:
-        launch(k_flash_prefill<64>, grid, dim3(256), 0, s, a);
+        if (q8) launch(k_flash_prefill<64, true>, grid, dim3(256), 0, s, a);
+        else launch(k_flash_prefill<64, false>, grid, dim3(256), 0, s, a);
         if (ns > 1) launch(k_flash_merge<64>, dim3(a.T, (a.H * 16 + 255) / 256), dim3(256), 0, s, a, 32 * Tb);
         return true;
     case 128:
-        launch(k_flash_prefill<128>, grid, dim3(256), 0, s, a);
+        if (q8) launch(k_flash_prefill<128, true>, grid, dim3(256), 0, s, a);
+        else launch(k_flash_prefill<128, false>, grid, dim3(256), 0, s, a);
         if (ns > 1) launch(k_flash_merge<128>, dim3(a.T, (a.H * 32 + 255) / 256), dim3(256), 0, s, a, 32 * Tb);
         return true;
     default: return false;

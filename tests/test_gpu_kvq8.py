@@ -113,3 +113,44 @@ def test_q8_cache_gguf_load(dec, orc, tmp_path):
     assert res[0][0] == res[1][0]
     for a, b in zip(res[0][1], res[1][1]):
         assert np.array_equal(np.asarray(a), np.asarray(b))
+
+
+@pytest.mark.parametrize("hd,H,Hkv", [(128, 8, 2), (64, 8, 8)])
+def test_q8_cache_flash_prefill_matches_splitk_and_oracle(dec, orc, hd, H, Hkv):
+    """Prefill ubatches over a Q8_0 cache take the flash kernel, whose K and V
+    tiles hold code * scale as f16 value + remainder (exact); the split-K
+    decode kernels (DECODE_PREFILL_ATTN=splitk) read the codes directly.
+    Every logits row of a 600-token prompt (ubatches of 128: key ranges split
+    over blocks, a ragged last ubatch) agrees between the two to rounding,
+    and rows at each ubatch's end meet the oracle."""
+    import os
+    hp = small_hp(synth.Q4_0, synth.Q8_0, n_layer=2, n_embd=H * hd, n_head=H, n_head_kv=Hkv, head_dim=hd,
+                  n_ff=1024, n_vocab=1024)
+    w = synth.weights_numpy(hp, 160 + hd, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], 600, 161)
+    gm = dec.Model(hp, w)
+    rows = {}
+    saved = os.environ.get("DECODE_PREFILL_ATTN")
+    try:
+        for form in ("flash", "splitk"):
+            if form == "splitk":
+                os.environ["DECODE_PREFILL_ATTN"] = "splitk"
+            else:
+                os.environ.pop("DECODE_PREFILL_ATTN", None)
+            ctx = dec.Context(gm, n_ctx=1024, n_batch=600, n_ubatch=128)
+            assert ctx.prefill(prompt, 0, output_all=True) == 0
+            rows[form] = np.stack([ctx.logits(i) for i in range(len(prompt))]).astype(np.float64)
+            del ctx
+    finally:
+        if saved is None:
+            os.environ.pop("DECODE_PREFILL_ATTN", None)
+        else:
+            os.environ["DECODE_PREFILL_ATTN"] = saved
+    a, b = rows["flash"], rows["splitk"]
+    assert np.abs(a).max() > 1e-2
+    assert np.abs(a - b).max() <= 1e-4 * np.abs(b).max(), np.abs(a - b).max()
+    oc = orc.Context(orc.Model(hp, w), 1, 1024)
+    for i, t in enumerate(prompt):
+        r = oc.eval(0, int(t))
+        if i in (127, 255, 383, 511, 599):
+            assert_logits_close(a[i], r, f"flash q8 row {i}")
