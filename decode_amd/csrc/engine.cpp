@@ -694,6 +694,7 @@ struct dec_ctx {
     struct Lane {
         hipStream_t s = nullptr;
         float *x = nullptr, *q = nullptr, *part = nullptr, *ml = nullptr, *ssp = nullptr, *gws = nullptr;
+        float *kv_stage = nullptr;       // Q8_0 cache: f32 rows of the ubatch's new K / V, coded after QKV
         uint16_t *qh = nullptr, *ql = nullptr, *xn = nullptr, *xn_lo = nullptr, *o = nullptr, *o_lo = nullptr,
                  *h = nullptr, *h_lo = nullptr;
         std::vector<hipEvent_t> kv_ev;   // per layer: this lane's K/V of the layer are in the cache
@@ -703,6 +704,7 @@ struct dec_ctx {
     Lane lanes[MAX_LANES];
     int n_lanes = 1;           // lanes allocated (more than 1: multi-ubatch prefill on an f16 / f32 cache)
     int lane_cur = 0;          // lane whose buffers the fields above hold
+    float *kv_stage = nullptr; // the current lane's Q8_0 staging rows (null: f16 / f32 cache)
     int lane_wait = -1;        // lane whose K/V events the running ubatch's attention waits for
                                // (-1: lanes unused; -2: the call's first ubatch, which only records)
     bool registered = false;   // counted in m->n_ctx_refs
@@ -754,6 +756,7 @@ static void use_lane(dec_ctx *c, int k) {
     c->o_lo = L.o_lo;
     c->h = L.h;
     c->h_lo = L.h_lo;
+    c->kv_stage = L.kv_stage;
     c->lane_cur = k;
 }
 
@@ -775,6 +778,7 @@ static void save_lane(dec_ctx *c, int k) {
     L.o_lo = c->o_lo;
     L.h = c->h;
     L.h_lo = c->h_lo;
+    L.kv_stage = c->kv_stage;
 }
 
 enum { SEG_ALL = 0, SEG_PRE = 1, SEG_MID = 2, SEG_POST = 3 };
@@ -984,6 +988,7 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
     const size_t kv_elems = (size_t)n_seq * h.n_head_kv * n_ctx * hd;
     float *kv_stage = q8 ? (float *)c->mem.get((size_t)c->Tmax * 2 * m->kd * 4) : nullptr;
     bool ok = !q8 || kv_stage;
+    c->kv_stage = kv_stage;
     c->kv.resize(h.n_layer);
     for (int l = 0; ok && l < h.n_layer; l++) {
         KVLayer &L = c->kv[l];
@@ -1034,15 +1039,14 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
              c->amax && c->dev_step;
     }
     if (ok) save_lane(c, 0);
-    // lanes 1.. (prefill calls of several ubatches; an f16 / f32 cache: the
-    // Q8_0 cache's staging rows are one buffer for the context);
-    // DECODE_PREFILL_LANES = 1..4 lanes, default 2
+    // lanes 1.. (prefill calls of several ubatches; a Q8_0 cache gives each
+    // lane its own staging rows); DECODE_PREFILL_LANES = 1..4 lanes, default 2
     int want = 2;
     if (const char *lv = getenv("DECODE_PREFILL_LANES")) {
         const int v = atoi(lv);
         want = v < 1 ? 1 : v > dec_ctx::MAX_LANES ? dec_ctx::MAX_LANES : v;
     }
-    if (ok && n_batch > n_ubatch && !q8 && want > 1) {
+    if (ok && n_batch > n_ubatch && want > 1) {
         bool lok = true;
         int k = 1;
         for (; lok && k < want; k++) {
@@ -1062,8 +1066,9 @@ extern "C" dec_ctx *dec_ctx_new(dec_model *m, const dec_ctx_params *pp) {
             L.part = (float *)c->mem.get(Tu * h.n_head * c->max_chunks * hd * 4);
             L.ml = (float *)c->mem.get(Tu * h.n_head * c->max_chunks * 2 * 4);
             L.gws = c->gws_bytes ? (float *)c->mem.get(c->gws_bytes) : nullptr;
+            L.kv_stage = q8 ? (float *)c->mem.get(Tu * 2 * m->kd * 4) : nullptr;
             lok = L.x && L.xn && L.xn_lo && L.ssp && L.q && L.qh && L.ql && L.o && L.o_lo && L.h && L.h_lo &&
-                  L.part && L.ml && (L.gws || !c->gws_bytes);
+                  L.part && L.ml && (L.gws || !c->gws_bytes) && (L.kv_stage || !q8);
             if (lok) HIP_OK(hipStreamCreateWithFlags(&L.s, hipStreamNonBlocking), lok = false);
         }
         const int nl = lok ? want : k - 1;               // lanes whose buffers and stream exist
@@ -1208,6 +1213,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         eq.qd = qd;
         eq.kd = m->kd;
         eq.kv = c->kv[l];
+        if (c->kv_stage) eq.kv.stage = c->kv_stage;      // this lane's staging rows
         eq.tok = ti;
         eq.rope_cs = c->rope_cs;
         ok = ok && stage(c, DEC_K_QKV, l, [&] {
@@ -1231,7 +1237,9 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
                                   attention_codes_rows(h.kvtype, h.head_dim);
         if (h.kvtype == DEC_Q8_0 && !code_in_attn)
             ok = ok && stage(c, -1, l, [&] {
-                launch_kv_quant(c->kv[l], ti, T, s);
+                KVLayer kq = c->kv[l];
+                kq.stage = c->kv_stage;
+                launch_kv_quant(kq, ti, T, s);
                 return true;
             });
         // prefill lanes: this ubatch's K/V of layer l are in the cache; the
@@ -1247,6 +1255,7 @@ static bool run_tokens(dec_ctx *c, int off, int T, int row0, int n_rows, int out
         at.qh = c->qh;
         at.ql = c->ql;
         at.kv = c->kv[l];
+        if (c->kv_stage) at.kv.stage = c->kv_stage;
         at.tok = ti;
         at.H = h.n_head;
         at.part = c->part;

@@ -211,7 +211,7 @@ typedef struct {
  *                         decode kernels instead of the flash kernel
  *   DECODE_PREFILL_LANES=n  buffer sets and streams the ubatches of a prefill
  *                         call go round (1..4, default 2; 1 runs them one
- *                         after another; a Q8_0 cache always takes 1); each
+ *                         after another); each
  *                         extra lane holds one ubatch's activations and
  *                         GEMM workspace.  With n >= 2 the wide GEMM form
  *                         splits K at most 4 ways (8 with one lane), so rows

@@ -60,10 +60,12 @@ def _run(dec, gm, prompt, feed, n_ubatch, lanes, split_at=None):
     return np.stack(rows), np.stack(steps)
 
 
-@pytest.mark.parametrize("wtype", [synth.Q4_0, synth.Q8_0])
-def test_lanes_bitwise_equal_one_lane_and_match_oracle(dec, orc, wtype):
-    hp = small_hp(wtype, synth.F16, n_layer=3, n_embd=512, n_head=8, n_head_kv=2, n_ff=1024, n_vocab=1024)
-    w = synth.weights_numpy(hp, 1410 + wtype, threads=4)
+@pytest.mark.parametrize("wtype,kvtype", [(synth.Q4_0, synth.F16), (synth.Q8_0, synth.F16),
+                                          (synth.Q4_0, synth.Q8_0)])
+def test_lanes_bitwise_equal_one_lane_and_match_oracle(dec, orc, wtype, kvtype):
+    # (a Q8_0 cache: each lane codes its ubatch's new K / V from staging rows of its own)
+    hp = small_hp(wtype, kvtype, n_layer=3, n_embd=512, n_head=8, n_head_kv=2, n_ff=1024, n_vocab=1024)
+    w = synth.weights_numpy(hp, 1410 + wtype + 7 * kvtype, threads=4)
     prompt = synth.prompt(hp["n_vocab"], 600, 1411)           # ubatches 128 x 4 and a ragged 88
     feed = synth.prompt(hp["n_vocab"], 3, 1412)
     gm = dec.Model(hp, w)
