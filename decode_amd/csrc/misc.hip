@@ -306,8 +306,29 @@ __global__ __launch_bounds__(1024) void k_argmax(const float *logits, int V, int
     const float *l = logits + (size_t)t * V;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    int j = tid;
-    for (; j + 3 * 1024 < V; j += 4 * 1024) {       // four independent loads in flight
+    int j = 0;
+    if (V % 4 == 0 && ((uintptr_t)l & 15) == 0) {
+        // up to 32768 values: every 16-byte load of the thread in flight at once
+        constexpr int R = 8;
+        float4 v[R];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int e = 4 * (tid + 1024 * r);
+            v[r] = e < V ? *(const float4 *)(l + e) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        }
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int e = 4 * (tid + 1024 * r);
+            if (e < V) {
+                amax_take(bv, bi, v[r].x, e);
+                amax_take(bv, bi, v[r].y, e + 1);
+                amax_take(bv, bi, v[r].z, e + 2);
+                amax_take(bv, bi, v[r].w, e + 3);
+            }
+        }
+        j = 4 * 1024 * R;
+    }
+    for (j += tid; j + 3 * 1024 < V; j += 4 * 1024) {   // four independent loads in flight
         const float v0 = l[j], v1 = l[j + 1024], v2 = l[j + 2048], v3 = l[j + 3072];
         amax_take(bv, bi, v0, j);
         amax_take(bv, bi, v1, j + 1024);
