@@ -304,6 +304,18 @@ __global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
     }
 }
 
+// Sum and max of a value over lanes l and l ^ 32 with one v_permlane32_swap
+// (each lane gets back its own value and its partner's, in lane order), in
+// place of a cross-lane shuffle through LDS.
+DEV float half_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+DEV float half_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 constexpr int MW = 2;                // wavefronts per block of the MFMA kernel
 constexpr int CHM = 32 * MW;        // cached rows per chunk of the MFMA kernel
 
@@ -413,6 +425,9 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
         const int pc = u * 64 + lane, key = min(k0 + pc / VP, pos);
         vraw[u] = *(const u32x4 *)(Vb + (size_t)key * HD + 8 * (pc % VP));
     }
+    // keep these requests here: left to itself the compiler issues them only
+    // after the scores' softmax, a second round trip in the wavefront's chain
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- KT: K tile through LDS (rows padded by 16 bytes) ----
     if constexpr (KT) {
@@ -445,7 +460,7 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
         if (key > pos) sacc[r] = -INFINITY;
         m = fmaxf(m, sacc[r]);
     }
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    m = half_max(m);
     float l = 0.f;
     h8 ph[2], pl[2];
 #pragma unroll
@@ -456,7 +471,7 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma(AttnArgs a) {
         ph[r >> 3][r & 7] = p16;
         pl[r >> 3][r & 7] = (f16)(p - (float)p16);
     }
-    l += __shfl_xor(l, 32, 64);
+    l = half_sum(l);
 
     // ---- V tile through LDS (rows padded by 16 bytes) ----
     f16 *vt = &vtile[w][0];
@@ -634,14 +649,14 @@ __global__ __launch_bounds__(MW * 64) void k_attn_mfma_q8(AttnArgs a) {
         if (key > pos) sacc[r] = -INFINITY;
         m = fmaxf(m, sacc[r]);
     }
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    m = half_max(m);
     float l = 0.f, p[16];
 #pragma unroll
     for (int r = 0; r < 16; r++) {
         p[r] = m == -INFINITY ? 0.f : __expf(sacc[r] - m);
         l += p[r];
     }
-    l += __shfl_xor(l, 32, 64);
+    l = half_sum(l);
 
     // ---- O = P V: tile dt takes A = P d_V(key, dt) (value + remainder) ----
     f16x o[NB];
