@@ -230,6 +230,7 @@ __global__ __launch_bounds__(256) void k_put_blocks_q4k(const uint4 *src, int ro
 }
 
 // ---- embedding: x[t] = dequantized row tok[t] (the article's get_rows) -----
+template <int WT>
 __global__ __launch_bounds__(256) void k_embed(QMat E, const int32_t *tok, float *x, int ldx, float *ss_out) {
     __shared__ float red[4];
     const int t = blockIdx.x;
@@ -237,32 +238,38 @@ __global__ __launch_bounds__(256) void k_embed(QMat E, const int32_t *tok, float
     const int row = tok[t];
     const int K = E.K, nb = K >> 5;
     float *xr = x + (size_t)t * ldx;
-    for (int j = threadIdx.x; j < K; j += 256) {
-        float v;
-        if (E.wtype == T_F32) {
-            v = ((const float *)E.qs)[(size_t)row * K + j];
-        } else if (E.wtype == T_Q4_K) {
+    // element j of the row, dequantized
+    auto elem = [&](int j) __attribute__((always_inline)) -> float {
+        if constexpr (WT == T_F32) return ((const float *)E.qs)[(size_t)row * K + j];
+        const int b = j >> 5, e = j & 31;
+        if constexpr (WT == T_Q4_K) {
 #pragma clang fp contract(off)
-            const int b = j >> 5, e = j & 31;
             const uint32_t dd = E.dm[(size_t)row * (K >> 8) + (b >> 3)];
             const uint16_t sm = E.d[(size_t)row * nb + b];
             const uint8_t byte = ((const uint8_t *)E.qs)[(size_t)row * (K >> 1) + b * 16 + (e & 15)];
             const int c = e < 16 ? (byte & 15) : (byte >> 4);
-            v = f16_bits_to_f32((uint16_t)dd) * (float)(sm & 63) * (float)c -
-                f16_bits_to_f32((uint16_t)(dd >> 16)) * (float)(sm >> 8);
-        } else {
-            const int b = j >> 5, e = j & 31;
-            const float d = f16_bits_to_f32(E.d[(size_t)row * nb + b]);
-            if (E.wtype == T_Q8_0) {
-                v = (float)((const int8_t *)E.qs)[(size_t)row * K + j] * d;
-            } else {
-                const uint8_t byte = ((const uint8_t *)E.qs)[(size_t)row * (K >> 1) + b * 16 + (e & 15)];
-                const int c = e < 16 ? (byte & 15) : (byte >> 4);
-                v = (float)(c - 8) * d;
-            }
+            return f16_bits_to_f32((uint16_t)dd) * (float)(sm & 63) * (float)c -
+                   f16_bits_to_f32((uint16_t)(dd >> 16)) * (float)(sm >> 8);
         }
-        xr[j] = v;
-        ss += v * v;
+        const float d = f16_bits_to_f32(E.d[(size_t)row * nb + b]);
+        if constexpr (WT == T_Q8_0) return (float)((const int8_t *)E.qs)[(size_t)row * K + j] * d;
+        const uint8_t byte = ((const uint8_t *)E.qs)[(size_t)row * (K >> 1) + b * 16 + (e & 15)];
+        const int c = e < 16 ? (byte & 15) : (byte >> 4);
+        return (float)(c - 8) * d;
+    };
+    // a thread's elements are computed 16 at a time and stored after them: a
+    // store between two loads of the table would make each load wait for it
+    constexpr int U = 16;
+    for (int j0 = threadIdx.x; j0 < K; j0 += 256 * U) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) v[u] = elem(min(j0 + 256 * u, K - 1));   // (past K: re-read, not stored)
+#pragma unroll
+        for (int u = 0; u < U; u++)
+            if (j0 + 256 * u < K) {
+                xr[j0 + 256 * u] = v[u];
+                ss += v[u] * v[u];
+            }
     }
     // sum of squares of the row for the first RMSNorm: slot 0, other slots 0
     if (ss_out) {
@@ -399,7 +406,12 @@ void launch_kv_quant(const KVLayer &kv, TokInfo tok, int T, hipStream_t s) {
 }
 
 void launch_embed(const QMat &E, const int32_t *tok, int T, float *x, int ldx, float *ss_out, hipStream_t s) {
-    launch(k_embed, dim3(T), dim3(256), 0, s, E, tok, x, ldx, ss_out);
+    switch (E.wtype) {
+    case T_F32: launch(k_embed<T_F32>, dim3(T), dim3(256), 0, s, E, tok, x, ldx, ss_out); break;
+    case T_Q8_0: launch(k_embed<T_Q8_0>, dim3(T), dim3(256), 0, s, E, tok, x, ldx, ss_out); break;
+    case T_Q4_K: launch(k_embed<T_Q4_K>, dim3(T), dim3(256), 0, s, E, tok, x, ldx, ss_out); break;
+    default: launch(k_embed<T_Q4_0>, dim3(T), dim3(256), 0, s, E, tok, x, ldx, ss_out); break;
+    }
 }
 
 void launch_rmsnorm(const float *x, int ldx, const float *g, int d, float eps,
