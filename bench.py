@@ -450,7 +450,7 @@ def main():
                          "scaling the HBM fetch/write counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on exactly one GPU (the decode step of one sequence "
+        print("bench.py: the library runs on exactly one GPU (the decode step of one sequence "
               "batch on one MI355X); --gpus N>1 is not supported.", file=sys.stderr)
         sys.exit(2)
 
