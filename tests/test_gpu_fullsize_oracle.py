@@ -13,7 +13,7 @@ ragged one (the 128-token GEMM tiles with their K split, the flash key
 ranges with their merge, the decode mat-vecs and split-K attention after
 it); the 1B Q8_0 workload's own 512-token ubatch; and a narrow model whose
 4200-token prompt makes attention read up to 4200 cached positions.
-Acceptance (the benchmark spec): max |g - o| <= 2e-2 and <= 1e-2 of the row's
+Acceptance: max |g - o| <= 2e-2 and <= 1e-2 of the row's
 largest |logit|; identical greedy tokens (a differing token is accepted only
 as a near-tie: top-2 margin below the measured error, and it is reported).
 """
