@@ -62,6 +62,24 @@ DEV int vt_col(int k) {         // permuted column of key k (0..63) in V^T
     return (s << 4) | (h << 3) | e;
 }
 
+// Q8_0 staging in f16 pairs: four codes (code k in byte k) become exact f16
+// pairs (c0, c1), (c2, c3) -- byte c + 128 under the exponent of 1024 is the
+// f16 1152 + c, less 1152 -- and a pair times the block scale s splits into
+// value RNE(c s) and remainder RNE(c s - value), the same numbers as
+// rounding the exact fp32 product and the exact fp32 difference.
+constexpr uint32_t FQ_1024_BYTES = 0x64646464u;   // every byte the high byte of f16 1024
+constexpr uint32_t FQ_1152 = 0x64806480u;         // f16 pair (1152, 1152)
+DEV void fq_codes4(uint32_t w, h2 &a, h2 &b) {
+    const uint32_t x = w ^ 0x80808080u;
+    a = as_h2(__builtin_amdgcn_perm(FQ_1024_BYTES, x, 0x04010400u)) - as_h2(FQ_1152);
+    b = as_h2(__builtin_amdgcn_perm(FQ_1024_BYTES, x, 0x04030402u)) - as_h2(FQ_1152);
+}
+DEV void fq_split(h2 c, h2 s2, uint32_t &hi, uint32_t &lo) {
+    const h2 h = c * s2;
+    hi = h2_bits(h);
+    lo = h2_bits(__builtin_elementwise_fma(c, s2, -h));
+}
+
 template <int HD, bool Q8>
 __global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
     constexpr int KS = HD / 16;     // k-steps of Q K^T
@@ -200,38 +218,48 @@ __global__ __launch_bounds__(256, 2) void k_flash_prefill(FlashArgs a) {
             }
         }
     };
-    // code * scale (exact in fp32) as f16 value + f16 remainder
-    auto dq_split = [](int code, float sc, f16 &hi, f16 &lo) __attribute__((always_inline)) {
-        const float v = (float)code * sc;
-        hi = (f16)v;
-        lo = (f16)(v - (float)hi);
-    };
     auto store_q8 = [&]() {
         if (tid < KPC) {
             const int key = tid / NB, blk = tid % NB;
-            const float sc = f16_bits_to_f32(ksc);
-            const int8_t *c8 = (const int8_t *)kq;
+            const h2 s2 = as_h2((uint32_t)ksc | ((uint32_t)ksc << 16));
+            const uint32_t *cw = (const uint32_t *)kq;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                f16 hv[8], lv[8];
-#pragma unroll
-                for (int e = 0; e < 8; e++) dq_split(c8[8 * i + e], sc, hv[e], lv[e]);
-                *(uint4 *)&Ks[0][key][32 * blk + 8 * i] = *(const uint4 *)hv;
-                *(uint4 *)&Ks[1][key][32 * blk + 8 * i] = *(const uint4 *)lv;
+            for (int i = 0; i < 4; i++) {                   // codes 8i .. 8i+7
+                h2 c[4];
+                fq_codes4(cw[2 * i], c[0], c[1]);
+                fq_codes4(cw[2 * i + 1], c[2], c[3]);
+                uint4 hv, lv;
+                fq_split(c[0], s2, hv.x, lv.x);
+                fq_split(c[1], s2, hv.y, lv.y);
+                fq_split(c[2], s2, hv.z, lv.z);
+                fq_split(c[3], s2, hv.w, lv.w);
+                *(uint4 *)&Ks[0][key][32 * blk + 8 * i] = hv;
+                *(uint4 *)&Ks[1][key][32 * blk + 8 * i] = lv;
             }
         }
         if (tid < VPC) {
             const int key = 2 * (tid & 31), hb = tid >> 5;
             const int col = vt_col(key);                    // even; key + 1 sits at col + 1
-            const float s0 = f16_bits_to_f32(vsc[0]), s1 = f16_bits_to_f32(vsc[1]);
-            const int8_t *c0 = (const int8_t *)&vq[0], *c1 = (const int8_t *)&vq[1];
+            uint32_t hk[2][8], lk[2][8];                    // [key][dim pair]
 #pragma unroll
-            for (int e = 0; e < 16; e++) {
-                f16 h0, l0, h1, l1;
-                dq_split(c0[e], s0, h0, l0);
-                dq_split(c1[e], s1, h1, l1);
-                *(uint32_t *)&Vt[0][16 * hb + e][col] = h2_bits(h2{h0, h1});
-                *(uint32_t *)&Vt[1][16 * hb + e][col] = h2_bits(h2{l0, l1});
+            for (int j = 0; j < 2; j++) {
+                const h2 s2 = as_h2((uint32_t)vsc[j] | ((uint32_t)vsc[j] << 16));
+                const uint32_t *cw = (const uint32_t *)&vq[j];
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    h2 c0, c1;
+                    fq_codes4(cw[q], c0, c1);
+                    fq_split(c0, s2, hk[j][2 * q], lk[j][2 * q]);
+                    fq_split(c1, s2, hk[j][2 * q + 1], lk[j][2 * q + 1]);
+                }
+            }
+            // dim 2m takes the low halves of both keys' pair m, dim 2m+1 the high
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                *(uint32_t *)&Vt[0][16 * hb + 2 * m][col] = __builtin_amdgcn_perm(hk[1][m], hk[0][m], 0x05040100u);
+                *(uint32_t *)&Vt[0][16 * hb + 2 * m + 1][col] = __builtin_amdgcn_perm(hk[1][m], hk[0][m], 0x07060302u);
+                *(uint32_t *)&Vt[1][16 * hb + 2 * m][col] = __builtin_amdgcn_perm(lk[1][m], lk[0][m], 0x05040100u);
+                *(uint32_t *)&Vt[1][16 * hb + 2 * m + 1][col] = __builtin_amdgcn_perm(lk[1][m], lk[0][m], 0x07060302u);
             }
         }
     };
