@@ -126,3 +126,45 @@ def test_lanes_split_cap_rows_agree(dec, orc):
         r = oc.eval(0, int(t))
         if i in want:
             assert_logits_close(two[0][i], r, f"prefill row {i}")
+
+
+def test_lanes_abort_then_continue(dec):
+    # an abort between ubatches returns after the lanes are joined: the rows
+    # written so far stay, and a later call continues from them
+    hp = small_hp(synth.Q4_0, synth.F16)
+    w = synth.weights_numpy(hp, 1440, threads=4)
+    gm = dec.Model(hp, w)
+    p = synth.prompt(hp["n_vocab"], 100, 1441)
+    key = "DECODE_PREFILL_LANES"
+    saved = os.environ.get(key)
+    last = {}
+    try:
+        for lanes in (1, 2):
+            os.environ[key] = str(lanes)
+            state = {"calls": 0, "armed": True}
+
+            def abort(ud):
+                state["calls"] += 1
+                return 1 if state["armed"] and state["calls"] >= 2 else 0
+
+            ctx = dec.Context(gm, n_ctx=256, n_batch=128, n_ubatch=32, abort=abort)
+            assert ctx.prefill(p, 0) == 2
+            assert ctx.pos_max(0) == 63
+            state["armed"] = False                      # no abort during the second call
+            assert ctx.prefill(p[64:], 0) == 0
+            assert ctx.pos_max(0) == 99
+            last[lanes] = ctx.logits(0)
+            assert ctx.decode([int(p[0])]) == 0
+            last[(lanes, "step")] = ctx.logits(0)
+            del ctx
+    finally:
+        if saved is None:
+            os.environ.pop(key, None)
+        else:
+            os.environ[key] = saved
+    assert np.array_equal(last[1], last[2])
+    assert np.array_equal(last[(1, "step")], last[(2, "step")])
+    whole = dec.Context(gm, n_ctx=256, n_batch=128, n_ubatch=32)
+    assert whole.prefill(p, 0) == 0
+    ref = whole.logits(0)
+    assert np.abs(last[2] - ref).max() <= 1e-4 * np.abs(ref).max()
