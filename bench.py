@@ -205,7 +205,7 @@ def kv_q8_leg(dec, torch, model, hp, prompt, n_ctx, n_ubatch, sp, warm, steps, p
             "kv_bytes_per_position": int(hp["n_layer"] * 2 * hp["n_head_kv"] * hp["head_dim"] * 34 / 32),
             "attention": attention_roofline(hp, 2, probe, mean_ctx),
             "note": "same weights and prompt, K/V cached as Q8_0 blocks; attention = split-K partials "
-                    "+ merge of one layer, timed live; prefill attention takes the split-K kernel"}
+                    "+ merge of one layer, timed live; prefill attention takes the flash kernel on the codes"}
 
 
 def q4k_leg(dec, torch, model, hp, prompt, n_ctx, n_ubatch, sp, warm, steps, probe_layer, log):

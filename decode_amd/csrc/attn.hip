@@ -242,9 +242,11 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
 
 // Merge of the chunk partials of one (head, token), 32 dims per block: one
 // wavefront, so every step is a lane exchange and nothing waits at a
-// barrier.  Lane l holds dims 4 (l % 8) .. +3 of chunks l / 8 + 8 i, and the
-// statistics of chunk l; all of them are requested at entry (rounds of 64
-// chunks past the first), then
+// barrier.  Lane l holds the statistics of chunks l and l + 64, and dims
+// 4 (l % 8) .. +3 of chunks l / 8 + 8 i (i < 16): the first 128 chunks'
+// loads are all requested at entry, the statistics first, so a context of
+// up to 128 chunks costs one memory latency (longer ones take further rounds
+// of 64 chunks).  Then
 //   M = max_c m_c, w_c = e^(m_c - M), L = sum_c l_c w_c, o = sum_c acc_c w_c / L.
 template <int HD>
 __global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
@@ -255,34 +257,41 @@ __global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
     const float *ml = a.ml + hh * a.max_chunks * 2;
     const float *pa = a.part + hh * a.max_chunks * HD + d0 + 4 * dq;
     // chunks past nch re-read the last one; their weights are 0
-    f4 v[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = *(const f4 *)(pa + (size_t)min(cg + 8 * i, nch - 1) * HD);
     const float2 s0 = *(const float2 *)(ml + 2 * min(lane, nch - 1));
-    float mloc = lane < nch ? s0.x : -INFINITY;
-    for (int c = lane + 64; c < nch; c += 64) mloc = fmaxf(mloc, ml[2 * c]);
+    const float2 s1 = *(const float2 *)(ml + 2 * min(lane + 64, nch - 1));
+    f4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) v[i] = *(const f4 *)(pa + (size_t)min(cg + 8 * i, nch - 1) * HD);
+    float mloc = fmaxf(lane < nch ? s0.x : -INFINITY, lane + 64 < nch ? s1.x : -INFINITY);
+    for (int c = lane + 128; c < nch; c += 64) mloc = fmaxf(mloc, ml[2 * c]);
     mloc = row16_max(mloc);
     const float M = fmaxf(fmaxf(readlane_f(mloc, 0), readlane_f(mloc, 16)), fmaxf(readlane_f(mloc, 32), readlane_f(mloc, 48)));
-    float wl = lane < nch && s0.x != -INFINITY ? __expf(s0.x - M) : 0.f;
-    float lloc = lane < nch ? s0.y * wl : 0.f;
-    for (int c = lane + 64; c < nch; c += 64) {
+    const float w0 = lane < nch && s0.x != -INFINITY ? __expf(s0.x - M) : 0.f;
+    const float w1 = lane + 64 < nch && s1.x != -INFINITY ? __expf(s1.x - M) : 0.f;
+    // (l of a chunk is finite: a weight of 0 zeroes it)
+    float lloc = s0.y * w0 + s1.y * w1;
+    for (int c = lane + 128; c < nch; c += 64) {
         const float2 sc = *(const float2 *)(ml + 2 * c);
         lloc += sc.x == -INFINITY ? 0.f : sc.y * __expf(sc.x - M);
     }
     const float L = wave_sum_dpp(lloc);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0;;) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        // chunk cg + 8 i: its weight is w0 (i < 8) or w1 (i >= 8) of lane cg + 8 (i % 8)
+        const float wc = __shfl(i < 8 ? w0 : w1, cg + 8 * (i & 7), 64);
+        if (cg + 8 * i < nch) acc += v[i] * wc;
+    }
+    for (int c0 = 128; c0 < nch; c0 += 64) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = *(const f4 *)(pa + (size_t)min(c0 + cg + 8 * i, nch - 1) * HD);
+        const float2 sc = *(const float2 *)(ml + 2 * min(c0 + lane, nch - 1));
+        const float wl = c0 + lane < nch && sc.x != -INFINITY ? __expf(sc.x - M) : 0.f;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const float wc = __shfl(wl, cg + 8 * i, 64);
             if (c0 + cg + 8 * i < nch) acc += v[i] * wc;
         }
-        c0 += 64;
-        if (c0 >= nch) break;
-#pragma unroll
-        for (int i = 0; i < 8; i++) v[i] = *(const f4 *)(pa + (size_t)min(c0 + cg + 8 * i, nch - 1) * HD);
-        const float2 sc = *(const float2 *)(ml + 2 * min(c0 + lane, nch - 1));
-        wl = c0 + lane < nch && sc.x != -INFINITY ? __expf(sc.x - M) : 0.f;
     }
     // sum over the 8 chunk groups (lane bits 3..5)
 #pragma unroll

@@ -192,3 +192,42 @@ def test_eager_decode_equals_graph_decode_and_probe_counts(dec):
     ms, n = b.probe()
     assert n == 3 + 6 and ms > 0
     assert a.stats()["n_graph_captures"] == 1 and b.stats()["n_graph_captures"] == 0
+
+
+@pytest.mark.parametrize("kvtype", [synth.F16, synth.Q8_0])
+def test_decode_merge_over_chunk_rounds_matches_prefill_rows(dec, kvtype):
+    # decode attention splits the keys into 64-key chunks and merges their
+    # partials; the merge loads the first 128 chunks at once and takes
+    # further rounds of 64 past them.  Decode steps at positions whose chunk
+    # counts sit at each edge (1, 64, 65, 128, 129, 130, 193) must give the
+    # rows that prefilling the same tokens gives (flash attention, no merge
+    # of decode partials).
+    hp = small_hp(synth.Q8_0, kvtype, n_layer=2, n_embd=256, n_head=4, n_head_kv=2, n_vocab=512)
+    w = synth.weights_numpy(hp, 1450 + kvtype, threads=4)
+    targets = [63, 4095, 4096, 8191, 8192, 8255, 8256, 12345]
+    n = targets[-1] + 1
+    prompt = synth.prompt(hp["n_vocab"], n, 1451)
+    gm = dec.Model(hp, w)
+    piece = 4096
+    a = dec.Context(gm, n_ctx=12544, n_batch=piece, n_ubatch=512)
+    steps, done = {}, 0
+    for t in targets:
+        for s in range(done, t, piece):
+            assert a.prefill(prompt[s:min(t, s + piece)], 0) == 0
+        assert a.decode([int(prompt[t])]) == 0
+        steps[t] = a.logits(0)
+        done = t + 1
+    assert a.pos_max(0) == targets[-1]
+    a.close()
+    b = dec.Context(gm, n_ctx=12544, n_batch=piece, n_ubatch=512)
+    rows = {}
+    for s in range(0, n, piece):
+        assert b.prefill(prompt[s:min(n, s + piece)], 0, output_all=True) == 0
+        for t in targets:
+            if s <= t < s + piece:
+                rows[t] = b.logits(t - s)
+    b.close()
+    for t in targets:
+        ma, rel = logit_err(steps[t], rows[t])
+        print(f"position {t} ({t // 64 + 1} chunks): max-abs {ma:.3e} rel {rel:.3e}")
+        assert rel <= 1e-4, (t, ma, rel)
