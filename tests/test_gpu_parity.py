@@ -231,3 +231,44 @@ def test_decode_merge_over_chunk_rounds_matches_prefill_rows(dec, kvtype):
         ma, rel = logit_err(steps[t], rows[t])
         print(f"position {t} ({t // 64 + 1} chunks): max-abs {ma:.3e} rel {rel:.3e}")
         assert rel <= 1e-4, (t, ma, rel)
+
+
+def test_largest_context_and_row(dec, orc):
+    # the limits the header states: a context of DEC_MAX_CTX positions
+    # (decode merges 1024 chunks there) and an FFN row of DEC_MAX_ROW
+    # elements (the down mat-vec's whole LDS image, K 16384 in the GEMMs)
+    max_ctx, max_row = 65536, 16384
+    hp = small_hp(synth.Q4_0, synth.F16, n_layer=1, n_embd=256, n_head=4, n_head_kv=2, n_ff=max_row,
+                  n_vocab=512)
+    w = synth.weights_numpy(hp, 1460, threads=4)
+    prompt = synth.prompt(hp["n_vocab"], max_ctx, 1461)
+    gm = dec.Model(hp, w)
+    piece = 8192
+    # b: the whole context as prefill; its first rows against the oracle
+    b = dec.Context(gm, n_ctx=max_ctx, n_batch=piece, n_ubatch=512)
+    assert b.prefill(prompt[:5], 0, output_all=True) == 0
+    oc = orc.Context(orc.Model(hp, w), 1, 16)
+    for i in range(5):
+        assert_logits_close(b.logits(i), oc.eval(0, int(prompt[i])), f"row {i}")
+    for s in range(5, max_ctx, piece):
+        assert b.prefill(prompt[s:min(max_ctx, s + piece)], 0) == 0
+    assert b.pos_max(0) == max_ctx - 1
+    want = b.logits(-1)
+    assert b.prefill(prompt[:1], 0) == 1          # full: nothing changes
+    assert b.pos_max(0) == max_ctx - 1
+    b.close()
+    # a: all but the last position as prefill, the last one as a decode step
+    a = dec.Context(gm, n_ctx=max_ctx, n_batch=piece, n_ubatch=512)
+    for s in range(0, max_ctx - 1, piece):
+        assert a.prefill(prompt[s:min(max_ctx - 1, s + piece)], 0) == 0
+    assert a.decode([int(prompt[-1])]) == 0
+    got = a.logits(0)
+    assert a.pos_max(0) == max_ctx - 1
+    assert a.decode([int(prompt[0])]) == 1        # no room for another position
+    a.close()
+    ma, rel = logit_err(got, want)
+    print(f"position {max_ctx - 1}: decode vs prefill max-abs {ma:.3e} rel {rel:.3e}")
+    # the two paths add 65536 keys' fp32 terms in different orders (1024
+    # chunk partials and a merge, against 64-key tiles in at most 8 key
+    # ranges); measured 4.3e-5
+    assert rel <= 2e-4, (ma, rel)
