@@ -240,18 +240,27 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
     }
 }
 
-// Merge of the chunk partials of one (head, token), 32 dims per block: one
+// Sum of a value over lanes l and l ^ 16 with one v_permlane16_swap (rows 0
+// and 1, and rows 2 and 3, of 16 lanes trade places; each lane gets back its
+// own value and its partner's).
+DEV float pair16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+DEV float half_sum(float v);
+
+// Merge of the chunk partials of one (head, token), 16 dims per block: one
 // wavefront, so every step is a lane exchange and nothing waits at a
 // barrier.  Lane l holds the statistics of chunks l and l + 64, and dims
-// 4 (l % 8) .. +3 of chunks l / 8 + 8 i (i < 16): the first 128 chunks'
+// 4 (l % 4) .. +3 of chunks l / 4 + 16 i (i < 8): the first 128 chunks'
 // loads are all requested at entry, the statistics first, so a context of
 // up to 128 chunks costs one memory latency (longer ones take further rounds
 // of 64 chunks).  Then
 //   M = max_c m_c, w_c = e^(m_c - M), L = sum_c l_c w_c, o = sum_c acc_c w_c / L.
 template <int HD>
 __global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
-    const int h = blockIdx.x, t = blockIdx.y, d0 = 32 * blockIdx.z, lane = threadIdx.x;
-    const int dq = lane & 7, cg = lane >> 3;
+    const int h = blockIdx.x, t = blockIdx.y, d0 = 16 * blockIdx.z, lane = threadIdx.x;
+    const int dq = lane & 3, cg = lane >> 2;
     const int nch = a.tok.pos[t] / a.chunk + 1;
     const size_t hh = (size_t)t * a.H + h;
     const float *ml = a.ml + hh * a.max_chunks * 2;
@@ -259,9 +268,9 @@ __global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
     // chunks past nch re-read the last one; their weights are 0
     const float2 s0 = *(const float2 *)(ml + 2 * min(lane, nch - 1));
     const float2 s1 = *(const float2 *)(ml + 2 * min(lane + 64, nch - 1));
-    f4 v[16];
+    f4 v[8];
 #pragma unroll
-    for (int i = 0; i < 16; i++) v[i] = *(const f4 *)(pa + (size_t)min(cg + 8 * i, nch - 1) * HD);
+    for (int i = 0; i < 8; i++) v[i] = *(const f4 *)(pa + (size_t)min(cg + 16 * i, nch - 1) * HD);
     float mloc = fmaxf(lane < nch ? s0.x : -INFINITY, lane + 64 < nch ? s1.x : -INFINITY);
     for (int c = lane + 128; c < nch; c += 64) mloc = fmaxf(mloc, ml[2 * c]);
     mloc = row16_max(mloc);
@@ -277,27 +286,32 @@ __global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
     const float L = wave_sum_dpp(lloc);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-        // chunk cg + 8 i: its weight is w0 (i < 8) or w1 (i >= 8) of lane cg + 8 (i % 8)
-        const float wc = __shfl(i < 8 ? w0 : w1, cg + 8 * (i & 7), 64);
-        if (cg + 8 * i < nch) acc += v[i] * wc;
+    for (int i = 0; i < 8; i++) {
+        // chunk cg + 16 i: its weight is w0 (i < 4) or w1 (i >= 4) of lane cg + 16 (i % 4)
+        const float wc = __shfl(i < 4 ? w0 : w1, cg + 16 * (i & 3), 64);
+        if (cg + 16 * i < nch) acc += v[i] * wc;
     }
     for (int c0 = 128; c0 < nch; c0 += 64) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) v[i] = *(const f4 *)(pa + (size_t)min(c0 + cg + 8 * i, nch - 1) * HD);
+        for (int i = 0; i < 4; i++) v[i] = *(const f4 *)(pa + (size_t)min(c0 + cg + 16 * i, nch - 1) * HD);
         const float2 sc = *(const float2 *)(ml + 2 * min(c0 + lane, nch - 1));
         const float wl = c0 + lane < nch && sc.x != -INFINITY ? __expf(sc.x - M) : 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const float wc = __shfl(wl, cg + 8 * i, 64);
-            if (c0 + cg + 8 * i < nch) acc += v[i] * wc;
+        for (int i = 0; i < 4; i++) {
+            const float wc = __shfl(wl, cg + 16 * i, 64);
+            if (c0 + cg + 16 * i < nch) acc += v[i] * wc;
         }
     }
-    // sum over the 8 chunk groups (lane bits 3..5)
+    // sum over the 16 chunk groups (lane bits 2..5): lanes l + 4 j of a row
+    // (rotations by 4 and 8), then the other rows (lane ^ 16, lane ^ 32)
 #pragma unroll
-    for (int o = 8; o < 64; o <<= 1)
-#pragma unroll
-        for (int e = 0; e < 4; e++) acc[e] += __shfl_xor(acc[e], o, 64);
+    for (int e = 0; e < 4; e++) {
+        float x = acc[e];
+        x += dpp_f<0x124>(x);
+        x += dpp_f<0x128>(x);
+        x = pair16_sum(x);
+        acc[e] = half_sum(x);
+    }
     if (cg == 0) {
         h2 o[2], ol[2];
 #pragma unroll
@@ -735,7 +749,7 @@ bool launch_hd(const AttnArgs &a, int T, hipStream_t s) {
                                      : launch_part<HD, T_F32>(a, T, s);
     }
     if (!ok) return false;
-    launch((k_attn_merge<HD>), dim3(a.H, T, HD / 32), dim3(64), 0, s, a);
+    launch((k_attn_merge<HD>), dim3(a.H, T, HD / 16), dim3(64), 0, s, a);
     return true;
 }
 
