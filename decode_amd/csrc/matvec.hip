@@ -120,7 +120,8 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         // the first D code pairs go out after the image inputs, so that waiting
         // for the inputs (loads complete in issue order) never waits for them
 #pragma unroll
-        for (int k = 0; k < D; k++) issue(L[k], k);
+        for (int k = 0; k < D; k++)
+            if (k < iters) issue(L[k], k);   // (iters is the same for every wavefront)
         float rs = 0.f;
         if (NORM) {
             float ss;
@@ -222,7 +223,10 @@ __global__ __launch_bounds__(1024) void k_matvec(QMat W, InArgs in, EpiArgs ep, 
         // refill: a use below it would wait for the refill too (loads complete
         // in issue order), which would leave one pair in flight instead of D
         __builtin_amdgcn_sched_barrier(0);
-        issue(cur, it + D);                              // refill with the pair D ahead
+        // refill with the pair D ahead, if there is one: a load of a pair past
+        // the last would re-read the grid's last pair, the same lines from
+        // every wavefront
+        if (it + D < iters) issue(cur, it + D);
         __builtin_amdgcn_sched_barrier(0);
         a0 = wave_sum_dpp(a0);
         a1 = wave_sum_dpp(a1);
